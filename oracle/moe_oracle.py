@@ -1,0 +1,483 @@
+"""CPU oracle for the fp8 block-quantized MoE expert layer.
+
+TEST INFRASTRUCTURE ONLY.  A plain, slow, obviously correct numpy model of
+what the layer computes.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the ``cpu_baseline`` leg of ``bench.py`` may import it; the product path
+never does, and this file shares no code, table or constant generator with
+the HIP library.
+
+Sources (all from the vLLM API documentation pages on the subject):
+  [STAGE]  "vllm.model_executor.layers.fused_moe.prepare_megamoe":
+           ``_quantize_fp8_groups``, ``_store_topk``, ``_pack_bytes``,
+           ``_eplb_kernel_args``, ``prepare_megamoe_inputs``.
+  [HUM]    "vllm.model_executor.layers.fused_moe.experts.fused_humming_moe"
+           (pull-request 58588 build): ``BatchedHummingGroupedExperts.apply``,
+           ``HummingGroupedExperts.apply``, ``HummingExpertsBase``
+           (``process_input``, ``get_buffer_metas``).
+
+Number formats.  bf16 -> fp64 and e4m3fn -> fp64 are exact.  fp32 steps are
+numpy float32 operations (IEEE binary32, round to nearest even).  Block
+partial sums of fp8 products are exact in fp64 (products of two e4m3fn
+values have at most 8 significant bits and lie in [2^-18, 2^17.6], so a sum
+of 128 of them needs fewer than 45 bits).
+
+Readings of points the pages leave open (each one is listed, with its
+reason, in the design notes):
+  * all of the group quantizer runs in fp32 after an exact bf16 -> fp32 upcast;
+  * fp32 divisions are correctly rounded; values are scaled as ``x * (1/s)``;
+  * fp32 -> e4m3fn rounds to nearest even and saturates to +-448;
+  * UE8M0 scale bytes are stored one per group, ``4*ceil(G/4)`` bytes per
+    row (byte-identical to little-endian packing four per int32), pad 0;
+  * w13 rows [0, N) are the gate projection, rows [N, 2N) the up projection;
+  * SiLU(gate)*up stays fp32 and is quantized directly (no bf16 rounding);
+  * gate_up and down are rounded once to bf16 (nearest even);
+  * padding tokens are unrouted (id -1, weight 0); ids outside [0, E) are
+    unrouted; an expert's rows are ordered by ascending (token, slot);
+  * expert replica choice under EPLB is ``token mod replica_count`` (parity
+    unpinned: the pages do not show ``eplb_map_and_record``'s body; only the
+    invariants it must satisfy are tested).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+GROUP = 128          # quantization group along K (and along N for w2's input)
+FP8_MAX = 448.0      # largest finite e4m3fn value
+
+
+# ---------------------------------------------------------------------------
+# Codecs
+# ---------------------------------------------------------------------------
+
+def _e4m3fn_table() -> np.ndarray:
+    """Value of every e4m3fn byte (OCP 8-bit float, 'fn' variant: exponent
+    bias 7, 3 mantissa bits, subnormals m*2^-9, no infinities, S.1111.111 is
+    NaN).  [STAGE] stores quantized hidden states as ``tl.float8e4nv``,
+    which is this format."""
+    vals = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        exp = (code >> 3) & 0xF
+        man = code & 0x7
+        if exp == 0xF and man == 0x7:
+            vals[code] = np.nan
+        elif exp == 0:
+            vals[code] = sign * man * 2.0 ** -9
+        else:
+            vals[code] = sign * (1.0 + man / 8.0) * 2.0 ** (exp - 7)
+    return vals
+
+
+E4M3_VALUES = _e4m3fn_table()
+_POS_FINITE = E4M3_VALUES[:0x7F]          # codes 0x00..0x7E, increasing
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return E4M3_VALUES[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(v) -> np.ndarray:
+    """fp32 values -> e4m3fn codes: nearest representable value, ties to the
+    even code (even mantissa), magnitudes above 448 saturate to 448, NaN ->
+    NaN; the sign is kept (-0 -> 0x80)."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v).astype(np.float64).ravel()
+    hi = np.searchsorted(_POS_FINITE, a, side="left")      # first value >= a
+    hi_c = np.minimum(hi, 0x7E)
+    lo_c = np.maximum(hi - 1, 0)
+    d_lo = a - _POS_FINITE[lo_c]
+    d_hi = _POS_FINITE[hi_c] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi_c % 2 == 0))
+    code = np.where(pick_hi, hi_c, lo_c)
+    code = np.where(hi == 0, 0, code)                       # a == 0
+    code = np.where(hi > 0x7E, 0x7E, code)                  # saturate
+    code = np.where(np.isnan(a), 0x7F, code).astype(np.uint8)
+    sign = (np.signbit(v.ravel())).astype(np.uint8) << 7
+    return (code | sign).reshape(v.shape)
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> exact fp64."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def bf16_round(x) -> np.ndarray:
+    """fp64 -> bf16 bit patterns, one rounding to nearest even (8 significant
+    bits; the fp32 exponent range, with subnormals below 2^-126)."""
+    x = np.asarray(x, dtype=np.float64)
+    mant, exp = np.frexp(x)                    # x = mant * 2^exp, |mant| in [0.5, 1)
+    normal = np.abs(x) >= 2.0 ** -126
+    q_norm = np.ldexp(np.rint(np.ldexp(mant, 8)), exp - 8)
+    q_sub = np.ldexp(np.rint(np.ldexp(x, 133)), -133)
+    q = np.where(normal, q_norm, q_sub)
+    q = np.where(np.abs(q) > 3.3895313892515355e38, np.copysign(np.inf, x), q)
+    q = np.where(np.isnan(x), np.nan, q)
+    bits = (q.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    return bits
+
+
+def ue8m0_decode(e) -> np.ndarray:
+    """UE8M0 scale byte e -> 2^(e-127)."""
+    return np.ldexp(1.0, np.asarray(e, dtype=np.int64) - 127)
+
+
+# ---------------------------------------------------------------------------
+# O2: per-128-group fp8 quantization  [STAGE, _quantize_fp8_groups]
+# ---------------------------------------------------------------------------
+
+def quantize_groups(x32, ue8m0: bool):
+    """Quantize rows of fp32 values in groups of 128 consecutive columns.
+
+    Per group, in fp32: amax = max|x|, amax = max(amax, 1e-4),
+    s = amax / 448.  UE8M0: the scale is rounded up to a power of two by
+    taking the fp32 exponent field of s plus one when its mantissa field is
+    non-zero, clamped to [1, 254]; the quantizing scale is 2^(e-127) and the
+    stored value is the byte e.  fp32: the quantizing scale is s itself and
+    the stored value is s.  Values are x * (1/scale) converted to e4m3fn.
+
+    Returns (codes uint8 [rows, C], stored scales: uint8 [rows, G] exponents
+    or float32 [rows, G]).
+    """
+    x32 = np.asarray(x32, dtype=np.float32)
+    rows, cols = x32.shape
+    assert cols % GROUP == 0
+    g = x32.reshape(rows, cols // GROUP, GROUP)
+    amax = np.max(np.abs(g), axis=2)
+    amax = np.maximum(amax, np.float32(1.0e-4))
+    s = (amax / np.float32(FP8_MAX)).astype(np.float32)
+    if ue8m0:
+        bits = s.view(np.uint32)
+        e = ((bits >> 23) & 0xFF) + ((bits & 0x7FFFFF) != 0).astype(np.uint32)
+        e = np.minimum(np.maximum(e, 1), 254).astype(np.uint32)
+        qscale = (e << 23).view(np.float32)
+        stored = e.astype(np.uint8)
+    else:
+        qscale = s
+        stored = s
+    recip = (np.float32(1.0) / qscale).astype(np.float32)
+    v = (g * recip[:, :, None]).astype(np.float32)
+    codes = e4m3_encode(v).reshape(rows, cols)
+    return codes, stored
+
+
+def scale_values(stored, ue8m0: bool) -> np.ndarray:
+    """Stored activation scales -> their exact fp64 values."""
+    return ue8m0_decode(stored) if ue8m0 else np.asarray(stored, np.float64)
+
+
+def pack_ue8m0_rows(exps) -> np.ndarray:
+    """[rows, G] exponent bytes -> [rows, 4*ceil(G/4)] bytes, pad bytes 0.
+    Little-endian int32 words with byte j at bits 8j hold the same bytes
+    ([STAGE, _pack_bytes])."""
+    exps = np.asarray(exps, dtype=np.uint8)
+    rows, G = exps.shape
+    out = np.zeros((rows, 4 * ((G + 3) // 4)), dtype=np.uint8)
+    out[:, :G] = exps
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O3: routing repack  [STAGE, _store_topk and _eplb_kernel_args]
+# ---------------------------------------------------------------------------
+
+def repack_topk(topk_ids, topk_weights, is_padding=None, eplb=None,
+                num_physical=None):
+    """Routing ids -> int64 (padding tokens -> -1), weights -> fp32 (padding
+    tokens -> 0).  With expert-replica tables, a logical id in
+    [0, num_logical) becomes ``l2p[id, t mod replica_count[id]]``; when the
+    record flag is set, every mapped id of a token t < num_unpadded adds one
+    to ``expert_load[id]``.
+
+    Returns (ids int64 [T, k], weights fp32 [T, k], load int32 [E] or None).
+    """
+    ids = np.asarray(topk_ids).astype(np.int64).copy()
+    w = np.asarray(topk_weights, dtype=np.float32).copy()
+    T, k = ids.shape
+    if is_padding is not None:
+        pad = np.asarray(is_padding).astype(bool)
+        ids[pad, :] = -1
+        w[pad, :] = 0.0
+    load = None
+    if eplb is not None:
+        l2p = np.asarray(eplb["l2p"], dtype=np.int64)
+        count = np.asarray(eplb["replica_count"], dtype=np.int64)
+        num_logical = l2p.shape[0]
+        record = int(np.asarray(eplb["record"]).ravel()[0]) != 0
+        num_unpadded = int(np.asarray(eplb["num_unpadded"]).ravel()[0])
+        load = np.zeros(num_physical, dtype=np.int32)
+        for t in range(T):
+            for j in range(k):
+                lid = ids[t, j]
+                if 0 <= lid < num_logical:
+                    pid = l2p[lid, t % count[lid]]
+                    ids[t, j] = pid
+                    if record and t < num_unpadded and 0 <= pid < num_physical:
+                        load[pid] += 1
+    return ids, w, load
+
+
+# ---------------------------------------------------------------------------
+# O4: per-expert counts, offsets and the row permutation
+#     [HUM, HummingGroupedExperts.apply: moe_prepare_scatter / moe_permute]
+# ---------------------------------------------------------------------------
+
+def route_layout(ids, E: int, max_tokens: int = 0):
+    """Group routed (token, slot) pairs by expert.
+
+    Rows of expert e are its slots in ascending flat order t*k + j.
+    Contiguous layout: row = offsets[e] + rank.  Batched-masked layout
+    (max_tokens > 0): row = e * max_tokens + rank.
+
+    Returns dict: counts int32 [E], offsets int32 [E+1], row_src int32 [M]
+    (token of each contiguous row), slot_row int32 [T, k] (-1: unrouted).
+    """
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    flat = ids.ravel()
+    valid = (flat >= 0) & (flat < E)
+    key = np.where(valid, flat, E)
+    order = np.argsort(key, kind="stable")
+    counts = np.bincount(flat[valid], minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    M = int(offsets[-1])
+    sorted_slots = order[:M]
+    row_src = (sorted_slots // k).astype(np.int32)
+    slot_row = np.full(T * k, -1, dtype=np.int64)
+    if max_tokens:
+        rank = np.arange(M) - offsets[flat[sorted_slots]]
+        slot_row[sorted_slots] = flat[sorted_slots] * max_tokens + rank
+    else:
+        slot_row[sorted_slots] = np.arange(M)
+    return {
+        "counts": counts,
+        "offsets": offsets.astype(np.int32),
+        "row_src": row_src,
+        "slot_row": slot_row.reshape(T, k).astype(np.int32),
+    }
+
+
+# ---------------------------------------------------------------------------
+# O5 / O7: block-scaled fp8 GEMM   [HUM, humming_forward on w13 and w2 with
+# the (kFp8Static128BlockSym weight, kFp8Dynamic128Sym activation) scheme]
+# ---------------------------------------------------------------------------
+
+def block_scaled_gemm_f64(a_codes, a_scale, w_codes, w_scale) -> np.ndarray:
+    """out[m, n] = sum_b a_scale[m, b] * w_scale[n // 128, b]
+                          * sum_{c in block b} a[m, c] * w[n, c]
+
+    a_codes uint8 [m, C] (e4m3fn), a_scale fp64 [m, C/128],
+    w_codes uint8 [n, C], w_scale fp32 [n/128, C/128].  Result in fp64
+    before the bf16 rounding; the inner block sums are exact.
+    """
+    a = e4m3_decode(a_codes)
+    w = e4m3_decode(w_codes)
+    m, C = a.shape
+    n = w.shape[0]
+    G = C // GROUP
+    a_b = a.reshape(m, G, GROUP).transpose(1, 0, 2)          # [G, m, 128]
+    w_b = w.reshape(n, G, GROUP).transpose(1, 2, 0)          # [G, 128, n]
+    partial = np.matmul(a_b, w_b)                            # [G, m, n], exact
+    ws = np.repeat(np.asarray(w_scale, np.float64), GROUP, axis=0)  # [n, G]
+    out = np.zeros((m, n), dtype=np.float64)
+    for b in range(G):
+        out += partial[b] * np.asarray(a_scale, np.float64)[:, b:b + 1] * ws[None, :, b]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# O6: SiLU(gate) * up, re-quantized  [HUM, process_input('w2', activation=...)]
+# ---------------------------------------------------------------------------
+
+def silu_mul_f32(gate_up_bits, N: int) -> np.ndarray:
+    """bf16 [rows, 2N] -> fp32 h = silu(g) * u with g = columns [0, N) and
+    u = columns [N, 2N); evaluated in fp64, rounded once to fp32."""
+    gu = bf16_to_f64(gate_up_bits)
+    g, u = gu[:, :N], gu[:, N:]
+    h = g / (1.0 + np.exp(-g)) * u
+    return h.astype(np.float32)
+
+
+def act_requant(gate_up_bits, N: int, ue8m0: bool):
+    return quantize_groups(silu_mul_f32(gate_up_bits, N), ue8m0)
+
+
+# ---------------------------------------------------------------------------
+# O8: top-k weighted reduce  [HUM, HummingGroupedExperts.apply: moe_unpermute;
+# HummingIndexedExperts.apply: moe_fused_mul_sum; router weight applied after
+# w2 since apply_router_weight_on_input is False]
+# ---------------------------------------------------------------------------
+
+def topk_reduce(down_bits, slot_row, weights) -> np.ndarray:
+    """out[t] = bf16(sum over slots j with slot_row[t, j] >= 0, ascending j,
+    of weights[t, j] * down[slot_row[t, j]]), accumulated in fp64."""
+    slot_row = np.asarray(slot_row, dtype=np.int64)
+    T, k = slot_row.shape
+    down = bf16_to_f64(down_bits)
+    acc = np.zeros((T, down.shape[1]), dtype=np.float64)
+    for j in range(k):
+        r = slot_row[:, j]
+        ok = r >= 0
+        acc[ok] += np.asarray(weights, np.float64)[ok, j:j + 1] * down[r[ok]]
+    return bf16_round(acc)
+
+
+# ---------------------------------------------------------------------------
+# The whole layer
+# ---------------------------------------------------------------------------
+
+def _np(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):
+        x = x.detach().to("cpu")
+        if str(x.dtype) == "torch.bfloat16":
+            return x.view(__import__("torch").int16).numpy().view(np.uint16)
+        return x.numpy()
+    return np.asarray(x)
+
+
+def host_inputs(inp: dict) -> dict:
+    """Host numpy copies of a generator input dict (bf16 as uint16 bits)."""
+    out = {}
+    for key, val in inp.items():
+        if key == "eplb" and val is not None:
+            out[key] = {k2: _np(v2) for k2, v2 in val.items()}
+        elif key == "cfg":
+            out[key] = val
+        else:
+            out[key] = _np(val)
+    return out
+
+
+def stage(h: dict):
+    """Steps 1-2: quantize the hidden rows that will be read, repack the
+    routing and build the expert layout."""
+    cfg = h["cfg"]
+    ue8m0 = cfg.act_quant == "ue8m0"
+    ids, w, load = repack_topk(h["topk_ids"], h["topk_weights"], h["is_padding"],
+                               h["eplb"], num_physical=cfg.E)
+    batched = cfg.layout == "batched"
+    lay = route_layout(ids, cfg.E, cfg.max_tokens if batched else 0)
+    hid = np.asarray(h["hidden"]).reshape(-1, cfg.K)
+    if batched:
+        # only rows below each slab's count exist; the rest are never read
+        valid_rows = np.concatenate(
+            [np.arange(e * cfg.max_tokens, e * cfg.max_tokens + int(c))
+             for e, c in enumerate(np.asarray(h["expert_num_tokens"]))]
+            + [np.zeros(0, dtype=np.int64)]).astype(np.int64)
+    else:
+        valid_rows = np.arange(hid.shape[0])
+    G = cfg.K // GROUP
+    x_q = np.zeros(hid.shape, dtype=np.uint8)
+    x_sf = np.zeros((hid.shape[0], G), dtype=np.uint8 if ue8m0 else np.float32)
+    x = bf16_to_f64(hid[valid_rows]).astype(np.float32)
+    x_q[valid_rows], x_sf[valid_rows] = quantize_groups(x, ue8m0)
+    return {"ids": ids, "weights": w, "load": load, "x_q": x_q, "x_sf": x_sf,
+            **lay}
+
+
+def forward(h: dict) -> dict:
+    """The full layer on every row; returns every intermediate.
+
+    Rows: contiguous layout -> M = offsets[E] permuted rows; batched layout
+    -> E * max_tokens rows of which only the first counts[e] of each slab
+    are computed (the rest stay 0 here and are never compared)."""
+    cfg = h["cfg"]
+    ue8m0 = cfg.act_quant == "ue8m0"
+    st = stage(h)
+    E, N, K = cfg.E, cfg.N, cfg.K
+    batched = cfg.layout == "batched"
+    counts = st["counts"]
+    if batched:
+        given = np.asarray(h["expert_num_tokens"]).astype(np.int32)
+        assert np.array_equal(given, counts), "staged counts disagree with routing"
+        rows_total = E * cfg.max_tokens
+    else:
+        rows_total = int(st["offsets"][-1])
+    gate_up = np.zeros((rows_total, 2 * N), dtype=np.uint16)
+    a2_q = np.zeros((rows_total, N), dtype=np.uint8)
+    a2_sf = np.zeros((rows_total, N // GROUP),
+                     dtype=np.uint8 if ue8m0 else np.float32)
+    down = np.zeros((rows_total, K), dtype=np.uint16)
+    xs = scale_values(st["x_sf"], ue8m0)
+    for e in range(E):
+        n_e = int(counts[e])
+        if n_e == 0:
+            continue
+        if batched:
+            rows = np.arange(e * cfg.max_tokens, e * cfg.max_tokens + n_e)
+            a_rows = rows
+        else:
+            lo = int(st["offsets"][e])
+            rows = np.arange(lo, lo + n_e)
+            a_rows = st["row_src"][rows]
+        gu = block_scaled_gemm_f64(st["x_q"][a_rows], xs[a_rows],
+                                   h["w13"][e], h["w13_sf"][e])
+        gate_up[rows] = bf16_round(gu)
+        q2, s2 = act_requant(gate_up[rows], N, ue8m0)
+        a2_q[rows], a2_sf[rows] = q2, s2
+        dn = block_scaled_gemm_f64(q2, scale_values(s2, ue8m0),
+                                   h["w2"][e], h["w2_sf"][e])
+        down[rows] = bf16_round(dn)
+    out = topk_reduce(down, st["slot_row"], st["weights"])
+    return {**st, "gate_up": gate_up, "a2_q": a2_q, "a2_sf": a2_sf,
+            "down": down, "out": out}
+
+
+def forward_tokens(h: dict, tokens, st: dict | None = None) -> dict:
+    """The layer for a few tokens only (for full-size workloads).
+
+    Computes the routing layout for all tokens (cheap), then for each chosen
+    token t and each of its routed slots the rows gate_up, a2 and down at the
+    row the layout gives, and the token's output row.  Returns
+    ``{"stage": st, "rows": {row: {...}}, "out": {t: bf16 bits [K]}}``.
+    """
+    cfg = h["cfg"]
+    ue8m0 = cfg.act_quant == "ue8m0"
+    N, K = cfg.N, cfg.K
+    if st is None:
+        st = stage_routing_only(h)
+    rows_info = {}
+    by_expert = {}
+    for t in tokens:
+        for j in range(cfg.top_k):
+            r = int(st["slot_row"][t, j])
+            if r >= 0:
+                by_expert.setdefault(int(st["ids"][t, j]), []).append((t, j, r))
+    hid = h["hidden"].reshape(-1, K)
+    for e, lst in sorted(by_expert.items()):
+        w13, w13s, w2, w2s = h["w13"][e], h["w13_sf"][e], h["w2"][e], h["w2_sf"][e]
+        if hasattr(w13, "detach"):
+            w13, w13s, w2, w2s = _np(w13), _np(w13s), _np(w2), _np(w2s)
+        for (t, j, r) in lst:
+            a_row = r if cfg.layout == "batched" else t
+            x = bf16_to_f64(hid[a_row:a_row + 1]).astype(np.float32)
+            xq, xsf = quantize_groups(x, ue8m0)
+            gu = bf16_round(block_scaled_gemm_f64(xq, scale_values(xsf, ue8m0),
+                                                  w13, w13s))
+            q2, s2 = act_requant(gu, N, ue8m0)
+            dn = bf16_round(block_scaled_gemm_f64(q2, scale_values(s2, ue8m0),
+                                                  w2, w2s))
+            rows_info[r] = {"token": t, "slot": j, "expert": e, "x_q": xq[0],
+                            "x_sf": xsf[0], "gate_up": gu[0], "a2_q": q2[0],
+                            "a2_sf": s2[0], "down": dn[0]}
+    outs = {}
+    for t in tokens:
+        acc = np.zeros(K, dtype=np.float64)
+        for j in range(cfg.top_k):
+            r = int(st["slot_row"][t, j])
+            if r >= 0:
+                acc += np.float64(st["weights"][t, j]) * bf16_to_f64(rows_info[r]["down"])
+        outs[t] = bf16_round(acc)
+    return {"stage": st, "rows": rows_info, "out": outs}
+
+
+def stage_routing_only(h: dict) -> dict:
+    """Routing repack and layout without quantizing any hidden row."""
+    cfg = h["cfg"]
+    ids, w, load = repack_topk(h["topk_ids"], h["topk_weights"], h["is_padding"],
+                               h["eplb"], num_physical=cfg.E)
+    lay = route_layout(ids, cfg.E, cfg.max_tokens if cfg.layout == "batched" else 0)
+    return {"ids": ids, "weights": w, "load": load, **lay}

@@ -1,0 +1,497 @@
+"""Pins of the CPU oracle to things other than itself.
+
+Each test checks an oracle function against exact rational arithmetic, a
+closed form, a library routine, brute force on tiny inputs, or an invariant
+the vLLM pages fix ("vllm.model_executor.layers.fused_moe.prepare_megamoe":
+``_quantize_fp8_groups`` / ``_store_topk``; "...experts.fused_humming_moe":
+the experts' ``apply`` methods).  No GPU is needed.
+"""
+import bisect
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+from oracle import moe_oracle as O
+
+
+# --------------------------------------------------------------------------
+# helpers written from scratch for the pins (exact rationals)
+# --------------------------------------------------------------------------
+
+def _frac_e4m3_values():
+    """The finite non-negative e4m3fn values as Fractions, code order."""
+    vals = []
+    for code in range(0x7F):
+        e, m = code >> 3, code & 7
+        if e == 0:
+            vals.append(Fraction(m, 512))
+        else:
+            vals.append(Fraction(8 + m, 8) * Fraction(2) ** (e - 7))
+    return vals
+
+
+_FV = _frac_e4m3_values()
+
+
+def _frac_encode(x: Fraction, negative: bool) -> int:
+    """Nearest e4m3fn code by exact comparison; ties -> even code; above the
+    largest finite value -> saturate."""
+    a = abs(x)
+    i = bisect.bisect_left(_FV, a)
+    if i == 0:
+        code = 0
+    elif i >= len(_FV):
+        code = 0x7E
+    else:
+        lo, hi = i - 1, i
+        dl, dh = a - _FV[lo], _FV[hi] - a
+        if dl < dh:
+            code = lo
+        elif dh < dl:
+            code = hi
+        else:
+            code = lo if lo % 2 == 0 else hi
+    return code | (0x80 if negative else 0)
+
+
+def _frac_bf16(x: Fraction) -> Fraction:
+    """Nearest bf16 value (8 significant bits), ties to even, normal range."""
+    if x == 0:
+        return Fraction(0)
+    sgn = -1 if x < 0 else 1
+    a = abs(x)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = Fraction(2) ** (e - 7)
+    n = a / q
+    fl = math.floor(n)
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sgn * fl * q
+
+
+def _ceil_log2(r: Fraction) -> int:
+    """Smallest integer j with 2^j >= r (r > 0), exactly."""
+    j = math.floor(math.log2(r.numerator) - math.log2(r.denominator)) - 2
+    while Fraction(2) ** j < r:
+        j += 1
+    while Fraction(2) ** (j - 1) >= r:
+        j -= 1
+    return j
+
+
+# --------------------------------------------------------------------------
+# e4m3fn codec
+# --------------------------------------------------------------------------
+
+def test_e4m3_table_spec_points():
+    V = O.E4M3_VALUES
+    assert V[0x7E] == 448.0
+    assert V[0x01] == 2.0 ** -9
+    assert V[0x07] == 7 * 2.0 ** -9
+    assert V[0x08] == 2.0 ** -6
+    assert V[0x38] == 1.0
+    assert V[0x00] == 0.0 and not np.signbit(V[0x00])
+    assert V[0x80] == 0.0 and np.signbit(V[0x80])
+    assert np.isnan(V[0x7F]) and np.isnan(V[0xFF])
+    assert np.all(np.diff(V[:0x7F]) > 0)
+    assert np.array_equal(V[0x80:0xFF], -V[0x00:0x7F])
+    assert np.isfinite(V).sum() == 254
+
+
+def test_e4m3_table_matches_torch_decode():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    fin = np.isfinite(ref)
+    assert np.array_equal(fin, np.isfinite(O.E4M3_VALUES))
+    assert np.array_equal(ref[fin], O.E4M3_VALUES[fin])
+
+
+def test_e4m3_encode_roundtrip_all_codes():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    vals = O.E4M3_VALUES[codes].astype(np.float32)
+    assert np.array_equal(O.e4m3_encode(vals), codes)
+
+
+def _midpoints_and_neighbours():
+    v = O.E4M3_VALUES[:0x7F]
+    mids = ((v[:-1] + v[1:]) / 2).astype(np.float32)        # exact in fp32
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(0))
+    return np.concatenate([mids, up, dn])
+
+
+def test_e4m3_encode_exact_rationals():
+    rng = np.random.default_rng(11)
+    logs = rng.uniform(-14, 9.2, 4000)
+    xs = (rng.choice([-1, 1], 4000) * np.exp2(logs)).astype(np.float32)
+    xs = np.concatenate([xs, _midpoints_and_neighbours(),
+                         np.float32([448, 456, 460, 463.99, 464, 465, 1e6,
+                                     2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -11, 0.0,
+                                     -0.0])])
+    got = O.e4m3_encode(xs)
+    want = np.array([_frac_encode(Fraction(float(x)), bool(np.signbit(x)))
+                     for x in xs], np.uint8)
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_encode_matches_torch_cast_in_range():
+    rng = np.random.default_rng(12)
+    xs = (rng.standard_normal(200000) * np.exp2(rng.uniform(-12, 8, 200000)))
+    xs = np.clip(xs, -448, 448).astype(np.float32)
+    xs = np.concatenate([xs, _midpoints_and_neighbours()])
+    ref = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.e4m3_encode(xs), ref)
+
+
+def test_e4m3_encode_saturates_and_nan():
+    xs = np.float32([449.0, 1e30, np.inf, -1e30, -np.inf, np.nan])
+    got = O.e4m3_encode(xs)
+    assert list(got[:5]) == [0x7E, 0x7E, 0x7E, 0xFE, 0xFE]
+    assert got[5] & 0x7F == 0x7F
+
+
+# --------------------------------------------------------------------------
+# bf16 rounding
+# --------------------------------------------------------------------------
+
+def test_bf16_round_exact_rationals():
+    rng = np.random.default_rng(13)
+    xs = rng.standard_normal(3000) * np.exp2(rng.uniform(-30, 30, 3000))
+    # exact ties and their neighbours: 8-bit values + half a unit
+    base = rng.integers(128, 256, 500) * 2.0 ** rng.integers(-20, 20, 500)
+    ties = base * (1 + 1 / 512)        # exactly half a bf16 unit above base
+    xs = np.concatenate([xs, ties, np.nextafter(ties, 0), np.nextafter(ties, np.inf),
+                         -ties])
+    got = O.bf16_to_f64(O.bf16_round(xs))
+    want = np.array([float(_frac_bf16(Fraction(float(x)))) for x in xs])
+    assert np.array_equal(got, want)
+
+
+def test_bf16_round_matches_torch_on_fp32_inputs():
+    rng = np.random.default_rng(14)
+    xs = (rng.standard_normal(100000) * np.exp2(rng.uniform(-60, 60, 100000)))
+    xs = xs.astype(np.float32)
+    ref = torch.from_numpy(xs).to(torch.bfloat16).view(torch.int16).numpy()
+    assert np.array_equal(O.bf16_round(xs.astype(np.float64)), ref.view(np.uint16))
+
+
+# --------------------------------------------------------------------------
+# group quantizer  [prepare_megamoe, _quantize_fp8_groups]
+# --------------------------------------------------------------------------
+
+def _all_finite_bf16():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = O.bf16_to_f64(bits)
+    keep = np.isfinite(v)
+    return bits[keep], v[keep]
+
+
+def test_ue8m0_exponent_closed_form_all_bf16():
+    """e = 127 + ceil(log2(max(amax, 1e-4) / 448)), clamped to [1, 254],
+    checked in exact rationals for every finite bf16 amax."""
+    _, v = _all_finite_bf16()
+    x = np.zeros((v.size, 128), np.float32)
+    x[:, 0] = v
+    codes, e = O.quantize_groups(x, ue8m0=True)
+    floor = Fraction(float(np.float32(1e-4)))
+    want = []
+    for a in np.abs(v):
+        A = max(Fraction(float(a)), floor)
+        want.append(min(max(127 + _ceil_log2(A / 448), 1), 254))
+    assert np.array_equal(e[:, 0].astype(int), np.array(want))
+    # the element itself: exact power-of-two scaling, then nearest e4m3fn
+    idx = np.random.default_rng(15).choice(v.size, 3000, replace=False)
+    for i in idx:
+        val = Fraction(float(v[i])) / Fraction(2) ** (int(e[i, 0]) - 127)
+        assert codes[i, 0] == _frac_encode(val, bool(np.signbit(v[i])))
+    assert np.all(codes[:, 1:] == 0)
+
+
+def test_ue8m0_group_max_lands_in_top_binade():
+    rng = np.random.default_rng(16)
+    x = (rng.standard_normal((500, 512)) * np.exp2(rng.uniform(-10, 10, (500, 1))))
+    x = x.astype(np.float32)
+    codes, e = O.quantize_groups(x, ue8m0=True)
+    dec = np.abs(O.e4m3_decode(codes)).reshape(500, 4, 128)
+    gmax = dec.max(axis=2)
+    amax = np.abs(x).reshape(500, 4, 128).max(axis=2)
+    ok = amax >= 1e-4
+    assert np.all(gmax[ok] >= 224) and np.all(gmax <= 448)
+    assert np.all(np.abs(O.e4m3_decode(codes)) <= 448)
+
+
+def test_quant_special_groups():
+    x = np.zeros((3, 128), np.float32)
+    x[1, 7] = 448 * 2.0 ** -5
+    x[2, 3] = -448 * 2.0 ** 6
+    for ue8m0 in (True, False):
+        codes, s = O.quantize_groups(x, ue8m0)
+        assert np.all(codes[0] == 0)
+        assert codes[1, 7] == 0x7E and codes[2, 3] == 0xFE
+        if ue8m0:
+            assert int(s[0, 0]) == 105
+            assert int(s[1, 0]) == 127 - 5 and int(s[2, 0]) == 127 + 6
+        else:
+            assert s[1, 0] == np.float32(2.0 ** -5) and s[2, 0] == np.float32(2.0 ** 6)
+
+
+def test_fp32_scale_mode_properties():
+    rng = np.random.default_rng(17)
+    x = (rng.standard_normal((400, 256)) * np.exp2(rng.uniform(-8, 8, (400, 1))))
+    x = x.astype(np.float32)
+    codes, s = O.quantize_groups(x, ue8m0=False)
+    g = x.reshape(400, 2, 128)
+    amax = np.abs(g).max(axis=2)
+    # the scale is amax/448 in fp32 to within one rounding
+    assert np.all(np.abs(s.astype(np.float64) * 448 - amax) <= amax * 2.0 ** -23)
+    # the element of largest magnitude lands on +-448
+    arg = np.abs(g).argmax(axis=2)
+    cg = codes.reshape(400, 2, 128)
+    top = np.take_along_axis(cg, arg[:, :, None], axis=2)[:, :, 0]
+    assert np.all((top & 0x7F) == 0x7E)
+    # dequantized values are within half an e4m3 step (relative 2^-4) of x
+    deq = O.e4m3_decode(codes).reshape(400, 2, 128) * s[:, :, None]
+    err = np.abs(deq - g)
+    assert np.all(err <= np.maximum(np.abs(g) * 2.0 ** -4, s[:, :, None] * 2.0 ** -10) * 1.0001)
+
+
+def test_pack_bytes_matches_int32_little_endian():
+    e = np.arange(1, 11, dtype=np.uint8).reshape(2, 5)
+    packed = O.pack_ue8m0_rows(e)
+    assert packed.shape == (2, 8)
+    words = packed.view(np.int32)
+    want0 = 1 | 2 << 8 | 3 << 16 | 4 << 24
+    assert words[0, 0] == want0 and words[0, 1] == 5
+    assert np.all(packed[:, 5:] == 0)
+
+
+# --------------------------------------------------------------------------
+# routing repack and layout  [prepare_megamoe, _store_topk; fused_humming_moe,
+# moe_prepare_scatter / moe_permute in HummingGroupedExperts.apply]
+# --------------------------------------------------------------------------
+
+def _brute_layout(ids, E, max_tokens=0):
+    T, k = ids.shape
+    lists = [[] for _ in range(E)]
+    for t in range(T):
+        for j in range(k):
+            if 0 <= ids[t, j] < E:
+                lists[ids[t, j]].append((t, j))
+    counts = [len(l) for l in lists]
+    offs = [0]
+    for c in counts:
+        offs.append(offs[-1] + c)
+    row_src, slot_row = [], -np.ones((T, k), np.int64)
+    for e in range(E):
+        for rank, (t, j) in enumerate(lists[e]):
+            row_src.append(t)
+            slot_row[t, j] = e * max_tokens + rank if max_tokens else offs[e] + rank
+    return counts, offs, row_src, slot_row
+
+
+@pytest.mark.parametrize("max_tokens", [0, 40])
+def test_route_layout_brute_force(max_tokens):
+    rng = np.random.default_rng(18)
+    for trial in range(20):
+        T, k, E = rng.integers(1, 30), rng.integers(1, 5), rng.integers(1, 9)
+        ids = rng.integers(-2, E + 2, (T, k))
+        lay = O.route_layout(ids, E, max_tokens)
+        c, o, rs, sr = _brute_layout(ids, E, max_tokens)
+        assert list(lay["counts"]) == c and list(lay["offsets"]) == o
+        assert list(lay["row_src"]) == rs
+        assert np.array_equal(lay["slot_row"], sr)
+
+
+def test_repack_padding_and_sum_of_counts():
+    rng = np.random.default_rng(19)
+    T, k, E = 300, 4, 7
+    ids = rng.integers(0, E, (T, k)).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    pad = (rng.random(T) < 0.1).astype(np.uint8)
+    out_ids, out_w, _ = O.repack_topk(ids, w, pad)
+    assert out_ids.dtype == np.int64 and out_w.dtype == np.float32
+    assert np.all(out_ids[pad == 1] == -1) and np.all(out_w[pad == 1] == 0)
+    assert np.array_equal(out_ids[pad == 0], ids[pad == 0])
+    lay = O.route_layout(out_ids, E)
+    assert lay["counts"].sum() == (pad == 0).sum() * k
+    assert np.all(lay["slot_row"][pad == 1] == -1)
+    # inverse maps
+    for t in range(T):
+        for j in range(k):
+            r = lay["slot_row"][t, j]
+            if r >= 0:
+                assert lay["row_src"][r] == t
+
+
+def test_eplb_map_invariants():
+    rng = np.random.default_rng(20)
+    El, extra, T, k = 12, 4, 200, 3
+    l2p = -np.ones((El, 2), np.int32)
+    l2p[:, 0] = np.arange(El)
+    count = np.ones(El, np.int32)
+    rep = rng.choice(El, extra, replace=False)
+    for i, le in enumerate(rep):
+        l2p[le, 1] = El + i
+        count[le] = 2
+    ids = rng.integers(0, El, (T, k)).astype(np.int32)
+    pad = np.zeros(T, np.uint8)
+    pad[:10] = 1
+    eplb = {"l2p": l2p, "replica_count": count, "record": np.array([1]),
+            "num_unpadded": np.array([150])}
+    out, _, load = O.repack_topk(ids, np.ones((T, k), np.float32), pad, eplb,
+                                 num_physical=El + extra)
+    back = np.full(El + extra, -1)
+    for le in range(El):
+        for r in range(count[le]):
+            back[l2p[le, r]] = le
+    routed = out >= 0
+    assert np.array_equal(back[out[routed]], ids[routed])      # logical(phys(id)) == id
+    assert np.all(out[pad == 1] == -1)
+    assert load.sum() == routed[:150].sum()
+    want = np.bincount(out[:150][routed[:150]], minlength=El + extra)
+    assert np.array_equal(load, want)
+    off = O.repack_topk(ids, np.ones((T, k), np.float32), pad,
+                        {**eplb, "record": np.array([0])}, num_physical=El + extra)[2]
+    assert off.sum() == 0
+
+
+# --------------------------------------------------------------------------
+# block-scaled GEMM  [fused_humming_moe, humming_forward with 128x128 fp32
+# weight block scales and per-128 activation group scales]
+# --------------------------------------------------------------------------
+
+def _finite_codes(rng, shape):
+    c = rng.integers(0, 256, shape).astype(np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x38
+    return c
+
+
+def test_block_gemm_equals_dense_dequantized_matmul():
+    rng = np.random.default_rng(21)
+    m, n, C = 37, 256, 384
+    a = _finite_codes(rng, (m, C))
+    w = _finite_codes(rng, (n, C))
+    sa = np.exp2(rng.integers(-10, 4, (m, C // 128))).astype(np.float64)
+    sw = rng.uniform(0.001, 0.01, (n // 128, C // 128)).astype(np.float32)
+    got = O.block_scaled_gemm_f64(a, sa, w, sw)
+    A = O.e4m3_decode(a) * np.repeat(sa, 128, axis=1)
+    W = O.e4m3_decode(w) * np.repeat(np.repeat(sw.astype(np.float64), 128, 0), 128, 1)
+    want = A @ W.T
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def test_block_gemm_identity_weights():
+    rng = np.random.default_rng(22)
+    m, C = 20, 256
+    a = _finite_codes(rng, (m, C))
+    sa = np.exp2(rng.integers(-6, 2, (m, 2))).astype(np.float64)
+    w = np.zeros((C, C), np.uint8)
+    w[np.arange(C), np.arange(C)] = 0x38
+    sw = np.ones((2, 2), np.float32)
+    got = O.block_scaled_gemm_f64(a, sa, w, sw)
+    assert np.array_equal(got, O.e4m3_decode(a) * np.repeat(sa, 128, axis=1))
+
+
+# --------------------------------------------------------------------------
+# SiLU(gate) * up and the reduce
+# --------------------------------------------------------------------------
+
+def test_silu_mul_matches_torch_and_gate_up_order():
+    rng = np.random.default_rng(23)
+    N = 256
+    gu = rng.standard_normal((50, 2 * N)) * 3
+    bits = O.bf16_round(gu)
+    g64 = torch.from_numpy(O.bf16_to_f64(bits))
+    ref = (torch.nn.functional.silu(g64[:, :N]) * g64[:, N:]).to(torch.float32).numpy()
+    got = O.silu_mul_f32(bits, N)
+    ulp = np.spacing(np.abs(ref).astype(np.float32))
+    assert np.all(np.abs(got - ref) <= ulp)
+    z = bits.copy()
+    z[:, :N] = 0                       # gate = 0 -> silu(0) = 0 whatever up is
+    assert np.all(O.silu_mul_f32(z, N) == 0)
+
+
+def test_reduce_special_cases():
+    rng = np.random.default_rng(24)
+    T, K = 9, 256
+    down = O.bf16_round(rng.standard_normal((T, K)))
+    slot = np.arange(T).reshape(T, 1)
+    assert np.array_equal(O.topk_reduce(down, slot, np.ones((T, 1), np.float32)), down)
+    none = -np.ones((T, 3), np.int64)
+    assert np.all(O.topk_reduce(down, none, np.ones((T, 3), np.float32)) == 0)
+    slot2 = rng.integers(0, T, (T, 3))
+    w = rng.random((T, 3)).astype(np.float32)
+    want = np.einsum("tj,tjc->tc", w.astype(np.float64), O.bf16_to_f64(down)[slot2])
+    assert np.array_equal(O.topk_reduce(down, slot2, w), O.bf16_round(want))
+
+
+# --------------------------------------------------------------------------
+# the whole layer
+# --------------------------------------------------------------------------
+
+def _dense_ffn(h, st):
+    """Unquantized activations, dequantized weights, fp64: the layer the
+    quantized one approximates."""
+    cfg = h["cfg"]
+    N = cfg.N
+    x = O.bf16_to_f64(h["tokens"])
+    out = np.zeros((cfg.T, cfg.K))
+    for t in range(cfg.T):
+        for j in range(cfg.top_k):
+            e = st["ids"][t, j]
+            if e < 0:
+                continue
+            W13 = O.e4m3_decode(h["w13"][e]) * np.repeat(np.repeat(
+                h["w13_sf"][e].astype(np.float64), 128, 0), 128, 1)
+            W2 = O.e4m3_decode(h["w2"][e]) * np.repeat(np.repeat(
+                h["w2_sf"][e].astype(np.float64), 128, 0), 128, 1)
+            gu = W13 @ x[t]
+            act = gu[:N] / (1 + np.exp(-gu[:N])) * gu[N:]
+            out[t] += st["weights"][t, j] * (W2 @ act)
+    return out
+
+
+def test_tiny_layer_tracks_unquantized_ffn():
+    h = O.host_inputs(moe_synth.make_inputs(moe_synth.CONFIGS["tiny"]))
+    r = O.forward(h)
+    ref = _dense_ffn(h, r)
+    got = O.bf16_to_f64(r["out"])
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert 1e-3 < rel < 0.08, rel
+
+
+def test_layouts_and_padding_agree():
+    base = dict(T=40, E=3, top_k=2, K=256, N=256, seed=9)
+    hc = O.host_inputs(moe_synth.make_inputs(moe_synth.custom(**base)))
+    hb = O.host_inputs(moe_synth.make_inputs(
+        moe_synth.custom(**base, layout="batched", max_tokens=64)))
+    rc, rb = O.forward(hc), O.forward(hb)
+    assert np.array_equal(rc["out"], rb["out"])
+    hp = O.host_inputs(moe_synth.make_inputs(moe_synth.custom(**base, pad_frac=0.2)))
+    rp = O.forward(hp)
+    pad = hp["is_padding"].astype(bool)
+    assert np.all(rp["out"][pad] == 0)
+    assert np.array_equal(rp["out"][~pad], rc["out"][~pad])
+
+
+def test_forward_tokens_matches_forward():
+    cfg = moe_synth.custom(T=30, E=5, top_k=3, K=256, N=384, seed=10,
+                           act_quant="fp32", num_logical=4, pad_frac=0.1)
+    h = O.host_inputs(moe_synth.make_inputs(cfg))
+    full = O.forward(h)
+    part = O.forward_tokens(h, [0, 7, 29])
+    for t in (0, 7, 29):
+        assert np.array_equal(part["out"][t], full["out"][t])
+    for r, info in part["rows"].items():
+        assert np.array_equal(info["gate_up"], full["gate_up"][r])
+        assert np.array_equal(info["a2_q"], full["a2_q"][r])
+        assert np.array_equal(info["down"], full["down"][r])
