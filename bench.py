@@ -1,0 +1,242 @@
+"""Benchmark of the fp8 block-quantized MoE expert layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config dsv3_prefill]
+
+One step = one moe_forward over one batch (stage + routing, w13 GEMM, SiLU
+re-quantization, w2 GEMM, top-k reduce), inputs resident in HBM.  Prints one
+JSON line: layer tokens/s, grouped-GEMM TFLOP/s against the fp8 dense MFMA
+peak, per-kernel times, the roofline of the dominant kernel (the w13 grouped
+GEMM) and the CPU oracle timed on a bounded sample.  Diagnostics go to
+stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fp8_block_quantized_group_amd as moe  # noqa: E402
+import moe_synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, TFLOP/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="dsv3_prefill", choices=list(moe_synth.CONFIGS))
+    ap.add_argument("--kernel-iters", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+class KernelTimer:
+    """HIP events on the stream the library launches on (torch's current
+    stream, passed to every C call)."""
+
+    def __init__(self):
+        self.stream = torch.cuda.current_stream()
+
+    def time(self, fn, iters, flush=None):
+        times = []
+        for _ in range(iters):
+            if flush is not None:
+                flush()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(self.stream)
+            fn()
+            b.record(self.stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b))
+        return float(np.mean(times)), float(np.min(times))
+
+
+def algorithmic(cfg, counts, T_valid):
+    """Minimum HBM bytes and flops of each step (one launch each)."""
+    K, N, k = cfg.K, cfg.N, cfg.top_k
+    GK, GN = K // 128, N // 128
+    M = int(counts.sum())
+    touched = int((counts > 0).sum())
+    ue = cfg.act_quant == "ue8m0"
+    sfb = 1 if ue else 4
+    rows_in = int(counts.sum()) if cfg.layout == "batched" else cfg.T
+    a = {}
+    a["stage"] = rows_in * K * 2 + rows_in * K + rows_in * GK * sfb
+    a["w13_bytes"] = (touched * (2 * N * K + (2 * N // 128) * GK * 4)
+                      + T_valid * (K + GK * sfb) + M * 2 * N * 2)
+    a["w13_flops"] = 2.0 * M * 2 * N * K
+    a["act"] = M * 2 * N * 2 + M * N + M * GN * sfb
+    a["w2_bytes"] = (touched * (K * N + (K // 128) * GN * 4) + M * (N + GN * sfb) + M * K * 2)
+    a["w2_flops"] = 2.0 * M * N * K
+    a["reduce"] = M * K * 2 + cfg.T * K * 2 + cfg.T * k * 8
+    return a
+
+
+def cpu_baseline(cfg, inp, st_dev, budget_s):
+    """The CPU oracle, as it stands, on a bounded sample of tokens."""
+    from oracle import moe_oracle as O
+    from threadpoolctl import threadpool_info
+    h = {}
+    for key, v in inp.items():
+        if key in ("w13", "w13_sf", "w2", "w2_sf") or key == "cfg":
+            h[key] = v
+        elif key == "eplb" and v is not None:
+            h[key] = {k2: O._np(v2) for k2, v2 in v.items()}
+        else:
+            h[key] = O._np(v)
+    t0 = time.perf_counter()
+    st = O.stage_routing_only(h)
+    routed = np.flatnonzero((st["slot_row"] >= 0).any(axis=1))
+    rng = np.random.default_rng(1234)
+    order = rng.permutation(routed)
+    done = 0
+    t_route = time.perf_counter() - t0
+    t1 = time.perf_counter()
+    while done < len(order) and time.perf_counter() - t1 < budget_s:
+        O.forward_tokens(h, [int(order[done])], st)
+        done += 1
+    dt = time.perf_counter() - t1
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": done / dt if dt > 0 else 0.0, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{done} routed tokens of {cfg.name} through the whole layer one by one "
+                       f"(numpy fp64), after the full routing layout ({t_route:.2f} s); "
+                       f"{dt:.1f} s of CPU work; host has {os.cpu_count()} cpus")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the expert layer "
+              "is not sharded across GPUs here.", file=sys.stderr)
+        sys.exit(2)
+    cfg = moe_synth.CONFIGS[args.config]
+    torch.cuda.set_device(0)
+    log(f"[bench] generating {cfg.name} inputs on the GPU")
+    inp = moe_synth.make_inputs(cfg, "cuda")
+    p = moe.Problem.from_config(cfg)
+    layer = moe.MoeLayer(p, inp["w13"], inp["w13_sf"], inp["w2"], inp["w2_sf"])
+    out = torch.empty((cfg.T, cfg.K), dtype=torch.bfloat16, device="cuda")
+
+    def step():
+        if inp["eplb"] is not None:
+            inp["eplb"]["expert_load"].zero_()
+        layer(inp["hidden"], inp["topk_ids"], inp["topk_weights"], out, inp["is_padding"],
+              inp["expert_num_tokens"], inp["eplb"])
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / max(args.steps, 1)
+
+    # ---- per-kernel timing through the separate entry points -------------
+    s = moe.sizes(p)
+    bufs = moe.alloc_stage_outputs(p)
+    ue = p.act_quant == moe.Q_FP8_UE8M0
+    gate_up = torch.empty((s["expert_rows"], 2 * cfg.N), dtype=torch.bfloat16, device="cuda")
+    a2_q = torch.empty((s["expert_rows"], cfg.N), dtype=torch.uint8, device="cuda")
+    a2_sf = torch.empty((s["expert_rows"], s["a2_sf_row"]),
+                        dtype=torch.uint8 if ue else torch.float32, device="cuda")
+    down = torch.empty((s["expert_rows"], cfg.K), dtype=torch.bfloat16, device="cuda")
+    flush_buf = torch.empty(1 << 28, dtype=torch.int32, device="cuda")   # 1 GiB > MALL
+
+    def flush():
+        flush_buf.add_(1)
+
+    def do_stage():
+        if inp["eplb"] is not None:
+            inp["eplb"]["expert_load"].zero_()
+        moe.stage(p, inp["hidden"], inp["topk_ids"], inp["topk_weights"], bufs,
+                  inp["is_padding"], inp["expert_num_tokens"], inp["eplb"])
+
+    kt = KernelTimer()
+    it = args.kernel_iters
+    t_stage = kt.time(do_stage, it, flush)
+    t_w13 = kt.time(lambda: moe.grouped_gemm_w13(p, bufs["x_q"], bufs["x_sf"], bufs,
+                                                 inp["w13"], inp["w13_sf"], gate_up), it, flush)
+    t_act = kt.time(lambda: moe.act_requant(p, gate_up, bufs, a2_q, a2_sf), it, flush)
+    t_w2 = kt.time(lambda: moe.grouped_gemm_w2(p, a2_q, a2_sf, bufs, inp["w2"], inp["w2_sf"],
+                                               down), it, flush)
+    t_red = kt.time(lambda: moe.topk_reduce(p, down, bufs["slot_row"], bufs["topk_w"], out),
+                    it, flush)
+    torch.cuda.synchronize()
+    counts = bufs["expert_num_tokens"].cpu().numpy()
+    T_valid = cfg.T - (int(inp["is_padding"].sum().item()) if inp["is_padding"] is not None
+                       else 0)
+    alg = algorithmic(cfg, counts, T_valid)
+
+    def gbs(b, t_ms):
+        return b / (t_ms * 1e-3) / 1e9
+
+    kernels = {
+        "stage_and_route": {"ms": t_stage[0], "GB/s": gbs(alg["stage"], t_stage[0])},
+        "grouped_gemm_w13": {"ms": t_w13[0], "GB/s": gbs(alg["w13_bytes"], t_w13[0]),
+                             "TFLOP/s": alg["w13_flops"] / (t_w13[0] * 1e-3) / 1e12},
+        "act_requant": {"ms": t_act[0], "GB/s": gbs(alg["act"], t_act[0])},
+        "grouped_gemm_w2": {"ms": t_w2[0], "GB/s": gbs(alg["w2_bytes"], t_w2[0]),
+                            "TFLOP/s": alg["w2_flops"] / (t_w2[0] * 1e-3) / 1e12},
+        "topk_reduce": {"ms": t_red[0], "GB/s": gbs(alg["reduce"], t_red[0])},
+    }
+    for v in kernels.values():
+        v["frac_hbm"] = v["GB/s"] / HBM_PEAK_GBS
+    gemm_flops = alg["w13_flops"] + alg["w2_flops"]
+    gemm_ms = t_w13[0] + t_w2[0]
+    gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
+    w13_gbs = kernels["grouped_gemm_w13"]["GB/s"]
+    roofline = {"bound": "hbm", "achieved": round(w13_gbs, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(w13_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": "grouped_gemm_w13",
+                "algorithmic_bytes_per_launch": alg["w13_bytes"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(cfg, inp, bufs, args.cpu_seconds)
+
+    tokens_per_s = cfg.T / (ms * 1e-3)
+    line = {
+        "metric": "MoE layer tokens/s (+ grouped-GEMM fp8 TFLOP/s as % of MFMA peak), 1 GPU",
+        "value": round(tokens_per_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "E": cfg.E, "top_k": cfg.top_k,
+                   "K": cfg.K, "N": cfg.N, "layout": cfg.layout, "act_quant": cfg.act_quant,
+                   "routing": cfg.routing, "pad_frac": cfg.pad_frac, "T_valid": T_valid,
+                   "routed_rows": int(counts.sum()), "tile_m": s["tile_m"]},
+        "gemm_tflops": round(gemm_tflops, 2),
+        "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+        "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,89 @@
+// Device helpers shared by the gfx950 kernels of the MoE expert layer.
+//
+// Number formats: bf16 in HBM, fp32 in registers, fp8 e4m3fn (OCP "fn"
+// variant, max 448, no infinities) for quantized activations and weights.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroup = 128;        // quantization group / scale block edge
+constexpr float kFp8Max = 448.0f;  // largest finite e4m3fn value
+
+// ---- bf16 <-> fp32 --------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t packed) {
+  return __uint_as_float(packed << 16);
+}
+__device__ __forceinline__ float bf16_hi(uint32_t packed) {
+  return __uint_as_float(packed & 0xFFFF0000u);
+}
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---- fp32 -> e4m3fn ---------------------------------------------------------
+// The hardware converter rounds to nearest even; clamping to +-448 first
+// makes out-of-range magnitudes saturate instead of becoming NaN.
+__device__ __forceinline__ uint32_t f32x4_to_e4m3x4(float a, float b, float c, float d) {
+  a = __builtin_amdgcn_fmed3f(a, -kFp8Max, kFp8Max);
+  b = __builtin_amdgcn_fmed3f(b, -kFp8Max, kFp8Max);
+  c = __builtin_amdgcn_fmed3f(c, -kFp8Max, kFp8Max);
+  d = __builtin_amdgcn_fmed3f(d, -kFp8Max, kFp8Max);
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
+// ---- cross-lane max over a row of 16 lanes (DPP) ---------------------------
+// quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror, row_mirror:
+// after the four steps every lane of the 16-lane row holds the row maximum.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  v = fmaxf(v, dpp_f32<0x140>(v));
+  return v;
+}
+
+// ---- the per-128 group scale ------------------------------------------------
+// Given the group's amax: floor it at 1e-4, divide by 448 (correctly rounded
+// fp32 division), and for UE8M0 round the scale up to a power of two through
+// its fp32 bit fields (exponent + 1 when the mantissa is non-zero, clamped to
+// [1, 254]).  Returns the reciprocal the values are multiplied by and the
+// value to store (exponent byte, or the fp32 scale's bits).
+struct GroupScale {
+  float recip;
+  uint32_t stored;
+};
+template <bool UE8M0>
+__device__ __forceinline__ GroupScale group_scale(float amax) {
+  amax = fmaxf(amax, 1.0e-4f);
+  const float s = amax / kFp8Max;
+  GroupScale r;
+  if (UE8M0) {
+    const uint32_t bits = __float_as_uint(s);
+    uint32_t e = ((bits >> 23) & 0xFFu) + ((bits & 0x7FFFFFu) != 0u ? 1u : 0u);
+    e = e < 1u ? 1u : (e > 254u ? 254u : e);
+    r.recip = 1.0f / __uint_as_float(e << 23);
+    r.stored = e;
+  } else {
+    r.recip = 1.0f / s;
+    r.stored = __float_as_uint(s);
+  }
+  return r;
+}
+
+}  // namespace moe

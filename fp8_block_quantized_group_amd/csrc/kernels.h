@@ -1,0 +1,65 @@
+// Internal launchers of the gfx950 kernels (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// activation quantization schemes (values match moe_quant_t)
+constexpr int kQuantUe8m0 = 0;
+constexpr int kQuantF32 = 1;
+constexpr int kQuantBf16 = 2;
+
+// routing: slots handled per block of the count / scatter kernels
+constexpr int kRouteChunk = 1024;
+constexpr int kRouteThreads = 256;
+
+struct EplbArgs {
+  const int32_t* l2p;            // [num_logical, map_stride] or nullptr
+  int map_stride;
+  const int32_t* replica_count;  // [num_logical]
+  int num_logical;
+  int32_t* expert_load;          // [E] or nullptr
+  const int32_t* record_flag;    // [1] device, or nullptr
+  const int32_t* num_unpadded;   // [1] device, or nullptr
+};
+
+// Grouped GEMM problem for one launch (w13 or w2).
+struct GemmArgs {
+  const uint8_t* a;          // activation codes, rows of Kd bytes
+  const void* a_sf;          // activation scales (UE8M0 bytes or fp32) per row
+  int a_sf_stride;           // scale row length: bytes (UE8M0) or floats (fp32)
+  const uint8_t* w;          // weight codes [E, Nout, Kd]
+  const float* w_sf;         // weight block scales [E, Nout/128, Kd/128]
+  uint16_t* out;             // bf16 [rows, Nout]
+  const int32_t* tile_list;  // [0] tile count, then (expert, m0) pairs
+  const int32_t* counts;     // [E] rows per expert
+  const int32_t* offsets;    // [E+1] contiguous row base, nullptr for batched slabs
+  const int32_t* row_src;    // A row gather (w13 on the contiguous layout) or nullptr
+  int max_tokens;            // batched slab rows
+  int Kd;                    // reduction length, multiple of 128
+  int Nout;                  // output columns, multiple of 128
+};
+
+hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, int K, int quant,
+                              const int32_t* counts, int max_tokens, hipStream_t stream);
+
+hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t rows_cap, int N,
+                              int quant, const int32_t* num_rows, const int32_t* counts,
+                              int max_tokens, hipStream_t stream);
+
+hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint8_t* is_padding,
+                        int T, int k, int E, const EplbArgs& eplb, int64_t* idx_out,
+                        float* w_out, int32_t* hist, const int32_t* counts_in, int max_tokens,
+                        int tile_m, int32_t* expert_num_tokens, int32_t* expert_offsets,
+                        int32_t* row_src, int32_t* slot_row, int32_t* tile_list,
+                        hipStream_t stream);
+
+hipError_t launch_grouped_gemm(const GemmArgs& args, int tile_m, int max_tiles, int quant,
+                               hipStream_t stream);
+
+hipError_t launch_topk_reduce(const void* down, const int32_t* slot_row, const float* w, void* out,
+                              int T, int k, int K, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,432 @@
+// Host side of the C ABI: argument validation, buffer planning, tile-size
+// choice and the launch sequence of the layer on one stream.
+//
+// Validation follows the error conditions of prepare_megamoe_inputs and
+// _resolve_hidden_quant ("vllm.model_executor.layers.fused_moe.
+// prepare_megamoe": hidden size a multiple of 128, matching top-k shapes,
+// scale buffer present iff quantizing, an empty batch is a no-op) and the
+// experts' apply() preconditions ("...experts.fused_humming_moe": batched
+// format needs expert_num_tokens).  The workspace plan mirrors
+// HummingExpertsBase.get_buffer_metas / prepare_buffers: neighbouring
+// buffers of the chain x_q -> gate_up -> a2 -> down live in different
+// regions, so two regions (fp8 side and bf16 side) suffice.
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "../../include/moe_fp8.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status_t fail(moe_status_t code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+moe_status_t fail(moe_status_t code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+moe_status_t ok() {
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+moe_status_t launch_status(hipError_t err, const char* what) {
+  if (err == hipSuccess) return ok();
+  return fail(MOE_ERR_LAUNCH, "%s: kernel launch failed: %s", what, hipGetErrorString(err));
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool batched(const moe_problem_t* p) { return p->layout == MOE_LAYOUT_BATCHED_MASKED; }
+
+// Activation rows per GEMM tile, from the expected rows per expert.  Rows
+// per expert below 16 leave a 16-row MFMA tile mostly empty, and there the
+// GEMM streams weights at HBM speed whatever the tile height, so the
+// smallest tile that covers the typical expert wins.
+int choose_tile_m(const moe_problem_t* p) {
+  const char* env = getenv("MOE_TILE_M");
+  if (env != nullptr) {
+    const int v = atoi(env);
+    if (v == 16 || v == 32 || v == 64 || v == 128) return v;
+  }
+  const double rows = (double)p->num_tokens * p->top_k / p->num_experts;
+  if (rows <= 12.0) return 16;
+  if (rows <= 24.0) return 32;
+  if (rows <= 48.0) return 64;
+  return 128;
+}
+
+moe_status_t validate_problem(const moe_problem_t* p, bool allow_bf16) {
+  if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "problem is NULL");
+  if (p->num_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens < 0 (%d)", p->num_tokens);
+  if (p->hidden <= 0 || p->hidden % 128 != 0)
+    return fail(MOE_ERR_INVALID_ARG, "hidden size must be a positive multiple of 128, got %d",
+                p->hidden);
+  if (p->intermediate <= 0 || p->intermediate % 128 != 0)
+    return fail(MOE_ERR_INVALID_ARG,
+                "intermediate size must be a positive multiple of 128, got %d", p->intermediate);
+  if (p->num_experts < 1 || p->num_experts > 1024)
+    return fail(MOE_ERR_UNSUPPORTED, "num_experts must be in [1, 1024], got %d", p->num_experts);
+  if (p->top_k < 1) return fail(MOE_ERR_INVALID_ARG, "top_k must be >= 1, got %d", p->top_k);
+  if ((int64_t)p->num_tokens * p->top_k >= (int64_t)1 << 31)
+    return fail(MOE_ERR_UNSUPPORTED, "num_tokens * top_k must be < 2^31");
+  if (p->layout != MOE_LAYOUT_CONTIGUOUS && p->layout != MOE_LAYOUT_BATCHED_MASKED)
+    return fail(MOE_ERR_INVALID_ARG, "unknown layout %d", p->layout);
+  if (batched(p) && p->max_tokens_per_expert < 1)
+    return fail(MOE_ERR_INVALID_ARG, "batched layout needs max_tokens_per_expert >= 1");
+  if (batched(p) && (int64_t)p->num_experts * p->max_tokens_per_expert >= (int64_t)1 << 31)
+    return fail(MOE_ERR_UNSUPPORTED, "num_experts * max_tokens_per_expert must be < 2^31");
+  if (p->act_quant != MOE_Q_FP8_UE8M0 && p->act_quant != MOE_Q_FP8_F32 &&
+      !(allow_bf16 && p->act_quant == MOE_Q_BF16))
+    return fail(allow_bf16 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED,
+                "activation quantization %d not supported by this call", p->act_quant);
+  return MOE_OK;
+}
+
+struct Plan {
+  moe_sizes_t s;
+  int64_t route_blocks;
+  int64_t max_tiles;
+  size_t x_q_bytes, x_sf_bytes, a2_q_bytes, a2_sf_bytes, gate_up_bytes, down_bytes;
+  size_t stage_ws_bytes;
+};
+
+Plan make_plan(const moe_problem_t* p) {
+  Plan pl;
+  const int64_t T = p->num_tokens, k = p->top_k, E = p->num_experts;
+  const int64_t K = p->hidden, N = p->intermediate;
+  const int64_t GK = K / 128, GN = N / 128;
+  const bool ue = p->act_quant == MOE_Q_FP8_UE8M0;
+  pl.s.slots = T * k;
+  pl.s.tile_m = choose_tile_m(p);
+  const int64_t bm = pl.s.tile_m;
+  if (batched(p)) {
+    pl.s.stage_rows = E * p->max_tokens_per_expert;
+    pl.s.expert_rows = pl.s.stage_rows;
+    pl.max_tiles = E * ((p->max_tokens_per_expert + bm - 1) / bm);
+  } else {
+    pl.s.stage_rows = T;
+    pl.s.expert_rows = T * k;
+    pl.max_tiles = (T * k + bm - 1) / bm + E;
+  }
+  pl.s.tile_list = 1 + 2 * pl.max_tiles;
+  pl.s.x_sf_row = ue ? 4 * ((GK + 3) / 4) : GK;
+  pl.s.a2_sf_row = ue ? 4 * ((GN + 3) / 4) : GN;
+  pl.route_blocks = (T * k + moe::kRouteChunk - 1) / moe::kRouteChunk;
+  pl.stage_ws_bytes = round_up((size_t)std::max<int64_t>(pl.route_blocks, 1) * E * 4);
+  const size_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
+  pl.x_q_bytes = (size_t)pl.s.stage_rows * K * elem;
+  pl.x_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.stage_rows * pl.s.x_sf_row * (ue ? 1 : 4);
+  pl.a2_q_bytes = (size_t)pl.s.expert_rows * N;
+  pl.a2_sf_bytes = (size_t)pl.s.expert_rows * pl.s.a2_sf_row * (ue ? 1 : 4);
+  pl.gate_up_bytes = (size_t)pl.s.expert_rows * 2 * N * 2;
+  pl.down_bytes = (size_t)pl.s.expert_rows * K * 2;
+  return pl;
+}
+
+// Device addresses of the forward workspace.
+struct Workspace {
+  uint8_t* x_q; uint8_t* x_sf; uint8_t* a2_q; uint8_t* a2_sf;
+  uint8_t* gate_up; uint8_t* down;
+  int64_t* idx; float* w; moe_routing_t routing; int32_t* stage_ws;
+  size_t total;
+};
+
+Workspace carve(const Plan& pl, const moe_problem_t* p, uint8_t* base) {
+  Workspace w;
+  size_t off = 0;
+  auto take = [&](size_t bytes) { uint8_t* r = base + off; off += round_up(bytes); return r; };
+  // region 1: fp8 activations (x_q + x_sf, later a2_q + a2_sf)
+  const size_t r1 = std::max(round_up(pl.x_q_bytes) + round_up(pl.x_sf_bytes),
+                             round_up(pl.a2_q_bytes) + round_up(pl.a2_sf_bytes));
+  uint8_t* reg1 = take(r1);
+  w.x_q = reg1;
+  w.x_sf = reg1 + round_up(pl.x_q_bytes);
+  w.a2_q = reg1;
+  w.a2_sf = reg1 + round_up(pl.a2_q_bytes);
+  // region 2: bf16 gate_up, later down
+  uint8_t* reg2 = take(std::max(pl.gate_up_bytes, pl.down_bytes));
+  w.gate_up = reg2;
+  w.down = reg2;
+  const size_t slots = (size_t)pl.s.slots;
+  w.idx = (int64_t*)take(slots * 8);
+  w.w = (float*)take(slots * 4);
+  w.routing.expert_num_tokens = (int32_t*)take((size_t)p->num_experts * 4);
+  w.routing.expert_offsets = (int32_t*)take((size_t)(p->num_experts + 1) * 4);
+  w.routing.row_src = (int32_t*)take(std::max<size_t>(slots, 1) * 4);
+  w.routing.slot_row = (int32_t*)take(std::max<size_t>(slots, 1) * 4);
+  w.routing.tile_list = (int32_t*)take((size_t)pl.s.tile_list * 4);
+  w.stage_ws = (int32_t*)take(pl.stage_ws_bytes);
+  w.total = off;
+  return w;
+}
+
+moe_status_t check_ptr(const void* ptr, const char* name, size_t align) {
+  if (ptr == nullptr) return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(ptr, align))
+    return fail(MOE_ERR_INVALID_ARG, "%s must be %zu-byte aligned", name, align);
+  return MOE_OK;
+}
+
+#define CHECK(expr)                         \
+  do {                                      \
+    const moe_status_t _s = (expr);         \
+    if (_s != MOE_OK) return _s;            \
+  } while (0)
+
+moe_status_t check_routing(const moe_routing_t* r) {
+  if (r == nullptr) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+  CHECK(check_ptr(r->expert_num_tokens, "routing.expert_num_tokens", 4));
+  CHECK(check_ptr(r->expert_offsets, "routing.expert_offsets", 4));
+  CHECK(check_ptr(r->row_src, "routing.row_src", 4));
+  CHECK(check_ptr(r->slot_row, "routing.slot_row", 4));
+  CHECK(check_ptr(r->tile_list, "routing.tile_list", 4));
+  return MOE_OK;
+}
+
+moe_status_t check_eplb(const moe_problem_t* p, const moe_eplb_t* eplb) {
+  if (eplb == nullptr) return MOE_OK;
+  CHECK(check_ptr(eplb->logical_to_physical, "eplb.logical_to_physical", 4));
+  CHECK(check_ptr(eplb->replica_count, "eplb.replica_count", 4));
+  if (eplb->map_stride < 1) return fail(MOE_ERR_INVALID_ARG, "eplb.map_stride must be >= 1");
+  if (eplb->num_logical < 1 || eplb->num_logical > p->num_experts)
+    return fail(MOE_ERR_INVALID_ARG, "eplb.num_logical must be in [1, num_experts]");
+  if (eplb->record_flag != nullptr && eplb->expert_load == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "eplb.record_flag given without eplb.expert_load");
+  return MOE_OK;
+}
+
+moe::EplbArgs eplb_args(const moe_eplb_t* eplb) {
+  moe::EplbArgs a{};
+  if (eplb != nullptr) {
+    a.l2p = eplb->logical_to_physical;
+    a.map_stride = eplb->map_stride;
+    a.replica_count = eplb->replica_count;
+    a.num_logical = eplb->num_logical;
+    a.expert_load = eplb->expert_load;
+    a.record_flag = eplb->record_flag;
+    a.num_unpadded = eplb->num_unpadded_tokens;
+  }
+  return a;
+}
+
+moe_status_t check_stage_args(const moe_problem_t* p, const void* hidden,
+                              const int32_t* counts_in, const int32_t* topk_ids,
+                              const float* topk_weights, const moe_eplb_t* eplb) {
+  CHECK(check_ptr(hidden, "hidden", 16));
+  CHECK(check_ptr(topk_ids, "topk_ids", 4));
+  CHECK(check_ptr(topk_weights, "topk_weights", 4));
+  if (batched(p)) CHECK(check_ptr(counts_in, "expert_num_tokens (batched layout)", 4));
+  CHECK(check_eplb(p, eplb));
+  return MOE_OK;
+}
+
+moe_status_t run_stage(const moe_problem_t* p, const Plan& pl, const void* hidden,
+                       const int32_t* counts_in, const int32_t* topk_ids,
+                       const float* topk_weights, const uint8_t* is_padding,
+                       const moe_eplb_t* eplb, void* x_q, void* x_sf, int64_t* idx_out,
+                       float* w_out, const moe_routing_t* r, int32_t* hist,
+                       hipStream_t stream) {
+  const int32_t* cin = batched(p) ? counts_in : nullptr;
+  hipError_t err = moe::launch_stage_quant(hidden, x_q, x_sf, pl.s.stage_rows, p->hidden,
+                                           p->act_quant, cin, p->max_tokens_per_expert, stream);
+  if (err != hipSuccess) return launch_status(err, "stage_quant");
+  err = moe::launch_route(topk_ids, topk_weights, is_padding, p->num_tokens, p->top_k,
+                          p->num_experts, eplb_args(eplb), idx_out, w_out, hist, cin,
+                          p->max_tokens_per_expert, pl.s.tile_m, r->expert_num_tokens,
+                          r->expert_offsets, r->row_src, r->slot_row, r->tile_list, stream);
+  return launch_status(err, "route");
+}
+
+moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const void* a_q,
+                      const void* a_sf, const moe_routing_t* r, const void* w, const float* w_sf,
+                      void* out, hipStream_t stream) {
+  moe::GemmArgs g{};
+  g.a = (const uint8_t*)a_q;
+  g.a_sf = a_sf;
+  g.a_sf_stride = (int)(w13 ? pl.s.x_sf_row : pl.s.a2_sf_row);
+  g.w = (const uint8_t*)w;
+  g.w_sf = w_sf;
+  g.out = (uint16_t*)out;
+  g.tile_list = r->tile_list;
+  g.counts = r->expert_num_tokens;
+  g.offsets = batched(p) ? nullptr : r->expert_offsets;
+  g.row_src = (w13 && !batched(p)) ? r->row_src : nullptr;
+  g.max_tokens = p->max_tokens_per_expert;
+  g.Kd = w13 ? p->hidden : p->intermediate;
+  g.Nout = w13 ? 2 * p->intermediate : p->hidden;
+  const hipError_t err =
+      moe::launch_grouped_gemm(g, pl.s.tile_m, (int)pl.max_tiles, p->act_quant, stream);
+  return launch_status(err, w13 ? "grouped_gemm_w13" : "grouped_gemm_w2");
+}
+
+moe_status_t run_act(const moe_problem_t* p, const Plan& pl, const void* gate_up,
+                     const moe_routing_t* r, void* a2_q, void* a2_sf, hipStream_t stream) {
+  const bool b = batched(p);
+  const hipError_t err = moe::launch_act_requant(
+      gate_up, a2_q, a2_sf, pl.s.expert_rows, p->intermediate, p->act_quant,
+      b ? nullptr : r->expert_offsets + p->num_experts, b ? r->expert_num_tokens : nullptr,
+      p->max_tokens_per_expert, stream);
+  return launch_status(err, "act_requant");
+}
+
+moe_status_t run_reduce(const moe_problem_t* p, const void* down, const int32_t* slot_row,
+                        const float* w, void* out, hipStream_t stream) {
+  const hipError_t err = moe::launch_topk_reduce(down, slot_row, w, out, p->num_tokens, p->top_k,
+                                                 p->hidden, stream);
+  return launch_status(err, "topk_reduce");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_last_error.c_str(); }
+
+moe_status_t moe_routing_sizes(const moe_problem_t* p, moe_sizes_t* out) {
+  CHECK(validate_problem(p, true));
+  if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+  *out = make_plan(p).s;
+  return ok();
+}
+
+moe_status_t moe_stage_workspace_size(const moe_problem_t* p, size_t* bytes) {
+  CHECK(validate_problem(p, true));
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = make_plan(p).stage_ws_bytes;
+  return ok();
+}
+
+moe_status_t moe_workspace_size(const moe_problem_t* p, size_t* bytes) {
+  CHECK(validate_problem(p, false));
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  const Plan pl = make_plan(p);
+  *bytes = carve(pl, p, nullptr).total;
+  return ok();
+}
+
+moe_status_t moe_stage(const moe_problem_t* p, const void* hidden,
+                       const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
+                       const float* topk_weights, const uint8_t* is_padding,
+                       const moe_eplb_t* eplb, void* x_q, void* x_sf, int64_t* topk_idx_out,
+                       float* topk_w_out, const moe_routing_t* routing, void* ws,
+                       size_t ws_bytes, void* stream) {
+  CHECK(validate_problem(p, true));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_stage_args(p, hidden, expert_num_tokens_in, topk_ids, topk_weights, eplb));
+  CHECK(check_ptr(x_q, "x_q", 16));
+  if ((p->act_quant == MOE_Q_BF16) != (x_sf == nullptr))
+    return fail(MOE_ERR_INVALID_ARG, "x_sf must be given iff the hidden states are quantized");
+  if (x_sf != nullptr) CHECK(check_ptr(x_sf, "x_sf", 4));
+  CHECK(check_ptr(topk_idx_out, "topk_idx_out", 8));
+  CHECK(check_ptr(topk_w_out, "topk_w_out", 4));
+  CHECK(check_routing(routing));
+  CHECK(check_ptr(ws, "ws", 4));
+  const Plan pl = make_plan(p);
+  if (ws_bytes < pl.stage_ws_bytes)
+    return fail(MOE_ERR_WORKSPACE, "stage workspace too small: %zu < %zu bytes", ws_bytes,
+                pl.stage_ws_bytes);
+  return run_stage(p, pl, hidden, expert_num_tokens_in, topk_ids, topk_weights, is_padding, eplb,
+                   x_q, x_sf, topk_idx_out, topk_w_out, routing, (int32_t*)ws,
+                   (hipStream_t)stream);
+}
+
+moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const void* a_sf,
+                                  const moe_routing_t* routing, const void* w13,
+                                  const float* w13_sf, void* gate_up, void* stream) {
+  CHECK(validate_problem(p, false));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_ptr(a_q, "a_q", 16));
+  CHECK(check_ptr(a_sf, "a_sf", 4));
+  CHECK(check_routing(routing));
+  CHECK(check_ptr(w13, "w13", 16));
+  CHECK(check_ptr(w13_sf, "w13_sf", 4));
+  CHECK(check_ptr(gate_up, "gate_up", 16));
+  const Plan pl = make_plan(p);
+  return run_gemm(p, pl, true, a_q, a_sf, routing, w13, w13_sf, gate_up, (hipStream_t)stream);
+}
+
+moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
+                             const moe_routing_t* routing, void* a2_q, void* a2_sf,
+                             void* stream) {
+  CHECK(validate_problem(p, false));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_ptr(gate_up, "gate_up", 16));
+  CHECK(check_routing(routing));
+  CHECK(check_ptr(a2_q, "a2_q", 16));
+  CHECK(check_ptr(a2_sf, "a2_sf", 4));
+  const Plan pl = make_plan(p);
+  return run_act(p, pl, gate_up, routing, a2_q, a2_sf, (hipStream_t)stream);
+}
+
+moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const void* a2_sf,
+                                 const moe_routing_t* routing, const void* w2,
+                                 const float* w2_sf, void* down, void* stream) {
+  CHECK(validate_problem(p, false));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_ptr(a2_q, "a2_q", 16));
+  CHECK(check_ptr(a2_sf, "a2_sf", 4));
+  CHECK(check_routing(routing));
+  CHECK(check_ptr(w2, "w2", 16));
+  CHECK(check_ptr(w2_sf, "w2_sf", 4));
+  CHECK(check_ptr(down, "down", 16));
+  const Plan pl = make_plan(p);
+  return run_gemm(p, pl, false, a2_q, a2_sf, routing, w2, w2_sf, down, (hipStream_t)stream);
+}
+
+moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int32_t* slot_row,
+                             const float* topk_w, void* out, void* stream) {
+  CHECK(validate_problem(p, true));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_ptr(down, "down", 16));
+  CHECK(check_ptr(slot_row, "slot_row", 4));
+  CHECK(check_ptr(topk_w, "topk_w", 4));
+  CHECK(check_ptr(out, "out", 16));
+  return run_reduce(p, down, slot_row, topk_w, out, (hipStream_t)stream);
+}
+
+moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
+                         const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
+                         const float* topk_weights, const uint8_t* is_padding,
+                         const moe_eplb_t* eplb, const void* w13, const float* w13_sf,
+                         const void* w2, const float* w2_sf, void* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  CHECK(validate_problem(p, false));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_stage_args(p, hidden, expert_num_tokens_in, topk_ids, topk_weights, eplb));
+  CHECK(check_ptr(w13, "w13", 16));
+  CHECK(check_ptr(w13_sf, "w13_sf", 4));
+  CHECK(check_ptr(w2, "w2", 16));
+  CHECK(check_ptr(w2_sf, "w2_sf", 4));
+  CHECK(check_ptr(out, "out", 16));
+  CHECK(check_ptr(ws, "ws", kAlign));
+  const Plan pl = make_plan(p);
+  const Workspace w = carve(pl, p, (uint8_t*)ws);
+  if (ws_bytes < w.total)
+    return fail(MOE_ERR_WORKSPACE, "forward workspace too small: %zu < %zu bytes", ws_bytes,
+                w.total);
+  const hipStream_t s = (hipStream_t)stream;
+  CHECK(run_stage(p, pl, hidden, expert_num_tokens_in, topk_ids, topk_weights, is_padding, eplb,
+                  w.x_q, w.x_sf, w.idx, w.w, &w.routing, w.stage_ws, s));
+  CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, w.gate_up, s));
+  CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s));
+  CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s));
+  CHECK(run_reduce(p, w.down, w.routing.slot_row, w.w, out, s));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,165 @@
+// Bandwidth-bound quantization kernels: hidden-state staging and the fused
+// SiLU(gate)*up + re-quantization of the w2 input.
+//
+// Group quantizer: "vllm.model_executor.layers.fused_moe.prepare_megamoe",
+// _quantize_fp8_groups (per-128 amax, 1e-4 floor, /448, UE8M0 rounding of
+// the scale through its fp32 bit fields, x * (1/scale) to e4m3fn).
+// Activation fused into the w2-input quantization:
+// "vllm.model_executor.layers.fused_moe.experts.fused_humming_moe",
+// HummingExpertsBase.process_input with activation (pull-request 58588 build).
+//
+// Work split: one 16-lane DPP row per 128-value group; each lane loads 8
+// bf16 (16 bytes), the row reduces |x| with four DPP max steps, each lane
+// writes 8 fp8 bytes.  A 64-lane wave covers four groups = 512 contiguous
+// input values, so every load and store instruction is fully coalesced.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// Quantize the 8 values a lane holds (its row of 16 lanes forms one group),
+// write the codes and, from lane 0 of the row, the group's scale.
+template <bool UE8M0>
+__device__ __forceinline__ void quantize_store(const float f[8], int lane16, uint8_t* q_dst,
+                                               uint8_t* sf_row, int g, int G, int sf_row_len) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = row16_max(amax);
+  const GroupScale gs = group_scale<UE8M0>(amax);
+  uint2 q;
+  q.x = f32x4_to_e4m3x4(f[0] * gs.recip, f[1] * gs.recip, f[2] * gs.recip, f[3] * gs.recip);
+  q.y = f32x4_to_e4m3x4(f[4] * gs.recip, f[5] * gs.recip, f[6] * gs.recip, f[7] * gs.recip);
+  *reinterpret_cast<uint2*>(q_dst) = q;
+  if (UE8M0) {
+    if (lane16 == 0) sf_row[g] = (uint8_t)gs.stored;
+    // the row's trailing pad bytes (4*ceil(G/4) - G of them) are zero
+    if (g == G - 1 && lane16 >= 1 && lane16 <= sf_row_len - G) sf_row[G + lane16 - 1] = 0;
+  } else {
+    if (lane16 == 0) reinterpret_cast<uint32_t*>(sf_row)[g] = gs.stored;
+  }
+}
+
+// Row r of a batched-masked slab array is live iff r % max_tokens < counts[r / max_tokens].
+__device__ __forceinline__ bool row_live(int64_t row, const int32_t* counts, int max_tokens) {
+  if (counts == nullptr) return true;
+  const int64_t e = row / max_tokens;
+  return (row - e * max_tokens) < (int64_t)counts[e];
+}
+
+template <bool UE8M0>
+__global__ __launch_bounds__(256) void stage_quant_kernel(
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
+    int64_t num_groups, int G, int sf_row_len, const int32_t* __restrict__ counts,
+    int max_tokens) {
+  const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int lane16 = threadIdx.x & 15;
+  if (gid >= num_groups) return;
+  const int64_t row = gid / G;
+  const int g = (int)(gid - row * G);
+  if (!row_live(row, counts, max_tokens)) return;
+  const uint4 v = reinterpret_cast<const uint4*>(x + gid * kGroup)[lane16];
+  float f[8];
+  unpack8(v, f);
+  uint8_t* sf_row = UE8M0 ? xsf + row * sf_row_len : xsf + row * (int64_t)G * 4;
+  quantize_store<UE8M0>(f, lane16, xq + gid * kGroup + lane16 * 8, sf_row, g, G, sf_row_len);
+}
+
+// bf16 staging without quantization: a masked 16-byte copy.
+__global__ __launch_bounds__(256) void stage_copy_kernel(
+    const uint4* __restrict__ x, uint4* __restrict__ y, int64_t num_vec, int vec_per_row,
+    const int32_t* __restrict__ counts, int max_tokens) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= num_vec) return;
+  if (!row_live(i / vec_per_row, counts, max_tokens)) return;
+  y[i] = x[i];
+}
+
+// h = silu(gate) * up for columns [g*128, g*128+128) of the gate half and
+// the same columns of the up half, then the group quantizer on h.
+template <bool UE8M0>
+__global__ __launch_bounds__(256) void act_requant_kernel(
+    const uint16_t* __restrict__ gu, uint8_t* __restrict__ aq, uint8_t* __restrict__ asf,
+    int64_t num_groups, int N, int GN, int sf_row_len, const int32_t* __restrict__ num_rows,
+    const int32_t* __restrict__ counts, int max_tokens) {
+  const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int lane16 = threadIdx.x & 15;
+  if (gid >= num_groups) return;
+  const int64_t row = gid / GN;
+  const int g = (int)(gid - row * GN);
+  if (num_rows != nullptr && row >= (int64_t)*num_rows) return;
+  if (!row_live(row, counts, max_tokens)) return;
+  const uint16_t* src = gu + row * (int64_t)(2 * N) + g * kGroup + lane16 * 8;
+  const uint4 vg = *reinterpret_cast<const uint4*>(src);
+  const uint4 vu = *reinterpret_cast<const uint4*>(src + N);
+  float fg[8], fu[8], h[8];
+  unpack8(vg, fg);
+  unpack8(vu, fu);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-fg[i]));
+    h[i] = fg[i] * sig * fu[i];
+  }
+  uint8_t* sf_row = UE8M0 ? asf + row * sf_row_len : asf + row * (int64_t)GN * 4;
+  quantize_store<UE8M0>(h, lane16, aq + row * (int64_t)N + g * kGroup + lane16 * 8, sf_row, g,
+                        GN, sf_row_len);
+}
+
+inline unsigned blocks_for(int64_t n, int per_block) {
+  return (unsigned)((n + per_block - 1) / per_block);
+}
+
+}  // namespace
+
+hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, int K,
+                              int quant, const int32_t* counts, int max_tokens,
+                              hipStream_t stream) {
+  const int G = K / kGroup;
+  const int64_t groups = rows * G;
+  if (groups == 0) return hipSuccess;
+  const int sf_row_len = 4 * ((G + 3) / 4);
+  if (quant == kQuantBf16) {
+    const int64_t nvec = rows * (K / 8);
+    stage_copy_kernel<<<blocks_for(nvec, 256), 256, 0, stream>>>(
+        (const uint4*)x, (uint4*)xq, nvec, K / 8, counts, max_tokens);
+  } else if (quant == kQuantUe8m0) {
+    stage_quant_kernel<true><<<blocks_for(groups, 16), 256, 0, stream>>>(
+        (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, groups, G, sf_row_len, counts,
+        max_tokens);
+  } else {
+    stage_quant_kernel<false><<<blocks_for(groups, 16), 256, 0, stream>>>(
+        (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, groups, G, sf_row_len, counts,
+        max_tokens);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t rows_cap, int N,
+                              int quant, const int32_t* num_rows, const int32_t* counts,
+                              int max_tokens, hipStream_t stream) {
+  const int GN = N / kGroup;
+  const int64_t groups = rows_cap * GN;
+  if (groups == 0) return hipSuccess;
+  const int sf_row_len = 4 * ((GN + 3) / 4);
+  if (quant == kQuantUe8m0) {
+    act_requant_kernel<true><<<blocks_for(groups, 16), 256, 0, stream>>>(
+        (const uint16_t*)gate_up, (uint8_t*)aq, (uint8_t*)asf, groups, N, GN, sf_row_len,
+        num_rows, counts, max_tokens);
+  } else {
+    act_requant_kernel<false><<<blocks_for(groups, 16), 256, 0, stream>>>(
+        (const uint16_t*)gate_up, (uint8_t*)aq, (uint8_t*)asf, groups, N, GN, sf_row_len,
+        num_rows, counts, max_tokens);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

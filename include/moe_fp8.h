@@ -1,0 +1,208 @@
+/*
+ * moe_fp8.h -- C ABI of the gfx950 fp8 block-quantized MoE expert layer.
+ *
+ * The layer, as the vLLM API documentation pages on the subject describe it:
+ *   1. stage: per-128-group fp8 e4m3fn quantization of the hidden states with
+ *      UE8M0 (power-of-two) or fp32 scales, and the top-k routing repack
+ *      ("vllm.model_executor.layers.fused_moe.prepare_megamoe",
+ *      prepare_megamoe_inputs, _quantize_fp8_groups, _store_topk);
+ *   2. per-expert counts, offsets and the token -> row permutation
+ *      ("vllm.model_executor.layers.fused_moe.experts.fused_humming_moe",
+ *      HummingGroupedExperts.apply: moe_prepare_scatter / moe_permute;
+ *      BatchedHummingGroupedExperts.apply: expert_num_tokens);
+ *   3. grouped GEMM with the fused gate/up weights w13;
+ *   4. SiLU(gate) * up re-quantized to fp8 (HummingExpertsBase.process_input
+ *      with an activation);
+ *   5. grouped GEMM with the down weights w2;
+ *   6. router-weighted top-k reduce back to token order (moe_unpermute /
+ *      moe_fused_mul_sum).
+ *
+ * Conventions for every call
+ *  - Pointers named "device" are HIP device pointers; the caller allocates and
+ *    owns every buffer; the library never allocates, frees or synchronizes.
+ *    Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
+ *    null stream) and buffers must stay valid until it completes.
+ *  - Arrays are dense row-major.  Vector-accessed buffers (hidden states, fp8
+ *    codes, bf16 intermediates, weights, output) must be 16-byte aligned,
+ *    scale and index arrays 4-byte aligned (int64 arrays 8-byte aligned).
+ *  - Return value: MOE_OK, or a negative moe_status_t after synchronous
+ *    argument validation (nothing is enqueued then); moe_last_error() gives
+ *    the message.  MOE_ERR_LAUNCH reports a failed kernel launch.
+ *  - num_tokens == 0 is a successful no-op (prepare_megamoe_inputs returns
+ *    early for an empty batch).
+ *  - Expert ids outside [0, num_experts) are treated as unrouted, never as
+ *    errors.
+ *
+ * Formats
+ *  - bf16: IEEE binary32's upper 16 bits.  fp8: OCP e4m3fn bytes.
+ *  - Activation scales, MOE_Q_FP8_UE8M0: one exponent byte e per 128-group
+ *    (scale 2^(e-127)), rows of 4*ceil(G/4) bytes with zero pad bytes; this is
+ *    byte-identical to the pages' "four per int32" little-endian packing
+ *    (_pack_bytes).  MOE_Q_FP8_F32: fp32 [rows, G].
+ *  - Weights: w13 [E, 2N, K] fp8 codes (rows [0, N) gate, [N, 2N) up) with
+ *    fp32 block scales w13_sf [E, 2N/128, K/128]; w2 [E, K, N] with
+ *    w2_sf [E, K/128, N/128]; dequantized weight = code * block scale
+ *    (the kFp8Static128BlockSym scheme).
+ */
+#ifndef MOE_FP8_H
+#define MOE_FP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1,
+  MOE_ERR_UNSUPPORTED = -2,
+  MOE_ERR_WORKSPACE = -3,
+  MOE_ERR_LAUNCH = -4
+} moe_status_t;
+
+/* Activation quantization (w13 input and w2 input use the same scheme). */
+typedef enum {
+  MOE_Q_FP8_UE8M0 = 0, /* fp8 e4m3fn, per-128 power-of-two scales          */
+  MOE_Q_FP8_F32 = 1,   /* fp8 e4m3fn, per-128 fp32 scales                   */
+  MOE_Q_BF16 = 2       /* staging only: hidden states copied unquantized    */
+} moe_quant_t;
+
+/* Expert-row layouts ("Standard" and "BatchedExperts" activation formats). */
+typedef enum {
+  MOE_LAYOUT_CONTIGUOUS = 0,     /* rows grouped by expert, offsets [E+1]   */
+  MOE_LAYOUT_BATCHED_MASKED = 1  /* [E, max_tokens_per_expert, K] slabs     */
+} moe_layout_t;
+
+/* Problem description (host struct).  T tokens, hidden size K, intermediate
+ * size N, E physical experts, top_k routed experts per token.
+ * Requirements: K and N multiples of 128; 1 <= E <= 1024; 1 <= top_k;
+ * T * top_k < 2^31; batched layout needs max_tokens_per_expert >= 1. */
+typedef struct {
+  int32_t num_tokens;
+  int32_t hidden;
+  int32_t intermediate;
+  int32_t num_experts;
+  int32_t top_k;
+  int32_t layout;                /* moe_layout_t */
+  int32_t max_tokens_per_expert; /* batched layout only */
+  int32_t act_quant;             /* moe_quant_t */
+} moe_problem_t;
+
+/* Expert-parallel load balancing state (optional; all device pointers).
+ * A routed logical id l in [0, num_logical) becomes the physical id
+ * logical_to_physical[l * map_stride + t % replica_count[l]] for token t
+ * (replica_count[l] <= 0 leaves the slot unrouted); when *record_flag != 0
+ * every mapped id of a token t < *num_unpadded_tokens adds one to
+ * expert_load[id] (accumulated: the caller zeroes it).  From _eplb_kernel_args
+ * on the prepare_megamoe page; the replica choice t % count is this
+ * library's reading (the map-and-record body is not shown there). */
+typedef struct {
+  const int32_t* logical_to_physical; /* [num_logical, map_stride]          */
+  int32_t map_stride;
+  const int32_t* replica_count;       /* [num_logical]                       */
+  int32_t num_logical;
+  int32_t* expert_load;               /* [num_experts] or NULL               */
+  const int32_t* record_flag;         /* [1] or NULL (= do not record)       */
+  const int32_t* num_unpadded_tokens; /* [1] or NULL (= num_tokens)          */
+} moe_eplb_t;
+
+/* Routing layout written by moe_stage and read by the later calls (device
+ * arrays, sizes from moe_routing_sizes):
+ *  expert_num_tokens [E]   rows per expert (batched: the given counts)
+ *  expert_offsets    [E+1] exclusive prefix of the routed counts
+ *  row_src           [T*top_k] token of each contiguous row (contiguous layout)
+ *  slot_row          [T*top_k] row of (token, slot), -1 when unrouted;
+ *                    batched: e * max_tokens + rank (rank >= max_tokens -> -1)
+ *  tile_list         [1 + 2*max_tiles] M-tile schedule for the GEMMs */
+typedef struct {
+  int32_t* expert_num_tokens;
+  int32_t* expert_offsets;
+  int32_t* row_src;
+  int32_t* slot_row;
+  int32_t* tile_list;
+} moe_routing_t;
+
+typedef struct {
+  int64_t slots;           /* T * top_k: row_src, slot_row, topk outputs     */
+  int64_t tile_list;       /* int32 elements of tile_list                     */
+  int64_t stage_rows;      /* rows of x_q / x_sf                              */
+  int64_t expert_rows;     /* rows of gate_up / a2 / down                     */
+  int64_t x_sf_row;        /* x_sf row length: bytes (UE8M0) / floats (fp32)  */
+  int64_t a2_sf_row;       /* a2_sf row length, same units                    */
+  int32_t tile_m;          /* activation rows per GEMM tile                   */
+} moe_sizes_t;
+
+/* Sizes of every buffer of `p` (host only). */
+moe_status_t moe_routing_sizes(const moe_problem_t* p, moe_sizes_t* out);
+
+/* Device scratch bytes moe_stage needs (host only). */
+moe_status_t moe_stage_workspace_size(const moe_problem_t* p, size_t* bytes);
+
+/* Device workspace bytes moe_forward needs (host only).  It holds the fp8
+ * activations, the bf16 gate_up / down intermediates (two ping-pong regions
+ * as in HummingExpertsBase.prepare_buffers) and the routing layout. */
+moe_status_t moe_workspace_size(const moe_problem_t* p, size_t* bytes);
+
+/* Steps 1-2.  hidden: bf16 [T, K] (contiguous) or [E, max_tokens, K]
+ * (batched; only rows below expert_num_tokens_in[e] are read).
+ * topk_ids int32 [T, top_k], topk_weights fp32 [T, top_k], is_padding uint8
+ * [T] or NULL (padding tokens: ids -1, weights 0, never routed; their hidden
+ * rows are still quantized).  expert_num_tokens_in: batched layout only,
+ * int32 [E], must equal the per-expert count of topk_ids.  eplb may be NULL.
+ * Outputs: x_q fp8 [rows, K] (MOE_Q_BF16: bf16 copy), x_sf (NULL for bf16),
+ * topk_idx_out int64 [T, top_k], topk_w_out fp32 [T, top_k], routing.
+ * ws: device scratch of moe_stage_workspace_size bytes. */
+moe_status_t moe_stage(const moe_problem_t* p, const void* hidden,
+                       const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
+                       const float* topk_weights, const uint8_t* is_padding,
+                       const moe_eplb_t* eplb, void* x_q, void* x_sf, int64_t* topk_idx_out,
+                       float* topk_w_out, const moe_routing_t* routing, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Step 3: gate_up[r, :] = block-scaled fp8 GEMM of activation row r with
+ * w13[e] for every routed row r of expert e (rows from `routing`; the
+ * contiguous layout gathers x_q rows through row_src).  gate_up: bf16
+ * [expert_rows, 2N]; rows past an expert's count are not written. */
+moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const void* a_sf,
+                                  const moe_routing_t* routing, const void* w13,
+                                  const float* w13_sf, void* gate_up, void* stream);
+
+/* Step 4: a2 = quant(silu(gate_up[:, :N]) * gate_up[:, N:]) per 128 columns,
+ * computed in fp32 and quantized without an intermediate rounding.
+ * a2_q fp8 [expert_rows, N], a2_sf per the activation scheme. */
+moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
+                             const moe_routing_t* routing, void* a2_q, void* a2_sf,
+                             void* stream);
+
+/* Step 5: down[r, :] = block-scaled fp8 GEMM of a2 row r with w2[e];
+ * down: bf16 [expert_rows, K]. */
+moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const void* a2_sf,
+                                 const moe_routing_t* routing, const void* w2,
+                                 const float* w2_sf, void* down, void* stream);
+
+/* Step 6: out[t] = bf16(sum over j ascending with slot_row[t, j] >= 0 of
+ * topk_w[t, j] * down[slot_row[t, j]]); tokens with no routed slot get 0.
+ * out: bf16 [T, K]. */
+moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int32_t* slot_row,
+                             const float* topk_w, void* out, void* stream);
+
+/* Steps 1-6 on one stream.  Arguments as in moe_stage plus the weights and
+ * out bf16 [T, K]; ws: device workspace of moe_workspace_size bytes.
+ * act_quant must be MOE_Q_FP8_UE8M0 or MOE_Q_FP8_F32. */
+moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
+                         const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
+                         const float* topk_weights, const uint8_t* is_padding,
+                         const moe_eplb_t* eplb, const void* w13, const float* w13_sf,
+                         const void* w2, const float* w2_sf, void* out, void* ws,
+                         size_t ws_bytes, void* stream);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_FP8_H */

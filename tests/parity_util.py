@@ -1,0 +1,177 @@
+"""Comparison metrics and device plumbing for the GPU parity tests.
+
+Tolerances (derived in the design notes from the arithmetic):
+  * quantized bytes, scale exponents, routing metadata: bit-exact;
+  * grouped-GEMM bf16 outputs: |gpu - oracle| <= one bf16 unit of the
+    oracle's value + 2^-11 * S_abs, where S_abs = sum over k of
+    |sa * sw * a * w| (the oracle's GEMM on absolute values).  The second
+    term bounds the fp8 MFMA's own accumulation error: a measured
+    v_mfma_f32_16x16x128_f8f6f4 misses the exact 128-term sum by up to
+    2^-12.3 (mean 2^-15.8) of the sum of |products|; and the relative
+    Frobenius difference is at most 2^-8;
+  * re-quantized fp8 activations, from the oracle's own gate_up: at most
+    1 ULP (sign-magnitude ordinal, +-0 equal) in at most 0.1% of elements;
+    a UE8M0 exponent may differ only where amax/448 is within 2^-20
+    (relative) of a power of two; fp32 scales within 2^-21 relative;
+  * re-quantized fp8 activations at the end of the GPU's own chain: each
+    value within half an fp8 step on each side plus the GEMM bound above
+    carried through silu(g) * u;
+  * final output: relative Frobenius <= 1e-2, max |diff| <= 2e-2 * max |ref|.
+"""
+import numpy as np
+import torch
+
+from oracle import moe_oracle as O
+
+
+def to_np(t):
+    """Device or host tensor -> numpy (bf16 as uint16 bits)."""
+    t = t.detach().to("cpu")
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def to_dev(a, dtype=None, device="cuda"):
+    """numpy -> device tensor; uint16 arrays become bf16."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    t = torch.from_numpy(a)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(device)
+
+
+def bf16_ulp(x64):
+    """Spacing of bf16 numbers at |x| (normal range)."""
+    a = np.maximum(np.abs(x64), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def check_bf16_close(got_bits, ref_bits, what, max_frac=0.01):
+    g = O.bf16_to_f64(got_bits)
+    r = O.bf16_to_f64(ref_bits)
+    assert g.shape == r.shape, what
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    d = np.abs(g - r)
+    rowmax = np.abs(r).max(axis=-1, keepdims=True) if r.ndim > 1 else np.abs(r).max()
+    tol = np.maximum(bf16_ulp(r), rowmax * 2.0 ** -14)
+    bad = d > tol * 1.0000001
+    assert not bad.any(), (f"{what}: {bad.sum()} elements beyond one bf16 unit, "
+                           f"worst {d[bad].max() if bad.any() else 0}")
+    frac = np.count_nonzero(d) / max(d.size, 1)
+    assert frac <= max_frac, f"{what}: {frac:.4%} of elements differ"
+    return frac
+
+
+def fp8_ordinal(codes):
+    c = codes.astype(np.int32)
+    mag = c & 0x7F
+    return np.where(c & 0x80, -mag, mag)
+
+
+MFMA_REL = 2.0 ** -11
+
+
+def abs_gemm(a_codes, a_scale, w_codes, w_sf):
+    """S_abs: the oracle's block-scaled GEMM on absolute values."""
+    return O.block_scaled_gemm_f64(np.asarray(a_codes) & 0x7F, np.abs(a_scale),
+                                   np.asarray(w_codes) & 0x7F, np.abs(np.asarray(w_sf)))
+
+
+def check_gemm(got_bits, ref_bits, s_abs, what):
+    g = O.bf16_to_f64(got_bits)
+    r = O.bf16_to_f64(ref_bits)
+    assert g.shape == r.shape == s_abs.shape, what
+    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
+    d = np.abs(g - r)
+    tol = bf16_ulp(r) + MFMA_REL * s_abs
+    bad = d > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} elements beyond the bound, worst excess "
+                           f"{(d - tol)[bad].max():.3e}")
+    den = np.linalg.norm(r)
+    rel = np.linalg.norm(d) / den if den > 0 else 0.0
+    assert rel <= 2.0 ** -8, f"{what}: relative Frobenius difference {rel:.3e}"
+    return np.count_nonzero(d) / max(d.size, 1)
+
+
+def _fp8_step(v_over_s):
+    """Spacing of e4m3fn values at |v| (in scale units)."""
+    return np.exp2(np.floor(np.log2(np.maximum(np.abs(v_over_s), 2.0 ** -6))) - 3)
+
+
+def check_requant(got_q, got_sf, ref_q, ref_sf, ref_h32, ue8m0, what):
+    """Isolation: the GPU re-quantized the oracle's own gate_up.
+    <= 1 ULP in <= 0.1% of the elements."""
+    rows, N = ref_q.shape
+    G = N // 128
+    got_sf = got_sf[:, :G]
+    ref_sf = ref_sf[:, :G]
+    ulp = np.abs(fp8_ordinal(got_q) - fp8_ordinal(ref_q))
+    if ue8m0:
+        diff_e = got_sf.astype(int) != ref_sf.astype(int)
+        if diff_e.any():
+            amax = np.abs(ref_h32.reshape(rows, G, 128)).max(axis=2).astype(np.float64)
+            s = np.maximum(amax, np.float32(1e-4)) / 448.0
+            near = np.abs(np.log2(s) - np.round(np.log2(s))) < 2.0 ** -20 * 1.5
+            assert np.all(near[diff_e]), f"{what}: exponent differs away from a power of two"
+            # those groups: compare values at the coarser of the two scales
+            sv_g = np.repeat(O.scale_values(got_sf, True), 128, axis=1)
+            sv_r = np.repeat(O.scale_values(ref_sf, True), 128, axis=1)
+            vg = O.e4m3_decode(got_q) * sv_g
+            vr = O.e4m3_decode(ref_q) * sv_r
+            coarse = np.maximum(sv_g, sv_r)
+            d = np.abs(vg - vr)
+            by_value = np.where(d == 0, 0, np.where(d <= _fp8_step(vr / coarse) * coarse, 1, 2))
+            ulp = np.where(np.repeat(diff_e, 128, axis=1), by_value, ulp)
+    else:
+        rel = np.abs(got_sf.astype(np.float64) - ref_sf.astype(np.float64)) / ref_sf
+        assert rel.max() <= 2.0 ** -21, f"{what}: fp32 scales differ by {rel.max():.3e}"
+    assert ulp.max() <= 1, f"{what}: {np.count_nonzero(ulp > 1)} codes off by more than 1 ULP"
+    frac = np.count_nonzero(ulp) / ulp.size
+    assert frac <= 1e-3, f"{what}: {frac:.4%} of codes differ"
+    return frac
+
+
+def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_gate_up, ue8m0,
+                        what):
+    """End of the GPU's own chain: its gate_up may differ from the oracle's
+    by the GEMM bound; carry that through h = silu(g) * u and allow half an
+    fp8 step of rounding on each side.  Returns the fraction of codes that
+    differ."""
+    rows, N = ref_q.shape
+    G = N // 128
+    gu = O.bf16_to_f64(ref_gate_up_bits)
+    g, u = gu[:, :N], gu[:, N:]
+    dgu = bf16_ulp(gu) + MFMA_REL * s_abs_gate_up
+    dg, du = dgu[:, :N], dgu[:, N:]
+    sig = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sig
+    dsilu = np.abs(sig * (1.0 + g * (1.0 - sig)))
+    dh = (dsilu * np.abs(u) * dg + np.abs(silu) * du + 1.1 * dg * du) * 1.01
+    dh += np.abs(silu * u) * 2.0 ** -20
+    sv_g = np.repeat(O.scale_values(got_sf[:, :G], ue8m0), 128, axis=1)
+    sv_r = np.repeat(O.scale_values(ref_sf[:, :G], ue8m0), 128, axis=1)
+    vg = O.e4m3_decode(got_q) * sv_g
+    vr = O.e4m3_decode(ref_q) * sv_r
+    assert np.all(np.isfinite(vg)), f"{what}: non-finite codes"
+    bound = 0.5 * (_fp8_step(vg / sv_g) * sv_g + _fp8_step(vr / sv_r) * sv_r) + dh
+    bad = np.abs(vg - vr) > bound * 1.000001
+    assert not bad.any(), f"{what}: {bad.sum()} values beyond the propagated bound"
+    if ue8m0:
+        assert np.abs(got_sf[:, :G].astype(int) - ref_sf[:, :G].astype(int)).max() <= 1
+    return np.count_nonzero(got_q != ref_q) / got_q.size
+
+
+def check_output(got_bits, ref_bits, what):
+    g = O.bf16_to_f64(got_bits)
+    r = O.bf16_to_f64(ref_bits)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    den = np.linalg.norm(r)
+    rel = np.linalg.norm(g - r) / den if den > 0 else np.linalg.norm(g)
+    mx = np.abs(g - r).max() if g.size else 0.0
+    ref_max = np.abs(r).max() if r.size else 0.0
+    assert rel <= 1e-2, f"{what}: relative Frobenius {rel:.3e}"
+    assert mx <= 2e-2 * ref_max + (0 if ref_max > 0 else 1e-30), f"{what}: max abs {mx:.3e}"
+    return rel, mx

@@ -1,0 +1,484 @@
+"""GPU parity of every step of the layer against the CPU oracle, through the
+C ABI (libmoe_fp8.so), at sizes the oracle runs in seconds that still span
+several GEMM tiles and ragged tails.
+
+Each step is first run in isolation on the oracle's own inputs for that
+step (so an upstream difference cannot hide a bug), then the whole layer is
+run end to end.  Masked rows of the batched layout and rows past an expert's
+count are poisoned with NaN codes / infinite scales on input and a sentinel
+on output, so reading or writing them fails the test.
+"""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import fp8_block_quantized_group_amd as moe
+import moe_synth
+from oracle import moe_oracle as O
+from parity_util import (abs_gemm, check_bf16_close, check_gemm, check_output, check_requant,
+                         check_requant_chain, to_dev, to_np)
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL_BF16 = 0x7FBF          # a NaN pattern no kernel produces
+SENTINEL_U8 = 0xA5
+
+SMALL = {
+    "tiny": moe_synth.CONFIGS["tiny"],
+    "ragged": moe_synth.custom(name="ragged", T=300, E=5, top_k=3, K=384, N=384, seed=21,
+                               pad_frac=0.07),
+    "batched": moe_synth.custom(name="batched", T=250, E=4, top_k=2, K=384, N=256, seed=22,
+                                layout="batched", max_tokens=160),
+    "eplb_fp32": moe_synth.custom(name="eplb_fp32", T=200, E=7, top_k=4, K=256, N=384,
+                                  seed=23, act_quant="fp32", num_logical=5),
+    "skewed": moe_synth.custom(name="skewed", T=400, E=16, top_k=4, K=256, N=256, seed=24,
+                               routing="zipf", zipf_s=1.1, pad_frac=0.05),
+}
+
+
+@pytest.fixture(scope="session")
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    moe.load_library()
+    return torch.device("cuda:0")
+
+
+_CACHE = {}
+
+
+def case(name):
+    """(cfg, host inputs, device inputs, oracle forward) for a small config."""
+    if name not in _CACHE:
+        cfg = SMALL[name]
+        inp = moe_synth.make_inputs(cfg, "cpu")
+        h = O.host_inputs(inp)
+        ref = O.forward(h)
+        _CACHE[name] = (cfg, h, inp, ref)
+    cfg, h, inp, ref = _CACHE[name]
+    dev = {}
+    for k, v in inp.items():
+        if isinstance(v, torch.Tensor):
+            dev[k] = v.to("cuda")
+        elif k == "eplb" and v is not None:
+            dev[k] = {k2: v2.to("cuda") if isinstance(v2, torch.Tensor) and k2 != "replica_of"
+                      else v2 for k2, v2 in v.items()}
+        else:
+            dev[k] = v
+    return cfg, h, dev, ref
+
+
+def problem(cfg):
+    return moe.Problem.from_config(cfg)
+
+
+def valid_rows(cfg, ref):
+    """Row indices holding routed data (the rest are masked)."""
+    if cfg.layout == "batched":
+        return np.concatenate([np.arange(e * cfg.max_tokens, e * cfg.max_tokens + int(c))
+                               for e, c in enumerate(ref["counts"])]).astype(np.int64)
+    return np.arange(int(ref["offsets"][-1]))
+
+
+def stage_on_gpu(cfg, dev):
+    p = problem(cfg)
+    bufs = moe.alloc_stage_outputs(p)
+    if dev["eplb"] is not None:
+        dev["eplb"]["expert_load"].zero_()
+    moe.stage(p, dev["hidden"], dev["topk_ids"], dev["topk_weights"], bufs,
+              dev["is_padding"], dev["expert_num_tokens"], dev["eplb"])
+    torch.cuda.synchronize()
+    return p, bufs
+
+
+def host_tile_list(counts, tile_m, n_entries):
+    """Every (expert, m0) tile in plain expert order (test plumbing: the GEMM
+    must not depend on the order the routing step emits)."""
+    tl = np.zeros(n_entries, np.int32)
+    pos = 0
+    for e, c in enumerate(counts):
+        for m0 in range(0, int(c), tile_m):
+            tl[1 + 2 * pos], tl[2 + 2 * pos] = e, m0
+            pos += 1
+    tl[0] = pos
+    return tl
+
+
+def oracle_routing(p, cfg, ref):
+    """Device routing arrays built from the oracle's layout."""
+    s = moe.sizes(p)
+    slots = max(s["slots"], 1)
+    row_src = np.zeros(slots, np.int32)
+    row_src[:len(ref["row_src"])] = ref["row_src"]
+    return {
+        "expert_num_tokens": to_dev(ref["counts"].astype(np.int32)),
+        "expert_offsets": to_dev(ref["offsets"].astype(np.int32)),
+        "row_src": to_dev(row_src),
+        "slot_row": to_dev(ref["slot_row"].reshape(-1).astype(np.int32)),
+        "tile_list": to_dev(host_tile_list(ref["counts"], s["tile_m"], s["tile_list"])),
+    }
+
+
+_ABS = {}
+
+
+def gemm_abs(cfg, h, ref, which):
+    """S_abs per output element (the oracle's GEMM on absolute values), for
+    the GEMM tolerance; rows laid out like the oracle's intermediates."""
+    key = (cfg.name, which)
+    if key in _ABS:
+        return _ABS[key]
+    ue = cfg.act_quant == "ue8m0"
+    cols = 2 * cfg.N if which == "w13" else cfg.K
+    out = np.zeros((ref["gate_up"].shape[0], cols))
+    for e, c in enumerate(ref["counts"]):
+        c = int(c)
+        if c == 0:
+            continue
+        if cfg.layout == "batched":
+            rows = np.arange(e * cfg.max_tokens, e * cfg.max_tokens + c)
+            a_rows = rows
+        else:
+            lo = int(ref["offsets"][e])
+            rows = np.arange(lo, lo + c)
+            a_rows = ref["row_src"][rows]
+        if which == "w13":
+            out[rows] = abs_gemm(ref["x_q"][a_rows], O.scale_values(ref["x_sf"][a_rows], ue),
+                                 h["w13"][e], h["w13_sf"][e])
+        else:
+            out[rows] = abs_gemm(ref["a2_q"][rows], O.scale_values(ref["a2_sf"][rows], ue),
+                                 h["w2"][e], h["w2_sf"][e])
+    _ABS[key] = out
+    return out
+
+
+def poisoned(arr, rows, value):
+    """Copy with every row not in `rows` set to `value`."""
+    out = np.full_like(arr, value)
+    out[rows] = arr[rows]
+    return out
+
+
+def sf_poison(ue8m0):
+    return 255 if ue8m0 else np.float32(np.inf)
+
+
+# ---------------------------------------------------------------------------
+# step 1: the group quantizer, exhaustively over bf16
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("ue8m0", [True, False])
+def test_stage_quant_every_bf16_value(gpu, ue8m0):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = np.isfinite(O.bf16_to_f64(bits))
+    vals = bits[finite]
+    n = vals.size
+    # (a) each value alone in its group: every amax the exponent rule can see
+    alone = np.zeros((n, 128), np.uint16)
+    alone[:, 5] = vals
+    # (b) dense groups: 128 consecutive values share one scale
+    dense = np.zeros(((n + 127) // 128) * 128, np.uint16)
+    dense[:n] = vals
+    dense = dense.reshape(-1, 128)
+    for x in (alone, dense):
+        rows = x.shape[0]
+        p = moe.Problem(rows, 128, 128, 1, 1, act_quant=moe.Q_FP8_UE8M0 if ue8m0 else moe.Q_FP8_F32)
+        bufs = moe.alloc_stage_outputs(p)
+        ids = torch.zeros((rows, 1), dtype=torch.int32, device="cuda")
+        w = torch.ones((rows, 1), dtype=torch.float32, device="cuda")
+        moe.stage(p, to_dev(x), ids, w, bufs)
+        torch.cuda.synchronize()
+        q_ref, s_ref = O.quantize_groups(O.bf16_to_f64(x).astype(np.float32), ue8m0)
+        assert np.array_equal(to_np(bufs["x_q"]), q_ref)
+        sf = to_np(bufs["x_sf"])
+        if ue8m0:
+            assert np.array_equal(sf, O.pack_ue8m0_rows(s_ref))
+        else:
+            assert np.array_equal(sf.view(np.uint32), s_ref.view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# step 1-2 on the configs: staging + routing, bit-exact
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_stage_and_route_bit_exact(gpu, name):
+    cfg, h, dev, ref = case(name)
+    p, bufs = stage_on_gpu(cfg, dev)
+    ue = cfg.act_quant == "ue8m0"
+    rows = valid_rows(cfg, ref) if cfg.layout == "batched" else np.arange(cfg.T)
+    assert np.array_equal(to_np(bufs["x_q"])[rows], ref["x_q"][rows])
+    sf = to_np(bufs["x_sf"])[rows]
+    if ue:
+        assert np.array_equal(sf, O.pack_ue8m0_rows(ref["x_sf"][rows]))
+    else:
+        assert np.array_equal(sf.view(np.uint32), ref["x_sf"][rows].view(np.uint32))
+    assert np.array_equal(to_np(bufs["topk_idx"]), ref["ids"])
+    assert np.array_equal(to_np(bufs["topk_w"]).view(np.uint32), ref["weights"].view(np.uint32))
+    assert np.array_equal(to_np(bufs["expert_num_tokens"]), ref["counts"])
+    M = int(ref["offsets"][-1])
+    if cfg.layout != "batched":
+        assert np.array_equal(to_np(bufs["expert_offsets"]), ref["offsets"])
+        assert np.array_equal(to_np(bufs["row_src"])[:M], ref["row_src"])
+    assert np.array_equal(to_np(bufs["slot_row"]).reshape(cfg.T, cfg.top_k), ref["slot_row"])
+    if cfg.eplb:
+        assert np.array_equal(to_np(dev["eplb"]["expert_load"]), ref["load"])
+    # tile schedule: each expert's tiles exactly once, heaviest experts first
+    s = moe.sizes(p)
+    tl = to_np(bufs["tile_list"])
+    n = int(tl[0])
+    pairs = tl[1:1 + 2 * n].reshape(n, 2)
+    bm = s["tile_m"]
+    want = sorted((e, m0) for e, c in enumerate(ref["counts"]) for m0 in range(0, int(c), bm))
+    assert sorted(map(tuple, pairs.tolist())) == want
+    per_expert = [-(-int(ref["counts"][e]) // bm) for e in pairs[:, 0]]
+    assert all(a >= b for a, b in zip(per_expert, per_expert[1:]))
+
+
+def test_stage_bf16_copy(gpu):
+    cfg, h, dev, ref = case("ragged")
+    p = moe.Problem.from_config(cfg, act_quant=moe.Q_BF16)
+    bufs = moe.alloc_stage_outputs(p)
+    moe.stage(p, dev["hidden"], dev["topk_ids"], dev["topk_weights"], bufs, dev["is_padding"])
+    torch.cuda.synchronize()
+    assert torch.equal(bufs["x_q"].view(torch.int16), dev["hidden"].view(torch.int16))
+    assert np.array_equal(to_np(bufs["topk_idx"]), ref["ids"])
+
+
+# ---------------------------------------------------------------------------
+# steps 3-6 in isolation, on the oracle's inputs
+# ---------------------------------------------------------------------------
+
+def _gemm_isolated(cfg, h, dev, ref, which):
+    p = problem(cfg)
+    s = moe.sizes(p)
+    ue = cfg.act_quant == "ue8m0"
+    routing = oracle_routing(p, cfg, ref)
+    vr = valid_rows(cfg, ref)
+    if which == "w13":
+        arows = (np.arange(s["stage_rows"]) if cfg.layout != "batched" else vr)
+        a_q = poisoned(ref["x_q"], arows, 0x7F)
+        a_sf = ref["x_sf"]
+        a_sf = O.pack_ue8m0_rows(a_sf) if ue else a_sf
+        a_sf = poisoned(a_sf, arows, sf_poison(ue))
+        cols = 2 * cfg.N
+        want = ref["gate_up"]
+    else:
+        a_q = np.full((s["expert_rows"], cfg.N), 0x7F, np.uint8)
+        a_q[vr] = ref["a2_q"][vr]
+        a_sf = O.pack_ue8m0_rows(ref["a2_sf"]) if ue else ref["a2_sf"]
+        a_sf = poisoned(a_sf, vr, sf_poison(ue))
+        cols = cfg.K
+        want = ref["down"]
+    out = torch.full((s["expert_rows"], cols), SENTINEL_BF16, dtype=torch.int16,
+                     device="cuda").view(torch.bfloat16)
+    w = dev["w13"] if which == "w13" else dev["w2"]
+    w_sf = dev["w13_sf"] if which == "w13" else dev["w2_sf"]
+    fn = moe.grouped_gemm_w13 if which == "w13" else moe.grouped_gemm_w2
+    fn(p, to_dev(a_q), to_dev(a_sf), routing, w, w_sf, out)
+    torch.cuda.synchronize()
+    got = to_np(out)
+    frac = check_gemm(got[vr], want[vr], gemm_abs(cfg, h, ref, which)[vr], f"{cfg.name} {which}")
+    print(f"{cfg.name} {which}: {frac:.3%} of bf16 outputs differ from the oracle's")
+    untouched = np.setdiff1d(np.arange(s["expert_rows"]), vr)
+    assert np.all(got[untouched] == SENTINEL_BF16), "rows outside the experts' counts written"
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_gemm_w13_isolated(gpu, name):
+    cfg, h, dev, ref = case(name)
+    _gemm_isolated(cfg, h, dev, ref, "w13")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_gemm_w2_isolated(gpu, name):
+    cfg, h, dev, ref = case(name)
+    _gemm_isolated(cfg, h, dev, ref, "w2")
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_act_requant_isolated(gpu, name):
+    cfg, h, dev, ref = case(name)
+    p = problem(cfg)
+    s = moe.sizes(p)
+    ue = cfg.act_quant == "ue8m0"
+    vr = valid_rows(cfg, ref)
+    gu = np.full((s["expert_rows"], 2 * cfg.N), 0x7FC0, np.uint16)   # NaN outside
+    gu[vr] = ref["gate_up"][vr]
+    routing = oracle_routing(p, cfg, ref)
+    a2_q = torch.full((s["expert_rows"], cfg.N), SENTINEL_U8, dtype=torch.uint8, device="cuda")
+    a2_sf = (torch.zeros((s["expert_rows"], s["a2_sf_row"]), dtype=torch.uint8, device="cuda")
+             if ue else torch.zeros((s["expert_rows"], s["a2_sf_row"]), dtype=torch.float32,
+                                    device="cuda"))
+    moe.act_requant(p, to_dev(gu), routing, a2_q, a2_sf)
+    torch.cuda.synchronize()
+    got_q, got_sf = to_np(a2_q), to_np(a2_sf)
+    h32 = O.silu_mul_f32(ref["gate_up"][vr], cfg.N)
+    check_requant(got_q[vr], got_sf[vr], ref["a2_q"][vr], ref["a2_sf"][vr], h32, ue,
+                  f"{name} act_requant")
+    if ue:
+        G = cfg.N // 128
+        assert np.all(got_sf[vr][:, G:] == 0), "pad bytes of the scale rows must be zero"
+    untouched = np.setdiff1d(np.arange(s["expert_rows"]), vr)
+    assert np.all(got_q[untouched] == SENTINEL_U8)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_topk_reduce_isolated(gpu, name):
+    cfg, h, dev, ref = case(name)
+    p = problem(cfg)
+    s = moe.sizes(p)
+    vr = valid_rows(cfg, ref)
+    down = np.full((s["expert_rows"], cfg.K), 0x7FC0, np.uint16)     # NaN outside
+    down[vr] = ref["down"][vr]
+    out = torch.empty((cfg.T, cfg.K), dtype=torch.bfloat16, device="cuda")
+    moe.topk_reduce(p, to_dev(down), to_dev(ref["slot_row"].astype(np.int32)),
+                    to_dev(ref["weights"]), out)
+    torch.cuda.synchronize()
+    check_bf16_close(to_np(out), ref["out"], f"{name} reduce")
+
+
+# ---------------------------------------------------------------------------
+# the whole layer
+# ---------------------------------------------------------------------------
+
+def run_chain(cfg, dev):
+    """moe_stage -> w13 -> act_requant -> w2 -> reduce through the separate
+    entry points; returns every intermediate."""
+    p, bufs = stage_on_gpu(cfg, dev)
+    s = moe.sizes(p)
+    ue = cfg.act_quant == "ue8m0"
+    gate_up = torch.full((s["expert_rows"], 2 * cfg.N), SENTINEL_BF16, dtype=torch.int16,
+                         device="cuda").view(torch.bfloat16)
+    moe.grouped_gemm_w13(p, bufs["x_q"], bufs["x_sf"], bufs, dev["w13"], dev["w13_sf"], gate_up)
+    a2_q = torch.full((s["expert_rows"], cfg.N), SENTINEL_U8, dtype=torch.uint8, device="cuda")
+    a2_sf = torch.zeros((s["expert_rows"], s["a2_sf_row"]),
+                        dtype=torch.uint8 if ue else torch.float32, device="cuda")
+    moe.act_requant(p, gate_up, bufs, a2_q, a2_sf)
+    down = torch.full((s["expert_rows"], cfg.K), SENTINEL_BF16, dtype=torch.int16,
+                      device="cuda").view(torch.bfloat16)
+    moe.grouped_gemm_w2(p, a2_q, a2_sf, bufs, dev["w2"], dev["w2_sf"], down)
+    out = torch.empty((cfg.T, cfg.K), dtype=torch.bfloat16, device="cuda")
+    moe.topk_reduce(p, down, bufs["slot_row"], bufs["topk_w"], out)
+    torch.cuda.synchronize()
+    return {"bufs": bufs, "gate_up": gate_up, "a2_q": a2_q, "a2_sf": a2_sf, "down": down,
+            "out": out}
+
+
+def run_forward(cfg, dev):
+    p = problem(cfg)
+    layer = moe.MoeLayer(p, dev["w13"], dev["w13_sf"], dev["w2"], dev["w2_sf"])
+    if dev["eplb"] is not None:
+        dev["eplb"]["expert_load"].zero_()
+    out = layer(dev["hidden"], dev["topk_ids"], dev["topk_weights"], None, dev["is_padding"],
+                dev["expert_num_tokens"], dev["eplb"])
+    torch.cuda.synchronize()
+    return out
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_end_to_end(gpu, name):
+    cfg, h, dev, ref = case(name)
+    ue = cfg.act_quant == "ue8m0"
+    chain = run_chain(cfg, dev)
+    vr = valid_rows(cfg, ref)
+    frac = check_requant_chain(to_np(chain["a2_q"])[vr], to_np(chain["a2_sf"])[vr],
+                               ref["a2_q"][vr], ref["a2_sf"][vr], ref["gate_up"][vr],
+                               gemm_abs(cfg, h, ref, "w13")[vr], ue, f"{name} a2 (chain)")
+    print(f"{name}: {frac:.3%} of a2 codes differ at the end of the GPU chain")
+    check_output(to_np(chain["out"]), ref["out"], f"{name} chained output")
+    out = run_forward(cfg, dev)
+    check_output(to_np(out), ref["out"], f"{name} moe_forward output")
+    # moe_forward runs the same kernels: identical bits; and it is deterministic
+    assert torch.equal(out.view(torch.int16), chain["out"].view(torch.int16))
+    out2 = run_forward(cfg, dev)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    if cfg.eplb:
+        assert np.array_equal(to_np(dev["eplb"]["expert_load"]), ref["load"])
+    if cfg.pad_frac > 0:
+        pad = h["is_padding"].astype(bool)
+        assert np.all(to_np(out)[pad] == 0)
+
+
+@pytest.mark.parametrize("tile_m", [16, 32, 64, 128])
+def test_every_tile_height(gpu, tile_m, monkeypatch):
+    monkeypatch.setenv("MOE_TILE_M", str(tile_m))
+    for name in ("ragged", "batched"):
+        cfg, h, dev, ref = case(name)
+        assert moe.sizes(problem(cfg))["tile_m"] == tile_m
+        chain = run_chain(cfg, dev)
+        vr = valid_rows(cfg, ref)
+        check_gemm(to_np(chain["gate_up"])[vr], ref["gate_up"][vr],
+                   gemm_abs(cfg, h, ref, "w13")[vr], f"{name} gate_up tile_m={tile_m}")
+        check_output(to_np(chain["out"]), ref["out"], f"{name} out tile_m={tile_m}")
+
+
+# ---------------------------------------------------------------------------
+# degenerate inputs
+# ---------------------------------------------------------------------------
+
+def _layer_out(cfg, inp):
+    dev = {k: (v.to("cuda") if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    return to_np(run_forward(cfg, dev))
+
+
+def test_empty_batch_noop(gpu):
+    p = moe.Problem(0, 256, 512, 4, 2)
+    out = torch.full((1, 256), 3, dtype=torch.bfloat16, device="cuda")
+    moe.forward(p, out, torch.zeros((1, 2), dtype=torch.int32, device="cuda"),
+                torch.zeros((1, 2), device="cuda"), out, out, out, out, out,
+                torch.empty(256, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.all(out == 3)
+
+
+def test_all_tokens_padding_or_unrouted(gpu):
+    cfg = moe_synth.custom(name="pad_all", T=40, E=3, top_k=2, K=256, N=256, seed=31)
+    inp = moe_synth.make_inputs(cfg, "cpu")
+    inp["is_padding"] = torch.ones(cfg.T, dtype=torch.uint8)
+    assert np.all(_layer_out(cfg, inp) == 0)
+    inp["is_padding"] = None
+    ids = inp["topk_ids"].clone()
+    ids[:, 0] = -1
+    ids[:, 1] = cfg.E + 5                 # out of range: unrouted, not an error
+    inp["topk_ids"] = ids
+    assert np.all(_layer_out(cfg, inp) == 0)
+
+
+def test_single_token_and_invalid_ids(gpu):
+    cfg = moe_synth.custom(name="one", T=1, E=6, top_k=3, K=256, N=256, seed=32)
+    inp = moe_synth.make_inputs(cfg, "cpu")
+    h = O.host_inputs(inp)
+    check_output(_layer_out(cfg, inp), O.forward(h)["out"], "single token")
+    cfg2 = moe_synth.custom(name="invalid", T=64, E=6, top_k=3, K=256, N=256, seed=33)
+    inp2 = moe_synth.make_inputs(cfg2, "cpu")
+    ids = inp2["topk_ids"].clone()
+    ids[::3, 1] = -7
+    ids[1::5, 2] = 99
+    inp2["topk_ids"] = ids
+    h2 = O.host_inputs(inp2)
+    check_output(_layer_out(cfg2, inp2), O.forward(h2)["out"], "invalid ids")
+
+
+def test_batched_empty_slabs_and_garbage(gpu):
+    cfg = moe_synth.custom(name="slabs", T=30, E=6, top_k=1, K=256, N=256, seed=34,
+                           layout="batched", max_tokens=48)
+    inp = moe_synth.make_inputs(cfg, "cpu")
+    # route every token to experts 1 and 4 only: the other slabs are empty
+    inp["topk_ids"] = torch.where(torch.arange(cfg.T)[:, None] % 2 == 0,
+                                  torch.tensor(1), torch.tensor(4)).to(torch.int32)
+    inp.update(moe_synth._stage_batched(cfg, inp["tokens"], inp["topk_ids"], "cpu"))
+    h = O.host_inputs(inp)
+    check_output(_layer_out(cfg, inp), O.forward(h)["out"], "batched with empty slabs")
+
+
+def test_expert_count_multiple_of_tile(gpu, monkeypatch):
+    """Counts landing exactly on tile boundaries (no ragged tail)."""
+    monkeypatch.setenv("MOE_TILE_M", "32")
+    cfg = moe_synth.custom(name="exact", T=128, E=4, top_k=1, K=256, N=256, seed=35)
+    inp = moe_synth.make_inputs(cfg, "cpu")
+    inp["topk_ids"] = (torch.arange(cfg.T) // 32).to(torch.int32)[:, None].contiguous()
+    h = O.host_inputs(inp)
+    check_output(_layer_out(cfg, inp), O.forward(h)["out"], "exact tiles")
