@@ -19,16 +19,28 @@
 //    (activation row) and 4*TN consecutive output columns after a fixed
 //    permutation of the weight rows inside the wave tile; the epilogue then
 //    writes 16-32 contiguous bytes per lane.
+//  * Operand tiles travel HBM -> LDS with buffer_load_dwordx4 ... lds
+//    (no register staging) through a ring of STAGES k-steps, so STAGES-1
+//    k-steps (up to ~96 KB per CU) are in flight while one is multiplied:
+//    enough outstanding bytes to cover HBM latency, which is what bounds a
+//    weight-streaming GEMM.  The fragment reads from LDS are inline
+//    ds_read_b128 so that the compiler, which cannot tell the ring slots
+//    apart, does not drain every outstanding load before each read; the
+//    waits are placed by hand (vmcnt per stage, one barrier per k-step).
+//  * Activation rows past an expert's count get an out-of-range buffer
+//    offset: they read as zeros and never reach an output.  Rows of a
+//    batched-masked slab past its count are therefore never read.
 //  * Work unit = (expert, 128-column weight tile, BM-row activation tile).
 //    The tile list comes from the routing step, heaviest experts first;
 //    grid.x runs over weight tiles, so the tiles of one expert that share a
 //    weight tile land on the same XCD (grid.x is a multiple of 8 for every
 //    supported width) and re-read it from that XCD's L2.
-//  * Rows beyond an expert's count are never loaded (zero-filled in LDS) or
-//    stored; the garbage rows of a batched-masked slab never reach an output.
-//  * LDS: A tile [BM][128] and B tile [128][128] fp8, double buffered, 16-byte
-//    chunks XOR-swizzled per row so the MFMA fragment reads spread across
-//    banks.  Global loads for k-step kb+1 are in flight while kb computes.
+//  * LDS rows are 128 bytes; 16-byte chunks are XOR-swizzled per row so that
+//    the fragment reads of a wave spread over the banks.
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -37,49 +49,157 @@ namespace moe {
 namespace {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kBN = 128;       // weight rows (output columns) per tile
-constexpr int kRowBytes = 128; // one k-step of a row: 128 fp8 values
+constexpr int kRowBytes = 128;      // one k-step of a row: 128 fp8 values
+constexpr uint32_t kOutOfRange = 0xF0000000u;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
+constexpr int kMaxGroups = 256;                // reduction length <= 32768
 
-template <int BM>
+// Tile geometry.  BM activation rows x BN weight rows (output columns) per
+// block, NW waves arranged WN x WM, each owning a WAVE_N x WAVE_M sub-tile
+// of TN x TM 16x16 MFMA tiles.  STAGES k-steps of the LDS ring.
+template <int BM_, int BN_, int NW_, int STAGES_>
 struct Shape {
+  static constexpr int BM = BM_, BN = BN_, NW = NW_, STAGES = STAGES_;
+  static constexpr int THREADS = 64 * NW;
   static constexpr int WM = BM >= 64 ? 2 : 1;        // waves along activation rows
-  static constexpr int WN = 4 / WM;                  // waves along weight rows
-  static constexpr int WAVE_N = kBN / WN;            // 64 or 32
-  static constexpr int WAVE_M = BM / WM;             // 64, 32, 32, 16
-  static constexpr int TN = WAVE_N / 16;             // 16-row MFMA sub-tiles along N
-  static constexpr int TM = WAVE_M / 16;             // sub-tiles along M
-  static constexpr int LOG_4TN = TN == 4 ? 4 : (TN == 2 ? 3 : 2);
-  static constexpr int A_CHUNKS = BM * 8;            // 16-byte chunks per k-step
-  static constexpr int A_ITERS = A_CHUNKS >= 256 ? A_CHUNKS / 256 : 1;
-  static constexpr int B_ITERS = kBN * 8 / 256;
-  static constexpr int TILE_BYTES = (BM + kBN) * kRowBytes;
+  static constexpr int WN = NW / WM;                 // waves along weight rows
+  static constexpr int WAVE_N = BN / WN;
+  static constexpr int WAVE_M = BM / WM;
+  static constexpr int TN = WAVE_N / 16;
+  static constexpr int TM = WAVE_M / 16;
+  static_assert(TN == 2 || TN == 4, "wave tile rows");
+  static_assert(TM >= 1 && TM <= 4, "wave tile columns");
+  static_assert(WAVE_N <= 128, "a wave's columns share one weight-scale block");
+  static constexpr int LOG_4TN = TN == 4 ? 4 : 3;
+  static constexpr int A_BYTES = BM * kRowBytes;
+  static constexpr int B_BYTES = BN * kRowBytes;
+  static constexpr int SC_WAVES = (BM + 63) / 64;          // waves that load row scales
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SC_WAVES * 256;
+  static constexpr int NBLK = BN / 128;                    // weight-scale blocks per tile
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + NBLK * kMaxGroups * 4;
+  // one buffer_load ... lds instruction moves 64 lanes x 16 bytes = 1 KB
+  static constexpr int A_CHUNKS = BM * 8;
+  static constexpr int A_INSTR = A_CHUNKS >= THREADS ? A_CHUNKS / THREADS : 1;
+  static constexpr int A_WAVES = A_CHUNKS >= THREADS ? NW : A_CHUNKS / 64;
+  static constexpr int B_INSTR = BN * 8 / THREADS;
+  static constexpr int BLOCKS_PER_CU = (2 * LDS_BYTES <= 160 * 1024) ? 2 : 1;
+  static constexpr int MIN_WAVES_PER_EU = BLOCKS_PER_CU * NW / 4;
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds the CU's LDS");
+  static_assert(B_INSTR * THREADS == BN * 8, "weight tile split");
+  // buffer loads into LDS a wave issues per k-step
+  template <int W>
+  static constexpr int loads() {
+    return (W < A_WAVES ? A_INSTR : 0) + B_INSTR + (W < SC_WAVES ? 1 : 0);
+  }
 };
 
-// 16-byte chunk c of row r lives at chunk position c ^ key(r).
-__device__ __forceinline__ int key_a(int r) { return r & 7; }
+// 16-byte chunk c of row r lives at chunk position c ^ key(r).  The keys
+// make every ds_read_b128 of a fragment hit distinct 16-byte bank groups,
+// both per 8-lane phase (32 banks) and per 16-lane phase (64 banks):
+// activation fragments read 16 consecutive rows, weight fragments the rows
+// (rho>>2) * 4TN + (rho&3) after the output-column permutation.
+__device__ __forceinline__ int key_a(int r) { return (r & 6) | ((r ^ (r >> 3)) & 1); }
 template <int LOG_4TN>
-__device__ __forceinline__ int key_b(int r) { return (r & 3) | (((r >> LOG_4TN) & 1) << 2); }
+__device__ __forceinline__ int key_b(int r) {
+  return ((r ^ (r >> (LOG_4TN + 1))) & 1) | (r & 2) | (((r >> LOG_4TN) & 1) << 2);
+}
 
-template <int BM, bool UE8M0>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(const GemmArgs p) {
-  using S = Shape<BM>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2][S::TILE_BYTES];
+// ---- LDS ring synchronisation ------------------------------------------
+// The ring is filled by buffer_load ... lds issued from inline asm, so the
+// compiler does not know LDS is written behind its back and neither drains
+// the outstanding loads before every LDS read nor reorders around them: the
+// waits below (asm with a memory clobber) are the only synchronisation.
+// vmcnt counts only these loads inside the main loop (every other operand
+// comes from LDS), so "at most N outstanding" means "all but the last N
+// issued have landed".
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
+// Wait until at most N of this wave's LDS-bound loads are in flight and its
+// own LDS reads have completed, then barrier.
+template <int N>
+__device__ __forceinline__ void wait_then_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
+#endif
+}
+
+// `after` = how many later k-steps (L loads each) may still be in flight.
+template <int L>
+__device__ __forceinline__ void wait_stages(int after) {
+  if (after <= 0)
+    wait_then_barrier<0>();
+  else if (after == 1)
+    wait_then_barrier<L>();
+  else if (after == 2)
+    wait_then_barrier<2 * L>();
+  else
+    wait_then_barrier<3 * L>();
+}
+
+// vmcnt is per wave and waves issue different numbers of loads per k-step.
+template <class S, int W = 0>
+__device__ __forceinline__ void stage_landed(int wave, int after) {
+  if constexpr (W + 1 < S::NW) {
+    if (wave != W) {
+      stage_landed<S, W + 1>(wave, after);
+      return;
+    }
+  }
+  wait_stages<S::template loads<W>()>(after);
+}
+
+// Raw buffer resource over [base, base + num_records): offsets at or past
+// num_records read zeros.  Kept in SGPRs.
+__device__ __forceinline__ v4i buffer_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t b = (uint64_t)base;
+  return v4i{__builtin_amdgcn_readfirstlane((int)(uint32_t)b),
+             __builtin_amdgcn_readfirstlane((int)((b >> 32) & 0xFFFFu)),
+             __builtin_amdgcn_readfirstlane((int)num_records), (int)kRsrcWord3};
+}
+
+// HBM -> LDS: lane l's 16 (4) bytes at rsrc + voffset land at lds + 16*l (4*l).
+__device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               ::"s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
+#endif
+}
+__device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voffset) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               ::"s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
+#endif
+}
+#pragma clang diagnostic pop
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+template <class S, bool UE8M0>
+__global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_kernel(
+    const GemmArgs p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS_BYTES];
 
   const int tile = blockIdx.y;
   if (tile >= p.tile_list[0]) return;
   const int e = p.tile_list[1 + 2 * tile];
   const int m0 = p.tile_list[2 + 2 * tile];
-  const int n0 = blockIdx.x * kBN;
+  const int n0 = blockIdx.x * S::BN;
   int cnt = p.counts[e];
   if (p.offsets == nullptr) cnt = min(cnt, p.max_tokens);
-  const int rows_here = min(BM, cnt - m0);
+  const int rows_here = min(S::BM, cnt - m0);
   const int64_t base = p.offsets != nullptr ? (int64_t)p.offsets[e] : (int64_t)e * p.max_tokens;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wn = wave % S::WN;
   const int wm = wave / S::WN;
   const int G = p.Kd / kGroup;
@@ -89,87 +209,80 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(const GemmArgs p) 
     return p.row_src != nullptr ? (int64_t)p.row_src[r] : r;
   };
 
-  // ---- global -> register -> LDS copy plan -----------------------------
-  const uint8_t* a_src[S::A_ITERS];
-  int a_lds[S::A_ITERS];
-  bool a_on[S::A_ITERS];
+  // ---- HBM -> LDS copy plan: thread tid fills 16-byte slot i*THREADS + tid
+  const v4i rs_a = buffer_rsrc(p.a, p.a_bytes);
+  const v4i rs_b = buffer_rsrc(p.w + ((int64_t)e * p.Nout + n0) * p.Kd, (uint32_t)(S::BN * p.Kd));
+  const v4i rs_s = buffer_rsrc(p.a_sf, p.a_sf_bytes);
+  const bool loads_a = wave < S::A_WAVES;
+  uint32_t a_off[S::A_INSTR];
 #pragma unroll
-  for (int i = 0; i < S::A_ITERS; ++i) {
-    const int chunk = tid + i * 256;
-    const int r = chunk >> 3, c = chunk & 7;
-    a_on[i] = chunk < S::A_CHUNKS;
-    const bool live = a_on[i] && r < rows_here;
-    a_src[i] = live ? p.a + a_row_of(r) * p.Kd + c * 16 : nullptr;
-    a_lds[i] = r * kRowBytes + ((c ^ key_a(r)) << 4);
+  for (int i = 0; i < S::A_INSTR; ++i) {
+    const int slot = i * S::THREADS + tid;
+    const int r = slot >> 3, c = (slot & 7) ^ key_a(slot >> 3);
+    a_off[i] = (loads_a && r < rows_here) ? (uint32_t)(a_row_of(r) * p.Kd + c * 16) : kOutOfRange;
   }
-  const uint8_t* b_src[S::B_ITERS];
-  int b_lds[S::B_ITERS];
-  const uint8_t* w_e = p.w + ((int64_t)e * p.Nout + n0) * p.Kd;
+  uint32_t b_off[S::B_INSTR];
 #pragma unroll
-  for (int i = 0; i < S::B_ITERS; ++i) {
-    const int chunk = tid + i * 256;
-    const int r = chunk >> 3, c = chunk & 7;
-    b_src[i] = w_e + (int64_t)r * p.Kd + c * 16;
-    b_lds[i] = BM * kRowBytes + r * kRowBytes + ((c ^ key_b<S::LOG_4TN>(r)) << 4);
+  for (int i = 0; i < S::B_INSTR; ++i) {
+    const int slot = i * S::THREADS + tid;
+    const int r = slot >> 3, c = (slot & 7) ^ key_b<S::LOG_4TN>(slot >> 3);
+    b_off[i] = (uint32_t)(r * p.Kd + c * 16);
   }
-  const float* sw_row = p.w_sf + ((int64_t)e * (p.Nout / kGroup) + n0 / kGroup) * G;
+  // activation scales: one 4-byte word per row and k-step (UE8M0: the word
+  // holding the step's exponent byte; fp32: the scale itself)
+  const bool loads_sc = wave < S::SC_WAVES;
+  uint32_t sc_off = kOutOfRange;
+  {
+    const int r = wave * 64 + lane;
+    if (loads_sc && r < rows_here)
+      sc_off = (uint32_t)(a_row_of(r) * p.a_sf_stride * (UE8M0 ? 1 : 4));
+  }
+  const int wave_slot = __builtin_amdgcn_readfirstlane(wave * 1024);
+  const int wave_sc = __builtin_amdgcn_readfirstlane(wave * 256);
+  // weight block scales of this tile's NBLK 128-column blocks, one per k-step
+  float* sw_panel = reinterpret_cast<float*>(smem + S::STAGES * S::STAGE_BYTES);
+  for (int i = tid; i < S::NBLK * G; i += S::THREADS) {
+    const int b = i / G, g = i - b * G;
+    sw_panel[b * kMaxGroups + g] =
+        p.w_sf[((int64_t)e * (p.Nout / kGroup) + n0 / kGroup + b) * G + g];
+  }
+  __syncthreads();
 
-  // ---- per-lane MFMA fragment addresses --------------------------------
+  // ---- per-lane MFMA fragment offsets (within a stage) -------------------
   const int rho = lane & 15;
   const int kq = lane >> 4;
-  int wf_off[S::TN];
-#pragma unroll
-  for (int i = 0; i < S::TN; ++i) {
-    const int nl = wn * S::WAVE_N + (rho >> 2) * (4 * S::TN) + i * 4 + (rho & 3);
-    wf_off[i] = BM * kRowBytes + nl * kRowBytes;
-  }
-  const int kb_sw = key_b<S::LOG_4TN>(wn * S::WAVE_N + (rho >> 2) * (4 * S::TN) + (rho & 3));
-  int af_off[S::TM];
-  int af_key[S::TM];
-  // activation scale source per sub-tile column (this lane's output row)
-  const uint8_t* sa_u8[S::TM];
-  const float* sa_f32[S::TM];
+  const int c0 = 2 * kq, c1 = 2 * kq + 1;
+  // weight sub-tile i's row for this lane is nl0 + 4*i (same swizzle key)
+  const int nl0 = wn * S::WAVE_N + (rho >> 2) * (4 * S::TN) + (rho & 3);
+  const int kbw = key_b<S::LOG_4TN>(nl0);
+  const int w_frag0 = S::A_BYTES + nl0 * kRowBytes + ((c0 ^ kbw) << 4);
+  const int w_frag1 = S::A_BYTES + nl0 * kRowBytes + ((c1 ^ kbw) << 4);
+  // activation sub-tile j's row is ml0 + 16*j (same swizzle key)
+  const int ml0 = wm * S::WAVE_M + rho;
+  const int a_frag0 = ml0 * kRowBytes + ((c0 ^ key_a(ml0)) << 4);
+  const int a_frag1 = ml0 * kRowBytes + ((c1 ^ key_a(ml0)) << 4);
+  const int sc_frag = S::A_BYTES + S::B_BYTES + ml0 * 4;
   bool m_live[S::TM];
 #pragma unroll
-  for (int j = 0; j < S::TM; ++j) {
-    const int ml = wm * S::WAVE_M + j * 16 + rho;
-    af_off[j] = ml * kRowBytes;
-    af_key[j] = key_a(ml);
-    m_live[j] = ml < rows_here;
-    const int64_t ar = m_live[j] ? a_row_of(ml) : 0;
-    sa_u8[j] = (const uint8_t*)p.a_sf + ar * p.a_sf_stride;
-    sa_f32[j] = (const float*)p.a_sf + ar * p.a_sf_stride;
-  }
+  for (int j = 0; j < S::TM; ++j) m_live[j] = ml0 + 16 * j < rows_here;
+  const uint32_t smem_base = lds_addr(smem);
+  const float* sw_mine = sw_panel + ((wn * S::WAVE_N) / 128) * kMaxGroups;
 
-  uint4 a_reg[S::A_ITERS];
-  uint4 b_reg[S::B_ITERS];
-  float sa_next[S::TM];
-  float sw_next;
-
-  auto load_global = [&](int kb) {
+  auto issue = [&](int kb) {
+    const uint32_t st = smem_base + (kb % S::STAGES) * S::STAGE_BYTES;
+    const uint32_t koff = (uint32_t)kb * kRowBytes;
+    if (loads_a) {
 #pragma unroll
-    for (int i = 0; i < S::A_ITERS; ++i)
-      a_reg[i] = a_src[i] != nullptr
-                     ? *reinterpret_cast<const uint4*>(a_src[i] + kb * kRowBytes)
-                     : make_uint4(0, 0, 0, 0);
-#pragma unroll
-    for (int i = 0; i < S::B_ITERS; ++i)
-      b_reg[i] = *reinterpret_cast<const uint4*>(b_src[i] + kb * kRowBytes);
-#pragma unroll
-    for (int j = 0; j < S::TM; ++j) {
-      float s = 0.0f;
-      if (m_live[j]) s = UE8M0 ? __uint_as_float((uint32_t)sa_u8[j][kb] << 23) : sa_f32[j][kb];
-      sa_next[j] = s;
+      for (int i = 0; i < S::A_INSTR; ++i)
+        dma16(rs_a, st + i * S::THREADS * 16 + wave_slot, a_off[i] + koff);
     }
-    sw_next = sw_row[kb];
-  };
-  auto store_lds = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < S::A_ITERS; ++i)
-      if (a_on[i]) *reinterpret_cast<uint4*>(&smem[buf][a_lds[i]]) = a_reg[i];
-#pragma unroll
-    for (int i = 0; i < S::B_ITERS; ++i)
-      *reinterpret_cast<uint4*>(&smem[buf][b_lds[i]]) = b_reg[i];
+    for (int i = 0; i < S::B_INSTR; ++i)
+      dma16(rs_b, st + S::A_BYTES + i * S::THREADS * 16 + wave_slot, b_off[i] + koff);
+    if (loads_sc) {
+      const uint32_t soff = UE8M0 ? (uint32_t)(kb & ~3) : (uint32_t)kb * 4;
+      dma4(rs_s, st + S::A_BYTES + S::B_BYTES + wave_sc, sc_off + soff);
+    }
   };
 
   v4f acc[S::TN][S::TM];
@@ -178,60 +291,57 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(const GemmArgs p) 
 #pragma unroll
     for (int j = 0; j < S::TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  load_global(0);
-  store_lds(0);
-  float sa_cur[S::TM];
-  float sw_cur;
-#pragma unroll
-  for (int j = 0; j < S::TM; ++j) sa_cur[j] = sa_next[j];
-  sw_cur = sw_next;
-  __syncthreads();
-
-  for (int kb = 0; kb < G; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < G) load_global(kb + 1);
-
-    const uint8_t* sb = smem[buf];
-    v8i wf[S::TN];
-    v8i af[S::TM];
-    const int c0 = 2 * kq, c1 = 2 * kq + 1;
+  // One k-step: TN*TM MFMAs (one per 16x16 sub-tile, K = 128 = one scale
+  // block), each partial promoted into the fp32 accumulator two MFMAs later,
+  // once it has left the matrix pipe.
+  auto compute = [&](int kb) {
+    const uint8_t* sb = smem + (kb % S::STAGES) * S::STAGE_BYTES;
+    v8i wf[S::TN], af[S::TM];
 #pragma unroll
     for (int i = 0; i < S::TN; ++i) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(sb + wf_off[i] + ((c0 ^ kb_sw) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(sb + wf_off[i] + ((c1 ^ kb_sw) << 4));
-      wf[i] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
-                  (int)hi.w};
+      const v4i lo = *reinterpret_cast<const v4i*>(sb + w_frag0 + i * 4 * kRowBytes);
+      const v4i hi = *reinterpret_cast<const v4i*>(sb + w_frag1 + i * 4 * kRowBytes);
+      wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
     }
+    float fs[S::TM];
+    const float sw = sw_mine[kb];
 #pragma unroll
     for (int j = 0; j < S::TM; ++j) {
-      const uint4 lo = *reinterpret_cast<const uint4*>(sb + af_off[j] + ((c0 ^ af_key[j]) << 4));
-      const uint4 hi = *reinterpret_cast<const uint4*>(sb + af_off[j] + ((c1 ^ af_key[j]) << 4));
-      af[j] = v8i{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z,
-                  (int)hi.w};
+      const v4i lo = *reinterpret_cast<const v4i*>(sb + a_frag0 + j * 16 * kRowBytes);
+      const v4i hi = *reinterpret_cast<const v4i*>(sb + a_frag1 + j * 16 * kRowBytes);
+      af[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      const uint32_t word = *reinterpret_cast<const uint32_t*>(sb + sc_frag + j * 64);
+      const float sa = UE8M0 ? __uint_as_float(((word >> ((kb & 3) * 8)) & 0xFFu) << 23)
+                             : __uint_as_float(word);
+      fs[j] = m_live[j] ? sa * sw : 0.0f;
     }
-    float f[S::TM];
+    constexpr int NT = S::TN * S::TM;
+    v4f part[3];
 #pragma unroll
-    for (int j = 0; j < S::TM; ++j) f[j] = sa_cur[j] * sw_cur;
-#pragma unroll
-    for (int i = 0; i < S::TN; ++i) {
-#pragma unroll
-      for (int j = 0; j < S::TM; ++j) {
+    for (int t = 0; t < NT + 2; ++t) {
+      if (t < NT) {
         const v4f z = {0.f, 0.f, 0.f, 0.f};
-        const v4f part =
-            __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], af[j], z, 0, 0, 0, 0, 0, 0);
-        acc[i][j][0] = fmaf(part[0], f[j], acc[i][j][0]);
-        acc[i][j][1] = fmaf(part[1], f[j], acc[i][j][1]);
-        acc[i][j][2] = fmaf(part[2], f[j], acc[i][j][2]);
-        acc[i][j][3] = fmaf(part[3], f[j], acc[i][j][3]);
+        part[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            wf[t / S::TM], af[t % S::TM], z, 0, 0, 0, 0, 0, 0);
+      }
+      if (t >= 2) {
+        const int u = t - 2, i = u / S::TM, j = u % S::TM;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[u % 3][r], fs[j], acc[i][j][r]);
       }
     }
-    if (kb + 1 < G) {
-      store_lds(buf ^ 1);
+  };
+
+  // prologue: STAGES-1 k-steps in flight
 #pragma unroll
-      for (int j = 0; j < S::TM; ++j) sa_cur[j] = sa_next[j];
-      sw_cur = sw_next;
-    }
-    __syncthreads();
+  for (int s = 0; s < S::STAGES - 1; ++s)
+    if (s < G) issue(s);
+  for (int kb = 0; kb < G; ++kb) {
+    // k-step kb has landed for every wave, and every wave's reads of k-step
+    // kb-1 (whose slot the next issue reuses) have completed
+    stage_landed<S>(wave, min(kb + S::STAGES - 2, G - 1) - kb);
+    if (kb + S::STAGES - 1 < G) issue(kb + S::STAGES - 1);
+    compute(kb);
   }
 
   // ---- epilogue: lane owns output row m, columns n_first .. n_first+4*TN-1
@@ -239,7 +349,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(const GemmArgs p) 
 #pragma unroll
   for (int j = 0; j < S::TM; ++j) {
     if (!m_live[j]) continue;
-    const int ml = wm * S::WAVE_M + j * 16 + rho;
+    const int ml = ml0 + 16 * j;
     uint16_t* dst = p.out + (base + m0 + ml) * (int64_t)p.Nout + n_first;
     uint32_t packed[2 * S::TN];
 #pragma unroll
@@ -251,17 +361,16 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_kernel(const GemmArgs p) 
     for (int v = 0; v < S::TN / 2; ++v)
       reinterpret_cast<uint4*>(dst)[v] =
           make_uint4(packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]);
-    if (S::TN == 1) reinterpret_cast<uint2*>(dst)[0] = make_uint2(packed[0], packed[1]);
   }
 }
 
-template <int BM>
-hipError_t launch_bm(const GemmArgs& p, int max_tiles, int quant, hipStream_t stream) {
-  const dim3 grid(p.Nout / kBN, max_tiles);
+template <class S>
+hipError_t launch_shape(const GemmArgs& p, int max_tiles, int quant, hipStream_t stream) {
+  const dim3 grid(p.Nout / S::BN, max_tiles);
   if (quant == kQuantUe8m0)
-    grouped_gemm_kernel<BM, true><<<grid, 256, 0, stream>>>(p);
+    grouped_gemm_kernel<S, true><<<grid, S::THREADS, 0, stream>>>(p);
   else
-    grouped_gemm_kernel<BM, false><<<grid, 256, 0, stream>>>(p);
+    grouped_gemm_kernel<S, false><<<grid, S::THREADS, 0, stream>>>(p);
   return hipGetLastError();
 }
 
@@ -271,10 +380,18 @@ hipError_t launch_grouped_gemm(const GemmArgs& p, int tile_m, int max_tiles, int
                                hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
   switch (tile_m) {
-    case 16: return launch_bm<16>(p, max_tiles, quant, stream);
-    case 32: return launch_bm<32>(p, max_tiles, quant, stream);
-    case 64: return launch_bm<64>(p, max_tiles, quant, stream);
-    case 128: return launch_bm<128>(p, max_tiles, quant, stream);
+    case 16: return launch_shape<Shape<16, 128, 4, 4>>(p, max_tiles, quant, stream);
+    case 32: return launch_shape<Shape<32, 128, 4, 3>>(p, max_tiles, quant, stream);
+    case 64: return launch_shape<Shape<64, 128, 4, 3>>(p, max_tiles, quant, stream);
+    case 128: {
+      // 256-column tiles (8 waves) halve the activation re-reads; 128-column
+      // tiles run two blocks per CU.  MOE_GEMM_WIDE=0 forces the latter.
+      static const char* env = getenv("MOE_GEMM_WIDE");
+      const bool wide = env == nullptr || env[0] != '0';
+      if (wide && p.Nout % 256 == 0)
+        return launch_shape<Shape<128, 256, 8, 3>>(p, max_tiles, quant, stream);
+      return launch_shape<Shape<128, 128, 4, 2>>(p, max_tiles, quant, stream);
+    }
     default: return hipErrorInvalidValue;
   }
 }

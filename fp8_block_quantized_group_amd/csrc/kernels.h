@@ -28,7 +28,9 @@ struct EplbArgs {
 // Grouped GEMM problem for one launch (w13 or w2).
 struct GemmArgs {
   const uint8_t* a;          // activation codes, rows of Kd bytes
+  uint32_t a_bytes;          // size of the activation-code buffer (< 2^32)
   const void* a_sf;          // activation scales (UE8M0 bytes or fp32) per row
+  uint32_t a_sf_bytes;       // size of the activation-scale buffer (< 2^32)
   int a_sf_stride;           // scale row length: bytes (UE8M0) or floats (fp32)
   const uint8_t* w;          // weight codes [E, Nout, Kd]
   const float* w_sf;         // weight block scales [E, Nout/128, Kd/128]

@@ -90,6 +90,16 @@ moe_status_t validate_problem(const moe_problem_t* p, bool allow_bf16) {
     return fail(MOE_ERR_INVALID_ARG, "batched layout needs max_tokens_per_expert >= 1");
   if (batched(p) && (int64_t)p->num_experts * p->max_tokens_per_expert >= (int64_t)1 << 31)
     return fail(MOE_ERR_UNSUPPORTED, "num_experts * max_tokens_per_expert must be < 2^31");
+  if (p->hidden > 32768 || p->intermediate > 32768)
+    return fail(MOE_ERR_UNSUPPORTED, "hidden and intermediate sizes are limited to 32768");
+  {
+    // activation buffers are addressed with 32-bit buffer offsets
+    const int64_t rows = batched(p) ? (int64_t)p->num_experts * p->max_tokens_per_expert
+                                    : (int64_t)p->num_tokens * p->top_k;
+    const int64_t in_rows = batched(p) ? rows : p->num_tokens;
+    if (in_rows * p->hidden >= ((int64_t)7 << 29) || rows * p->intermediate >= ((int64_t)7 << 29))
+      return fail(MOE_ERR_UNSUPPORTED, "activation buffers are limited to 3.5 GiB");
+  }
   if (p->act_quant != MOE_Q_FP8_UE8M0 && p->act_quant != MOE_Q_FP8_F32 &&
       !(allow_bf16 && p->act_quant == MOE_Q_BF16))
     return fail(allow_bf16 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED,
@@ -256,9 +266,12 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
                       const void* a_sf, const moe_routing_t* r, const void* w, const float* w_sf,
                       void* out, hipStream_t stream) {
   moe::GemmArgs g{};
+  const bool ue = p->act_quant == MOE_Q_FP8_UE8M0;
   g.a = (const uint8_t*)a_q;
+  g.a_bytes = (uint32_t)(w13 ? pl.x_q_bytes : pl.a2_q_bytes);
   g.a_sf = a_sf;
   g.a_sf_stride = (int)(w13 ? pl.s.x_sf_row : pl.s.a2_sf_row);
+  g.a_sf_bytes = (uint32_t)((w13 ? pl.s.stage_rows : pl.s.expert_rows) * g.a_sf_stride * (ue ? 1 : 4));
   g.w = (const uint8_t*)w;
   g.w_sf = w_sf;
   g.out = (uint16_t*)out;
