@@ -30,11 +30,10 @@
 //  * Activation rows past an expert's count get an out-of-range buffer
 //    offset: they read as zeros and never reach an output.  Rows of a
 //    batched-masked slab past its count are therefore never read.
-//  * Work unit = (expert, 128-column weight tile, BM-row activation tile).
-//    The tile list comes from the routing step, heaviest experts first;
-//    grid.x runs over weight tiles, so the tiles of one expert that share a
-//    weight tile land on the same XCD (grid.x is a multiple of 8 for every
-//    supported width) and re-read it from that XCD's L2.
+//  * Work unit = (expert, BN-column weight tile, BM-row activation tile).
+//    The tile list comes from the routing step, heaviest experts first; the
+//    1-D grid is remapped so that each XCD processes a contiguous run of
+//    work, expert by expert, and re-reads shared tiles from its own L2.
 //  * LDS rows are 128 bytes; 16-byte chunks are XOR-swizzled per row so that
 //    the fragment reads of a wave spread over the banks.
 #include <stdlib.h>
@@ -166,13 +165,13 @@ __device__ __forceinline__ v4i buffer_rsrc(const void* base, uint32_t num_record
 // HBM -> LDS: lane l's 16 (4) bytes at rsrc + voffset land at lds + 16*l (4*l).
 __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                ::"s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
 #endif
 }
 __device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
                ::"s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
 #endif
 }
@@ -187,11 +186,38 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     const GemmArgs p) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS_BYTES];
 
-  const int tile = blockIdx.y;
-  if (tile >= p.tile_list[0]) return;
+  // ---- which (expert, m-tile, n-tile) this block computes ----------------
+  // Workgroups go to the 8 XCDs round-robin (block L to XCD L % 8).  Each
+  // XCD walks its own contiguous range of the work list, ordered expert by
+  // expert (heaviest first) and, inside an expert, n-tile-major: the
+  // blocks that run together on one XCD share weight tiles (the expert's
+  // m-tiles) and activation tiles (neighbouring n-tiles) in its L2.
+  const int NT = p.Nout / S::BN;
+  const int64_t work = (int64_t)p.tile_list[0] * NT;
+  const int64_t per_xcd = (work + 7) / 8;
+  const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (blockIdx.x / 8 >= per_xcd || wl >= work) return;
+  int tile, nt;
+  {
+    // group g with groups[g] <= wl / NT < groups[g+1] (binary search in LDS)
+    int* groups = reinterpret_cast<int*>(smem);
+    for (int i = threadIdx.x; i <= p.num_experts; i += S::THREADS) groups[i] = p.tile_groups[i];
+    __syncthreads();
+    const int t0 = (int)(wl / NT);
+    int lo = 0, hi = p.num_experts;   // groups[lo] <= t0 < groups[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (groups[mid] <= t0) lo = mid; else hi = mid;
+    }
+    const int first = groups[lo], mtiles = groups[lo + 1] - first;
+    const int r = (int)(wl - (int64_t)first * NT);
+    nt = r / mtiles;
+    tile = first + r % mtiles;
+    __syncthreads();
+  }
   const int e = p.tile_list[1 + 2 * tile];
   const int m0 = p.tile_list[2 + 2 * tile];
-  const int n0 = blockIdx.x * S::BN;
+  const int n0 = nt * S::BN;
   int cnt = p.counts[e];
   if (p.offsets == nullptr) cnt = min(cnt, p.max_tokens);
   const int rows_here = min(S::BM, cnt - m0);
@@ -366,7 +392,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
 
 template <class S>
 hipError_t launch_shape(const GemmArgs& p, int max_tiles, int quant, hipStream_t stream) {
-  const dim3 grid(p.Nout / S::BN, max_tiles);
+  const int64_t blocks = ((int64_t)max_tiles * (p.Nout / S::BN) + 7) / 8 * 8;
+  const dim3 grid((unsigned)blocks);
   if (quant == kQuantUe8m0)
     grouped_gemm_kernel<S, true><<<grid, S::THREADS, 0, stream>>>(p);
   else

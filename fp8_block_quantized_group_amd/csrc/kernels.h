@@ -36,6 +36,8 @@ struct GemmArgs {
   const float* w_sf;         // weight block scales [E, Nout/128, Kd/128]
   uint16_t* out;             // bf16 [rows, Nout]
   const int32_t* tile_list;  // [0] tile count, then (expert, m0) pairs
+  const int32_t* tile_groups;  // [E+1] first tile of each expert group (heavy-first)
+  int num_experts;
   const int32_t* counts;     // [E] rows per expert
   const int32_t* offsets;    // [E+1] contiguous row base, nullptr for batched slabs
   const int32_t* row_src;    // A row gather (w13 on the contiguous layout) or nullptr
@@ -54,9 +56,9 @@ hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t 
 hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint8_t* is_padding,
                         int T, int k, int E, const EplbArgs& eplb, int64_t* idx_out,
                         float* w_out, int32_t* hist, const int32_t* counts_in, int max_tokens,
-                        int tile_m, int32_t* expert_num_tokens, int32_t* expert_offsets,
-                        int32_t* row_src, int32_t* slot_row, int32_t* tile_list,
-                        hipStream_t stream);
+                        int tile_m, int max_tiles, int32_t* expert_num_tokens,
+                        int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
+                        int32_t* tile_list, hipStream_t stream);
 
 hipError_t launch_grouped_gemm(const GemmArgs& args, int tile_m, int max_tiles, int quant,
                                hipStream_t stream);

@@ -133,7 +133,7 @@ Plan make_plan(const moe_problem_t* p) {
     pl.s.expert_rows = T * k;
     pl.max_tiles = (T * k + bm - 1) / bm + E;
   }
-  pl.s.tile_list = 1 + 2 * pl.max_tiles;
+  pl.s.tile_list = 1 + 2 * pl.max_tiles + (E + 1);
   pl.s.x_sf_row = ue ? 4 * ((GK + 3) / 4) : GK;
   pl.s.a2_sf_row = ue ? 4 * ((GN + 3) / 4) : GN;
   pl.route_blocks = (T * k + moe::kRouteChunk - 1) / moe::kRouteChunk;
@@ -257,7 +257,8 @@ moe_status_t run_stage(const moe_problem_t* p, const Plan& pl, const void* hidde
   if (err != hipSuccess) return launch_status(err, "stage_quant");
   err = moe::launch_route(topk_ids, topk_weights, is_padding, p->num_tokens, p->top_k,
                           p->num_experts, eplb_args(eplb), idx_out, w_out, hist, cin,
-                          p->max_tokens_per_expert, pl.s.tile_m, r->expert_num_tokens,
+                          p->max_tokens_per_expert, pl.s.tile_m, (int)pl.max_tiles,
+                          r->expert_num_tokens,
                           r->expert_offsets, r->row_src, r->slot_row, r->tile_list, stream);
   return launch_status(err, "route");
 }
@@ -276,6 +277,8 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
   g.w_sf = w_sf;
   g.out = (uint16_t*)out;
   g.tile_list = r->tile_list;
+  g.tile_groups = r->tile_list + 1 + 2 * pl.max_tiles;
+  g.num_experts = p->num_experts;
   g.counts = r->expert_num_tokens;
   g.offsets = batched(p) ? nullptr : r->expert_offsets;
   g.row_src = (w13 && !batched(p)) ? r->row_src : nullptr;

@@ -13,7 +13,8 @@
 // Three launches, no host synchronisation:
 //   1. repack + per-block expert histogram (LDS atomics), EPLB load counts;
 //   2. one block: per-expert exclusive scan over blocks, offsets, and the
-//      heavy-first M-tile list for the grouped GEMMs;
+//      heavy-first M-tile list for the grouped GEMMs (tiles of one expert
+//      contiguous, with per-expert group offsets);
 //   3. per-block stable ranks (wave ballots + LDS running counters) ->
 //      row_src and slot_row.
 // Rows of one expert come out in ascending flat slot order t*top_k + j, so
@@ -87,7 +88,7 @@ __device__ int block_inclusive_scan(int v, int* buf) {
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(
     int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
-    int max_tokens, int tile_m, int32_t* __restrict__ expert_num_tokens,
+    int max_tokens, int tile_m, int max_tiles, int32_t* __restrict__ expert_num_tokens,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ tile_list) {
   __shared__ int buf[1024];
   __shared__ int tiles[1024];
@@ -125,14 +126,20 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   __syncthreads();
   const int mine = e < E ? tiles[order[e]] : 0;
   const int incl_t = block_inclusive_scan(mine, buf);
+  // group e (the e-th heaviest expert) owns tiles [group_off[e], group_off[e+1])
+  int32_t* group_off = tile_list + 1 + 2 * max_tiles;
   if (e < E) {
     const int ex = order[e];
     int pos = incl_t - mine;
+    group_off[e] = pos;
     for (int i = 0; i < mine; ++i, ++pos) {
       tile_list[1 + 2 * pos] = ex;
       tile_list[2 + 2 * pos] = i * tile_m;
     }
-    if (e == E - 1) tile_list[0] = incl_t;
+    if (e == E - 1) {
+      tile_list[0] = incl_t;
+      group_off[E] = incl_t;
+    }
   }
 }
 
@@ -187,9 +194,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
 hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint8_t* is_padding,
                         int T, int k, int E, const EplbArgs& eplb, int64_t* idx_out,
                         float* w_out, int32_t* hist, const int32_t* counts_in, int max_tokens,
-                        int tile_m, int32_t* expert_num_tokens, int32_t* expert_offsets,
-                        int32_t* row_src, int32_t* slot_row, int32_t* tile_list,
-                        hipStream_t stream) {
+                        int tile_m, int max_tiles, int32_t* expert_num_tokens,
+                        int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
+                        int32_t* tile_list, hipStream_t stream) {
   const int64_t total = (int64_t)T * k;
   const int nblocks = (int)((total + kRouteChunk - 1) / kRouteChunk);
   if (nblocks > 0) {
@@ -197,7 +204,8 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint
         topk_ids, topk_w, is_padding, T, k, E, eplb, idx_out, w_out, hist);
   }
   route_scan_kernel<<<1, 1024, 0, stream>>>(hist, nblocks, E, counts_in, max_tokens, tile_m,
-                                            expert_num_tokens, expert_offsets, tile_list);
+                                            max_tiles, expert_num_tokens, expert_offsets,
+                                            tile_list);
   if (nblocks > 0) {
     route_scatter_kernel<<<nblocks, kRouteThreads, E * sizeof(int32_t), stream>>>(
         idx_out, T, k, E, hist, expert_offsets, counts_in != nullptr ? max_tokens : 0, row_src,

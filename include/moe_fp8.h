@@ -115,7 +115,10 @@ typedef struct {
  *  row_src           [T*top_k] token of each contiguous row (contiguous layout)
  *  slot_row          [T*top_k] row of (token, slot), -1 when unrouted;
  *                    batched: e * max_tokens + rank (rank >= max_tokens -> -1)
- *  tile_list         [1 + 2*max_tiles] M-tile schedule for the GEMMs */
+ *  tile_list         [1 + 2*max_tiles + E + 1] M-tile schedule for the GEMMs:
+ *                    tile count, (expert, first row) pairs with each expert's
+ *                    tiles contiguous and the most-loaded experts first, then
+ *                    the first tile of each expert group (E + 1 offsets) */
 typedef struct {
   int32_t* expert_num_tokens;
   int32_t* expert_offsets;

@@ -94,14 +94,20 @@ def stage_on_gpu(cfg, dev):
 
 
 def host_tile_list(counts, tile_m, n_entries):
-    """Every (expert, m0) tile in plain expert order (test plumbing: the GEMM
-    must not depend on the order the routing step emits)."""
+    """Every (expert, m0) tile in plain expert order plus the per-expert
+    group offsets (test plumbing: the GEMM must not depend on the order the
+    routing step emits)."""
+    E = len(counts)
+    max_tiles = (n_entries - 1 - (E + 1)) // 2
     tl = np.zeros(n_entries, np.int32)
+    groups = tl[1 + 2 * max_tiles:]
     pos = 0
     for e, c in enumerate(counts):
+        groups[e] = pos
         for m0 in range(0, int(c), tile_m):
             tl[1 + 2 * pos], tl[2 + 2 * pos] = e, m0
             pos += 1
+    groups[E] = pos
     tl[0] = pos
     return tl
 
@@ -235,6 +241,15 @@ def test_stage_and_route_bit_exact(gpu, name):
     assert sorted(map(tuple, pairs.tolist())) == want
     per_expert = [-(-int(ref["counts"][e]) // bm) for e in pairs[:, 0]]
     assert all(a >= b for a, b in zip(per_expert, per_expert[1:]))
+    # group offsets: group g = the g-th heaviest expert's contiguous tiles
+    max_tiles = (s["tile_list"] - 1 - (cfg.E + 1)) // 2
+    groups = tl[1 + 2 * max_tiles:1 + 2 * max_tiles + cfg.E + 1]
+    assert groups[0] == 0 and groups[-1] == n and np.all(np.diff(groups) >= 0)
+    for g in range(cfg.E):
+        seg = pairs[groups[g]:groups[g + 1]]
+        if len(seg):
+            assert np.all(seg[:, 0] == seg[0, 0])
+            assert list(seg[:, 1]) == list(range(0, len(seg) * bm, bm))
 
 
 def test_stage_bf16_copy(gpu):
