@@ -21,15 +21,19 @@
 //    writes 16-32 contiguous bytes per lane.
 //  * Operand tiles travel HBM -> LDS with buffer_load_dwordx4 ... lds
 //    (no register staging) through a ring of STAGES k-steps, so STAGES-1
-//    k-steps (up to ~96 KB per CU) are in flight while one is multiplied:
-//    enough outstanding bytes to cover HBM latency, which is what bounds a
-//    weight-streaming GEMM.  The fragment reads from LDS are inline
-//    ds_read_b128 so that the compiler, which cannot tell the ring slots
-//    apart, does not drain every outstanding load before each read; the
-//    waits are placed by hand (vmcnt per stage, one barrier per k-step).
-//  * Activation rows past an expert's count get an out-of-range buffer
-//    offset: they read as zeros and never reach an output.  Rows of a
-//    batched-masked slab past its count are therefore never read.
+//    k-steps (up to ~96 KB per CU) are in flight while one is multiplied.
+//    The loads are issued from inline asm, so the compiler, which cannot see
+//    LDS being written behind its back, neither drains the outstanding
+//    loads before every fragment read nor reorders around them; the waits
+//    are placed by hand (vmcnt per stage, one barrier per k-step).
+//  * Activation rows past an expert's count are never loaded (whole 8-row
+//    load groups are skipped, partial ones read zeros through an
+//    out-of-range buffer offset) and 16-row sub-tiles without rows of the
+//    expert cost no fragment reads and no MFMAs: the number of live
+//    sub-tiles is a compile-time constant of the main loop, dispatched once
+//    per block.  Sub-tiles are interleaved across the two wave rows so that
+//    a short expert still keeps both busy.  Rows of a batched-masked slab
+//    past its count are therefore never read.
 //  * Work unit = (expert, BN-column weight tile, BM-row activation tile).
 //    The tile list comes from the routing step, heaviest experts first; the
 //    1-D grid is remapped so that each XCD processes a contiguous run of
@@ -71,7 +75,7 @@ struct Shape {
   static constexpr int TN = WAVE_N / 16;
   static constexpr int TM = WAVE_M / 16;
   static_assert(TN == 2 || TN == 4, "wave tile rows");
-  static_assert(TM >= 1 && TM <= 4, "wave tile columns");
+  static_assert(TM >= 1 && TM <= 8, "wave tile columns");
   static_assert(WAVE_N <= 128, "a wave's columns share one weight-scale block");
   static constexpr int LOG_4TN = TN == 4 ? 4 : 3;
   static constexpr int A_BYTES = BM * kRowBytes;
@@ -83,17 +87,14 @@ struct Shape {
   // one buffer_load ... lds instruction moves 64 lanes x 16 bytes = 1 KB
   static constexpr int A_CHUNKS = BM * 8;
   static constexpr int A_INSTR = A_CHUNKS >= THREADS ? A_CHUNKS / THREADS : 1;
-  static constexpr int A_WAVES = A_CHUNKS >= THREADS ? NW : A_CHUNKS / 64;
   static constexpr int B_INSTR = BN * 8 / THREADS;
   static constexpr int BLOCKS_PER_CU = (2 * LDS_BYTES <= 160 * 1024) ? 2 : 1;
   static constexpr int MIN_WAVES_PER_EU = BLOCKS_PER_CU * NW / 4;
   static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds the CU's LDS");
   static_assert(B_INSTR * THREADS == BN * 8, "weight tile split");
-  // buffer loads into LDS a wave issues per k-step
-  template <int W>
-  static constexpr int loads() {
-    return (W < A_WAVES ? A_INSTR : 0) + B_INSTR + (W < SC_WAVES ? 1 : 0);
-  }
+  // most buffer loads into LDS a wave issues per k-step
+  static constexpr int LMAX = A_INSTR + B_INSTR + 1;
+  static_assert(3 * LMAX < 64, "vmcnt range");
 };
 
 // 16-byte chunk c of row r lives at chunk position c ^ key(r).  The keys
@@ -129,8 +130,10 @@ __device__ __forceinline__ void wait_then_barrier() {
 }
 
 // `after` = how many later k-steps (L loads each) may still be in flight.
+// L is per wave and per block (waves skip the loads of rows an expert does
+// not have), so it is dispatched to a compile-time immediate here.
 template <int L>
-__device__ __forceinline__ void wait_stages(int after) {
+__device__ __forceinline__ void wait_stages_l(int after) {
   if (after <= 0)
     wait_then_barrier<0>();
   else if (after == 1)
@@ -140,17 +143,15 @@ __device__ __forceinline__ void wait_stages(int after) {
   else
     wait_then_barrier<3 * L>();
 }
-
-// vmcnt is per wave and waves issue different numbers of loads per k-step.
-template <class S, int W = 0>
-__device__ __forceinline__ void stage_landed(int wave, int after) {
-  if constexpr (W + 1 < S::NW) {
-    if (wave != W) {
-      stage_landed<S, W + 1>(wave, after);
+template <int LMAX, int L = 0>
+__device__ __forceinline__ void stage_landed(int loads_per_stage, int after) {
+  if constexpr (L < LMAX) {
+    if (loads_per_stage != L) {
+      stage_landed<LMAX, L + 1>(loads_per_stage, after);
       return;
     }
   }
-  wait_stages<S::template loads<W>()>(after);
+  wait_stages_l<L>(after);
 }
 
 // Raw buffer resource over [base, base + num_records): offsets at or past
@@ -176,6 +177,20 @@ __device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voffset) {
 #endif
 }
 #pragma clang diagnostic pop
+
+// f(integral_constant<int, v>) for a wave-uniform v in [0, N].
+template <int N, class F>
+__device__ __forceinline__ void with_constant(int v, F&& f) {
+  if constexpr (N > 0) {
+    if (v == N) {
+      f(std::integral_constant<int, N>{});
+      return;
+    }
+    with_constant<N - 1>(v, f);
+  } else {
+    f(std::integral_constant<int, 0>{});
+  }
+}
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
@@ -211,8 +226,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     }
     const int first = groups[lo], mtiles = groups[lo + 1] - first;
     const int r = (int)(wl - (int64_t)first * NT);
-    nt = r / mtiles;
-    tile = first + r % mtiles;
+    nt = __builtin_amdgcn_readfirstlane(r / mtiles);
+    tile = __builtin_amdgcn_readfirstlane(first + r % mtiles);
     __syncthreads();
   }
   const int e = p.tile_list[1 + 2 * tile];
@@ -239,13 +254,18 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const v4i rs_a = buffer_rsrc(p.a, p.a_bytes);
   const v4i rs_b = buffer_rsrc(p.w + ((int64_t)e * p.Nout + n0) * p.Kd, (uint32_t)(S::BN * p.Kd));
   const v4i rs_s = buffer_rsrc(p.a_sf, p.a_sf_bytes);
-  const bool loads_a = wave < S::A_WAVES;
+  // A: load instruction q (64 lanes = 8 rows x 8 chunks) belongs to wave
+  // q % NW; only instructions covering rows of the expert are issued (rows
+  // past its count are never read; their LDS slots keep stale bytes, which
+  // only ever meet output rows that are not stored).
+  const int a_groups = (rows_here + 7) >> 3;
+  const int a_loads = a_groups > wave ? (a_groups - wave + S::NW - 1) / S::NW : 0;
   uint32_t a_off[S::A_INSTR];
 #pragma unroll
   for (int i = 0; i < S::A_INSTR; ++i) {
     const int slot = i * S::THREADS + tid;
     const int r = slot >> 3, c = (slot & 7) ^ key_a(slot >> 3);
-    a_off[i] = (loads_a && r < rows_here) ? (uint32_t)(a_row_of(r) * p.Kd + c * 16) : kOutOfRange;
+    a_off[i] = (r < rows_here) ? (uint32_t)(a_row_of(r) * p.Kd + c * 16) : kOutOfRange;
   }
   uint32_t b_off[S::B_INSTR];
 #pragma unroll
@@ -256,7 +276,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   }
   // activation scales: one 4-byte word per row and k-step (UE8M0: the word
   // holding the step's exponent byte; fp32: the scale itself)
-  const bool loads_sc = wave < S::SC_WAVES;
+  const bool loads_sc = wave < S::SC_WAVES && wave * 64 < rows_here;
+  const int loads_per_stage = a_loads + S::B_INSTR + (loads_sc ? 1 : 0);
   uint32_t sc_off = kOutOfRange;
   {
     const int r = wave * 64 + lane;
@@ -283,25 +304,24 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int kbw = key_b<S::LOG_4TN>(nl0);
   const int w_frag0 = S::A_BYTES + nl0 * kRowBytes + ((c0 ^ kbw) << 4);
   const int w_frag1 = S::A_BYTES + nl0 * kRowBytes + ((c1 ^ kbw) << 4);
-  // activation sub-tile j's row is ml0 + 16*j (same swizzle key)
-  const int ml0 = wm * S::WAVE_M + rho;
+  // activation sub-tile j of this wave holds rows 16*(j*WM + wm) + [0, 16)
+  // (interleaved across the WM wave rows, so that a short expert still
+  // spreads its rows over them); this lane's row is ml0 + 16*WM*j (same
+  // swizzle key)
+  const int ml0 = wm * 16 + rho;
   const int a_frag0 = ml0 * kRowBytes + ((c0 ^ key_a(ml0)) << 4);
   const int a_frag1 = ml0 * kRowBytes + ((c1 ^ key_a(ml0)) << 4);
   const int sc_frag = S::A_BYTES + S::B_BYTES + ml0 * 4;
-  bool m_live[S::TM];
-#pragma unroll
-  for (int j = 0; j < S::TM; ++j) m_live[j] = ml0 + 16 * j < rows_here;
+  constexpr int kSubStride = 16 * S::WM;
   const uint32_t smem_base = lds_addr(smem);
   const float* sw_mine = sw_panel + ((wn * S::WAVE_N) / 128) * kMaxGroups;
 
   auto issue = [&](int kb) {
     const uint32_t st = smem_base + (kb % S::STAGES) * S::STAGE_BYTES;
     const uint32_t koff = (uint32_t)kb * kRowBytes;
-    if (loads_a) {
 #pragma unroll
-      for (int i = 0; i < S::A_INSTR; ++i)
-        dma16(rs_a, st + i * S::THREADS * 16 + wave_slot, a_off[i] + koff);
-    }
+    for (int i = 0; i < S::A_INSTR; ++i)
+      if (i < a_loads) dma16(rs_a, st + i * S::THREADS * 16 + wave_slot, a_off[i] + koff);
 #pragma unroll
     for (int i = 0; i < S::B_INSTR; ++i)
       dma16(rs_b, st + S::A_BYTES + i * S::THREADS * 16 + wave_slot, b_off[i] + koff);
@@ -317,65 +337,84 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
 #pragma unroll
     for (int j = 0; j < S::TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  // One k-step: TN*TM MFMAs (one per 16x16 sub-tile, K = 128 = one scale
-  // block), each partial promoted into the fp32 accumulator two MFMAs later,
-  // once it has left the matrix pipe.
-  auto compute = [&](int kb) {
-    const uint8_t* sb = smem + (kb % S::STAGES) * S::STAGE_BYTES;
-    v8i wf[S::TN], af[S::TM];
+  // One k-step over the first LIVE activation sub-tiles (the ones holding
+  // rows of the expert; the rest cost no LDS reads and no MFMAs): one MFMA
+  // per 16x16 sub-tile (K = 128 = one scale block), in activation-major
+  // order t = j*TN + i; each partial is promoted into the fp32 accumulator
+  // two MFMAs after issue, once it has left the matrix pipe.
+  auto compute = [&](int kb, auto live_c) {
+    constexpr int LIVE = decltype(live_c)::value;
+    if constexpr (LIVE > 0) {
+      const uint8_t* sb = smem + (kb % S::STAGES) * S::STAGE_BYTES;
+      v8i wf[S::TN], af[LIVE];
+      float fs[LIVE];
 #pragma unroll
-    for (int i = 0; i < S::TN; ++i) {
-      const v4i lo = *reinterpret_cast<const v4i*>(sb + w_frag0 + i * 4 * kRowBytes);
-      const v4i hi = *reinterpret_cast<const v4i*>(sb + w_frag1 + i * 4 * kRowBytes);
-      wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-    float fs[S::TM];
-    const float sw = sw_mine[kb];
-#pragma unroll
-    for (int j = 0; j < S::TM; ++j) {
-      const v4i lo = *reinterpret_cast<const v4i*>(sb + a_frag0 + j * 16 * kRowBytes);
-      const v4i hi = *reinterpret_cast<const v4i*>(sb + a_frag1 + j * 16 * kRowBytes);
-      af[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-      const uint32_t word = *reinterpret_cast<const uint32_t*>(sb + sc_frag + j * 64);
-      const float sa = UE8M0 ? __uint_as_float(((word >> ((kb & 3) * 8)) & 0xFFu) << 23)
-                             : __uint_as_float(word);
-      fs[j] = m_live[j] ? sa * sw : 0.0f;
-    }
-    constexpr int NT = S::TN * S::TM;
-    v4f part[3];
-#pragma unroll
-    for (int t = 0; t < NT + 2; ++t) {
-      if (t < NT) {
-        const v4f z = {0.f, 0.f, 0.f, 0.f};
-        part[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            wf[t / S::TM], af[t % S::TM], z, 0, 0, 0, 0, 0, 0);
+      for (int i = 0; i < S::TN; ++i) {
+        const v4i lo = *reinterpret_cast<const v4i*>(sb + w_frag0 + i * 4 * kRowBytes);
+        const v4i hi = *reinterpret_cast<const v4i*>(sb + w_frag1 + i * 4 * kRowBytes);
+        wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      if (t >= 2) {
-        const int u = t - 2, i = u / S::TM, j = u % S::TM;
+      const float sw = sw_mine[kb];
+      // activation fragment j (and its scale) is read when sub-tile j-1's
+      // MFMAs start, so at most two are live
+      auto load_a = [&](int j, v8i& f, float& fs) {
+        const v4i lo = *reinterpret_cast<const v4i*>(sb + a_frag0 + j * kSubStride * kRowBytes);
+        const v4i hi = *reinterpret_cast<const v4i*>(sb + a_frag1 + j * kSubStride * kRowBytes);
+        f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const uint32_t word = *reinterpret_cast<const uint32_t*>(sb + sc_frag + j * kSubStride * 4);
+        const float sa = UE8M0 ? __uint_as_float(((word >> ((kb & 3) * 8)) & 0xFFu) << 23)
+                               : __uint_as_float(word);
+        fs = sa * sw;
+      };
+      load_a(0, af[0], fs[0]);
+      constexpr int NT = S::TN * LIVE;
+      v4f part[3];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[u % 3][r], fs[j], acc[i][j][r]);
+      for (int t = 0; t < NT + 2; ++t) {
+        if (t < NT) {
+          if (t % S::TN == 0 && t / S::TN + 1 < LIVE)
+            load_a(t / S::TN + 1, af[t / S::TN + 1], fs[t / S::TN + 1]);
+          const v4f z = {0.f, 0.f, 0.f, 0.f};
+          part[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf[t % S::TN], af[t / S::TN], z, 0, 0, 0, 0, 0, 0);
+        }
+        if (t >= 2) {
+          const int u = t - 2, i = u % S::TN, j = u / S::TN;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[u % 3][r], fs[j], acc[i][j][r]);
+        }
+        // keep the rolling order: without this fence the scheduler sinks
+        // every promotion to the end of the k-step, which keeps all
+        // partials live at once
+        if constexpr (S::TM * S::TN > 16) __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
 
-  // prologue: STAGES-1 k-steps in flight
+  auto main_loop = [&](auto live_c) {
+    // prologue: STAGES-1 k-steps in flight
 #pragma unroll
-  for (int s = 0; s < S::STAGES - 1; ++s)
-    if (s < G) issue(s);
-  for (int kb = 0; kb < G; ++kb) {
-    // k-step kb has landed for every wave, and every wave's reads of k-step
-    // kb-1 (whose slot the next issue reuses) have completed
-    stage_landed<S>(wave, min(kb + S::STAGES - 2, G - 1) - kb);
-    if (kb + S::STAGES - 1 < G) issue(kb + S::STAGES - 1);
-    compute(kb);
-  }
+    for (int s = 0; s < S::STAGES - 1; ++s)
+      if (s < G) issue(s);
+    for (int kb = 0; kb < G; ++kb) {
+      // k-step kb has landed for every wave, and every wave's reads of
+      // k-step kb-1 (whose slot the next issue reuses) have completed
+      stage_landed<S::LMAX>(loads_per_stage, min(kb + S::STAGES - 2, G - 1) - kb);
+      if (kb + S::STAGES - 1 < G) issue(kb + S::STAGES - 1);
+      compute(kb, live_c);
+    }
+  };
+  // live sub-tiles of this wave (wave-uniform)
+  const int live = __builtin_amdgcn_readfirstlane(
+      max(0, min(S::TM, (rows_here - wm * 16 + kSubStride - 1) / kSubStride)));
+  with_constant<S::TM>(live, main_loop);
 
   // ---- epilogue: lane owns output row m, columns n_first .. n_first+4*TN-1
   const int n_first = n0 + wn * S::WAVE_N + kq * (4 * S::TN);
 #pragma unroll
   for (int j = 0; j < S::TM; ++j) {
-    if (!m_live[j]) continue;
-    const int ml = ml0 + 16 * j;
+    const int ml = ml0 + kSubStride * j;
+    if (ml >= rows_here) continue;
     uint16_t* dst = p.out + (base + m0 + ml) * (int64_t)p.Nout + n_first;
     uint32_t packed[2 * S::TN];
 #pragma unroll
@@ -419,6 +458,17 @@ hipError_t launch_grouped_gemm(const GemmArgs& p, int tile_m, int max_tiles, int
         return launch_shape<Shape<128, 256, 8, 3>>(p, max_tiles, quant, stream);
       return launch_shape<Shape<128, 128, 4, 2>>(p, max_tiles, quant, stream);
     }
+    // Experts with hundreds of rows: 1.5x / 2x fewer weight re-reads than
+    // 128-row tiles, at the price of a two-slot ring (LDS) and of 128
+    // accumulator VGPRs per lane at 256 rows.
+    case 192:
+      if (p.Nout % 256 == 0)
+        return launch_shape<Shape<192, 256, 8, 2>>(p, max_tiles, quant, stream);
+      return launch_shape<Shape<192, 128, 8, 2>>(p, max_tiles, quant, stream);
+    case 256:
+      if (p.Nout % 256 == 0)
+        return launch_shape<Shape<256, 256, 8, 2>>(p, max_tiles, quant, stream);
+      return launch_shape<Shape<256, 128, 8, 2>>(p, max_tiles, quant, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -56,18 +56,21 @@ bool batched(const moe_problem_t* p) { return p->layout == MOE_LAYOUT_BATCHED_MA
 // Activation rows per GEMM tile, from the expected rows per expert.  Rows
 // per expert below 16 leave a 16-row MFMA tile mostly empty, and there the
 // GEMM streams weights at HBM speed whatever the tile height, so the
-// smallest tile that covers the typical expert wins.
+// smallest tile that covers the typical expert wins.  Experts with hundreds
+// of rows re-read their weights once per tile, so they take the tallest
+// tile that fits the register file (256 rows).
 int choose_tile_m(const moe_problem_t* p) {
   const char* env = getenv("MOE_TILE_M");
   if (env != nullptr) {
     const int v = atoi(env);
-    if (v == 16 || v == 32 || v == 64 || v == 128) return v;
+    if (v == 16 || v == 32 || v == 64 || v == 128 || v == 192 || v == 256) return v;
   }
   const double rows = (double)p->num_tokens * p->top_k / p->num_experts;
   if (rows <= 12.0) return 16;
   if (rows <= 24.0) return 32;
   if (rows <= 48.0) return 64;
-  return 128;
+  if (rows <= 384.0) return 128;
+  return 256;
 }
 
 moe_status_t validate_problem(const moe_problem_t* p, bool allow_bf16) {

@@ -56,7 +56,7 @@ def test_sizes_follow_the_problem(lib):
             assert s["stage_rows"] == cfg.T and s["expert_rows"] == cfg.T * cfg.top_k
         G = cfg.K // 128
         assert s["x_sf_row"] == (4 * ((G + 3) // 4) if cfg.act_quant == "ue8m0" else G)
-        assert s["tile_m"] in (16, 32, 64, 128)
+        assert s["tile_m"] in (16, 32, 64, 128, 192, 256)
         ws = moe.workspace_size(p)
         gate_up = s["expert_rows"] * 2 * cfg.N * 2
         assert ws >= gate_up + s["expert_rows"] * cfg.N

@@ -417,7 +417,7 @@ def test_forward_end_to_end(gpu, name):
         assert np.all(to_np(out)[pad] == 0)
 
 
-@pytest.mark.parametrize("tile_m", [16, 32, 64, 128])
+@pytest.mark.parametrize("tile_m", [16, 32, 64, 128, 192, 256])
 def test_every_tile_height(gpu, tile_m, monkeypatch):
     monkeypatch.setenv("MOE_TILE_M", str(tile_m))
     for name in ("ragged", "batched"):
