@@ -56,8 +56,8 @@ class _Sizes(ctypes.Structure):
 
 
 EXPORTS = ("moe_routing_sizes", "moe_stage_workspace_size", "moe_workspace_size", "moe_stage",
-           "moe_grouped_gemm_w13", "moe_act_requant", "moe_grouped_gemm_w2", "moe_topk_reduce",
-           "moe_forward", "moe_last_error")
+           "moe_grouped_gemm_w13", "moe_grouped_gemm_w13_act", "moe_act_requant",
+           "moe_grouped_gemm_w2", "moe_topk_reduce", "moe_forward", "moe_last_error")
 
 _lib = None
 
@@ -79,12 +79,19 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_stage.argtypes = [P(_Problem), V, V, V, V, V, P(_Eplb), V, V, V, V, P(_Routing),
                               V, S, V]
     lib.moe_grouped_gemm_w13.argtypes = [P(_Problem), V, V, P(_Routing), V, V, V, V]
+    lib.moe_grouped_gemm_w13_act.argtypes = [P(_Problem), V, V, P(_Routing), V, V, V, V, V]
     lib.moe_act_requant.argtypes = [P(_Problem), V, P(_Routing), V, V, V]
     lib.moe_grouped_gemm_w2.argtypes = [P(_Problem), V, V, P(_Routing), V, V, V, V]
     lib.moe_topk_reduce.argtypes = [P(_Problem), V, V, V, V, V]
     lib.moe_forward.argtypes = [P(_Problem), V, V, V, V, V, P(_Eplb), V, V, V, V, V, V, S, V]
+    lib.moe_last_error.argtypes = []
     for name in EXPORTS:
-        getattr(lib, name).restype = ctypes.c_int if name != "moe_last_error" else ctypes.c_char_p
+        fn = getattr(lib, name)
+        fn.restype = ctypes.c_int if name != "moe_last_error" else ctypes.c_char_p
+        # without argtypes ctypes passes Python ints as 32-bit C ints, which
+        # would truncate every device pointer
+        if fn.argtypes is None:
+            raise RuntimeError(f"{name}: no ctypes signature declared")
     _lib = lib
     return lib
 
@@ -206,6 +213,15 @@ def grouped_gemm_w13(p: Problem, a_q, a_sf, routing: dict, w13, w13_sf, gate_up)
     _check(load_library().moe_grouped_gemm_w13(ctypes.byref(p.c()), _ptr(a_q), _ptr(a_sf),
                                                 ctypes.byref(r), _ptr(w13), _ptr(w13_sf),
                                                 _ptr(gate_up), _stream()))
+
+
+def grouped_gemm_w13_act(p: Problem, a_q, a_sf, routing: dict, w13, w13_sf, a2_q, a2_sf):
+    """w13 GEMM with SiLU(gate)*up and the fp8 re-quantization in its epilogue;
+    a2_q / a2_sf equal grouped_gemm_w13 followed by act_requant bit for bit."""
+    r = _routing(routing)
+    _check(load_library().moe_grouped_gemm_w13_act(ctypes.byref(p.c()), _ptr(a_q), _ptr(a_sf),
+                                                    ctypes.byref(r), _ptr(w13), _ptr(w13_sf),
+                                                    _ptr(a2_q), _ptr(a2_sf), _stream()))
 
 
 def act_requant(p: Problem, gate_up, routing: dict, a2_q, a2_sf):

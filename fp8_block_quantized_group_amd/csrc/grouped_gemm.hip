@@ -196,9 +196,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
 
-template <class S, bool UE8M0>
+// ACT (w13 only): the block's 256 weight rows are the gate rows j0 + [0, 128)
+// and the up rows N + j0 + [0, 128) of one 128-column group j0 of h, laid
+// out so that each wave holds 32 gate rows followed by the 32 matching up
+// rows; the epilogue turns the result into silu(gate) * up, quantized per
+// 128 columns, instead of storing it.
+template <class S, bool UE8M0, bool ACT>
 __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_kernel(
     const GemmArgs p) {
+  static_assert(!ACT || (S::BN == 256 && S::WN == 4 && S::TN == 4), "fused activation tile");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS_BYTES];
 
   // ---- which (expert, m-tile, n-tile) this block computes ----------------
@@ -232,7 +238,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   }
   const int e = p.tile_list[1 + 2 * tile];
   const int m0 = p.tile_list[2 + 2 * tile];
-  const int n0 = nt * S::BN;
+  const int n0 = nt * S::BN;          // first output column (plain GEMM)
+  const int Nh = p.Nout / 2;            // ACT: columns of h
+  const int j0 = nt * (S::BN / 2);      // ACT: first column of h
   int cnt = p.counts[e];
   if (p.offsets == nullptr) cnt = min(cnt, p.max_tokens);
   const int rows_here = min(S::BM, cnt - m0);
@@ -252,7 +260,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
 
   // ---- HBM -> LDS copy plan: thread tid fills 16-byte slot i*THREADS + tid
   const v4i rs_a = buffer_rsrc(p.a, p.a_bytes);
-  const v4i rs_b = buffer_rsrc(p.w + ((int64_t)e * p.Nout + n0) * p.Kd, (uint32_t)(S::BN * p.Kd));
+  const v4i rs_b =
+      ACT ? buffer_rsrc(p.w + (int64_t)e * p.Nout * p.Kd, (uint32_t)((int64_t)p.Nout * p.Kd))
+          : buffer_rsrc(p.w + ((int64_t)e * p.Nout + n0) * p.Kd, (uint32_t)(S::BN * p.Kd));
   const v4i rs_s = buffer_rsrc(p.a_sf, p.a_sf_bytes);
   // A: load instruction q (64 lanes = 8 rows x 8 chunks) belongs to wave
   // q % NW; only instructions covering rows of the expert are issued (rows
@@ -272,7 +282,13 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   for (int i = 0; i < S::B_INSTR; ++i) {
     const int slot = i * S::THREADS + tid;
     const int r = slot >> 3, c = (slot & 7) ^ key_b<S::LOG_4TN>(slot >> 3);
-    b_off[i] = (uint32_t)(r * p.Kd + c * 16);
+    int64_t wrow = r;
+    if (ACT) {
+      // tile row r = 64*w + q: gate row j0 + 32w + q (q < 32), else up row
+      const int q = r & 63, w = r >> 6;
+      wrow = (q < 32 ? 0 : Nh - 32) + j0 + 32 * w + q;
+    }
+    b_off[i] = (uint32_t)(wrow * p.Kd + c * 16);
   }
   // activation scales: one 4-byte word per row and k-step (UE8M0: the word
   // holding the step's exponent byte; fp32: the scale itself)
@@ -290,8 +306,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   float* sw_panel = reinterpret_cast<float*>(smem + S::STAGES * S::STAGE_BYTES);
   for (int i = tid; i < S::NBLK * G; i += S::THREADS) {
     const int b = i / G, g = i - b * G;
-    sw_panel[b * kMaxGroups + g] =
-        p.w_sf[((int64_t)e * (p.Nout / kGroup) + n0 / kGroup + b) * G + g];
+    // ACT: block 0 = the gate rows' scale block, block 1 = the up rows'
+    const int blk = ACT ? (b == 0 ? j0 : Nh + j0) / kGroup : n0 / kGroup + b;
+    sw_panel[b * kMaxGroups + g] = p.w_sf[((int64_t)e * (p.Nout / kGroup) + blk) * G + g];
   }
   __syncthreads();
 
@@ -314,7 +331,10 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int sc_frag = S::A_BYTES + S::B_BYTES + ml0 * 4;
   constexpr int kSubStride = 16 * S::WM;
   const uint32_t smem_base = lds_addr(smem);
-  const float* sw_mine = sw_panel + ((wn * S::WAVE_N) / 128) * kMaxGroups;
+  // the weight-scale block of this lane's output columns (ACT: lanes 0-31
+  // hold gate rows, lanes 32-63 up rows)
+  const float* sw_mine =
+      sw_panel + (ACT ? (kq >= 2 ? 1 : 0) : (wn * S::WAVE_N) / 128) * kMaxGroups;
 
   auto issue = [&](int kb) {
     const uint32_t st = smem_base + (kb % S::STAGES) * S::STAGE_BYTES;
@@ -409,66 +429,152 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       max(0, min(S::TM, (rows_here - wm * 16 + kSubStride - 1) / kSubStride)));
   with_constant<S::TM>(live, main_loop);
 
-  // ---- epilogue: lane owns output row m, columns n_first .. n_first+4*TN-1
-  const int n_first = n0 + wn * S::WAVE_N + kq * (4 * S::TN);
+  if constexpr (ACT) {
+    // ---- fused activation epilogue ----------------------------------------
+    // Lane (kq, rho) holds, for activation sub-tile j, wave rows
+    // q = 16*kq + 4*i + r: gate columns j0 + 32*wn + q of h for kq < 2, the up
+    // columns j0 + 32*wn + q - 32 for kq >= 2, so lanes l and l ^ 32 hold the
+    // two halves of the same 32 columns.  After one exchange each lane owns 8
+    // consecutive columns: col_off + [0, 8) inside the group.  The values are
+    // rounded to bf16 first (the precision of the gate_up buffer of the
+    // unfused path), then combined and quantized exactly as the standalone
+    // activation kernel does.
+    const bool gate_lane = kq < 2;
+    const int col_off = 32 * wn + (gate_lane ? 16 * kq : 16 * (kq - 2) + 8);
+    float h[S::TM][8];
+    float amax[S::TM];
 #pragma unroll
-  for (int j = 0; j < S::TM; ++j) {
-    const int ml = ml0 + kSubStride * j;
-    if (ml >= rows_here) continue;
-    uint16_t* dst = p.out + (base + m0 + ml) * (int64_t)p.Nout + n_first;
-    uint32_t packed[2 * S::TN];
+    for (int j = 0; j < S::TM; ++j) {
+      amax[j] = 0.0f;
 #pragma unroll
-    for (int i = 0; i < S::TN; ++i) {
-      packed[2 * i] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-      packed[2 * i + 1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      for (int ii = 0; ii < 2; ++ii) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float lo = __uint_as_float(f32_to_bf16_bits(acc[ii][j][r]) << 16);
+          const float hi = __uint_as_float(f32_to_bf16_bits(acc[ii + 2][j][r]) << 16);
+          const float recv = __shfl_xor(gate_lane ? hi : lo, 32);
+          const float g = gate_lane ? lo : recv;
+          const float u = gate_lane ? recv : hi;
+          const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+          const float v = g * sig * u;
+          h[j][4 * ii + r] = v;
+          amax[j] = fmaxf(amax[j], fabsf(v));
+        }
+      }
+      // the 4 lanes of this row in the wave: rho, rho + 16, rho + 32, rho + 48
+      amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 16));
+      amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 32));
     }
+    // group maximum across the WN = 4 waves sharing the rows, through LDS
+    float* red = reinterpret_cast<float*>(smem);   // [WN][BM]
+    __syncthreads();                               // every wave is done with the ring
+    if (kq == 0) {
 #pragma unroll
-    for (int v = 0; v < S::TN / 2; ++v)
-      reinterpret_cast<uint4*>(dst)[v] =
-          make_uint4(packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]);
+      for (int j = 0; j < S::TM; ++j) red[wn * S::BM + ml0 + kSubStride * j] = amax[j];
+    }
+    __syncthreads();
+    const int GN = Nh / kGroup;
+#pragma unroll
+    for (int j = 0; j < S::TM; ++j) {
+      const int ml = ml0 + kSubStride * j;
+      if (ml >= rows_here) continue;
+      const float a = fmaxf(fmaxf(red[ml], red[S::BM + ml]),
+                            fmaxf(red[2 * S::BM + ml], red[3 * S::BM + ml]));
+      const GroupScale gs = group_scale<UE8M0>(a);
+      uint2 q;
+      q.x = f32x4_to_e4m3x4(h[j][0] * gs.recip, h[j][1] * gs.recip, h[j][2] * gs.recip,
+                            h[j][3] * gs.recip);
+      q.y = f32x4_to_e4m3x4(h[j][4] * gs.recip, h[j][5] * gs.recip, h[j][6] * gs.recip,
+                            h[j][7] * gs.recip);
+      const int64_t row = base + m0 + ml;
+      *reinterpret_cast<uint2*>(p.act_q + row * Nh + j0 + col_off) = q;
+      if (wn == 0 && kq == 0) {
+        if (UE8M0) {
+          uint8_t* sf = p.act_sf + row * p.act_sf_row;
+          sf[nt] = (uint8_t)gs.stored;
+          // the row's trailing pad bytes are zero
+          if (nt == GN - 1)
+            for (int pad = GN; pad < p.act_sf_row; ++pad) sf[pad] = 0;
+        } else {
+          reinterpret_cast<uint32_t*>(p.act_sf)[row * p.act_sf_row + nt] = gs.stored;
+        }
+      }
+    }
+  } else {
+    // ---- epilogue: lane owns output row m, columns n_first .. n_first+4*TN-1
+    const int n_first = n0 + wn * S::WAVE_N + kq * (4 * S::TN);
+#pragma unroll
+    for (int j = 0; j < S::TM; ++j) {
+      const int ml = ml0 + kSubStride * j;
+      if (ml >= rows_here) continue;
+      uint16_t* dst = p.out + (base + m0 + ml) * (int64_t)p.Nout + n_first;
+      uint32_t packed[2 * S::TN];
+#pragma unroll
+      for (int i = 0; i < S::TN; ++i) {
+        packed[2 * i] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+        packed[2 * i + 1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+      }
+#pragma unroll
+      for (int v = 0; v < S::TN / 2; ++v)
+        reinterpret_cast<uint4*>(dst)[v] =
+            make_uint4(packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]);
+    }
   }
 }
 
-template <class S>
+template <class S, bool ACT>
 hipError_t launch_shape(const GemmArgs& p, int max_tiles, int quant, hipStream_t stream) {
   const int64_t blocks = ((int64_t)max_tiles * (p.Nout / S::BN) + 7) / 8 * 8;
   const dim3 grid((unsigned)blocks);
   if (quant == kQuantUe8m0)
-    grouped_gemm_kernel<S, true><<<grid, S::THREADS, 0, stream>>>(p);
+    grouped_gemm_kernel<S, true, ACT><<<grid, S::THREADS, 0, stream>>>(p);
   else
-    grouped_gemm_kernel<S, false><<<grid, S::THREADS, 0, stream>>>(p);
+    grouped_gemm_kernel<S, false, ACT><<<grid, S::THREADS, 0, stream>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_grouped_gemm(const GemmArgs& p, int tile_m, int max_tiles, int quant,
+hipError_t launch_grouped_gemm(const GemmArgs& p, int tile_m, int max_tiles, int quant, bool act,
                                hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
+  if (act) {
+    // 256 weight rows = 128 gate + 128 up rows per block, any tile height
+    if (p.Nout % 256 != 0) return hipErrorInvalidValue;
+    switch (tile_m) {
+      case 16: return launch_shape<Shape<16, 256, 4, 3>, true>(p, max_tiles, quant, stream);
+      case 32: return launch_shape<Shape<32, 256, 4, 3>, true>(p, max_tiles, quant, stream);
+      case 64: return launch_shape<Shape<64, 256, 8, 3>, true>(p, max_tiles, quant, stream);
+      case 128: return launch_shape<Shape<128, 256, 8, 3>, true>(p, max_tiles, quant, stream);
+      case 192: return launch_shape<Shape<192, 256, 8, 2>, true>(p, max_tiles, quant, stream);
+      case 256: return launch_shape<Shape<256, 256, 8, 2>, true>(p, max_tiles, quant, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (tile_m) {
-    case 16: return launch_shape<Shape<16, 128, 4, 4>>(p, max_tiles, quant, stream);
-    case 32: return launch_shape<Shape<32, 128, 4, 3>>(p, max_tiles, quant, stream);
-    case 64: return launch_shape<Shape<64, 128, 4, 3>>(p, max_tiles, quant, stream);
+    case 16: return launch_shape<Shape<16, 128, 4, 4>, false>(p, max_tiles, quant, stream);
+    case 32: return launch_shape<Shape<32, 128, 4, 3>, false>(p, max_tiles, quant, stream);
+    case 64: return launch_shape<Shape<64, 128, 4, 3>, false>(p, max_tiles, quant, stream);
     case 128: {
       // 256-column tiles (8 waves) halve the activation re-reads; 128-column
       // tiles run two blocks per CU.  MOE_GEMM_WIDE=0 forces the latter.
       static const char* env = getenv("MOE_GEMM_WIDE");
       const bool wide = env == nullptr || env[0] != '0';
       if (wide && p.Nout % 256 == 0)
-        return launch_shape<Shape<128, 256, 8, 3>>(p, max_tiles, quant, stream);
-      return launch_shape<Shape<128, 128, 4, 2>>(p, max_tiles, quant, stream);
+        return launch_shape<Shape<128, 256, 8, 3>, false>(p, max_tiles, quant, stream);
+      return launch_shape<Shape<128, 128, 4, 2>, false>(p, max_tiles, quant, stream);
     }
     // Experts with hundreds of rows: 1.5x / 2x fewer weight re-reads than
     // 128-row tiles, at the price of a two-slot ring (LDS) and of 128
     // accumulator VGPRs per lane at 256 rows.
     case 192:
       if (p.Nout % 256 == 0)
-        return launch_shape<Shape<192, 256, 8, 2>>(p, max_tiles, quant, stream);
-      return launch_shape<Shape<192, 128, 8, 2>>(p, max_tiles, quant, stream);
+        return launch_shape<Shape<192, 256, 8, 2>, false>(p, max_tiles, quant, stream);
+      return launch_shape<Shape<192, 128, 8, 2>, false>(p, max_tiles, quant, stream);
     case 256:
       if (p.Nout % 256 == 0)
-        return launch_shape<Shape<256, 256, 8, 2>>(p, max_tiles, quant, stream);
-      return launch_shape<Shape<256, 128, 8, 2>>(p, max_tiles, quant, stream);
+        return launch_shape<Shape<256, 256, 8, 2>, false>(p, max_tiles, quant, stream);
+      return launch_shape<Shape<256, 128, 8, 2>, false>(p, max_tiles, quant, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -34,7 +34,10 @@ struct GemmArgs {
   int a_sf_stride;           // scale row length: bytes (UE8M0) or floats (fp32)
   const uint8_t* w;          // weight codes [E, Nout, Kd]
   const float* w_sf;         // weight block scales [E, Nout/128, Kd/128]
-  uint16_t* out;             // bf16 [rows, Nout]
+  uint16_t* out;             // bf16 [rows, Nout] (plain GEMM)
+  uint8_t* act_q;            // fused activation: fp8 [rows, Nout/2]
+  uint8_t* act_sf;           //   and its per-128 scales (UE8M0 bytes or fp32)
+  int act_sf_row;            //   scale row length: bytes (UE8M0) or floats (fp32)
   const int32_t* tile_list;  // [0] tile count, then (expert, m0) pairs
   const int32_t* tile_groups;  // [E+1] first tile of each expert group (heavy-first)
   int num_experts;
@@ -60,8 +63,12 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint
                         int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
                         int32_t* tile_list, hipStream_t stream);
 
+// act = false: out = bf16 GEMM result.  act = true (w13 only): the result's
+// gate half [0, Nout/2) and up half [Nout/2, Nout) are combined into
+// silu(gate) * up and quantized per 128 columns into act_q / act_sf; nothing
+// is written to out.
 hipError_t launch_grouped_gemm(const GemmArgs& args, int tile_m, int max_tiles, int quant,
-                               hipStream_t stream);
+                               bool act, hipStream_t stream);
 
 hipError_t launch_topk_reduce(const void* down, const int32_t* slot_row, const float* w, void* out,
                               int T, int k, int K, hipStream_t stream);

@@ -114,7 +114,7 @@ struct Plan {
   moe_sizes_t s;
   int64_t route_blocks;
   int64_t max_tiles;
-  size_t x_q_bytes, x_sf_bytes, a2_q_bytes, a2_sf_bytes, gate_up_bytes, down_bytes;
+  size_t x_q_bytes, x_sf_bytes, a2_q_bytes, a2_sf_bytes, down_bytes;
   size_t stage_ws_bytes;
 };
 
@@ -146,35 +146,29 @@ Plan make_plan(const moe_problem_t* p) {
   pl.x_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.stage_rows * pl.s.x_sf_row * (ue ? 1 : 4);
   pl.a2_q_bytes = (size_t)pl.s.expert_rows * N;
   pl.a2_sf_bytes = (size_t)pl.s.expert_rows * pl.s.a2_sf_row * (ue ? 1 : 4);
-  pl.gate_up_bytes = (size_t)pl.s.expert_rows * 2 * N * 2;
   pl.down_bytes = (size_t)pl.s.expert_rows * K * 2;
   return pl;
 }
 
 // Device addresses of the forward workspace.
 struct Workspace {
-  uint8_t* x_q; uint8_t* x_sf; uint8_t* a2_q; uint8_t* a2_sf;
-  uint8_t* gate_up; uint8_t* down;
+  uint8_t* x_q; uint8_t* x_sf; uint8_t* a2_q; uint8_t* a2_sf; uint8_t* down;
   int64_t* idx; float* w; moe_routing_t routing; int32_t* stage_ws;
   size_t total;
 };
 
+// The forward pass runs w13 with the fused activation, which reads x_q while
+// it writes a2: the staged activations, a2 and the bf16 down projection each
+// get their own region (no gate_up buffer).
 Workspace carve(const Plan& pl, const moe_problem_t* p, uint8_t* base) {
   Workspace w;
   size_t off = 0;
   auto take = [&](size_t bytes) { uint8_t* r = base + off; off += round_up(bytes); return r; };
-  // region 1: fp8 activations (x_q + x_sf, later a2_q + a2_sf)
-  const size_t r1 = std::max(round_up(pl.x_q_bytes) + round_up(pl.x_sf_bytes),
-                             round_up(pl.a2_q_bytes) + round_up(pl.a2_sf_bytes));
-  uint8_t* reg1 = take(r1);
-  w.x_q = reg1;
-  w.x_sf = reg1 + round_up(pl.x_q_bytes);
-  w.a2_q = reg1;
-  w.a2_sf = reg1 + round_up(pl.a2_q_bytes);
-  // region 2: bf16 gate_up, later down
-  uint8_t* reg2 = take(std::max(pl.gate_up_bytes, pl.down_bytes));
-  w.gate_up = reg2;
-  w.down = reg2;
+  w.x_q = take(pl.x_q_bytes);
+  w.x_sf = take(pl.x_sf_bytes);
+  w.a2_q = take(pl.a2_q_bytes);
+  w.a2_sf = take(pl.a2_sf_bytes);
+  w.down = take(pl.down_bytes);
   const size_t slots = (size_t)pl.s.slots;
   w.idx = (int64_t*)take(slots * 8);
   w.w = (float*)take(slots * 4);
@@ -266,9 +260,11 @@ moe_status_t run_stage(const moe_problem_t* p, const Plan& pl, const void* hidde
   return launch_status(err, "route");
 }
 
+// w13 with act: out unused, the activation goes to act_q / act_sf.
 moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const void* a_q,
                       const void* a_sf, const moe_routing_t* r, const void* w, const float* w_sf,
-                      void* out, hipStream_t stream) {
+                      void* out, hipStream_t stream, bool act = false, void* act_q = nullptr,
+                      void* act_sf = nullptr) {
   moe::GemmArgs g{};
   const bool ue = p->act_quant == MOE_Q_FP8_UE8M0;
   g.a = (const uint8_t*)a_q;
@@ -279,6 +275,9 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
   g.w = (const uint8_t*)w;
   g.w_sf = w_sf;
   g.out = (uint16_t*)out;
+  g.act_q = (uint8_t*)act_q;
+  g.act_sf = (uint8_t*)act_sf;
+  g.act_sf_row = (int)pl.s.a2_sf_row;
   g.tile_list = r->tile_list;
   g.tile_groups = r->tile_list + 1 + 2 * pl.max_tiles;
   g.num_experts = p->num_experts;
@@ -289,8 +288,8 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
   g.Kd = w13 ? p->hidden : p->intermediate;
   g.Nout = w13 ? 2 * p->intermediate : p->hidden;
   const hipError_t err =
-      moe::launch_grouped_gemm(g, pl.s.tile_m, (int)pl.max_tiles, p->act_quant, stream);
-  return launch_status(err, w13 ? "grouped_gemm_w13" : "grouped_gemm_w2");
+      moe::launch_grouped_gemm(g, pl.s.tile_m, (int)pl.max_tiles, p->act_quant, act, stream);
+  return launch_status(err, act ? "grouped_gemm_w13_act" : w13 ? "grouped_gemm_w13" : "grouped_gemm_w2");
 }
 
 moe_status_t run_act(const moe_problem_t* p, const Plan& pl, const void* gate_up,
@@ -379,6 +378,24 @@ moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const
   return run_gemm(p, pl, true, a_q, a_sf, routing, w13, w13_sf, gate_up, (hipStream_t)stream);
 }
 
+moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q, const void* a_sf,
+                                      const moe_routing_t* routing, const void* w13,
+                                      const float* w13_sf, void* a2_q, void* a2_sf,
+                                      void* stream) {
+  CHECK(validate_problem(p, false));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_ptr(a_q, "a_q", 16));
+  CHECK(check_ptr(a_sf, "a_sf", 4));
+  CHECK(check_routing(routing));
+  CHECK(check_ptr(w13, "w13", 16));
+  CHECK(check_ptr(w13_sf, "w13_sf", 4));
+  CHECK(check_ptr(a2_q, "a2_q", 16));
+  CHECK(check_ptr(a2_sf, "a2_sf", 4));
+  const Plan pl = make_plan(p);
+  return run_gemm(p, pl, true, a_q, a_sf, routing, w13, w13_sf, nullptr, (hipStream_t)stream,
+                  true, a2_q, a2_sf);
+}
+
 moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
                              const moe_routing_t* routing, void* a2_q, void* a2_sf,
                              void* stream) {
@@ -441,8 +458,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
   const hipStream_t s = (hipStream_t)stream;
   CHECK(run_stage(p, pl, hidden, expert_num_tokens_in, topk_ids, topk_weights, is_padding, eplb,
                   w.x_q, w.x_sf, w.idx, w.w, &w.routing, w.stage_ws, s));
-  CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, w.gate_up, s));
-  CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s));
+  CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, nullptr, s, true, w.a2_q,
+                 w.a2_sf));
   CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s));
   CHECK(run_reduce(p, w.down, w.routing.slot_row, w.w, out, s));
   return ok();

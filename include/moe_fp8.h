@@ -143,9 +143,10 @@ moe_status_t moe_routing_sizes(const moe_problem_t* p, moe_sizes_t* out);
 /* Device scratch bytes moe_stage needs (host only). */
 moe_status_t moe_stage_workspace_size(const moe_problem_t* p, size_t* bytes);
 
-/* Device workspace bytes moe_forward needs (host only).  It holds the fp8
- * activations, the bf16 gate_up / down intermediates (two ping-pong regions
- * as in HummingExpertsBase.prepare_buffers) and the routing layout. */
+/* Device workspace bytes moe_forward needs (host only).  It holds the staged
+ * fp8 activations, the fp8 w2 input, the bf16 down projection and the
+ * routing layout (the workspace of HummingExpertsBase.prepare_buffers minus
+ * the gate_up buffer, which the fused w13 call never materializes). */
 moe_status_t moe_workspace_size(const moe_problem_t* p, size_t* bytes);
 
 /* Steps 1-2.  hidden: bf16 [T, K] (contiguous) or [E, max_tokens, K]
@@ -172,6 +173,20 @@ moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const
                                   const moe_routing_t* routing, const void* w13,
                                   const float* w13_sf, void* gate_up, void* stream);
 
+/* Steps 3 + 4 in one pass: the w13 GEMM of moe_grouped_gemm_w13 whose result
+ * never leaves the chip; each output row's gate and up halves are rounded to
+ * bf16 (the gate_up buffer's precision) and turned into a2 exactly as
+ * moe_act_requant would, so a2_q / a2_sf are bit-identical to that chain.
+ * The pages fuse the activation into the w2-input quantization
+ * (HummingExpertsBase.process_input with an activation); here it moves one
+ * step earlier, into the producing GEMM.  a2_q fp8 [expert_rows, N], a2_sf per
+ * the activation scheme; rows past an expert's count are not written.
+ * a2_q / a2_sf must not overlap a_q / a_sf. */
+moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q,
+                                      const void* a_sf, const moe_routing_t* routing,
+                                      const void* w13, const float* w13_sf, void* a2_q,
+                                      void* a2_sf, void* stream);
+
 /* Step 4: a2 = quant(silu(gate_up[:, :N]) * gate_up[:, N:]) per 128 columns,
  * computed in fp32 and quantized without an intermediate rounding.
  * a2_q fp8 [expert_rows, N], a2_sf per the activation scheme. */
@@ -191,8 +206,9 @@ moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const
 moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int32_t* slot_row,
                              const float* topk_w, void* out, void* stream);
 
-/* Steps 1-6 on one stream.  Arguments as in moe_stage plus the weights and
- * out bf16 [T, K]; ws: device workspace of moe_workspace_size bytes.
+/* Steps 1-6 on one stream (stage, fused w13 + activation, w2, reduce).
+ * Arguments as in moe_stage plus the weights and out bf16 [T, K]; ws: device
+ * workspace of moe_workspace_size bytes.
  * act_quant must be MOE_Q_FP8_UE8M0 or MOE_Q_FP8_F32. */
 moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
                          const int32_t* expert_num_tokens_in, const int32_t* topk_ids,

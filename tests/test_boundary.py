@@ -41,6 +41,27 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, n), n
 
 
+def _param_counts():
+    """Parameter count of every function include/moe_fp8.h declares."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    out = {}
+    for m in re.finditer(r"\b(moe_\w+)\s*\(([^)]*)\)\s*;", text):
+        params = m.group(2).strip()
+        out[m.group(1)] = 0 if params in ("", "void") else params.count(",") + 1
+    return out
+
+
+def test_binding_signatures_match_the_header(lib):
+    # every export has a ctypes signature of the header's arity (a missing
+    # one makes ctypes truncate pointers to 32-bit ints)
+    counts = _param_counts()
+    assert set(counts) == set(moe.EXPORTS)
+    for name, n in counts.items():
+        argtypes = getattr(lib, name).argtypes
+        assert argtypes is not None, name
+        assert len(argtypes) == n, (name, len(argtypes), n)
+
+
 def _status(fn, *args):
     return fn(*args)
 
@@ -58,8 +79,12 @@ def test_sizes_follow_the_problem(lib):
         assert s["x_sf_row"] == (4 * ((G + 3) // 4) if cfg.act_quant == "ue8m0" else G)
         assert s["tile_m"] in (16, 32, 64, 128, 192, 256)
         ws = moe.workspace_size(p)
-        gate_up = s["expert_rows"] * 2 * cfg.N * 2
-        assert ws >= gate_up + s["expert_rows"] * cfg.N
+        # staged x_q, the w2 input a2 and the bf16 down projection coexist
+        # (the fused w13 call reads x_q while it writes a2)
+        x_q = s["stage_rows"] * cfg.K
+        a2 = s["expert_rows"] * cfg.N
+        down = s["expert_rows"] * cfg.K * 2
+        assert ws >= x_q + a2 + down
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -117,6 +142,16 @@ def test_call_validation_before_launch(lib):
     st = lib.moe_stage(ctypes.byref(pb), V, None, V, V, None, None, V, V, V, V,
                        ctypes.byref(r), V, 1 << 20, None)
     assert st == -1 and "x_sf" in lib.moe_last_error().decode()
+    # the fused w13 + activation call needs its fp8 outputs
+    st = lib.moe_grouped_gemm_w13_act(ctypes.byref(p), V, V, ctypes.byref(r), V, V, None, V,
+                                      None)
+    assert st == -1 and "a2_q" in lib.moe_last_error().decode()
+    st = lib.moe_grouped_gemm_w13_act(ctypes.byref(p), V, V, ctypes.byref(r), V, V, V,
+                                      _fake((1 << 20) + 2), None)
+    assert st == -1 and "a2_sf" in lib.moe_last_error().decode()
+    # ... and is a quantized-activation scheme only
+    st = lib.moe_grouped_gemm_w13_act(ctypes.byref(pb), V, V, ctypes.byref(r), V, V, V, V, None)
+    assert st == -2
 
 
 def test_empty_batch_is_a_noop(lib):

@@ -340,6 +340,59 @@ def test_act_requant_isolated(gpu, name):
     assert np.all(got_q[untouched] == SENTINEL_U8)
 
 
+@pytest.mark.parametrize("tile_m", [16, 32, 64, 128, 192, 256])
+@pytest.mark.parametrize("name", list(SMALL))
+def test_gemm_w13_act_fused_equals_chain(gpu, name, tile_m, monkeypatch):
+    """The fused w13 + activation call against the two calls it replaces, on
+    the oracle's staged inputs (rows outside the counts poisoned): a2 codes and
+    scales bit-identical on every routed row, nothing written elsewhere.  The
+    unfused pair is itself checked against the oracle above; the fused path
+    additionally against the oracle's a2 through check_requant_chain."""
+    monkeypatch.setenv("MOE_TILE_M", str(tile_m))
+    cfg, h, dev, ref = case(name)
+    p = problem(cfg)
+    s = moe.sizes(p)
+    assert s["tile_m"] == tile_m
+    ue = cfg.act_quant == "ue8m0"
+    routing = oracle_routing(p, cfg, ref)
+    vr = valid_rows(cfg, ref)
+    arows = (np.arange(s["stage_rows"]) if cfg.layout != "batched" else vr)
+    a_q = to_dev(poisoned(ref["x_q"], arows, 0x7F))
+    a_sf = O.pack_ue8m0_rows(ref["x_sf"]) if ue else ref["x_sf"]
+    a_sf = to_dev(poisoned(a_sf, arows, sf_poison(ue)))
+    rows, G = s["expert_rows"], cfg.N // 128
+    sf_dtype = torch.uint8 if ue else torch.float32
+
+    gate_up = torch.empty((rows, 2 * cfg.N), dtype=torch.bfloat16, device="cuda")
+    moe.grouped_gemm_w13(p, a_q, a_sf, routing, dev["w13"], dev["w13_sf"], gate_up)
+    want_q = torch.full((rows, cfg.N), SENTINEL_U8, dtype=torch.uint8, device="cuda")
+    want_sf = torch.zeros((rows, s["a2_sf_row"]), dtype=sf_dtype, device="cuda")
+    moe.act_requant(p, gate_up, routing, want_q, want_sf)
+
+    got_q = torch.full((rows, cfg.N), SENTINEL_U8, dtype=torch.uint8, device="cuda")
+    got_sf = torch.full((rows, s["a2_sf_row"]), SENTINEL_U8, dtype=torch.uint8,
+                        device="cuda").view(sf_dtype) if ue else \
+        torch.full((rows, s["a2_sf_row"]), float("nan"), dtype=torch.float32, device="cuda")
+    moe.grouped_gemm_w13_act(p, a_q, a_sf, routing, dev["w13"], dev["w13_sf"], got_q, got_sf)
+    torch.cuda.synchronize()
+    gq, gs, wq, ws = to_np(got_q), to_np(got_sf), to_np(want_q), to_np(want_sf)
+    assert np.array_equal(gq[vr], wq[vr]), f"{name} tile {tile_m}: fused a2 codes differ"
+    if ue:
+        assert np.array_equal(gs[vr], ws[vr]), f"{name} tile {tile_m}: fused exponents differ"
+        assert np.all(gs[vr][:, G:] == 0), "pad bytes of the scale rows must be zero"
+    else:
+        assert np.array_equal(gs[vr].view(np.uint32), ws[vr].view(np.uint32)), \
+            f"{name} tile {tile_m}: fused fp32 scales differ"
+    untouched = np.setdiff1d(np.arange(rows), vr)
+    assert np.all(gq[untouched] == SENTINEL_U8), "fused call wrote rows outside the counts"
+    if ue:
+        assert np.all(gs[untouched] == SENTINEL_U8)
+    else:
+        assert np.all(np.isnan(gs[untouched]))
+    check_requant_chain(gq[vr], gs[vr], ref["a2_q"][vr], ref["a2_sf"][vr], ref["gate_up"][vr],
+                        gemm_abs(cfg, h, ref, "w13")[vr], ue, f"{name} fused tile {tile_m}")
+
+
 @pytest.mark.parametrize("name", list(SMALL))
 def test_topk_reduce_isolated(gpu, name):
     cfg, h, dev, ref = case(name)
@@ -406,7 +459,8 @@ def test_forward_end_to_end(gpu, name):
     check_output(to_np(chain["out"]), ref["out"], f"{name} chained output")
     out = run_forward(cfg, dev)
     check_output(to_np(out), ref["out"], f"{name} moe_forward output")
-    # moe_forward runs the same kernels: identical bits; and it is deterministic
+    # moe_forward runs the fused w13 + activation call, bit-identical to the
+    # unfused pair of the chain: identical bits; and it is deterministic
     assert torch.equal(out.view(torch.int16), chain["out"].view(torch.int16))
     out2 = run_forward(cfg, dev)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
