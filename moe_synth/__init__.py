@@ -59,7 +59,8 @@ class MoeConfig:
     seed: int
     layout: str = "contiguous"          # "contiguous" | "batched"
     max_tokens: int = 0                 # batched layout: rows per expert slab
-    act_quant: str = "ue8m0"            # "ue8m0" | "fp32"
+    act_quant: str = "ue8m0"            # "ue8m0" | "fp32" (128-groups) | "mxfp8" (32-groups)
+    weight_quant: str = "fp8_block128"  # "fp8_block128" | "mxfp8" | "mxfp4"
     routing: str = "uniform"            # "uniform" | "zipf"
     zipf_s: float = 1.1
     pad_frac: float = 0.0
@@ -90,6 +91,18 @@ CONFIGS = {
 }
 
 
+# The same DeepSeek-V3-shaped prefill batch with the MX scheme pairs the
+# Humming experts accept: (kMxfp8Static weights, kMxfp8Dynamic activations)
+# and (kMxfp4Static, kMxfp8Dynamic); plus small cases for parity tests.
+MX_CONFIGS = {
+    "dsv3_prefill_mxfp8": MoeConfig("dsv3_prefill_mxfp8", T=4096, E=256, top_k=8, K=7168,
+                                    N=2048, seed=6, routing="zipf", zipf_s=1.1,
+                                    pad_frac=0.05, act_quant="mxfp8", weight_quant="mxfp8"),
+}
+
+ALL_CONFIGS = {**CONFIGS, **MX_CONFIGS}
+
+
 def _gen(device, seed: int, stream: str) -> torch.Generator:
     g = torch.Generator(device=device)
     g.manual_seed(seed * 1_000_003 + _STREAMS.index(stream) * 7919 + 17)
@@ -107,18 +120,59 @@ def _quantize_weight_blocks(w: torch.Tensor):
     return q.view(R, C).view(torch.uint8), scale
 
 
+# e2m1 magnitudes by 3-bit code (OCP MX fp4: 1 sign, 2 exponent, 1 mantissa bit)
+_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _quantize_weight_mx(w: torch.Tensor, fp4: bool):
+    """fp32 [R, C] -> MX codes + E8M0 scales per 32 consecutive columns, with
+    the OCP MX shared-exponent rule: exponent = floor(log2(block amax)) minus
+    the element format's largest exponent (8 for e4m3, 2 for e2m1), elements
+    rounded to nearest and saturated.  e4m3: codes uint8 [R, C]; e2m1: two
+    codes per byte, column 2j in the low nibble, uint8 [R, C/2].  Scales uint8
+    [R, C/32] (2^(byte - 127))."""
+    R, C = w.shape
+    blocks = w.view(R, C // 32, 32)
+    amax = blocks.abs().amax(dim=2)
+    emax = 2 if fp4 else 8
+    shared = torch.floor(torch.log2(amax.clamp_min(2.0 ** -120))) - emax
+    shared = shared.clamp(-127, 127)
+    v = blocks / torch.exp2(shared)[:, :, None]
+    if not fp4:
+        q = v.clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8).view(R, C)
+    else:
+        mags = torch.tensor(_E2M1, device=w.device)
+        mid = (mags[1:] + mags[:-1]) / 2
+        code = torch.bucketize(v.abs().clamp(max=6.0), mid).to(torch.uint8)
+        code = code | ((v < 0).to(torch.uint8) << 3)
+        code = code.view(R, C)
+        q = code[:, 0::2] | (code[:, 1::2] << 4)
+    return q.contiguous(), (shared + 127).to(torch.uint8)
+
+
 def _draw_weights(cfg: MoeConfig, device, which: str):
-    """w13 [E_log, 2N, K] or w2 [E_log, K, N] fp8 codes + block scales,
-    one expert at a time so the fp32 draw never exceeds one expert."""
+    """w13 [E_log, 2N, K] or w2 [E_log, K, N] codes + scales, one expert at a
+    time so the fp32 draw never exceeds one expert.  fp8_block128: e4m3 codes
+    and fp32 scales per 128x128 block; mxfp8 / mxfp4: MX codes and E8M0
+    scales per row and 32 columns."""
     g = _gen(device, cfg.seed, which)
     rows, cols = (2 * cfg.N, cfg.K) if which == "w13" else (cfg.K, cfg.N)
-    q = torch.empty((cfg.E_log, rows, cols), dtype=torch.uint8, device=device)
-    s = torch.empty((cfg.E_log, rows // 128, cols // 128), dtype=torch.float32,
-                    device=device)
+    if cfg.weight_quant == "fp8_block128":
+        q = torch.empty((cfg.E_log, rows, cols), dtype=torch.uint8, device=device)
+        s = torch.empty((cfg.E_log, rows // 128, cols // 128), dtype=torch.float32,
+                        device=device)
+    else:
+        fp4 = cfg.weight_quant == "mxfp4"
+        q = torch.empty((cfg.E_log, rows, cols // 2 if fp4 else cols), dtype=torch.uint8,
+                        device=device)
+        s = torch.empty((cfg.E_log, rows, cols // 32), dtype=torch.uint8, device=device)
     for e in range(cfg.E_log):
         w = torch.randn((rows, cols), generator=g, device=device,
                         dtype=torch.float32) * cfg.weight_std
-        q[e], s[e] = _quantize_weight_blocks(w)
+        if cfg.weight_quant == "fp8_block128":
+            q[e], s[e] = _quantize_weight_blocks(w)
+        else:
+            q[e], s[e] = _quantize_weight_mx(w, cfg.weight_quant == "mxfp4")
     return q, s
 
 

@@ -13,7 +13,15 @@ Sources (all from the vLLM API documentation pages on the subject):
   [HUM]    "vllm.model_executor.layers.fused_moe.experts.fused_humming_moe"
            (pull-request 58588 build): ``BatchedHummingGroupedExperts.apply``,
            ``HummingGroupedExperts.apply``, ``HummingExpertsBase``
-           (``process_input``, ``get_buffer_metas``).
+           (``process_input``, ``get_buffer_metas``,
+           ``_supports_quant_scheme``).
+
+Schemes: block fp8 (kFp8Static128BlockSym weights with 128x128 fp32 scales,
+kFp8Dynamic128Sym activations with UE8M0 or fp32 per-128 scales) and MX
+(kMxfp8Static / kMxfp4Static weights with one E8M0 scale per row and 32
+columns, kMxfp8Dynamic activations: the staging quantizer with 32-column
+groups and E8M0 scales, which [STAGE] ``_resolve_hidden_quant`` maps to
+GROUP_K = 32, USE_UE8M0).
 
 Number formats.  bf16 -> fp64 and e4m3fn -> fp64 are exact.  fp32 steps are
 numpy float32 operations (IEEE binary32, round to nearest even).  Block
@@ -35,7 +43,11 @@ reason, in the design notes):
     unrouted; an expert's rows are ordered by ascending (token, slot);
   * expert replica choice under EPLB is ``token mod replica_count`` (parity
     unpinned: the pages do not show ``eplb_map_and_record``'s body; only the
-    invariants it must satisfy are tested).
+    invariants it must satisfy are tested);
+  * MX: the w2 input (SiLU(gate)*up) is quantized like the staged hidden
+    states, 32-column groups with E8M0 scales (Humming's own input quantizer
+    is not shown); E8M0 byte e means 2^(e-127); e2m1 codes are packed two per
+    byte, even column in the low nibble.
 """
 from __future__ import annotations
 
@@ -126,8 +138,9 @@ def ue8m0_decode(e) -> np.ndarray:
 # O2: per-128-group fp8 quantization  [STAGE, _quantize_fp8_groups]
 # ---------------------------------------------------------------------------
 
-def quantize_groups(x32, ue8m0: bool):
-    """Quantize rows of fp32 values in groups of 128 consecutive columns.
+def quantize_groups(x32, ue8m0: bool, group: int = GROUP):
+    """Quantize rows of fp32 values in groups of ``group`` consecutive columns
+    (128 for the block scheme, 32 for MXFP8; any divisor of 128 for [STAGE]).
 
     Per group, in fp32: amax = max|x|, amax = max(amax, 1e-4),
     s = amax / 448.  UE8M0: the scale is rounded up to a power of two by
@@ -141,8 +154,8 @@ def quantize_groups(x32, ue8m0: bool):
     """
     x32 = np.asarray(x32, dtype=np.float32)
     rows, cols = x32.shape
-    assert cols % GROUP == 0
-    g = x32.reshape(rows, cols // GROUP, GROUP)
+    assert cols % group == 0
+    g = x32.reshape(rows, cols // group, group)
     amax = np.max(np.abs(g), axis=2)
     amax = np.maximum(amax, np.float32(1.0e-4))
     s = (amax / np.float32(FP8_MAX)).astype(np.float32)
@@ -159,6 +172,29 @@ def quantize_groups(x32, ue8m0: bool):
     v = (g * recip[:, :, None]).astype(np.float32)
     codes = e4m3_encode(v).reshape(rows, cols)
     return codes, stored
+
+
+# ---------------------------------------------------------------------------
+# MX element formats (OCP Microscaling: E8M0 scales, e4m3 / e2m1 elements)
+# ---------------------------------------------------------------------------
+
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0,
+                        -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0])
+
+
+def e2m1_decode(nibbles) -> np.ndarray:
+    """4-bit e2m1 codes (sign bit 3, exponent bits 2..1 with bias 1, mantissa
+    bit 0; exponent 0 is subnormal: 0.5 * mantissa) -> fp64."""
+    return E2M1_VALUES[np.asarray(nibbles, dtype=np.int64) & 0xF]
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    """uint8 [..., C/2] -> nibbles [..., C]: column 2j is byte j's low nibble."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
 
 
 def scale_values(stored, ue8m0: bool) -> np.ndarray:
@@ -286,6 +322,53 @@ def block_scaled_gemm_f64(a_codes, a_scale, w_codes, w_scale) -> np.ndarray:
     return out
 
 
+def mx_gemm_f64(a_codes, a_exps, w_codes, w_exps, fp4: bool) -> np.ndarray:
+    """out[m, n] = sum_b 2^(ea[m, b] - 127) * 2^(ew[n, b] - 127)
+                          * sum_{c in block b} a[m, c] * w[n, c]
+    over 32-column blocks b (the MX scheme pairs (kMxfp8Static or
+    kMxfp4Static, kMxfp8Dynamic) of [HUM, _supports_quant_scheme]).
+
+    a_codes uint8 [m, C] e4m3fn, a_exps uint8 [m, C/32]; w_codes uint8 [n, C]
+    e4m3fn or [n, C/2] packed e2m1 (fp4), w_exps uint8 [n, C/32].  Result in
+    fp64; the block sums are exact (at most 8-bit products, 32 terms).
+    """
+    a = e4m3_decode(a_codes)
+    w = e2m1_decode(unpack_fp4(w_codes)) if fp4 else e4m3_decode(w_codes)
+    m, C = a.shape
+    n = w.shape[0]
+    G = C // 32
+    a_b = a.reshape(m, G, 32).transpose(1, 0, 2)            # [G, m, 32]
+    w_b = w.reshape(n, G, 32).transpose(1, 2, 0)            # [G, 32, n]
+    partial = np.matmul(a_b, w_b)                           # [G, m, n], exact
+    sa = ue8m0_decode(a_exps)                               # [m, G]
+    sw = ue8m0_decode(w_exps)                               # [n, G]
+    out = np.zeros((m, n), dtype=np.float64)
+    for b in range(G):
+        out += partial[b] * sa[:, b:b + 1] * sw[None, :, b]
+    return out
+
+
+# ---------------------------------------------------------------------------
+# scheme selection
+# ---------------------------------------------------------------------------
+
+def act_group(cfg) -> int:
+    """Activation quantization group: 32 for MXFP8, else 128."""
+    return 32 if cfg.act_quant == "mxfp8" else GROUP
+
+
+def act_e8m0(cfg) -> bool:
+    """Activation scales are E8M0 exponent bytes (else fp32)."""
+    return cfg.act_quant in ("ue8m0", "mxfp8")
+
+
+def expert_gemm(cfg, a_codes, a_stored, w, w_sf) -> np.ndarray:
+    """One expert's GEMM in the workload's scheme (fp64, before rounding)."""
+    if cfg.weight_quant == "fp8_block128":
+        return block_scaled_gemm_f64(a_codes, scale_values(a_stored, act_e8m0(cfg)), w, w_sf)
+    return mx_gemm_f64(a_codes, a_stored, w, w_sf, fp4=cfg.weight_quant == "mxfp4")
+
+
 # ---------------------------------------------------------------------------
 # O6: SiLU(gate) * up, re-quantized  [HUM, process_input('w2', activation=...)]
 # ---------------------------------------------------------------------------
@@ -299,8 +382,8 @@ def silu_mul_f32(gate_up_bits, N: int) -> np.ndarray:
     return h.astype(np.float32)
 
 
-def act_requant(gate_up_bits, N: int, ue8m0: bool):
-    return quantize_groups(silu_mul_f32(gate_up_bits, N), ue8m0)
+def act_requant(gate_up_bits, N: int, ue8m0: bool, group: int = GROUP):
+    return quantize_groups(silu_mul_f32(gate_up_bits, N), ue8m0, group)
 
 
 # ---------------------------------------------------------------------------
@@ -355,7 +438,7 @@ def stage(h: dict):
     """Steps 1-2: quantize the hidden rows that will be read, repack the
     routing and build the expert layout."""
     cfg = h["cfg"]
-    ue8m0 = cfg.act_quant == "ue8m0"
+    ue8m0, grp = act_e8m0(cfg), act_group(cfg)
     ids, w, load = repack_topk(h["topk_ids"], h["topk_weights"], h["is_padding"],
                                h["eplb"], num_physical=cfg.E)
     batched = cfg.layout == "batched"
@@ -369,11 +452,11 @@ def stage(h: dict):
             + [np.zeros(0, dtype=np.int64)]).astype(np.int64)
     else:
         valid_rows = np.arange(hid.shape[0])
-    G = cfg.K // GROUP
+    G = cfg.K // grp
     x_q = np.zeros(hid.shape, dtype=np.uint8)
     x_sf = np.zeros((hid.shape[0], G), dtype=np.uint8 if ue8m0 else np.float32)
     x = bf16_to_f64(hid[valid_rows]).astype(np.float32)
-    x_q[valid_rows], x_sf[valid_rows] = quantize_groups(x, ue8m0)
+    x_q[valid_rows], x_sf[valid_rows] = quantize_groups(x, ue8m0, grp)
     return {"ids": ids, "weights": w, "load": load, "x_q": x_q, "x_sf": x_sf,
             **lay}
 
@@ -385,7 +468,7 @@ def forward(h: dict) -> dict:
     -> E * max_tokens rows of which only the first counts[e] of each slab
     are computed (the rest stay 0 here and are never compared)."""
     cfg = h["cfg"]
-    ue8m0 = cfg.act_quant == "ue8m0"
+    ue8m0, grp = act_e8m0(cfg), act_group(cfg)
     st = stage(h)
     E, N, K = cfg.E, cfg.N, cfg.K
     batched = cfg.layout == "batched"
@@ -398,10 +481,9 @@ def forward(h: dict) -> dict:
         rows_total = int(st["offsets"][-1])
     gate_up = np.zeros((rows_total, 2 * N), dtype=np.uint16)
     a2_q = np.zeros((rows_total, N), dtype=np.uint8)
-    a2_sf = np.zeros((rows_total, N // GROUP),
+    a2_sf = np.zeros((rows_total, N // grp),
                      dtype=np.uint8 if ue8m0 else np.float32)
     down = np.zeros((rows_total, K), dtype=np.uint16)
-    xs = scale_values(st["x_sf"], ue8m0)
     for e in range(E):
         n_e = int(counts[e])
         if n_e == 0:
@@ -413,13 +495,12 @@ def forward(h: dict) -> dict:
             lo = int(st["offsets"][e])
             rows = np.arange(lo, lo + n_e)
             a_rows = st["row_src"][rows]
-        gu = block_scaled_gemm_f64(st["x_q"][a_rows], xs[a_rows],
-                                   h["w13"][e], h["w13_sf"][e])
+        gu = expert_gemm(cfg, st["x_q"][a_rows], st["x_sf"][a_rows],
+                         h["w13"][e], h["w13_sf"][e])
         gate_up[rows] = bf16_round(gu)
-        q2, s2 = act_requant(gate_up[rows], N, ue8m0)
+        q2, s2 = act_requant(gate_up[rows], N, ue8m0, grp)
         a2_q[rows], a2_sf[rows] = q2, s2
-        dn = block_scaled_gemm_f64(q2, scale_values(s2, ue8m0),
-                                   h["w2"][e], h["w2_sf"][e])
+        dn = expert_gemm(cfg, q2, s2, h["w2"][e], h["w2_sf"][e])
         down[rows] = bf16_round(dn)
     out = topk_reduce(down, st["slot_row"], st["weights"])
     return {**st, "gate_up": gate_up, "a2_q": a2_q, "a2_sf": a2_sf,
@@ -435,7 +516,7 @@ def forward_tokens(h: dict, tokens, st: dict | None = None) -> dict:
     ``{"stage": st, "rows": {row: {...}}, "out": {t: bf16 bits [K]}}``.
     """
     cfg = h["cfg"]
-    ue8m0 = cfg.act_quant == "ue8m0"
+    ue8m0, grp = act_e8m0(cfg), act_group(cfg)
     N, K = cfg.N, cfg.K
     if st is None:
         st = stage_routing_only(h)
@@ -454,12 +535,10 @@ def forward_tokens(h: dict, tokens, st: dict | None = None) -> dict:
         for (t, j, r) in lst:
             a_row = r if cfg.layout == "batched" else t
             x = bf16_to_f64(hid[a_row:a_row + 1]).astype(np.float32)
-            xq, xsf = quantize_groups(x, ue8m0)
-            gu = bf16_round(block_scaled_gemm_f64(xq, scale_values(xsf, ue8m0),
-                                                  w13, w13s))
-            q2, s2 = act_requant(gu, N, ue8m0)
-            dn = bf16_round(block_scaled_gemm_f64(q2, scale_values(s2, ue8m0),
-                                                  w2, w2s))
+            xq, xsf = quantize_groups(x, ue8m0, grp)
+            gu = bf16_round(expert_gemm(cfg, xq, xsf, w13, w13s))
+            q2, s2 = act_requant(gu, N, ue8m0, grp)
+            dn = bf16_round(expert_gemm(cfg, q2, s2, w2, w2s))
             rows_info[r] = {"token": t, "slot": j, "expert": e, "x_q": xq[0],
                             "x_sf": xsf[0], "gate_up": gu[0], "a2_q": q2[0],
                             "a2_sf": s2[0], "down": dn[0]}

@@ -367,6 +367,92 @@ def test_eplb_map_invariants():
 # --------------------------------------------------------------------------
 # block-scaled GEMM  [fused_humming_moe, humming_forward with 128x128 fp32
 # weight block scales and per-128 activation group scales]
+def test_group32_quantizer_exact_rationals():
+    """32-column groups (MXFP8 activations): every group's exponent from the
+    closed form in exact rationals, a sample of codes by exact nearest-even
+    encoding, and the group layout (column c belongs to group c // 32)."""
+    rng = np.random.default_rng(18)
+    rows, cols = 60, 256
+    mag = np.exp2(rng.uniform(-20, 12, (rows, cols // 32)))
+    x = (rng.standard_normal((rows, cols)) * np.repeat(mag, 32, axis=1)).astype(np.float32)
+    x[3, 32:64] = 0.0                                   # an all-zero group
+    codes, e = O.quantize_groups(x, ue8m0=True, group=32)
+    assert e.shape == (rows, cols // 32)
+    floor = Fraction(float(np.float32(1e-4)))
+    for r in range(rows):
+        for g in range(cols // 32):
+            A = max(Fraction(float(np.abs(x[r, 32 * g:32 * g + 32]).max())), floor)
+            assert int(e[r, g]) == min(max(127 + _ceil_log2(A / 448), 1), 254)
+    assert int(e[3, 1]) == 105 and np.all(codes[3, 32:64] == 0)
+    for _ in range(3000):
+        r, c = int(rng.integers(rows)), int(rng.integers(cols))
+        val = Fraction(float(x[r, c])) / Fraction(2) ** (int(e[r, c // 32]) - 127)
+        assert codes[r, c] == _frac_encode(val, bool(np.signbit(x[r, c])))
+
+
+def test_e2m1_table_from_bit_fields():
+    # OCP MX fp4: sign bit 3, two exponent bits (bias 1), one mantissa bit;
+    # exponent field 0 is subnormal (0.5 * mantissa)
+    for code in range(16):
+        s, ex, m = code >> 3, (code >> 1) & 3, code & 1
+        mag = Fraction(m, 2) if ex == 0 else Fraction(2) ** (ex - 1) * (1 + Fraction(m, 2))
+        assert O.e2m1_decode(code) == (-1) ** s * float(mag)
+        assert np.signbit(O.e2m1_decode(code)) == bool(s)
+    assert O.e2m1_decode(0x7) == 6.0 and O.e2m1_decode(0xF) == -6.0
+
+
+def test_unpack_fp4_low_nibble_first():
+    got = O.unpack_fp4(np.array([[0x21, 0xF0, 0x7A]], np.uint8))
+    assert got.tolist() == [[1, 2, 0, 15, 10, 7]]
+
+
+def _mx_dense(codes, exps, fp4):
+    """Dequantize MX operands element by element (independent of the oracle's
+    GEMM): value = element * 2^(e - 127) with e the byte of column c // 32."""
+    if fp4:
+        nib = np.empty((codes.shape[0], codes.shape[1] * 2), np.int64)
+        for c in range(nib.shape[1]):
+            byte = codes[:, c // 2].astype(np.int64)
+            nib[:, c] = (byte >> 4) if c % 2 else (byte & 15)
+        vals = np.array([float(O.e2m1_decode(n)) for n in range(16)])[nib]
+    else:
+        vals = O.e4m3_decode(codes)
+    scale = np.exp2(np.repeat(exps.astype(np.float64), 32, axis=1) - 127)
+    return vals * scale
+
+
+@pytest.mark.parametrize("fp4", [False, True])
+def test_mx_gemm_equals_dense_dequantized_matmul(fp4):
+    rng = np.random.default_rng(24 + fp4)
+    m, n, C = 29, 96, 256
+    a = _finite_codes(rng, (m, C))
+    ea = rng.integers(100, 140, (m, C // 32)).astype(np.uint8)
+    w = (rng.integers(0, 256, (n, C // 2)).astype(np.uint8) if fp4
+         else _finite_codes(rng, (n, C)))
+    ew = rng.integers(110, 130, (n, C // 32)).astype(np.uint8)
+    got = O.mx_gemm_f64(a, ea, w, ew, fp4)
+    want = _mx_dense(a, ea, False) @ _mx_dense(w, ew, fp4).T
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+@pytest.mark.parametrize("fp4", [False, True])
+def test_mx_gemm_identity_weights(fp4):
+    rng = np.random.default_rng(26)
+    m, C = 12, 128
+    a = _finite_codes(rng, (m, C))
+    ea = rng.integers(110, 135, (m, C // 32)).astype(np.uint8)
+    ew = np.full((C, C // 32), 127, np.uint8)
+    if fp4:      # e2m1 code 2 is 1.0
+        nib = np.zeros((C, C), np.uint8)
+        nib[np.arange(C), np.arange(C)] = 2
+        w = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)
+    else:        # e4m3 code 0x38 is 1.0
+        w = np.zeros((C, C), np.uint8)
+        w[np.arange(C), np.arange(C)] = 0x38
+    got = O.mx_gemm_f64(a, ea, w, ew, fp4)
+    assert np.array_equal(got, _mx_dense(a, ea, False))
+
+
 # --------------------------------------------------------------------------
 
 def _finite_codes(rng, shape):
@@ -450,10 +536,15 @@ def _dense_ffn(h, st):
             e = st["ids"][t, j]
             if e < 0:
                 continue
-            W13 = O.e4m3_decode(h["w13"][e]) * np.repeat(np.repeat(
-                h["w13_sf"][e].astype(np.float64), 128, 0), 128, 1)
-            W2 = O.e4m3_decode(h["w2"][e]) * np.repeat(np.repeat(
-                h["w2_sf"][e].astype(np.float64), 128, 0), 128, 1)
+            if cfg.weight_quant == "fp8_block128":
+                W13 = O.e4m3_decode(h["w13"][e]) * np.repeat(np.repeat(
+                    h["w13_sf"][e].astype(np.float64), 128, 0), 128, 1)
+                W2 = O.e4m3_decode(h["w2"][e]) * np.repeat(np.repeat(
+                    h["w2_sf"][e].astype(np.float64), 128, 0), 128, 1)
+            else:
+                fp4 = cfg.weight_quant == "mxfp4"
+                W13 = _mx_dense(h["w13"][e], h["w13_sf"][e], fp4)
+                W2 = _mx_dense(h["w2"][e], h["w2_sf"][e], fp4)
             gu = W13 @ x[t]
             act = gu[:N] / (1 + np.exp(-gu[:N])) * gu[N:]
             out[t] += st["weights"][t, j] * (W2 @ act)
@@ -463,6 +554,22 @@ def _dense_ffn(h, st):
 def test_tiny_layer_tracks_unquantized_ffn():
     h = O.host_inputs(moe_synth.make_inputs(moe_synth.CONFIGS["tiny"]))
     r = O.forward(h)
+    ref = _dense_ffn(h, r)
+    got = O.bf16_to_f64(r["out"])
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert 1e-3 < rel < 0.08, rel
+
+
+@pytest.mark.parametrize("wq", ["mxfp8", "mxfp4"])
+def test_tiny_mx_layer_tracks_unquantized_ffn(wq):
+    """MXFP8 activations with MXFP8 / MXFP4 weights: the quantized layer stays
+    within a few percent of the same weights with unquantized activations,
+    and is not identical to it (the activations really are quantized)."""
+    cfg = moe_synth.custom(T=16, E=4, top_k=2, K=256, N=512, seed=1,
+                           act_quant="mxfp8", weight_quant=wq)
+    h = O.host_inputs(moe_synth.make_inputs(cfg))
+    r = O.forward(h)
+    assert r["x_sf"].shape == (16, 256 // 32) and r["a2_sf"].shape[1] == 512 // 32
     ref = _dense_ffn(h, r)
     got = O.bf16_to_f64(r["out"])
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
