@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="dsv3_prefill", choices=list(moe_synth.CONFIGS))
+    ap.add_argument("--config", default="dsv3_prefill", choices=list(moe_synth.ALL_CONFIGS))
     ap.add_argument("--kernel-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -72,18 +72,23 @@ class KernelTimer:
 def algorithmic(cfg, counts, T_valid):
     """Minimum HBM bytes and flops of each step (one launch each)."""
     K, N, k = cfg.K, cfg.N, cfg.top_k
-    GK, GN = K // 128, N // 128
     M = int(counts.sum())
     touched = int((counts > 0).sum())
-    ue = cfg.act_quant == "ue8m0"
-    sfb = 1 if ue else 4
+    group = 32 if cfg.act_quant == "mxfp8" else 128
+    sfb = 4 if cfg.act_quant == "fp32" else 1       # bytes per activation scale
+    GK, GN = K // group, N // group
     rows_in = int(counts.sum()) if cfg.layout == "batched" else cfg.T
     a = {}
     a["stage"] = rows_in * K * 2 + rows_in * K + rows_in * GK * sfb
-    w13_in = touched * (2 * N * K + (2 * N // 128) * GK * 4) + T_valid * (K + GK * sfb)
+    if cfg.weight_quant == "fp8_block128":
+        w13_sf, w2_sf = (2 * N // 128) * (K // 128) * 4, (K // 128) * (N // 128) * 4
+    else:                                            # E8M0 byte per row and 32 columns
+        w13_sf, w2_sf = 2 * N * (K // 32), K * (N // 32)
+    w_elem = 0.5 if cfg.weight_quant == "mxfp4" else 1
+    w13_in = touched * (2 * N * K * w_elem + w13_sf) + T_valid * (K + GK * sfb)
     a["w13_act_bytes"] = w13_in + M * (N + GN * sfb)        # fp8 a2 + scales out
     a["w13_flops"] = 2.0 * M * 2 * N * K
-    a["w2_bytes"] = (touched * (K * N + (K // 128) * GN * 4) + M * (N + GN * sfb) + M * K * 2)
+    a["w2_bytes"] = (touched * (K * N * w_elem + w2_sf) + M * (N + GN * sfb) + M * K * 2)
     a["w2_flops"] = 2.0 * M * N * K
     a["reduce"] = M * K * 2 + cfg.T * K * 2 + cfg.T * k * 8
     return a
@@ -135,11 +140,10 @@ def profile_pass(p, cfg, inp, out):
     torch.cuda.synchronize()
     del src, dst
     s = moe.sizes(p)
-    ue = p.act_quant == moe.Q_FP8_UE8M0
     bufs = moe.alloc_stage_outputs(p)
     a2_q = torch.empty((s["expert_rows"], cfg.N), dtype=torch.uint8, device="cuda")
     a2_sf = torch.empty((s["expert_rows"], s["a2_sf_row"]),
-                        dtype=torch.uint8 if ue else torch.float32, device="cuda")
+                        dtype=moe.scale_dtype(p), device="cuda")
     down = torch.empty((s["expert_rows"], cfg.K), dtype=torch.bfloat16, device="cuda")
     moe.stage(p, inp["hidden"], inp["topk_ids"], inp["topk_weights"], bufs, inp["is_padding"],
               inp["expert_num_tokens"], inp["eplb"])
@@ -176,7 +180,7 @@ def main():
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the expert layer "
               "is not sharded across GPUs here.", file=sys.stderr)
         sys.exit(2)
-    cfg = moe_synth.CONFIGS[args.config]
+    cfg = moe_synth.ALL_CONFIGS[args.config]
     torch.cuda.set_device(0)
     log(f"[bench] generating {cfg.name} inputs on the GPU")
     inp = moe_synth.make_inputs(cfg, "cuda")
@@ -211,10 +215,9 @@ def main():
     # ---- per-kernel timing through the separate entry points -------------
     s = moe.sizes(p)
     bufs = moe.alloc_stage_outputs(p)
-    ue = p.act_quant == moe.Q_FP8_UE8M0
     a2_q = torch.empty((s["expert_rows"], cfg.N), dtype=torch.uint8, device="cuda")
     a2_sf = torch.empty((s["expert_rows"], s["a2_sf_row"]),
-                        dtype=torch.uint8 if ue else torch.float32, device="cuda")
+                        dtype=moe.scale_dtype(p), device="cuda")
     down = torch.empty((s["expert_rows"], cfg.K), dtype=torch.bfloat16, device="cuda")
     flush_buf = torch.empty(1 << 28, dtype=torch.int32, device="cuda")   # 1 GiB > MALL
 

@@ -18,7 +18,10 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_fp8.so")
 
-Q_FP8_UE8M0, Q_FP8_F32, Q_BF16 = 0, 1, 2
+Q_FP8_UE8M0, Q_FP8_F32, Q_BF16, Q_MXFP8 = 0, 1, 2, 3
+W_FP8_BLOCK128, W_MXFP8, W_MXFP4 = 0, 1, 2
+_ACT_QUANT = {"ue8m0": Q_FP8_UE8M0, "fp32": Q_FP8_F32, "bf16": Q_BF16, "mxfp8": Q_MXFP8}
+_WEIGHT_QUANT = {"fp8_block128": W_FP8_BLOCK128, "mxfp8": W_MXFP8, "mxfp4": W_MXFP4}
 LAYOUT_CONTIGUOUS, LAYOUT_BATCHED = 0, 1
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_LAUNCH"}
@@ -33,7 +36,7 @@ class MoeError(RuntimeError):
 class _Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden", "intermediate", "num_experts", "top_k", "layout",
-        "max_tokens_per_expert", "act_quant")]
+        "max_tokens_per_expert", "act_quant", "weight_quant")]
 
 
 class _Eplb(ctypes.Structure):
@@ -123,19 +126,20 @@ class Problem:
     layout: int = LAYOUT_CONTIGUOUS
     max_tokens_per_expert: int = 0
     act_quant: int = Q_FP8_UE8M0
+    weight_quant: int = W_FP8_BLOCK128
 
     def c(self) -> _Problem:
         return _Problem(self.num_tokens, self.hidden, self.intermediate, self.num_experts,
-                        self.top_k, self.layout, self.max_tokens_per_expert, self.act_quant)
+                        self.top_k, self.layout, self.max_tokens_per_expert, self.act_quant,
+                        self.weight_quant)
 
     @staticmethod
     def from_config(cfg, act_quant: Optional[int] = None) -> "Problem":
         """From a ``moe_synth.MoeConfig``."""
-        q = act_quant if act_quant is not None else (
-            Q_FP8_UE8M0 if cfg.act_quant == "ue8m0" else Q_FP8_F32)
+        q = act_quant if act_quant is not None else _ACT_QUANT[cfg.act_quant]
         return Problem(cfg.T, cfg.K, cfg.N, cfg.E, cfg.top_k,
                        LAYOUT_BATCHED if cfg.layout == "batched" else LAYOUT_CONTIGUOUS,
-                       cfg.max_tokens, q)
+                       cfg.max_tokens, q, _WEIGHT_QUANT[cfg.weight_quant])
 
 
 def sizes(p: Problem) -> dict:
@@ -171,18 +175,21 @@ def _routing(r: dict) -> _Routing:
                                           "slot_row", "tile_list")])
 
 
+def scale_dtype(p: Problem):
+    """torch dtype of the activation scales (E8M0 bytes or fp32)."""
+    return torch.float32 if p.act_quant == Q_FP8_F32 else torch.uint8
+
+
 def alloc_stage_outputs(p: Problem, device="cuda") -> dict:
     """Caller-side buffers for moe_stage (allocated by torch)."""
     s = sizes(p)
     dev = torch.device(device)
-    ue = p.act_quant == Q_FP8_UE8M0
     out = {
         "x_q": torch.empty((s["stage_rows"], p.hidden),
                            dtype=torch.bfloat16 if p.act_quant == Q_BF16 else torch.uint8,
                            device=dev),
         "x_sf": None if p.act_quant == Q_BF16 else torch.empty(
-            (s["stage_rows"], s["x_sf_row"]), dtype=torch.uint8 if ue else torch.float32,
-            device=dev),
+            (s["stage_rows"], s["x_sf_row"]), dtype=scale_dtype(p), device=dev),
         "topk_idx": torch.empty((p.num_tokens, p.top_k), dtype=torch.int64, device=dev),
         "topk_w": torch.empty((p.num_tokens, p.top_k), dtype=torch.float32, device=dev),
         "expert_num_tokens": torch.empty(p.num_experts, dtype=torch.int32, device=dev),

@@ -58,7 +58,14 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
-// ---- the per-128 group scale ------------------------------------------------
+// max over a quad of 4 lanes (quad_perm [1,0,3,2], [2,3,0,1])
+__device__ __forceinline__ float quad_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  return v;
+}
+
+// ---- the per-group scale -----------------------------------------------------
 // Given the group's amax: floor it at 1e-4, divide by 448 (correctly rounded
 // fp32 division), and for UE8M0 round the scale up to a power of two through
 // its fp32 bit fields (exponent + 1 when the mantissa is non-zero, clamped to

@@ -143,6 +143,19 @@ __device__ __forceinline__ void wait_stages_l(int after) {
   else
     wait_then_barrier<3 * L>();
 }
+// Wait until at most n (wave-uniform, <= NMAX) LDS-bound loads are in
+// flight, then barrier.
+template <int NMAX, int N = 0>
+__device__ __forceinline__ void wait_n_then_barrier(int n) {
+  if constexpr (N < NMAX) {
+    if (n != N) {
+      wait_n_then_barrier<NMAX, N + 1>(n);
+      return;
+    }
+  }
+  wait_then_barrier<N>();
+}
+
 template <int LMAX, int L = 0>
 __device__ __forceinline__ void stage_landed(int loads_per_stage, int after) {
   if constexpr (L < LMAX) {
@@ -201,11 +214,27 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // out so that each wave holds 32 gate rows followed by the 32 matching up
 // rows; the epilogue turns the result into silu(gate) * up, quantized per
 // 128 columns, instead of storing it.
-template <class S, bool UE8M0, bool ACT>
+//
+// SC selects the scale scheme: kQuantUe8m0 / kQuantF32 (128x128 fp32 weight
+// block scales, per-128 activation scales, fp32 promotion per k-step) or
+// kQuantMxfp8 (E8M0 scale per row and 32 columns on both operands, handed
+// to the MFMA itself, which then accumulates across k-steps directly).
+template <class S, int SC, bool ACT>
 __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_kernel(
     const GemmArgs p) {
   static_assert(!ACT || (S::BN == 256 && S::WN == 4 && S::TN == 4), "fused activation tile");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S::LDS_BYTES];
+  constexpr bool MX = SC == kQuantMxfp8;
+  constexpr bool UE8M0 = SC == kQuantUe8m0;
+  // MX: the weight rows' E8M0 bytes of 4 k-steps (16 per row) arrive with
+  // every fourth stage into one of two panel slots after the ring; the
+  // block scheme keeps its fp32 weight-scale panel there instead
+  constexpr int STAGE = S::STAGE_BYTES;
+  constexpr int WSC_SLOT = S::BN * 16;
+  constexpr int PANEL = MX ? 2 * WSC_SLOT : S::NBLK * kMaxGroups * 4;
+  constexpr int LDS = S::STAGES * STAGE + PANEL;
+  constexpr int LMAX = S::LMAX + (MX ? 1 : 0);
+  static_assert(LDS <= 160 * 1024 && 3 * LMAX < 64, "LDS ring / vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
 
   // ---- which (expert, m-tile, n-tile) this block computes ----------------
   // Workgroups go to the 8 XCDs round-robin (block L to XCD L % 8).  Each
@@ -291,31 +320,57 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     b_off[i] = (uint32_t)(wrow * p.Kd + c * 16);
   }
   // activation scales: one 4-byte word per row and k-step (UE8M0: the word
-  // holding the step's exponent byte; fp32: the scale itself)
+  // holding the step's exponent byte; fp32: the scale itself; MX: the step's
+  // four 32-column exponent bytes)
   const bool loads_sc = wave < S::SC_WAVES && wave * 64 < rows_here;
+  // MX weight scales: tile row wave*64 + lane's 16 bytes (4 k-steps), loaded
+  // with stages kb = 0 mod 4 only
+  const bool loads_wsc = MX && wave < S::BN / 64;
   const int loads_per_stage = a_loads + S::B_INSTR + (loads_sc ? 1 : 0);
   uint32_t sc_off = kOutOfRange;
   {
     const int r = wave * 64 + lane;
     if (loads_sc && r < rows_here)
-      sc_off = (uint32_t)(a_row_of(r) * p.a_sf_stride * (UE8M0 ? 1 : 4));
+      sc_off = (uint32_t)(a_row_of(r) * p.a_sf_stride * (SC == kQuantF32 ? 4 : 1));
+  }
+  const int Gw = p.Kd / 32;   // MX weight-scale bytes per row
+  const v4i rs_w = MX ? buffer_rsrc((const uint8_t*)p.w_sf + (int64_t)e * p.Nout * Gw,
+                                    (uint32_t)((int64_t)p.Nout * Gw))
+                      : v4i{0, 0, 0, 0};
+  uint32_t wsc_off = 0;
+  if (MX) {
+    const int r = (wave * 64 + lane) % S::BN;
+    int64_t wrow = n0 + r;
+    if (ACT) {
+      const int q = r & 63, w = r >> 6;
+      wrow = (q < 32 ? 0 : Nh - 32) + j0 + 32 * w + q;
+    }
+    wsc_off = (uint32_t)(wrow * Gw);
   }
   const int wave_slot = __builtin_amdgcn_readfirstlane(wave * 1024);
   const int wave_sc = __builtin_amdgcn_readfirstlane(wave * 256);
   // weight block scales of this tile's NBLK 128-column blocks, one per k-step
-  float* sw_panel = reinterpret_cast<float*>(smem + S::STAGES * S::STAGE_BYTES);
-  for (int i = tid; i < S::NBLK * G; i += S::THREADS) {
+  float* sw_panel = reinterpret_cast<float*>(smem + S::STAGES * STAGE);
+  for (int i = tid; i < (MX ? 0 : S::NBLK * G); i += S::THREADS) {
     const int b = i / G, g = i - b * G;
     // ACT: block 0 = the gate rows' scale block, block 1 = the up rows'
     const int blk = ACT ? (b == 0 ? j0 : Nh + j0) / kGroup : n0 / kGroup + b;
-    sw_panel[b * kMaxGroups + g] = p.w_sf[((int64_t)e * (p.Nout / kGroup) + blk) * G + g];
+    sw_panel[b * kMaxGroups + g] =
+        ((const float*)p.w_sf)[((int64_t)e * (p.Nout / kGroup) + blk) * G + g];
   }
   __syncthreads();
 
   // ---- per-lane MFMA fragment offsets (within a stage) -------------------
+  // The 16x16x128 f8f6f4 MFMA reads lane l's 32 operand bytes as k values
+  // 16*(l>>4) + [0, 16) (registers 0-3) and 64 + 16*(l>>4) + [0, 16)
+  // (registers 4-7), and takes the E8M0 scale of 32-column block b from lane
+  // group b: under MX, lane group kq therefore loads 16-byte chunks kq and
+  // kq + 4 of the row's 128-byte k-step.  With per-128 promotion any
+  // consistent placement gives the same sum; there chunks 2kq and 2kq + 1
+  // (adjacent) measured a few percent faster.
   const int rho = lane & 15;
   const int kq = lane >> 4;
-  const int c0 = 2 * kq, c1 = 2 * kq + 1;
+  const int c0 = MX ? kq : 2 * kq, c1 = MX ? kq + 4 : 2 * kq + 1;
   // weight sub-tile i's row for this lane is nl0 + 4*i (same swizzle key)
   const int nl0 = wn * S::WAVE_N + (rho >> 2) * (4 * S::TN) + (rho & 3);
   const int kbw = key_b<S::LOG_4TN>(nl0);
@@ -329,6 +384,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int a_frag0 = ml0 * kRowBytes + ((c0 ^ key_a(ml0)) << 4);
   const int a_frag1 = ml0 * kRowBytes + ((c1 ^ key_a(ml0)) << 4);
   const int sc_frag = S::A_BYTES + S::B_BYTES + ml0 * 4;
+  // MX: weight row nl0's 16 bytes in a panel slot (+64 per sub-tile)
+  const int wsc_frag = S::STAGES * STAGE + nl0 * 16;
+  const int scale_shift = 8 * kq;            // MX: this lane's 32-column k-group byte
   constexpr int kSubStride = 16 * S::WM;
   const uint32_t smem_base = lds_addr(smem);
   // the weight-scale block of this lane's output columns (ACT: lanes 0-31
@@ -337,7 +395,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       sw_panel + (ACT ? (kq >= 2 ? 1 : 0) : (wn * S::WAVE_N) / 128) * kMaxGroups;
 
   auto issue = [&](int kb) {
-    const uint32_t st = smem_base + (kb % S::STAGES) * S::STAGE_BYTES;
+    const uint32_t st = smem_base + (kb % S::STAGES) * STAGE;
     const uint32_t koff = (uint32_t)kb * kRowBytes;
 #pragma unroll
     for (int i = 0; i < S::A_INSTR; ++i)
@@ -349,6 +407,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       const uint32_t soff = UE8M0 ? (uint32_t)(kb & ~3) : (uint32_t)kb * 4;
       dma4(rs_s, st + S::A_BYTES + S::B_BYTES + wave_sc, sc_off + soff);
     }
+    if (loads_wsc && (kb & 3) == 0)
+      dma16(rs_w, smem_base + S::STAGES * STAGE + ((kb >> 2) & 1) * WSC_SLOT + wave_slot,
+            wsc_off + (uint32_t)kb * 4);
   };
 
   v4f acc[S::TN][S::TM];
@@ -364,8 +425,37 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // two MFMAs after issue, once it has left the matrix pipe.
   auto compute = [&](int kb, auto live_c) {
     constexpr int LIVE = decltype(live_c)::value;
-    if constexpr (LIVE > 0) {
-      const uint8_t* sb = smem + (kb % S::STAGES) * S::STAGE_BYTES;
+    if constexpr (MX && LIVE > 0) {
+      // both operands carry E8M0 scales per (row, 32 columns): lane l's byte
+      // for its row and k-group l >> 4 goes to the MFMA, which accumulates
+      // straight into acc (byte 127 = 1.0)
+      const uint8_t* sb = smem + (kb % S::STAGES) * STAGE;
+      v8i wf[S::TN];
+      int sw[S::TN];
+#pragma unroll
+      for (int i = 0; i < S::TN; ++i) {
+        const v4i lo = *reinterpret_cast<const v4i*>(sb + w_frag0 + i * 4 * kRowBytes);
+        const v4i hi = *reinterpret_cast<const v4i*>(sb + w_frag1 + i * 4 * kRowBytes);
+        wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        sw[i] = (int)(*reinterpret_cast<const uint32_t*>(
+                          smem + wsc_frag + ((kb >> 2) & 1) * WSC_SLOT + 64 * i + (kb & 3) * 4) >>
+                      scale_shift);
+      }
+#pragma unroll
+      for (int j = 0; j < LIVE; ++j) {
+        const v4i lo = *reinterpret_cast<const v4i*>(sb + a_frag0 + j * kSubStride * kRowBytes);
+        const v4i hi = *reinterpret_cast<const v4i*>(sb + a_frag1 + j * kSubStride * kRowBytes);
+        const v8i af = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const int sa =
+            (int)(*reinterpret_cast<const uint32_t*>(sb + sc_frag + j * kSubStride * 4) >>
+                  scale_shift);
+#pragma unroll
+        for (int i = 0; i < S::TN; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], af, acc[i][j], 0,
+                                                                       0, 0, sw[i], 0, sa);
+      }
+    } else if constexpr (LIVE > 0) {
+      const uint8_t* sb = smem + (kb % S::STAGES) * STAGE;
       v8i wf[S::TN], af[LIVE];
       float fs[LIVE];
 #pragma unroll
@@ -395,6 +485,12 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
           if (t % S::TN == 0 && t / S::TN + 1 < LIVE)
             load_a(t / S::TN + 1, af[t / S::TN + 1], fs[t / S::TN + 1]);
           const v4f z = {0.f, 0.f, 0.f, 0.f};
+          // Constant zero scale operands make the compiler emit the unscaled
+          // v_mfma_f32_16x16x128_f8f6f4 (scale 1.0; the scales are applied in
+          // the promotion).  A register holding E8M0 127 would mean the same
+          // but selects the scaled encoding, measured ~2% slower here; a
+          // scaled instruction with zero operands would mean 2^-254, which
+          // every parity test would catch.
           part[t % 3] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
               wf[t % S::TN], af[t / S::TN], z, 0, 0, 0, 0, 0, 0);
         }
@@ -419,7 +515,16 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     for (int kb = 0; kb < G; ++kb) {
       // k-step kb has landed for every wave, and every wave's reads of
       // k-step kb-1 (whose slot the next issue reuses) have completed
-      stage_landed<S::LMAX>(loads_per_stage, min(kb + S::STAGES - 2, G - 1) - kb);
+      const int after = min(kb + S::STAGES - 2, G - 1) - kb;
+      if constexpr (MX) {
+        // later stages in flight, plus the panel loads among them
+        int n = after * loads_per_stage;
+        if (loads_wsc)
+          for (int s2 = kb + 1; s2 <= kb + after; ++s2) n += (s2 & 3) == 0 ? 1 : 0;
+        wait_n_then_barrier<3 * LMAX>(n);
+      } else {
+        stage_landed<LMAX>(loads_per_stage, after);
+      }
       if (kb + S::STAGES - 1 < G) issue(kb + S::STAGES - 1);
       compute(kb, live_c);
     }
@@ -465,22 +570,27 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 16));
       amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 32));
     }
-    // group maximum across the WN = 4 waves sharing the rows, through LDS
+    // 128-column groups: maximum across the WN = 4 waves sharing the rows,
+    // through LDS.  MX 32-column groups: one wave's columns, already reduced.
     float* red = reinterpret_cast<float*>(smem);   // [WN][BM]
-    __syncthreads();                               // every wave is done with the ring
-    if (kq == 0) {
+    if constexpr (!MX) {
+      __syncthreads();                             // every wave is done with the ring
+      if (kq == 0) {
 #pragma unroll
-      for (int j = 0; j < S::TM; ++j) red[wn * S::BM + ml0 + kSubStride * j] = amax[j];
+        for (int j = 0; j < S::TM; ++j) red[wn * S::BM + ml0 + kSubStride * j] = amax[j];
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    const int GN = Nh / kGroup;
+    const int GN = Nh / (MX ? 32 : kGroup);
+    const int g_out = MX ? 4 * nt + wn : nt;       // this lane's scale group
 #pragma unroll
     for (int j = 0; j < S::TM; ++j) {
       const int ml = ml0 + kSubStride * j;
       if (ml >= rows_here) continue;
-      const float a = fmaxf(fmaxf(red[ml], red[S::BM + ml]),
-                            fmaxf(red[2 * S::BM + ml], red[3 * S::BM + ml]));
-      const GroupScale gs = group_scale<UE8M0>(a);
+      const float a = MX ? amax[j]
+                         : fmaxf(fmaxf(red[ml], red[S::BM + ml]),
+                                 fmaxf(red[2 * S::BM + ml], red[3 * S::BM + ml]));
+      const GroupScale gs = group_scale<UE8M0 || MX>(a);
       uint2 q;
       q.x = f32x4_to_e4m3x4(h[j][0] * gs.recip, h[j][1] * gs.recip, h[j][2] * gs.recip,
                             h[j][3] * gs.recip);
@@ -488,15 +598,16 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
                             h[j][7] * gs.recip);
       const int64_t row = base + m0 + ml;
       *reinterpret_cast<uint2*>(p.act_q + row * Nh + j0 + col_off) = q;
-      if (wn == 0 && kq == 0) {
-        if (UE8M0) {
+      if (kq == 0 && (MX || wn == 0)) {
+        if (UE8M0 || MX) {
           uint8_t* sf = p.act_sf + row * p.act_sf_row;
-          sf[nt] = (uint8_t)gs.stored;
-          // the row's trailing pad bytes are zero
-          if (nt == GN - 1)
+          sf[g_out] = (uint8_t)gs.stored;
+          // the row's trailing pad bytes are zero (128-column groups only;
+          // 32-column rows have none)
+          if (!MX && g_out == GN - 1)
             for (int pad = GN; pad < p.act_sf_row; ++pad) sf[pad] = 0;
         } else {
-          reinterpret_cast<uint32_t*>(p.act_sf)[row * p.act_sf_row + nt] = gs.stored;
+          reinterpret_cast<uint32_t*>(p.act_sf)[row * p.act_sf_row + g_out] = gs.stored;
         }
       }
     }
@@ -527,9 +638,13 @@ hipError_t launch_shape(const GemmArgs& p, int max_tiles, int quant, hipStream_t
   const int64_t blocks = ((int64_t)max_tiles * (p.Nout / S::BN) + 7) / 8 * 8;
   const dim3 grid((unsigned)blocks);
   if (quant == kQuantUe8m0)
-    grouped_gemm_kernel<S, true, ACT><<<grid, S::THREADS, 0, stream>>>(p);
+    grouped_gemm_kernel<S, kQuantUe8m0, ACT><<<grid, S::THREADS, 0, stream>>>(p);
+  else if (quant == kQuantF32)
+    grouped_gemm_kernel<S, kQuantF32, ACT><<<grid, S::THREADS, 0, stream>>>(p);
+  else if (quant == kQuantMxfp8)
+    grouped_gemm_kernel<S, kQuantMxfp8, ACT><<<grid, S::THREADS, 0, stream>>>(p);
   else
-    grouped_gemm_kernel<S, false, ACT><<<grid, S::THREADS, 0, stream>>>(p);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

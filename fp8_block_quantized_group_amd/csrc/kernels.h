@@ -7,9 +7,13 @@
 namespace moe {
 
 // activation quantization schemes (values match moe_quant_t)
-constexpr int kQuantUe8m0 = 0;
-constexpr int kQuantF32 = 1;
-constexpr int kQuantBf16 = 2;
+constexpr int kQuantUe8m0 = 0;   // per-128 groups, E8M0 scale bytes
+constexpr int kQuantF32 = 1;     // per-128 groups, fp32 scales
+constexpr int kQuantBf16 = 2;    // unquantized copy
+constexpr int kQuantMxfp8 = 3;   // per-32 groups, E8M0 scale bytes
+// weight schemes (values match moe_weight_t)
+constexpr int kWeightBlock128 = 0;   // e4m3, fp32 scale per 128x128 block
+constexpr int kWeightMxfp8 = 1;      // e4m3, E8M0 scale per row and 32 columns
 
 // routing: slots handled per block of the count / scatter kernels
 constexpr int kRouteChunk = 1024;
@@ -33,7 +37,8 @@ struct GemmArgs {
   uint32_t a_sf_bytes;       // size of the activation-scale buffer (< 2^32)
   int a_sf_stride;           // scale row length: bytes (UE8M0) or floats (fp32)
   const uint8_t* w;          // weight codes [E, Nout, Kd]
-  const float* w_sf;         // weight block scales [E, Nout/128, Kd/128]
+  const void* w_sf;          // weight scales: fp32 [E, Nout/128, Kd/128] (block),
+                             //   E8M0 bytes [E, Nout, Kd/32] (MX)
   uint16_t* out;             // bf16 [rows, Nout] (plain GEMM)
   uint8_t* act_q;            // fused activation: fp8 [rows, Nout/2]
   uint8_t* act_sf;           //   and its per-128 scales (UE8M0 bytes or fp32)
@@ -63,10 +68,11 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint
                         int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
                         int32_t* tile_list, hipStream_t stream);
 
+// quant: the activation scheme (kQuant*, kQuantMxfp8 implies MX weights).
 // act = false: out = bf16 GEMM result.  act = true (w13 only): the result's
 // gate half [0, Nout/2) and up half [Nout/2, Nout) are combined into
-// silu(gate) * up and quantized per 128 columns into act_q / act_sf; nothing
-// is written to out.
+// silu(gate) * up and quantized per group (128, or 32 for MX) into act_q /
+// act_sf; nothing is written to out.
 hipError_t launch_grouped_gemm(const GemmArgs& args, int tile_m, int max_tiles, int quant,
                                bool act, hipStream_t stream);
 

@@ -7,9 +7,9 @@
 // scale buffer present iff quantizing, an empty batch is a no-op) and the
 // experts' apply() preconditions ("...experts.fused_humming_moe": batched
 // format needs expert_num_tokens).  The workspace plan mirrors
-// HummingExpertsBase.get_buffer_metas / prepare_buffers: neighbouring
-// buffers of the chain x_q -> gate_up -> a2 -> down live in different
-// regions, so two regions (fp8 side and bf16 side) suffice.
+// HummingExpertsBase.get_buffer_metas / prepare_buffers, minus the gate_up
+// buffer the fused w13 call never materializes.  Scheme pairs follow
+// HummingExpertsBase._supports_quant_scheme.
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -103,10 +103,23 @@ moe_status_t validate_problem(const moe_problem_t* p, bool allow_bf16) {
     if (in_rows * p->hidden >= ((int64_t)7 << 29) || rows * p->intermediate >= ((int64_t)7 << 29))
       return fail(MOE_ERR_UNSUPPORTED, "activation buffers are limited to 3.5 GiB");
   }
-  if (p->act_quant != MOE_Q_FP8_UE8M0 && p->act_quant != MOE_Q_FP8_F32 &&
-      !(allow_bf16 && p->act_quant == MOE_Q_BF16))
-    return fail(allow_bf16 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED,
+  if (p->act_quant < MOE_Q_FP8_UE8M0 || p->act_quant > MOE_Q_MXFP8)
+    return fail(MOE_ERR_INVALID_ARG, "unknown activation quantization %d", p->act_quant);
+  if (p->weight_quant < MOE_W_FP8_BLOCK128 || p->weight_quant > MOE_W_MXFP4)
+    return fail(MOE_ERR_INVALID_ARG, "unknown weight quantization %d", p->weight_quant);
+  if (p->act_quant == MOE_Q_BF16 && !allow_bf16)
+    return fail(MOE_ERR_UNSUPPORTED,
                 "activation quantization %d not supported by this call", p->act_quant);
+  // (weight, activation) pairs: block fp8 weights with per-128 activations,
+  // MXFP8 weights with MXFP8 activations
+  const bool mx_w = p->weight_quant != MOE_W_FP8_BLOCK128;
+  const bool mx_a = p->act_quant == MOE_Q_MXFP8;
+  if (p->weight_quant == MOE_W_MXFP4)
+    return fail(MOE_ERR_UNSUPPORTED, "MXFP4 weights are not supported by this build");
+  if (mx_w != mx_a && p->act_quant != MOE_Q_BF16)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "weight quantization %d cannot pair with activation quantization %d",
+                p->weight_quant, p->act_quant);
   return MOE_OK;
 }
 
@@ -137,15 +150,17 @@ Plan make_plan(const moe_problem_t* p) {
     pl.max_tiles = (T * k + bm - 1) / bm + E;
   }
   pl.s.tile_list = 1 + 2 * pl.max_tiles + (E + 1);
-  pl.s.x_sf_row = ue ? 4 * ((GK + 3) / 4) : GK;
-  pl.s.a2_sf_row = ue ? 4 * ((GN + 3) / 4) : GN;
+  const bool mx = p->act_quant == MOE_Q_MXFP8;
+  pl.s.x_sf_row = mx ? K / 32 : ue ? 4 * ((GK + 3) / 4) : GK;
+  pl.s.a2_sf_row = mx ? N / 32 : ue ? 4 * ((GN + 3) / 4) : GN;
   pl.route_blocks = (T * k + moe::kRouteChunk - 1) / moe::kRouteChunk;
   pl.stage_ws_bytes = round_up((size_t)std::max<int64_t>(pl.route_blocks, 1) * E * 4);
   const size_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
   pl.x_q_bytes = (size_t)pl.s.stage_rows * K * elem;
-  pl.x_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.stage_rows * pl.s.x_sf_row * (ue ? 1 : 4);
+  const size_t sfb = p->act_quant == MOE_Q_FP8_F32 ? 4 : 1;
+  pl.x_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.stage_rows * pl.s.x_sf_row * sfb;
   pl.a2_q_bytes = (size_t)pl.s.expert_rows * N;
-  pl.a2_sf_bytes = (size_t)pl.s.expert_rows * pl.s.a2_sf_row * (ue ? 1 : 4);
+  pl.a2_sf_bytes = (size_t)pl.s.expert_rows * pl.s.a2_sf_row * sfb;
   pl.down_bytes = (size_t)pl.s.expert_rows * K * 2;
   return pl;
 }
@@ -262,16 +277,16 @@ moe_status_t run_stage(const moe_problem_t* p, const Plan& pl, const void* hidde
 
 // w13 with act: out unused, the activation goes to act_q / act_sf.
 moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const void* a_q,
-                      const void* a_sf, const moe_routing_t* r, const void* w, const float* w_sf,
+                      const void* a_sf, const moe_routing_t* r, const void* w, const void* w_sf,
                       void* out, hipStream_t stream, bool act = false, void* act_q = nullptr,
                       void* act_sf = nullptr) {
   moe::GemmArgs g{};
-  const bool ue = p->act_quant == MOE_Q_FP8_UE8M0;
+  const size_t sfb = p->act_quant == MOE_Q_FP8_F32 ? 4 : 1;
   g.a = (const uint8_t*)a_q;
   g.a_bytes = (uint32_t)(w13 ? pl.x_q_bytes : pl.a2_q_bytes);
   g.a_sf = a_sf;
   g.a_sf_stride = (int)(w13 ? pl.s.x_sf_row : pl.s.a2_sf_row);
-  g.a_sf_bytes = (uint32_t)((w13 ? pl.s.stage_rows : pl.s.expert_rows) * g.a_sf_stride * (ue ? 1 : 4));
+  g.a_sf_bytes = (uint32_t)((w13 ? pl.s.stage_rows : pl.s.expert_rows) * g.a_sf_stride * sfb);
   g.w = (const uint8_t*)w;
   g.w_sf = w_sf;
   g.out = (uint16_t*)out;
@@ -365,7 +380,7 @@ moe_status_t moe_stage(const moe_problem_t* p, const void* hidden,
 
 moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const void* a_sf,
                                   const moe_routing_t* routing, const void* w13,
-                                  const float* w13_sf, void* gate_up, void* stream) {
+                                  const void* w13_sf, void* gate_up, void* stream) {
   CHECK(validate_problem(p, false));
   if (p->num_tokens == 0) return ok();
   CHECK(check_ptr(a_q, "a_q", 16));
@@ -380,7 +395,7 @@ moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const
 
 moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q, const void* a_sf,
                                       const moe_routing_t* routing, const void* w13,
-                                      const float* w13_sf, void* a2_q, void* a2_sf,
+                                      const void* w13_sf, void* a2_q, void* a2_sf,
                                       void* stream) {
   CHECK(validate_problem(p, false));
   if (p->num_tokens == 0) return ok();
@@ -411,7 +426,7 @@ moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
 
 moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const void* a2_sf,
                                  const moe_routing_t* routing, const void* w2,
-                                 const float* w2_sf, void* down, void* stream) {
+                                 const void* w2_sf, void* down, void* stream) {
   CHECK(validate_problem(p, false));
   if (p->num_tokens == 0) return ok();
   CHECK(check_ptr(a2_q, "a2_q", 16));
@@ -438,8 +453,8 @@ moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int
 moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
                          const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
                          const float* topk_weights, const uint8_t* is_padding,
-                         const moe_eplb_t* eplb, const void* w13, const float* w13_sf,
-                         const void* w2, const float* w2_sf, void* out, void* ws,
+                         const moe_eplb_t* eplb, const void* w13, const void* w13_sf,
+                         const void* w2, const void* w2_sf, void* out, void* ws,
                          size_t ws_bytes, void* stream) {
   CHECK(validate_problem(p, false));
   if (p->num_tokens == 0) return ok();

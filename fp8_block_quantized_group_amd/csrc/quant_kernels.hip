@@ -8,10 +8,14 @@
 // "vllm.model_executor.layers.fused_moe.experts.fused_humming_moe",
 // HummingExpertsBase.process_input with activation (pull-request 58588 build).
 //
-// Work split: one 16-lane DPP row per 128-value group; each lane loads 8
-// bf16 (16 bytes), the row reduces |x| with four DPP max steps, each lane
-// writes 8 fp8 bytes.  A 64-lane wave covers four groups = 512 contiguous
-// input values, so every load and store instruction is fully coalesced.
+// MXFP8 (kMxfp8Dynamic) is the same quantizer with 32-value groups and E8M0
+// scales ("...prepare_megamoe", _resolve_hidden_quant: GROUP_K = 32).
+//
+// Work split: LANES = group/8 lanes per group (a 16-lane DPP row per
+// 128-value group, a quad per 32-value group); each lane loads 8 bf16
+// (16 bytes), the lanes reduce |x| with DPP max steps, each lane writes 8
+// fp8 bytes.  A 64-lane wave covers 512 contiguous input values, so every
+// load and store instruction is fully coalesced.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -26,15 +30,16 @@ __device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
   f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
 }
 
-// Quantize the 8 values a lane holds (its row of 16 lanes forms one group),
-// write the codes and, from lane 0 of the row, the group's scale.
-template <bool UE8M0>
+// Quantize the 8 values a lane holds (LANES consecutive lanes form one
+// group), write the codes and, from the group's first lane, its scale.
+template <bool UE8M0, int LANES>
 __device__ __forceinline__ void quantize_store(const float f[8], int lane16, uint8_t* q_dst,
                                                uint8_t* sf_row, int g, int G, int sf_row_len) {
+  static_assert(LANES == 16 || LANES == 4, "128- or 32-value groups");
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  amax = row16_max(amax);
+  amax = LANES == 16 ? row16_max(amax) : quad_max(amax);
   const GroupScale gs = group_scale<UE8M0>(amax);
   uint2 q;
   q.x = f32x4_to_e4m3x4(f[0] * gs.recip, f[1] * gs.recip, f[2] * gs.recip, f[3] * gs.recip);
@@ -56,22 +61,24 @@ __device__ __forceinline__ bool row_live(int64_t row, const int32_t* counts, int
   return (row - e * max_tokens) < (int64_t)counts[e];
 }
 
-template <bool UE8M0>
+template <bool UE8M0, int LANES>
 __global__ __launch_bounds__(256) void stage_quant_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
     int64_t num_groups, int G, int sf_row_len, const int32_t* __restrict__ counts,
     int max_tokens) {
-  const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int lane16 = threadIdx.x & 15;
+  constexpr int GROUP = 8 * LANES;
+  const int64_t gid = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
+  const int lane_g = threadIdx.x % LANES;
   if (gid >= num_groups) return;
   const int64_t row = gid / G;
   const int g = (int)(gid - row * G);
   if (!row_live(row, counts, max_tokens)) return;
-  const uint4 v = reinterpret_cast<const uint4*>(x + gid * kGroup)[lane16];
+  const uint4 v = reinterpret_cast<const uint4*>(x + gid * GROUP)[lane_g];
   float f[8];
   unpack8(v, f);
   uint8_t* sf_row = UE8M0 ? xsf + row * sf_row_len : xsf + row * (int64_t)G * 4;
-  quantize_store<UE8M0>(f, lane16, xq + gid * kGroup + lane16 * 8, sf_row, g, G, sf_row_len);
+  quantize_store<UE8M0, LANES>(f, lane_g, xq + gid * GROUP + lane_g * 8, sf_row, g, G,
+                               sf_row_len);
 }
 
 // bf16 staging without quantization: a masked 16-byte copy.
@@ -84,21 +91,22 @@ __global__ __launch_bounds__(256) void stage_copy_kernel(
   y[i] = x[i];
 }
 
-// h = silu(gate) * up for columns [g*128, g*128+128) of the gate half and
-// the same columns of the up half, then the group quantizer on h.
-template <bool UE8M0>
+// h = silu(gate) * up for columns [g*GROUP, (g+1)*GROUP) of the gate half
+// and the same columns of the up half, then the group quantizer on h.
+template <bool UE8M0, int LANES>
 __global__ __launch_bounds__(256) void act_requant_kernel(
     const uint16_t* __restrict__ gu, uint8_t* __restrict__ aq, uint8_t* __restrict__ asf,
     int64_t num_groups, int N, int GN, int sf_row_len, const int32_t* __restrict__ num_rows,
     const int32_t* __restrict__ counts, int max_tokens) {
-  const int64_t gid = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int lane16 = threadIdx.x & 15;
+  constexpr int GROUP = 8 * LANES;
+  const int64_t gid = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
+  const int lane_g = threadIdx.x % LANES;
   if (gid >= num_groups) return;
   const int64_t row = gid / GN;
   const int g = (int)(gid - row * GN);
   if (num_rows != nullptr && row >= (int64_t)*num_rows) return;
   if (!row_live(row, counts, max_tokens)) return;
-  const uint16_t* src = gu + row * (int64_t)(2 * N) + g * kGroup + lane16 * 8;
+  const uint16_t* src = gu + row * (int64_t)(2 * N) + g * GROUP + lane_g * 8;
   const uint4 vg = *reinterpret_cast<const uint4*>(src);
   const uint4 vu = *reinterpret_cast<const uint4*>(src + N);
   float fg[8], fu[8], h[8];
@@ -110,8 +118,8 @@ __global__ __launch_bounds__(256) void act_requant_kernel(
     h[i] = fg[i] * sig * fu[i];
   }
   uint8_t* sf_row = UE8M0 ? asf + row * sf_row_len : asf + row * (int64_t)GN * 4;
-  quantize_store<UE8M0>(h, lane16, aq + row * (int64_t)N + g * kGroup + lane16 * 8, sf_row, g,
-                        GN, sf_row_len);
+  quantize_store<UE8M0, LANES>(h, lane_g, aq + row * (int64_t)N + g * GROUP + lane_g * 8,
+                               sf_row, g, GN, sf_row_len);
 }
 
 inline unsigned blocks_for(int64_t n, int per_block) {
@@ -123,22 +131,26 @@ inline unsigned blocks_for(int64_t n, int per_block) {
 hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, int K,
                               int quant, const int32_t* counts, int max_tokens,
                               hipStream_t stream) {
-  const int G = K / kGroup;
-  const int64_t groups = rows * G;
-  if (groups == 0) return hipSuccess;
-  const int sf_row_len = 4 * ((G + 3) / 4);
+  if (rows == 0) return hipSuccess;
   if (quant == kQuantBf16) {
     const int64_t nvec = rows * (K / 8);
     stage_copy_kernel<<<blocks_for(nvec, 256), 256, 0, stream>>>(
         (const uint4*)x, (uint4*)xq, nvec, K / 8, counts, max_tokens);
-  } else if (quant == kQuantUe8m0) {
-    stage_quant_kernel<true><<<blocks_for(groups, 16), 256, 0, stream>>>(
-        (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, groups, G, sf_row_len, counts,
-        max_tokens);
+  } else if (quant == kQuantMxfp8) {
+    const int G = K / 32;   // K is a multiple of 128: rows of G bytes, no pad
+    stage_quant_kernel<true, 4><<<blocks_for(rows * G, 64), 256, 0, stream>>>(
+        (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, rows * G, G, G, counts, max_tokens);
   } else {
-    stage_quant_kernel<false><<<blocks_for(groups, 16), 256, 0, stream>>>(
-        (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, groups, G, sf_row_len, counts,
-        max_tokens);
+    const int G = K / kGroup;
+    const int sf_row_len = 4 * ((G + 3) / 4);
+    if (quant == kQuantUe8m0)
+      stage_quant_kernel<true, 16><<<blocks_for(rows * G, 16), 256, 0, stream>>>(
+          (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, rows * G, G, sf_row_len, counts,
+          max_tokens);
+    else
+      stage_quant_kernel<false, 16><<<blocks_for(rows * G, 16), 256, 0, stream>>>(
+          (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, rows * G, G, sf_row_len, counts,
+          max_tokens);
   }
   return hipGetLastError();
 }
@@ -146,18 +158,24 @@ hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, 
 hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t rows_cap, int N,
                               int quant, const int32_t* num_rows, const int32_t* counts,
                               int max_tokens, hipStream_t stream) {
+  if (rows_cap == 0) return hipSuccess;
+  if (quant == kQuantMxfp8) {
+    const int GN = N / 32;
+    act_requant_kernel<true, 4><<<blocks_for(rows_cap * GN, 64), 256, 0, stream>>>(
+        (const uint16_t*)gate_up, (uint8_t*)aq, (uint8_t*)asf, rows_cap * GN, N, GN, GN,
+        num_rows, counts, max_tokens);
+    return hipGetLastError();
+  }
   const int GN = N / kGroup;
-  const int64_t groups = rows_cap * GN;
-  if (groups == 0) return hipSuccess;
   const int sf_row_len = 4 * ((GN + 3) / 4);
   if (quant == kQuantUe8m0) {
-    act_requant_kernel<true><<<blocks_for(groups, 16), 256, 0, stream>>>(
-        (const uint16_t*)gate_up, (uint8_t*)aq, (uint8_t*)asf, groups, N, GN, sf_row_len,
-        num_rows, counts, max_tokens);
+    act_requant_kernel<true, 16><<<blocks_for(rows_cap * GN, 16), 256, 0, stream>>>(
+        (const uint16_t*)gate_up, (uint8_t*)aq, (uint8_t*)asf, rows_cap * GN, N, GN,
+        sf_row_len, num_rows, counts, max_tokens);
   } else {
-    act_requant_kernel<false><<<blocks_for(groups, 16), 256, 0, stream>>>(
-        (const uint16_t*)gate_up, (uint8_t*)aq, (uint8_t*)asf, groups, N, GN, sf_row_len,
-        num_rows, counts, max_tokens);
+    act_requant_kernel<false, 16><<<blocks_for(rows_cap * GN, 16), 256, 0, stream>>>(
+        (const uint16_t*)gate_up, (uint8_t*)aq, (uint8_t*)asf, rows_cap * GN, N, GN,
+        sf_row_len, num_rows, counts, max_tokens);
   }
   return hipGetLastError();
 }

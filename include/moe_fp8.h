@@ -38,11 +38,18 @@
  *  - Activation scales, MOE_Q_FP8_UE8M0: one exponent byte e per 128-group
  *    (scale 2^(e-127)), rows of 4*ceil(G/4) bytes with zero pad bytes; this is
  *    byte-identical to the pages' "four per int32" little-endian packing
- *    (_pack_bytes).  MOE_Q_FP8_F32: fp32 [rows, G].
- *  - Weights: w13 [E, 2N, K] fp8 codes (rows [0, N) gate, [N, 2N) up) with
- *    fp32 block scales w13_sf [E, 2N/128, K/128]; w2 [E, K, N] with
- *    w2_sf [E, K/128, N/128]; dequantized weight = code * block scale
- *    (the kFp8Static128BlockSym scheme).
+ *    (_pack_bytes).  MOE_Q_FP8_F32: fp32 [rows, G].  MOE_Q_MXFP8: one
+ *    exponent byte per 32-group, rows of K/32 bytes (no pad: K % 128 == 0).
+ *  - Weights: w13 [E, 2N, K] fp8 codes (rows [0, N) gate, [N, 2N) up), w2
+ *    [E, K, N].  MOE_W_FP8_BLOCK128 (kFp8Static128BlockSym): fp32 block scales
+ *    w13_sf [E, 2N/128, K/128], w2_sf [E, K/128, N/128], dequantized weight =
+ *    code * block scale.  MOE_W_MXFP8 (kMxfp8Static): E8M0 bytes w13_sf
+ *    [E, 2N, K/32], w2_sf [E, K, N/32], one per row and 32 columns,
+ *    dequantized weight = code * 2^(byte-127).
+ *  - Scheme pairs (HummingExpertsBase._supports_quant_scheme): block fp8
+ *    weights with UE8M0 or fp32 per-128 activations; MXFP8 weights with MXFP8
+ *    activations.  MXFP4 weights (kMxfp4Static) are declared but rejected
+ *    with MOE_ERR_UNSUPPORTED.
  */
 #ifndef MOE_FP8_H
 #define MOE_FP8_H
@@ -66,8 +73,16 @@ typedef enum {
 typedef enum {
   MOE_Q_FP8_UE8M0 = 0, /* fp8 e4m3fn, per-128 power-of-two scales          */
   MOE_Q_FP8_F32 = 1,   /* fp8 e4m3fn, per-128 fp32 scales                   */
-  MOE_Q_BF16 = 2       /* staging only: hidden states copied unquantized    */
+  MOE_Q_BF16 = 2,      /* staging only: hidden states copied unquantized    */
+  MOE_Q_MXFP8 = 3      /* fp8 e4m3fn, per-32 E8M0 scales (kMxfp8Dynamic)    */
 } moe_quant_t;
+
+/* Weight quantization of w13 and w2. */
+typedef enum {
+  MOE_W_FP8_BLOCK128 = 0, /* e4m3fn, fp32 scale per 128x128 block           */
+  MOE_W_MXFP8 = 1,        /* e4m3fn, E8M0 scale per row and 32 columns      */
+  MOE_W_MXFP4 = 2         /* e2m1 (two per byte), E8M0 per row and 32 cols  */
+} moe_weight_t;
 
 /* Expert-row layouts ("Standard" and "BatchedExperts" activation formats). */
 typedef enum {
@@ -88,6 +103,7 @@ typedef struct {
   int32_t layout;                /* moe_layout_t */
   int32_t max_tokens_per_expert; /* batched layout only */
   int32_t act_quant;             /* moe_quant_t */
+  int32_t weight_quant;          /* moe_weight_t */
 } moe_problem_t;
 
 /* Expert-parallel load balancing state (optional; all device pointers).
@@ -171,7 +187,7 @@ moe_status_t moe_stage(const moe_problem_t* p, const void* hidden,
  * [expert_rows, 2N]; rows past an expert's count are not written. */
 moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const void* a_sf,
                                   const moe_routing_t* routing, const void* w13,
-                                  const float* w13_sf, void* gate_up, void* stream);
+                                  const void* w13_sf, void* gate_up, void* stream);
 
 /* Steps 3 + 4 in one pass: the w13 GEMM of moe_grouped_gemm_w13 whose result
  * never leaves the chip; each output row's gate and up halves are rounded to
@@ -184,7 +200,7 @@ moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const
  * a2_q / a2_sf must not overlap a_q / a_sf. */
 moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q,
                                       const void* a_sf, const moe_routing_t* routing,
-                                      const void* w13, const float* w13_sf, void* a2_q,
+                                      const void* w13, const void* w13_sf, void* a2_q,
                                       void* a2_sf, void* stream);
 
 /* Step 4: a2 = quant(silu(gate_up[:, :N]) * gate_up[:, N:]) per 128 columns,
@@ -198,7 +214,7 @@ moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
  * down: bf16 [expert_rows, K]. */
 moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const void* a2_sf,
                                  const moe_routing_t* routing, const void* w2,
-                                 const float* w2_sf, void* down, void* stream);
+                                 const void* w2_sf, void* down, void* stream);
 
 /* Step 6: out[t] = bf16(sum over j ascending with slot_row[t, j] >= 0 of
  * topk_w[t, j] * down[slot_row[t, j]]); tokens with no routed slot get 0.
@@ -213,8 +229,8 @@ moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int
 moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
                          const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
                          const float* topk_weights, const uint8_t* is_padding,
-                         const moe_eplb_t* eplb, const void* w13, const float* w13_sf,
-                         const void* w2, const float* w2_sf, void* out, void* ws,
+                         const moe_eplb_t* eplb, const void* w13, const void* w13_sf,
+                         const void* w2, const void* w2_sf, void* out, void* ws,
                          size_t ws_bytes, void* stream);
 
 /* Message of the last failed call on this thread ("" if none). */

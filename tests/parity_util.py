@@ -80,6 +80,16 @@ def abs_gemm(a_codes, a_scale, w_codes, w_sf):
                                    np.asarray(w_codes) & 0x7F, np.abs(np.asarray(w_sf)))
 
 
+def abs_gemm_cfg(cfg, a_codes, a_stored, w_codes, w_sf):
+    """S_abs in the workload's scheme: block fp8 (scale values) or MX (E8M0
+    bytes on both operands; e2m1 sign bits cleared nibble by nibble)."""
+    if cfg.weight_quant == "fp8_block128":
+        return abs_gemm(a_codes, O.scale_values(a_stored, O.act_e8m0(cfg)), w_codes, w_sf)
+    fp4 = cfg.weight_quant == "mxfp4"
+    return O.mx_gemm_f64(np.asarray(a_codes) & 0x7F, a_stored,
+                         np.asarray(w_codes) & (0x77 if fp4 else 0x7F), w_sf, fp4)
+
+
 def check_gemm(got_bits, ref_bits, s_abs, what):
     g = O.bf16_to_f64(got_bits)
     r = O.bf16_to_f64(ref_bits)
@@ -101,30 +111,30 @@ def _fp8_step(v_over_s):
     return np.exp2(np.floor(np.log2(np.maximum(np.abs(v_over_s), 2.0 ** -6))) - 3)
 
 
-def check_requant(got_q, got_sf, ref_q, ref_sf, ref_h32, ue8m0, what):
-    """Isolation: the GPU re-quantized the oracle's own gate_up.
-    <= 1 ULP in <= 0.1% of the elements."""
+def check_requant(got_q, got_sf, ref_q, ref_sf, ref_h32, ue8m0, what, group=128):
+    """Isolation: the GPU re-quantized the oracle's own gate_up (groups of
+    ``group`` columns).  <= 1 ULP in <= 0.1% of the elements."""
     rows, N = ref_q.shape
-    G = N // 128
+    G = N // group
     got_sf = got_sf[:, :G]
     ref_sf = ref_sf[:, :G]
     ulp = np.abs(fp8_ordinal(got_q) - fp8_ordinal(ref_q))
     if ue8m0:
         diff_e = got_sf.astype(int) != ref_sf.astype(int)
         if diff_e.any():
-            amax = np.abs(ref_h32.reshape(rows, G, 128)).max(axis=2).astype(np.float64)
+            amax = np.abs(ref_h32.reshape(rows, G, group)).max(axis=2).astype(np.float64)
             s = np.maximum(amax, np.float32(1e-4)) / 448.0
             near = np.abs(np.log2(s) - np.round(np.log2(s))) < 2.0 ** -20 * 1.5
             assert np.all(near[diff_e]), f"{what}: exponent differs away from a power of two"
             # those groups: compare values at the coarser of the two scales
-            sv_g = np.repeat(O.scale_values(got_sf, True), 128, axis=1)
-            sv_r = np.repeat(O.scale_values(ref_sf, True), 128, axis=1)
+            sv_g = np.repeat(O.scale_values(got_sf, True), group, axis=1)
+            sv_r = np.repeat(O.scale_values(ref_sf, True), group, axis=1)
             vg = O.e4m3_decode(got_q) * sv_g
             vr = O.e4m3_decode(ref_q) * sv_r
             coarse = np.maximum(sv_g, sv_r)
             d = np.abs(vg - vr)
             by_value = np.where(d == 0, 0, np.where(d <= _fp8_step(vr / coarse) * coarse, 1, 2))
-            ulp = np.where(np.repeat(diff_e, 128, axis=1), by_value, ulp)
+            ulp = np.where(np.repeat(diff_e, group, axis=1), by_value, ulp)
     else:
         rel = np.abs(got_sf.astype(np.float64) - ref_sf.astype(np.float64)) / ref_sf
         assert rel.max() <= 2.0 ** -21, f"{what}: fp32 scales differ by {rel.max():.3e}"
@@ -135,13 +145,13 @@ def check_requant(got_q, got_sf, ref_q, ref_sf, ref_h32, ue8m0, what):
 
 
 def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_gate_up, ue8m0,
-                        what):
+                        what, group=128):
     """End of the GPU's own chain: its gate_up may differ from the oracle's
     by the GEMM bound; carry that through h = silu(g) * u and allow half an
     fp8 step of rounding on each side.  Returns the fraction of codes that
     differ."""
     rows, N = ref_q.shape
-    G = N // 128
+    G = N // group
     gu = O.bf16_to_f64(ref_gate_up_bits)
     g, u = gu[:, :N], gu[:, N:]
     dgu = bf16_ulp(gu) + MFMA_REL * s_abs_gate_up
@@ -151,8 +161,8 @@ def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_ga
     dsilu = np.abs(sig * (1.0 + g * (1.0 - sig)))
     dh = (dsilu * np.abs(u) * dg + np.abs(silu) * du + 1.1 * dg * du) * 1.01
     dh += np.abs(silu * u) * 2.0 ** -20
-    sv_g = np.repeat(O.scale_values(got_sf[:, :G], ue8m0), 128, axis=1)
-    sv_r = np.repeat(O.scale_values(ref_sf[:, :G], ue8m0), 128, axis=1)
+    sv_g = np.repeat(O.scale_values(got_sf[:, :G], ue8m0), group, axis=1)
+    sv_r = np.repeat(O.scale_values(ref_sf[:, :G], ue8m0), group, axis=1)
     vg = O.e4m3_decode(got_q) * sv_g
     vr = O.e4m3_decode(ref_q) * sv_r
     assert np.all(np.isfinite(vg)), f"{what}: non-finite codes"

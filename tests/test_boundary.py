@@ -77,6 +77,9 @@ def test_sizes_follow_the_problem(lib):
             assert s["stage_rows"] == cfg.T and s["expert_rows"] == cfg.T * cfg.top_k
         G = cfg.K // 128
         assert s["x_sf_row"] == (4 * ((G + 3) // 4) if cfg.act_quant == "ue8m0" else G)
+    for name, cfg in moe_synth.MX_CONFIGS.items():
+        s = moe.sizes(moe.Problem.from_config(cfg))
+        assert s["x_sf_row"] == cfg.K // 32 and s["a2_sf_row"] == cfg.N // 32
         assert s["tile_m"] in (16, 32, 64, 128, 192, 256)
         ws = moe.workspace_size(p)
         # staged x_q, the w2 input a2 and the bf16 down projection coexist
@@ -100,6 +103,20 @@ def test_invalid_problem_rejected(lib, field, value, status):
         moe.sizes(p)
     assert ei.value.status == status
     assert lib.moe_last_error().decode()
+
+
+def test_scheme_pairs(lib):
+    # (weight, activation) pairs of the experts' supported-scheme list that
+    # this library implements; the rest are rejected before any launch
+    base = dict(num_tokens=16, hidden=256, intermediate=512, num_experts=4, top_k=2)
+    s = moe.sizes(moe.Problem(**base, act_quant=moe.Q_MXFP8, weight_quant=moe.W_MXFP8))
+    assert s["x_sf_row"] == 256 // 32 and s["a2_sf_row"] == 512 // 32
+    for act, wq, status in [(moe.Q_FP8_UE8M0, moe.W_MXFP8, -2), (moe.Q_FP8_F32, moe.W_MXFP8, -2),
+                            (moe.Q_MXFP8, moe.W_FP8_BLOCK128, -2), (moe.Q_MXFP8, moe.W_MXFP4, -2),
+                            (moe.Q_MXFP8, 7, -1), (9, moe.W_MXFP8, -1)]:
+        with pytest.raises(moe.MoeError) as ei:
+            moe.sizes(moe.Problem(**base, act_quant=act, weight_quant=wq))
+        assert ei.value.status == status, (act, wq)
 
 
 def test_batched_needs_max_tokens(lib):

@@ -1,5 +1,6 @@
-"""Parity at the five workloads' full sizes, in the launch configuration the
-benchmark times (moe_forward, same tile height).
+"""Parity at the workloads' full sizes (the five block-fp8 ones and the
+MX-scheme DeepSeek-V3 prefill), in the launch configuration the benchmark
+times (moe_forward, same tile height).
 
 The oracle cannot run these layers whole, so it checks what it can compute
 piece by piece: the complete routing layout and EPLB load (cheap), the
@@ -15,12 +16,12 @@ import torch
 import fp8_block_quantized_group_amd as moe
 import moe_synth
 from oracle import moe_oracle as O
-from parity_util import abs_gemm, check_gemm, check_output, check_requant_chain, to_np
+from parity_util import abs_gemm_cfg, check_gemm, check_output, check_requant_chain, to_np
 from test_gpu_parity import run_chain, run_forward
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["tiny", "mixtral", "dsv3_prefill", "dsv3_decode", "qwen3"]
+FULL = ["tiny", "mixtral", "dsv3_prefill", "dsv3_decode", "qwen3", "dsv3_prefill_mxfp8"]
 
 
 def _host_light(inp):
@@ -43,7 +44,7 @@ def _host_light(inp):
 def test_full_size_sampled(name):
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need a GPU")
-    cfg = moe_synth.CONFIGS[name]
+    cfg = moe_synth.ALL_CONFIGS[name]
     print(f"\n[fullsize] {name}: generating inputs", flush=True)
     inp = moe_synth.make_inputs(cfg, "cuda")
     torch.cuda.synchronize()
@@ -69,7 +70,7 @@ def test_full_size_sampled(name):
         assert np.array_equal(to_np(inp["eplb"]["expert_load"]), st["load"])
     # quantized hidden rows of a token sample, bit-exact
     rng = np.random.default_rng(cfg.seed + 100)
-    ue = cfg.act_quant == "ue8m0"
+    ue, grp = O.act_e8m0(cfg), O.act_group(cfg)
     hid = h["hidden"].reshape(-1, cfg.K)
     if cfg.layout == "batched":
         live = np.concatenate([np.arange(e * cfg.max_tokens, e * cfg.max_tokens + int(c))
@@ -77,7 +78,7 @@ def test_full_size_sampled(name):
     else:
         live = np.arange(cfg.T)
     rows = np.sort(rng.choice(live, min(256, live.size), replace=False))
-    q_ref, s_ref = O.quantize_groups(O.bf16_to_f64(hid[rows]).astype(np.float32), ue)
+    q_ref, s_ref = O.quantize_groups(O.bf16_to_f64(hid[rows]).astype(np.float32), ue, grp)
     xq = to_np(bufs["x_q"][torch.from_numpy(rows).cuda()])
     xsf = to_np(bufs["x_sf"][torch.from_numpy(rows).cuda()])
     assert np.array_equal(xq, q_ref)
@@ -93,12 +94,12 @@ def test_full_size_sampled(name):
     gate_up, a2_q, a2_sf, down = (to_np(chain[k]) for k in ("gate_up", "a2_q", "a2_sf", "down"))
     for r, info in ref["rows"].items():
         e = info["expert"]
-        s_abs = abs_gemm(info["x_q"][None], O.scale_values(info["x_sf"][None], ue),
-                         O._np(inp["w13"][e]), O._np(inp["w13_sf"][e]))
+        s_abs = abs_gemm_cfg(cfg, info["x_q"][None], info["x_sf"][None],
+                             O._np(inp["w13"][e]), O._np(inp["w13_sf"][e]))
         check_gemm(gate_up[r:r + 1], info["gate_up"][None], s_abs, f"{name} gate_up row {r}")
         check_requant_chain(a2_q[r:r + 1], a2_sf[r:r + 1], info["a2_q"][None],
                             info["a2_sf"][None], info["gate_up"][None], s_abs, ue,
-                            f"{name} a2 row {r}")
+                            f"{name} a2 row {r}", grp)
         check_output(down[r:r + 1], info["down"][None], f"{name} down row {r}")
     got = to_np(out)[tokens]
     want = np.stack([ref["out"][t] for t in tokens])

@@ -17,8 +17,8 @@ import torch
 import fp8_block_quantized_group_amd as moe
 import moe_synth
 from oracle import moe_oracle as O
-from parity_util import (abs_gemm, check_bf16_close, check_gemm, check_output, check_requant,
-                         check_requant_chain, to_dev, to_np)
+from parity_util import (abs_gemm_cfg, check_bf16_close, check_gemm, check_output,
+                         check_requant, check_requant_chain, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,6 +35,13 @@ SMALL = {
                                   seed=23, act_quant="fp32", num_logical=5),
     "skewed": moe_synth.custom(name="skewed", T=400, E=16, top_k=4, K=256, N=256, seed=24,
                                routing="zipf", zipf_s=1.1, pad_frac=0.05),
+    # MX scheme pair (kMxfp8Static, kMxfp8Dynamic): 32-column E8M0 scales
+    "mx_ragged": moe_synth.custom(name="mx_ragged", T=300, E=5, top_k=3, K=384, N=384,
+                                  seed=25, pad_frac=0.07, act_quant="mxfp8",
+                                  weight_quant="mxfp8"),
+    "mx_batched": moe_synth.custom(name="mx_batched", T=250, E=4, top_k=2, K=384, N=256,
+                                   seed=26, layout="batched", max_tokens=160,
+                                   act_quant="mxfp8", weight_quant="mxfp8"),
 }
 
 
@@ -136,7 +143,7 @@ def gemm_abs(cfg, h, ref, which):
     key = (cfg.name, which)
     if key in _ABS:
         return _ABS[key]
-    ue = cfg.act_quant == "ue8m0"
+    ue = O.act_e8m0(cfg)
     cols = 2 * cfg.N if which == "w13" else cfg.K
     out = np.zeros((ref["gate_up"].shape[0], cols))
     for e, c in enumerate(ref["counts"]):
@@ -151,11 +158,11 @@ def gemm_abs(cfg, h, ref, which):
             rows = np.arange(lo, lo + c)
             a_rows = ref["row_src"][rows]
         if which == "w13":
-            out[rows] = abs_gemm(ref["x_q"][a_rows], O.scale_values(ref["x_sf"][a_rows], ue),
-                                 h["w13"][e], h["w13_sf"][e])
+            out[rows] = abs_gemm_cfg(cfg, ref["x_q"][a_rows], ref["x_sf"][a_rows],
+                                     h["w13"][e], h["w13_sf"][e])
         else:
-            out[rows] = abs_gemm(ref["a2_q"][rows], O.scale_values(ref["a2_sf"][rows], ue),
-                                 h["w2"][e], h["w2_sf"][e])
+            out[rows] = abs_gemm_cfg(cfg, ref["a2_q"][rows], ref["a2_sf"][rows],
+                                     h["w2"][e], h["w2_sf"][e])
     _ABS[key] = out
     return out
 
@@ -175,8 +182,15 @@ def sf_poison(ue8m0):
 # step 1: the group quantizer, exhaustively over bf16
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("ue8m0", [True, False])
-def test_stage_quant_every_bf16_value(gpu, ue8m0):
+@pytest.mark.parametrize("scheme", ["ue8m0", "fp32", "mxfp8"])
+def test_stage_quant_every_bf16_value(gpu, scheme):
+    """Every finite bf16 value alone in its group and packed densely, for the
+    per-128 UE8M0 / fp32 schemes and the per-32 MXFP8 scheme: codes and
+    scales bit-exact."""
+    ue8m0 = scheme != "fp32"
+    group = 32 if scheme == "mxfp8" else 128
+    act = {"ue8m0": moe.Q_FP8_UE8M0, "fp32": moe.Q_FP8_F32, "mxfp8": moe.Q_MXFP8}[scheme]
+    wq = moe.W_MXFP8 if scheme == "mxfp8" else moe.W_FP8_BLOCK128
     bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
     finite = np.isfinite(O.bf16_to_f64(bits))
     vals = bits[finite]
@@ -190,13 +204,13 @@ def test_stage_quant_every_bf16_value(gpu, ue8m0):
     dense = dense.reshape(-1, 128)
     for x in (alone, dense):
         rows = x.shape[0]
-        p = moe.Problem(rows, 128, 128, 1, 1, act_quant=moe.Q_FP8_UE8M0 if ue8m0 else moe.Q_FP8_F32)
+        p = moe.Problem(rows, 128, 128, 1, 1, act_quant=act, weight_quant=wq)
         bufs = moe.alloc_stage_outputs(p)
         ids = torch.zeros((rows, 1), dtype=torch.int32, device="cuda")
         w = torch.ones((rows, 1), dtype=torch.float32, device="cuda")
         moe.stage(p, to_dev(x), ids, w, bufs)
         torch.cuda.synchronize()
-        q_ref, s_ref = O.quantize_groups(O.bf16_to_f64(x).astype(np.float32), ue8m0)
+        q_ref, s_ref = O.quantize_groups(O.bf16_to_f64(x).astype(np.float32), ue8m0, group)
         assert np.array_equal(to_np(bufs["x_q"]), q_ref)
         sf = to_np(bufs["x_sf"])
         if ue8m0:
@@ -213,7 +227,7 @@ def test_stage_quant_every_bf16_value(gpu, ue8m0):
 def test_stage_and_route_bit_exact(gpu, name):
     cfg, h, dev, ref = case(name)
     p, bufs = stage_on_gpu(cfg, dev)
-    ue = cfg.act_quant == "ue8m0"
+    ue = O.act_e8m0(cfg)
     rows = valid_rows(cfg, ref) if cfg.layout == "batched" else np.arange(cfg.T)
     assert np.array_equal(to_np(bufs["x_q"])[rows], ref["x_q"][rows])
     sf = to_np(bufs["x_sf"])[rows]
@@ -269,7 +283,7 @@ def test_stage_bf16_copy(gpu):
 def _gemm_isolated(cfg, h, dev, ref, which):
     p = problem(cfg)
     s = moe.sizes(p)
-    ue = cfg.act_quant == "ue8m0"
+    ue = O.act_e8m0(cfg)
     routing = oracle_routing(p, cfg, ref)
     vr = valid_rows(cfg, ref)
     if which == "w13":
@@ -318,7 +332,7 @@ def test_act_requant_isolated(gpu, name):
     cfg, h, dev, ref = case(name)
     p = problem(cfg)
     s = moe.sizes(p)
-    ue = cfg.act_quant == "ue8m0"
+    ue = O.act_e8m0(cfg)
     vr = valid_rows(cfg, ref)
     gu = np.full((s["expert_rows"], 2 * cfg.N), 0x7FC0, np.uint16)   # NaN outside
     gu[vr] = ref["gate_up"][vr]
@@ -331,10 +345,11 @@ def test_act_requant_isolated(gpu, name):
     torch.cuda.synchronize()
     got_q, got_sf = to_np(a2_q), to_np(a2_sf)
     h32 = O.silu_mul_f32(ref["gate_up"][vr], cfg.N)
+    grp = O.act_group(cfg)
     check_requant(got_q[vr], got_sf[vr], ref["a2_q"][vr], ref["a2_sf"][vr], h32, ue,
-                  f"{name} act_requant")
+                  f"{name} act_requant", grp)
     if ue:
-        G = cfg.N // 128
+        G = cfg.N // grp
         assert np.all(got_sf[vr][:, G:] == 0), "pad bytes of the scale rows must be zero"
     untouched = np.setdiff1d(np.arange(s["expert_rows"]), vr)
     assert np.all(got_q[untouched] == SENTINEL_U8)
@@ -353,14 +368,14 @@ def test_gemm_w13_act_fused_equals_chain(gpu, name, tile_m, monkeypatch):
     p = problem(cfg)
     s = moe.sizes(p)
     assert s["tile_m"] == tile_m
-    ue = cfg.act_quant == "ue8m0"
+    ue = O.act_e8m0(cfg)
     routing = oracle_routing(p, cfg, ref)
     vr = valid_rows(cfg, ref)
     arows = (np.arange(s["stage_rows"]) if cfg.layout != "batched" else vr)
     a_q = to_dev(poisoned(ref["x_q"], arows, 0x7F))
     a_sf = O.pack_ue8m0_rows(ref["x_sf"]) if ue else ref["x_sf"]
     a_sf = to_dev(poisoned(a_sf, arows, sf_poison(ue)))
-    rows, G = s["expert_rows"], cfg.N // 128
+    rows, G = s["expert_rows"], cfg.N // O.act_group(cfg)
     sf_dtype = torch.uint8 if ue else torch.float32
 
     gate_up = torch.empty((rows, 2 * cfg.N), dtype=torch.bfloat16, device="cuda")
@@ -390,7 +405,8 @@ def test_gemm_w13_act_fused_equals_chain(gpu, name, tile_m, monkeypatch):
     else:
         assert np.all(np.isnan(gs[untouched]))
     check_requant_chain(gq[vr], gs[vr], ref["a2_q"][vr], ref["a2_sf"][vr], ref["gate_up"][vr],
-                        gemm_abs(cfg, h, ref, "w13")[vr], ue, f"{name} fused tile {tile_m}")
+                        gemm_abs(cfg, h, ref, "w13")[vr], ue, f"{name} fused tile {tile_m}",
+                        O.act_group(cfg))
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -417,7 +433,7 @@ def run_chain(cfg, dev):
     entry points; returns every intermediate."""
     p, bufs = stage_on_gpu(cfg, dev)
     s = moe.sizes(p)
-    ue = cfg.act_quant == "ue8m0"
+    ue = O.act_e8m0(cfg)
     gate_up = torch.full((s["expert_rows"], 2 * cfg.N), SENTINEL_BF16, dtype=torch.int16,
                          device="cuda").view(torch.bfloat16)
     moe.grouped_gemm_w13(p, bufs["x_q"], bufs["x_sf"], bufs, dev["w13"], dev["w13_sf"], gate_up)
@@ -449,12 +465,13 @@ def run_forward(cfg, dev):
 @pytest.mark.parametrize("name", list(SMALL))
 def test_forward_end_to_end(gpu, name):
     cfg, h, dev, ref = case(name)
-    ue = cfg.act_quant == "ue8m0"
+    ue = O.act_e8m0(cfg)
     chain = run_chain(cfg, dev)
     vr = valid_rows(cfg, ref)
     frac = check_requant_chain(to_np(chain["a2_q"])[vr], to_np(chain["a2_sf"])[vr],
                                ref["a2_q"][vr], ref["a2_sf"][vr], ref["gate_up"][vr],
-                               gemm_abs(cfg, h, ref, "w13")[vr], ue, f"{name} a2 (chain)")
+                               gemm_abs(cfg, h, ref, "w13")[vr], ue, f"{name} a2 (chain)",
+                               O.act_group(cfg))
     print(f"{name}: {frac:.3%} of a2 codes differ at the end of the GPU chain")
     check_output(to_np(chain["out"]), ref["out"], f"{name} chained output")
     out = run_forward(cfg, dev)
