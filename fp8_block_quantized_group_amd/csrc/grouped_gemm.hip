@@ -107,6 +107,12 @@ template <int LOG_4TN>
 __device__ __forceinline__ int key_b(int r) {
   return ((r ^ (r >> (LOG_4TN + 1))) & 1) | (r & 2) | (((r >> LOG_4TN) & 1) << 2);
 }
+// e2m1 weight rows are 64 bytes (4 chunks) per k-step: the same requirement
+// (checked on the CPU for both bank phases and both wave-tile widths)
+template <int LOG_4TN>
+__device__ __forceinline__ int key_w4(int r) {
+  return ((r >> LOG_4TN) & 1) | ((((r >> 1) ^ (r >> (LOG_4TN + 1))) & 1) << 1);
+}
 
 // ---- LDS ring synchronisation ------------------------------------------
 // The ring is filled by buffer_load ... lds issued from inline asm, so the
@@ -223,16 +229,23 @@ template <class S, int SC, bool ACT>
 __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_kernel(
     const GemmArgs p) {
   static_assert(!ACT || (S::BN == 256 && S::WN == 4 && S::TN == 4), "fused activation tile");
-  constexpr bool MX = SC == kQuantMxfp8;
+  constexpr bool W4 = SC == kSchemeMxfp8W4;   // e2m1 weights
+  constexpr bool MX = SC == kQuantMxfp8 || W4;
   constexpr bool UE8M0 = SC == kQuantUe8m0;
+  // weight-tile bytes per row and k-step (128 e4m3 or 128 e2m1 values)
+  constexpr int WROW = W4 ? 64 : kRowBytes;
+  constexpr int BB = S::BN * WROW;
+  constexpr int BI = BB / (S::THREADS * 16);
+  static_assert(BI * S::THREADS * 16 == BB, "weight tile split");
+  constexpr int SC_OFF = S::A_BYTES + BB;     // activation-scale words of a stage
   // MX: the weight rows' E8M0 bytes of 4 k-steps (16 per row) arrive with
   // every fourth stage into one of two panel slots after the ring; the
   // block scheme keeps its fp32 weight-scale panel there instead
-  constexpr int STAGE = S::STAGE_BYTES;
+  constexpr int STAGE = SC_OFF + S::SC_WAVES * 256;
   constexpr int WSC_SLOT = S::BN * 16;
   constexpr int PANEL = MX ? 2 * WSC_SLOT : S::NBLK * kMaxGroups * 4;
   constexpr int LDS = S::STAGES * STAGE + PANEL;
-  constexpr int LMAX = S::LMAX + (MX ? 1 : 0);
+  constexpr int LMAX = S::A_INSTR + BI + 1 + (MX ? 1 : 0);
   static_assert(LDS <= 160 * 1024 && 3 * LMAX < 64, "LDS ring / vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
 
@@ -289,9 +302,11 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
 
   // ---- HBM -> LDS copy plan: thread tid fills 16-byte slot i*THREADS + tid
   const v4i rs_a = buffer_rsrc(p.a, p.a_bytes);
+  const int wstride = W4 ? p.Kd / 2 : p.Kd;   // weight row bytes
   const v4i rs_b =
-      ACT ? buffer_rsrc(p.w + (int64_t)e * p.Nout * p.Kd, (uint32_t)((int64_t)p.Nout * p.Kd))
-          : buffer_rsrc(p.w + ((int64_t)e * p.Nout + n0) * p.Kd, (uint32_t)(S::BN * p.Kd));
+      ACT ? buffer_rsrc(p.w + (int64_t)e * p.Nout * wstride,
+                        (uint32_t)((int64_t)p.Nout * wstride))
+          : buffer_rsrc(p.w + ((int64_t)e * p.Nout + n0) * wstride, (uint32_t)(S::BN * wstride));
   const v4i rs_s = buffer_rsrc(p.a_sf, p.a_sf_bytes);
   // A: load instruction q (64 lanes = 8 rows x 8 chunks) belongs to wave
   // q % NW; only instructions covering rows of the expert are issued (rows
@@ -306,18 +321,19 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     const int r = slot >> 3, c = (slot & 7) ^ key_a(slot >> 3);
     a_off[i] = (r < rows_here) ? (uint32_t)(a_row_of(r) * p.Kd + c * 16) : kOutOfRange;
   }
-  uint32_t b_off[S::B_INSTR];
+  uint32_t b_off[BI];
 #pragma unroll
-  for (int i = 0; i < S::B_INSTR; ++i) {
+  for (int i = 0; i < BI; ++i) {
     const int slot = i * S::THREADS + tid;
-    const int r = slot >> 3, c = (slot & 7) ^ key_b<S::LOG_4TN>(slot >> 3);
+    const int r = W4 ? slot >> 2 : slot >> 3;
+    const int c = W4 ? (slot & 3) ^ key_w4<S::LOG_4TN>(r) : (slot & 7) ^ key_b<S::LOG_4TN>(r);
     int64_t wrow = r;
     if (ACT) {
       // tile row r = 64*w + q: gate row j0 + 32w + q (q < 32), else up row
       const int q = r & 63, w = r >> 6;
       wrow = (q < 32 ? 0 : Nh - 32) + j0 + 32 * w + q;
     }
-    b_off[i] = (uint32_t)(wrow * p.Kd + c * 16);
+    b_off[i] = (uint32_t)(wrow * wstride + c * 16);
   }
   // activation scales: one 4-byte word per row and k-step (UE8M0: the word
   // holding the step's exponent byte; fp32: the scale itself; MX: the step's
@@ -326,7 +342,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // MX weight scales: tile row wave*64 + lane's 16 bytes (4 k-steps), loaded
   // with stages kb = 0 mod 4 only
   const bool loads_wsc = MX && wave < S::BN / 64;
-  const int loads_per_stage = a_loads + S::B_INSTR + (loads_sc ? 1 : 0);
+  const int loads_per_stage = a_loads + BI + (loads_sc ? 1 : 0);
   uint32_t sc_off = kOutOfRange;
   {
     const int r = wave * 64 + lane;
@@ -373,9 +389,10 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int c0 = MX ? kq : 2 * kq, c1 = MX ? kq + 4 : 2 * kq + 1;
   // weight sub-tile i's row for this lane is nl0 + 4*i (same swizzle key)
   const int nl0 = wn * S::WAVE_N + (rho >> 2) * (4 * S::TN) + (rho & 3);
-  const int kbw = key_b<S::LOG_4TN>(nl0);
-  const int w_frag0 = S::A_BYTES + nl0 * kRowBytes + ((c0 ^ kbw) << 4);
-  const int w_frag1 = S::A_BYTES + nl0 * kRowBytes + ((c1 ^ kbw) << 4);
+  // e2m1 weights: lane group kq holds k = 32kq + [0, 32), one 16-byte chunk
+  const int kbw = W4 ? key_w4<S::LOG_4TN>(nl0) : key_b<S::LOG_4TN>(nl0);
+  const int w_frag0 = S::A_BYTES + nl0 * WROW + (((W4 ? kq : c0) ^ kbw) << 4);
+  const int w_frag1 = S::A_BYTES + nl0 * WROW + ((c1 ^ kbw) << 4);
   // activation sub-tile j of this wave holds rows 16*(j*WM + wm) + [0, 16)
   // (interleaved across the WM wave rows, so that a short expert still
   // spreads its rows over them); this lane's row is ml0 + 16*WM*j (same
@@ -383,7 +400,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int ml0 = wm * 16 + rho;
   const int a_frag0 = ml0 * kRowBytes + ((c0 ^ key_a(ml0)) << 4);
   const int a_frag1 = ml0 * kRowBytes + ((c1 ^ key_a(ml0)) << 4);
-  const int sc_frag = S::A_BYTES + S::B_BYTES + ml0 * 4;
+  const int sc_frag = SC_OFF + ml0 * 4;
   // MX: weight row nl0's 16 bytes in a panel slot (+64 per sub-tile)
   const int wsc_frag = S::STAGES * STAGE + nl0 * 16;
   const int scale_shift = 8 * kq;            // MX: this lane's 32-column k-group byte
@@ -401,11 +418,12 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     for (int i = 0; i < S::A_INSTR; ++i)
       if (i < a_loads) dma16(rs_a, st + i * S::THREADS * 16 + wave_slot, a_off[i] + koff);
 #pragma unroll
-    for (int i = 0; i < S::B_INSTR; ++i)
-      dma16(rs_b, st + S::A_BYTES + i * S::THREADS * 16 + wave_slot, b_off[i] + koff);
+    for (int i = 0; i < BI; ++i)
+      dma16(rs_b, st + S::A_BYTES + i * S::THREADS * 16 + wave_slot,
+            b_off[i] + (uint32_t)kb * WROW);
     if (loads_sc) {
       const uint32_t soff = UE8M0 ? (uint32_t)(kb & ~3) : (uint32_t)kb * 4;
-      dma4(rs_s, st + S::A_BYTES + S::B_BYTES + wave_sc, sc_off + soff);
+      dma4(rs_s, st + SC_OFF + wave_sc, sc_off + soff);
     }
     if (loads_wsc && (kb & 3) == 0)
       dma16(rs_w, smem_base + S::STAGES * STAGE + ((kb >> 2) & 1) * WSC_SLOT + wave_slot,
@@ -434,9 +452,14 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       int sw[S::TN];
 #pragma unroll
       for (int i = 0; i < S::TN; ++i) {
-        const v4i lo = *reinterpret_cast<const v4i*>(sb + w_frag0 + i * 4 * kRowBytes);
-        const v4i hi = *reinterpret_cast<const v4i*>(sb + w_frag1 + i * 4 * kRowBytes);
-        wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        const v4i lo = *reinterpret_cast<const v4i*>(sb + w_frag0 + i * 4 * WROW);
+        if constexpr (W4) {
+          // an e2m1 operand is 4 registers; the upper four are not read
+          wf[i] = v8i{lo.x, lo.y, lo.z, lo.w, 0, 0, 0, 0};
+        } else {
+          const v4i hi = *reinterpret_cast<const v4i*>(sb + w_frag1 + i * 4 * WROW);
+          wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
         sw[i] = (int)(*reinterpret_cast<const uint32_t*>(
                           smem + wsc_frag + ((kb >> 2) & 1) * WSC_SLOT + 64 * i + (kb & 3) * 4) >>
                       scale_shift);
@@ -451,8 +474,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
                   scale_shift);
 #pragma unroll
         for (int i = 0; i < S::TN; ++i)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wf[i], af, acc[i][j], 0,
-                                                                       0, 0, sw[i], 0, sa);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+              wf[i], af, acc[i][j], W4 ? 4 : 0, 0, 0, sw[i], 0, sa);
       }
     } else if constexpr (LIVE > 0) {
       const uint8_t* sb = smem + (kb % S::STAGES) * STAGE;
@@ -643,6 +666,8 @@ hipError_t launch_shape(const GemmArgs& p, int max_tiles, int quant, hipStream_t
     grouped_gemm_kernel<S, kQuantF32, ACT><<<grid, S::THREADS, 0, stream>>>(p);
   else if (quant == kQuantMxfp8)
     grouped_gemm_kernel<S, kQuantMxfp8, ACT><<<grid, S::THREADS, 0, stream>>>(p);
+  else if (quant == kSchemeMxfp8W4)
+    grouped_gemm_kernel<S, kSchemeMxfp8W4, ACT><<<grid, S::THREADS, 0, stream>>>(p);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

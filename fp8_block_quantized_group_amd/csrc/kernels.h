@@ -14,6 +14,10 @@ constexpr int kQuantMxfp8 = 3;   // per-32 groups, E8M0 scale bytes
 // weight schemes (values match moe_weight_t)
 constexpr int kWeightBlock128 = 0;   // e4m3, fp32 scale per 128x128 block
 constexpr int kWeightMxfp8 = 1;      // e4m3, E8M0 scale per row and 32 columns
+constexpr int kWeightMxfp4 = 2;      // e2m1 (two per byte), E8M0 per row and 32 columns
+// GEMM scale scheme beyond the activation schemes: MXFP8 activations with
+// e2m1 weights
+constexpr int kSchemeMxfp8W4 = 4;
 
 // routing: slots handled per block of the count / scatter kernels
 constexpr int kRouteChunk = 1024;
@@ -68,7 +72,8 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint
                         int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
                         int32_t* tile_list, hipStream_t stream);
 
-// quant: the activation scheme (kQuant*, kQuantMxfp8 implies MX weights).
+// quant: the scale scheme: an activation scheme (kQuant*; kQuantMxfp8 with
+// e4m3 MX weights) or kSchemeMxfp8W4 (MXFP8 activations, e2m1 MX weights).
 // act = false: out = bf16 GEMM result.  act = true (w13 only): the result's
 // gate half [0, Nout/2) and up half [Nout/2, Nout) are combined into
 // silu(gate) * up and quantized per group (128, or 32 for MX) into act_q /

@@ -111,11 +111,9 @@ moe_status_t validate_problem(const moe_problem_t* p, bool allow_bf16) {
     return fail(MOE_ERR_UNSUPPORTED,
                 "activation quantization %d not supported by this call", p->act_quant);
   // (weight, activation) pairs: block fp8 weights with per-128 activations,
-  // MXFP8 weights with MXFP8 activations
+  // MXFP8 or MXFP4 weights with MXFP8 activations
   const bool mx_w = p->weight_quant != MOE_W_FP8_BLOCK128;
   const bool mx_a = p->act_quant == MOE_Q_MXFP8;
-  if (p->weight_quant == MOE_W_MXFP4)
-    return fail(MOE_ERR_UNSUPPORTED, "MXFP4 weights are not supported by this build");
   if (mx_w != mx_a && p->act_quant != MOE_Q_BF16)
     return fail(MOE_ERR_UNSUPPORTED,
                 "weight quantization %d cannot pair with activation quantization %d",
@@ -302,8 +300,10 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
   g.max_tokens = p->max_tokens_per_expert;
   g.Kd = w13 ? p->hidden : p->intermediate;
   g.Nout = w13 ? 2 * p->intermediate : p->hidden;
+  const int scheme =
+      p->weight_quant == MOE_W_MXFP4 ? moe::kSchemeMxfp8W4 : p->act_quant;
   const hipError_t err =
-      moe::launch_grouped_gemm(g, pl.s.tile_m, (int)pl.max_tiles, p->act_quant, act, stream);
+      moe::launch_grouped_gemm(g, pl.s.tile_m, (int)pl.max_tiles, scheme, act, stream);
   return launch_status(err, act ? "grouped_gemm_w13_act" : w13 ? "grouped_gemm_w13" : "grouped_gemm_w2");
 }
 

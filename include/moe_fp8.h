@@ -45,11 +45,12 @@
  *    w13_sf [E, 2N/128, K/128], w2_sf [E, K/128, N/128], dequantized weight =
  *    code * block scale.  MOE_W_MXFP8 (kMxfp8Static): E8M0 bytes w13_sf
  *    [E, 2N, K/32], w2_sf [E, K, N/32], one per row and 32 columns,
- *    dequantized weight = code * 2^(byte-127).
+ *    dequantized weight = code * 2^(byte-127).  MOE_W_MXFP4 (kMxfp4Static):
+ *    e2m1 codes two per byte, column 2j in the low nibble: w13 [E, 2N, K/2],
+ *    w2 [E, K, N/2] bytes, scales as MXFP8.
  *  - Scheme pairs (HummingExpertsBase._supports_quant_scheme): block fp8
- *    weights with UE8M0 or fp32 per-128 activations; MXFP8 weights with MXFP8
- *    activations.  MXFP4 weights (kMxfp4Static) are declared but rejected
- *    with MOE_ERR_UNSUPPORTED.
+ *    weights with UE8M0 or fp32 per-128 activations; MXFP8 or MXFP4 weights
+ *    with MXFP8 activations.
  */
 #ifndef MOE_FP8_H
 #define MOE_FP8_H

@@ -98,6 +98,9 @@ MX_CONFIGS = {
     "dsv3_prefill_mxfp8": MoeConfig("dsv3_prefill_mxfp8", T=4096, E=256, top_k=8, K=7168,
                                     N=2048, seed=6, routing="zipf", zipf_s=1.1,
                                     pad_frac=0.05, act_quant="mxfp8", weight_quant="mxfp8"),
+    "dsv3_prefill_mxfp4": MoeConfig("dsv3_prefill_mxfp4", T=4096, E=256, top_k=8, K=7168,
+                                    N=2048, seed=7, routing="zipf", zipf_s=1.1,
+                                    pad_frac=0.05, act_quant="mxfp8", weight_quant="mxfp4"),
 }
 
 ALL_CONFIGS = {**CONFIGS, **MX_CONFIGS}

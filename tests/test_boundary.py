@@ -109,10 +109,11 @@ def test_scheme_pairs(lib):
     # (weight, activation) pairs of the experts' supported-scheme list that
     # this library implements; the rest are rejected before any launch
     base = dict(num_tokens=16, hidden=256, intermediate=512, num_experts=4, top_k=2)
-    s = moe.sizes(moe.Problem(**base, act_quant=moe.Q_MXFP8, weight_quant=moe.W_MXFP8))
-    assert s["x_sf_row"] == 256 // 32 and s["a2_sf_row"] == 512 // 32
+    for wq in (moe.W_MXFP8, moe.W_MXFP4):
+        s = moe.sizes(moe.Problem(**base, act_quant=moe.Q_MXFP8, weight_quant=wq))
+        assert s["x_sf_row"] == 256 // 32 and s["a2_sf_row"] == 512 // 32
     for act, wq, status in [(moe.Q_FP8_UE8M0, moe.W_MXFP8, -2), (moe.Q_FP8_F32, moe.W_MXFP8, -2),
-                            (moe.Q_MXFP8, moe.W_FP8_BLOCK128, -2), (moe.Q_MXFP8, moe.W_MXFP4, -2),
+                            (moe.Q_MXFP8, moe.W_FP8_BLOCK128, -2), (moe.Q_FP8_UE8M0, moe.W_MXFP4, -2),
                             (moe.Q_MXFP8, 7, -1), (9, moe.W_MXFP8, -1)]:
         with pytest.raises(moe.MoeError) as ei:
             moe.sizes(moe.Problem(**base, act_quant=act, weight_quant=wq))

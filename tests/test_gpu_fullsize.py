@@ -21,7 +21,8 @@ from test_gpu_parity import run_chain, run_forward
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["tiny", "mixtral", "dsv3_prefill", "dsv3_decode", "qwen3", "dsv3_prefill_mxfp8"]
+FULL = ["tiny", "mixtral", "dsv3_prefill", "dsv3_decode", "qwen3", "dsv3_prefill_mxfp8",
+        "dsv3_prefill_mxfp4"]
 
 
 def _host_light(inp):

@@ -42,6 +42,13 @@ SMALL = {
     "mx_batched": moe_synth.custom(name="mx_batched", T=250, E=4, top_k=2, K=384, N=256,
                                    seed=26, layout="batched", max_tokens=160,
                                    act_quant="mxfp8", weight_quant="mxfp8"),
+    # (kMxfp4Static, kMxfp8Dynamic): e2m1 weights
+    "mx4_ragged": moe_synth.custom(name="mx4_ragged", T=300, E=5, top_k=3, K=384, N=384,
+                                   seed=27, pad_frac=0.07, act_quant="mxfp8",
+                                   weight_quant="mxfp4"),
+    "mx4_skewed": moe_synth.custom(name="mx4_skewed", T=400, E=16, top_k=4, K=256, N=256,
+                                   seed=28, routing="zipf", zipf_s=1.1, act_quant="mxfp8",
+                                   weight_quant="mxfp4"),
 }
 
 
