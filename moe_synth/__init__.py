@@ -59,7 +59,7 @@ class MoeConfig:
     seed: int
     layout: str = "contiguous"          # "contiguous" | "batched"
     max_tokens: int = 0                 # batched layout: rows per expert slab
-    act_quant: str = "ue8m0"            # "ue8m0" | "fp32" (128-groups) | "mxfp8" (32-groups)
+    act_quant: str = "ue8m0"            # "ue8m0" | "fp32" (128-groups) | "mxfp8" (32-groups) | "bf16"
     weight_quant: str = "fp8_block128"  # "fp8_block128" | "mxfp8" | "mxfp4"
     routing: str = "uniform"            # "uniform" | "zipf"
     zipf_s: float = 1.1

@@ -16,7 +16,10 @@ Sources (all from the vLLM API documentation pages on the subject):
            (``process_input``, ``get_buffer_metas``,
            ``_supports_quant_scheme``).
 
-Schemes: block fp8 (kFp8Static128BlockSym weights with 128x128 fp32 scales,
+Schemes: unquantized bf16 activations with block fp8 weights (the
+(kFp8Static128BlockSym, None) pair; staging copies the hidden states, the w2
+input is silu(gate)*up rounded to bf16); block fp8 (kFp8Static128BlockSym
+weights with 128x128 fp32 scales,
 kFp8Dynamic128Sym activations with UE8M0 or fp32 per-128 scales) and MX
 (kMxfp8Static / kMxfp4Static weights with one E8M0 scale per row and 32
 columns, kMxfp8Dynamic activations: the staging quantizer with 32-column
@@ -348,6 +351,28 @@ def mx_gemm_f64(a_codes, a_exps, w_codes, w_exps, fp4: bool) -> np.ndarray:
     return out
 
 
+def bf16_gemm_f64(a_bits, w_codes, w_scale) -> np.ndarray:
+    """out[m, n] = sum_b w_scale[n // 128, b] * sum_{c in block b} a[m, c] * w[n, c]
+    with bf16 activations (the (kFp8Static128BlockSym, None) scheme pair).
+
+    a_bits uint16 [m, C] (bf16), w_codes uint8 [n, C] (e4m3fn), w_scale fp32
+    [n/128, C/128].  Result in fp64; each product is exact, the sums are
+    fp64 sums."""
+    a = bf16_to_f64(a_bits)
+    w = e4m3_decode(w_codes)
+    m, C = a.shape
+    n = w.shape[0]
+    G = C // GROUP
+    a_b = a.reshape(m, G, GROUP).transpose(1, 0, 2)          # [G, m, 128]
+    w_b = w.reshape(n, G, GROUP).transpose(1, 2, 0)          # [G, 128, n]
+    partial = np.matmul(a_b, w_b)                            # [G, m, n]
+    ws = np.repeat(np.asarray(w_scale, np.float64), GROUP, axis=0)  # [n, G]
+    out = np.zeros((m, n), dtype=np.float64)
+    for b in range(G):
+        out += partial[b] * ws[None, :, b]
+    return out
+
+
 # ---------------------------------------------------------------------------
 # scheme selection
 # ---------------------------------------------------------------------------
@@ -363,7 +388,10 @@ def act_e8m0(cfg) -> bool:
 
 
 def expert_gemm(cfg, a_codes, a_stored, w, w_sf) -> np.ndarray:
-    """One expert's GEMM in the workload's scheme (fp64, before rounding)."""
+    """One expert's GEMM in the workload's scheme (fp64, before rounding).
+    bf16 activations: a_codes holds their bits and a_stored is unused."""
+    if cfg.act_quant == "bf16":
+        return bf16_gemm_f64(a_codes, w, w_sf)
     if cfg.weight_quant == "fp8_block128":
         return block_scaled_gemm_f64(a_codes, scale_values(a_stored, act_e8m0(cfg)), w, w_sf)
     return mx_gemm_f64(a_codes, a_stored, w, w_sf, fp4=cfg.weight_quant == "mxfp4")
@@ -384,6 +412,20 @@ def silu_mul_f32(gate_up_bits, N: int) -> np.ndarray:
 
 def act_requant(gate_up_bits, N: int, ue8m0: bool, group: int = GROUP):
     return quantize_groups(silu_mul_f32(gate_up_bits, N), ue8m0, group)
+
+
+def act_bf16(gate_up_bits, N: int):
+    """Unquantized w2 input: h = silu(g) * u (fp32, as above) rounded once to
+    bf16 (the c_dtype of the activation buffer)."""
+    return bf16_round(silu_mul_f32(gate_up_bits, N).astype(np.float64))
+
+
+def act_step(cfg, gate_up_bits):
+    """The w2 input in the workload's scheme: (codes or bf16 bits, scales or
+    None)."""
+    if cfg.act_quant == "bf16":
+        return act_bf16(gate_up_bits, cfg.N), None
+    return act_requant(gate_up_bits, cfg.N, act_e8m0(cfg), act_group(cfg))
 
 
 # ---------------------------------------------------------------------------
@@ -452,6 +494,11 @@ def stage(h: dict):
             + [np.zeros(0, dtype=np.int64)]).astype(np.int64)
     else:
         valid_rows = np.arange(hid.shape[0])
+    if cfg.act_quant == "bf16":
+        # staging copies the hidden states unquantized ([STAGE]: no hidden_quant)
+        x_q = np.zeros(hid.shape, dtype=np.uint16)
+        x_q[valid_rows] = hid[valid_rows]
+        return {"ids": ids, "weights": w, "load": load, "x_q": x_q, "x_sf": None, **lay}
     G = cfg.K // grp
     x_q = np.zeros(hid.shape, dtype=np.uint8)
     x_sf = np.zeros((hid.shape[0], G), dtype=np.uint8 if ue8m0 else np.float32)
@@ -479,10 +526,11 @@ def forward(h: dict) -> dict:
         rows_total = E * cfg.max_tokens
     else:
         rows_total = int(st["offsets"][-1])
+    bf16_act = cfg.act_quant == "bf16"
     gate_up = np.zeros((rows_total, 2 * N), dtype=np.uint16)
-    a2_q = np.zeros((rows_total, N), dtype=np.uint8)
-    a2_sf = np.zeros((rows_total, N // grp),
-                     dtype=np.uint8 if ue8m0 else np.float32)
+    a2_q = np.zeros((rows_total, N), dtype=np.uint16 if bf16_act else np.uint8)
+    a2_sf = None if bf16_act else np.zeros((rows_total, N // grp),
+                                           dtype=np.uint8 if ue8m0 else np.float32)
     down = np.zeros((rows_total, K), dtype=np.uint16)
     for e in range(E):
         n_e = int(counts[e])
@@ -495,11 +543,13 @@ def forward(h: dict) -> dict:
             lo = int(st["offsets"][e])
             rows = np.arange(lo, lo + n_e)
             a_rows = st["row_src"][rows]
-        gu = expert_gemm(cfg, st["x_q"][a_rows], st["x_sf"][a_rows],
-                         h["w13"][e], h["w13_sf"][e])
+        x_sf = None if st["x_sf"] is None else st["x_sf"][a_rows]
+        gu = expert_gemm(cfg, st["x_q"][a_rows], x_sf, h["w13"][e], h["w13_sf"][e])
         gate_up[rows] = bf16_round(gu)
-        q2, s2 = act_requant(gate_up[rows], N, ue8m0, grp)
-        a2_q[rows], a2_sf[rows] = q2, s2
+        q2, s2 = act_step(cfg, gate_up[rows])
+        a2_q[rows] = q2
+        if s2 is not None:
+            a2_sf[rows] = s2
         dn = expert_gemm(cfg, q2, s2, h["w2"][e], h["w2_sf"][e])
         down[rows] = bf16_round(dn)
     out = topk_reduce(down, st["slot_row"], st["weights"])
@@ -534,14 +584,18 @@ def forward_tokens(h: dict, tokens, st: dict | None = None) -> dict:
             w13, w13s, w2, w2s = _np(w13), _np(w13s), _np(w2), _np(w2s)
         for (t, j, r) in lst:
             a_row = r if cfg.layout == "batched" else t
-            x = bf16_to_f64(hid[a_row:a_row + 1]).astype(np.float32)
-            xq, xsf = quantize_groups(x, ue8m0, grp)
+            if cfg.act_quant == "bf16":
+                xq, xsf = hid[a_row:a_row + 1].copy(), None
+            else:
+                x = bf16_to_f64(hid[a_row:a_row + 1]).astype(np.float32)
+                xq, xsf = quantize_groups(x, ue8m0, grp)
             gu = bf16_round(expert_gemm(cfg, xq, xsf, w13, w13s))
-            q2, s2 = act_requant(gu, N, ue8m0, grp)
+            q2, s2 = act_step(cfg, gu)
             dn = bf16_round(expert_gemm(cfg, q2, s2, w2, w2s))
             rows_info[r] = {"token": t, "slot": j, "expert": e, "x_q": xq[0],
-                            "x_sf": xsf[0], "gate_up": gu[0], "a2_q": q2[0],
-                            "a2_sf": s2[0], "down": dn[0]}
+                            "x_sf": None if xsf is None else xsf[0], "gate_up": gu[0],
+                            "a2_q": q2[0], "a2_sf": None if s2 is None else s2[0],
+                            "down": dn[0]}
     outs = {}
     for t in tokens:
         acc = np.zeros(K, dtype=np.float64)

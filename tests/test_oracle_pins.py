@@ -487,6 +487,47 @@ def test_block_gemm_identity_weights():
     assert np.array_equal(got, O.e4m3_decode(a) * np.repeat(sa, 128, axis=1))
 
 
+def _finite_bf16(rng, shape, scale=1.0):
+    x = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)     # truncation: any finite bf16
+
+
+def test_bf16_gemm_equals_dense_dequantized_matmul():
+    rng = np.random.default_rng(27)
+    m, n, C = 23, 256, 384
+    a = _finite_bf16(rng, (m, C), 3.0)
+    w = _finite_codes(rng, (n, C))
+    sw = rng.uniform(0.001, 0.01, (n // 128, C // 128)).astype(np.float32)
+    got = O.bf16_gemm_f64(a, w, sw)
+    A = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    W = O.e4m3_decode(w) * np.repeat(np.repeat(sw.astype(np.float64), 128, 0), 128, 1)
+    want = A @ W.T
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12 * np.abs(want).max())
+
+
+def test_bf16_gemm_identity_weights():
+    rng = np.random.default_rng(28)
+    a = _finite_bf16(rng, (9, 256))
+    w = np.zeros((256, 256), np.uint8)
+    w[np.arange(256), np.arange(256)] = 0x38
+    got = O.bf16_gemm_f64(a, w, np.ones((2, 2), np.float32))
+    assert np.array_equal(got, (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+
+
+def test_act_bf16_matches_torch():
+    rng = np.random.default_rng(29)
+    N = 256
+    gu = _finite_bf16(rng, (64, 2 * N), 2.0)
+    got = O.act_bf16(gu, N)
+    t = torch.from_numpy(gu.view(np.int16)).view(torch.bfloat16).float()
+    want = (torch.nn.functional.silu(t[:, :N]) * t[:, N:]).to(torch.bfloat16)
+    want = want.view(torch.int16).numpy().view(np.uint16)
+    # fp32 silu may differ from the fp64 evaluation in its last bit, which
+    # can move a bf16 rounding by one unit
+    diff = np.abs(got.astype(np.int32) - want.astype(np.int32))
+    assert diff.max() <= 1 and np.count_nonzero(diff) <= 0.005 * diff.size
+
+
 # --------------------------------------------------------------------------
 # SiLU(gate) * up and the reduce
 # --------------------------------------------------------------------------
@@ -574,6 +615,20 @@ def test_tiny_mx_layer_tracks_unquantized_ffn(wq):
     got = O.bf16_to_f64(r["out"])
     rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
     assert 1e-3 < rel < 0.08, rel
+
+
+def test_tiny_bf16_layer_tracks_unquantized_ffn():
+    """bf16 activations (staging copy, bf16 w2 input): only bf16 roundings
+    separate it from the fp64 FFN with the same weights."""
+    cfg = moe_synth.custom(T=16, E=4, top_k=2, K=256, N=512, seed=1, act_quant="bf16")
+    h = O.host_inputs(moe_synth.make_inputs(cfg))
+    r = O.forward(h)
+    assert r["x_sf"] is None and r["a2_sf"] is None
+    assert np.array_equal(r["x_q"], h["hidden"])
+    ref = _dense_ffn(h, r)
+    got = O.bf16_to_f64(r["out"])
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert 1e-4 < rel < 1e-2, rel
 
 
 def test_layouts_and_padding_agree():
