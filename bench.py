@@ -76,19 +76,22 @@ def algorithmic(cfg, counts, T_valid):
     touched = int((counts > 0).sum())
     group = 32 if cfg.act_quant == "mxfp8" else 128
     sfb = 4 if cfg.act_quant == "fp32" else 1       # bytes per activation scale
+    ab = 2 if cfg.act_quant == "bf16" else 1        # bytes per activation value
+    if cfg.act_quant == "bf16":
+        sfb = 0
     GK, GN = K // group, N // group
     rows_in = int(counts.sum()) if cfg.layout == "batched" else cfg.T
     a = {}
-    a["stage"] = rows_in * K * 2 + rows_in * K + rows_in * GK * sfb
+    a["stage"] = rows_in * K * 2 + rows_in * K * ab + rows_in * GK * sfb
     if cfg.weight_quant == "fp8_block128":
         w13_sf, w2_sf = (2 * N // 128) * (K // 128) * 4, (K // 128) * (N // 128) * 4
     else:                                            # E8M0 byte per row and 32 columns
         w13_sf, w2_sf = 2 * N * (K // 32), K * (N // 32)
     w_elem = 0.5 if cfg.weight_quant == "mxfp4" else 1
-    w13_in = touched * (2 * N * K * w_elem + w13_sf) + T_valid * (K + GK * sfb)
-    a["w13_act_bytes"] = w13_in + M * (N + GN * sfb)        # fp8 a2 + scales out
+    w13_in = touched * (2 * N * K * w_elem + w13_sf) + T_valid * (K * ab + GK * sfb)
+    a["w13_act_bytes"] = w13_in + M * (N * ab + GN * sfb)   # a2 (+ scales) out
     a["w13_flops"] = 2.0 * M * 2 * N * K
-    a["w2_bytes"] = (touched * (K * N * w_elem + w2_sf) + M * (N + GN * sfb) + M * K * 2)
+    a["w2_bytes"] = (touched * (K * N * w_elem + w2_sf) + M * (N * ab + GN * sfb) + M * K * 2)
     a["w2_flops"] = 2.0 * M * N * K
     a["reduce"] = M * K * 2 + cfg.T * K * 2 + cfg.T * k * 8
     return a
@@ -141,9 +144,7 @@ def profile_pass(p, cfg, inp, out):
     del src, dst
     s = moe.sizes(p)
     bufs = moe.alloc_stage_outputs(p)
-    a2_q = torch.empty((s["expert_rows"], cfg.N), dtype=torch.uint8, device="cuda")
-    a2_sf = torch.empty((s["expert_rows"], s["a2_sf_row"]),
-                        dtype=moe.scale_dtype(p), device="cuda")
+    a2_q, a2_sf = moe.alloc_act_outputs(p)
     down = torch.empty((s["expert_rows"], cfg.K), dtype=torch.bfloat16, device="cuda")
     moe.stage(p, inp["hidden"], inp["topk_ids"], inp["topk_weights"], bufs, inp["is_padding"],
               inp["expert_num_tokens"], inp["eplb"])
@@ -215,9 +216,7 @@ def main():
     # ---- per-kernel timing through the separate entry points -------------
     s = moe.sizes(p)
     bufs = moe.alloc_stage_outputs(p)
-    a2_q = torch.empty((s["expert_rows"], cfg.N), dtype=torch.uint8, device="cuda")
-    a2_sf = torch.empty((s["expert_rows"], s["a2_sf_row"]),
-                        dtype=moe.scale_dtype(p), device="cuda")
+    a2_q, a2_sf = moe.alloc_act_outputs(p)
     down = torch.empty((s["expert_rows"], cfg.K), dtype=torch.bfloat16, device="cuda")
     flush_buf = torch.empty(1 << 28, dtype=torch.int32, device="cuda")   # 1 GiB > MALL
 

@@ -180,6 +180,17 @@ def scale_dtype(p: Problem):
     return torch.float32 if p.act_quant == Q_FP8_F32 else torch.uint8
 
 
+def alloc_act_outputs(p: Problem, device="cuda"):
+    """(a2_q, a2_sf) for the w2 input: fp8 codes and scales, or bf16 values
+    and None for unquantized activations."""
+    s = sizes(p)
+    rows = s["expert_rows"]
+    if p.act_quant == Q_BF16:
+        return torch.empty((rows, p.intermediate), dtype=torch.bfloat16, device=device), None
+    return (torch.empty((rows, p.intermediate), dtype=torch.uint8, device=device),
+            torch.empty((rows, s["a2_sf_row"]), dtype=scale_dtype(p), device=device))
+
+
 def alloc_stage_outputs(p: Problem, device="cuda") -> dict:
     """Caller-side buffers for moe_stage (allocated by torch)."""
     s = sizes(p)

@@ -54,6 +54,8 @@ namespace {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kRowBytes = 128;      // one k-step of a row: 128 fp8 values
@@ -230,6 +232,13 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     const GemmArgs p) {
   static_assert(!ACT || (S::BN == 256 && S::WN == 4 && S::TN == 4), "fused activation tile");
   constexpr bool W4 = SC == kSchemeMxfp8W4;   // e2m1 weights
+  constexpr bool A16 = SC == kQuantBf16;      // unquantized bf16 activations
+  // activation-tile bytes per row and k-step (128 fp8 or 128 bf16 values)
+  constexpr int AROW = A16 ? 2 * kRowBytes : kRowBytes;
+  constexpr int AB = S::BM * AROW;
+  constexpr int ACH = AROW / 16;                          // 16-byte chunks per row
+  constexpr int AI = S::BM * ACH >= S::THREADS ? S::BM * ACH / S::THREADS : 1;
+  constexpr int RPI = 64 / ACH;                           // rows per load instruction
   constexpr bool MX = SC == kQuantMxfp8 || W4;
   constexpr bool UE8M0 = SC == kQuantUe8m0;
   // weight-tile bytes per row and k-step (128 e4m3 or 128 e2m1 values)
@@ -237,15 +246,15 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   constexpr int BB = S::BN * WROW;
   constexpr int BI = BB / (S::THREADS * 16);
   static_assert(BI * S::THREADS * 16 == BB, "weight tile split");
-  constexpr int SC_OFF = S::A_BYTES + BB;     // activation-scale words of a stage
+  constexpr int SC_OFF = AB + BB;            // activation-scale words of a stage
   // MX: the weight rows' E8M0 bytes of 4 k-steps (16 per row) arrive with
   // every fourth stage into one of two panel slots after the ring; the
   // block scheme keeps its fp32 weight-scale panel there instead
-  constexpr int STAGE = SC_OFF + S::SC_WAVES * 256;
+  constexpr int STAGE = SC_OFF + (A16 ? 0 : S::SC_WAVES * 256);
   constexpr int WSC_SLOT = S::BN * 16;
   constexpr int PANEL = MX ? 2 * WSC_SLOT : S::NBLK * kMaxGroups * 4;
   constexpr int LDS = S::STAGES * STAGE + PANEL;
-  constexpr int LMAX = S::A_INSTR + BI + 1 + (MX ? 1 : 0);
+  constexpr int LMAX = AI + BI + 1 + (MX ? 1 : 0);
   static_assert(LDS <= 160 * 1024 && 3 * LMAX < 64, "LDS ring / vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS];
 
@@ -312,14 +321,18 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // q % NW; only instructions covering rows of the expert are issued (rows
   // past its count are never read; their LDS slots keep stale bytes, which
   // only ever meet output rows that are not stored).
-  const int a_groups = (rows_here + 7) >> 3;
+  const int a_groups = (rows_here + RPI - 1) / RPI;
   const int a_loads = a_groups > wave ? (a_groups - wave + S::NW - 1) / S::NW : 0;
-  uint32_t a_off[S::A_INSTR];
+  uint32_t a_off[AI];
 #pragma unroll
-  for (int i = 0; i < S::A_INSTR; ++i) {
+  for (int i = 0; i < AI; ++i) {
     const int slot = i * S::THREADS + tid;
-    const int r = slot >> 3, c = (slot & 7) ^ key_a(slot >> 3);
-    a_off[i] = (r < rows_here) ? (uint32_t)(a_row_of(r) * p.Kd + c * 16) : kOutOfRange;
+    // bf16 rows (16 chunks) use key r & 15: a fragment read touches 16
+    // consecutive rows at one chunk index
+    const int r = slot / ACH;
+    const int c = A16 ? (slot % ACH) ^ (r & 15) : (slot & 7) ^ key_a(r);
+    a_off[i] = (r < rows_here) ? (uint32_t)(a_row_of(r) * p.Kd * (A16 ? 2 : 1) + c * 16)
+                               : kOutOfRange;
   }
   uint32_t b_off[BI];
 #pragma unroll
@@ -338,7 +351,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // activation scales: one 4-byte word per row and k-step (UE8M0: the word
   // holding the step's exponent byte; fp32: the scale itself; MX: the step's
   // four 32-column exponent bytes)
-  const bool loads_sc = wave < S::SC_WAVES && wave * 64 < rows_here;
+  const bool loads_sc = !A16 && wave < S::SC_WAVES && wave * 64 < rows_here;
   // MX weight scales: tile row wave*64 + lane's 16 bytes (4 k-steps), loaded
   // with stages kb = 0 mod 4 only
   const bool loads_wsc = MX && wave < S::BN / 64;
@@ -391,8 +404,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int nl0 = wn * S::WAVE_N + (rho >> 2) * (4 * S::TN) + (rho & 3);
   // e2m1 weights: lane group kq holds k = 32kq + [0, 32), one 16-byte chunk
   const int kbw = W4 ? key_w4<S::LOG_4TN>(nl0) : key_b<S::LOG_4TN>(nl0);
-  const int w_frag0 = S::A_BYTES + nl0 * WROW + (((W4 ? kq : c0) ^ kbw) << 4);
-  const int w_frag1 = S::A_BYTES + nl0 * WROW + ((c1 ^ kbw) << 4);
+  const int w_frag0 = AB + nl0 * WROW + (((W4 ? kq : c0) ^ kbw) << 4);
+  const int w_frag1 = AB + nl0 * WROW + ((c1 ^ kbw) << 4);
   // activation sub-tile j of this wave holds rows 16*(j*WM + wm) + [0, 16)
   // (interleaved across the WM wave rows, so that a short expert still
   // spreads its rows over them); this lane's row is ml0 + 16*WM*j (same
@@ -400,6 +413,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int ml0 = wm * 16 + rho;
   const int a_frag0 = ml0 * kRowBytes + ((c0 ^ key_a(ml0)) << 4);
   const int a_frag1 = ml0 * kRowBytes + ((c1 ^ key_a(ml0)) << 4);
+  // bf16 activations: MFMA m of a k-step covers k = 32kq + 8m + [0, 8), i.e.
+  // chunk 4kq + m of the row (the weight bytes 32kq + 8m + [0, 8) match)
+  const int a16_frag = ml0 * AROW + ((4 * kq) ^ rho) * 16;
   const int sc_frag = SC_OFF + ml0 * 4;
   // MX: weight row nl0's 16 bytes in a panel slot (+64 per sub-tile)
   const int wsc_frag = S::STAGES * STAGE + nl0 * 16;
@@ -413,14 +429,13 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
 
   auto issue = [&](int kb) {
     const uint32_t st = smem_base + (kb % S::STAGES) * STAGE;
-    const uint32_t koff = (uint32_t)kb * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < S::A_INSTR; ++i)
-      if (i < a_loads) dma16(rs_a, st + i * S::THREADS * 16 + wave_slot, a_off[i] + koff);
+    for (int i = 0; i < AI; ++i)
+      if (i < a_loads)
+        dma16(rs_a, st + i * S::THREADS * 16 + wave_slot, a_off[i] + (uint32_t)kb * AROW);
 #pragma unroll
     for (int i = 0; i < BI; ++i)
-      dma16(rs_b, st + S::A_BYTES + i * S::THREADS * 16 + wave_slot,
-            b_off[i] + (uint32_t)kb * WROW);
+      dma16(rs_b, st + AB + i * S::THREADS * 16 + wave_slot, b_off[i] + (uint32_t)kb * WROW);
     if (loads_sc) {
       const uint32_t soff = UE8M0 ? (uint32_t)(kb & ~3) : (uint32_t)kb * 4;
       dma4(rs_s, st + SC_OFF + wave_sc, sc_off + soff);
@@ -443,7 +458,57 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // two MFMAs after issue, once it has left the matrix pipe.
   auto compute = [&](int kb, auto live_c) {
     constexpr int LIVE = decltype(live_c)::value;
-    if constexpr (MX && LIVE > 0) {
+    if constexpr (A16 && LIVE > 0) {
+      // bf16 activations x fp8 weights converted to bf16 (exact): four
+      // 16x16x32 bf16 MFMAs per sub-tile per 128-deep block, chained in a
+      // partial, then acc += partial * sw
+      const uint8_t* sb = smem + (kb % S::STAGES) * STAGE;
+      const float sw = sw_mine[kb];
+      v8bf wb[S::TN][4];
+#pragma unroll
+      for (int i = 0; i < S::TN; ++i) {
+        const v4i lo = *reinterpret_cast<const v4i*>(sb + w_frag0 + i * 4 * WROW);
+        const v4i hi = *reinterpret_cast<const v4i*>(sb + w_frag1 + i * 4 * WROW);
+        const int words[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          v4i packed;
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const int w = words[2 * m + h2];
+            const v2f f01 = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+            const v2f f23 = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+            // e4m3 values are exact in bf16: keep the upper halves
+            packed[2 * h2] = (int)__builtin_amdgcn_perm(__float_as_uint(f01.y),
+                                                        __float_as_uint(f01.x), 0x07060302u);
+            packed[2 * h2 + 1] = (int)__builtin_amdgcn_perm(__float_as_uint(f23.y),
+                                                            __float_as_uint(f23.x), 0x07060302u);
+          }
+          wb[i][m] = __builtin_bit_cast(v8bf, packed);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < LIVE; ++j) {
+        v8bf ab[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          ab[m] = __builtin_bit_cast(
+              v8bf, *reinterpret_cast<const v4i*>(sb + (a16_frag ^ (m << 4)) +
+                                                  j * kSubStride * AROW));
+        v4f part[S::TN];
+#pragma unroll
+        for (int i = 0; i < S::TN; ++i) part[i] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+          for (int i = 0; i < S::TN; ++i)
+            part[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i][m], ab[m], part[i], 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < S::TN; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(part[i][r], sw, acc[i][j][r]);
+      }
+    } else if constexpr (MX && LIVE > 0) {
       // both operands carry E8M0 scales per (row, 32 columns): lane l's byte
       // for its row and k-group l >> 4 goes to the MFMA, which accumulates
       // straight into acc (byte 127 = 1.0)
@@ -593,6 +658,19 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 16));
       amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 32));
     }
+    if constexpr (A16) {
+      // unquantized w2 input: h rounded once to bf16, 16 bytes per lane
+#pragma unroll
+      for (int j = 0; j < S::TM; ++j) {
+        const int ml = ml0 + kSubStride * j;
+        if (ml >= rows_here) continue;
+        const int64_t row = base + m0 + ml;
+        *reinterpret_cast<uint4*>(p.act_q + (row * Nh + j0 + col_off) * 2) =
+            make_uint4(pack_bf16x2(h[j][0], h[j][1]), pack_bf16x2(h[j][2], h[j][3]),
+                       pack_bf16x2(h[j][4], h[j][5]), pack_bf16x2(h[j][6], h[j][7]));
+      }
+      return;
+    }
     // 128-column groups: maximum across the WN = 4 waves sharing the rows,
     // through LDS.  MX 32-column groups: one wave's columns, already reduced.
     float* red = reinterpret_cast<float*>(smem);   // [WN][BM]
@@ -668,6 +746,16 @@ hipError_t launch_shape(const GemmArgs& p, int max_tiles, int quant, hipStream_t
     grouped_gemm_kernel<S, kQuantMxfp8, ACT><<<grid, S::THREADS, 0, stream>>>(p);
   else if (quant == kSchemeMxfp8W4)
     grouped_gemm_kernel<S, kSchemeMxfp8W4, ACT><<<grid, S::THREADS, 0, stream>>>(p);
+  else if (quant == kQuantBf16) {
+    // bf16 activation tiles take twice the LDS: only shapes whose ring fits
+    constexpr bool fits =
+        S::STAGES * (S::BM * 2 * kRowBytes + S::BN * kRowBytes) + S::NBLK * kMaxGroups * 4 <=
+        160 * 1024;
+    if constexpr (fits)
+      grouped_gemm_kernel<S, kQuantBf16, ACT><<<grid, S::THREADS, 0, stream>>>(p);
+    else
+      return hipErrorInvalidValue;
+  }
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -675,9 +763,40 @@ hipError_t launch_shape(const GemmArgs& p, int max_tiles, int quant, hipStream_t
 
 }  // namespace
 
+// bf16 activations take twice the activation-tile LDS: two-slot rings and
+// tiles of at most 128 rows
+template <bool ACT>
+hipError_t launch_a16(const GemmArgs& p, int tile_m, int max_tiles, hipStream_t stream) {
+  const int q = kQuantBf16;
+  if (ACT || p.Nout % 256 == 0) {
+    switch (tile_m) {
+      case 16: return launch_shape<Shape<16, 256, 4, 2>, ACT>(p, max_tiles, q, stream);
+      case 32: return launch_shape<Shape<32, 256, 4, 2>, ACT>(p, max_tiles, q, stream);
+      case 64: return launch_shape<Shape<64, 256, 8, 2>, ACT>(p, max_tiles, q, stream);
+      case 128: return launch_shape<Shape<128, 256, 8, 2>, ACT>(p, max_tiles, q, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if constexpr (!ACT) {
+    switch (tile_m) {
+      case 16: return launch_shape<Shape<16, 128, 4, 2>, false>(p, max_tiles, q, stream);
+      case 32: return launch_shape<Shape<32, 128, 4, 2>, false>(p, max_tiles, q, stream);
+      case 64: return launch_shape<Shape<64, 128, 4, 2>, false>(p, max_tiles, q, stream);
+      case 128: return launch_shape<Shape<128, 128, 4, 2>, false>(p, max_tiles, q, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& p, int tile_m, int max_tiles, int quant, bool act,
                                hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
+  if (quant == kQuantBf16) {
+    if (act && p.Nout % 256 != 0) return hipErrorInvalidValue;
+    return act ? launch_a16<true>(p, tile_m, max_tiles, stream)
+               : launch_a16<false>(p, tile_m, max_tiles, stream);
+  }
   if (act) {
     // 256 weight rows = 128 gate + 128 up rows per block, any tile height
     if (p.Nout % 256 != 0) return hipErrorInvalidValue;

@@ -63,9 +63,13 @@ int choose_tile_m(const moe_problem_t* p) {
   const char* env = getenv("MOE_TILE_M");
   if (env != nullptr) {
     const int v = atoi(env);
-    if (v == 16 || v == 32 || v == 64 || v == 128 || v == 192 || v == 256) return v;
+    if (v == 16 || v == 32 || v == 64 || v == 128 ||
+        ((v == 192 || v == 256) && p->act_quant != MOE_Q_BF16))
+      return v;
   }
   const double rows = (double)p->num_tokens * p->top_k / p->num_experts;
+  // bf16 activation tiles take twice the LDS: at most 128 rows
+  if (p->act_quant == MOE_Q_BF16 && rows > 48.0) return 128;
   if (rows <= 12.0) return 16;
   if (rows <= 24.0) return 32;
   if (rows <= 48.0) return 64;
@@ -73,7 +77,7 @@ int choose_tile_m(const moe_problem_t* p) {
   return 256;
 }
 
-moe_status_t validate_problem(const moe_problem_t* p, bool allow_bf16) {
+moe_status_t validate_problem(const moe_problem_t* p) {
   if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "problem is NULL");
   if (p->num_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens < 0 (%d)", p->num_tokens);
   if (p->hidden <= 0 || p->hidden % 128 != 0)
@@ -100,21 +104,20 @@ moe_status_t validate_problem(const moe_problem_t* p, bool allow_bf16) {
     const int64_t rows = batched(p) ? (int64_t)p->num_experts * p->max_tokens_per_expert
                                     : (int64_t)p->num_tokens * p->top_k;
     const int64_t in_rows = batched(p) ? rows : p->num_tokens;
-    if (in_rows * p->hidden >= ((int64_t)7 << 29) || rows * p->intermediate >= ((int64_t)7 << 29))
+    const int64_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
+    if (in_rows * p->hidden * elem >= ((int64_t)7 << 29) ||
+        rows * p->intermediate * elem >= ((int64_t)7 << 29))
       return fail(MOE_ERR_UNSUPPORTED, "activation buffers are limited to 3.5 GiB");
   }
   if (p->act_quant < MOE_Q_FP8_UE8M0 || p->act_quant > MOE_Q_MXFP8)
     return fail(MOE_ERR_INVALID_ARG, "unknown activation quantization %d", p->act_quant);
   if (p->weight_quant < MOE_W_FP8_BLOCK128 || p->weight_quant > MOE_W_MXFP4)
     return fail(MOE_ERR_INVALID_ARG, "unknown weight quantization %d", p->weight_quant);
-  if (p->act_quant == MOE_Q_BF16 && !allow_bf16)
-    return fail(MOE_ERR_UNSUPPORTED,
-                "activation quantization %d not supported by this call", p->act_quant);
-  // (weight, activation) pairs: block fp8 weights with per-128 activations,
-  // MXFP8 or MXFP4 weights with MXFP8 activations
+  // (weight, activation) pairs: block fp8 weights with per-128 or bf16
+  // activations, MXFP8 or MXFP4 weights with MXFP8 activations
   const bool mx_w = p->weight_quant != MOE_W_FP8_BLOCK128;
   const bool mx_a = p->act_quant == MOE_Q_MXFP8;
-  if (mx_w != mx_a && p->act_quant != MOE_Q_BF16)
+  if (mx_w != mx_a || (mx_w && p->act_quant == MOE_Q_BF16))
     return fail(MOE_ERR_UNSUPPORTED,
                 "weight quantization %d cannot pair with activation quantization %d",
                 p->weight_quant, p->act_quant);
@@ -149,16 +152,17 @@ Plan make_plan(const moe_problem_t* p) {
   }
   pl.s.tile_list = 1 + 2 * pl.max_tiles + (E + 1);
   const bool mx = p->act_quant == MOE_Q_MXFP8;
-  pl.s.x_sf_row = mx ? K / 32 : ue ? 4 * ((GK + 3) / 4) : GK;
-  pl.s.a2_sf_row = mx ? N / 32 : ue ? 4 * ((GN + 3) / 4) : GN;
+  const bool bf = p->act_quant == MOE_Q_BF16;
+  pl.s.x_sf_row = bf ? 0 : mx ? K / 32 : ue ? 4 * ((GK + 3) / 4) : GK;
+  pl.s.a2_sf_row = bf ? 0 : mx ? N / 32 : ue ? 4 * ((GN + 3) / 4) : GN;
   pl.route_blocks = (T * k + moe::kRouteChunk - 1) / moe::kRouteChunk;
   pl.stage_ws_bytes = round_up((size_t)std::max<int64_t>(pl.route_blocks, 1) * E * 4);
   const size_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
   pl.x_q_bytes = (size_t)pl.s.stage_rows * K * elem;
   const size_t sfb = p->act_quant == MOE_Q_FP8_F32 ? 4 : 1;
   pl.x_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.stage_rows * pl.s.x_sf_row * sfb;
-  pl.a2_q_bytes = (size_t)pl.s.expert_rows * N;
-  pl.a2_sf_bytes = (size_t)pl.s.expert_rows * pl.s.a2_sf_row * sfb;
+  pl.a2_q_bytes = (size_t)pl.s.expert_rows * N * elem;
+  pl.a2_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.expert_rows * pl.s.a2_sf_row * sfb;
   pl.down_bytes = (size_t)pl.s.expert_rows * K * 2;
   return pl;
 }
@@ -207,6 +211,16 @@ moe_status_t check_ptr(const void* ptr, const char* name, size_t align) {
     const moe_status_t _s = (expr);         \
     if (_s != MOE_OK) return _s;            \
   } while (0)
+
+// Activation-scale pointer: required for quantized activations, NULL for bf16.
+moe_status_t check_sf(const moe_problem_t* p, const void* sf, const char* name) {
+  if (p->act_quant == MOE_Q_BF16) {
+    if (sf != nullptr)
+      return fail(MOE_ERR_INVALID_ARG, "%s must be NULL for bf16 activations", name);
+    return MOE_OK;
+  }
+  return check_ptr(sf, name, 4);
+}
 
 moe_status_t check_routing(const moe_routing_t* r) {
   if (r == nullptr) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
@@ -331,21 +345,21 @@ extern "C" {
 const char* moe_last_error(void) { return g_last_error.c_str(); }
 
 moe_status_t moe_routing_sizes(const moe_problem_t* p, moe_sizes_t* out) {
-  CHECK(validate_problem(p, true));
+  CHECK(validate_problem(p));
   if (out == nullptr) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
   *out = make_plan(p).s;
   return ok();
 }
 
 moe_status_t moe_stage_workspace_size(const moe_problem_t* p, size_t* bytes) {
-  CHECK(validate_problem(p, true));
+  CHECK(validate_problem(p));
   if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
   *bytes = make_plan(p).stage_ws_bytes;
   return ok();
 }
 
 moe_status_t moe_workspace_size(const moe_problem_t* p, size_t* bytes) {
-  CHECK(validate_problem(p, false));
+  CHECK(validate_problem(p));
   if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
   const Plan pl = make_plan(p);
   *bytes = carve(pl, p, nullptr).total;
@@ -358,7 +372,7 @@ moe_status_t moe_stage(const moe_problem_t* p, const void* hidden,
                        const moe_eplb_t* eplb, void* x_q, void* x_sf, int64_t* topk_idx_out,
                        float* topk_w_out, const moe_routing_t* routing, void* ws,
                        size_t ws_bytes, void* stream) {
-  CHECK(validate_problem(p, true));
+  CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
   CHECK(check_stage_args(p, hidden, expert_num_tokens_in, topk_ids, topk_weights, eplb));
   CHECK(check_ptr(x_q, "x_q", 16));
@@ -381,10 +395,10 @@ moe_status_t moe_stage(const moe_problem_t* p, const void* hidden,
 moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const void* a_sf,
                                   const moe_routing_t* routing, const void* w13,
                                   const void* w13_sf, void* gate_up, void* stream) {
-  CHECK(validate_problem(p, false));
+  CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
   CHECK(check_ptr(a_q, "a_q", 16));
-  CHECK(check_ptr(a_sf, "a_sf", 4));
+  CHECK(check_sf(p, a_sf, "a_sf"));
   CHECK(check_routing(routing));
   CHECK(check_ptr(w13, "w13", 16));
   CHECK(check_ptr(w13_sf, "w13_sf", 4));
@@ -397,15 +411,15 @@ moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q, c
                                       const moe_routing_t* routing, const void* w13,
                                       const void* w13_sf, void* a2_q, void* a2_sf,
                                       void* stream) {
-  CHECK(validate_problem(p, false));
+  CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
   CHECK(check_ptr(a_q, "a_q", 16));
-  CHECK(check_ptr(a_sf, "a_sf", 4));
+  CHECK(check_sf(p, a_sf, "a_sf"));
   CHECK(check_routing(routing));
   CHECK(check_ptr(w13, "w13", 16));
   CHECK(check_ptr(w13_sf, "w13_sf", 4));
   CHECK(check_ptr(a2_q, "a2_q", 16));
-  CHECK(check_ptr(a2_sf, "a2_sf", 4));
+  CHECK(check_sf(p, a2_sf, "a2_sf"));
   const Plan pl = make_plan(p);
   return run_gemm(p, pl, true, a_q, a_sf, routing, w13, w13_sf, nullptr, (hipStream_t)stream,
                   true, a2_q, a2_sf);
@@ -414,12 +428,12 @@ moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q, c
 moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
                              const moe_routing_t* routing, void* a2_q, void* a2_sf,
                              void* stream) {
-  CHECK(validate_problem(p, false));
+  CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
   CHECK(check_ptr(gate_up, "gate_up", 16));
   CHECK(check_routing(routing));
   CHECK(check_ptr(a2_q, "a2_q", 16));
-  CHECK(check_ptr(a2_sf, "a2_sf", 4));
+  CHECK(check_sf(p, a2_sf, "a2_sf"));
   const Plan pl = make_plan(p);
   return run_act(p, pl, gate_up, routing, a2_q, a2_sf, (hipStream_t)stream);
 }
@@ -427,10 +441,10 @@ moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
 moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const void* a2_sf,
                                  const moe_routing_t* routing, const void* w2,
                                  const void* w2_sf, void* down, void* stream) {
-  CHECK(validate_problem(p, false));
+  CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
   CHECK(check_ptr(a2_q, "a2_q", 16));
-  CHECK(check_ptr(a2_sf, "a2_sf", 4));
+  CHECK(check_sf(p, a2_sf, "a2_sf"));
   CHECK(check_routing(routing));
   CHECK(check_ptr(w2, "w2", 16));
   CHECK(check_ptr(w2_sf, "w2_sf", 4));
@@ -441,7 +455,7 @@ moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const
 
 moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int32_t* slot_row,
                              const float* topk_w, void* out, void* stream) {
-  CHECK(validate_problem(p, true));
+  CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
   CHECK(check_ptr(down, "down", 16));
   CHECK(check_ptr(slot_row, "slot_row", 4));
@@ -456,7 +470,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
                          const moe_eplb_t* eplb, const void* w13, const void* w13_sf,
                          const void* w2, const void* w2_sf, void* out, void* ws,
                          size_t ws_bytes, void* stream) {
-  CHECK(validate_problem(p, false));
+  CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
   CHECK(check_stage_args(p, hidden, expert_num_tokens_in, topk_ids, topk_weights, eplb));
   CHECK(check_ptr(w13, "w13", 16));

@@ -122,6 +122,32 @@ __global__ __launch_bounds__(256) void act_requant_kernel(
                                sf_row, g, GN, sf_row_len);
 }
 
+// bf16 activations (no quantization): h = silu(gate) * up, computed as
+// above and rounded once to bf16; 8 columns per thread.
+__global__ __launch_bounds__(256) void act_bf16_kernel(
+    const uint16_t* __restrict__ gu, uint16_t* __restrict__ out, int64_t num_vec, int N,
+    const int32_t* __restrict__ num_rows, const int32_t* __restrict__ counts, int max_tokens) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= num_vec) return;
+  const int vpr = N / 8;
+  const int64_t row = i / vpr;
+  const int col = (int)(i - row * vpr) * 8;
+  if (num_rows != nullptr && row >= (int64_t)*num_rows) return;
+  if (!row_live(row, counts, max_tokens)) return;
+  const uint16_t* src = gu + row * (int64_t)(2 * N) + col;
+  float fg[8], fu[8], h[8];
+  unpack8(*reinterpret_cast<const uint4*>(src), fg);
+  unpack8(*reinterpret_cast<const uint4*>(src + N), fu);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-fg[k]));
+    h[k] = fg[k] * sig * fu[k];
+  }
+  *reinterpret_cast<uint4*>(out + row * (int64_t)N + col) =
+      make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
+                 pack_bf16x2(h[6], h[7]));
+}
+
 inline unsigned blocks_for(int64_t n, int per_block) {
   return (unsigned)((n + per_block - 1) / per_block);
 }
@@ -159,6 +185,12 @@ hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t 
                               int quant, const int32_t* num_rows, const int32_t* counts,
                               int max_tokens, hipStream_t stream) {
   if (rows_cap == 0) return hipSuccess;
+  if (quant == kQuantBf16) {
+    const int64_t nvec = rows_cap * (N / 8);
+    act_bf16_kernel<<<blocks_for(nvec, 256), 256, 0, stream>>>(
+        (const uint16_t*)gate_up, (uint16_t*)aq, nvec, N, num_rows, counts, max_tokens);
+    return hipGetLastError();
+  }
   if (quant == kQuantMxfp8) {
     const int GN = N / 32;
     act_requant_kernel<true, 4><<<blocks_for(rows_cap * GN, 64), 256, 0, stream>>>(

@@ -49,8 +49,11 @@
  *    e2m1 codes two per byte, column 2j in the low nibble: w13 [E, 2N, K/2],
  *    w2 [E, K, N/2] bytes, scales as MXFP8.
  *  - Scheme pairs (HummingExpertsBase._supports_quant_scheme): block fp8
- *    weights with UE8M0 or fp32 per-128 activations; MXFP8 or MXFP4 weights
- *    with MXFP8 activations.
+ *    weights with UE8M0 or fp32 per-128 activations or with unquantized bf16
+ *    activations (the (kFp8Static128BlockSym, None) pair: staging copies the
+ *    hidden states, the w2 input is silu(gate)*up rounded to bf16, every
+ *    activation-scale pointer is NULL); MXFP8 or MXFP4 weights with MXFP8
+ *    activations.
  */
 #ifndef MOE_FP8_H
 #define MOE_FP8_H
@@ -74,7 +77,7 @@ typedef enum {
 typedef enum {
   MOE_Q_FP8_UE8M0 = 0, /* fp8 e4m3fn, per-128 power-of-two scales          */
   MOE_Q_FP8_F32 = 1,   /* fp8 e4m3fn, per-128 fp32 scales                   */
-  MOE_Q_BF16 = 2,      /* staging only: hidden states copied unquantized    */
+  MOE_Q_BF16 = 2,      /* bf16 activations, unquantized (no scales)          */
   MOE_Q_MXFP8 = 3      /* fp8 e4m3fn, per-32 E8M0 scales (kMxfp8Dynamic)    */
 } moe_quant_t;
 
@@ -197,22 +200,25 @@ moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const
  * The pages fuse the activation into the w2-input quantization
  * (HummingExpertsBase.process_input with an activation); here it moves one
  * step earlier, into the producing GEMM.  a2_q fp8 [expert_rows, N], a2_sf per
- * the activation scheme; rows past an expert's count are not written.
+ * the activation scheme (bf16 activations: a2_q bf16 [expert_rows, N], a2_sf
+ * NULL); rows past an expert's count are not written.
  * a2_q / a2_sf must not overlap a_q / a_sf. */
 moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q,
                                       const void* a_sf, const moe_routing_t* routing,
                                       const void* w13, const void* w13_sf, void* a2_q,
                                       void* a2_sf, void* stream);
 
-/* Step 4: a2 = quant(silu(gate_up[:, :N]) * gate_up[:, N:]) per 128 columns,
- * computed in fp32 and quantized without an intermediate rounding.
- * a2_q fp8 [expert_rows, N], a2_sf per the activation scheme. */
+/* Step 4: a2 = quant(silu(gate_up[:, :N]) * gate_up[:, N:]) per group (128
+ * columns, 32 for MXFP8), computed in fp32 and quantized without an
+ * intermediate rounding.  a2_q fp8 [expert_rows, N], a2_sf per the activation
+ * scheme; bf16 activations: a2_q = bf16(silu(g) * u) [expert_rows, N], a2_sf
+ * NULL. */
 moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
                              const moe_routing_t* routing, void* a2_q, void* a2_sf,
                              void* stream);
 
-/* Step 5: down[r, :] = block-scaled fp8 GEMM of a2 row r with w2[e];
- * down: bf16 [expert_rows, K]. */
+/* Step 5: down[r, :] = block-scaled GEMM of a2 row r with w2[e] (fp8 or bf16
+ * a2 per the activation scheme); down: bf16 [expert_rows, K]. */
 moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const void* a2_sf,
                                  const moe_routing_t* routing, const void* w2,
                                  const void* w2_sf, void* down, void* stream);
@@ -225,8 +231,7 @@ moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int
 
 /* Steps 1-6 on one stream (stage, fused w13 + activation, w2, reduce).
  * Arguments as in moe_stage plus the weights and out bf16 [T, K]; ws: device
- * workspace of moe_workspace_size bytes.
- * act_quant must be MOE_Q_FP8_UE8M0 or MOE_Q_FP8_F32. */
+ * workspace of moe_workspace_size bytes.  Any supported scheme pair. */
 moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
                          const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
                          const float* topk_weights, const uint8_t* is_padding,

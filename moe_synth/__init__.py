@@ -103,7 +103,15 @@ MX_CONFIGS = {
                                     pad_frac=0.05, act_quant="mxfp8", weight_quant="mxfp4"),
 }
 
-ALL_CONFIGS = {**CONFIGS, **MX_CONFIGS}
+# The Qwen3-shaped batch with unquantized bf16 activations (the staging copy
+# variant, carried through the layer with the (kFp8Static128BlockSym, None)
+# scheme pair).
+BF16_CONFIGS = {
+    "qwen3_bf16": MoeConfig("qwen3_bf16", T=16384, E=144, top_k=8, K=4096, N=1536,
+                            seed=5, act_quant="bf16", num_logical=128),
+}
+
+ALL_CONFIGS = {**CONFIGS, **MX_CONFIGS, **BF16_CONFIGS}
 
 
 def _gen(device, seed: int, stream: str) -> torch.Generator:

@@ -81,8 +81,12 @@ def abs_gemm(a_codes, a_scale, w_codes, w_sf):
 
 
 def abs_gemm_cfg(cfg, a_codes, a_stored, w_codes, w_sf):
-    """S_abs in the workload's scheme: block fp8 (scale values) or MX (E8M0
-    bytes on both operands; e2m1 sign bits cleared nibble by nibble)."""
+    """S_abs in the workload's scheme: bf16 activations, block fp8 (scale
+    values) or MX (E8M0 bytes on both operands; e2m1 sign bits cleared nibble
+    by nibble)."""
+    if cfg.act_quant == "bf16":
+        return O.bf16_gemm_f64(np.asarray(a_codes) & 0x7FFF, np.asarray(w_codes) & 0x7F,
+                               np.abs(np.asarray(w_sf)))
     if cfg.weight_quant == "fp8_block128":
         return abs_gemm(a_codes, O.scale_values(a_stored, O.act_e8m0(cfg)), w_codes, w_sf)
     fp4 = cfg.weight_quant == "mxfp4"
@@ -172,6 +176,27 @@ def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_ga
     if ue8m0:
         assert np.abs(got_sf[:, :G].astype(int) - ref_sf[:, :G].astype(int)).max() <= 1
     return np.count_nonzero(got_q != ref_q) / got_q.size
+
+
+def check_bf16_act_chain(got_bits, ref_bits, ref_gate_up_bits, s_abs_gate_up, what):
+    """bf16 w2 input at the end of the GPU's own chain: the GEMM bound on
+    gate_up carried through silu(g) * u, plus one bf16 rounding on each side.
+    Returns the fraction of values that differ."""
+    N = ref_bits.shape[1]
+    gu = O.bf16_to_f64(ref_gate_up_bits)
+    g, u = gu[:, :N], gu[:, N:]
+    dgu = bf16_ulp(gu) + MFMA_REL * s_abs_gate_up
+    dg, du = dgu[:, :N], dgu[:, N:]
+    sig = 1.0 / (1.0 + np.exp(-g))
+    silu = g * sig
+    dsilu = np.abs(sig * (1.0 + g * (1.0 - sig)))
+    dh = (dsilu * np.abs(u) * dg + np.abs(silu) * du + 1.1 * dg * du) * 1.01
+    vg, vr = O.bf16_to_f64(got_bits), O.bf16_to_f64(ref_bits)
+    assert np.all(np.isfinite(vg)), f"{what}: non-finite values"
+    bound = dh + bf16_ulp(vr) + np.abs(silu * u) * 2.0 ** -20
+    bad = np.abs(vg - vr) > bound * 1.000001
+    assert not bad.any(), f"{what}: {bad.sum()} values beyond the propagated bound"
+    return np.count_nonzero(got_bits != ref_bits) / got_bits.size
 
 
 def check_output(got_bits, ref_bits, what):

@@ -144,11 +144,12 @@ def test_call_validation_before_launch(lib):
     # workspace too small
     st = lib.moe_forward(ctypes.byref(p), V, None, V, V, None, None, V, V, V, V, V, V, 16, None)
     assert st == -3
-    # bf16 activations are a staging-only scheme
-    pb = moe.Problem(16, 256, 512, 4, 2, act_quant=moe.Q_BF16).c()
-    st = lib.moe_forward(ctypes.byref(pb), V, None, V, V, None, None, V, V, V, V, V, V,
+    # bf16 activations pair only with block fp8 weights
+    pbm = moe.Problem(16, 256, 512, 4, 2, act_quant=moe.Q_BF16, weight_quant=moe.W_MXFP8).c()
+    st = lib.moe_forward(ctypes.byref(pbm), V, None, V, V, None, None, V, V, V, V, V, V,
                          1 << 30, None)
     assert st == -2
+    pb = moe.Problem(16, 256, 512, 4, 2, act_quant=moe.Q_BF16).c()
     # batched layout without expert_num_tokens
     pbt = moe.Problem(16, 256, 512, 4, 2, layout=moe.LAYOUT_BATCHED,
                       max_tokens_per_expert=8).c()
@@ -167,9 +168,13 @@ def test_call_validation_before_launch(lib):
     st = lib.moe_grouped_gemm_w13_act(ctypes.byref(p), V, V, ctypes.byref(r), V, V, V,
                                       _fake((1 << 20) + 2), None)
     assert st == -1 and "a2_sf" in lib.moe_last_error().decode()
-    # ... and is a quantized-activation scheme only
-    st = lib.moe_grouped_gemm_w13_act(ctypes.byref(pb), V, V, ctypes.byref(r), V, V, V, V, None)
-    assert st == -2
+    # bf16 activations carry no scales
+    st = lib.moe_grouped_gemm_w13_act(ctypes.byref(pb), V, V, ctypes.byref(r), V, V, V, None,
+                                      None)
+    assert st == -1 and "a_sf" in lib.moe_last_error().decode()
+    st = lib.moe_grouped_gemm_w13_act(ctypes.byref(pb), V, None, ctypes.byref(r), V, V, V, V,
+                                      None)
+    assert st == -1 and "a2_sf" in lib.moe_last_error().decode()
 
 
 def test_empty_batch_is_a_noop(lib):

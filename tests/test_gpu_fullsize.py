@@ -16,13 +16,14 @@ import torch
 import fp8_block_quantized_group_amd as moe
 import moe_synth
 from oracle import moe_oracle as O
-from parity_util import abs_gemm_cfg, check_gemm, check_output, check_requant_chain, to_np
+from parity_util import (abs_gemm_cfg, check_bf16_act_chain, check_gemm, check_output,
+                         check_requant_chain, to_np)
 from test_gpu_parity import run_chain, run_forward
 
 pytestmark = pytest.mark.gpu
 
 FULL = ["tiny", "mixtral", "dsv3_prefill", "dsv3_decode", "qwen3", "dsv3_prefill_mxfp8",
-        "dsv3_prefill_mxfp4"]
+        "dsv3_prefill_mxfp4", "qwen3_bf16"]
 
 
 def _host_light(inp):
@@ -79,28 +80,37 @@ def test_full_size_sampled(name):
     else:
         live = np.arange(cfg.T)
     rows = np.sort(rng.choice(live, min(256, live.size), replace=False))
-    q_ref, s_ref = O.quantize_groups(O.bf16_to_f64(hid[rows]).astype(np.float32), ue, grp)
     xq = to_np(bufs["x_q"][torch.from_numpy(rows).cuda()])
-    xsf = to_np(bufs["x_sf"][torch.from_numpy(rows).cuda()])
-    assert np.array_equal(xq, q_ref)
-    if ue:
-        assert np.array_equal(xsf, O.pack_ue8m0_rows(s_ref))
+    if cfg.act_quant == "bf16":
+        assert np.array_equal(xq, hid[rows]) and bufs["x_sf"] is None   # staging copy
     else:
-        assert np.array_equal(xsf.view(np.uint32), s_ref.view(np.uint32))
+        q_ref, s_ref = O.quantize_groups(O.bf16_to_f64(hid[rows]).astype(np.float32), ue, grp)
+        xsf = to_np(bufs["x_sf"][torch.from_numpy(rows).cuda()])
+        assert np.array_equal(xq, q_ref)
+        if ue:
+            assert np.array_equal(xsf, O.pack_ue8m0_rows(s_ref))
+        else:
+            assert np.array_equal(xsf.view(np.uint32), s_ref.view(np.uint32))
     # a few whole tokens through the oracle
     routed = np.flatnonzero((st["slot_row"] >= 0).any(axis=1))
     tokens = sorted(set(rng.choice(routed, min(3, routed.size), replace=False).tolist()))
     print(f"[fullsize] {name}: oracle on tokens {tokens}", flush=True)
     ref = O.forward_tokens(h, tokens, st)
-    gate_up, a2_q, a2_sf, down = (to_np(chain[k]) for k in ("gate_up", "a2_q", "a2_sf", "down"))
+    gate_up, a2_q, down = (to_np(chain[k]) for k in ("gate_up", "a2_q", "down"))
+    a2_sf = None if chain["a2_sf"] is None else to_np(chain["a2_sf"])
     for r, info in ref["rows"].items():
         e = info["expert"]
-        s_abs = abs_gemm_cfg(cfg, info["x_q"][None], info["x_sf"][None],
+        s_abs = abs_gemm_cfg(cfg, info["x_q"][None],
+                             None if info["x_sf"] is None else info["x_sf"][None],
                              O._np(inp["w13"][e]), O._np(inp["w13_sf"][e]))
         check_gemm(gate_up[r:r + 1], info["gate_up"][None], s_abs, f"{name} gate_up row {r}")
-        check_requant_chain(a2_q[r:r + 1], a2_sf[r:r + 1], info["a2_q"][None],
-                            info["a2_sf"][None], info["gate_up"][None], s_abs, ue,
-                            f"{name} a2 row {r}", grp)
+        if cfg.act_quant == "bf16":
+            check_bf16_act_chain(a2_q[r:r + 1], info["a2_q"][None], info["gate_up"][None],
+                                 s_abs, f"{name} a2 row {r}")
+        else:
+            check_requant_chain(a2_q[r:r + 1], a2_sf[r:r + 1], info["a2_q"][None],
+                                info["a2_sf"][None], info["gate_up"][None], s_abs, ue,
+                                f"{name} a2 row {r}", grp)
         check_output(down[r:r + 1], info["down"][None], f"{name} down row {r}")
     got = to_np(out)[tokens]
     want = np.stack([ref["out"][t] for t in tokens])

@@ -17,8 +17,8 @@ import torch
 import fp8_block_quantized_group_amd as moe
 import moe_synth
 from oracle import moe_oracle as O
-from parity_util import (abs_gemm_cfg, check_bf16_close, check_gemm, check_output,
-                         check_requant, check_requant_chain, to_dev, to_np)
+from parity_util import (abs_gemm_cfg, check_bf16_act_chain, check_bf16_close, check_gemm,
+                         check_output, check_requant, check_requant_chain, to_dev, to_np)
 
 pytestmark = pytest.mark.gpu
 
@@ -42,6 +42,12 @@ SMALL = {
     "mx_batched": moe_synth.custom(name="mx_batched", T=250, E=4, top_k=2, K=384, N=256,
                                    seed=26, layout="batched", max_tokens=160,
                                    act_quant="mxfp8", weight_quant="mxfp8"),
+    # (kFp8Static128BlockSym, None): unquantized bf16 activations
+    "bf16_ragged": moe_synth.custom(name="bf16_ragged", T=300, E=5, top_k=3, K=384, N=384,
+                                    seed=29, pad_frac=0.07, act_quant="bf16"),
+    "bf16_batched": moe_synth.custom(name="bf16_batched", T=250, E=4, top_k=2, K=384, N=256,
+                                     seed=30, layout="batched", max_tokens=160,
+                                     act_quant="bf16"),
     # (kMxfp4Static, kMxfp8Dynamic): e2m1 weights
     "mx4_ragged": moe_synth.custom(name="mx4_ragged", T=300, E=5, top_k=3, K=384, N=384,
                                    seed=27, pad_frac=0.07, act_quant="mxfp8",
@@ -165,10 +171,12 @@ def gemm_abs(cfg, h, ref, which):
             rows = np.arange(lo, lo + c)
             a_rows = ref["row_src"][rows]
         if which == "w13":
-            out[rows] = abs_gemm_cfg(cfg, ref["x_q"][a_rows], ref["x_sf"][a_rows],
+            x_sf = None if ref["x_sf"] is None else ref["x_sf"][a_rows]
+            out[rows] = abs_gemm_cfg(cfg, ref["x_q"][a_rows], x_sf,
                                      h["w13"][e], h["w13_sf"][e])
         else:
-            out[rows] = abs_gemm_cfg(cfg, ref["a2_q"][rows], ref["a2_sf"][rows],
+            a2_sf = None if ref["a2_sf"] is None else ref["a2_sf"][rows]
+            out[rows] = abs_gemm_cfg(cfg, ref["a2_q"][rows], a2_sf,
                                      h["w2"][e], h["w2_sf"][e])
     _ABS[key] = out
     return out
@@ -237,10 +245,13 @@ def test_stage_and_route_bit_exact(gpu, name):
     ue = O.act_e8m0(cfg)
     rows = valid_rows(cfg, ref) if cfg.layout == "batched" else np.arange(cfg.T)
     assert np.array_equal(to_np(bufs["x_q"])[rows], ref["x_q"][rows])
-    sf = to_np(bufs["x_sf"])[rows]
-    if ue:
+    if cfg.act_quant == "bf16":
+        assert bufs["x_sf"] is None and ref["x_sf"] is None
+    elif ue:
+        sf = to_np(bufs["x_sf"])[rows]
         assert np.array_equal(sf, O.pack_ue8m0_rows(ref["x_sf"][rows]))
     else:
+        sf = to_np(bufs["x_sf"])[rows]
         assert np.array_equal(sf.view(np.uint32), ref["x_sf"][rows].view(np.uint32))
     assert np.array_equal(to_np(bufs["topk_idx"]), ref["ids"])
     assert np.array_equal(to_np(bufs["topk_w"]).view(np.uint32), ref["weights"].view(np.uint32))
@@ -293,19 +304,24 @@ def _gemm_isolated(cfg, h, dev, ref, which):
     ue = O.act_e8m0(cfg)
     routing = oracle_routing(p, cfg, ref)
     vr = valid_rows(cfg, ref)
+    bf = cfg.act_quant == "bf16"
+    poison = 0x7FC0 if bf else 0x7F            # bf16 NaN / e4m3 NaN outside the counts
     if which == "w13":
         arows = (np.arange(s["stage_rows"]) if cfg.layout != "batched" else vr)
-        a_q = poisoned(ref["x_q"], arows, 0x7F)
-        a_sf = ref["x_sf"]
-        a_sf = O.pack_ue8m0_rows(a_sf) if ue else a_sf
-        a_sf = poisoned(a_sf, arows, sf_poison(ue))
+        a_q = poisoned(ref["x_q"], arows, poison)
+        a_sf = None
+        if not bf:
+            a_sf = O.pack_ue8m0_rows(ref["x_sf"]) if ue else ref["x_sf"]
+            a_sf = poisoned(a_sf, arows, sf_poison(ue))
         cols = 2 * cfg.N
         want = ref["gate_up"]
     else:
-        a_q = np.full((s["expert_rows"], cfg.N), 0x7F, np.uint8)
+        a_q = np.full((s["expert_rows"], cfg.N), poison, ref["a2_q"].dtype)
         a_q[vr] = ref["a2_q"][vr]
-        a_sf = O.pack_ue8m0_rows(ref["a2_sf"]) if ue else ref["a2_sf"]
-        a_sf = poisoned(a_sf, vr, sf_poison(ue))
+        a_sf = None
+        if not bf:
+            a_sf = O.pack_ue8m0_rows(ref["a2_sf"]) if ue else ref["a2_sf"]
+            a_sf = poisoned(a_sf, vr, sf_poison(ue))
         cols = cfg.K
         want = ref["down"]
     out = torch.full((s["expert_rows"], cols), SENTINEL_BF16, dtype=torch.int16,
@@ -313,7 +329,7 @@ def _gemm_isolated(cfg, h, dev, ref, which):
     w = dev["w13"] if which == "w13" else dev["w2"]
     w_sf = dev["w13_sf"] if which == "w13" else dev["w2_sf"]
     fn = moe.grouped_gemm_w13 if which == "w13" else moe.grouped_gemm_w2
-    fn(p, to_dev(a_q), to_dev(a_sf), routing, w, w_sf, out)
+    fn(p, to_dev(a_q), None if a_sf is None else to_dev(a_sf), routing, w, w_sf, out)
     torch.cuda.synchronize()
     got = to_np(out)
     frac = check_gemm(got[vr], want[vr], gemm_abs(cfg, h, ref, which)[vr], f"{cfg.name} {which}")
@@ -344,6 +360,18 @@ def test_act_requant_isolated(gpu, name):
     gu = np.full((s["expert_rows"], 2 * cfg.N), 0x7FC0, np.uint16)   # NaN outside
     gu[vr] = ref["gate_up"][vr]
     routing = oracle_routing(p, cfg, ref)
+    if cfg.act_quant == "bf16":
+        # unquantized: h rounded to bf16, within one bf16 unit of the oracle's
+        # (fp32 exp / reciprocal vs fp64, then one rounding each)
+        a2 = torch.full((s["expert_rows"], cfg.N), SENTINEL_BF16, dtype=torch.int16,
+                        device="cuda").view(torch.bfloat16)
+        moe.act_requant(p, to_dev(gu), routing, a2, None)
+        torch.cuda.synchronize()
+        got = to_np(a2)
+        check_bf16_close(got[vr], ref["a2_q"][vr], f"{name} act bf16")
+        untouched = np.setdiff1d(np.arange(s["expert_rows"]), vr)
+        assert np.all(got[untouched] == SENTINEL_BF16)
+        return
     a2_q = torch.full((s["expert_rows"], cfg.N), SENTINEL_U8, dtype=torch.uint8, device="cuda")
     a2_sf = (torch.zeros((s["expert_rows"], s["a2_sf_row"]), dtype=torch.uint8, device="cuda")
              if ue else torch.zeros((s["expert_rows"], s["a2_sf_row"]), dtype=torch.float32,
@@ -372,6 +400,8 @@ def test_gemm_w13_act_fused_equals_chain(gpu, name, tile_m, monkeypatch):
     additionally against the oracle's a2 through check_requant_chain."""
     monkeypatch.setenv("MOE_TILE_M", str(tile_m))
     cfg, h, dev, ref = case(name)
+    if cfg.act_quant == "bf16" and tile_m > 128:
+        pytest.skip("bf16 activation tiles are at most 128 rows (LDS)")
     p = problem(cfg)
     s = moe.sizes(p)
     assert s["tile_m"] == tile_m
@@ -379,6 +409,25 @@ def test_gemm_w13_act_fused_equals_chain(gpu, name, tile_m, monkeypatch):
     routing = oracle_routing(p, cfg, ref)
     vr = valid_rows(cfg, ref)
     arows = (np.arange(s["stage_rows"]) if cfg.layout != "batched" else vr)
+    if cfg.act_quant == "bf16":
+        rows = s["expert_rows"]
+        a_q = to_dev(poisoned(ref["x_q"], arows, 0x7FC0))
+        gate_up = torch.empty((rows, 2 * cfg.N), dtype=torch.bfloat16, device="cuda")
+        moe.grouped_gemm_w13(p, a_q, None, routing, dev["w13"], dev["w13_sf"], gate_up)
+        want = torch.full((rows, cfg.N), SENTINEL_BF16, dtype=torch.int16,
+                          device="cuda").view(torch.bfloat16)
+        moe.act_requant(p, gate_up, routing, want, None)
+        got = torch.full((rows, cfg.N), SENTINEL_BF16, dtype=torch.int16,
+                         device="cuda").view(torch.bfloat16)
+        moe.grouped_gemm_w13_act(p, a_q, None, routing, dev["w13"], dev["w13_sf"], got, None)
+        torch.cuda.synchronize()
+        g, w = to_np(got), to_np(want)
+        assert np.array_equal(g[vr], w[vr]), f"{name} tile {tile_m}: fused bf16 a2 differs"
+        untouched = np.setdiff1d(np.arange(rows), vr)
+        assert np.all(g[untouched] == SENTINEL_BF16), "fused call wrote rows outside the counts"
+        check_bf16_act_chain(g[vr], ref["a2_q"][vr], ref["gate_up"][vr],
+                             gemm_abs(cfg, h, ref, "w13")[vr], f"{name} fused tile {tile_m}")
+        return
     a_q = to_dev(poisoned(ref["x_q"], arows, 0x7F))
     a_sf = O.pack_ue8m0_rows(ref["x_sf"]) if ue else ref["x_sf"]
     a_sf = to_dev(poisoned(a_sf, arows, sf_poison(ue)))
@@ -444,9 +493,15 @@ def run_chain(cfg, dev):
     gate_up = torch.full((s["expert_rows"], 2 * cfg.N), SENTINEL_BF16, dtype=torch.int16,
                          device="cuda").view(torch.bfloat16)
     moe.grouped_gemm_w13(p, bufs["x_q"], bufs["x_sf"], bufs, dev["w13"], dev["w13_sf"], gate_up)
-    a2_q = torch.full((s["expert_rows"], cfg.N), SENTINEL_U8, dtype=torch.uint8, device="cuda")
-    a2_sf = torch.zeros((s["expert_rows"], s["a2_sf_row"]),
-                        dtype=torch.uint8 if ue else torch.float32, device="cuda")
+    if cfg.act_quant == "bf16":
+        a2_q = torch.full((s["expert_rows"], cfg.N), SENTINEL_BF16, dtype=torch.int16,
+                          device="cuda").view(torch.bfloat16)
+        a2_sf = None
+    else:
+        a2_q = torch.full((s["expert_rows"], cfg.N), SENTINEL_U8, dtype=torch.uint8,
+                          device="cuda")
+        a2_sf = torch.zeros((s["expert_rows"], s["a2_sf_row"]),
+                            dtype=torch.uint8 if ue else torch.float32, device="cuda")
     moe.act_requant(p, gate_up, bufs, a2_q, a2_sf)
     down = torch.full((s["expert_rows"], cfg.K), SENTINEL_BF16, dtype=torch.int16,
                       device="cuda").view(torch.bfloat16)
@@ -475,10 +530,15 @@ def test_forward_end_to_end(gpu, name):
     ue = O.act_e8m0(cfg)
     chain = run_chain(cfg, dev)
     vr = valid_rows(cfg, ref)
-    frac = check_requant_chain(to_np(chain["a2_q"])[vr], to_np(chain["a2_sf"])[vr],
-                               ref["a2_q"][vr], ref["a2_sf"][vr], ref["gate_up"][vr],
-                               gemm_abs(cfg, h, ref, "w13")[vr], ue, f"{name} a2 (chain)",
-                               O.act_group(cfg))
+    if cfg.act_quant == "bf16":
+        frac = check_bf16_act_chain(to_np(chain["a2_q"])[vr], ref["a2_q"][vr],
+                                    ref["gate_up"][vr], gemm_abs(cfg, h, ref, "w13")[vr],
+                                    f"{name} a2 (chain)")
+    else:
+        frac = check_requant_chain(to_np(chain["a2_q"])[vr], to_np(chain["a2_sf"])[vr],
+                                   ref["a2_q"][vr], ref["a2_sf"][vr], ref["gate_up"][vr],
+                                   gemm_abs(cfg, h, ref, "w13")[vr], ue, f"{name} a2 (chain)",
+                                   O.act_group(cfg))
     print(f"{name}: {frac:.3%} of a2 codes differ at the end of the GPU chain")
     check_output(to_np(chain["out"]), ref["out"], f"{name} chained output")
     out = run_forward(cfg, dev)
