@@ -297,6 +297,47 @@ def route_layout(ids, E: int, max_tokens: int = 0):
     }
 
 
+def align_block_size(ids, E: int, block_size: int):
+    """The indexed experts' alignment ([HUM] HummingIndexedExperts
+    .prepare_humming_moe_kwargs calls moe_align_block_size; its body is not
+    on the pages, this is the plainest reading): each expert's routed flat
+    slot indices t*k + j in ascending order, the segment padded with the
+    sentinel T*k up to a multiple of block_size, experts in id order; the
+    expert id of every block; the padded total.  Invalid ids are ignored.
+
+    Returns (sorted_ids int32 [P], expert_ids int32 [P / block_size], P)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    flat = ids.ravel()
+    numel = T * k
+    sorted_ids, expert_ids = [], []
+    for e in range(E):
+        slots = np.flatnonzero(flat == e)
+        if slots.size == 0:
+            continue
+        padded = -(-slots.size // block_size) * block_size
+        seg = np.full(padded, numel, dtype=np.int64)
+        seg[:slots.size] = slots
+        sorted_ids.append(seg)
+        expert_ids += [e] * (padded // block_size)
+    sorted_ids = (np.concatenate(sorted_ids) if sorted_ids else np.zeros(0, np.int64))
+    return sorted_ids.astype(np.int32), np.asarray(expert_ids, dtype=np.int32), int(sorted_ids.size)
+
+
+def fused_mul_sum(down_bits, ids, weights, E: int) -> np.ndarray:
+    """out[t] = bf16(sum over slots j ascending with a valid id of
+    weights[t, j] * down[t*k + j]) — down in (token, slot) row order, as the
+    indexed experts' moe_fused_mul_sum reads it.  fp64 accumulation."""
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    down = bf16_to_f64(down_bits).reshape(T, k, -1)
+    acc = np.zeros((T, down.shape[2]), dtype=np.float64)
+    for j in range(k):
+        ok = (ids[:, j] >= 0) & (ids[:, j] < E)
+        acc[ok] += np.asarray(weights, np.float64)[ok, j:j + 1] * down[ok, j]
+    return bf16_round(acc)
+
+
 # ---------------------------------------------------------------------------
 # O5 / O7: block-scaled fp8 GEMM   [HUM, humming_forward on w13 and w2 with
 # the (kFp8Static128BlockSym weight, kFp8Dynamic128Sym activation) scheme]
@@ -554,6 +595,40 @@ def forward(h: dict) -> dict:
         down[rows] = bf16_round(dn)
     out = topk_reduce(down, st["slot_row"], st["weights"])
     return {**st, "gate_up": gate_up, "a2_q": a2_q, "a2_sf": a2_sf,
+            "down": down, "out": out}
+
+
+def forward_indexed(h: dict, block_size: int) -> dict:
+    """The layer in the indexed layout ([HUM] HummingIndexedExperts.apply):
+    align, w13 on the rows of sorted_ids (activation row = id // top_k) into
+    an intermediate in sorted order, the activation, w2 written back to row
+    id (the (token, slot) order), then the fused mul-sum.  Per row the
+    arithmetic is the contiguous layout's, so the output must be identical."""
+    cfg = h["cfg"]
+    assert cfg.layout != "batched"
+    st = stage(h)
+    E, N, K, k = cfg.E, cfg.N, cfg.K, cfg.top_k
+    sorted_ids, expert_ids, P = align_block_size(st["ids"], E, block_size)
+    numel = cfg.T * k
+    bf16_act = cfg.act_quant == "bf16"
+    a2_rows = np.zeros((P, N), dtype=np.uint16 if bf16_act else np.uint8)
+    down = np.zeros((numel, K), dtype=np.uint16)
+    for b, e in enumerate(expert_ids):
+        pos = np.arange(b * block_size, (b + 1) * block_size)
+        ids_b = sorted_ids[pos]
+        live = ids_b < numel
+        if not live.any():
+            continue
+        slots = ids_b[live]
+        tokens = slots // k
+        x_sf = None if st["x_sf"] is None else st["x_sf"][tokens]
+        gu = bf16_round(expert_gemm(cfg, st["x_q"][tokens], x_sf, h["w13"][e], h["w13_sf"][e]))
+        q2, s2 = act_step(cfg, gu)
+        a2_rows[pos[live]] = q2
+        dn = expert_gemm(cfg, q2, s2, h["w2"][e], h["w2_sf"][e])
+        down[slots] = bf16_round(dn)
+    out = fused_mul_sum(down, st["ids"], st["weights"], E)
+    return {"sorted_ids": sorted_ids, "expert_ids": expert_ids, "num_tokens_padded": P,
             "down": down, "out": out}
 
 

@@ -631,6 +631,58 @@ def test_tiny_bf16_layer_tracks_unquantized_ffn():
     assert 1e-4 < rel < 1e-2, rel
 
 
+def test_align_block_size_brute_force():
+    rng = np.random.default_rng(31)
+    T, k, E, bs = 37, 3, 6, 8
+    ids = rng.integers(-1, E + 1, (T, k))          # includes invalid ids
+    sorted_ids, expert_ids, P = O.align_block_size(ids, E, bs)
+    assert P == sorted_ids.size == expert_ids.size * bs and P % bs == 0
+    pos = 0
+    for e in range(E):
+        slots = [t * k + j for t in range(T) for j in range(k) if ids[t, j] == e]
+        if not slots:
+            assert e not in expert_ids
+            continue
+        nb = (len(slots) + bs - 1) // bs
+        assert list(sorted_ids[pos:pos + len(slots)]) == slots
+        assert np.all(sorted_ids[pos + len(slots):pos + nb * bs] == T * k)
+        assert list(expert_ids[pos // bs:pos // bs + nb]) == [e] * nb
+        pos += nb * bs
+    assert pos == P
+
+
+def test_fused_mul_sum_matches_topk_reduce():
+    rng = np.random.default_rng(32)
+    T, k, E, K = 20, 3, 5, 64
+    ids = rng.integers(-1, E, (T, k))
+    w = rng.random((T, k)).astype(np.float32)
+    lay = O.route_layout(ids, E)
+    down_perm = O.bf16_round(rng.standard_normal((int(lay["offsets"][-1]), K)))
+    down_tk = np.zeros((T * k, K), np.uint16)
+    for t in range(T):
+        for j in range(k):
+            if lay["slot_row"][t, j] >= 0:
+                down_tk[t * k + j] = down_perm[lay["slot_row"][t, j]]
+    assert np.array_equal(O.fused_mul_sum(down_tk, ids, w, E),
+                          O.topk_reduce(down_perm, lay["slot_row"], w))
+
+
+@pytest.mark.parametrize("act", ["ue8m0", "fp32", "mxfp8", "bf16"])
+def test_indexed_layout_equals_contiguous(act):
+    """Same per-row arithmetic, different row placement: identical bits."""
+    wq = "mxfp8" if act == "mxfp8" else "fp8_block128"
+    cfg = moe_synth.custom(T=40, E=5, top_k=3, K=256, N=256, seed=33, pad_frac=0.1,
+                           act_quant=act, weight_quant=wq)
+    h = O.host_inputs(moe_synth.make_inputs(cfg))
+    a = O.forward(h)
+    for bs in (16, 64):
+        b = O.forward_indexed(h, bs)
+        assert np.array_equal(a["out"], b["out"])
+        rows = a["slot_row"].ravel()
+        ok = rows >= 0
+        assert np.array_equal(b["down"][ok], a["down"][rows[ok]])
+
+
 def test_layouts_and_padding_agree():
     base = dict(T=40, E=3, top_k=2, K=256, N=256, seed=9)
     hc = O.host_inputs(moe_synth.make_inputs(moe_synth.custom(**base)))
