@@ -4,7 +4,8 @@
 
 One step = one moe_forward over one batch (stage + routing, the w13 GEMM
 with SiLU(gate)*up and the fp8 re-quantization fused into its epilogue, the
-w2 GEMM, top-k reduce), inputs resident in HBM.  Prints one JSON line: layer
+w2 GEMM, top-k reduce; for the indexed layout the block map, the gather /
+scatter GEMMs and the fused mul-sum), inputs resident in HBM.  Prints one JSON line: layer
 tokens/s, grouped-GEMM TFLOP/s against the fp8 dense MFMA peak, per-kernel
 times, the roofline of the dominant kernel (the fused w13 GEMM) and the CPU
 oracle timed on a bounded sample.  Diagnostics go to stderr.
@@ -94,6 +95,8 @@ def algorithmic(cfg, counts, T_valid):
     a["w2_bytes"] = (touched * (K * N * w_elem + w2_sf) + M * (N * ab + GN * sfb) + M * K * 2)
     a["w2_flops"] = 2.0 * M * N * K
     a["reduce"] = M * K * 2 + cfg.T * K * 2 + cfg.T * k * 8
+    # indexed layout: slot rows and ids in, one sorted id per routed slot out
+    a["align"] = cfg.T * k * (4 + 8) + M * 4
     return a
 
 
@@ -132,6 +135,51 @@ def cpu_baseline(cfg, inp, st_dev, budget_s):
 CALIB_BYTES = 1 << 30
 
 
+def layer_kernels(p, cfg, inp, out):
+    """Buffers and one callable per step of the layer through the separate
+    entry points, in moe_forward's launch configuration: (bufs, calls) with
+    calls = [(name, fn)] in launch order.  The indexed layout runs the block
+    map (moe_align_block_size), the gather / scatter GEMMs and the fused
+    mul-sum."""
+    s = moe.sizes(p)
+    bufs = moe.alloc_stage_outputs(p)
+    a2_q, a2_sf = moe.alloc_act_outputs(p)
+    down = torch.empty((s["expert_rows"], cfg.K), dtype=torch.bfloat16, device="cuda")
+
+    def do_stage():
+        if inp["eplb"] is not None:
+            inp["eplb"]["expert_load"].zero_()
+        moe.stage(p, inp["hidden"], inp["topk_ids"], inp["topk_weights"], bufs,
+                  inp["is_padding"], inp["expert_num_tokens"], inp["eplb"])
+
+    calls = [("stage_and_route", do_stage)]
+    if p.layout == moe.LAYOUT_INDEXED:
+        ix = moe.alloc_indexed(p, s["tile_m"])
+        calls += [
+            ("align_block_size",
+             lambda: moe.align_block_size(p, bufs["topk_idx"], bufs, ix)),
+            ("grouped_gemm_w13_act",
+             lambda: moe.grouped_gemm_w13_act_indexed(p, bufs["x_q"], bufs["x_sf"], ix,
+                                                      inp["w13"], inp["w13_sf"], a2_q, a2_sf)),
+            ("grouped_gemm_w2",
+             lambda: moe.grouped_gemm_w2_indexed(p, a2_q, a2_sf, ix, inp["w2"], inp["w2_sf"],
+                                                 down)),
+            ("topk_reduce",
+             lambda: moe.fused_mul_sum(p, down, bufs["topk_idx"], bufs["topk_w"], out)),
+        ]
+    else:
+        calls += [
+            ("grouped_gemm_w13_act",
+             lambda: moe.grouped_gemm_w13_act(p, bufs["x_q"], bufs["x_sf"], bufs, inp["w13"],
+                                              inp["w13_sf"], a2_q, a2_sf)),
+            ("grouped_gemm_w2",
+             lambda: moe.grouped_gemm_w2(p, a2_q, a2_sf, bufs, inp["w2"], inp["w2_sf"], down)),
+            ("topk_reduce",
+             lambda: moe.topk_reduce(p, down, bufs["slot_row"], bufs["topk_w"], out)),
+        ]
+    return bufs, calls
+
+
 def profile_pass(p, cfg, inp, out):
     """A plain 1 GiB device-to-device copy (so HBM byte counters can be scaled
     by what they read for a known size), then each kernel of the layer once
@@ -142,16 +190,9 @@ def profile_pass(p, cfg, inp, out):
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    s = moe.sizes(p)
-    bufs = moe.alloc_stage_outputs(p)
-    a2_q, a2_sf = moe.alloc_act_outputs(p)
-    down = torch.empty((s["expert_rows"], cfg.K), dtype=torch.bfloat16, device="cuda")
-    moe.stage(p, inp["hidden"], inp["topk_ids"], inp["topk_weights"], bufs, inp["is_padding"],
-              inp["expert_num_tokens"], inp["eplb"])
-    moe.grouped_gemm_w13_act(p, bufs["x_q"], bufs["x_sf"], bufs, inp["w13"], inp["w13_sf"],
-                             a2_q, a2_sf)
-    moe.grouped_gemm_w2(p, a2_q, a2_sf, bufs, inp["w2"], inp["w2_sf"], down)
-    moe.topk_reduce(p, down, bufs["slot_row"], bufs["topk_w"], out)
+    _, calls = layer_kernels(p, cfg, inp, out)
+    for _, fn in calls:
+        fn()
     torch.cuda.synchronize()
     log(f"[bench] profile pass done ({cfg.name})")
 
@@ -215,30 +256,19 @@ def main():
 
     # ---- per-kernel timing through the separate entry points -------------
     s = moe.sizes(p)
-    bufs = moe.alloc_stage_outputs(p)
-    a2_q, a2_sf = moe.alloc_act_outputs(p)
-    down = torch.empty((s["expert_rows"], cfg.K), dtype=torch.bfloat16, device="cuda")
+    bufs, calls = layer_kernels(p, cfg, inp, out)
     flush_buf = torch.empty(1 << 28, dtype=torch.int32, device="cuda")   # 1 GiB > MALL
 
     def flush():
         flush_buf.add_(1)
 
-    def do_stage():
-        if inp["eplb"] is not None:
-            inp["eplb"]["expert_load"].zero_()
-        moe.stage(p, inp["hidden"], inp["topk_ids"], inp["topk_weights"], bufs,
-                  inp["is_padding"], inp["expert_num_tokens"], inp["eplb"])
-
     kt = KernelTimer()
     it = args.kernel_iters
-    t_stage = kt.time(do_stage, it, flush)
-    t_w13 = kt.time(lambda: moe.grouped_gemm_w13_act(p, bufs["x_q"], bufs["x_sf"], bufs,
-                                                     inp["w13"], inp["w13_sf"], a2_q, a2_sf),
-                    it, flush)
-    t_w2 = kt.time(lambda: moe.grouped_gemm_w2(p, a2_q, a2_sf, bufs, inp["w2"], inp["w2_sf"],
-                                               down), it, flush)
-    t_red = kt.time(lambda: moe.topk_reduce(p, down, bufs["slot_row"], bufs["topk_w"], out),
-                    it, flush)
+    # each call is timed after the ones before it have run (their outputs are
+    # its inputs)
+    t = {name: kt.time(fn, it, flush) for name, fn in calls}
+    t_stage, t_w13, t_w2, t_red = (t["stage_and_route"], t["grouped_gemm_w13_act"],
+                                   t["grouped_gemm_w2"], t["topk_reduce"])
     torch.cuda.synchronize()
     counts = bufs["expert_num_tokens"].cpu().numpy()
     T_valid = cfg.T - (int(inp["is_padding"].sum().item()) if inp["is_padding"] is not None
@@ -256,6 +286,9 @@ def main():
                             "TFLOP/s": alg["w2_flops"] / (t_w2[0] * 1e-3) / 1e12},
         "topk_reduce": {"ms": t_red[0], "GB/s": gbs(alg["reduce"], t_red[0])},
     }
+    if "align_block_size" in t:
+        kernels["align_block_size"] = {"ms": t["align_block_size"][0],
+                                       "GB/s": gbs(alg["align"], t["align_block_size"][0])}
     for v in kernels.values():
         v["frac_hbm"] = v["GB/s"] / HBM_PEAK_GBS
     gemm_flops = alg["w13_flops"] + alg["w2_flops"]

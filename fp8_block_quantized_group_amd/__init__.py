@@ -22,7 +22,8 @@ Q_FP8_UE8M0, Q_FP8_F32, Q_BF16, Q_MXFP8 = 0, 1, 2, 3
 W_FP8_BLOCK128, W_MXFP8, W_MXFP4 = 0, 1, 2
 _ACT_QUANT = {"ue8m0": Q_FP8_UE8M0, "fp32": Q_FP8_F32, "bf16": Q_BF16, "mxfp8": Q_MXFP8}
 _WEIGHT_QUANT = {"fp8_block128": W_FP8_BLOCK128, "mxfp8": W_MXFP8, "mxfp4": W_MXFP4}
-LAYOUT_CONTIGUOUS, LAYOUT_BATCHED = 0, 1
+LAYOUT_CONTIGUOUS, LAYOUT_BATCHED, LAYOUT_INDEXED = 0, 1, 2
+_LAYOUT = {"contiguous": LAYOUT_CONTIGUOUS, "batched": LAYOUT_BATCHED, "indexed": LAYOUT_INDEXED}
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
            -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_LAUNCH"}
 
@@ -55,12 +56,15 @@ class _Sizes(ctypes.Structure):
     _fields_ = [("slots", ctypes.c_int64), ("tile_list", ctypes.c_int64),
                 ("stage_rows", ctypes.c_int64), ("expert_rows", ctypes.c_int64),
                 ("x_sf_row", ctypes.c_int64), ("a2_sf_row", ctypes.c_int64),
+                ("padded_rows", ctypes.c_int64), ("blocks", ctypes.c_int64),
                 ("tile_m", ctypes.c_int32)]
 
 
 EXPORTS = ("moe_routing_sizes", "moe_stage_workspace_size", "moe_workspace_size", "moe_stage",
            "moe_grouped_gemm_w13", "moe_grouped_gemm_w13_act", "moe_act_requant",
-           "moe_grouped_gemm_w2", "moe_topk_reduce", "moe_forward", "moe_last_error")
+           "moe_grouped_gemm_w2", "moe_topk_reduce", "moe_align_capacity",
+           "moe_align_block_size", "moe_grouped_gemm_w13_act_indexed",
+           "moe_grouped_gemm_w2_indexed", "moe_fused_mul_sum", "moe_forward", "moe_last_error")
 
 _lib = None
 
@@ -86,6 +90,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_act_requant.argtypes = [P(_Problem), V, P(_Routing), V, V, V]
     lib.moe_grouped_gemm_w2.argtypes = [P(_Problem), V, V, P(_Routing), V, V, V, V]
     lib.moe_topk_reduce.argtypes = [P(_Problem), V, V, V, V, V]
+    I32, I64 = ctypes.c_int32, ctypes.c_int64
+    lib.moe_align_capacity.argtypes = [P(_Problem), I32, P(I64), P(I64)]
+    lib.moe_align_block_size.argtypes = [P(_Problem), V, P(_Routing), I32, V, V, V, V]
+    lib.moe_grouped_gemm_w13_act_indexed.argtypes = [P(_Problem), V, V, V, V, V, I32, V, V, V,
+                                                     V, V]
+    lib.moe_grouped_gemm_w2_indexed.argtypes = [P(_Problem), V, V, V, V, V, I32, V, V, V, V]
+    lib.moe_fused_mul_sum.argtypes = [P(_Problem), V, V, V, V, V]
     lib.moe_forward.argtypes = [P(_Problem), V, V, V, V, V, P(_Eplb), V, V, V, V, V, V, S, V]
     lib.moe_last_error.argtypes = []
     for name in EXPORTS:
@@ -137,8 +148,7 @@ class Problem:
     def from_config(cfg, act_quant: Optional[int] = None) -> "Problem":
         """From a ``moe_synth.MoeConfig``."""
         q = act_quant if act_quant is not None else _ACT_QUANT[cfg.act_quant]
-        return Problem(cfg.T, cfg.K, cfg.N, cfg.E, cfg.top_k,
-                       LAYOUT_BATCHED if cfg.layout == "batched" else LAYOUT_CONTIGUOUS,
+        return Problem(cfg.T, cfg.K, cfg.N, cfg.E, cfg.top_k, _LAYOUT[cfg.layout],
                        cfg.max_tokens, q, _WEIGHT_QUANT[cfg.weight_quant])
 
 
@@ -180,11 +190,12 @@ def scale_dtype(p: Problem):
     return torch.float32 if p.act_quant == Q_FP8_F32 else torch.uint8
 
 
-def alloc_act_outputs(p: Problem, device="cuda"):
+def alloc_act_outputs(p: Problem, device="cuda", rows: Optional[int] = None):
     """(a2_q, a2_sf) for the w2 input: fp8 codes and scales, or bf16 values
-    and None for unquantized activations."""
+    and None for unquantized activations; ``rows`` defaults to the layout's
+    a2 rows (the indexed layout's padded capacity)."""
     s = sizes(p)
-    rows = s["expert_rows"]
+    rows = s["padded_rows"] if rows is None else rows
     if p.act_quant == Q_BF16:
         return torch.empty((rows, p.intermediate), dtype=torch.bfloat16, device=device), None
     return (torch.empty((rows, p.intermediate), dtype=torch.uint8, device=device),
@@ -258,6 +269,52 @@ def grouped_gemm_w2(p: Problem, a2_q, a2_sf, routing: dict, w2, w2_sf, down):
 def topk_reduce(p: Problem, down, slot_row, topk_w, out):
     _check(load_library().moe_topk_reduce(ctypes.byref(p.c()), _ptr(down), _ptr(slot_row),
                                            _ptr(topk_w), _ptr(out), _stream()))
+
+
+def align_capacity(p: Problem, block_size: int):
+    """(sorted_ids length, expert_ids length) for ``block_size``."""
+    n, b = ctypes.c_int64(), ctypes.c_int64()
+    _check(load_library().moe_align_capacity(ctypes.byref(p.c()), block_size, ctypes.byref(n),
+                                             ctypes.byref(b)))
+    return n.value, b.value
+
+
+def alloc_indexed(p: Problem, block_size: int, device="cuda") -> dict:
+    """sorted_ids / expert_ids / num_tokens_padded buffers of the block map."""
+    n, b = align_capacity(p, block_size)
+    return {"sorted_ids": torch.empty(max(n, 1), dtype=torch.int32, device=device),
+            "expert_ids": torch.empty(max(b, 1), dtype=torch.int32, device=device),
+            "num_tokens_padded": torch.empty(1, dtype=torch.int32, device=device),
+            "block_size": block_size}
+
+
+def align_block_size(p: Problem, topk_idx, routing: dict, ix: dict):
+    """moe_align_block_size: fills ix (from alloc_indexed) from moe_stage's
+    topk_idx and routing."""
+    r = _routing(routing)
+    _check(load_library().moe_align_block_size(
+        ctypes.byref(p.c()), _ptr(topk_idx), ctypes.byref(r), ix["block_size"],
+        _ptr(ix["sorted_ids"]), _ptr(ix["expert_ids"]), _ptr(ix["num_tokens_padded"]),
+        _stream()))
+
+
+def grouped_gemm_w13_act_indexed(p: Problem, a_q, a_sf, ix: dict, w13, w13_sf, a2_q, a2_sf):
+    _check(load_library().moe_grouped_gemm_w13_act_indexed(
+        ctypes.byref(p.c()), _ptr(a_q), _ptr(a_sf), _ptr(ix["sorted_ids"]),
+        _ptr(ix["expert_ids"]), _ptr(ix["num_tokens_padded"]), ix["block_size"], _ptr(w13),
+        _ptr(w13_sf), _ptr(a2_q), _ptr(a2_sf), _stream()))
+
+
+def grouped_gemm_w2_indexed(p: Problem, a2_q, a2_sf, ix: dict, w2, w2_sf, down):
+    _check(load_library().moe_grouped_gemm_w2_indexed(
+        ctypes.byref(p.c()), _ptr(a2_q), _ptr(a2_sf), _ptr(ix["sorted_ids"]),
+        _ptr(ix["expert_ids"]), _ptr(ix["num_tokens_padded"]), ix["block_size"], _ptr(w2),
+        _ptr(w2_sf), _ptr(down), _stream()))
+
+
+def fused_mul_sum(p: Problem, down, topk_idx, topk_w, out):
+    _check(load_library().moe_fused_mul_sum(ctypes.byref(p.c()), _ptr(down), _ptr(topk_idx),
+                                             _ptr(topk_w), _ptr(out), _stream()))
 
 
 def forward(p: Problem, hidden, topk_ids, topk_weights, w13, w13_sf, w2, w2_sf, out, ws,

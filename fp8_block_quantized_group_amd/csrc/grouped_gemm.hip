@@ -264,13 +264,21 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // expert (heaviest first) and, inside an expert, n-tile-major: the
   // blocks that run together on one XCD share weight tiles (the expert's
   // m-tiles) and activation tiles (neighbouring n-tiles) in its L2.
+  // Indexed layout: tile b is block b of sorted_ids (n-tile-minor, so an
+  // XCD's range covers whole blocks, each expert's blocks adjacent).
+  const bool indexed = p.sorted_ids != nullptr;
   const int NT = p.Nout / S::BN;
-  const int64_t work = (int64_t)p.tile_list[0] * NT;
+  const int64_t ntiles =
+      indexed ? (int64_t)min(max(*p.num_padded, 0) / S::BM, p.max_blocks) : (int64_t)p.tile_list[0];
+  const int64_t work = ntiles * NT;
   const int64_t per_xcd = (work + 7) / 8;
   const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
   if (blockIdx.x / 8 >= per_xcd || wl >= work) return;
   int tile, nt;
-  {
+  if (indexed) {
+    tile = __builtin_amdgcn_readfirstlane((int)(wl / NT));
+    nt = __builtin_amdgcn_readfirstlane((int)(wl % NT));
+  } else {
     // group g with groups[g] <= wl / NT < groups[g+1] (binary search in LDS)
     int* groups = reinterpret_cast<int*>(smem);
     for (int i = threadIdx.x; i <= p.num_experts; i += S::THREADS) groups[i] = p.tile_groups[i];
@@ -287,15 +295,28 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     tile = __builtin_amdgcn_readfirstlane(first + r % mtiles);
     __syncthreads();
   }
-  const int e = p.tile_list[1 + 2 * tile];
-  const int m0 = p.tile_list[2 + 2 * tile];
+  int e, m0, rows_here;
+  int64_t base;
+  if (indexed) {
+    // the block's routed entries (ids below numel) lead, padding follows
+    e = __builtin_amdgcn_readfirstlane(p.expert_ids[tile]);
+    m0 = 0;
+    base = (int64_t)tile * S::BM;
+    const bool valid =
+        threadIdx.x < S::BM && (uint32_t)p.sorted_ids[base + threadIdx.x] < (uint32_t)p.numel;
+    rows_here = __syncthreads_count(valid);
+    if ((uint32_t)e >= (uint32_t)p.num_experts) return;
+  } else {
+    e = p.tile_list[1 + 2 * tile];
+    m0 = p.tile_list[2 + 2 * tile];
+    int cnt = p.counts[e];
+    if (p.offsets == nullptr) cnt = min(cnt, p.max_tokens);
+    rows_here = min(S::BM, cnt - m0);
+    base = p.offsets != nullptr ? (int64_t)p.offsets[e] : (int64_t)e * p.max_tokens;
+  }
   const int n0 = nt * S::BN;          // first output column (plain GEMM)
   const int Nh = p.Nout / 2;            // ACT: columns of h
   const int j0 = nt * (S::BN / 2);      // ACT: first column of h
-  int cnt = p.counts[e];
-  if (p.offsets == nullptr) cnt = min(cnt, p.max_tokens);
-  const int rows_here = min(S::BM, cnt - m0);
-  const int64_t base = p.offsets != nullptr ? (int64_t)p.offsets[e] : (int64_t)e * p.max_tokens;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -304,8 +325,11 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int wm = wave / S::WN;
   const int G = p.Kd / kGroup;
 
+  // activation row of tile row m (an id that is padding gathers row T,
+  // past the buffer's end: the buffer loads return zeros there)
   auto a_row_of = [&](int m) -> int64_t {
     const int64_t r = base + m0 + m;
+    if (p.gather_sorted) return (int64_t)((uint32_t)p.sorted_ids[r] / (uint32_t)p.top_k);
     return p.row_src != nullptr ? (int64_t)p.row_src[r] : r;
   };
 
@@ -719,7 +743,13 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     for (int j = 0; j < S::TM; ++j) {
       const int ml = ml0 + kSubStride * j;
       if (ml >= rows_here) continue;
-      uint16_t* dst = p.out + (base + m0 + ml) * (int64_t)p.Nout + n_first;
+      int64_t row = base + m0 + ml;
+      if (p.scatter_sorted) {
+        const uint32_t id = (uint32_t)p.sorted_ids[row];
+        if (id >= (uint32_t)p.numel) continue;
+        row = id;
+      }
+      uint16_t* dst = p.out + row * (int64_t)p.Nout + n_first;
       uint32_t packed[2 * S::TN];
 #pragma unroll
       for (int i = 0; i < S::TN; ++i) {

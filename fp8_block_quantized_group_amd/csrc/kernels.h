@@ -54,6 +54,19 @@ struct GemmArgs {
   const int32_t* offsets;    // [E+1] contiguous row base, nullptr for batched slabs
   const int32_t* row_src;    // A row gather (w13 on the contiguous layout) or nullptr
   int max_tokens;            // batched slab rows
+  // indexed layout (sorted_ids != nullptr): tile b is the block of BM rows
+  // [b*BM, (b+1)*BM) of sorted_ids, of expert expert_ids[b]; entries not
+  // below numel are padding and come after the block's routed entries.
+  // tile_list / counts / offsets / row_src unused; the ACT output rows are
+  // the sorted positions.
+  const int32_t* sorted_ids;
+  const int32_t* expert_ids;
+  const int32_t* num_padded;       // [1] device: the padded total
+  int max_blocks;                  // blocks of sorted_ids (bounds *num_padded)
+  int top_k;
+  int numel;                       // T * top_k
+  int gather_sorted;               // A row = sorted_ids[pos] / top_k (w13); else pos
+  int scatter_sorted;              // output row = sorted_ids[pos] (w2); else pos
   int Kd;                    // reduction length, multiple of 128
   int Nout;                  // output columns, multiple of 128
 };
@@ -83,5 +96,16 @@ hipError_t launch_grouped_gemm(const GemmArgs& args, int tile_m, int max_tiles, 
 
 hipError_t launch_topk_reduce(const void* down, const int32_t* slot_row, const float* w, void* out,
                               int T, int k, int K, hipStream_t stream);
+
+// down rows in (token, slot) order; a slot counts when idx is in [0, E)
+hipError_t launch_fused_mul_sum(const void* down, const int64_t* idx, const float* w, void* out,
+                                int T, int k, int K, int E, hipStream_t stream);
+
+// indexed layout from the contiguous routing: sorted_ids [T*k + E*(block_size-1)
+// rounded down to a block multiple], expert_ids [that / block_size]
+hipError_t launch_align(const int64_t* idx, const int32_t* slot_row, const int32_t* counts,
+                        const int32_t* offsets, int T, int k, int E, int block_size,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_padded,
+                        hipStream_t stream);
 
 }  // namespace moe

@@ -52,6 +52,21 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool batched(const moe_problem_t* p) { return p->layout == MOE_LAYOUT_BATCHED_MASKED; }
+bool indexed(const moe_problem_t* p) { return p->layout == MOE_LAYOUT_INDEXED; }
+
+// Block sizes of the indexed layout: the GEMM tile heights.
+bool valid_block_size(const moe_problem_t* p, int bs) {
+  if (bs == 16 || bs == 32 || bs == 64 || bs == 128) return true;
+  return (bs == 192 || bs == 256) && p->act_quant != MOE_Q_BF16;
+}
+
+// Entries of sorted_ids: every routed expert pads its segment by fewer than
+// bs entries, so T*k + min(E, T*k) * (bs - 1), rounded down to whole blocks.
+int64_t padded_capacity(const moe_problem_t* p, int64_t bs) {
+  const int64_t slots = (int64_t)p->num_tokens * p->top_k;
+  const int64_t cap = slots + std::min<int64_t>(p->num_experts, slots) * (bs - 1);
+  return cap / bs * bs;
+}
 
 // Activation rows per GEMM tile, from the expected rows per expert.  Rows
 // per expert below 16 leave a 16-row MFMA tile mostly empty, and there the
@@ -91,7 +106,8 @@ moe_status_t validate_problem(const moe_problem_t* p) {
   if (p->top_k < 1) return fail(MOE_ERR_INVALID_ARG, "top_k must be >= 1, got %d", p->top_k);
   if ((int64_t)p->num_tokens * p->top_k >= (int64_t)1 << 31)
     return fail(MOE_ERR_UNSUPPORTED, "num_tokens * top_k must be < 2^31");
-  if (p->layout != MOE_LAYOUT_CONTIGUOUS && p->layout != MOE_LAYOUT_BATCHED_MASKED)
+  if (p->layout != MOE_LAYOUT_CONTIGUOUS && p->layout != MOE_LAYOUT_BATCHED_MASKED &&
+      p->layout != MOE_LAYOUT_INDEXED)
     return fail(MOE_ERR_INVALID_ARG, "unknown layout %d", p->layout);
   if (batched(p) && p->max_tokens_per_expert < 1)
     return fail(MOE_ERR_INVALID_ARG, "batched layout needs max_tokens_per_expert >= 1");
@@ -104,9 +120,11 @@ moe_status_t validate_problem(const moe_problem_t* p) {
     const int64_t rows = batched(p) ? (int64_t)p->num_experts * p->max_tokens_per_expert
                                     : (int64_t)p->num_tokens * p->top_k;
     const int64_t in_rows = batched(p) ? rows : p->num_tokens;
+    // the indexed layout's w2 input has padded rows (blocks of up to 256)
+    const int64_t a2_rows = indexed(p) ? padded_capacity(p, 256) : rows;
     const int64_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
     if (in_rows * p->hidden * elem >= ((int64_t)7 << 29) ||
-        rows * p->intermediate * elem >= ((int64_t)7 << 29))
+        a2_rows * p->intermediate * elem >= ((int64_t)7 << 29))
       return fail(MOE_ERR_UNSUPPORTED, "activation buffers are limited to 3.5 GiB");
   }
   if (p->act_quant < MOE_Q_FP8_UE8M0 || p->act_quant > MOE_Q_MXFP8)
@@ -150,6 +168,8 @@ Plan make_plan(const moe_problem_t* p) {
     pl.s.expert_rows = T * k;
     pl.max_tiles = (T * k + bm - 1) / bm + E;
   }
+  pl.s.padded_rows = indexed(p) ? padded_capacity(p, bm) : pl.s.expert_rows;
+  pl.s.blocks = indexed(p) ? pl.s.padded_rows / bm : 0;
   pl.s.tile_list = 1 + 2 * pl.max_tiles + (E + 1);
   const bool mx = p->act_quant == MOE_Q_MXFP8;
   const bool bf = p->act_quant == MOE_Q_BF16;
@@ -161,8 +181,8 @@ Plan make_plan(const moe_problem_t* p) {
   pl.x_q_bytes = (size_t)pl.s.stage_rows * K * elem;
   const size_t sfb = p->act_quant == MOE_Q_FP8_F32 ? 4 : 1;
   pl.x_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.stage_rows * pl.s.x_sf_row * sfb;
-  pl.a2_q_bytes = (size_t)pl.s.expert_rows * N * elem;
-  pl.a2_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.expert_rows * pl.s.a2_sf_row * sfb;
+  pl.a2_q_bytes = (size_t)pl.s.padded_rows * N * elem;
+  pl.a2_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.padded_rows * pl.s.a2_sf_row * sfb;
   pl.down_bytes = (size_t)pl.s.expert_rows * K * 2;
   return pl;
 }
@@ -171,6 +191,7 @@ Plan make_plan(const moe_problem_t* p) {
 struct Workspace {
   uint8_t* x_q; uint8_t* x_sf; uint8_t* a2_q; uint8_t* a2_sf; uint8_t* down;
   int64_t* idx; float* w; moe_routing_t routing; int32_t* stage_ws;
+  int32_t* sorted_ids; int32_t* expert_ids; int32_t* num_padded;   // indexed layout
   size_t total;
 };
 
@@ -195,6 +216,9 @@ Workspace carve(const Plan& pl, const moe_problem_t* p, uint8_t* base) {
   w.routing.slot_row = (int32_t*)take(std::max<size_t>(slots, 1) * 4);
   w.routing.tile_list = (int32_t*)take((size_t)pl.s.tile_list * 4);
   w.stage_ws = (int32_t*)take(pl.stage_ws_bytes);
+  w.sorted_ids = (int32_t*)take((size_t)pl.s.padded_rows * 4);
+  w.expert_ids = (int32_t*)take((size_t)pl.s.blocks * 4);
+  w.num_padded = (int32_t*)take(indexed(p) ? 4 : 0);
   w.total = off;
   return w;
 }
@@ -287,37 +311,66 @@ moe_status_t run_stage(const moe_problem_t* p, const Plan& pl, const void* hidde
   return launch_status(err, "route");
 }
 
-// w13 with act: out unused, the activation goes to act_q / act_sf.
+// The indexed layout's block map (moe_align_block_size outputs).
+struct Indexed {
+  const int32_t* sorted_ids;
+  const int32_t* expert_ids;
+  const int32_t* num_padded;
+  int block_size;
+};
+
+// w13 with act: out unused, the activation goes to act_q / act_sf.  ix: the
+// indexed layout (r unused then): w13 gathers rows sorted_ids / top_k and
+// writes sorted positions, w2 reads sorted positions and writes rows
+// sorted_ids.
 moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const void* a_q,
                       const void* a_sf, const moe_routing_t* r, const void* w, const void* w_sf,
                       void* out, hipStream_t stream, bool act = false, void* act_q = nullptr,
-                      void* act_sf = nullptr) {
+                      void* act_sf = nullptr, const Indexed* ix = nullptr) {
   moe::GemmArgs g{};
   const size_t sfb = p->act_quant == MOE_Q_FP8_F32 ? 4 : 1;
+  const size_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
+  const int64_t cap = ix != nullptr ? padded_capacity(p, ix->block_size) : 0;
   g.a = (const uint8_t*)a_q;
-  g.a_bytes = (uint32_t)(w13 ? pl.x_q_bytes : pl.a2_q_bytes);
+  g.a_bytes = (uint32_t)(w13 ? pl.x_q_bytes
+                         : ix != nullptr ? (size_t)cap * p->intermediate * elem
+                                         : pl.a2_q_bytes);
   g.a_sf = a_sf;
   g.a_sf_stride = (int)(w13 ? pl.s.x_sf_row : pl.s.a2_sf_row);
-  g.a_sf_bytes = (uint32_t)((w13 ? pl.s.stage_rows : pl.s.expert_rows) * g.a_sf_stride * sfb);
+  g.a_sf_bytes = (uint32_t)((w13 ? pl.s.stage_rows : ix != nullptr ? cap : pl.s.expert_rows) *
+                            g.a_sf_stride * sfb);
   g.w = (const uint8_t*)w;
   g.w_sf = w_sf;
   g.out = (uint16_t*)out;
   g.act_q = (uint8_t*)act_q;
   g.act_sf = (uint8_t*)act_sf;
   g.act_sf_row = (int)pl.s.a2_sf_row;
-  g.tile_list = r->tile_list;
-  g.tile_groups = r->tile_list + 1 + 2 * pl.max_tiles;
   g.num_experts = p->num_experts;
-  g.counts = r->expert_num_tokens;
-  g.offsets = batched(p) ? nullptr : r->expert_offsets;
-  g.row_src = (w13 && !batched(p)) ? r->row_src : nullptr;
-  g.max_tokens = p->max_tokens_per_expert;
+  int tile_m = pl.s.tile_m, max_tiles = (int)pl.max_tiles;
+  if (ix != nullptr) {
+    g.sorted_ids = ix->sorted_ids;
+    g.expert_ids = ix->expert_ids;
+    g.num_padded = ix->num_padded;
+    g.max_blocks = (int)(cap / ix->block_size);
+    g.top_k = p->top_k;
+    g.numel = p->num_tokens * p->top_k;
+    g.gather_sorted = w13 ? 1 : 0;
+    g.scatter_sorted = w13 ? 0 : 1;
+    tile_m = ix->block_size;
+    max_tiles = g.max_blocks;
+  } else {
+    g.tile_list = r->tile_list;
+    g.tile_groups = r->tile_list + 1 + 2 * pl.max_tiles;
+    g.counts = r->expert_num_tokens;
+    g.offsets = batched(p) ? nullptr : r->expert_offsets;
+    g.row_src = (w13 && !batched(p)) ? r->row_src : nullptr;
+    g.max_tokens = p->max_tokens_per_expert;
+  }
   g.Kd = w13 ? p->hidden : p->intermediate;
   g.Nout = w13 ? 2 * p->intermediate : p->hidden;
   const int scheme =
       p->weight_quant == MOE_W_MXFP4 ? moe::kSchemeMxfp8W4 : p->act_quant;
-  const hipError_t err =
-      moe::launch_grouped_gemm(g, pl.s.tile_m, (int)pl.max_tiles, scheme, act, stream);
+  const hipError_t err = moe::launch_grouped_gemm(g, tile_m, max_tiles, scheme, act, stream);
   return launch_status(err, act ? "grouped_gemm_w13_act" : w13 ? "grouped_gemm_w13" : "grouped_gemm_w2");
 }
 
@@ -336,6 +389,37 @@ moe_status_t run_reduce(const moe_problem_t* p, const void* down, const int32_t*
   const hipError_t err = moe::launch_topk_reduce(down, slot_row, w, out, p->num_tokens, p->top_k,
                                                  p->hidden, stream);
   return launch_status(err, "topk_reduce");
+}
+
+moe_status_t run_align(const moe_problem_t* p, const int64_t* idx, const moe_routing_t* r,
+                       const Indexed& ix, hipStream_t stream) {
+  const hipError_t err = moe::launch_align(
+      idx, r->slot_row, r->expert_num_tokens, r->expert_offsets, p->num_tokens, p->top_k,
+      p->num_experts, ix.block_size, const_cast<int32_t*>(ix.sorted_ids),
+      const_cast<int32_t*>(ix.expert_ids), const_cast<int32_t*>(ix.num_padded), stream);
+  return launch_status(err, "align_block_size");
+}
+
+moe_status_t run_mul_sum(const moe_problem_t* p, const void* down, const int64_t* idx,
+                         const float* w, void* out, hipStream_t stream) {
+  const hipError_t err = moe::launch_fused_mul_sum(down, idx, w, out, p->num_tokens, p->top_k,
+                                                   p->hidden, p->num_experts, stream);
+  return launch_status(err, "fused_mul_sum");
+}
+
+moe_status_t check_indexed(const moe_problem_t* p, const int32_t* sorted_ids,
+                           const int32_t* expert_ids, const int32_t* num_padded, int bs) {
+  if (batched(p))
+    return fail(MOE_ERR_UNSUPPORTED, "the indexed layout needs the contiguous routing");
+  if (!valid_block_size(p, bs))
+    return fail(MOE_ERR_UNSUPPORTED, "block_size %d is not a GEMM tile height", bs);
+  const int64_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
+  if (padded_capacity(p, bs) * p->intermediate * elem >= ((int64_t)7 << 29))
+    return fail(MOE_ERR_UNSUPPORTED, "activation buffers are limited to 3.5 GiB");
+  CHECK(check_ptr(sorted_ids, "sorted_ids", 4));
+  CHECK(check_ptr(expert_ids, "expert_ids", 4));
+  CHECK(check_ptr(num_padded, "num_tokens_padded", 4));
+  return MOE_OK;
 }
 
 }  // namespace
@@ -464,6 +548,79 @@ moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int
   return run_reduce(p, down, slot_row, topk_w, out, (hipStream_t)stream);
 }
 
+moe_status_t moe_align_capacity(const moe_problem_t* p, int32_t block_size,
+                                int64_t* sorted_ids_len, int64_t* blocks) {
+  CHECK(validate_problem(p));
+  if (!valid_block_size(p, block_size))
+    return fail(MOE_ERR_UNSUPPORTED, "block_size %d is not a GEMM tile height", block_size);
+  if (sorted_ids_len == nullptr || blocks == nullptr)
+    return fail(MOE_ERR_INVALID_ARG, "output pointer is NULL");
+  *sorted_ids_len = padded_capacity(p, block_size);
+  *blocks = *sorted_ids_len / block_size;
+  return ok();
+}
+
+moe_status_t moe_align_block_size(const moe_problem_t* p, const int64_t* topk_idx,
+                                  const moe_routing_t* routing, int32_t block_size,
+                                  int32_t* sorted_ids, int32_t* expert_ids,
+                                  int32_t* num_tokens_padded, void* stream) {
+  CHECK(validate_problem(p));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_indexed(p, sorted_ids, expert_ids, num_tokens_padded, block_size));
+  CHECK(check_ptr(topk_idx, "topk_idx", 8));
+  CHECK(check_routing(routing));
+  const Indexed ix{sorted_ids, expert_ids, num_tokens_padded, block_size};
+  return run_align(p, topk_idx, routing, ix, (hipStream_t)stream);
+}
+
+moe_status_t moe_grouped_gemm_w13_act_indexed(
+    const moe_problem_t* p, const void* a_q, const void* a_sf, const int32_t* sorted_ids,
+    const int32_t* expert_ids, const int32_t* num_tokens_padded, int32_t block_size,
+    const void* w13, const void* w13_sf, void* a2_q, void* a2_sf, void* stream) {
+  CHECK(validate_problem(p));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_indexed(p, sorted_ids, expert_ids, num_tokens_padded, block_size));
+  CHECK(check_ptr(a_q, "a_q", 16));
+  CHECK(check_sf(p, a_sf, "a_sf"));
+  CHECK(check_ptr(w13, "w13", 16));
+  CHECK(check_ptr(w13_sf, "w13_sf", 4));
+  CHECK(check_ptr(a2_q, "a2_q", 16));
+  CHECK(check_sf(p, a2_sf, "a2_sf"));
+  const Plan pl = make_plan(p);
+  const Indexed ix{sorted_ids, expert_ids, num_tokens_padded, block_size};
+  return run_gemm(p, pl, true, a_q, a_sf, nullptr, w13, w13_sf, nullptr, (hipStream_t)stream,
+                  true, a2_q, a2_sf, &ix);
+}
+
+moe_status_t moe_grouped_gemm_w2_indexed(
+    const moe_problem_t* p, const void* a2_q, const void* a2_sf, const int32_t* sorted_ids,
+    const int32_t* expert_ids, const int32_t* num_tokens_padded, int32_t block_size,
+    const void* w2, const void* w2_sf, void* down, void* stream) {
+  CHECK(validate_problem(p));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_indexed(p, sorted_ids, expert_ids, num_tokens_padded, block_size));
+  CHECK(check_ptr(a2_q, "a2_q", 16));
+  CHECK(check_sf(p, a2_sf, "a2_sf"));
+  CHECK(check_ptr(w2, "w2", 16));
+  CHECK(check_ptr(w2_sf, "w2_sf", 4));
+  CHECK(check_ptr(down, "down", 16));
+  const Plan pl = make_plan(p);
+  const Indexed ix{sorted_ids, expert_ids, num_tokens_padded, block_size};
+  return run_gemm(p, pl, false, a2_q, a2_sf, nullptr, w2, w2_sf, down, (hipStream_t)stream,
+                  false, nullptr, nullptr, &ix);
+}
+
+moe_status_t moe_fused_mul_sum(const moe_problem_t* p, const void* down, const int64_t* topk_idx,
+                               const float* topk_w, void* out, void* stream) {
+  CHECK(validate_problem(p));
+  if (p->num_tokens == 0) return ok();
+  CHECK(check_ptr(down, "down", 16));
+  CHECK(check_ptr(topk_idx, "topk_idx", 8));
+  CHECK(check_ptr(topk_w, "topk_w", 4));
+  CHECK(check_ptr(out, "out", 16));
+  return run_mul_sum(p, down, topk_idx, topk_w, out, (hipStream_t)stream);
+}
+
 moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
                          const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
                          const float* topk_weights, const uint8_t* is_padding,
@@ -487,6 +644,16 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
   const hipStream_t s = (hipStream_t)stream;
   CHECK(run_stage(p, pl, hidden, expert_num_tokens_in, topk_ids, topk_weights, is_padding, eplb,
                   w.x_q, w.x_sf, w.idx, w.w, &w.routing, w.stage_ws, s));
+  if (indexed(p)) {
+    const Indexed ix{w.sorted_ids, w.expert_ids, w.num_padded, pl.s.tile_m};
+    CHECK(run_align(p, w.idx, &w.routing, ix, s));
+    CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, nullptr, w13, w13_sf, nullptr, s, true, w.a2_q,
+                   w.a2_sf, &ix));
+    CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, nullptr, w2, w2_sf, w.down, s, false, nullptr,
+                   nullptr, &ix));
+    CHECK(run_mul_sum(p, w.down, w.idx, w.w, out, s));
+    return ok();
+  }
   CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, nullptr, s, true, w.a2_q,
                  w.a2_sf));
   CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s));

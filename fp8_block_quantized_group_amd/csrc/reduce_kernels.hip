@@ -25,17 +25,26 @@ namespace {
 constexpr int kReduceThreads = 128;
 constexpr int kReduceCols = kReduceThreads * 8;
 
+// slot_row == nullptr: down rows are in (token, slot) order (the indexed
+// layout's moe_fused_mul_sum); slot j of token t is row t*k + j when its
+// repacked id idx[t, j] is a valid expert.
 __global__ __launch_bounds__(kReduceThreads) void topk_reduce_kernel(
     const uint16_t* __restrict__ down, const int32_t* __restrict__ slot_row,
-    const float* __restrict__ w, uint16_t* __restrict__ out, int k, int K) {
+    const int64_t* __restrict__ idx, const float* __restrict__ w, uint16_t* __restrict__ out,
+    int k, int K, int E) {
   const int t = blockIdx.y;
   const int c = blockIdx.x * kReduceCols + threadIdx.x * 8;
   if (c >= K) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const int32_t* rows = slot_row + (int64_t)t * k;
   const float* wt = w + (int64_t)t * k;
   for (int j = 0; j < k; ++j) {
-    const int r = rows[j];
+    int r;
+    if (slot_row != nullptr) {
+      r = slot_row[(int64_t)t * k + j];
+    } else {
+      const int64_t id = idx[(int64_t)t * k + j];
+      r = (id >= 0 && id < E) ? t * k + j : -1;
+    }
     if (r < 0) continue;
     const float s = wt[j];
     const uint4 v = *reinterpret_cast<const uint4*>(down + (int64_t)r * K + c);
@@ -63,7 +72,16 @@ hipError_t launch_topk_reduce(const void* down, const int32_t* slot_row, const f
   if (T == 0) return hipSuccess;
   const dim3 grid((K + kReduceCols - 1) / kReduceCols, T);
   topk_reduce_kernel<<<grid, kReduceThreads, 0, stream>>>(
-      (const uint16_t*)down, slot_row, w, (uint16_t*)out, k, K);
+      (const uint16_t*)down, slot_row, nullptr, w, (uint16_t*)out, k, K, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_fused_mul_sum(const void* down, const int64_t* idx, const float* w, void* out,
+                                int T, int k, int K, int E, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((K + kReduceCols - 1) / kReduceCols, T);
+  topk_reduce_kernel<<<grid, kReduceThreads, 0, stream>>>(
+      (const uint16_t*)down, nullptr, idx, w, (uint16_t*)out, k, K, E);
   return hipGetLastError();
 }
 

@@ -189,7 +189,62 @@ __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
   }
 }
 
+// Indexed layout ("...fused_humming_moe", HummingIndexedExperts: the
+// outputs of moe_align_block_size, whose body the pages do not show).
+// Each expert's routed slots, in the contiguous layout's row order, fill a
+// segment of sorted_ids padded with numel to a multiple of the block size;
+// segments follow in expert order and empty experts have none.  Every block
+// scans the padded counts (E <= 1024) into LDS and places its 1024 slots;
+// block 0 also writes the expert of every block, the padding and the total.
+constexpr int kAlignThreads = 1024;
+
+__global__ __launch_bounds__(kAlignThreads) void align_kernel(
+    const int64_t* __restrict__ idx, const int32_t* __restrict__ slot_row,
+    const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets, int total, int E,
+    int bs, int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ num_padded) {
+  __shared__ int32_t scan[kAlignThreads];
+  const int t = threadIdx.x;
+  const int cnt = t < E ? counts[t] : 0;
+  const int pc = (cnt + bs - 1) / bs * bs;
+  scan[t] = pc;
+  __syncthreads();
+  for (int d = 1; d < kAlignThreads; d <<= 1) {   // inclusive Hillis-Steele scan
+    const int v = t >= d ? scan[t - d] : 0;
+    __syncthreads();
+    scan[t] += v;
+    __syncthreads();
+  }
+  if (blockIdx.x == 0) {
+    const int end = scan[t], start = end - pc;
+    if (t < E) {
+      for (int b = start / bs; b < end / bs; ++b) expert_ids[b] = t;
+      for (int q = start + cnt; q < end; ++q) sorted_ids[q] = total;
+    }
+    if (t == kAlignThreads - 1) *num_padded = end;
+  }
+  const int slot = blockIdx.x * kAlignThreads + t;
+  if (slot >= total) return;
+  const int r = slot_row[slot];
+  if (r < 0) return;
+  const int64_t e = idx[slot];
+  if (e < 0 || e >= E) return;
+  sorted_ids[scan[e] - ((counts[e] + bs - 1) / bs * bs) + (r - offsets[e])] = slot;
+}
+
 }  // namespace
+
+hipError_t launch_align(const int64_t* idx, const int32_t* slot_row, const int32_t* counts,
+                        const int32_t* offsets, int T, int k, int E, int block_size,
+                        int32_t* sorted_ids, int32_t* expert_ids, int32_t* num_padded,
+                        hipStream_t stream) {
+  const int total = T * k;
+  const int blocks = total > 0 ? (total + kAlignThreads - 1) / kAlignThreads : 1;
+  align_kernel<<<blocks, kAlignThreads, 0, stream>>>(idx, slot_row, counts, offsets, total, E,
+                                                     block_size, sorted_ids, expert_ids,
+                                                     num_padded);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint8_t* is_padding,
                         int T, int k, int E, const EplbArgs& eplb, int64_t* idx_out,

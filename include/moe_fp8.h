@@ -88,10 +88,13 @@ typedef enum {
   MOE_W_MXFP4 = 2         /* e2m1 (two per byte), E8M0 per row and 32 cols  */
 } moe_weight_t;
 
-/* Expert-row layouts ("Standard" and "BatchedExperts" activation formats). */
+/* Expert-row layouts ("Standard" and "BatchedExperts" activation formats of
+ * HummingGroupedExperts / BatchedHummingGroupedExperts, and the block map of
+ * HummingIndexedExperts). */
 typedef enum {
   MOE_LAYOUT_CONTIGUOUS = 0,     /* rows grouped by expert, offsets [E+1]   */
-  MOE_LAYOUT_BATCHED_MASKED = 1  /* [E, max_tokens_per_expert, K] slabs     */
+  MOE_LAYOUT_BATCHED_MASKED = 1, /* [E, max_tokens_per_expert, K] slabs     */
+  MOE_LAYOUT_INDEXED = 2         /* blocks of sorted slot ids, see below    */
 } moe_layout_t;
 
 /* Problem description (host struct).  T tokens, hidden size K, intermediate
@@ -154,7 +157,11 @@ typedef struct {
   int64_t expert_rows;     /* rows of gate_up / a2 / down                     */
   int64_t x_sf_row;        /* x_sf row length: bytes (UE8M0) / floats (fp32)  */
   int64_t a2_sf_row;       /* a2_sf row length, same units                    */
-  int32_t tile_m;          /* activation rows per GEMM tile                   */
+  int64_t padded_rows;     /* rows of a2 (indexed: sorted_ids capacity; else
+                              expert_rows)                                    */
+  int64_t blocks;          /* indexed: expert_ids capacity; else 0            */
+  int32_t tile_m;          /* activation rows per GEMM tile (indexed: the
+                              block size moe_forward uses)                    */
 } moe_sizes_t;
 
 /* Sizes of every buffer of `p` (host only). */
@@ -229,9 +236,67 @@ moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const
 moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int32_t* slot_row,
                              const float* topk_w, void* out, void* stream);
 
+/* ---- Indexed layout ("...experts.fused_humming_moe",
+ * HummingIndexedExperts.apply / prepare_humming_moe_kwargs).  The routed
+ * (token, slot) pairs are addressed by their flat slot id t * top_k + j.
+ * sorted_ids holds, expert by expert in id order, the slot ids routed to
+ * that expert in ascending order, each expert's segment padded with the
+ * sentinel T * top_k to a multiple of block_size (experts with no slot have
+ * no segment); expert_ids[b] is the expert of block b (entries
+ * [b*block_size, (b+1)*block_size)); *num_tokens_padded is the padded total.
+ * The pages call moe_align_block_size without showing its body; this is the
+ * plain reading (the order inside a segment is the contiguous layout's row
+ * order).  block_size is a GEMM tile height: 16, 32, 64, 128, and for
+ * quantized activations 192 or 256.  These calls need the contiguous routing
+ * (layout CONTIGUOUS or INDEXED; BATCHED_MASKED -> MOE_ERR_UNSUPPORTED). */
+
+/* Capacity of sorted_ids (T*k + min(E, T*k) * (block_size - 1), rounded down
+ * to whole blocks) and of expert_ids (that / block_size) (host only). */
+moe_status_t moe_align_capacity(const moe_problem_t* p, int32_t block_size,
+                                int64_t* sorted_ids_len, int64_t* blocks);
+
+/* Builds the block map from moe_stage's outputs: topk_idx int64 [T, top_k]
+ * and its routing (expert_num_tokens, expert_offsets and slot_row are read).
+ * Outputs (device int32): sorted_ids [capacity], expert_ids [blocks],
+ * num_tokens_padded [1]; entries past the padded total are not written. */
+moe_status_t moe_align_block_size(const moe_problem_t* p, const int64_t* topk_idx,
+                                  const moe_routing_t* routing, int32_t block_size,
+                                  int32_t* sorted_ids, int32_t* expert_ids,
+                                  int32_t* num_tokens_padded, void* stream);
+
+/* Steps 3 + 4 on the block map: for every routed position q (sorted_ids[q]
+ * = s < T*k), a2 row q = the fused w13 + activation of moe_grouped_gemm_w13_act
+ * applied to activation row s / top_k with the weights of expert
+ * expert_ids[q / block_size].  a2_q [capacity, N] (fp8, or bf16 for bf16
+ * activations), a2_sf per the activation scheme with capacity rows; padding
+ * positions are not written.  The routed entries of every block must precede
+ * its padding (as moe_align_block_size writes them); *num_tokens_padded is
+ * clamped to the capacity. */
+moe_status_t moe_grouped_gemm_w13_act_indexed(
+    const moe_problem_t* p, const void* a_q, const void* a_sf, const int32_t* sorted_ids,
+    const int32_t* expert_ids, const int32_t* num_tokens_padded, int32_t block_size,
+    const void* w13, const void* w13_sf, void* a2_q, void* a2_sf, void* stream);
+
+/* Step 5 on the block map: down[s] = the w2 GEMM of a2 row q for every routed
+ * position q with s = sorted_ids[q]; down bf16 [T*top_k, K] in (token, slot)
+ * order; rows of unrouted slots are not written. */
+moe_status_t moe_grouped_gemm_w2_indexed(
+    const moe_problem_t* p, const void* a2_q, const void* a2_sf, const int32_t* sorted_ids,
+    const int32_t* expert_ids, const int32_t* num_tokens_padded, int32_t block_size,
+    const void* w2, const void* w2_sf, void* down, void* stream);
+
+/* Step 6 on the (token, slot) order (moe_fused_mul_sum): out[t] =
+ * bf16(sum over j ascending with topk_idx[t, j] in [0, E) of topk_w[t, j] *
+ * down[t * top_k + j]), accumulated in fp32; tokens with no routed slot get
+ * 0.  out: bf16 [T, K]. */
+moe_status_t moe_fused_mul_sum(const moe_problem_t* p, const void* down, const int64_t* topk_idx,
+                               const float* topk_w, void* out, void* stream);
+
 /* Steps 1-6 on one stream (stage, fused w13 + activation, w2, reduce).
  * Arguments as in moe_stage plus the weights and out bf16 [T, K]; ws: device
- * workspace of moe_workspace_size bytes.  Any supported scheme pair. */
+ * workspace of moe_workspace_size bytes.  Any supported scheme pair.  Layout
+ * INDEXED runs stage, moe_align_block_size with block size tile_m, the two
+ * indexed GEMMs and moe_fused_mul_sum. */
 moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
                          const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
                          const float* topk_weights, const uint8_t* is_padding,

@@ -57,7 +57,7 @@ class MoeConfig:
     K: int
     N: int
     seed: int
-    layout: str = "contiguous"          # "contiguous" | "batched"
+    layout: str = "contiguous"          # "contiguous" | "batched" | "indexed"
     max_tokens: int = 0                 # batched layout: rows per expert slab
     act_quant: str = "ue8m0"            # "ue8m0" | "fp32" (128-groups) | "mxfp8" (32-groups) | "bf16"
     weight_quant: str = "fp8_block128"  # "fp8_block128" | "mxfp8" | "mxfp4"
@@ -111,7 +111,15 @@ BF16_CONFIGS = {
                             seed=5, act_quant="bf16", num_logical=128),
 }
 
-ALL_CONFIGS = {**CONFIGS, **MX_CONFIGS, **BF16_CONFIGS}
+# The DeepSeek-V3-shaped prefill batch (the same inputs: same seed) run
+# through the indexed experts' block map instead of the contiguous rows.
+INDEXED_CONFIGS = {
+    "dsv3_prefill_indexed": MoeConfig("dsv3_prefill_indexed", T=4096, E=256, top_k=8, K=7168,
+                                      N=2048, seed=3, routing="zipf", zipf_s=1.1,
+                                      pad_frac=0.05, layout="indexed"),
+}
+
+ALL_CONFIGS = {**CONFIGS, **MX_CONFIGS, **BF16_CONFIGS, **INDEXED_CONFIGS}
 
 
 def _gen(device, seed: int, stream: str) -> torch.Generator:

@@ -78,7 +78,8 @@ def test_sizes_follow_the_problem(lib):
         G = cfg.K // 128
         assert s["x_sf_row"] == (4 * ((G + 3) // 4) if cfg.act_quant == "ue8m0" else G)
     for name, cfg in moe_synth.MX_CONFIGS.items():
-        s = moe.sizes(moe.Problem.from_config(cfg))
+        p = moe.Problem.from_config(cfg)
+        s = moe.sizes(p)
         assert s["x_sf_row"] == cfg.K // 32 and s["a2_sf_row"] == cfg.N // 32
         assert s["tile_m"] in (16, 32, 64, 128, 192, 256)
         ws = moe.workspace_size(p)
@@ -184,3 +185,72 @@ def test_empty_batch_is_a_noop(lib):
     assert lib.moe_stage(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
                          None, None, None, 0, None) == 0
     assert lib.moe_last_error().decode() == ""
+
+
+def test_indexed_sizes(lib):
+    # the indexed layout: a2 has the padded capacity, down stays T*k rows
+    for name, cfg in moe_synth.INDEXED_CONFIGS.items():
+        p = moe.Problem.from_config(cfg)
+        assert p.layout == moe.LAYOUT_INDEXED
+        s = moe.sizes(p)
+        bm, slots = s["tile_m"], cfg.T * cfg.top_k
+        cap = (slots + min(cfg.E, slots) * (bm - 1)) // bm * bm
+        assert s["padded_rows"] == cap and s["blocks"] == cap // bm
+        assert s["expert_rows"] == slots
+        assert moe.align_capacity(p, bm) == (cap, cap // bm)
+        ws = moe.workspace_size(p)
+        assert ws >= s["stage_rows"] * cfg.K + cap * cfg.N + slots * cfg.K * 2 + cap * 4
+
+
+@pytest.mark.parametrize("T,E,k,bs,seed", [(1, 4, 1, 16, 0), (37, 8, 3, 16, 1),
+                                           (300, 64, 8, 64, 2), (50, 256, 8, 256, 3),
+                                           (5, 1024, 2, 128, 4)])
+def test_align_capacity_bounds_the_padded_total(lib, T, E, k, bs, seed):
+    # the capacity the library reports holds the oracle's padded layout for
+    # any routing, including the worst case (every expert one slot)
+    import numpy as np
+    from oracle import moe_oracle as O
+    rng = np.random.default_rng(seed)
+    p = moe.Problem(T, 256, 512, E, k)
+    cap, blocks = moe.align_capacity(p, bs)
+    ids = np.stack([rng.permutation(E)[:k] if k <= E else rng.integers(0, E, k)
+                    for _ in range(T)])
+    worst = (np.arange(T * k) % E).reshape(T, k)
+    for routing in (ids, worst):
+        sorted_ids, expert_ids, P = O.align_block_size(routing, E, bs)
+        assert P <= cap and len(expert_ids) <= blocks
+
+
+def test_indexed_validation(lib):
+    V = _fake()
+    base = dict(num_tokens=16, hidden=256, intermediate=512, num_experts=4, top_k=2)
+    p = moe.Problem(**base)
+    for bs, status in [(16, 0), (256, 0), (48, -2), (0, -2), (512, -2)]:
+        if status:
+            with pytest.raises(moe.MoeError) as ei:
+                moe.align_capacity(p, bs)
+            assert ei.value.status == status
+        else:
+            moe.align_capacity(p, bs)
+    # bf16 activations: blocks up to 128 rows
+    pb = moe.Problem(**base, act_quant=moe.Q_BF16)
+    moe.align_capacity(pb, 128)
+    with pytest.raises(moe.MoeError):
+        moe.align_capacity(pb, 256)
+    c = p.c()
+    # batched routing has no block map
+    pbat = moe.Problem(**base, layout=moe.LAYOUT_BATCHED, max_tokens_per_expert=8).c()
+    st = lib.moe_align_block_size(ctypes.byref(pbat), V, None, 16, V, V, V, None)
+    assert st == -2
+    # a missing block-map pointer is caught before any launch
+    st = lib.moe_grouped_gemm_w13_act_indexed(ctypes.byref(c), V, V, None, V, V, 16, V, V, V,
+                                              V, None)
+    assert st == -1 and "sorted_ids" in lib.moe_last_error().decode()
+    st = lib.moe_grouped_gemm_w2_indexed(ctypes.byref(c), V, V, V, V, None, 16, V, V, V, None)
+    assert st == -1 and "num_tokens_padded" in lib.moe_last_error().decode()
+    st = lib.moe_grouped_gemm_w2_indexed(ctypes.byref(c), V, V, V, V, V, 24, V, V, V, None)
+    assert st == -2
+    st = lib.moe_fused_mul_sum(ctypes.byref(c), V, _fake((1 << 20) + 4), V, V, None)
+    assert st == -1 and "topk_idx" in lib.moe_last_error().decode()
+    st = lib.moe_align_block_size(ctypes.byref(c), V, None, 16, V, V, V, None)
+    assert st == -1 and "routing" in lib.moe_last_error().decode()
