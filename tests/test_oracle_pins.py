@@ -651,6 +651,30 @@ def test_align_block_size_brute_force():
     assert pos == P
 
 
+@pytest.mark.parametrize("T,k,E,bs,seed", [(1, 1, 1, 16, 0), (50, 4, 64, 16, 1),
+                                           (300, 8, 16, 128, 2), (7, 2, 300, 256, 3)])
+def test_align_block_size_invariants(T, k, E, bs, seed):
+    """Every routed slot appears exactly once, each block holds one expert's
+    slots (ascending, routed entries before the padding), and the padded
+    total is the sum of the per-expert counts rounded up to blocks."""
+    rng = np.random.default_rng(seed)
+    ids = rng.integers(-2, E + 2, (T, k))
+    sorted_ids, expert_ids, P = O.align_block_size(ids, E, bs)
+    flat = ids.ravel()
+    valid = (flat >= 0) & (flat < E)
+    live = sorted_ids[sorted_ids < T * k]
+    assert np.array_equal(np.sort(live), np.flatnonzero(valid))
+    counts = np.bincount(flat[valid], minlength=E)
+    assert P == int(sum(-(-c // bs) * bs for c in counts))
+    for b, e in enumerate(expert_ids):
+        blk = sorted_ids[b * bs:(b + 1) * bs]
+        n = int((blk < T * k).sum())
+        assert n > 0                              # padding never fills a whole block
+        assert np.all(blk[:n] < T * k) and np.all(blk[n:] == T * k)
+        assert np.all(flat[blk[:n]] == e) and np.all(np.diff(blk[:n]) > 0)
+    assert np.all(np.diff(expert_ids) >= 0)
+
+
 def test_fused_mul_sum_matches_topk_reduce():
     rng = np.random.default_rng(32)
     T, k, E, K = 20, 3, 5, 64
