@@ -66,6 +66,18 @@ class MoeConfig:
     pad_frac: float = 0.0
     num_logical: int = 0                # >0: EPLB with E - num_logical replicas
     weight_std: float = 0.02
+    # "silu" | "gelu" | "gelu_tanh" (gated: w13 has 2N rows, gate then up) |
+    # "silu_no_mul" | "gelu_no_mul" | "gelu_tanh_no_mul" | "relu2_no_mul"
+    # (w13 has N rows, the activation applies to all of them)
+    activation: str = "silu"
+
+    @property
+    def gated(self) -> bool:
+        return not self.activation.endswith("_no_mul")
+
+    @property
+    def w13_rows(self) -> int:
+        return 2 * self.N if self.gated else self.N
 
     @property
     def E_log(self) -> int:
@@ -170,12 +182,12 @@ def _quantize_weight_mx(w: torch.Tensor, fp4: bool):
 
 
 def _draw_weights(cfg: MoeConfig, device, which: str):
-    """w13 [E_log, 2N, K] or w2 [E_log, K, N] codes + scales, one expert at a
+    """w13 [E_log, 2N (N without gating), K] or w2 [E_log, K, N] codes + scales, one expert at a
     time so the fp32 draw never exceeds one expert.  fp8_block128: e4m3 codes
     and fp32 scales per 128x128 block; mxfp8 / mxfp4: MX codes and E8M0
     scales per row and 32 columns."""
     g = _gen(device, cfg.seed, which)
-    rows, cols = (2 * cfg.N, cfg.K) if which == "w13" else (cfg.K, cfg.N)
+    rows, cols = (cfg.w13_rows, cfg.K) if which == "w13" else (cfg.K, cfg.N)
     if cfg.weight_quant == "fp8_block128":
         q = torch.empty((cfg.E_log, rows, cols), dtype=torch.uint8, device=device)
         s = torch.empty((cfg.E_log, rows // 128, cols // 128), dtype=torch.float32,

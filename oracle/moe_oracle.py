@@ -15,6 +15,9 @@ Sources (all from the vLLM API documentation pages on the subject):
            ``HummingGroupedExperts.apply``, ``HummingExpertsBase``
            (``process_input``, ``get_buffer_metas``,
            ``_supports_quant_scheme``).
+  [HUM2]   the same module on the latest-docs page: the activation list of
+           ``_supports_activation`` and the activation buffer widths of
+           ``get_buffer_metas``.
 
 Schemes: unquantized bf16 activations with block fp8 weights (the
 (kFp8Static128BlockSym, None) pair; staging copies the hidden states, the w2
@@ -47,12 +50,18 @@ reason, in the design notes):
   * expert replica choice under EPLB is ``token mod replica_count`` (parity
     unpinned: the pages do not show ``eplb_map_and_record``'s body; only the
     invariants it must satisfy are tested);
+  * activations other than SiLU (named on the pages, formulas not shown)
+    take their standard definitions; gated ones read w13's 2N columns as
+    gate then up, the _no_mul ones act on all N columns of a w13 with N rows
+    (the w2 input width is N in both cases);
   * MX: the w2 input (SiLU(gate)*up) is quantized like the staged hidden
     states, 32-column groups with E8M0 scales (Humming's own input quantizer
     is not shown); E8M0 byte e means 2^(e-127); e2m1 codes are packed two per
     byte, even column in the low nibble.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -439,34 +448,68 @@ def expert_gemm(cfg, a_codes, a_stored, w, w_sf) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
-# O6: SiLU(gate) * up, re-quantized  [HUM, process_input('w2', activation=...)]
+# O6: activation, re-quantized  [HUM, process_input('w2', activation=...);
+# HUM2, HummingExpertsBase._supports_activation and get_buffer_metas: the
+# activation list, and the w2 input width N for gated activations, the whole
+# w13 output for the _NO_MUL ones]
 # ---------------------------------------------------------------------------
 
-def silu_mul_f32(gate_up_bits, N: int) -> np.ndarray:
-    """bf16 [rows, 2N] -> fp32 h = silu(g) * u with g = columns [0, N) and
-    u = columns [N, 2N); evaluated in fp64, rounded once to fp32."""
+def _erf(x: np.ndarray) -> np.ndarray:
+    return np.vectorize(math.erf, otypes=[np.float64])(x)
+
+
+# The activation functions by name.  The pages list them (the activation
+# enum members the experts accept) without their formulas; these are the
+# standard definitions: SiLU x*sigmoid(x); GELU x*Phi(x) with the exact
+# normal CDF; GELU_TANH its tanh approximation with sqrt(2/pi) and 0.044715;
+# RELU2 max(x, 0)^2.
+ACT_FUNCS = {
+    "silu": lambda x: x / (1.0 + np.exp(-x)),
+    "gelu": lambda x: 0.5 * x * (1.0 + _erf(x / math.sqrt(2.0))),
+    "gelu_tanh": lambda x: 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi)
+                                                    * (x + 0.044715 * x ** 3))),
+    "relu2": lambda x: np.maximum(x, 0.0) ** 2,
+}
+GATED = ("silu", "gelu", "gelu_tanh")
+NO_MUL = ("silu_no_mul", "gelu_no_mul", "gelu_tanh_no_mul", "relu2_no_mul")
+
+
+def act_f32(gate_up_bits, N: int, activation: str = "silu") -> np.ndarray:
+    """The w2 input before quantization, in fp64 rounded once to fp32.
+    Gated: bf16 [rows, 2N] -> h = f(g) * u with g = columns [0, N) and
+    u = columns [N, 2N).  _no_mul: bf16 [rows, N] -> h = f(x)."""
     gu = bf16_to_f64(gate_up_bits)
-    g, u = gu[:, :N], gu[:, N:]
-    h = g / (1.0 + np.exp(-g)) * u
+    if activation in GATED:
+        g, u = gu[:, :N], gu[:, N:2 * N]
+        h = ACT_FUNCS[activation](g) * u
+    else:
+        assert activation in NO_MUL, activation
+        h = ACT_FUNCS[activation[:-len("_no_mul")]](gu[:, :N])
     return h.astype(np.float32)
 
 
-def act_requant(gate_up_bits, N: int, ue8m0: bool, group: int = GROUP):
-    return quantize_groups(silu_mul_f32(gate_up_bits, N), ue8m0, group)
+def silu_mul_f32(gate_up_bits, N: int) -> np.ndarray:
+    return act_f32(gate_up_bits, N, "silu")
 
 
-def act_bf16(gate_up_bits, N: int):
-    """Unquantized w2 input: h = silu(g) * u (fp32, as above) rounded once to
-    bf16 (the c_dtype of the activation buffer)."""
-    return bf16_round(silu_mul_f32(gate_up_bits, N).astype(np.float64))
+def act_requant(gate_up_bits, N: int, ue8m0: bool, group: int = GROUP,
+                activation: str = "silu"):
+    return quantize_groups(act_f32(gate_up_bits, N, activation), ue8m0, group)
+
+
+def act_bf16(gate_up_bits, N: int, activation: str = "silu"):
+    """Unquantized w2 input: h (fp32, as above) rounded once to bf16 (the
+    c_dtype of the activation buffer)."""
+    return bf16_round(act_f32(gate_up_bits, N, activation).astype(np.float64))
 
 
 def act_step(cfg, gate_up_bits):
     """The w2 input in the workload's scheme: (codes or bf16 bits, scales or
     None)."""
+    act = getattr(cfg, "activation", "silu")
     if cfg.act_quant == "bf16":
-        return act_bf16(gate_up_bits, cfg.N), None
-    return act_requant(gate_up_bits, cfg.N, act_e8m0(cfg), act_group(cfg))
+        return act_bf16(gate_up_bits, cfg.N, act), None
+    return act_requant(gate_up_bits, cfg.N, act_e8m0(cfg), act_group(cfg), act)
 
 
 # ---------------------------------------------------------------------------
@@ -568,7 +611,7 @@ def forward(h: dict) -> dict:
     else:
         rows_total = int(st["offsets"][-1])
     bf16_act = cfg.act_quant == "bf16"
-    gate_up = np.zeros((rows_total, 2 * N), dtype=np.uint16)
+    gate_up = np.zeros((rows_total, cfg.w13_rows), dtype=np.uint16)
     a2_q = np.zeros((rows_total, N), dtype=np.uint16 if bf16_act else np.uint8)
     a2_sf = None if bf16_act else np.zeros((rows_total, N // grp),
                                            dtype=np.uint8 if ue8m0 else np.float32)

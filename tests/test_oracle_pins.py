@@ -586,10 +586,73 @@ def _dense_ffn(h, st):
                 fp4 = cfg.weight_quant == "mxfp4"
                 W13 = _mx_dense(h["w13"][e], h["w13_sf"][e], fp4)
                 W2 = _mx_dense(h["w2"][e], h["w2_sf"][e], fp4)
-            gu = W13 @ x[t]
-            act = gu[:N] / (1 + np.exp(-gu[:N])) * gu[N:]
+            gu = torch.from_numpy(W13 @ x[t])
+            act = _TORCH_ACT[cfg.activation](gu, N).numpy()
             out[t] += st["weights"][t, j] * (W2 @ act)
     return out
+
+
+# the activations through torch's own functions (independent of the oracle)
+_F = torch.nn.functional
+_TORCH_ACT = {
+    "silu": lambda gu, N: _F.silu(gu[..., :N]) * gu[..., N:2 * N],
+    "gelu": lambda gu, N: _F.gelu(gu[..., :N]) * gu[..., N:2 * N],
+    "gelu_tanh": lambda gu, N: _F.gelu(gu[..., :N], approximate="tanh") * gu[..., N:2 * N],
+    "silu_no_mul": lambda gu, N: _F.silu(gu[..., :N]),
+    "gelu_no_mul": lambda gu, N: _F.gelu(gu[..., :N]),
+    "gelu_tanh_no_mul": lambda gu, N: _F.gelu(gu[..., :N], approximate="tanh"),
+    "relu2_no_mul": lambda gu, N: _F.relu(gu[..., :N]) ** 2,
+}
+
+
+@pytest.mark.parametrize("act", sorted(_TORCH_ACT))
+def test_activation_matches_torch(act):
+    """fp64 evaluation rounded once to fp32: within one fp32 unit of torch's
+    float64 function rounded the same way (plus 1e-12 absolute: far in the
+    negative tail 1 + tanh(y) is a few 1e-15 in one libm and 0 in another)."""
+    rng = np.random.default_rng(37)
+    N = 256
+    width = 2 * N if act in O.GATED else N
+    bits = O.bf16_round(rng.standard_normal((40, width)) * 4)
+    ref = _TORCH_ACT[act](torch.from_numpy(O.bf16_to_f64(bits)), N).to(torch.float32).numpy()
+    got = O.act_f32(bits, N, act)
+    assert got.shape == (40, N)
+    ulp = np.spacing(np.abs(ref).astype(np.float32))
+    assert np.all(np.abs(got - ref) <= ulp + 1e-12), act
+
+
+def test_activation_identities():
+    x = np.linspace(-9, 9, 1001)
+    gelu, tanh_gelu = O.ACT_FUNCS["gelu"], O.ACT_FUNCS["gelu_tanh"]
+    # x * Phi(x) - (-x) * Phi(-x) = x, since Phi(x) + Phi(-x) = 1
+    assert np.allclose(gelu(x) - gelu(-x), x, rtol=0, atol=1e-14)
+    assert gelu(np.array([0.0]))[0] == 0 and abs(gelu(np.array([9.0]))[0] - 9) < 1e-15
+    # the tanh form approximates the erf form to about 2e-4 (the published
+    # approximation's accuracy)
+    assert np.max(np.abs(tanh_gelu(x) - gelu(x))) < 1e-3
+    assert np.all(O.ACT_FUNCS["relu2"](np.array([-2.0, 0.0, 3.0])) == [0.0, 0.0, 9.0])
+    # gated with up = 1 equals the ungated form on the gate half
+    rng = np.random.default_rng(38)
+    N = 128
+    g = O.bf16_round(rng.standard_normal((8, N)) * 3)
+    one = O.bf16_round(np.ones((8, N)))
+    for base in ("silu", "gelu", "gelu_tanh"):
+        assert np.array_equal(O.act_f32(np.concatenate([g, one], 1), N, base),
+                              O.act_f32(g, N, base + "_no_mul"))
+
+
+@pytest.mark.parametrize("act", ["gelu", "gelu_tanh", "silu_no_mul", "gelu_no_mul",
+                                 "gelu_tanh_no_mul", "relu2_no_mul"])
+def test_tiny_layer_other_activations_track_unquantized_ffn(act):
+    cfg = moe_synth.custom(T=16, E=4, top_k=2, K=256, N=512, seed=1, activation=act)
+    h = O.host_inputs(moe_synth.make_inputs(cfg))
+    assert h["w13"].shape[1] == (2 if cfg.gated else 1) * cfg.N
+    r = O.forward(h)
+    assert r["gate_up"].shape[1] == cfg.w13_rows and r["a2_q"].shape[1] == cfg.N
+    ref = _dense_ffn(h, r)
+    got = O.bf16_to_f64(r["out"])
+    rel = np.linalg.norm(got - ref) / np.linalg.norm(ref)
+    assert 1e-3 < rel < 0.08, (act, rel)
 
 
 def test_tiny_layer_tracks_unquantized_ffn():
