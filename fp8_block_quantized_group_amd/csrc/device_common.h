@@ -93,4 +93,54 @@ __device__ __forceinline__ GroupScale group_scale(float amax) {
   return r;
 }
 
+// ---- activations ------------------------------------------------------------
+// Kinds (values match moe_act_t).  Gated kinds combine the gate column g with
+// its up column u as f(g) * u; _no_mul kinds return f(g) of the single w13
+// output column.  The experts' activation list names them; the functions are
+// the standard ones: SiLU g * sigmoid(g); GELU g * Phi(g) with the exact
+// normal CDF; the tanh form of GELU; ReLU^2 = max(g, 0)^2.
+constexpr int kActSilu = 0;
+constexpr int kActGelu = 1;
+constexpr int kActGeluTanh = 2;
+constexpr int kActSiluNoMul = 3;
+constexpr int kActGeluNoMul = 4;
+constexpr int kActGeluTanhNoMul = 5;
+constexpr int kActRelu2NoMul = 6;
+constexpr bool act_is_gated(int kind) { return kind < kActSiluNoMul; }
+
+__device__ __forceinline__ float silu_f32(float g) {
+  const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+  return g * sig;
+}
+
+// kind is uniform across the launch (a kernel argument), so the switch is a
+// scalar branch.  SiLU keeps the g * sigmoid(g) * u order in fp32.
+__device__ __forceinline__ float apply_act(int kind, float g, float u) {
+  switch (kind) {
+    case kActGelu:
+    case kActGeluNoMul: {
+      // 1 + erf(g / sqrt 2) as erfc(-g / sqrt 2): no cancellation for g < 0
+      const float f = 0.5f * g * erfcf(-g * 0.70710678118654752f);
+      return kind == kActGelu ? f * u : f;
+    }
+    case kActGeluTanh:
+    case kActGeluTanhNoMul: {
+      // (1 + tanh y) / 2 = sigmoid(2y): no cancellation for y < 0
+      const float y = 0.79788456080286536f * (g + 0.044715f * g * g * g);
+      const float f = g * __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * y));
+      return kind == kActGeluTanh ? f * u : f;
+    }
+    case kActRelu2NoMul: {
+      const float r = fmaxf(g, 0.0f);
+      return r * r;
+    }
+    case kActSiluNoMul:
+      return silu_f32(g);
+    default: {
+      const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
+      return g * sig * u;
+    }
+  }
+}
+
 }  // namespace moe

@@ -220,8 +220,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // ACT (w13 only): the block's 256 weight rows are the gate rows j0 + [0, 128)
 // and the up rows N + j0 + [0, 128) of one 128-column group j0 of h, laid
 // out so that each wave holds 32 gate rows followed by the 32 matching up
-// rows; the epilogue turns the result into silu(gate) * up, quantized per
-// 128 columns, instead of storing it.
+// rows; the epilogue turns the result into f(gate) * up (f the gated
+// activation p.activation, SiLU on the hot path), quantized per 128 columns,
+// instead of storing it.
 //
 // SC selects the scale scheme: kQuantUe8m0 / kQuantF32 (128x128 fp32 weight
 // block scales, per-128 activation scales, fp32 promotion per k-step) or
@@ -660,28 +661,35 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     const int col_off = 32 * wn + (gate_lane ? 16 * kq : 16 * (kq - 2) + 8);
     float h[S::TM][8];
     float amax[S::TM];
+    auto activate = [&](auto f) {
 #pragma unroll
-    for (int j = 0; j < S::TM; ++j) {
-      amax[j] = 0.0f;
+      for (int j = 0; j < S::TM; ++j) {
+        amax[j] = 0.0f;
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
+        for (int ii = 0; ii < 2; ++ii) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float lo = __uint_as_float(f32_to_bf16_bits(acc[ii][j][r]) << 16);
-          const float hi = __uint_as_float(f32_to_bf16_bits(acc[ii + 2][j][r]) << 16);
-          const float recv = __shfl_xor(gate_lane ? hi : lo, 32);
-          const float g = gate_lane ? lo : recv;
-          const float u = gate_lane ? recv : hi;
-          const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
-          const float v = g * sig * u;
-          h[j][4 * ii + r] = v;
-          amax[j] = fmaxf(amax[j], fabsf(v));
+          for (int r = 0; r < 4; ++r) {
+            const float lo = __uint_as_float(f32_to_bf16_bits(acc[ii][j][r]) << 16);
+            const float hi = __uint_as_float(f32_to_bf16_bits(acc[ii + 2][j][r]) << 16);
+            const float recv = __shfl_xor(gate_lane ? hi : lo, 32);
+            const float g = gate_lane ? lo : recv;
+            const float u = gate_lane ? recv : hi;
+            const float v = f(g, u);
+            h[j][4 * ii + r] = v;
+            amax[j] = fmaxf(amax[j], fabsf(v));
+          }
         }
+        // the 4 lanes of this row in the wave: rho, rho + 16, rho + 32, rho + 48
+        amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 16));
+        amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 32));
       }
-      // the 4 lanes of this row in the wave: rho, rho + 16, rho + 32, rho + 48
-      amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 16));
-      amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 32));
-    }
+    };
+    // SiLU gets its own unrolled copy (no per-element branch); the other
+    // gated activations share one that switches on the kind
+    if (p.activation == kActSilu)
+      activate([](float g, float u) { return apply_act(kActSilu, g, u); });
+    else
+      activate([&](float g, float u) { return apply_act(p.activation, g, u); });
     if constexpr (A16) {
       // unquantized w2 input: h rounded once to bf16, 16 bytes per lane
 #pragma unroll

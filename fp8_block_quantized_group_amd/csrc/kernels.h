@@ -67,6 +67,7 @@ struct GemmArgs {
   int numel;                       // T * top_k
   int gather_sorted;               // A row = sorted_ids[pos] / top_k (w13); else pos
   int scatter_sorted;              // output row = sorted_ids[pos] (w2); else pos
+  int activation;             // ACT epilogue: a gated activation kind (moe_act_t)
   int Kd;                    // reduction length, multiple of 128
   int Nout;                  // output columns, multiple of 128
 };
@@ -74,9 +75,11 @@ struct GemmArgs {
 hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, int K, int quant,
                               const int32_t* counts, int max_tokens, hipStream_t stream);
 
+// act: activation kind (moe_act_t); gate_up rows are 2N wide for gated
+// kinds, N for the _no_mul ones
 hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t rows_cap, int N,
                               int quant, const int32_t* num_rows, const int32_t* counts,
-                              int max_tokens, hipStream_t stream);
+                              int max_tokens, int act, hipStream_t stream);
 
 hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint8_t* is_padding,
                         int T, int k, int E, const EplbArgs& eplb, int64_t* idx_out,

@@ -53,6 +53,9 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool batched(const moe_problem_t* p) { return p->layout == MOE_LAYOUT_BATCHED_MASKED; }
 bool indexed(const moe_problem_t* p) { return p->layout == MOE_LAYOUT_INDEXED; }
+// gated activations: w13 has 2N rows (gate, up); the _no_mul ones: N rows
+bool gated(const moe_problem_t* p) { return p->activation < MOE_ACT_SILU_NO_MUL; }
+int64_t w13_rows(const moe_problem_t* p) { return (gated(p) ? 2 : 1) * (int64_t)p->intermediate; }
 
 // Block sizes of the indexed layout: the GEMM tile heights.
 bool valid_block_size(const moe_problem_t* p, int bs) {
@@ -131,6 +134,8 @@ moe_status_t validate_problem(const moe_problem_t* p) {
     return fail(MOE_ERR_INVALID_ARG, "unknown activation quantization %d", p->act_quant);
   if (p->weight_quant < MOE_W_FP8_BLOCK128 || p->weight_quant > MOE_W_MXFP4)
     return fail(MOE_ERR_INVALID_ARG, "unknown weight quantization %d", p->weight_quant);
+  if (p->activation < MOE_ACT_SILU || p->activation > MOE_ACT_RELU2_NO_MUL)
+    return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", p->activation);
   // (weight, activation) pairs: block fp8 weights with per-128 or bf16
   // activations, MXFP8 or MXFP4 weights with MXFP8 activations
   const bool mx_w = p->weight_quant != MOE_W_FP8_BLOCK128;
@@ -147,6 +152,7 @@ struct Plan {
   int64_t route_blocks;
   int64_t max_tiles;
   size_t x_q_bytes, x_sf_bytes, a2_q_bytes, a2_sf_bytes, down_bytes;
+  size_t gate_up_bytes;   // forward workspace: only for _no_mul activations
   size_t stage_ws_bytes;
 };
 
@@ -184,12 +190,13 @@ Plan make_plan(const moe_problem_t* p) {
   pl.a2_q_bytes = (size_t)pl.s.padded_rows * N * elem;
   pl.a2_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.padded_rows * pl.s.a2_sf_row * sfb;
   pl.down_bytes = (size_t)pl.s.expert_rows * K * 2;
+  pl.gate_up_bytes = gated(p) ? 0 : (size_t)pl.s.padded_rows * N * 2;
   return pl;
 }
 
 // Device addresses of the forward workspace.
 struct Workspace {
-  uint8_t* x_q; uint8_t* x_sf; uint8_t* a2_q; uint8_t* a2_sf; uint8_t* down;
+  uint8_t* x_q; uint8_t* x_sf; uint8_t* a2_q; uint8_t* a2_sf; uint8_t* down; uint8_t* gate_up;
   int64_t* idx; float* w; moe_routing_t routing; int32_t* stage_ws;
   int32_t* sorted_ids; int32_t* expert_ids; int32_t* num_padded;   // indexed layout
   size_t total;
@@ -207,6 +214,7 @@ Workspace carve(const Plan& pl, const moe_problem_t* p, uint8_t* base) {
   w.a2_q = take(pl.a2_q_bytes);
   w.a2_sf = take(pl.a2_sf_bytes);
   w.down = take(pl.down_bytes);
+  w.gate_up = take(pl.gate_up_bytes);
   const size_t slots = (size_t)pl.s.slots;
   w.idx = (int64_t*)take(slots * 8);
   w.w = (float*)take(slots * 4);
@@ -367,21 +375,32 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
     g.max_tokens = p->max_tokens_per_expert;
   }
   g.Kd = w13 ? p->hidden : p->intermediate;
-  g.Nout = w13 ? 2 * p->intermediate : p->hidden;
+  g.Nout = w13 ? (int)w13_rows(p) : p->hidden;
+  g.activation = p->activation;
   const int scheme =
       p->weight_quant == MOE_W_MXFP4 ? moe::kSchemeMxfp8W4 : p->act_quant;
   const hipError_t err = moe::launch_grouped_gemm(g, tile_m, max_tiles, scheme, act, stream);
   return launch_status(err, act ? "grouped_gemm_w13_act" : w13 ? "grouped_gemm_w13" : "grouped_gemm_w2");
 }
 
+// num_rows: device row count for the contiguous / indexed layouts (nullptr:
+// the expert offsets' total); the batched layout uses the slab counts.
 moe_status_t run_act(const moe_problem_t* p, const Plan& pl, const void* gate_up,
-                     const moe_routing_t* r, void* a2_q, void* a2_sf, hipStream_t stream) {
+                     const moe_routing_t* r, void* a2_q, void* a2_sf, hipStream_t stream,
+                     const int32_t* num_rows = nullptr) {
   const bool b = batched(p);
+  if (num_rows == nullptr && !b) num_rows = r->expert_offsets + p->num_experts;
   const hipError_t err = moe::launch_act_requant(
-      gate_up, a2_q, a2_sf, pl.s.expert_rows, p->intermediate, p->act_quant,
-      b ? nullptr : r->expert_offsets + p->num_experts, b ? r->expert_num_tokens : nullptr,
-      p->max_tokens_per_expert, stream);
+      gate_up, a2_q, a2_sf, pl.s.padded_rows, p->intermediate, p->act_quant, num_rows,
+      b ? r->expert_num_tokens : nullptr, p->max_tokens_per_expert, p->activation, stream);
   return launch_status(err, "act_requant");
+}
+
+moe_status_t need_gated(const moe_problem_t* p) {
+  if (gated(p)) return MOE_OK;
+  return fail(MOE_ERR_UNSUPPORTED,
+              "the fused w13 call pairs gate and up columns; activation %d has no up half "
+              "(use the w13 GEMM and moe_act_requant)", p->activation);
 }
 
 moe_status_t run_reduce(const moe_problem_t* p, const void* down, const int32_t* slot_row,
@@ -497,6 +516,7 @@ moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q, c
                                       void* stream) {
   CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
+  CHECK(need_gated(p));
   CHECK(check_ptr(a_q, "a_q", 16));
   CHECK(check_sf(p, a_sf, "a_sf"));
   CHECK(check_routing(routing));
@@ -579,6 +599,7 @@ moe_status_t moe_grouped_gemm_w13_act_indexed(
     const void* w13, const void* w13_sf, void* a2_q, void* a2_sf, void* stream) {
   CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
+  CHECK(need_gated(p));
   CHECK(check_indexed(p, sorted_ids, expert_ids, num_tokens_padded, block_size));
   CHECK(check_ptr(a_q, "a_q", 16));
   CHECK(check_sf(p, a_sf, "a_sf"));
@@ -644,18 +665,31 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
   const hipStream_t s = (hipStream_t)stream;
   CHECK(run_stage(p, pl, hidden, expert_num_tokens_in, topk_ids, topk_weights, is_padding, eplb,
                   w.x_q, w.x_sf, w.idx, w.w, &w.routing, w.stage_ws, s));
+  // gated activations: w13 with the activation fused; _no_mul ones: the w13
+  // GEMM into gate_up, then the activation kernel
   if (indexed(p)) {
     const Indexed ix{w.sorted_ids, w.expert_ids, w.num_padded, pl.s.tile_m};
     CHECK(run_align(p, w.idx, &w.routing, ix, s));
-    CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, nullptr, w13, w13_sf, nullptr, s, true, w.a2_q,
-                   w.a2_sf, &ix));
+    if (gated(p)) {
+      CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, nullptr, w13, w13_sf, nullptr, s, true, w.a2_q,
+                     w.a2_sf, &ix));
+    } else {
+      CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, nullptr, w13, w13_sf, w.gate_up, s, false,
+                     nullptr, nullptr, &ix));
+      CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s, w.num_padded));
+    }
     CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, nullptr, w2, w2_sf, w.down, s, false, nullptr,
                    nullptr, &ix));
     CHECK(run_mul_sum(p, w.down, w.idx, w.w, out, s));
     return ok();
   }
-  CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, nullptr, s, true, w.a2_q,
-                 w.a2_sf));
+  if (gated(p)) {
+    CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, nullptr, s, true, w.a2_q,
+                   w.a2_sf));
+  } else {
+    CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, w.gate_up, s));
+    CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s));
+  }
   CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s));
   CHECK(run_reduce(p, w.down, w.routing.slot_row, w.w, out, s));
   return ok();

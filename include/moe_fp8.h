@@ -40,7 +40,8 @@
  *    byte-identical to the pages' "four per int32" little-endian packing
  *    (_pack_bytes).  MOE_Q_FP8_F32: fp32 [rows, G].  MOE_Q_MXFP8: one
  *    exponent byte per 32-group, rows of K/32 bytes (no pad: K % 128 == 0).
- *  - Weights: w13 [E, 2N, K] fp8 codes (rows [0, N) gate, [N, 2N) up), w2
+ *  - Weights: w13 [E, 2N, K] fp8 codes (rows [0, N) gate, [N, 2N) up; a
+ *    _NO_MUL activation: [E, N, K] and every "2N" below reads N), w2
  *    [E, K, N].  MOE_W_FP8_BLOCK128 (kFp8Static128BlockSym): fp32 block scales
  *    w13_sf [E, 2N/128, K/128], w2_sf [E, K/128, N/128], dequantized weight =
  *    code * block scale.  MOE_W_MXFP8 (kMxfp8Static): E8M0 bytes w13_sf
@@ -88,6 +89,25 @@ typedef enum {
   MOE_W_MXFP4 = 2         /* e2m1 (two per byte), E8M0 per row and 32 cols  */
 } moe_weight_t;
 
+/* Activation between the two GEMMs (HummingExpertsBase._supports_activation
+ * lists these; the pages do not show their formulas, so the standard ones are
+ * used: SiLU g*sigmoid(g), GELU g*Phi(g) with the exact normal CDF, its tanh
+ * approximation 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))), ReLU^2
+ * max(g, 0)^2).  Gated kinds: w13 has 2N rows, h = f(gate) * up.  _NO_MUL
+ * kinds: w13 has N rows, h = f(w13 output) (get_buffer_metas: the w2 input
+ * is the whole w13 output for non-gated activations).  SWIGLUOAI, SWIGLUSTEP
+ * and the SiLU clamp limit are not provided (their parameters are not on the
+ * pages). */
+typedef enum {
+  MOE_ACT_SILU = 0,
+  MOE_ACT_GELU = 1,
+  MOE_ACT_GELU_TANH = 2,
+  MOE_ACT_SILU_NO_MUL = 3,
+  MOE_ACT_GELU_NO_MUL = 4,
+  MOE_ACT_GELU_TANH_NO_MUL = 5,
+  MOE_ACT_RELU2_NO_MUL = 6
+} moe_act_t;
+
 /* Expert-row layouts ("Standard" and "BatchedExperts" activation formats of
  * HummingGroupedExperts / BatchedHummingGroupedExperts, and the block map of
  * HummingIndexedExperts). */
@@ -111,6 +131,7 @@ typedef struct {
   int32_t max_tokens_per_expert; /* batched layout only */
   int32_t act_quant;             /* moe_quant_t */
   int32_t weight_quant;          /* moe_weight_t */
+  int32_t activation;            /* moe_act_t (0 = SiLU(gate) * up) */
 } moe_problem_t;
 
 /* Expert-parallel load balancing state (optional; all device pointers).
@@ -209,17 +230,20 @@ moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const
  * step earlier, into the producing GEMM.  a2_q fp8 [expert_rows, N], a2_sf per
  * the activation scheme (bf16 activations: a2_q bf16 [expert_rows, N], a2_sf
  * NULL); rows past an expert's count are not written.
- * a2_q / a2_sf must not overlap a_q / a_sf. */
+ * a2_q / a2_sf must not overlap a_q / a_sf.  Gated activations only (a
+ * _NO_MUL activation has no up half to pair: MOE_ERR_UNSUPPORTED; use
+ * moe_grouped_gemm_w13 + moe_act_requant, as moe_forward does). */
 moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q,
                                       const void* a_sf, const moe_routing_t* routing,
                                       const void* w13, const void* w13_sf, void* a2_q,
                                       void* a2_sf, void* stream);
 
-/* Step 4: a2 = quant(silu(gate_up[:, :N]) * gate_up[:, N:]) per group (128
- * columns, 32 for MXFP8), computed in fp32 and quantized without an
- * intermediate rounding.  a2_q fp8 [expert_rows, N], a2_sf per the activation
- * scheme; bf16 activations: a2_q = bf16(silu(g) * u) [expert_rows, N], a2_sf
- * NULL. */
+/* Step 4: a2 = quant(h) per group (128 columns, 32 for MXFP8) with h =
+ * f(gate_up[:, :N]) * gate_up[:, N:] (gated activations, SiLU by default) or
+ * f(gate_up) (_NO_MUL, gate_up [expert_rows, N]), computed in fp32 and
+ * quantized without an intermediate rounding.  a2_q fp8 [expert_rows, N],
+ * a2_sf per the activation scheme; bf16 activations: a2_q = bf16(h)
+ * [expert_rows, N], a2_sf NULL. */
 moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
                              const moe_routing_t* routing, void* a2_q, void* a2_sf,
                              void* stream);
@@ -294,7 +318,9 @@ moe_status_t moe_fused_mul_sum(const moe_problem_t* p, const void* down, const i
 
 /* Steps 1-6 on one stream (stage, fused w13 + activation, w2, reduce).
  * Arguments as in moe_stage plus the weights and out bf16 [T, K]; ws: device
- * workspace of moe_workspace_size bytes.  Any supported scheme pair.  Layout
+ * workspace of moe_workspace_size bytes.  Any supported scheme pair and
+ * activation (_NO_MUL ones run the w13 GEMM and the activation kernel
+ * separately, through a gate_up region of the workspace).  Layout
  * INDEXED runs stage, moe_align_block_size with block size tile_m, the two
  * indexed GEMMs and moe_fused_mul_sum. */
 moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,

@@ -148,23 +148,43 @@ def check_requant(got_q, got_sf, ref_q, ref_sf, ref_h32, ue8m0, what, group=128)
     return frac
 
 
+def act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation="silu"):
+    """(h, dh): the oracle's h in fp64 and a bound on how far h moves when
+    gate_up moves by the GEMM bound (bf16 unit + MFMA term), for the given
+    activation.  SiLU uses its derivative; the others the largest change of
+    f over [g - dg, g + dg] sampled at eight points, with a 25 % margin for
+    the curvature between samples."""
+    gu = O.bf16_to_f64(ref_gate_up_bits)
+    dgu = bf16_ulp(gu) + MFMA_REL * s_abs_gate_up
+    gated = activation in O.GATED
+    g, dg = gu[:, :N], dgu[:, :N]
+    u, du = (gu[:, N:2 * N], dgu[:, N:2 * N]) if gated else (np.ones_like(g), np.zeros_like(g))
+    if activation == "silu":
+        sig = 1.0 / (1.0 + np.exp(-g))
+        f = g * sig
+        sens = np.abs(sig * (1.0 + g * (1.0 - sig))) * dg
+    else:
+        fn = O.ACT_FUNCS[activation.replace("_no_mul", "")]
+        f = fn(g)
+        sens = np.zeros_like(g)
+        for t in (-1.0, -0.75, -0.5, -0.25, 0.25, 0.5, 0.75, 1.0):
+            sens = np.maximum(sens, np.abs(fn(g + t * dg) - f))
+        sens *= 1.25
+    dh = (sens * np.abs(u) + np.abs(f) * du + 1.1 * sens * du) * 1.01
+    h = f * u
+    dh += np.abs(h) * 2.0 ** -20 + 2.0 ** -40
+    return h, dh
+
+
 def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_gate_up, ue8m0,
-                        what, group=128):
+                        what, group=128, activation="silu"):
     """End of the GPU's own chain: its gate_up may differ from the oracle's
-    by the GEMM bound; carry that through h = silu(g) * u and allow half an
+    by the GEMM bound; carry that through the activation and allow half an
     fp8 step of rounding on each side.  Returns the fraction of codes that
     differ."""
     rows, N = ref_q.shape
     G = N // group
-    gu = O.bf16_to_f64(ref_gate_up_bits)
-    g, u = gu[:, :N], gu[:, N:]
-    dgu = bf16_ulp(gu) + MFMA_REL * s_abs_gate_up
-    dg, du = dgu[:, :N], dgu[:, N:]
-    sig = 1.0 / (1.0 + np.exp(-g))
-    silu = g * sig
-    dsilu = np.abs(sig * (1.0 + g * (1.0 - sig)))
-    dh = (dsilu * np.abs(u) * dg + np.abs(silu) * du + 1.1 * dg * du) * 1.01
-    dh += np.abs(silu * u) * 2.0 ** -20
+    _, dh = act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation)
     sv_g = np.repeat(O.scale_values(got_sf[:, :G], ue8m0), group, axis=1)
     sv_r = np.repeat(O.scale_values(ref_sf[:, :G], ue8m0), group, axis=1)
     vg = O.e4m3_decode(got_q) * sv_g
@@ -178,22 +198,16 @@ def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_ga
     return np.count_nonzero(got_q != ref_q) / got_q.size
 
 
-def check_bf16_act_chain(got_bits, ref_bits, ref_gate_up_bits, s_abs_gate_up, what):
+def check_bf16_act_chain(got_bits, ref_bits, ref_gate_up_bits, s_abs_gate_up, what,
+                         activation="silu"):
     """bf16 w2 input at the end of the GPU's own chain: the GEMM bound on
-    gate_up carried through silu(g) * u, plus one bf16 rounding on each side.
-    Returns the fraction of values that differ."""
+    gate_up carried through the activation, plus one bf16 rounding on each
+    side.  Returns the fraction of values that differ."""
     N = ref_bits.shape[1]
-    gu = O.bf16_to_f64(ref_gate_up_bits)
-    g, u = gu[:, :N], gu[:, N:]
-    dgu = bf16_ulp(gu) + MFMA_REL * s_abs_gate_up
-    dg, du = dgu[:, :N], dgu[:, N:]
-    sig = 1.0 / (1.0 + np.exp(-g))
-    silu = g * sig
-    dsilu = np.abs(sig * (1.0 + g * (1.0 - sig)))
-    dh = (dsilu * np.abs(u) * dg + np.abs(silu) * du + 1.1 * dg * du) * 1.01
+    h, dh = act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation)
     vg, vr = O.bf16_to_f64(got_bits), O.bf16_to_f64(ref_bits)
     assert np.all(np.isfinite(vg)), f"{what}: non-finite values"
-    bound = dh + bf16_ulp(vr) + np.abs(silu * u) * 2.0 ** -20
+    bound = dh + bf16_ulp(vr)
     bad = np.abs(vg - vr) > bound * 1.000001
     assert not bad.any(), f"{what}: {bad.sum()} values beyond the propagated bound"
     return np.count_nonzero(got_bits != ref_bits) / got_bits.size

@@ -254,3 +254,27 @@ def test_indexed_validation(lib):
     assert st == -1 and "topk_idx" in lib.moe_last_error().decode()
     st = lib.moe_align_block_size(ctypes.byref(c), V, None, 16, V, V, V, None)
     assert st == -1 and "routing" in lib.moe_last_error().decode()
+
+
+def test_activation_validation_and_workspace(lib):
+    base = dict(num_tokens=16, hidden=256, intermediate=512, num_experts=4, top_k=2)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.sizes(moe.Problem(**base, activation=7))
+    assert ei.value.status == -1
+    # _no_mul activations keep a gate_up region (T*k rows of N bf16) in the
+    # forward workspace; gated ones do not
+    ws_silu = moe.workspace_size(moe.Problem(**base))
+    ws_gelu = moe.workspace_size(moe.Problem(**base, activation=1))
+    ws_relu2 = moe.workspace_size(moe.Problem(**base, activation=6))
+    assert ws_silu == ws_gelu
+    assert ws_relu2 >= ws_silu + 16 * 2 * 512 * 2
+    # the fused w13 call has no up half to pair for _no_mul activations: it is
+    # refused before anything else is looked at
+    V = _fake()
+    for act, status in [(3, -2), (4, -2), (5, -2), (6, -2)]:
+        c = moe.Problem(**base, activation=act).c()
+        st = lib.moe_grouped_gemm_w13_act(ctypes.byref(c), V, V, None, V, V, V, V, None)
+        assert st == status, act
+        st = lib.moe_grouped_gemm_w13_act_indexed(ctypes.byref(c), V, V, V, V, V, 16, V, V, V,
+                                                  V, None)
+        assert st == status, act
