@@ -271,6 +271,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int NT = p.Nout / S::BN;
   const int64_t ntiles =
       indexed ? (int64_t)min(max(*p.num_padded, 0) / S::BM, p.max_blocks) : (int64_t)p.tile_list[0];
+  const int ngroups = indexed ? 0 : p.tile_list[1];
   const int64_t work = ntiles * NT;
   const int64_t per_xcd = (work + 7) / 8;
   const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
@@ -282,10 +283,10 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   } else {
     // group g with groups[g] <= wl / NT < groups[g+1] (binary search in LDS)
     int* groups = reinterpret_cast<int*>(smem);
-    for (int i = threadIdx.x; i <= p.num_experts; i += S::THREADS) groups[i] = p.tile_groups[i];
+    for (int i = threadIdx.x; i <= ngroups; i += S::THREADS) groups[i] = p.tile_groups[i];
     __syncthreads();
     const int t0 = (int)(wl / NT);
-    int lo = 0, hi = p.num_experts;   // groups[lo] <= t0 < groups[hi]
+    int lo = 0, hi = ngroups;   // groups[lo] <= t0 < groups[hi]
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (groups[mid] <= t0) lo = mid; else hi = mid;
@@ -308,8 +309,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     rows_here = __syncthreads_count(valid);
     if ((uint32_t)e >= (uint32_t)p.num_experts) return;
   } else {
-    e = p.tile_list[1 + 2 * tile];
-    m0 = p.tile_list[2 + 2 * tile];
+    e = p.tile_list[2 + 2 * tile];
+    m0 = p.tile_list[3 + 2 * tile];
     int cnt = p.counts[e];
     if (p.offsets == nullptr) cnt = min(cnt, p.max_tokens);
     rows_here = min(S::BM, cnt - m0);

@@ -47,8 +47,9 @@ struct GemmArgs {
   uint8_t* act_q;            // fused activation: fp8 [rows, Nout/2]
   uint8_t* act_sf;           //   and its per-128 scales (UE8M0 bytes or fp32)
   int act_sf_row;            //   scale row length: bytes (UE8M0) or floats (fp32)
-  const int32_t* tile_list;  // [0] tile count, then (expert, m0) pairs
-  const int32_t* tile_groups;  // [E+1] first tile of each expert group (heavy-first)
+  const int32_t* tile_list;  // [0] tile count, [1] group count G, then (expert, m0) pairs
+  const int32_t* tile_groups;  // [G+1] first tile of each group (one expert's
+                               // consecutive m-tiles), in XCD-balanced order
   int num_experts;
   const int32_t* counts;     // [E] rows per expert
   const int32_t* offsets;    // [E+1] contiguous row base, nullptr for batched slabs

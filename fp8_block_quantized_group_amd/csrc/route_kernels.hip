@@ -19,6 +19,8 @@
 //      row_src and slot_row.
 // Rows of one expert come out in ascending flat slot order t*top_k + j, so
 // the layout is deterministic.
+#include <limits.h>
+
 #include "device_common.h"
 #include "kernels.h"
 
@@ -70,37 +72,72 @@ __global__ __launch_bounds__(kRouteThreads) void route_repack_hist_kernel(
   }
 }
 
-// Inclusive scan of one value per thread over a 1024-thread block.
+// Inclusive scan of one value per thread over a 1024-thread block: each wave
+// scans its 64 values with lane shuffles, wave 0 scans the 16 wave totals,
+// every thread adds its wave's offset.  buf needs 32 ints and is free again
+// when the function returns.
 __device__ int block_inclusive_scan(int v, int* buf) {
-  const int tid = threadIdx.x;
-  buf[tid] = v;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int add = tid >= d ? buf[tid - d] : 0;
-    __syncthreads();
-    buf[tid] += add;
-    __syncthreads();
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    if (lane >= d) v += t;
   }
-  const int r = buf[tid];
+  if (lane == 63) buf[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? buf[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int t = __shfl_up(w, d);
+      if (lane >= d) w += t;
+    }
+    if (lane < 16) buf[16 + lane] = w;
+  }
+  __syncthreads();
+  const int r = v + (wave > 0 ? buf[16 + wave - 1] : 0);
   __syncthreads();
   return r;
 }
+
+// M-tile schedule for the grouped GEMMs.  The GEMM hands its 1-D work list
+// to the 8 XCDs in 8 equal contiguous ranges (block L runs on XCD L % 8), so
+// the list is ordered to give every range the same mix: each expert's
+// m-tiles are cut into chunks of at most S tiles (S = 8, more only when
+// there would be over 1024 chunks), the chunks sorted by size class (full
+// chunks first in expert order, then the remainders r by the class
+// floor(8r / S), largest first, ties by expert; for S = 8 the class is the
+// size), and dealt in rounds of 8: the round's first chunk to the bin with
+// the fewest tiles so far, and so on (round-based longest-processing-time).  Bins are concatenated.  Every range then holds
+// about the same number of tiles (MFMA work) and of weight chunks (HBM
+// bytes); a heaviest-expert-first list instead left some XCDs streaming most
+// of the weights while others did most of the arithmetic.
+constexpr int kChunkCap = 2048;
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(
     int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
     int max_tokens, int tile_m, int max_tiles, int32_t* __restrict__ expert_num_tokens,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ tile_list) {
   __shared__ int buf[1024];
-  __shared__ int tiles[1024];
-  __shared__ int order[1024];
+  __shared__ int wcnt[16][8];      // remainder chunks per wave and size class
+  __shared__ int woff[16][8];      // their first index
+  __shared__ int chunk_e[kChunkCap], chunk_m[kChunkCap], chunk_n[kChunkCap];
+  __shared__ int chunk_bin[kChunkCap], chunk_off[kChunkCap], chunk_idx[kChunkCap];
+  __shared__ int bin_load[8], bin_cnt[8];
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E) {
-    // per-block bases (relative to the expert's first row)
-    for (int b = 0; b < nblocks; ++b) {
-      const int c = hist[(int64_t)b * E + e];
-      hist[(int64_t)b * E + e] = cnt;
-      cnt += c;
+    // per-block bases (relative to the expert's first row); the counts are
+    // loaded 16 blocks at a time so their latencies overlap
+    for (int b0 = 0; b0 < nblocks; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) c[j] = b0 + j < nblocks ? hist[(int64_t)(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (b0 + j < nblocks) hist[(int64_t)(b0 + j) * E + e] = cnt;
+        cnt += c[j];
+      }
     }
   }
   const int incl = block_inclusive_scan(e < E ? cnt : 0, buf);
@@ -112,34 +149,123 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     expert_num_tokens[e] = counts_in != nullptr ? rows : cnt;
     if (e == E - 1) expert_offsets[E] = incl;
   }
-  tiles[e] = nt;
+  const int incl_nt = block_inclusive_scan(nt, buf);
+  // the last thread's inclusive value is the total: broadcast it
+  if (e == 1023) buf[0] = incl_nt;
   __syncthreads();
-  // heavy-first order: rank by tile count descending, ties by expert id
-  if (e < E) {
-    int rank = 0;
-    for (int o = 0; o < E; ++o) {
-      const int to = tiles[o];
-      rank += (to > nt || (to == nt && o < e)) ? 1 : 0;
-    }
-    order[rank] = e;
+  const int total = buf[0];
+  __syncthreads();
+  const int S = max(8, (total + 1023) / 1024);
+  const int full = nt / S, r = nt % S;
+  const int fstart = block_inclusive_scan(full, buf) - full;
+  if (e == 1023) bin_load[0] = fstart + full;      // F, the number of full chunks
+  // remainder chunks: counting sort by size class with one ballot per class
+  const int lane = e & 63, wave = e >> 6;
+  const int cls = r > 0 ? (r * 8) / S : -1;
+  int rank_w = 0;
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const uint64_t m = __ballot(cls == c);
+    if (lane == 0) wcnt[wave][c] = __popcll(m);
+    if (cls == c) rank_w = __popcll(m & ((1ull << lane) - 1ull));
   }
   __syncthreads();
-  const int mine = e < E ? tiles[order[e]] : 0;
-  const int incl_t = block_inclusive_scan(mine, buf);
-  // group e (the e-th heaviest expert) owns tiles [group_off[e], group_off[e+1])
-  int32_t* group_off = tile_list + 1 + 2 * max_tiles;
-  if (e < E) {
-    const int ex = order[e];
-    int pos = incl_t - mine;
-    group_off[e] = pos;
-    for (int i = 0; i < mine; ++i, ++pos) {
-      tile_list[1 + 2 * pos] = ex;
-      tile_list[2 + 2 * pos] = i * tile_m;
+  const int F = bin_load[0];
+  if (e < 128) {
+    // first index of (wave w, class c): F, then the classes above c, then the
+    // waves before w within class c
+    const int w = e >> 3, c = e & 7;
+    int off = F;
+    for (int c2 = c + 1; c2 < 8; ++c2)
+      for (int w2 = 0; w2 < 16; ++w2) off += wcnt[w2][c2];
+    for (int w2 = 0; w2 < w; ++w2) off += wcnt[w2][c];
+    woff[w][c] = off;
+  }
+  __syncthreads();
+  const int ridx = cls >= 0 ? woff[wave][cls] + rank_w : 0;
+  for (int j = 0; j < full; ++j) {
+    chunk_e[fstart + j] = e;
+    chunk_m[fstart + j] = j * S;
+    chunk_n[fstart + j] = S;
+  }
+  if (r > 0) {
+    chunk_e[ridx] = e;
+    chunk_m[ridx] = full * S;
+    chunk_n[ridx] = r;
+  }
+  const int C = F + block_inclusive_scan(r > 0 ? 1 : 0, buf);   // valid in thread 1023
+  if (e == 1023) bin_cnt[0] = C;
+  __syncthreads();
+  const int nchunks = bin_cnt[0];
+  __syncthreads();
+  // round-based dealing by wave 0; lane x < 8 is bin x.  Lane y also holds
+  // the size of the round's chunk y (loaded one round ahead).
+  if (e < 64) {
+    int load = 0, count = 0;
+    const int rounds = (nchunks + 7) / 8;
+    int sz = e < 8 && e < nchunks ? chunk_n[e] : 0;
+    int rank = e;            // all loads 0: bin x has rank x
+    bool uniform = true;     // the previous round's chunks were all one size
+    for (int rd = 0; rd < rounds; ++rd) {
+      const int nxt = 8 * (rd + 1) + e;
+      const int sz_next = e < 8 && nxt < nchunks ? chunk_n[nxt] : 0;
+      // After a round whose chunks all had one size every bin grew by the
+      // same amount and the ranking stands; otherwise rank the loads again
+      // (through scalar registers: no LDS round trip on this serial path).
+      if (!uniform) {
+        rank = 0;
+#pragma unroll
+        for (int y = 0; y < 8; ++y) {
+          const int ly = __builtin_amdgcn_readlane(load, y);
+          rank += (ly < load || (ly == load && y < e)) ? 1 : 0;
+        }
+      }
+      // the size of this bin's chunk, and whether the round is full and of
+      // one size (then the next round keeps the ranking)
+      int mine = 0, smin = INT_MAX, smax = 0;
+#pragma unroll
+      for (int y = 0; y < 8; ++y) {
+        const int sy = __builtin_amdgcn_readlane(sz, y);
+        mine = rank == y ? sy : mine;
+        smin = min(smin, sy);
+        smax = max(smax, sy);
+      }
+      uniform = smin == smax && 8 * rd + 7 < nchunks;
+      const int i = 8 * rd + rank;
+      if (e < 8 && i < nchunks) {
+        chunk_bin[i] = e;
+        chunk_off[i] = load;
+        chunk_idx[i] = count;
+        load += mine;
+        count += 1;
+      }
+      sz = sz_next;
     }
-    if (e == E - 1) {
-      tile_list[0] = incl_t;
-      group_off[E] = incl_t;
+    if (e < 8) {
+      bin_load[e] = load;
+      bin_cnt[e] = count;
     }
+  }
+  __syncthreads();
+  int32_t* pairs = tile_list + 2;
+  int32_t* group_off = tile_list + 2 + 2 * max_tiles;
+  for (int i = e; i < nchunks; i += 1024) {
+    const int x = chunk_bin[i];
+    int tile0 = chunk_off[i], g = chunk_idx[i];
+    for (int y = 0; y < x; ++y) {
+      tile0 += bin_load[y];
+      g += bin_cnt[y];
+    }
+    group_off[g] = tile0;
+    for (int t = 0; t < chunk_n[i]; ++t) {
+      pairs[2 * (tile0 + t)] = chunk_e[i];
+      pairs[2 * (tile0 + t) + 1] = (chunk_m[i] + t) * tile_m;
+    }
+  }
+  if (e == 0) {
+    tile_list[0] = total;
+    tile_list[1] = nchunks;
+    group_off[nchunks] = total;
   }
 }
 
@@ -204,17 +330,12 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     int bs, int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
     int32_t* __restrict__ num_padded) {
   __shared__ int32_t scan[kAlignThreads];
+  __shared__ int buf[32];
   const int t = threadIdx.x;
   const int cnt = t < E ? counts[t] : 0;
   const int pc = (cnt + bs - 1) / bs * bs;
-  scan[t] = pc;
+  scan[t] = block_inclusive_scan(pc, buf);
   __syncthreads();
-  for (int d = 1; d < kAlignThreads; d <<= 1) {   // inclusive Hillis-Steele scan
-    const int v = t >= d ? scan[t - d] : 0;
-    __syncthreads();
-    scan[t] += v;
-    __syncthreads();
-  }
   if (blockIdx.x == 0) {
     const int end = scan[t], start = end - pc;
     if (t < E) {

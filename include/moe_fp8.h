@@ -159,10 +159,13 @@ typedef struct {
  *  row_src           [T*top_k] token of each contiguous row (contiguous layout)
  *  slot_row          [T*top_k] row of (token, slot), -1 when unrouted;
  *                    batched: e * max_tokens + rank (rank >= max_tokens -> -1)
- *  tile_list         [1 + 2*max_tiles + E + 1] M-tile schedule for the GEMMs:
- *                    tile count, (expert, first row) pairs with each expert's
- *                    tiles contiguous and the most-loaded experts first, then
- *                    the first tile of each expert group (E + 1 offsets) */
+ *  tile_list         [moe_sizes_t.tile_list] M-tile schedule for the GEMMs:
+ *                    tile count n, group count G, n (expert, first row)
+ *                    pairs, then G + 1 group offsets; a group is a run of at
+ *                    most 8 consecutive m-tiles of one expert (more only for
+ *                    very large batches), and the groups are ordered so that
+ *                    8 equal slices of the list hold similar work and weight
+ *                    bytes (one slice per XCD) */
 typedef struct {
   int32_t* expert_num_tokens;
   int32_t* expert_offsets;

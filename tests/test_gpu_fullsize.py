@@ -1,6 +1,7 @@
-"""Parity at the workloads' full sizes (the five block-fp8 ones and the
-MX-scheme DeepSeek-V3 prefill), in the launch configuration the benchmark
-times (moe_forward, same tile height).
+"""Parity at the workloads' full sizes (the five block-fp8 ones, the MX and
+bf16-activation variants and the indexed-layout DeepSeek-V3 prefill), in
+the launch configuration the benchmark times (moe_forward, same tile
+height).
 
 The oracle cannot run these layers whole, so it checks what it can compute
 piece by piece: the complete routing layout and EPLB load (cheap), the
@@ -18,12 +19,12 @@ import moe_synth
 from oracle import moe_oracle as O
 from parity_util import (abs_gemm_cfg, check_bf16_act_chain, check_gemm, check_output,
                          check_requant_chain, to_np)
-from test_gpu_parity import run_chain, run_forward
+from test_gpu_parity import check_schedule, run_chain, run_forward
 
 pytestmark = pytest.mark.gpu
 
 FULL = ["tiny", "mixtral", "dsv3_prefill", "dsv3_decode", "qwen3", "dsv3_prefill_mxfp8",
-        "dsv3_prefill_mxfp4", "qwen3_bf16"]
+        "dsv3_prefill_mxfp4", "qwen3_bf16", "dsv3_prefill_indexed"]
 
 
 def _host_light(inp):
@@ -70,6 +71,8 @@ def test_full_size_sampled(name):
         assert np.array_equal(to_np(bufs["row_src"])[:M], st["row_src"])
     if cfg.eplb:
         assert np.array_equal(to_np(inp["eplb"]["expert_load"]), st["load"])
+    counts = st["counts"] if cfg.layout != "batched" else np.minimum(st["counts"], cfg.max_tokens)
+    check_schedule(bufs["tile_list"], counts, moe.sizes(moe.Problem.from_config(cfg)), cfg.E)
     # quantized hidden rows of a token sample, bit-exact
     rng = np.random.default_rng(cfg.seed + 100)
     ue, grp = O.act_e8m0(cfg), O.act_group(cfg)

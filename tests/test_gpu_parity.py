@@ -113,23 +113,55 @@ def stage_on_gpu(cfg, dev):
     return p, bufs
 
 
+def _max_tiles(n_entries, E):
+    # n_entries = 2 + 2 * max_tiles + E + max_tiles + 1
+    return (n_entries - 3 - E) // 3
+
+
 def host_tile_list(counts, tile_m, n_entries):
-    """Every (expert, m0) tile in plain expert order plus the per-expert
-    group offsets (test plumbing: the GEMM must not depend on the order the
-    routing step emits)."""
+    """Every (expert, m0) tile in plain expert order, one group per expert
+    (test plumbing: the GEMM must not depend on the order the routing step
+    emits)."""
     E = len(counts)
-    max_tiles = (n_entries - 1 - (E + 1)) // 2
+    max_tiles = _max_tiles(n_entries, E)
     tl = np.zeros(n_entries, np.int32)
-    groups = tl[1 + 2 * max_tiles:]
+    groups = tl[2 + 2 * max_tiles:]
     pos = 0
     for e, c in enumerate(counts):
         groups[e] = pos
         for m0 in range(0, int(c), tile_m):
-            tl[1 + 2 * pos], tl[2 + 2 * pos] = e, m0
+            tl[2 + 2 * pos], tl[3 + 2 * pos] = e, m0
             pos += 1
     groups[E] = pos
-    tl[0] = pos
+    tl[0], tl[1] = pos, E
     return tl
+
+
+def expected_schedule(tiles_per_expert):
+    """The documented schedule: chunks of at most S = max(8, ceil(n / 1024))
+    m-tiles per expert, sorted by size (full chunks first in expert order,
+    then remainders r by the class floor(8r / S) descending, ties by expert),
+    dealt in rounds of 8 to the bins ranked by (tiles so far, bin index),
+    bins concatenated.
+    Returns the (expert, m-tile index) sequence and the group sizes."""
+    n = int(sum(tiles_per_expert))
+    S = max(8, -(-n // 1024))
+    full = [(e, j * S, S) for e, t in enumerate(tiles_per_expert) for j in range(t // S)]
+    rem = sorted(((e, (t // S) * S, t % S) for e, t in enumerate(tiles_per_expert) if t % S),
+                 key=lambda c: (-(c[2] * 8 // S), c[0]))
+    chunks = full + rem
+    load, bins = [0] * 8, [[] for _ in range(8)]
+    for r0 in range(0, len(chunks), 8):
+        rank = sorted(range(8), key=lambda x: (load[x], x))
+        for i, ch in enumerate(chunks[r0:r0 + 8]):
+            bins[rank[i]].append(ch)
+            load[rank[i]] += ch[2]
+    seq, sizes = [], []
+    for b in bins:
+        for e, m, c in b:
+            seq += [(e, m + t) for t in range(c)]
+            sizes.append(c)
+    return seq, sizes
 
 
 def oracle_routing(p, cfg, ref):
@@ -263,25 +295,29 @@ def test_stage_and_route_bit_exact(gpu, name):
     assert np.array_equal(to_np(bufs["slot_row"]).reshape(cfg.T, cfg.top_k), ref["slot_row"])
     if cfg.eplb:
         assert np.array_equal(to_np(dev["eplb"]["expert_load"]), ref["load"])
-    # tile schedule: each expert's tiles exactly once, heaviest experts first
-    s = moe.sizes(p)
-    tl = to_np(bufs["tile_list"])
-    n = int(tl[0])
-    pairs = tl[1:1 + 2 * n].reshape(n, 2)
+    check_schedule(bufs["tile_list"], ref["counts"], moe.sizes(p), cfg.E)
+
+
+def check_schedule(tile_list, counts, s, E):
+    """The tile schedule: every expert's tiles exactly once, in the
+    documented XCD-balanced order, groups of consecutive m-tiles of one
+    expert."""
+    tl = to_np(tile_list)
+    n, G = int(tl[0]), int(tl[1])
     bm = s["tile_m"]
-    want = sorted((e, m0) for e, c in enumerate(ref["counts"]) for m0 in range(0, int(c), bm))
-    assert sorted(map(tuple, pairs.tolist())) == want
-    per_expert = [-(-int(ref["counts"][e]) // bm) for e in pairs[:, 0]]
-    assert all(a >= b for a, b in zip(per_expert, per_expert[1:]))
-    # group offsets: group g = the g-th heaviest expert's contiguous tiles
-    max_tiles = (s["tile_list"] - 1 - (cfg.E + 1)) // 2
-    groups = tl[1 + 2 * max_tiles:1 + 2 * max_tiles + cfg.E + 1]
-    assert groups[0] == 0 and groups[-1] == n and np.all(np.diff(groups) >= 0)
-    for g in range(cfg.E):
+    pairs = tl[2:2 + 2 * n].reshape(n, 2)
+    tiles = [-(-int(c) // bm) for c in counts]
+    seq, sizes = expected_schedule(tiles)
+    assert [(int(e), int(m0) // bm) for e, m0 in pairs] == seq
+    assert np.all(pairs[:, 1] % bm == 0)
+    max_tiles = _max_tiles(s["tile_list"], E)
+    groups = tl[2 + 2 * max_tiles:2 + 2 * max_tiles + G + 1]
+    assert G == len(sizes) and groups[0] == 0 and groups[-1] == n
+    assert list(np.diff(groups)) == sizes
+    for g in range(G):
         seg = pairs[groups[g]:groups[g + 1]]
-        if len(seg):
-            assert np.all(seg[:, 0] == seg[0, 0])
-            assert list(seg[:, 1]) == list(range(0, len(seg) * bm, bm))
+        assert np.all(seg[:, 0] == seg[0, 0])
+        assert list(seg[:, 1]) == list(range(int(seg[0, 1]), int(seg[0, 1]) + len(seg) * bm, bm))
 
 
 def test_stage_bf16_copy(gpu):
