@@ -855,9 +855,13 @@ hipError_t launch_grouped_gemm(const GemmArgs& p, int tile_m, int max_tiles, int
     case 64: return launch_shape<Shape<64, 128, 4, 3>, false>(p, max_tiles, quant, stream);
     case 128: {
       // 256-column tiles (8 waves) halve the activation re-reads; 128-column
-      // tiles run two blocks per CU.  MOE_GEMM_WIDE=0 forces the latter.
+      // tiles run two blocks per CU, which measured faster for the MX
+      // schemes (whose MFMA consumes its scales directly: less per-k-step
+      // work to hide the block prologue behind).  MOE_GEMM_WIDE=0 / 1 forces
+      // one or the other.
       static const char* env = getenv("MOE_GEMM_WIDE");
-      const bool wide = env == nullptr || env[0] != '0';
+      const bool mx = quant == kQuantMxfp8 || quant == kSchemeMxfp8W4;
+      const bool wide = env != nullptr ? env[0] != '0' : !mx;
       if (wide && p.Nout % 256 == 0)
         return launch_shape<Shape<128, 256, 8, 3>, false>(p, max_tiles, quant, stream);
       return launch_shape<Shape<128, 128, 4, 2>, false>(p, max_tiles, quant, stream);

@@ -13,8 +13,8 @@
 // One block of 128 threads covers 1024 columns of one token; each thread
 // owns 8 columns (one 16-byte load per routed row, one 16-byte store).  The
 // token's slot rows and weights are block-uniform, so they come in through
-// scalar loads; the top_k row loads of a thread are independent and stay in
-// flight together.
+// scalar loads; the row loads of a thread are issued 8 at a time so that
+// they are in flight together.
 #include "device_common.h"
 #include "kernels.h"
 
@@ -37,25 +37,42 @@ __global__ __launch_bounds__(kReduceThreads) void topk_reduce_kernel(
   if (c >= K) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const float* wt = w + (int64_t)t * k;
-  for (int j = 0; j < k; ++j) {
-    int r;
-    if (slot_row != nullptr) {
-      r = slot_row[(int64_t)t * k + j];
-    } else {
-      const int64_t id = idx[(int64_t)t * k + j];
-      r = (id >= 0 && id < E) ? t * k + j : -1;
+  // slots in groups of 8: the group's row numbers and weights first, then
+  // its row loads all in flight together, then the sums in slot order
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    int r[8];
+    float s[8];
+    uint4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = j0 + u;
+      r[u] = -1;
+      s[u] = 0.0f;
+      if (j < k) {
+        if (slot_row != nullptr) {
+          r[u] = slot_row[(int64_t)t * k + j];
+        } else {
+          const int64_t id = idx[(int64_t)t * k + j];
+          r[u] = (id >= 0 && id < E) ? t * k + j : -1;
+        }
+        s[u] = wt[j];
+      }
     }
-    if (r < 0) continue;
-    const float s = wt[j];
-    const uint4 v = *reinterpret_cast<const uint4*>(down + (int64_t)r * K + c);
-    acc[0] = fmaf(s, bf16_lo(v.x), acc[0]);
-    acc[1] = fmaf(s, bf16_hi(v.x), acc[1]);
-    acc[2] = fmaf(s, bf16_lo(v.y), acc[2]);
-    acc[3] = fmaf(s, bf16_hi(v.y), acc[3]);
-    acc[4] = fmaf(s, bf16_lo(v.z), acc[4]);
-    acc[5] = fmaf(s, bf16_hi(v.z), acc[5]);
-    acc[6] = fmaf(s, bf16_lo(v.w), acc[6]);
-    acc[7] = fmaf(s, bf16_hi(v.w), acc[7]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (r[u] >= 0) v[u] = *reinterpret_cast<const uint4*>(down + (int64_t)r[u] * K + c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (r[u] < 0) continue;
+      acc[0] = fmaf(s[u], bf16_lo(v[u].x), acc[0]);
+      acc[1] = fmaf(s[u], bf16_hi(v[u].x), acc[1]);
+      acc[2] = fmaf(s[u], bf16_lo(v[u].y), acc[2]);
+      acc[3] = fmaf(s[u], bf16_hi(v[u].y), acc[3]);
+      acc[4] = fmaf(s[u], bf16_lo(v[u].z), acc[4]);
+      acc[5] = fmaf(s[u], bf16_hi(v[u].z), acc[5]);
+      acc[6] = fmaf(s[u], bf16_lo(v[u].w), acc[6]);
+      acc[7] = fmaf(s[u], bf16_hi(v[u].w), acc[7]);
+    }
   }
   uint4 o;
   o.x = pack_bf16x2(acc[0], acc[1]);
