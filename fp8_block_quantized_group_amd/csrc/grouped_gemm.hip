@@ -261,45 +261,26 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
 
   // ---- which (expert, m-tile, n-tile) this block computes ----------------
   // Workgroups go to the 8 XCDs round-robin (block L to XCD L % 8).  Each
-  // XCD walks its own contiguous range of the work list, ordered expert by
-  // expert (heaviest first) and, inside an expert, n-tile-major: the
-  // blocks that run together on one XCD share weight tiles (the expert's
-  // m-tiles) and activation tiles (neighbouring n-tiles) in its L2.
-  // Indexed layout: tile b is block b of sorted_ids (n-tile-minor, so an
-  // XCD's range covers whole blocks, each expert's blocks adjacent).
+  // XCD walks its own share of the work, group by group and, inside a group
+  // (one expert's consecutive m-tiles), n-tile-major: the blocks that run
+  // together on one XCD share weight tiles (the group's m-tiles) and
+  // activation tiles (neighbouring n-tiles) in its L2.
+  // Indexed layout: tile b is block b of sorted_ids; XCD x walks the x-th of
+  // 8 equal slices of the (block, n-tile) list, n-tiles innermost.  (Runs of
+  // 8 blocks dealt to the XCDs in turn measured slower: they split the
+  // heavy experts' blocks over more XCDs.)
   const bool indexed = p.sorted_ids != nullptr;
   const int NT = p.Nout / S::BN;
-  const int64_t ntiles =
-      indexed ? (int64_t)min(max(*p.num_padded, 0) / S::BM, p.max_blocks) : (int64_t)p.tile_list[0];
-  const int ngroups = indexed ? 0 : p.tile_list[1];
-  const int64_t work = ntiles * NT;
-  const int64_t per_xcd = (work + 7) / 8;
-  const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (blockIdx.x / 8 >= per_xcd || wl >= work) return;
-  int tile, nt;
-  if (indexed) {
-    tile = __builtin_amdgcn_readfirstlane((int)(wl / NT));
-    nt = __builtin_amdgcn_readfirstlane((int)(wl % NT));
-  } else {
-    // group g with groups[g] <= wl / NT < groups[g+1] (binary search in LDS)
-    int* groups = reinterpret_cast<int*>(smem);
-    for (int i = threadIdx.x; i <= ngroups; i += S::THREADS) groups[i] = p.tile_groups[i];
-    __syncthreads();
-    const int t0 = (int)(wl / NT);
-    int lo = 0, hi = ngroups;   // groups[lo] <= t0 < groups[hi]
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (groups[mid] <= t0) lo = mid; else hi = mid;
-    }
-    const int first = groups[lo], mtiles = groups[lo + 1] - first;
-    const int r = (int)(wl - (int64_t)first * NT);
-    nt = __builtin_amdgcn_readfirstlane(r / mtiles);
-    tile = __builtin_amdgcn_readfirstlane(first + r % mtiles);
-    __syncthreads();
-  }
-  int e, m0, rows_here;
+  int tile, nt, e, m0, rows_here;
   int64_t base;
   if (indexed) {
+    const int64_t nblk = min(max(*p.num_padded, 0) / S::BM, p.max_blocks);
+    const int64_t work = nblk * NT;
+    const int64_t per_xcd = (work + 7) / 8;
+    const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (blockIdx.x / 8 >= per_xcd || wl >= work) return;
+    tile = __builtin_amdgcn_readfirstlane((int)(wl / NT));
+    nt = __builtin_amdgcn_readfirstlane((int)(wl % NT));
     // the block's routed entries (ids below numel) lead, padding follows
     e = __builtin_amdgcn_readfirstlane(p.expert_ids[tile]);
     m0 = 0;
@@ -309,12 +290,24 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     rows_here = __syncthreads_count(valid);
     if ((uint32_t)e >= (uint32_t)p.num_experts) return;
   } else {
-    e = p.tile_list[2 + 2 * tile];
-    m0 = p.tile_list[3 + 2 * tile];
-    int cnt = p.counts[e];
-    if (p.offsets == nullptr) cnt = min(cnt, p.max_tokens);
-    rows_here = min(S::BM, cnt - m0);
-    base = p.offsets != nullptr ? (int64_t)p.offsets[e] : (int64_t)e * p.max_tokens;
+    // Contiguous / batched layouts: XCD x walks the x-th of 8 equal slices
+    // of the schedule the routing step built.  One scalar load of tile t0's
+    // information gives its group (first tile, size), expert, rows and first
+    // row; the block's tile is in the same group, so the rest follows.
+    const int64_t work = (int64_t)p.tile_list[0] * NT;
+    const int64_t per_xcd = (work + 7) / 8;
+    const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+    if (blockIdx.x / 8 >= per_xcd || wl >= work) return;
+    const int t0 = __builtin_amdgcn_readfirstlane((int)(wl / NT));
+    const int32_t* info = p.tile_list + 4 + 8 * (int64_t)t0;
+    const int first = info[2], mtiles = info[3];
+    const int r = (int)(wl - (int64_t)first * NT);
+    nt = __builtin_amdgcn_readfirstlane(r / mtiles);
+    tile = __builtin_amdgcn_readfirstlane(first + r % mtiles);
+    e = info[0];
+    m0 = info[1] + (tile - t0) * S::BM;
+    rows_here = min(S::BM, info[4] - m0);
+    base = info[5];
   }
   const int n0 = nt * S::BN;          // first output column (plain GEMM)
   const int Nh = p.Nout / 2;            // ACT: columns of h
@@ -336,12 +329,41 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   };
 
   // ---- HBM -> LDS copy plan: thread tid fills 16-byte slot i*THREADS + tid
-  const v4i rs_a = buffer_rsrc(p.a, p.a_bytes);
+  // The weight tile needs only the expert and the n-tile: its first k-steps
+  // are issued before the activation rows are looked up (their gather loads
+  // then overlap these copies).
+  const uint32_t smem_base = lds_addr(smem);
+  const int wave_slot = __builtin_amdgcn_readfirstlane(wave * 1024);
   const int wstride = W4 ? p.Kd / 2 : p.Kd;   // weight row bytes
   const v4i rs_b =
       ACT ? buffer_rsrc(p.w + (int64_t)e * p.Nout * wstride,
                         (uint32_t)((int64_t)p.Nout * wstride))
           : buffer_rsrc(p.w + ((int64_t)e * p.Nout + n0) * wstride, (uint32_t)(S::BN * wstride));
+  uint32_t b_off[BI];
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int slot = i * S::THREADS + tid;
+    const int r = W4 ? slot >> 2 : slot >> 3;
+    const int c = W4 ? (slot & 3) ^ key_w4<S::LOG_4TN>(r) : (slot & 7) ^ key_b<S::LOG_4TN>(r);
+    int64_t wrow = r;
+    if (ACT) {
+      // tile row r = 64*w + q: gate row j0 + 32w + q (q < 32), else up row
+      const int q = r & 63, w = r >> 6;
+      wrow = (q < 32 ? 0 : Nh - 32) + j0 + 32 * w + q;
+    }
+    b_off[i] = (uint32_t)(wrow * wstride + c * 16);
+  }
+  auto issue_b = [&](int kb) {
+    const uint32_t st = smem_base + (kb % S::STAGES) * STAGE;
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      dma16(rs_b, st + AB + i * S::THREADS * 16 + wave_slot, b_off[i] + (uint32_t)kb * WROW);
+  };
+#pragma unroll
+  for (int s = 0; s < S::STAGES - 1; ++s)
+    if (s < G) issue_b(s);
+
+  const v4i rs_a = buffer_rsrc(p.a, p.a_bytes);
   const v4i rs_s = buffer_rsrc(p.a_sf, p.a_sf_bytes);
   // A: load instruction q (64 lanes = 8 rows x 8 chunks) belongs to wave
   // q % NW; only instructions covering rows of the expert are issued (rows
@@ -359,20 +381,6 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     const int c = A16 ? (slot % ACH) ^ (r & 15) : (slot & 7) ^ key_a(r);
     a_off[i] = (r < rows_here) ? (uint32_t)(a_row_of(r) * p.Kd * (A16 ? 2 : 1) + c * 16)
                                : kOutOfRange;
-  }
-  uint32_t b_off[BI];
-#pragma unroll
-  for (int i = 0; i < BI; ++i) {
-    const int slot = i * S::THREADS + tid;
-    const int r = W4 ? slot >> 2 : slot >> 3;
-    const int c = W4 ? (slot & 3) ^ key_w4<S::LOG_4TN>(r) : (slot & 7) ^ key_b<S::LOG_4TN>(r);
-    int64_t wrow = r;
-    if (ACT) {
-      // tile row r = 64*w + q: gate row j0 + 32w + q (q < 32), else up row
-      const int q = r & 63, w = r >> 6;
-      wrow = (q < 32 ? 0 : Nh - 32) + j0 + 32 * w + q;
-    }
-    b_off[i] = (uint32_t)(wrow * wstride + c * 16);
   }
   // activation scales: one 4-byte word per row and k-step (UE8M0: the word
   // holding the step's exponent byte; fp32: the scale itself; MX: the step's
@@ -402,18 +410,25 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     }
     wsc_off = (uint32_t)(wrow * Gw);
   }
-  const int wave_slot = __builtin_amdgcn_readfirstlane(wave * 1024);
   const int wave_sc = __builtin_amdgcn_readfirstlane(wave * 256);
-  // weight block scales of this tile's NBLK 128-column blocks, one per k-step
+  // weight block scales of this tile's NBLK 128-column blocks, one per
+  // k-step: wave b copies block b's G floats straight into the LDS panel
+  // (no register round trip, so nothing waits on these loads here: the
+  // first k-step's wait covers them)
   float* sw_panel = reinterpret_cast<float*>(smem + S::STAGES * STAGE);
-  for (int i = tid; i < (MX ? 0 : S::NBLK * G); i += S::THREADS) {
-    const int b = i / G, g = i - b * G;
-    // ACT: block 0 = the gate rows' scale block, block 1 = the up rows'
-    const int blk = ACT ? (b == 0 ? j0 : Nh + j0) / kGroup : n0 / kGroup + b;
-    sw_panel[b * kMaxGroups + g] =
-        ((const float*)p.w_sf)[((int64_t)e * (p.Nout / kGroup) + blk) * G + g];
+  if constexpr (!MX) {
+    if (wave < S::NBLK) {
+      const int b = wave;
+      // ACT: block 0 = the gate rows' scale block, block 1 = the up rows'
+      const int blk = ACT ? (b == 0 ? j0 : Nh + j0) / kGroup : n0 / kGroup + b;
+      const v4i rs_p = buffer_rsrc((const uint8_t*)p.w_sf +
+                                       (((int64_t)e * (p.Nout / kGroup) + blk) * G) * 4,
+                                   (uint32_t)(G * 4));
+      const uint32_t dst = smem_base + S::STAGES * STAGE + b * kMaxGroups * 4;
+      for (int g0 = 0; g0 < G; g0 += 64)
+        dma4(rs_p, dst + g0 * 4, (uint32_t)((g0 + lane) * 4));
+    }
   }
-  __syncthreads();
 
   // ---- per-lane MFMA fragment offsets (within a stage) -------------------
   // The 16x16x128 f8f6f4 MFMA reads lane l's 32 operand bytes as k values
@@ -447,21 +462,18 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int wsc_frag = S::STAGES * STAGE + nl0 * 16;
   const int scale_shift = 8 * kq;            // MX: this lane's 32-column k-group byte
   constexpr int kSubStride = 16 * S::WM;
-  const uint32_t smem_base = lds_addr(smem);
   // the weight-scale block of this lane's output columns (ACT: lanes 0-31
   // hold gate rows, lanes 32-63 up rows)
   const float* sw_mine =
       sw_panel + (ACT ? (kq >= 2 ? 1 : 0) : (wn * S::WAVE_N) / 128) * kMaxGroups;
 
-  auto issue = [&](int kb) {
+  // the rest of a k-step: activation rows, their scales, MX weight scales
+  auto issue_as = [&](int kb) {
     const uint32_t st = smem_base + (kb % S::STAGES) * STAGE;
 #pragma unroll
     for (int i = 0; i < AI; ++i)
       if (i < a_loads)
         dma16(rs_a, st + i * S::THREADS * 16 + wave_slot, a_off[i] + (uint32_t)kb * AROW);
-#pragma unroll
-    for (int i = 0; i < BI; ++i)
-      dma16(rs_b, st + AB + i * S::THREADS * 16 + wave_slot, b_off[i] + (uint32_t)kb * WROW);
     if (loads_sc) {
       const uint32_t soff = UE8M0 ? (uint32_t)(kb & ~3) : (uint32_t)kb * 4;
       dma4(rs_s, st + SC_OFF + wave_sc, sc_off + soff);
@@ -469,6 +481,14 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     if (loads_wsc && (kb & 3) == 0)
       dma16(rs_w, smem_base + S::STAGES * STAGE + ((kb >> 2) & 1) * WSC_SLOT + wave_slot,
             wsc_off + (uint32_t)kb * 4);
+  };
+  auto issue = [&](int kb) {
+    issue_as(kb);
+    issue_b(kb);
+  };
+  // loads of k-step s that the prologue issues after every weight copy
+  auto as_loads = [&](int s) {
+    return a_loads + (loads_sc ? 1 : 0) + (loads_wsc && (s & 3) == 0 ? 1 : 0);
   };
 
   v4f acc[S::TN][S::TM];
@@ -622,15 +642,22 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   };
 
   auto main_loop = [&](auto live_c) {
-    // prologue: STAGES-1 k-steps in flight
+    // prologue: STAGES-1 k-steps in flight (their weight copies went first)
 #pragma unroll
     for (int s = 0; s < S::STAGES - 1; ++s)
-      if (s < G) issue(s);
+      if (s < G) issue_as(s);
     for (int kb = 0; kb < G; ++kb) {
       // k-step kb has landed for every wave, and every wave's reads of
       // k-step kb-1 (whose slot the next issue reuses) have completed
       const int after = min(kb + S::STAGES - 2, G - 1) - kb;
-      if constexpr (MX) {
+      if (kb < S::STAGES - 2) {
+        // loads issued after k-step kb's last one: the activation parts of
+        // the later prologue k-steps and the whole k-steps issued since
+        int n = 0;
+        for (int s2 = kb + 1; s2 <= kb + after; ++s2)
+          n += as_loads(s2) + (s2 < S::STAGES - 1 ? 0 : BI);
+        wait_n_then_barrier<3 * LMAX>(n);
+      } else if constexpr (MX) {
         // later stages in flight, plus the panel loads among them
         int n = after * loads_per_stage;
         if (loads_wsc)

@@ -47,14 +47,13 @@ struct GemmArgs {
   uint8_t* act_q;            // fused activation: fp8 [rows, Nout/2]
   uint8_t* act_sf;           //   and its per-128 scales (UE8M0 bytes or fp32)
   int act_sf_row;            //   scale row length: bytes (UE8M0) or floats (fp32)
-  const int32_t* tile_list;  // [0] tile count, [1] group count G, then (expert, m0) pairs
-  const int32_t* tile_groups;  // [G+1] first tile of each group (one expert's
-                               // consecutive m-tiles), in XCD-balanced order
+  // [0] tile count, [1] group count, [2..3] 0, then per tile 8 ints: expert, first
+  // row within the expert, first tile and size of its group (one expert's
+  // consecutive m-tiles, groups in XCD-balanced order), the expert's rows
+  // and its first row in the GEMM's row space (contiguous offset or slab)
+  const int32_t* tile_list;
   int num_experts;
-  const int32_t* counts;     // [E] rows per expert
-  const int32_t* offsets;    // [E+1] contiguous row base, nullptr for batched slabs
   const int32_t* row_src;    // A row gather (w13 on the contiguous layout) or nullptr
-  int max_tokens;            // batched slab rows
   // indexed layout (sorted_ids != nullptr): tile b is the block of BM rows
   // [b*BM, (b+1)*BM) of sorted_ids, of expert expert_ids[b]; entries not
   // below numel are padding and come after the block's routed entries.

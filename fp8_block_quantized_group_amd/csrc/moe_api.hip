@@ -176,9 +176,10 @@ Plan make_plan(const moe_problem_t* p) {
   }
   pl.s.padded_rows = indexed(p) ? padded_capacity(p, bm) : pl.s.expert_rows;
   pl.s.blocks = indexed(p) ? pl.s.padded_rows / bm : 0;
-  // count, group count, (expert, m0) pairs, group offsets (at most one group
-  // per expert plus one per 8 tiles, so E + max_tiles + 1 is a safe bound)
-  pl.s.tile_list = 2 + 2 * pl.max_tiles + (E + pl.max_tiles + 1);
+  // count, group count, 8 ints of per-tile information, group offsets (at
+  // most one group per expert plus one per 8 tiles, so E + max_tiles + 1 is
+  // a safe bound)
+  pl.s.tile_list = 4 + 8 * pl.max_tiles + (E + pl.max_tiles + 1);
   const bool mx = p->act_quant == MOE_Q_MXFP8;
   const bool bf = p->act_quant == MOE_Q_BF16;
   pl.s.x_sf_row = bf ? 0 : mx ? K / 32 : ue ? 4 * ((GK + 3) / 4) : GK;
@@ -262,7 +263,7 @@ moe_status_t check_routing(const moe_routing_t* r) {
   CHECK(check_ptr(r->expert_offsets, "routing.expert_offsets", 4));
   CHECK(check_ptr(r->row_src, "routing.row_src", 4));
   CHECK(check_ptr(r->slot_row, "routing.slot_row", 4));
-  CHECK(check_ptr(r->tile_list, "routing.tile_list", 4));
+  CHECK(check_ptr(r->tile_list, "routing.tile_list", 16));
   return MOE_OK;
 }
 
@@ -370,11 +371,7 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
     max_tiles = g.max_blocks;
   } else {
     g.tile_list = r->tile_list;
-    g.tile_groups = r->tile_list + 2 + 2 * pl.max_tiles;
-    g.counts = r->expert_num_tokens;
-    g.offsets = batched(p) ? nullptr : r->expert_offsets;
     g.row_src = (w13 && !batched(p)) ? r->row_src : nullptr;
-    g.max_tokens = p->max_tokens_per_expert;
   }
   g.Kd = w13 ? p->hidden : p->intermediate;
   g.Nout = w13 ? (int)w13_rows(p) : p->hidden;

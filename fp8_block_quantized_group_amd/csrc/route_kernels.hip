@@ -124,6 +124,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   __shared__ int chunk_e[kChunkCap], chunk_m[kChunkCap], chunk_n[kChunkCap];
   __shared__ int chunk_bin[kChunkCap], chunk_off[kChunkCap], chunk_idx[kChunkCap];
   __shared__ int bin_load[8], bin_cnt[8];
+  __shared__ int exp_rows[1024], exp_base[1024];   // per expert: GEMM rows, first row
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E) {
@@ -149,6 +150,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     expert_num_tokens[e] = counts_in != nullptr ? rows : cnt;
     if (e == E - 1) expert_offsets[E] = incl;
   }
+  exp_rows[e] = rows;
+  exp_base[e] = counts_in != nullptr ? e * max_tokens : incl - cnt;
   const int incl_nt = block_inclusive_scan(nt, buf);
   // the last thread's inclusive value is the total: broadcast it
   if (e == 1023) buf[0] = incl_nt;
@@ -247,8 +250,8 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     }
   }
   __syncthreads();
-  int32_t* pairs = tile_list + 2;
-  int32_t* group_off = tile_list + 2 + 2 * max_tiles;
+  int32_t* info = tile_list + 4;                     // 16-byte aligned
+  int32_t* group_off = tile_list + 4 + 8 * max_tiles;
   for (int i = e; i < nchunks; i += 1024) {
     const int x = chunk_bin[i];
     int tile0 = chunk_off[i], g = chunk_idx[i];
@@ -257,14 +260,20 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
       g += bin_cnt[y];
     }
     group_off[g] = tile0;
-    for (int t = 0; t < chunk_n[i]; ++t) {
-      pairs[2 * (tile0 + t)] = chunk_e[i];
-      pairs[2 * (tile0 + t) + 1] = (chunk_m[i] + t) * tile_m;
+    const int ex = chunk_e[i], n = chunk_n[i];
+    for (int t = 0; t < n; ++t) {
+      // expert, first row, its group's first tile and size, the expert's
+      // rows and first row in the GEMM's row space
+      int4* d = reinterpret_cast<int4*>(info + 8 * (tile0 + t));
+      d[0] = make_int4(ex, (chunk_m[i] + t) * tile_m, tile0, n);
+      d[1] = make_int4(exp_rows[ex], exp_base[ex], 0, 0);
     }
   }
   if (e == 0) {
     tile_list[0] = total;
     tile_list[1] = nchunks;
+    tile_list[2] = 0;
+    tile_list[3] = 0;
     group_off[nchunks] = total;
   }
 }

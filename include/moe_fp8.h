@@ -159,13 +159,16 @@ typedef struct {
  *  row_src           [T*top_k] token of each contiguous row (contiguous layout)
  *  slot_row          [T*top_k] row of (token, slot), -1 when unrouted;
  *                    batched: e * max_tokens + rank (rank >= max_tokens -> -1)
- *  tile_list         [moe_sizes_t.tile_list] M-tile schedule for the GEMMs:
- *                    tile count n, group count G, n (expert, first row)
- *                    pairs, then G + 1 group offsets; a group is a run of at
- *                    most 8 consecutive m-tiles of one expert (more only for
- *                    very large batches), and the groups are ordered so that
- *                    8 equal slices of the list hold similar work and weight
- *                    bytes (one slice per XCD) */
+ *  tile_list         [moe_sizes_t.tile_list] M-tile schedule for the GEMMs
+ *                    (16-byte aligned): tile count n, group count G, two
+ *                    zeros, per tile 8 ints (expert, first row within the
+ *                    expert, first tile and size of its group, the expert's
+ *                    rows, its first row, two zeros), then G + 1 group
+ *                    offsets; a group is a run of at most 8 consecutive
+ *                    m-tiles of one expert (more only for very large
+ *                    batches), and the groups are ordered so that 8 equal
+ *                    slices of the list hold similar work and weight bytes
+ *                    (one slice per XCD) */
 typedef struct {
   int32_t* expert_num_tokens;
   int32_t* expert_offsets;

@@ -72,7 +72,10 @@ def test_full_size_sampled(name):
     if cfg.eplb:
         assert np.array_equal(to_np(inp["eplb"]["expert_load"]), st["load"])
     counts = st["counts"] if cfg.layout != "batched" else np.minimum(st["counts"], cfg.max_tokens)
-    check_schedule(bufs["tile_list"], counts, moe.sizes(moe.Problem.from_config(cfg)), cfg.E)
+    bases = ([e * cfg.max_tokens for e in range(cfg.E)] if cfg.layout == "batched"
+             else st["offsets"][:-1])
+    check_schedule(bufs["tile_list"], counts, moe.sizes(moe.Problem.from_config(cfg)), cfg.E,
+                   bases)
     # quantized hidden rows of a token sample, bit-exact
     rng = np.random.default_rng(cfg.seed + 100)
     ue, grp = O.act_e8m0(cfg), O.act_group(cfg)

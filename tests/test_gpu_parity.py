@@ -114,23 +114,25 @@ def stage_on_gpu(cfg, dev):
 
 
 def _max_tiles(n_entries, E):
-    # n_entries = 2 + 2 * max_tiles + E + max_tiles + 1
-    return (n_entries - 3 - E) // 3
+    # n_entries = 4 + 8 * max_tiles + E + max_tiles + 1
+    return (n_entries - 5 - E) // 9
 
 
-def host_tile_list(counts, tile_m, n_entries):
+def host_tile_list(counts, tile_m, n_entries, bases):
     """Every (expert, m0) tile in plain expert order, one group per expert
     (test plumbing: the GEMM must not depend on the order the routing step
-    emits)."""
+    emits).  bases: each expert's first row in the GEMM's row space."""
     E = len(counts)
     max_tiles = _max_tiles(n_entries, E)
     tl = np.zeros(n_entries, np.int32)
-    groups = tl[2 + 2 * max_tiles:]
+    info = tl[4:4 + 8 * max_tiles].reshape(max_tiles, 8)
+    groups = tl[4 + 8 * max_tiles:]
     pos = 0
     for e, c in enumerate(counts):
         groups[e] = pos
+        first, n = pos, -(-int(c) // tile_m)
         for m0 in range(0, int(c), tile_m):
-            tl[2 + 2 * pos], tl[3 + 2 * pos] = e, m0
+            info[pos] = (e, m0, first, n, int(c), int(bases[e]), 0, 0)
             pos += 1
     groups[E] = pos
     tl[0], tl[1] = pos, E
@@ -175,7 +177,10 @@ def oracle_routing(p, cfg, ref):
         "expert_offsets": to_dev(ref["offsets"].astype(np.int32)),
         "row_src": to_dev(row_src),
         "slot_row": to_dev(ref["slot_row"].reshape(-1).astype(np.int32)),
-        "tile_list": to_dev(host_tile_list(ref["counts"], s["tile_m"], s["tile_list"])),
+        "tile_list": to_dev(host_tile_list(
+            ref["counts"], s["tile_m"], s["tile_list"],
+            [e * cfg.max_tokens for e in range(cfg.E)] if cfg.layout == "batched"
+            else ref["offsets"][:-1])),
     }
 
 
@@ -295,29 +300,36 @@ def test_stage_and_route_bit_exact(gpu, name):
     assert np.array_equal(to_np(bufs["slot_row"]).reshape(cfg.T, cfg.top_k), ref["slot_row"])
     if cfg.eplb:
         assert np.array_equal(to_np(dev["eplb"]["expert_load"]), ref["load"])
-    check_schedule(bufs["tile_list"], ref["counts"], moe.sizes(p), cfg.E)
+    bases = ([e * cfg.max_tokens for e in range(cfg.E)] if cfg.layout == "batched"
+             else ref["offsets"][:-1])
+    check_schedule(bufs["tile_list"], ref["counts"], moe.sizes(p), cfg.E, bases)
 
 
-def check_schedule(tile_list, counts, s, E):
+def check_schedule(tile_list, counts, s, E, bases):
     """The tile schedule: every expert's tiles exactly once, in the
     documented XCD-balanced order, groups of consecutive m-tiles of one
-    expert."""
+    expert, and each tile's information (group, expert rows, first row)."""
     tl = to_np(tile_list)
     n, G = int(tl[0]), int(tl[1])
+    assert tl[2] == 0 and tl[3] == 0
     bm = s["tile_m"]
-    pairs = tl[2:2 + 2 * n].reshape(n, 2)
+    max_tiles = _max_tiles(s["tile_list"], E)
+    info = tl[4:4 + 8 * n].reshape(n, 8)
     tiles = [-(-int(c) // bm) for c in counts]
     seq, sizes = expected_schedule(tiles)
-    assert [(int(e), int(m0) // bm) for e, m0 in pairs] == seq
-    assert np.all(pairs[:, 1] % bm == 0)
-    max_tiles = _max_tiles(s["tile_list"], E)
-    groups = tl[2 + 2 * max_tiles:2 + 2 * max_tiles + G + 1]
+    assert [(int(e), int(m0) // bm) for e, m0 in info[:, :2]] == seq
+    assert np.all(info[:, 1] % bm == 0)
+    groups = tl[4 + 8 * max_tiles:4 + 8 * max_tiles + G + 1]
     assert G == len(sizes) and groups[0] == 0 and groups[-1] == n
     assert list(np.diff(groups)) == sizes
     for g in range(G):
-        seg = pairs[groups[g]:groups[g + 1]]
+        seg = info[groups[g]:groups[g + 1]]
         assert np.all(seg[:, 0] == seg[0, 0])
         assert list(seg[:, 1]) == list(range(int(seg[0, 1]), int(seg[0, 1]) + len(seg) * bm, bm))
+        assert np.all(seg[:, 2] == groups[g]) and np.all(seg[:, 3] == len(seg))
+        e = int(seg[0, 0])
+        assert np.all(seg[:, 4] == int(counts[e])) and np.all(seg[:, 5] == int(bases[e]))
+        assert np.all(seg[:, 6:] == 0)
 
 
 def test_stage_bf16_copy(gpu):
