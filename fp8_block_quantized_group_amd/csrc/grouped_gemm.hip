@@ -697,19 +697,26 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
         for (int ii = 0; ii < 2; ++ii) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const float lo = __uint_as_float(f32_to_bf16_bits(acc[ii][j][r]) << 16);
-            const float hi = __uint_as_float(f32_to_bf16_bits(acc[ii + 2][j][r]) << 16);
-            const float recv = __shfl_xor(gate_lane ? hi : lo, 32);
-            const float g = gate_lane ? lo : recv;
-            const float u = gate_lane ? recv : hi;
-            const float v = f(g, u);
+            // swapping the upper half-wave of lo with the lower half-wave of
+            // hi leaves, in every lane, its gate value in the first result
+            // and its up value in the second (gate lanes keep lo and take the
+            // partner's lo; up lanes take the partner's hi and keep hi)
+            const uint32_t lo = f32_to_bf16_bits(acc[ii][j][r]) << 16;
+            const uint32_t hi = f32_to_bf16_bits(acc[ii + 2][j][r]) << 16;
+            const auto gu = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
+            const float v = f(__uint_as_float(gu[0]), __uint_as_float(gu[1]));
             h[j][4 * ii + r] = v;
             amax[j] = fmaxf(amax[j], fabsf(v));
           }
         }
         // the 4 lanes of this row in the wave: rho, rho + 16, rho + 32, rho + 48
-        amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 16));
-        amax[j] = fmaxf(amax[j], __shfl_xor(amax[j], 32));
+        // (each swap leaves the lane's own value and its partner's)
+        const auto m16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(amax[j]),
+                                                          __float_as_uint(amax[j]), false, false);
+        amax[j] = fmaxf(__uint_as_float(m16[0]), __uint_as_float(m16[1]));
+        const auto m32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(amax[j]),
+                                                          __float_as_uint(amax[j]), false, false);
+        amax[j] = fmaxf(__uint_as_float(m32[0]), __uint_as_float(m32[1]));
       }
     };
     // SiLU gets its own unrolled copy (no per-element branch); the other
