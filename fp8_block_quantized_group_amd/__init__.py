@@ -197,9 +197,9 @@ def scale_dtype(p: Problem):
 def alloc_act_outputs(p: Problem, device="cuda", rows: Optional[int] = None):
     """(a2_q, a2_sf) for the w2 input: fp8 codes and scales, or bf16 values
     and None for unquantized activations; ``rows`` defaults to the layout's
-    a2 rows (the indexed layout's padded capacity)."""
+    expert rows."""
     s = sizes(p)
-    rows = s["padded_rows"] if rows is None else rows
+    rows = s["expert_rows"] if rows is None else rows
     if p.act_quant == Q_BF16:
         return torch.empty((rows, p.intermediate), dtype=torch.bfloat16, device=device), None
     return (torch.empty((rows, p.intermediate), dtype=torch.uint8, device=device),

@@ -327,6 +327,14 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     if (p.gather_sorted) return (int64_t)((uint32_t)p.sorted_ids[r] / (uint32_t)p.top_k);
     return p.row_src != nullptr ? (int64_t)p.row_src[r] : r;
   };
+  // output row of tile row m, or -1 for a padding entry of the indexed layout
+  // (which writes row sorted_ids[position], the (token, slot) order)
+  auto out_row_of = [&](int m) -> int64_t {
+    const int64_t r = base + m0 + m;
+    if (!p.scatter_sorted) return r;
+    const uint32_t id = (uint32_t)p.sorted_ids[r];
+    return id < (uint32_t)p.numel ? (int64_t)id : -1;
+  };
 
   // ---- HBM -> LDS copy plan: thread tid fills 16-byte slot i*THREADS + tid
   // The weight tile needs only the expert and the n-tile: its first k-steps
@@ -731,7 +739,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       for (int j = 0; j < S::TM; ++j) {
         const int ml = ml0 + kSubStride * j;
         if (ml >= rows_here) continue;
-        const int64_t row = base + m0 + ml;
+        const int64_t row = out_row_of(ml);
+        if (row < 0) continue;
         *reinterpret_cast<uint4*>(p.act_q + (row * Nh + j0 + col_off) * 2) =
             make_uint4(pack_bf16x2(h[j][0], h[j][1]), pack_bf16x2(h[j][2], h[j][3]),
                        pack_bf16x2(h[j][4], h[j][5]), pack_bf16x2(h[j][6], h[j][7]));
@@ -764,7 +773,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
                             h[j][3] * gs.recip);
       q.y = f32x4_to_e4m3x4(h[j][4] * gs.recip, h[j][5] * gs.recip, h[j][6] * gs.recip,
                             h[j][7] * gs.recip);
-      const int64_t row = base + m0 + ml;
+      const int64_t row = out_row_of(ml);
+      if (row < 0) continue;
       *reinterpret_cast<uint2*>(p.act_q + row * Nh + j0 + col_off) = q;
       if (kq == 0 && (MX || wn == 0)) {
         if (UE8M0 || MX) {
@@ -786,12 +796,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     for (int j = 0; j < S::TM; ++j) {
       const int ml = ml0 + kSubStride * j;
       if (ml >= rows_here) continue;
-      int64_t row = base + m0 + ml;
-      if (p.scatter_sorted) {
-        const uint32_t id = (uint32_t)p.sorted_ids[row];
-        if (id >= (uint32_t)p.numel) continue;
-        row = id;
-      }
+      const int64_t row = out_row_of(ml);
+      if (row < 0) continue;
       uint16_t* dst = p.out + row * (int64_t)p.Nout + n_first;
       uint32_t packed[2 * S::TN];
 #pragma unroll

@@ -57,16 +57,15 @@ struct GemmArgs {
   // indexed layout (sorted_ids != nullptr): tile b is the block of BM rows
   // [b*BM, (b+1)*BM) of sorted_ids, of expert expert_ids[b]; entries not
   // below numel are padding and come after the block's routed entries.
-  // tile_list / counts / offsets / row_src unused; the ACT output rows are
-  // the sorted positions.
+  // tile_list / row_src unused.
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
   const int32_t* num_padded;       // [1] device: the padded total
   int max_blocks;                  // blocks of sorted_ids (bounds *num_padded)
-  int top_k;
+  int top_k;                       // w13: the routing's top_k; w2: 1
   int numel;                       // T * top_k
-  int gather_sorted;               // A row = sorted_ids[pos] / top_k (w13); else pos
-  int scatter_sorted;              // output row = sorted_ids[pos] (w2); else pos
+  int gather_sorted;               // A row = sorted_ids[pos] / top_k; else pos
+  int scatter_sorted;              // output row = sorted_ids[pos] (padding skipped)
   int activation;             // ACT epilogue: a gated activation kind (moe_act_t)
   int Kd;                    // reduction length, multiple of 128
   int Nout;                  // output columns, multiple of 128

@@ -123,11 +123,9 @@ moe_status_t validate_problem(const moe_problem_t* p) {
     const int64_t rows = batched(p) ? (int64_t)p->num_experts * p->max_tokens_per_expert
                                     : (int64_t)p->num_tokens * p->top_k;
     const int64_t in_rows = batched(p) ? rows : p->num_tokens;
-    // the indexed layout's w2 input has padded rows (blocks of up to 256)
-    const int64_t a2_rows = indexed(p) ? padded_capacity(p, 256) : rows;
     const int64_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
     if (in_rows * p->hidden * elem >= ((int64_t)7 << 29) ||
-        a2_rows * p->intermediate * elem >= ((int64_t)7 << 29))
+        rows * p->intermediate * elem >= ((int64_t)7 << 29))
       return fail(MOE_ERR_UNSUPPORTED, "activation buffers are limited to 3.5 GiB");
   }
   if (p->act_quant < MOE_Q_FP8_UE8M0 || p->act_quant > MOE_Q_MXFP8)
@@ -190,10 +188,10 @@ Plan make_plan(const moe_problem_t* p) {
   pl.x_q_bytes = (size_t)pl.s.stage_rows * K * elem;
   const size_t sfb = p->act_quant == MOE_Q_FP8_F32 ? 4 : 1;
   pl.x_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.stage_rows * pl.s.x_sf_row * sfb;
-  pl.a2_q_bytes = (size_t)pl.s.padded_rows * N * elem;
-  pl.a2_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.padded_rows * pl.s.a2_sf_row * sfb;
+  pl.a2_q_bytes = (size_t)pl.s.expert_rows * N * elem;
+  pl.a2_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.expert_rows * pl.s.a2_sf_row * sfb;
   pl.down_bytes = (size_t)pl.s.expert_rows * K * 2;
-  pl.gate_up_bytes = gated(p) ? 0 : (size_t)pl.s.padded_rows * N * 2;
+  pl.gate_up_bytes = gated(p) ? 0 : (size_t)pl.s.expert_rows * N * 2;
   return pl;
 }
 
@@ -322,7 +320,9 @@ moe_status_t run_stage(const moe_problem_t* p, const Plan& pl, const void* hidde
   return launch_status(err, "route");
 }
 
-// The indexed layout's block map (moe_align_block_size outputs).
+// The indexed layout's block map (moe_align_block_size outputs).  Both
+// GEMMs write their rows in (token, slot) order, row sorted_ids[position]:
+// w13 reads activation row id / top_k, w2 reads w13's row id.
 struct Indexed {
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
@@ -331,9 +331,7 @@ struct Indexed {
 };
 
 // w13 with act: out unused, the activation goes to act_q / act_sf.  ix: the
-// indexed layout (r unused then): w13 gathers rows sorted_ids / top_k and
-// writes sorted positions, w2 reads sorted positions and writes rows
-// sorted_ids.
+// indexed layout (r unused then).
 moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const void* a_q,
                       const void* a_sf, const moe_routing_t* r, const void* w, const void* w_sf,
                       void* out, hipStream_t stream, bool act = false, void* act_q = nullptr,
@@ -342,14 +340,12 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
   const size_t sfb = p->act_quant == MOE_Q_FP8_F32 ? 4 : 1;
   const size_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
   const int64_t cap = ix != nullptr ? padded_capacity(p, ix->block_size) : 0;
+  (void)elem;
   g.a = (const uint8_t*)a_q;
-  g.a_bytes = (uint32_t)(w13 ? pl.x_q_bytes
-                         : ix != nullptr ? (size_t)cap * p->intermediate * elem
-                                         : pl.a2_q_bytes);
+  g.a_bytes = (uint32_t)(w13 ? pl.x_q_bytes : pl.a2_q_bytes);
   g.a_sf = a_sf;
   g.a_sf_stride = (int)(w13 ? pl.s.x_sf_row : pl.s.a2_sf_row);
-  g.a_sf_bytes = (uint32_t)((w13 ? pl.s.stage_rows : ix != nullptr ? cap : pl.s.expert_rows) *
-                            g.a_sf_stride * sfb);
+  g.a_sf_bytes = (uint32_t)((w13 ? pl.s.stage_rows : pl.s.expert_rows) * g.a_sf_stride * sfb);
   g.w = (const uint8_t*)w;
   g.w_sf = w_sf;
   g.out = (uint16_t*)out;
@@ -363,10 +359,10 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
     g.expert_ids = ix->expert_ids;
     g.num_padded = ix->num_padded;
     g.max_blocks = (int)(cap / ix->block_size);
-    g.top_k = p->top_k;
+    g.top_k = w13 ? p->top_k : 1;
     g.numel = p->num_tokens * p->top_k;
-    g.gather_sorted = w13 ? 1 : 0;
-    g.scatter_sorted = w13 ? 0 : 1;
+    g.gather_sorted = 1;
+    g.scatter_sorted = 1;
     tile_m = ix->block_size;
     max_tiles = g.max_blocks;
   } else {
@@ -384,13 +380,15 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
 
 // num_rows: device row count for the contiguous / indexed layouts (nullptr:
 // the expert offsets' total); the batched layout uses the slab counts.
+// slot_order: the indexed layout's (token, slot)-ordered rows, all T*k of
+// them (rows of unrouted slots hold whatever was there and are never read)
 moe_status_t run_act(const moe_problem_t* p, const Plan& pl, const void* gate_up,
                      const moe_routing_t* r, void* a2_q, void* a2_sf, hipStream_t stream,
-                     const int32_t* num_rows = nullptr) {
+                     bool slot_order = false) {
   const bool b = batched(p);
-  if (num_rows == nullptr && !b) num_rows = r->expert_offsets + p->num_experts;
+  const int32_t* num_rows = b || slot_order ? nullptr : r->expert_offsets + p->num_experts;
   const hipError_t err = moe::launch_act_requant(
-      gate_up, a2_q, a2_sf, pl.s.padded_rows, p->intermediate, p->act_quant, num_rows,
+      gate_up, a2_q, a2_sf, pl.s.expert_rows, p->intermediate, p->act_quant, num_rows,
       b ? r->expert_num_tokens : nullptr, p->max_tokens_per_expert, p->activation, stream);
   return launch_status(err, "act_requant");
 }
@@ -431,9 +429,6 @@ moe_status_t check_indexed(const moe_problem_t* p, const int32_t* sorted_ids,
     return fail(MOE_ERR_UNSUPPORTED, "the indexed layout needs the contiguous routing");
   if (!valid_block_size(p, bs))
     return fail(MOE_ERR_UNSUPPORTED, "block_size %d is not a GEMM tile height", bs);
-  const int64_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
-  if (padded_capacity(p, bs) * p->intermediate * elem >= ((int64_t)7 << 29))
-    return fail(MOE_ERR_UNSUPPORTED, "activation buffers are limited to 3.5 GiB");
   CHECK(check_ptr(sorted_ids, "sorted_ids", 4));
   CHECK(check_ptr(expert_ids, "expert_ids", 4));
   CHECK(check_ptr(num_padded, "num_tokens_padded", 4));
@@ -675,7 +670,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
     } else {
       CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, nullptr, w13, w13_sf, w.gate_up, s, false,
                      nullptr, nullptr, &ix));
-      CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s, w.num_padded));
+      CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s, true));
     }
     CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, nullptr, w2, w2_sf, w.down, s, false, nullptr,
                    nullptr, &ix));

@@ -184,8 +184,7 @@ typedef struct {
   int64_t expert_rows;     /* rows of gate_up / a2 / down                     */
   int64_t x_sf_row;        /* x_sf row length: bytes (UE8M0) / floats (fp32)  */
   int64_t a2_sf_row;       /* a2_sf row length, same units                    */
-  int64_t padded_rows;     /* rows of a2 (indexed: sorted_ids capacity; else
-                              expert_rows)                                    */
+  int64_t padded_rows;     /* indexed: sorted_ids capacity; else expert_rows  */
   int64_t blocks;          /* indexed: expert_ids capacity; else 0            */
   int32_t tile_m;          /* activation rows per GEMM tile (indexed: the
                               block size moe_forward uses)                    */
@@ -295,21 +294,24 @@ moe_status_t moe_align_block_size(const moe_problem_t* p, const int64_t* topk_id
                                   int32_t* num_tokens_padded, void* stream);
 
 /* Steps 3 + 4 on the block map: for every routed position q (sorted_ids[q]
- * = s < T*k), a2 row q = the fused w13 + activation of moe_grouped_gemm_w13_act
+ * = s < T*k), a2 row s = the fused w13 + activation of moe_grouped_gemm_w13_act
  * applied to activation row s / top_k with the weights of expert
- * expert_ids[q / block_size].  a2_q [capacity, N] (fp8, or bf16 for bf16
- * activations), a2_sf per the activation scheme with capacity rows; padding
- * positions are not written.  The routed entries of every block must precede
- * its padding (as moe_align_block_size writes them); *num_tokens_padded is
- * clamped to the capacity. */
+ * expert_ids[q / block_size].  a2 is in (token, slot) order: a2_q [T*top_k,
+ * N] (fp8, or bf16 for bf16 activations), a2_sf per the activation scheme
+ * with T*top_k rows; rows of unrouted slots are not written.  The routed
+ * entries of every block must precede its padding (as moe_align_block_size
+ * writes them); *num_tokens_padded is clamped to the capacity. */
 moe_status_t moe_grouped_gemm_w13_act_indexed(
     const moe_problem_t* p, const void* a_q, const void* a_sf, const int32_t* sorted_ids,
     const int32_t* expert_ids, const int32_t* num_tokens_padded, int32_t block_size,
     const void* w13, const void* w13_sf, void* a2_q, void* a2_sf, void* stream);
 
-/* Step 5 on the block map: down[s] = the w2 GEMM of a2 row q for every routed
- * position q with s = sorted_ids[q]; down bf16 [T*top_k, K] in (token, slot)
- * order; rows of unrouted slots are not written. */
+/* Step 5 on the block map: down[s] = the w2 GEMM of a2 row s for every routed
+ * position q with s = sorted_ids[q] (the experts run w2 with top_k 1 on the
+ * (token, slot)-ordered w13 output, so its block map may be another one, of
+ * another block size, from moe_align_block_size on the same routing); down
+ * bf16 [T*top_k, K] in (token, slot) order; rows of unrouted slots are not
+ * written. */
 moe_status_t moe_grouped_gemm_w2_indexed(
     const moe_problem_t* p, const void* a2_q, const void* a2_sf, const int32_t* sorted_ids,
     const int32_t* expert_ids, const int32_t* num_tokens_padded, int32_t block_size,

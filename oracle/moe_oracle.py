@@ -642,10 +642,11 @@ def forward(h: dict) -> dict:
 
 
 def forward_indexed(h: dict, block_size: int) -> dict:
-    """The layer in the indexed layout ([HUM] HummingIndexedExperts.apply):
-    align, w13 on the rows of sorted_ids (activation row = id // top_k) into
-    an intermediate in sorted order, the activation, w2 written back to row
-    id (the (token, slot) order), then the fused mul-sum.  Per row the
+    """The layer in the indexed layout ([HUM] HummingIndexedExperts.apply and
+    prepare_humming_moe_kwargs): align, w13 on the rows of sorted_ids
+    (activation row = id // top_k) written to row id of an intermediate in
+    (token, slot) order, the activation, w2 on that intermediate (top_k 1:
+    row id) written back to row id, then the fused mul-sum.  Per row the
     arithmetic is the contiguous layout's, so the output must be identical."""
     cfg = h["cfg"]
     assert cfg.layout != "batched"
@@ -654,7 +655,7 @@ def forward_indexed(h: dict, block_size: int) -> dict:
     sorted_ids, expert_ids, P = align_block_size(st["ids"], E, block_size)
     numel = cfg.T * k
     bf16_act = cfg.act_quant == "bf16"
-    a2_rows = np.zeros((P, N), dtype=np.uint16 if bf16_act else np.uint8)
+    a2_rows = np.zeros((numel, N), dtype=np.uint16 if bf16_act else np.uint8)
     down = np.zeros((numel, K), dtype=np.uint16)
     for b, e in enumerate(expert_ids):
         pos = np.arange(b * block_size, (b + 1) * block_size)
@@ -667,7 +668,7 @@ def forward_indexed(h: dict, block_size: int) -> dict:
         x_sf = None if st["x_sf"] is None else st["x_sf"][tokens]
         gu = bf16_round(expert_gemm(cfg, st["x_q"][tokens], x_sf, h["w13"][e], h["w13_sf"][e]))
         q2, s2 = act_step(cfg, gu)
-        a2_rows[pos[live]] = q2
+        a2_rows[slots] = q2
         dn = expert_gemm(cfg, q2, s2, h["w2"][e], h["w2_sf"][e])
         down[slots] = bf16_round(dn)
     out = fused_mul_sum(down, st["ids"], st["weights"], E)

@@ -188,7 +188,7 @@ def test_empty_batch_is_a_noop(lib):
 
 
 def test_indexed_sizes(lib):
-    # the indexed layout: a2 has the padded capacity, down stays T*k rows
+    # the indexed layout: sorted_ids has the padded capacity, a2 and down T*k rows
     for name, cfg in moe_synth.INDEXED_CONFIGS.items():
         p = moe.Problem.from_config(cfg)
         assert p.layout == moe.LAYOUT_INDEXED
@@ -199,7 +199,8 @@ def test_indexed_sizes(lib):
         assert s["expert_rows"] == slots
         assert moe.align_capacity(p, bm) == (cap, cap // bm)
         ws = moe.workspace_size(p)
-        assert ws >= s["stage_rows"] * cfg.K + cap * cfg.N + slots * cfg.K * 2 + cap * 4
+        # a2 and down in (token, slot) order, plus the block map
+        assert ws >= s["stage_rows"] * cfg.K + slots * cfg.N + slots * cfg.K * 2 + cap * 4
 
 
 @pytest.mark.parametrize("T,E,k,bs,seed", [(1, 4, 1, 16, 0), (37, 8, 3, 16, 1),

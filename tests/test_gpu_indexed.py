@@ -3,11 +3,12 @@ gather / scatter GEMMs on the block map and moe_fused_mul_sum) against the
 oracle's align_block_size / forward_indexed, through the C ABI.
 
 The block map is integer work: compared bit for bit.  Per row the indexed
-GEMMs run the contiguous layout's arithmetic, so their a2 / down rows and
-the fused mul-sum must equal the contiguous chain's bits exactly; the layer
-output is also checked against the oracle's indexed forward.  Padding
-positions of a2 and the rows of unrouted slots in down carry a sentinel that
-must survive.
+GEMMs run the contiguous layout's arithmetic, so their a2 / down rows (both
+in (token, slot) order) and the fused mul-sum must equal the contiguous
+chain's bits exactly; the layer output is also checked against the oracle's
+indexed forward.  Rows of unrouted slots in a2 and down carry a sentinel that
+must survive.  w2 also runs on a block map of another block size, as the
+experts do when their w2 tuning picks one.
 """
 import dataclasses
 import os
@@ -33,27 +34,32 @@ def _block_sizes(cfg):
     return [16, 32, 64, 128] + ([] if cfg.act_quant == "bf16" else [192, 256])
 
 
-def run_indexed(cfg, dev, bs):
-    """stage -> align -> w13+act (indexed) -> w2 (indexed) -> fused mul-sum."""
+def run_indexed(cfg, dev, bs, bs2=None):
+    """stage -> align -> w13+act (indexed) -> w2 (indexed, on a block map of
+    block size bs2, default bs) -> fused mul-sum."""
     p, bufs = stage_on_gpu(cfg, dev)
     ix = moe.alloc_indexed(p, bs)
     ix["sorted_ids"].fill_(-5)
     ix["expert_ids"].fill_(-5)
     moe.align_block_size(p, bufs["topk_idx"], bufs, ix)
-    cap = ix["sorted_ids"].numel()
+    ix2 = ix
+    if bs2 is not None and bs2 != bs:
+        ix2 = moe.alloc_indexed(p, bs2)
+        moe.align_block_size(p, bufs["topk_idx"], bufs, ix2)
+    rows = cfg.T * cfg.top_k
     if cfg.act_quant == "bf16":
-        a2_q = torch.full((cap, cfg.N), SENTINEL_BF16, dtype=torch.int16,
+        a2_q = torch.full((rows, cfg.N), SENTINEL_BF16, dtype=torch.int16,
                           device="cuda").view(torch.bfloat16)
         a2_sf = None
     else:
-        a2_q = torch.full((cap, cfg.N), SENTINEL_U8, dtype=torch.uint8, device="cuda")
-        a2_sf = torch.full((cap, moe.sizes(p)["a2_sf_row"]), 0x7F,
+        a2_q = torch.full((rows, cfg.N), SENTINEL_U8, dtype=torch.uint8, device="cuda")
+        a2_sf = torch.full((rows, moe.sizes(p)["a2_sf_row"]), 0x7F,
                            dtype=moe.scale_dtype(p), device="cuda")
     moe.grouped_gemm_w13_act_indexed(p, bufs["x_q"], bufs["x_sf"], ix, dev["w13"],
                                      dev["w13_sf"], a2_q, a2_sf)
-    down = torch.full((cfg.T * cfg.top_k, cfg.K), SENTINEL_BF16, dtype=torch.int16,
+    down = torch.full((rows, cfg.K), SENTINEL_BF16, dtype=torch.int16,
                       device="cuda").view(torch.bfloat16)
-    moe.grouped_gemm_w2_indexed(p, a2_q, a2_sf, ix, dev["w2"], dev["w2_sf"], down)
+    moe.grouped_gemm_w2_indexed(p, a2_q, a2_sf, ix2, dev["w2"], dev["w2_sf"], down)
     out = torch.empty((cfg.T, cfg.K), dtype=torch.bfloat16, device="cuda")
     moe.fused_mul_sum(p, down, bufs["topk_idx"], bufs["topk_w"], out)
     torch.cuda.synchronize()
@@ -91,20 +97,22 @@ def test_indexed_layer_matches_contiguous_and_oracle(gpu, name):
     numel = cfg.T * cfg.top_k
     routed = np.flatnonzero(slot_row >= 0)
     unrouted = np.flatnonzero(slot_row < 0)
-    for bs in _block_sizes(cfg):
-        r = run_indexed(cfg, dev, bs)
+    sizes = _block_sizes(cfg)
+    for n_bs, bs in enumerate(sizes):
+        # w2 on its own block map (another block size) every other time
+        bs2 = sizes[(n_bs + 1) % len(sizes)] if n_bs % 2 else bs
+        r = run_indexed(cfg, dev, bs, bs2)
         P = int(r["ix"]["num_tokens_padded"].item())
         sid = to_np(r["ix"]["sorted_ids"])[:P]
-        live = np.flatnonzero(sid < numel)
-        pad = np.flatnonzero(sid >= numel)
-        # a2 row q is the contiguous a2 row of slot sorted_ids[q], bit for bit
+        assert np.array_equal(np.sort(sid[sid < numel]), routed)
+        # a2 row s is the contiguous a2 row of slot s, bit for bit
         a2 = _u16(r["a2_q"])
-        rows = slot_row[sid[live]]
-        assert np.array_equal(a2[live], c_a2[rows]), (name, bs, "a2")
+        assert np.array_equal(a2[routed], c_a2[slot_row[routed]]), (name, bs, "a2")
         if c_sf is not None:
-            assert np.array_equal(to_np(r["a2_sf"])[live], c_sf[rows]), (name, bs, "a2_sf")
+            assert np.array_equal(to_np(r["a2_sf"])[routed], c_sf[slot_row[routed]]), \
+                (name, bs, "a2_sf")
         sent = SENTINEL_BF16 if cfg.act_quant == "bf16" else SENTINEL_U8
-        assert np.all(a2[pad] == sent), (name, bs, "padding rows written")
+        assert np.all(a2[unrouted] == sent), (name, bs, "unrouted rows written")
         # down row s (token, slot order) is the contiguous down row of that slot
         down = _u16(r["down"])
         assert np.array_equal(down[routed], c_down[slot_row[routed]]), (name, bs, "down")
