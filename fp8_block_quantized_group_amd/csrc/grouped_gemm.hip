@@ -191,6 +191,22 @@ __device__ __forceinline__ void dma16(v4i rsrc, uint32_t lds, uint32_t voffset) 
                ::"s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
 #endif
 }
+// Weight tiles.  stream (wave-uniform): no other block reads this tile, so
+// the copy carries the non-temporal hint and leaves L2 to the tiles that
+// are shared (activation rows, the weight tiles of multi-tile groups).
+// Measured: DSv3-shaped decode w13 -15 %, w2 -19 %; prefill w13 -1 %, w2
+// -2 %; the hint on every weight tile instead costs 1.7 % where groups of
+// many m-tiles share them (Qwen3-shaped).
+__device__ __forceinline__ void dma16_w(v4i rsrc, uint32_t lds, uint32_t voffset, bool stream) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if (stream)
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen nt lds"
+                 ::"s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 ::"s"(lds), "v"(voffset), "s"(rsrc) : "memory", "m0");
+#endif
+}
 __device__ __forceinline__ void dma4(v4i rsrc, uint32_t lds, uint32_t voffset) {
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
@@ -272,6 +288,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const bool indexed = p.sorted_ids != nullptr;
   const int NT = p.Nout / S::BN;
   int tile, nt, e, m0, rows_here;
+  bool w_once = false;   // this block is the weight tile's only reader
   int64_t base;
   if (indexed) {
     const int64_t nblk = min(max(*p.num_padded, 0) / S::BM, p.max_blocks);
@@ -307,6 +324,13 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     e = info[0];
     m0 = info[1] + (tile - t0) * S::BM;
     rows_here = min(S::BM, info[4] - m0);
+    // (e2m1 rows are 64 bytes per k-step: two k-steps share each cache
+    // line, so the hint would evict the line before its second half is
+    // read — measured +8 % w13, +20 % w2 at the MXFP4 DSv3 batch)
+    // Tiles of 192 / 256 rows are picked for experts with hundreds of rows,
+    // whose weight tiles are shared: those shapes keep one load form (the
+    // run-time choice alone cost 2-3 % on the Qwen3-shaped fused w13).
+    w_once = S::BM <= 128 && !W4 && mtiles == 1;
     base = info[5];
   }
   const int n0 = nt * S::BN;          // first output column (plain GEMM)
@@ -365,7 +389,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     const uint32_t st = smem_base + (kb % S::STAGES) * STAGE;
 #pragma unroll
     for (int i = 0; i < BI; ++i)
-      dma16(rs_b, st + AB + i * S::THREADS * 16 + wave_slot, b_off[i] + (uint32_t)kb * WROW);
+      dma16_w(rs_b, st + AB + i * S::THREADS * 16 + wave_slot, b_off[i] + (uint32_t)kb * WROW,
+              w_once);
   };
 #pragma unroll
   for (int s = 0; s < S::STAGES - 1; ++s)
@@ -806,119 +831,127 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
         packed[2 * i + 1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
       }
 #pragma unroll
-      for (int v = 0; v < S::TN / 2; ++v)
-        reinterpret_cast<uint4*>(dst)[v] =
-            make_uint4(packed[4 * v], packed[4 * v + 1], packed[4 * v + 2], packed[4 * v + 3]);
+      for (int v = 0; v < S::TN / 2; ++v) {
+        // written once, read once by the reduce: non-temporal (measured
+        // w2 -0.6 % DSv3-shaped, -2.2 % Qwen3-shaped)
+        const v4i o = {(int)packed[4 * v], (int)packed[4 * v + 1], (int)packed[4 * v + 2],
+                       (int)packed[4 * v + 3]};
+        __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(dst) + v);
+      }
     }
   }
 }
 
-template <class S, bool ACT>
-hipError_t launch_shape(const GemmArgs& p, int max_tiles, int quant, hipStream_t stream) {
+template <class S, int SC, bool ACT>
+hipError_t launch_shape(const GemmArgs& p, int max_tiles, hipStream_t stream) {
   const int64_t blocks = ((int64_t)max_tiles * (p.Nout / S::BN) + 7) / 8 * 8;
   const dim3 grid((unsigned)blocks);
-  if (quant == kQuantUe8m0)
-    grouped_gemm_kernel<S, kQuantUe8m0, ACT><<<grid, S::THREADS, 0, stream>>>(p);
-  else if (quant == kQuantF32)
-    grouped_gemm_kernel<S, kQuantF32, ACT><<<grid, S::THREADS, 0, stream>>>(p);
-  else if (quant == kQuantMxfp8)
-    grouped_gemm_kernel<S, kQuantMxfp8, ACT><<<grid, S::THREADS, 0, stream>>>(p);
-  else if (quant == kSchemeMxfp8W4)
-    grouped_gemm_kernel<S, kSchemeMxfp8W4, ACT><<<grid, S::THREADS, 0, stream>>>(p);
-  else if (quant == kQuantBf16) {
+  if constexpr (SC == kQuantBf16) {
     // bf16 activation tiles take twice the LDS: only shapes whose ring fits
     constexpr bool fits =
         S::STAGES * (S::BM * 2 * kRowBytes + S::BN * kRowBytes) + S::NBLK * kMaxGroups * 4 <=
         160 * 1024;
     if constexpr (fits)
-      grouped_gemm_kernel<S, kQuantBf16, ACT><<<grid, S::THREADS, 0, stream>>>(p);
+      grouped_gemm_kernel<S, SC, ACT><<<grid, S::THREADS, 0, stream>>>(p);
     else
       return hipErrorInvalidValue;
+  } else {
+    grouped_gemm_kernel<S, SC, ACT><<<grid, S::THREADS, 0, stream>>>(p);
   }
-  else
-    return hipErrorInvalidValue;
   return hipGetLastError();
 }
-
-}  // namespace
 
 // bf16 activations take twice the activation-tile LDS: two-slot rings and
 // tiles of at most 128 rows
 template <bool ACT>
 hipError_t launch_a16(const GemmArgs& p, int tile_m, int max_tiles, hipStream_t stream) {
-  const int q = kQuantBf16;
+  constexpr int q = kQuantBf16;
   if (ACT || p.Nout % 256 == 0) {
     switch (tile_m) {
-      case 16: return launch_shape<Shape<16, 256, 4, 2>, ACT>(p, max_tiles, q, stream);
-      case 32: return launch_shape<Shape<32, 256, 4, 2>, ACT>(p, max_tiles, q, stream);
-      case 64: return launch_shape<Shape<64, 256, 8, 2>, ACT>(p, max_tiles, q, stream);
-      case 128: return launch_shape<Shape<128, 256, 8, 2>, ACT>(p, max_tiles, q, stream);
+      case 16: return launch_shape<Shape<16, 256, 4, 2>, q, ACT>(p, max_tiles, stream);
+      case 32: return launch_shape<Shape<32, 256, 4, 2>, q, ACT>(p, max_tiles, stream);
+      case 64: return launch_shape<Shape<64, 256, 8, 2>, q, ACT>(p, max_tiles, stream);
+      case 128: return launch_shape<Shape<128, 256, 8, 2>, q, ACT>(p, max_tiles, stream);
       default: return hipErrorInvalidValue;
     }
   }
   if constexpr (!ACT) {
     switch (tile_m) {
-      case 16: return launch_shape<Shape<16, 128, 4, 2>, false>(p, max_tiles, q, stream);
-      case 32: return launch_shape<Shape<32, 128, 4, 2>, false>(p, max_tiles, q, stream);
-      case 64: return launch_shape<Shape<64, 128, 4, 2>, false>(p, max_tiles, q, stream);
-      case 128: return launch_shape<Shape<128, 128, 4, 2>, false>(p, max_tiles, q, stream);
+      case 16: return launch_shape<Shape<16, 128, 4, 2>, q, false>(p, max_tiles, stream);
+      case 32: return launch_shape<Shape<32, 128, 4, 2>, q, false>(p, max_tiles, stream);
+      case 64: return launch_shape<Shape<64, 128, 4, 2>, q, false>(p, max_tiles, stream);
+      case 128: return launch_shape<Shape<128, 128, 4, 2>, q, false>(p, max_tiles, stream);
       default: return hipErrorInvalidValue;
     }
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_grouped_gemm(const GemmArgs& p, int tile_m, int max_tiles, int quant, bool act,
-                               hipStream_t stream) {
+}  // namespace
+
+// One scale scheme's kernels.  This file is compiled once per scheme
+// (MOE_GEMM_SCHEME = the scheme's kQuant* / kScheme* value), so the schemes'
+// instantiations build in parallel; launch_grouped_gemm (kernels.h) picks
+// the scheme at run time.
+template <int SC>
+hipError_t launch_grouped_gemm_sc(const GemmArgs& p, int tile_m, int max_tiles, bool act,
+                                  hipStream_t stream) {
   if (max_tiles <= 0) return hipSuccess;
-  if (quant == kQuantBf16) {
+  if constexpr (SC == kQuantBf16) {
     if (act && p.Nout % 256 != 0) return hipErrorInvalidValue;
     return act ? launch_a16<true>(p, tile_m, max_tiles, stream)
                : launch_a16<false>(p, tile_m, max_tiles, stream);
-  }
-  if (act) {
-    // 256 weight rows = 128 gate + 128 up rows per block, any tile height
-    if (p.Nout % 256 != 0) return hipErrorInvalidValue;
+  } else {
+    if (act) {
+      // 256 weight rows = 128 gate + 128 up rows per block, any tile height
+      if (p.Nout % 256 != 0) return hipErrorInvalidValue;
+      switch (tile_m) {
+        case 16: return launch_shape<Shape<16, 256, 4, 3>, SC, true>(p, max_tiles, stream);
+        case 32: return launch_shape<Shape<32, 256, 4, 3>, SC, true>(p, max_tiles, stream);
+        case 64: return launch_shape<Shape<64, 256, 8, 3>, SC, true>(p, max_tiles, stream);
+        case 128: return launch_shape<Shape<128, 256, 8, 3>, SC, true>(p, max_tiles, stream);
+        case 192: return launch_shape<Shape<192, 256, 8, 2>, SC, true>(p, max_tiles, stream);
+        case 256: return launch_shape<Shape<256, 256, 8, 2>, SC, true>(p, max_tiles, stream);
+        default: return hipErrorInvalidValue;
+      }
+    }
     switch (tile_m) {
-      case 16: return launch_shape<Shape<16, 256, 4, 3>, true>(p, max_tiles, quant, stream);
-      case 32: return launch_shape<Shape<32, 256, 4, 3>, true>(p, max_tiles, quant, stream);
-      case 64: return launch_shape<Shape<64, 256, 8, 3>, true>(p, max_tiles, quant, stream);
-      case 128: return launch_shape<Shape<128, 256, 8, 3>, true>(p, max_tiles, quant, stream);
-      case 192: return launch_shape<Shape<192, 256, 8, 2>, true>(p, max_tiles, quant, stream);
-      case 256: return launch_shape<Shape<256, 256, 8, 2>, true>(p, max_tiles, quant, stream);
+      case 16: return launch_shape<Shape<16, 128, 4, 4>, SC, false>(p, max_tiles, stream);
+      case 32: return launch_shape<Shape<32, 128, 4, 3>, SC, false>(p, max_tiles, stream);
+      case 64: return launch_shape<Shape<64, 128, 4, 3>, SC, false>(p, max_tiles, stream);
+      case 128: {
+        // 256-column tiles (8 waves) halve the activation re-reads; 128-column
+        // tiles run two blocks per CU, which measured faster for the MX
+        // schemes (whose MFMA consumes its scales directly: less per-k-step
+        // work to hide the block prologue behind).  MOE_GEMM_WIDE=0 / 1 forces
+        // one or the other.
+        static const char* env = getenv("MOE_GEMM_WIDE");
+        constexpr bool mx = SC == kQuantMxfp8 || SC == kSchemeMxfp8W4;
+        const bool wide = env != nullptr ? env[0] != '0' : !mx;
+        if (wide && p.Nout % 256 == 0)
+          return launch_shape<Shape<128, 256, 8, 3>, SC, false>(p, max_tiles, stream);
+        return launch_shape<Shape<128, 128, 4, 2>, SC, false>(p, max_tiles, stream);
+      }
+      // Experts with hundreds of rows: 1.5x / 2x fewer weight re-reads than
+      // 128-row tiles, at the price of a two-slot ring (LDS) and of 128
+      // accumulator VGPRs per lane at 256 rows.
+      case 192:
+        if (p.Nout % 256 == 0)
+          return launch_shape<Shape<192, 256, 8, 2>, SC, false>(p, max_tiles, stream);
+        return launch_shape<Shape<192, 128, 8, 2>, SC, false>(p, max_tiles, stream);
+      case 256:
+        if (p.Nout % 256 == 0)
+          return launch_shape<Shape<256, 256, 8, 2>, SC, false>(p, max_tiles, stream);
+        return launch_shape<Shape<256, 128, 8, 2>, SC, false>(p, max_tiles, stream);
       default: return hipErrorInvalidValue;
     }
   }
-  switch (tile_m) {
-    case 16: return launch_shape<Shape<16, 128, 4, 4>, false>(p, max_tiles, quant, stream);
-    case 32: return launch_shape<Shape<32, 128, 4, 3>, false>(p, max_tiles, quant, stream);
-    case 64: return launch_shape<Shape<64, 128, 4, 3>, false>(p, max_tiles, quant, stream);
-    case 128: {
-      // 256-column tiles (8 waves) halve the activation re-reads; 128-column
-      // tiles run two blocks per CU, which measured faster for the MX
-      // schemes (whose MFMA consumes its scales directly: less per-k-step
-      // work to hide the block prologue behind).  MOE_GEMM_WIDE=0 / 1 forces
-      // one or the other.
-      static const char* env = getenv("MOE_GEMM_WIDE");
-      const bool mx = quant == kQuantMxfp8 || quant == kSchemeMxfp8W4;
-      const bool wide = env != nullptr ? env[0] != '0' : !mx;
-      if (wide && p.Nout % 256 == 0)
-        return launch_shape<Shape<128, 256, 8, 3>, false>(p, max_tiles, quant, stream);
-      return launch_shape<Shape<128, 128, 4, 2>, false>(p, max_tiles, quant, stream);
-    }
-    // Experts with hundreds of rows: 1.5x / 2x fewer weight re-reads than
-    // 128-row tiles, at the price of a two-slot ring (LDS) and of 128
-    // accumulator VGPRs per lane at 256 rows.
-    case 192:
-      if (p.Nout % 256 == 0)
-        return launch_shape<Shape<192, 256, 8, 2>, false>(p, max_tiles, quant, stream);
-      return launch_shape<Shape<192, 128, 8, 2>, false>(p, max_tiles, quant, stream);
-    case 256:
-      if (p.Nout % 256 == 0)
-        return launch_shape<Shape<256, 256, 8, 2>, false>(p, max_tiles, quant, stream);
-      return launch_shape<Shape<256, 128, 8, 2>, false>(p, max_tiles, quant, stream);
-    default: return hipErrorInvalidValue;
-  }
 }
+
+#ifndef MOE_GEMM_SCHEME
+#error "compile this file once per scale scheme with -DMOE_GEMM_SCHEME=<scheme>"
+#endif
+template hipError_t launch_grouped_gemm_sc<MOE_GEMM_SCHEME>(const GemmArgs&, int, int, bool,
+                                                            hipStream_t);
 
 }  // namespace moe

@@ -93,8 +93,32 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint
 // gate half [0, Nout/2) and up half [Nout/2, Nout) are combined into
 // silu(gate) * up and quantized per group (128, or 32 for MX) into act_q /
 // act_sf; nothing is written to out.
-hipError_t launch_grouped_gemm(const GemmArgs& args, int tile_m, int max_tiles, int quant,
-                               bool act, hipStream_t stream);
+// One object per scheme (grouped_gemm.hip built with MOE_GEMM_SCHEME = SC).
+template <int SC>
+hipError_t launch_grouped_gemm_sc(const GemmArgs& args, int tile_m, int max_tiles, bool act,
+                                  hipStream_t stream);
+extern template hipError_t launch_grouped_gemm_sc<kQuantUe8m0>(const GemmArgs&, int, int, bool,
+                                                               hipStream_t);
+extern template hipError_t launch_grouped_gemm_sc<kQuantF32>(const GemmArgs&, int, int, bool,
+                                                             hipStream_t);
+extern template hipError_t launch_grouped_gemm_sc<kQuantBf16>(const GemmArgs&, int, int, bool,
+                                                              hipStream_t);
+extern template hipError_t launch_grouped_gemm_sc<kQuantMxfp8>(const GemmArgs&, int, int, bool,
+                                                               hipStream_t);
+extern template hipError_t launch_grouped_gemm_sc<kSchemeMxfp8W4>(const GemmArgs&, int, int, bool,
+                                                                  hipStream_t);
+inline hipError_t launch_grouped_gemm(const GemmArgs& args, int tile_m, int max_tiles, int quant,
+                                      bool act, hipStream_t stream) {
+  switch (quant) {
+    case kQuantUe8m0: return launch_grouped_gemm_sc<kQuantUe8m0>(args, tile_m, max_tiles, act, stream);
+    case kQuantF32: return launch_grouped_gemm_sc<kQuantF32>(args, tile_m, max_tiles, act, stream);
+    case kQuantBf16: return launch_grouped_gemm_sc<kQuantBf16>(args, tile_m, max_tiles, act, stream);
+    case kQuantMxfp8: return launch_grouped_gemm_sc<kQuantMxfp8>(args, tile_m, max_tiles, act, stream);
+    case kSchemeMxfp8W4:
+      return launch_grouped_gemm_sc<kSchemeMxfp8W4>(args, tile_m, max_tiles, act, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_topk_reduce(const void* down, const int32_t* slot_row, const float* w, void* out,
                               int T, int k, int K, hipStream_t stream);

