@@ -62,6 +62,10 @@ constexpr int kRowBytes = 128;      // one k-step of a row: 128 fp8 values
 constexpr uint32_t kOutOfRange = 0xF0000000u;
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format
 constexpr int kMaxGroups = 256;                // reduction length <= 32768
+#ifndef MOE_ZIP
+#define MOE_ZIP 16
+#endif
+constexpr int kZip = MOE_ZIP;                  // zipper run length (work items)
 
 // Tile geometry.  BM activation rows x BN weight rows (output columns) per
 // block, NW waves arranged WN x WM, each owning a WAVE_N x WAVE_M sub-tile
@@ -311,10 +315,25 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     // of the schedule the routing step built.  One scalar load of tile t0's
     // information gives its group (first tile, size), expert, rows and first
     // row; the block's tile is in the same group, so the rest follows.
+    //
+    // The slice lists its heaviest groups first.  Walked in that order, the
+    // whole chip first runs only the heavy experts' blocks (many m-tiles
+    // sharing weight tiles: bound by L2 / MALL latency, HBM mostly idle),
+    // then only the light experts' blocks (weight streaming at the HBM
+    // ceiling, matrix cores idle) — measured at the DSv3-shaped prefill
+    // batch as two back-to-back phases of about 1 ms each.  So the blocks
+    // take the slice in a zipper order instead: kZip items from its front,
+    // kZip from its back (walked backwards), and so on, until front and back
+    // meet.  Blocks running together on an XCD then mix both kinds, and
+    // consecutive items still share a weight tile (heavy side) or an
+    // activation tile (light side).
     const int64_t work = (int64_t)p.tile_list[0] * NT;
     const int64_t per_xcd = (work + 7) / 8;
-    const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (blockIdx.x / 8 >= per_xcd || wl >= work) return;
+    const int64_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const int64_t items = min(per_xcd, work - xcd * per_xcd);   // this XCD's slice
+    if (j >= items) return;
+    const int64_t u = j / (2 * kZip), v = j % (2 * kZip);
+    const int64_t wl = xcd * per_xcd + (v < kZip ? u * kZip + v : items - 1 - (u * kZip + v - kZip));
     const int t0 = __builtin_amdgcn_readfirstlane((int)(wl / NT));
     const int32_t* info = p.tile_list + 4 + 8 * (int64_t)t0;
     const int first = info[2], mtiles = info[3];
