@@ -294,14 +294,46 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   int tile, nt, e, m0, rows_here;
   bool w_once = false;   // this block is the weight tile's only reader
   int64_t base;
-  if (indexed) {
-    const int64_t nblk = min(max(*p.num_padded, 0) / S::BM, p.max_blocks);
-    const int64_t work = nblk * NT;
+  // The schedule the routing step built, as a work list: this XCD's slice,
+  // taken in the zipper order described below, then the (tile, n-tile) item
+  // it names.  Returns false past the work.
+  auto schedule_item = [&](int& t_out, int& nt_out, const int32_t*& info_out) -> bool {
+    const int64_t work = (int64_t)p.tile_list[0] * NT;
     const int64_t per_xcd = (work + 7) / 8;
-    const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-    if (blockIdx.x / 8 >= per_xcd || wl >= work) return;
-    tile = __builtin_amdgcn_readfirstlane((int)(wl / NT));
-    nt = __builtin_amdgcn_readfirstlane((int)(wl % NT));
+    const int64_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
+    const int64_t items = min(per_xcd, work - xcd * per_xcd);   // this XCD's slice
+    if (j >= items) return false;
+    const int64_t u = j / (2 * kZip), v = j % (2 * kZip);
+    const int64_t wl =
+        xcd * per_xcd + (v < kZip ? u * kZip + v : items - 1 - (u * kZip + v - kZip));
+    const int t0 = __builtin_amdgcn_readfirstlane((int)(wl / NT));
+    const int32_t* info = p.tile_list + 4 + 8 * (int64_t)t0;
+    const int first = info[2], mtiles = info[3];
+    const int r = (int)(wl - (int64_t)first * NT);
+    nt_out = __builtin_amdgcn_readfirstlane(r / mtiles);
+    t_out = __builtin_amdgcn_readfirstlane(first + r % mtiles);
+    info_out = info;
+    return true;
+  };
+  if (indexed) {
+    if (p.tile_list != nullptr) {
+      // moe_forward: the blocks in the schedule's XCD-balanced zipper order;
+      // tile (e, m-tile i) of the schedule is block first-m-tile(e) + i
+      int t = 0;
+      const int32_t* info = nullptr;
+      if (!schedule_item(t, nt, info)) return;
+      const int t0 = (int)(info - (p.tile_list + 4)) / 8;
+      tile = __builtin_amdgcn_readfirstlane(info[6] + (info[1] / S::BM) + (t - t0));
+      w_once = S::BM <= 128 && !W4 && info[3] == 1;
+    } else {
+      const int64_t nblk = min(max(*p.num_padded, 0) / S::BM, p.max_blocks);
+      const int64_t work = nblk * NT;
+      const int64_t per_xcd = (work + 7) / 8;
+      const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+      if (blockIdx.x / 8 >= per_xcd || wl >= work) return;
+      tile = __builtin_amdgcn_readfirstlane((int)(wl / NT));
+      nt = __builtin_amdgcn_readfirstlane((int)(wl % NT));
+    }
     // the block's routed entries (ids below numel) lead, padding follows
     e = __builtin_amdgcn_readfirstlane(p.expert_ids[tile]);
     m0 = 0;
@@ -327,19 +359,12 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     // meet.  Blocks running together on an XCD then mix both kinds, and
     // consecutive items still share a weight tile (heavy side) or an
     // activation tile (light side).
-    const int64_t work = (int64_t)p.tile_list[0] * NT;
-    const int64_t per_xcd = (work + 7) / 8;
-    const int64_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
-    const int64_t items = min(per_xcd, work - xcd * per_xcd);   // this XCD's slice
-    if (j >= items) return;
-    const int64_t u = j / (2 * kZip), v = j % (2 * kZip);
-    const int64_t wl = xcd * per_xcd + (v < kZip ? u * kZip + v : items - 1 - (u * kZip + v - kZip));
-    const int t0 = __builtin_amdgcn_readfirstlane((int)(wl / NT));
-    const int32_t* info = p.tile_list + 4 + 8 * (int64_t)t0;
-    const int first = info[2], mtiles = info[3];
-    const int r = (int)(wl - (int64_t)first * NT);
-    nt = __builtin_amdgcn_readfirstlane(r / mtiles);
-    tile = __builtin_amdgcn_readfirstlane(first + r % mtiles);
+    int t = 0;
+    const int32_t* info = nullptr;
+    if (!schedule_item(t, nt, info)) return;
+    const int t0 = (int)(info - (p.tile_list + 4)) / 8;
+    const int mtiles = info[3];
+    tile = t;
     e = info[0];
     m0 = info[1] + (tile - t0) * S::BM;
     rows_here = min(S::BM, info[4] - m0);

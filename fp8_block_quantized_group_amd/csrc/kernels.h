@@ -49,15 +49,18 @@ struct GemmArgs {
   int act_sf_row;            //   scale row length: bytes (UE8M0) or floats (fp32)
   // [0] tile count, [1] group count, [2..3] 0, then per tile 8 ints: expert, first
   // row within the expert, first tile and size of its group (one expert's
-  // consecutive m-tiles, groups in XCD-balanced order), the expert's rows
-  // and its first row in the GEMM's row space (contiguous offset or slab)
+  // consecutive m-tiles, groups in XCD-balanced order), the expert's rows,
+  // its first row in the GEMM's row space (contiguous offset or slab), its
+  // first m-tile in expert order, 0
   const int32_t* tile_list;
   int num_experts;
   const int32_t* row_src;    // A row gather (w13 on the contiguous layout) or nullptr
   // indexed layout (sorted_ids != nullptr): tile b is the block of BM rows
   // [b*BM, (b+1)*BM) of sorted_ids, of expert expert_ids[b]; entries not
   // below numel are padding and come after the block's routed entries.
-  // tile_list / row_src unused.
+  // row_src unused; tile_list, when given (block size = BM = the routing's
+  // tile height), orders the blocks: the schedule's tile (e, m-tile i) is
+  // block first-m-tile(e) + i.
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
   const int32_t* num_padded;       // [1] device: the padded total

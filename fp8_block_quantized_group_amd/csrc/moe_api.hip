@@ -331,7 +331,7 @@ struct Indexed {
 };
 
 // w13 with act: out unused, the activation goes to act_q / act_sf.  ix: the
-// indexed layout (r unused then).
+// indexed layout (r, if given, only orders its blocks).
 moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const void* a_q,
                       const void* a_sf, const moe_routing_t* r, const void* w, const void* w_sf,
                       void* out, hipStream_t stream, bool act = false, void* act_q = nullptr,
@@ -365,6 +365,9 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
     g.scatter_sorted = 1;
     tile_m = ix->block_size;
     max_tiles = g.max_blocks;
+    // moe_forward hands in its routing: with blocks of the tile height the
+    // GEMM takes them in the routing's XCD-balanced order
+    if (r != nullptr && ix->block_size == pl.s.tile_m) g.tile_list = r->tile_list;
   } else {
     g.tile_list = r->tile_list;
     g.row_src = (w13 && !batched(p)) ? r->row_src : nullptr;
@@ -665,15 +668,15 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
     const Indexed ix{w.sorted_ids, w.expert_ids, w.num_padded, pl.s.tile_m};
     CHECK(run_align(p, w.idx, &w.routing, ix, s));
     if (gated(p)) {
-      CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, nullptr, w13, w13_sf, nullptr, s, true, w.a2_q,
-                     w.a2_sf, &ix));
+      CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, nullptr, s, true,
+                     w.a2_q, w.a2_sf, &ix));
     } else {
-      CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, nullptr, w13, w13_sf, w.gate_up, s, false,
+      CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, w.gate_up, s, false,
                      nullptr, nullptr, &ix));
       CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s, true));
     }
-    CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, nullptr, w2, w2_sf, w.down, s, false, nullptr,
-                   nullptr, &ix));
+    CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s, false,
+                   nullptr, nullptr, &ix));
     CHECK(run_mul_sum(p, w.down, w.idx, w.w, out, s));
     return ok();
   }

@@ -125,6 +125,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   __shared__ int chunk_bin[kChunkCap], chunk_off[kChunkCap], chunk_idx[kChunkCap];
   __shared__ int bin_load[8], bin_cnt[8];
   __shared__ int exp_rows[1024], exp_base[1024];   // per expert: GEMM rows, first row
+  __shared__ int exp_tile0[1024];                   // its first m-tile in expert order
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E) {
@@ -153,6 +154,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   exp_rows[e] = rows;
   exp_base[e] = counts_in != nullptr ? e * max_tokens : incl - cnt;
   const int incl_nt = block_inclusive_scan(nt, buf);
+  exp_tile0[e] = incl_nt - nt;
   // the last thread's inclusive value is the total: broadcast it
   if (e == 1023) buf[0] = incl_nt;
   __syncthreads();
@@ -263,10 +265,12 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
     const int ex = chunk_e[i], n = chunk_n[i];
     for (int t = 0; t < n; ++t) {
       // expert, first row, its group's first tile and size, the expert's
-      // rows and first row in the GEMM's row space
+      // rows, its first row in the GEMM's row space and its first m-tile in
+      // expert order (the indexed layout's first block of the expert when
+      // its block size is the tile height)
       int4* d = reinterpret_cast<int4*>(info + 8 * (tile0 + t));
       d[0] = make_int4(ex, (chunk_m[i] + t) * tile_m, tile0, n);
-      d[1] = make_int4(exp_rows[ex], exp_base[ex], 0, 0);
+      d[1] = make_int4(exp_rows[ex], exp_base[ex], exp_tile0[ex], 0);
     }
   }
   if (e == 0) {

@@ -132,7 +132,7 @@ def host_tile_list(counts, tile_m, n_entries, bases):
         groups[e] = pos
         first, n = pos, -(-int(c) // tile_m)
         for m0 in range(0, int(c), tile_m):
-            info[pos] = (e, m0, first, n, int(c), int(bases[e]), 0, 0)
+            info[pos] = (e, m0, first, n, int(c), int(bases[e]), first, 0)
             pos += 1
     groups[E] = pos
     tl[0], tl[1] = pos, E
@@ -317,6 +317,7 @@ def check_schedule(tile_list, counts, s, E, bases):
     info = tl[4:4 + 8 * n].reshape(n, 8)
     tiles = [-(-int(c) // bm) for c in counts]
     seq, sizes = expected_schedule(tiles)
+    tile0 = np.concatenate([[0], np.cumsum(tiles)[:-1]])
     assert [(int(e), int(m0) // bm) for e, m0 in info[:, :2]] == seq
     assert np.all(info[:, 1] % bm == 0)
     groups = tl[4 + 8 * max_tiles:4 + 8 * max_tiles + G + 1]
@@ -329,7 +330,9 @@ def check_schedule(tile_list, counts, s, E, bases):
         assert np.all(seg[:, 2] == groups[g]) and np.all(seg[:, 3] == len(seg))
         e = int(seg[0, 0])
         assert np.all(seg[:, 4] == int(counts[e])) and np.all(seg[:, 5] == int(bases[e]))
-        assert np.all(seg[:, 6:] == 0)
+        # the expert's first m-tile in expert order (the indexed layout's
+        # first block of the expert at this block size)
+        assert np.all(seg[:, 6] == tile0[e]) and np.all(seg[:, 7] == 0)
 
 
 def test_stage_bf16_copy(gpu):
