@@ -19,15 +19,17 @@ __device__ __forceinline__ float bf16_lo(uint32_t packed) {
 __device__ __forceinline__ float bf16_hi(uint32_t packed) {
   return __uint_as_float(packed & 0xFFFF0000u);
 }
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.  One
+// v_cvt_pk_bf16_f32 per pair (gfx950): checked on the GPU to give the bits of
+// the integer formula -- add 0x7FFF plus the kept lsb, then truncate; a NaN
+// keeps its upper bits with the quiet bit set -- for all 2^32 inputs.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return pack_bf16x2(f, 0.0f) & 0xFFFFu;
 }
 
 // ---- fp32 -> e4m3fn ---------------------------------------------------------

@@ -778,8 +778,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
             // hi leaves, in every lane, its gate value in the first result
             // and its up value in the second (gate lanes keep lo and take the
             // partner's lo; up lanes take the partner's hi and keep hi)
-            const uint32_t lo = f32_to_bf16_bits(acc[ii][j][r]) << 16;
-            const uint32_t hi = f32_to_bf16_bits(acc[ii + 2][j][r]) << 16;
+            const uint32_t pk = pack_bf16x2(acc[ii][j][r], acc[ii + 2][j][r]);
+            const uint32_t lo = pk << 16;
+            const uint32_t hi = pk & 0xFFFF0000u;
             const auto gu = __builtin_amdgcn_permlane32_swap(lo, hi, false, false);
             const float v = f(__uint_as_float(gu[0]), __uint_as_float(gu[1]));
             h[j][4 * ii + r] = v;
