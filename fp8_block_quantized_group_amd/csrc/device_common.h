@@ -60,6 +60,14 @@ __device__ __forceinline__ float row16_max(float v) {
   return v;
 }
 
+// max over a half-row of 8 lanes: the two quad steps, then row_half_mirror
+__device__ __forceinline__ float row8_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));
+  v = fmaxf(v, dpp_f32<0x4E>(v));
+  v = fmaxf(v, dpp_f32<0x141>(v));
+  return v;
+}
+
 // max over a quad of 4 lanes (quad_perm [1,0,3,2], [2,3,0,1])
 __device__ __forceinline__ float quad_max(float v) {
   v = fmaxf(v, dpp_f32<0xB1>(v));
