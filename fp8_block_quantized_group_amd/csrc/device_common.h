@@ -103,6 +103,63 @@ __device__ __forceinline__ GroupScale group_scale(float amax) {
   return r;
 }
 
+__device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+
+// Row r of a batched-masked slab array is live iff r % max_tokens < counts[r / max_tokens].
+__device__ __forceinline__ bool row_live(int64_t row, const int32_t* counts, int max_tokens) {
+  if (counts == nullptr) return true;
+  const int64_t e = row / max_tokens;
+  return (row - e * max_tokens) < (int64_t)counts[e];
+}
+
+// The group quantizer on one 128-value group gid of bf16 rows of G groups
+// (per-128 scales, UE8M0 bytes in rows of sf_row_len or fp32 [rows, G]):
+// 8 lanes per group, 16 values per lane from two adjacent 16-byte loads and
+// one 16-byte store of codes.  The hidden states are read once, so the loads
+// are non-temporal; the codes are not (the w13 GEMM re-reads them).
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+template <bool UE8M0>
+__device__ __forceinline__ void quantize_group128(const uint16_t* __restrict__ x,
+                                                  uint8_t* __restrict__ xq,
+                                                  uint8_t* __restrict__ xsf, int64_t gid,
+                                                  int lane8, int G, int sf_row_len,
+                                                  const int32_t* __restrict__ counts,
+                                                  int max_tokens) {
+  const int64_t row = gid / G;
+  const int g = (int)(gid - row * G);
+  if (!row_live(row, counts, max_tokens)) return;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + gid * kGroup) + 2 * lane8;
+  const u32x4_t a = __builtin_nontemporal_load(src);
+  const u32x4_t b = __builtin_nontemporal_load(src + 1);
+  float f[16];
+  unpack8(make_uint4(a.x, a.y, a.z, a.w), f);
+  unpack8(make_uint4(b.x, b.y, b.z, b.w), f + 8);
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = row8_max(amax);
+  const GroupScale gs = group_scale<UE8M0>(amax);
+  uint4 q;
+  q.x = f32x4_to_e4m3x4(f[0] * gs.recip, f[1] * gs.recip, f[2] * gs.recip, f[3] * gs.recip);
+  q.y = f32x4_to_e4m3x4(f[4] * gs.recip, f[5] * gs.recip, f[6] * gs.recip, f[7] * gs.recip);
+  q.z = f32x4_to_e4m3x4(f[8] * gs.recip, f[9] * gs.recip, f[10] * gs.recip, f[11] * gs.recip);
+  q.w = f32x4_to_e4m3x4(f[12] * gs.recip, f[13] * gs.recip, f[14] * gs.recip, f[15] * gs.recip);
+  *reinterpret_cast<uint4*>(xq + gid * kGroup + lane8 * 16) = q;
+  if (UE8M0) {
+    uint8_t* sf_row = xsf + row * sf_row_len;
+    if (lane8 == 0) sf_row[g] = (uint8_t)gs.stored;
+    // the row's trailing pad bytes (4*ceil(G/4) - G of them) are zero
+    if (g == G - 1 && lane8 >= 1 && lane8 <= sf_row_len - G) sf_row[G + lane8 - 1] = 0;
+  } else {
+    if (lane8 == 0) reinterpret_cast<uint32_t*>(xsf + row * (int64_t)G * 4)[g] = gs.stored;
+  }
+}
+
 // ---- activations ------------------------------------------------------------
 // Kinds (values match moe_act_t).  Gated kinds combine the gate column g with
 // its up column u as f(g) * u; _no_mul kinds return f(g) of the single w13

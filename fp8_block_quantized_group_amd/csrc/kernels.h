@@ -74,6 +74,9 @@ struct GemmArgs {
   int Nout;                  // output columns, multiple of 128
 };
 
+// Staging on its own launch: the MXFP8 group quantizer (32-value groups) or
+// the bf16 copy.  Per-128 fp8 staging runs inside launch_route (StageQuant);
+// here it returns hipErrorInvalidValue.
 hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, int K, int quant,
                               const int32_t* counts, int max_tokens, hipStream_t stream);
 
@@ -83,12 +86,25 @@ hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t 
                               int quant, const int32_t* num_rows, const int32_t* counts,
                               int max_tokens, int act, hipStream_t stream);
 
+// Optional: the hidden states' per-128 quantization (UE8M0 or fp32 scales)
+// run inside the routing scan's launch; rows / K / counts as for
+// launch_stage_quant.
+struct StageQuant {
+  const void* x;
+  void* xq;
+  void* xsf;
+  int64_t rows;
+  int K;
+  bool ue8m0;
+};
+
 hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint8_t* is_padding,
                         int T, int k, int E, const EplbArgs& eplb, int64_t* idx_out,
                         float* w_out, int32_t* hist, const int32_t* counts_in, int max_tokens,
                         int tile_m, int max_tiles, int32_t* expert_num_tokens,
                         int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
-                        int32_t* tile_list, hipStream_t stream);
+                        int32_t* tile_list, hipStream_t stream,
+                        const StageQuant* sq = nullptr);
 
 // quant: the scale scheme: an activation scheme (kQuant*; kQuantMxfp8 with
 // e4m3 MX weights) or kSchemeMxfp8W4 (MXFP8 activations, e2m1 MX weights).

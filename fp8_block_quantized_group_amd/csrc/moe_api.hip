@@ -309,15 +309,23 @@ moe_status_t run_stage(const moe_problem_t* p, const Plan& pl, const void* hidde
                        float* w_out, const moe_routing_t* r, int32_t* hist,
                        hipStream_t stream) {
   const int32_t* cin = batched(p) ? counts_in : nullptr;
-  hipError_t err = moe::launch_stage_quant(hidden, x_q, x_sf, pl.s.stage_rows, p->hidden,
-                                           p->act_quant, cin, p->max_tokens_per_expert, stream);
-  if (err != hipSuccess) return launch_status(err, "stage_quant");
-  err = moe::launch_route(topk_ids, topk_weights, is_padding, p->num_tokens, p->top_k,
-                          p->num_experts, eplb_args(eplb), idx_out, w_out, hist, cin,
-                          p->max_tokens_per_expert, pl.s.tile_m, (int)pl.max_tiles,
-                          r->expert_num_tokens,
-                          r->expert_offsets, r->row_src, r->slot_row, r->tile_list, stream);
-  return launch_status(err, "route");
+  // per-128 fp8 quantization runs inside the routing scan's launch; the
+  // other schemes (MXFP8 groups of 32, the bf16 copy) launch on their own
+  const bool fused = p->act_quant == MOE_Q_FP8_UE8M0 || p->act_quant == MOE_Q_FP8_F32;
+  const moe::StageQuant sq{hidden, x_q, x_sf, pl.s.stage_rows, p->hidden,
+                           p->act_quant == MOE_Q_FP8_UE8M0};
+  if (!fused) {
+    const hipError_t err =
+        moe::launch_stage_quant(hidden, x_q, x_sf, pl.s.stage_rows, p->hidden, p->act_quant,
+                                cin, p->max_tokens_per_expert, stream);
+    if (err != hipSuccess) return launch_status(err, "stage_quant");
+  }
+  const hipError_t err = moe::launch_route(
+      topk_ids, topk_weights, is_padding, p->num_tokens, p->top_k, p->num_experts,
+      eplb_args(eplb), idx_out, w_out, hist, cin, p->max_tokens_per_expert, pl.s.tile_m,
+      (int)pl.max_tiles, r->expert_num_tokens, r->expert_offsets, r->row_src, r->slot_row,
+      r->tile_list, stream, fused ? &sq : nullptr);
+  return launch_status(err, fused ? "route + stage_quant" : "route");
 }
 
 // The indexed layout's block map (moe_align_block_size outputs).  Both

@@ -15,20 +15,16 @@
 // 128-value group, a quad per 32-value group); each lane loads 8 bf16
 // (16 bytes), the lanes reduce |x| with DPP max steps, each lane writes 8
 // fp8 bytes.  A 64-lane wave covers 512 contiguous input values, so every
-// load and store instruction is fully coalesced.
+// load and store instruction is fully coalesced.  (The hidden states'
+// per-128 staging uses quantize_group128 from device_common.h inside the
+// routing scan's launch; the kernels here stage MXFP8 groups, copy bf16 and
+// re-quantize the w2 input of the unfused path.)
 #include "device_common.h"
 #include "kernels.h"
 
 namespace moe {
 
 namespace {
-
-__device__ __forceinline__ void unpack8(const uint4 v, float f[8]) {
-  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
-  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
-  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-}
 
 // Quantize the 8 values a lane holds (LANES consecutive lanes form one
 // group), write the codes and, from the group's first lane, its scale.
@@ -54,13 +50,6 @@ __device__ __forceinline__ void quantize_store(const float f[8], int lane16, uin
   }
 }
 
-// Row r of a batched-masked slab array is live iff r % max_tokens < counts[r / max_tokens].
-__device__ __forceinline__ bool row_live(int64_t row, const int32_t* counts, int max_tokens) {
-  if (counts == nullptr) return true;
-  const int64_t e = row / max_tokens;
-  return (row - e * max_tokens) < (int64_t)counts[e];
-}
-
 template <bool UE8M0, int LANES>
 __global__ __launch_bounds__(256) void stage_quant_kernel(
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
@@ -79,51 +68,6 @@ __global__ __launch_bounds__(256) void stage_quant_kernel(
   uint8_t* sf_row = UE8M0 ? xsf + row * sf_row_len : xsf + row * (int64_t)G * 4;
   quantize_store<UE8M0, LANES>(f, lane_g, xq + gid * GROUP + lane_g * 8, sf_row, g, G,
                                sf_row_len);
-}
-
-// Per-128 groups (UE8M0 or fp32 scales): 8 lanes per group, 16 values per
-// lane from two adjacent 16-byte loads and one 16-byte store of codes.  The
-// hidden states are read once, so the loads are non-temporal; the codes are
-// not (the w13 GEMM re-reads them).  Twice the bytes in flight per thread
-// of the 16-lane form: 21.3 -> 19.4 us at the DSv3-shaped prefill batch
-// (MALL flushed), bit-identical.
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-template <bool UE8M0>
-__global__ __launch_bounds__(256) void stage_quant128_kernel(
-    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
-    int64_t num_groups, int G, int sf_row_len, const int32_t* __restrict__ counts,
-    int max_tokens) {
-  const int64_t gid = (int64_t)blockIdx.x * 32 + threadIdx.x / 8;
-  const int lane8 = threadIdx.x % 8;
-  if (gid >= num_groups) return;
-  const int64_t row = gid / G;
-  const int g = (int)(gid - row * G);
-  if (!row_live(row, counts, max_tokens)) return;
-  const u32x4* src = reinterpret_cast<const u32x4*>(x + gid * kGroup) + 2 * lane8;
-  const u32x4 a = __builtin_nontemporal_load(src);
-  const u32x4 b = __builtin_nontemporal_load(src + 1);
-  float f[16];
-  unpack8(make_uint4(a.x, a.y, a.z, a.w), f);
-  unpack8(make_uint4(b.x, b.y, b.z, b.w), f + 8);
-  float amax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  amax = row8_max(amax);
-  const GroupScale gs = group_scale<UE8M0>(amax);
-  uint4 q;
-  q.x = f32x4_to_e4m3x4(f[0] * gs.recip, f[1] * gs.recip, f[2] * gs.recip, f[3] * gs.recip);
-  q.y = f32x4_to_e4m3x4(f[4] * gs.recip, f[5] * gs.recip, f[6] * gs.recip, f[7] * gs.recip);
-  q.z = f32x4_to_e4m3x4(f[8] * gs.recip, f[9] * gs.recip, f[10] * gs.recip, f[11] * gs.recip);
-  q.w = f32x4_to_e4m3x4(f[12] * gs.recip, f[13] * gs.recip, f[14] * gs.recip, f[15] * gs.recip);
-  *reinterpret_cast<uint4*>(xq + gid * kGroup + lane8 * 16) = q;
-  if (UE8M0) {
-    uint8_t* sf_row = xsf + row * sf_row_len;
-    if (lane8 == 0) sf_row[g] = (uint8_t)gs.stored;
-    // the row's trailing pad bytes (4*ceil(G/4) - G of them) are zero
-    if (g == G - 1 && lane8 >= 1 && lane8 <= sf_row_len - G) sf_row[G + lane8 - 1] = 0;
-  } else {
-    if (lane8 == 0) reinterpret_cast<uint32_t*>(xsf + row * (int64_t)G * 4)[g] = gs.stored;
-  }
 }
 
 // bf16 staging without quantization: a masked 16-byte copy.
@@ -207,16 +151,8 @@ hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, 
     stage_quant_kernel<true, 4><<<blocks_for(rows * G, 64), 256, 0, stream>>>(
         (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, rows * G, G, G, counts, max_tokens);
   } else {
-    const int G = K / kGroup;
-    const int sf_row_len = 4 * ((G + 3) / 4);
-    if (quant == kQuantUe8m0)
-      stage_quant128_kernel<true><<<blocks_for(rows * G, 32), 256, 0, stream>>>(
-          (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, rows * G, G, sf_row_len, counts,
-          max_tokens);
-    else
-      stage_quant128_kernel<false><<<blocks_for(rows * G, 32), 256, 0, stream>>>(
-          (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, rows * G, G, sf_row_len, counts,
-          max_tokens);
+    // per-128 groups run inside the routing scan's launch (launch_route)
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

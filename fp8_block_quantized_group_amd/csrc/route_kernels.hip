@@ -114,7 +114,7 @@ __device__ int block_inclusive_scan(int v, int* buf) {
 // of the weights while others did most of the arithmetic.
 constexpr int kChunkCap = 2048;
 
-__global__ __launch_bounds__(1024) void route_scan_kernel(
+__device__ __forceinline__ void route_scan_body(
     int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
     int max_tokens, int tile_m, int max_tiles, int32_t* __restrict__ expert_num_tokens,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ tile_list) {
@@ -282,6 +282,37 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
   }
 }
 
+__global__ __launch_bounds__(1024) void route_scan_kernel(
+    int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
+    int max_tokens, int tile_m, int max_tiles, int32_t* __restrict__ expert_num_tokens,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ tile_list) {
+  route_scan_body(hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles, expert_num_tokens,
+                  expert_offsets, tile_list);
+}
+
+// The scan is one block of latency-bound work; the hidden states' group
+// quantization is independent of it and bandwidth-bound.  Block 0 runs the
+// scan while blocks 1.. quantize 128 groups each (quantize_group128), so the
+// scan hides under the quantization's memory stream: one launch instead of
+// two back to back.
+template <bool UE8M0>
+__global__ __launch_bounds__(1024) void route_scan_quant_kernel(
+    int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
+    int max_tokens, int tile_m, int max_tiles, int32_t* __restrict__ expert_num_tokens,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ tile_list,
+    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
+    int64_t num_groups, int G, int sf_row_len) {
+  if (blockIdx.x == 0) {
+    route_scan_body(hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles,
+                    expert_num_tokens, expert_offsets, tile_list);
+    return;
+  }
+  const int64_t gid = (int64_t)(blockIdx.x - 1) * 128 + threadIdx.x / 8;
+  if (gid >= num_groups) return;
+  quantize_group128<UE8M0>(x, xq, xsf, gid, threadIdx.x % 8, G, sf_row_len, counts_in,
+                           max_tokens);
+}
+
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
     const int64_t* __restrict__ idx, int T, int k, int E, const int32_t* __restrict__ hist_base,
     const int32_t* __restrict__ expert_offsets, int max_tokens, int32_t* __restrict__ row_src,
@@ -385,16 +416,33 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint
                         float* w_out, int32_t* hist, const int32_t* counts_in, int max_tokens,
                         int tile_m, int max_tiles, int32_t* expert_num_tokens,
                         int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
-                        int32_t* tile_list, hipStream_t stream) {
+                        int32_t* tile_list, hipStream_t stream, const StageQuant* sq) {
   const int64_t total = (int64_t)T * k;
   const int nblocks = (int)((total + kRouteChunk - 1) / kRouteChunk);
   if (nblocks > 0) {
     route_repack_hist_kernel<<<nblocks, kRouteThreads, 2 * E * sizeof(int32_t), stream>>>(
         topk_ids, topk_w, is_padding, T, k, E, eplb, idx_out, w_out, hist);
   }
-  route_scan_kernel<<<1, 1024, 0, stream>>>(hist, nblocks, E, counts_in, max_tokens, tile_m,
-                                            max_tiles, expert_num_tokens, expert_offsets,
-                                            tile_list);
+  if (sq != nullptr && sq->rows > 0) {
+    // the hidden states' per-128 quantization rides along with the scan
+    const int G = sq->K / kGroup;
+    const int64_t ng = sq->rows * G;
+    const unsigned grid = (unsigned)(1 + (ng + 127) / 128);
+    if (sq->ue8m0)
+      route_scan_quant_kernel<true><<<grid, 1024, 0, stream>>>(
+          hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles, expert_num_tokens,
+          expert_offsets, tile_list, (const uint16_t*)sq->x, (uint8_t*)sq->xq,
+          (uint8_t*)sq->xsf, ng, G, 4 * ((G + 3) / 4));
+    else
+      route_scan_quant_kernel<false><<<grid, 1024, 0, stream>>>(
+          hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles, expert_num_tokens,
+          expert_offsets, tile_list, (const uint16_t*)sq->x, (uint8_t*)sq->xq,
+          (uint8_t*)sq->xsf, ng, G, 4 * ((G + 3) / 4));
+  } else {
+    route_scan_kernel<<<1, 1024, 0, stream>>>(hist, nblocks, E, counts_in, max_tokens, tile_m,
+                                              max_tiles, expert_num_tokens, expert_offsets,
+                                              tile_list);
+  }
   if (nblocks > 0) {
     route_scatter_kernel<<<nblocks, kRouteThreads, E * sizeof(int32_t), stream>>>(
         idx_out, T, k, E, hist, expert_offsets, counts_in != nullptr ? max_tokens : 0, row_src,
