@@ -117,23 +117,25 @@ __device__ __forceinline__ bool row_live(int64_t row, const int32_t* counts, int
   return (row - e * max_tokens) < (int64_t)counts[e];
 }
 
-// The group quantizer on one 128-value group gid of bf16 rows of G groups
-// (per-128 scales, UE8M0 bytes in rows of sf_row_len or fp32 [rows, G]):
-// 8 lanes per group, 16 values per lane from two adjacent 16-byte loads and
-// one 16-byte store of codes.  The hidden states are read once, so the loads
-// are non-temporal; the codes are not (the w13 GEMM re-reads them).
+// The group quantizer on one group gid of GROUP values (128: per-128
+// scales, UE8M0 bytes in rows of sf_row_len or fp32 [rows, G]; 32: MXFP8,
+// E8M0 bytes in rows of G) of bf16 rows of G groups: GROUP/16 lanes per
+// group, 16 values per lane from two adjacent 16-byte loads and one 16-byte
+// store of codes.  The hidden states are read once, so the loads are
+// non-temporal; the codes are not (the w13 GEMM re-reads them).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-template <bool UE8M0>
-__device__ __forceinline__ void quantize_group128(const uint16_t* __restrict__ x,
-                                                  uint8_t* __restrict__ xq,
-                                                  uint8_t* __restrict__ xsf, int64_t gid,
-                                                  int lane8, int G, int sf_row_len,
-                                                  const int32_t* __restrict__ counts,
-                                                  int max_tokens) {
+template <int GROUP, bool UE8M0>
+__device__ __forceinline__ void quantize_group(const uint16_t* __restrict__ x,
+                                               uint8_t* __restrict__ xq,
+                                               uint8_t* __restrict__ xsf, int64_t gid, int lane,
+                                               int G, int sf_row_len,
+                                               const int32_t* __restrict__ counts,
+                                               int max_tokens) {
+  static_assert(GROUP == 128 || (GROUP == 32 && UE8M0), "per-128 groups, or MX groups of 32");
   const int64_t row = gid / G;
   const int g = (int)(gid - row * G);
   if (!row_live(row, counts, max_tokens)) return;
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + gid * kGroup) + 2 * lane8;
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + gid * GROUP) + 2 * lane;
   const u32x4_t a = __builtin_nontemporal_load(src);
   const u32x4_t b = __builtin_nontemporal_load(src + 1);
   float f[16];
@@ -142,21 +144,24 @@ __device__ __forceinline__ void quantize_group128(const uint16_t* __restrict__ x
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(f[i]));
-  amax = row8_max(amax);
+  // 8 lanes: two quad steps and row_half_mirror; 2 lanes: swap neighbours
+  amax = GROUP == 128 ? row8_max(amax) : fmaxf(amax, dpp_f32<0xB1>(amax));
   const GroupScale gs = group_scale<UE8M0>(amax);
   uint4 q;
   q.x = f32x4_to_e4m3x4(f[0] * gs.recip, f[1] * gs.recip, f[2] * gs.recip, f[3] * gs.recip);
   q.y = f32x4_to_e4m3x4(f[4] * gs.recip, f[5] * gs.recip, f[6] * gs.recip, f[7] * gs.recip);
   q.z = f32x4_to_e4m3x4(f[8] * gs.recip, f[9] * gs.recip, f[10] * gs.recip, f[11] * gs.recip);
   q.w = f32x4_to_e4m3x4(f[12] * gs.recip, f[13] * gs.recip, f[14] * gs.recip, f[15] * gs.recip);
-  *reinterpret_cast<uint4*>(xq + gid * kGroup + lane8 * 16) = q;
+  *reinterpret_cast<uint4*>(xq + gid * GROUP + lane * 16) = q;
   if (UE8M0) {
     uint8_t* sf_row = xsf + row * sf_row_len;
-    if (lane8 == 0) sf_row[g] = (uint8_t)gs.stored;
-    // the row's trailing pad bytes (4*ceil(G/4) - G of them) are zero
-    if (g == G - 1 && lane8 >= 1 && lane8 <= sf_row_len - G) sf_row[G + lane8 - 1] = 0;
+    if (lane == 0) sf_row[g] = (uint8_t)gs.stored;
+    // the row's trailing pad bytes (sf_row_len - G of them; 128-groups: up
+    // to 3, MX rows have none) are zero
+    if (GROUP == 128 && g == G - 1 && lane >= 1 && lane <= sf_row_len - G)
+      sf_row[G + lane - 1] = 0;
   } else {
-    if (lane8 == 0) reinterpret_cast<uint32_t*>(xsf + row * (int64_t)G * 4)[g] = gs.stored;
+    if (lane == 0) reinterpret_cast<uint32_t*>(xsf + row * (int64_t)G * 4)[g] = gs.stored;
   }
 }
 

@@ -35,9 +35,14 @@
 //    a short expert still keeps both busy.  Rows of a batched-masked slab
 //    past its count are therefore never read.
 //  * Work unit = (expert, BN-column weight tile, BM-row activation tile).
-//    The tile list comes from the routing step, heaviest experts first; the
-//    1-D grid is remapped so that each XCD processes a contiguous run of
-//    work, expert by expert, and re-reads shared tiles from its own L2.
+//    The tile list comes from the routing step, dealt into 8 XCD-balanced
+//    slices; block L runs on XCD L % 8, which walks its own slice in a
+//    zipper order (heavy groups from the front, light ones from the back)
+//    so that matrix-bound and weight-streaming tiles run together, while
+//    consecutive items still share weight or activation tiles in its L2.
+//  * Cache policy: weight tiles read by a single block stream with the
+//    non-temporal hint; the plain epilogue's outputs are stored
+//    non-temporally (the reduce reads them once).
 //  * LDS rows are 128 bytes; 16-byte chunks are XOR-swizzled per row so that
 //    the fragment reads of a wave spread over the banks.
 #include <stdlib.h>

@@ -74,9 +74,8 @@ struct GemmArgs {
   int Nout;                  // output columns, multiple of 128
 };
 
-// Staging on its own launch: the MXFP8 group quantizer (32-value groups) or
-// the bf16 copy.  Per-128 fp8 staging runs inside launch_route (StageQuant);
-// here it returns hipErrorInvalidValue.
+// Staging on its own launch: the bf16 copy.  fp8 staging runs inside
+// launch_route (StageQuant); here it returns hipErrorInvalidValue.
 hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, int K, int quant,
                               const int32_t* counts, int max_tokens, hipStream_t stream);
 
@@ -86,15 +85,16 @@ hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t 
                               int quant, const int32_t* num_rows, const int32_t* counts,
                               int max_tokens, int act, hipStream_t stream);
 
-// Optional: the hidden states' per-128 quantization (UE8M0 or fp32 scales)
-// run inside the routing scan's launch; rows / K / counts as for
-// launch_stage_quant.
+// Optional: the hidden states' group quantization run inside the routing
+// scan's launch: groups of 128 (UE8M0 or fp32 scales) or 32 (MXFP8, E8M0);
+// rows: staged rows ([T] or [E * max_tokens], masked by the counts).
 struct StageQuant {
   const void* x;
   void* xq;
   void* xsf;
   int64_t rows;
   int K;
+  int group;
   bool ue8m0;
 };
 

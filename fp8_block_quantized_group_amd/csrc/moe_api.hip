@@ -309,11 +309,12 @@ moe_status_t run_stage(const moe_problem_t* p, const Plan& pl, const void* hidde
                        float* w_out, const moe_routing_t* r, int32_t* hist,
                        hipStream_t stream) {
   const int32_t* cin = batched(p) ? counts_in : nullptr;
-  // per-128 fp8 quantization runs inside the routing scan's launch; the
-  // other schemes (MXFP8 groups of 32, the bf16 copy) launch on their own
-  const bool fused = p->act_quant == MOE_Q_FP8_UE8M0 || p->act_quant == MOE_Q_FP8_F32;
+  // fp8 quantization runs inside the routing scan's launch; the bf16 copy
+  // launches on its own
+  const bool fused = p->act_quant != MOE_Q_BF16;
   const moe::StageQuant sq{hidden, x_q, x_sf, pl.s.stage_rows, p->hidden,
-                           p->act_quant == MOE_Q_FP8_UE8M0};
+                           p->act_quant == MOE_Q_MXFP8 ? 32 : 128,
+                           p->act_quant != MOE_Q_FP8_F32};
   if (!fused) {
     const hipError_t err =
         moe::launch_stage_quant(hidden, x_q, x_sf, pl.s.stage_rows, p->hidden, p->act_quant,

@@ -15,10 +15,10 @@
 // 128-value group, a quad per 32-value group); each lane loads 8 bf16
 // (16 bytes), the lanes reduce |x| with DPP max steps, each lane writes 8
 // fp8 bytes.  A 64-lane wave covers 512 contiguous input values, so every
-// load and store instruction is fully coalesced.  (The hidden states'
-// per-128 staging uses quantize_group128 from device_common.h inside the
-// routing scan's launch; the kernels here stage MXFP8 groups, copy bf16 and
-// re-quantize the w2 input of the unfused path.)
+// load and store instruction is fully coalesced.  (The hidden states' fp8
+// staging uses quantize_group from device_common.h inside the routing scan's
+// launch; the kernels here copy bf16 and re-quantize the w2 input of the
+// unfused path.)
 #include "device_common.h"
 #include "kernels.h"
 
@@ -48,26 +48,6 @@ __device__ __forceinline__ void quantize_store(const float f[8], int lane16, uin
   } else {
     if (lane16 == 0) reinterpret_cast<uint32_t*>(sf_row)[g] = gs.stored;
   }
-}
-
-template <bool UE8M0, int LANES>
-__global__ __launch_bounds__(256) void stage_quant_kernel(
-    const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
-    int64_t num_groups, int G, int sf_row_len, const int32_t* __restrict__ counts,
-    int max_tokens) {
-  constexpr int GROUP = 8 * LANES;
-  const int64_t gid = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
-  const int lane_g = threadIdx.x % LANES;
-  if (gid >= num_groups) return;
-  const int64_t row = gid / G;
-  const int g = (int)(gid - row * G);
-  if (!row_live(row, counts, max_tokens)) return;
-  const uint4 v = reinterpret_cast<const uint4*>(x + gid * GROUP)[lane_g];
-  float f[8];
-  unpack8(v, f);
-  uint8_t* sf_row = UE8M0 ? xsf + row * sf_row_len : xsf + row * (int64_t)G * 4;
-  quantize_store<UE8M0, LANES>(f, lane_g, xq + gid * GROUP + lane_g * 8, sf_row, g, G,
-                               sf_row_len);
 }
 
 // bf16 staging without quantization: a masked 16-byte copy.
@@ -146,12 +126,8 @@ hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, 
     const int64_t nvec = rows * (K / 8);
     stage_copy_kernel<<<blocks_for(nvec, 256), 256, 0, stream>>>(
         (const uint4*)x, (uint4*)xq, nvec, K / 8, counts, max_tokens);
-  } else if (quant == kQuantMxfp8) {
-    const int G = K / 32;   // K is a multiple of 128: rows of G bytes, no pad
-    stage_quant_kernel<true, 4><<<blocks_for(rows * G, 64), 256, 0, stream>>>(
-        (const uint16_t*)x, (uint8_t*)xq, (uint8_t*)xsf, rows * G, G, G, counts, max_tokens);
   } else {
-    // per-128 groups run inside the routing scan's launch (launch_route)
+    // fp8 staging runs inside the routing scan's launch (launch_route)
     return hipErrorInvalidValue;
   }
   return hipGetLastError();

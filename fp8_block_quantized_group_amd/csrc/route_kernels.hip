@@ -292,10 +292,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
 
 // The scan is one block of latency-bound work; the hidden states' group
 // quantization is independent of it and bandwidth-bound.  Block 0 runs the
-// scan while blocks 1.. quantize 128 groups each (quantize_group128), so the
-// scan hides under the quantization's memory stream: one launch instead of
-// two back to back.
-template <bool UE8M0>
+// scan while blocks 1.. quantize 1024 / (GROUP / 16) groups each
+// (quantize_group), so the scan hides under the quantization's memory
+// stream: one launch instead of two back to back.
+template <int GROUP, bool UE8M0>
 __global__ __launch_bounds__(1024) void route_scan_quant_kernel(
     int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
     int max_tokens, int tile_m, int max_tiles, int32_t* __restrict__ expert_num_tokens,
@@ -307,10 +307,11 @@ __global__ __launch_bounds__(1024) void route_scan_quant_kernel(
                     expert_num_tokens, expert_offsets, tile_list);
     return;
   }
-  const int64_t gid = (int64_t)(blockIdx.x - 1) * 128 + threadIdx.x / 8;
+  constexpr int LANES = GROUP / 16;
+  const int64_t gid = (int64_t)(blockIdx.x - 1) * (1024 / LANES) + threadIdx.x / LANES;
   if (gid >= num_groups) return;
-  quantize_group128<UE8M0>(x, xq, xsf, gid, threadIdx.x % 8, G, sf_row_len, counts_in,
-                           max_tokens);
+  quantize_group<GROUP, UE8M0>(x, xq, xsf, gid, threadIdx.x % LANES, G, sf_row_len, counts_in,
+                               max_tokens);
 }
 
 __global__ __launch_bounds__(kRouteThreads) void route_scatter_kernel(
@@ -424,20 +425,26 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint
         topk_ids, topk_w, is_padding, T, k, E, eplb, idx_out, w_out, hist);
   }
   if (sq != nullptr && sq->rows > 0) {
-    // the hidden states' per-128 quantization rides along with the scan
-    const int G = sq->K / kGroup;
+    // the hidden states' group quantization rides along with the scan
+    const int G = sq->K / sq->group;
     const int64_t ng = sq->rows * G;
-    const unsigned grid = (unsigned)(1 + (ng + 127) / 128);
-    if (sq->ue8m0)
-      route_scan_quant_kernel<true><<<grid, 1024, 0, stream>>>(
+    const int per_block = 1024 / (sq->group / 16);
+    const unsigned grid = (unsigned)(1 + (ng + per_block - 1) / per_block);
+    const uint16_t* x = (const uint16_t*)sq->x;
+    uint8_t* xq = (uint8_t*)sq->xq;
+    uint8_t* xsf = (uint8_t*)sq->xsf;
+    if (sq->group == 32)
+      route_scan_quant_kernel<32, true><<<grid, 1024, 0, stream>>>(
           hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles, expert_num_tokens,
-          expert_offsets, tile_list, (const uint16_t*)sq->x, (uint8_t*)sq->xq,
-          (uint8_t*)sq->xsf, ng, G, 4 * ((G + 3) / 4));
+          expert_offsets, tile_list, x, xq, xsf, ng, G, G);
+    else if (sq->ue8m0)
+      route_scan_quant_kernel<128, true><<<grid, 1024, 0, stream>>>(
+          hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles, expert_num_tokens,
+          expert_offsets, tile_list, x, xq, xsf, ng, G, 4 * ((G + 3) / 4));
     else
-      route_scan_quant_kernel<false><<<grid, 1024, 0, stream>>>(
+      route_scan_quant_kernel<128, false><<<grid, 1024, 0, stream>>>(
           hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles, expert_num_tokens,
-          expert_offsets, tile_list, (const uint16_t*)sq->x, (uint8_t*)sq->xq,
-          (uint8_t*)sq->xsf, ng, G, 4 * ((G + 3) / 4));
+          expert_offsets, tile_list, x, xq, xsf, ng, G, 4 * ((G + 3) / 4));
   } else {
     route_scan_kernel<<<1, 1024, 0, stream>>>(hist, nblocks, E, counts_in, max_tokens, tile_m,
                                               max_tiles, expert_num_tokens, expert_offsets,
