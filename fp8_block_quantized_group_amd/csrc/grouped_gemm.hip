@@ -331,13 +331,25 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       tile = __builtin_amdgcn_readfirstlane(info[6] + (info[1] / S::BM) + (t - t0));
       w_once = S::BM <= 128 && !W4 && info[3] == 1;
     } else {
+      // Block order, in groups of 8 blocks: a group of one expert's blocks
+      // (consecutive m-tiles of a heavy expert) is taken n-tile-major, so
+      // that 8 consecutive items share a weight tile; other groups take each
+      // block's n-tiles consecutively (they share its activation rows).
       const int64_t nblk = min(max(*p.num_padded, 0) / S::BM, p.max_blocks);
       const int64_t work = nblk * NT;
       const int64_t per_xcd = (work + 7) / 8;
       const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
       if (blockIdx.x / 8 >= per_xcd || wl >= work) return;
-      tile = __builtin_amdgcn_readfirstlane((int)(wl / NT));
-      nt = __builtin_amdgcn_readfirstlane((int)(wl % NT));
+      const int64_t g0 = wl / (8 * NT) * 8;          // the group's first block
+      const int64_t r = wl - g0 * NT;
+      const bool full = g0 + 8 <= nblk;
+      if (full && p.expert_ids[g0] == p.expert_ids[g0 + 7]) {
+        tile = __builtin_amdgcn_readfirstlane((int)(g0 + r % 8));
+        nt = __builtin_amdgcn_readfirstlane((int)(r / 8));
+      } else {
+        tile = __builtin_amdgcn_readfirstlane((int)(g0 + r / NT));
+        nt = __builtin_amdgcn_readfirstlane((int)(r % NT));
+      }
     }
     // the block's routed entries (ids below numel) lead, padding follows
     e = __builtin_amdgcn_readfirstlane(p.expert_ids[tile]);
