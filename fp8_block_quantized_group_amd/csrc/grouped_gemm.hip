@@ -238,6 +238,19 @@ __device__ __forceinline__ void with_constant(int v, F&& f) {
   }
 }
 
+// MX weight-scale panel: row n's 16 bytes sit at position wsc_rot(n), a
+// rotation by 4 * ((n >> 4) & 3) inside each group of 16 rows.  One read of
+// the panel covers the 16 rows wn*WAVE_N + 16q + r + 4i (q, r < 4): unrotated
+// they are 256 bytes apart in groups of four and hit only 4 banks (4-way
+// conflicts, measured as ~2e8 conflict cycles per launch); rotated, their
+// positions are distinct modulo 16, so their words fall in distinct banks.
+__device__ __forceinline__ int wsc_rot(int n) {
+  return (n & ~15) | ((n + 4 * ((n >> 4) & 3)) & 15);
+}
+__device__ __forceinline__ int wsc_unrot(int pos) {
+  return (pos & ~15) | ((pos - 4 * ((pos >> 4) & 3)) & 15);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
 }
@@ -496,7 +509,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
                       : v4i{0, 0, 0, 0};
   uint32_t wsc_off = 0;
   if (MX) {
-    const int r = (wave * 64 + lane) % S::BN;
+    // this lane fills panel position (wave * 64 + lane) % BN with the row
+    // stored there
+    const int r = wsc_unrot((wave * 64 + lane) % S::BN);
     int64_t wrow = n0 + r;
     if (ACT) {
       const int q = r & 63, w = r >> 6;
@@ -552,8 +567,10 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // chunk 4kq + m of the row (the weight bytes 32kq + 8m + [0, 8) match)
   const int a16_frag = ml0 * AROW + ((4 * kq) ^ rho) * 16;
   const int sc_frag = SC_OFF + ml0 * 4;
-  // MX: weight row nl0's 16 bytes in a panel slot (+64 per sub-tile)
-  const int wsc_frag = S::STAGES * STAGE + nl0 * 16;
+  // MX: the panel positions of weight rows nl0 + 4i (sub-tile i)
+  int wsc_frag[S::TN];
+#pragma unroll
+  for (int i = 0; i < S::TN; ++i) wsc_frag[i] = S::STAGES * STAGE + wsc_rot(nl0 + 4 * i) * 16;
   const int scale_shift = 8 * kq;            // MX: this lane's 32-column k-group byte
   constexpr int kSubStride = 16 * S::WM;
   // the weight-scale block of this lane's output columns (ACT: lanes 0-31
@@ -666,7 +683,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
           wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         }
         sw[i] = (int)(*reinterpret_cast<const uint32_t*>(
-                          smem + wsc_frag + ((kb >> 2) & 1) * WSC_SLOT + 64 * i + (kb & 3) * 4) >>
+                          smem + wsc_frag[i] + ((kb >> 2) & 1) * WSC_SLOT + (kb & 3) * 4) >>
                       scale_shift);
       }
 #pragma unroll
