@@ -238,6 +238,13 @@ __device__ __forceinline__ void with_constant(int v, F&& f) {
   }
 }
 
+// MX fp8 rows: logical 16-byte chunk c of a k-step is stored at physical
+// chunk 2 (c mod 4) + (c >= 4) (before the row's XOR key), so the chunk pair
+// (kq, kq + 4) the MX operand layout gives lane group kq is read from
+// physical chunks (2kq, 2kq + 1) -- the block scheme's pattern, which reads
+// without bank conflicts.  mx_chunk_of(p) = the logical chunk at physical p.
+__device__ __forceinline__ int mx_chunk_of(int p) { return (p >> 1) | ((p & 1) << 2); }
+
 // MX weight-scale panel: row n's 16 bytes sit at position wsc_rot(n), a
 // rotation by 4 * ((n >> 4) & 3) inside each group of 16 rows.  One read of
 // the panel covers the 16 rows wn*WAVE_N + 16q + r + 4i (q, r < 4): unrotated
@@ -450,7 +457,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   for (int i = 0; i < BI; ++i) {
     const int slot = i * S::THREADS + tid;
     const int r = W4 ? slot >> 2 : slot >> 3;
-    const int c = W4 ? (slot & 3) ^ key_w4<S::LOG_4TN>(r) : (slot & 7) ^ key_b<S::LOG_4TN>(r);
+    const int c = W4   ? (slot & 3) ^ key_w4<S::LOG_4TN>(r)
+                  : MX ? mx_chunk_of((slot & 7) ^ key_b<S::LOG_4TN>(r))
+                       : (slot & 7) ^ key_b<S::LOG_4TN>(r);
     int64_t wrow = r;
     if (ACT) {
       // tile row r = 64*w + q: gate row j0 + 32w + q (q < 32), else up row
@@ -485,7 +494,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     // bf16 rows (16 chunks) use key r & 15: a fragment read touches 16
     // consecutive rows at one chunk index
     const int r = slot / ACH;
-    const int c = A16 ? (slot % ACH) ^ (r & 15) : (slot & 7) ^ key_a(r);
+    const int c = A16  ? (slot % ACH) ^ (r & 15)
+                  : MX ? mx_chunk_of((slot & 7) ^ key_a(r))
+                       : (slot & 7) ^ key_a(r);
     a_off[i] = (r < rows_here) ? (uint32_t)(a_row_of(r) * p.Kd * (A16 ? 2 : 1) + c * 16)
                                : kOutOfRange;
   }
@@ -543,13 +554,15 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // The 16x16x128 f8f6f4 MFMA reads lane l's 32 operand bytes as k values
   // 16*(l>>4) + [0, 16) (registers 0-3) and 64 + 16*(l>>4) + [0, 16)
   // (registers 4-7), and takes the E8M0 scale of 32-column block b from lane
-  // group b: under MX, lane group kq therefore loads 16-byte chunks kq and
-  // kq + 4 of the row's 128-byte k-step.  With per-128 promotion any
-  // consistent placement gives the same sum; there chunks 2kq and 2kq + 1
-  // (adjacent) measured a few percent faster.
+  // group b: under MX, lane group kq therefore needs 16-byte chunks kq and
+  // kq + 4 of the row's 128-byte k-step, which the copies place at physical
+  // chunks 2kq and 2kq + 1 (mx_chunk_of).  With per-128 promotion any
+  // consistent placement gives the same sum; there the logical chunks 2kq and
+  // 2kq + 1 are read.  Either way every lane reads physical chunks 2kq and
+  // 2kq + 1 (before the row's XOR key).
   const int rho = lane & 15;
   const int kq = lane >> 4;
-  const int c0 = MX ? kq : 2 * kq, c1 = MX ? kq + 4 : 2 * kq + 1;
+  const int c0 = 2 * kq, c1 = 2 * kq + 1;
   // weight sub-tile i's row for this lane is nl0 + 4*i (same swizzle key)
   const int nl0 = wn * S::WAVE_N + (rho >> 2) * (4 * S::TN) + (rho & 3);
   // e2m1 weights: lane group kq holds k = 32kq + [0, 32), one 16-byte chunk
