@@ -238,6 +238,19 @@ __device__ __forceinline__ void with_constant(int v, F&& f) {
   }
 }
 
+// bf16 activation rows (256 bytes per k-step): the row is stored as two
+// 128-byte virtual rows v = 2r + bit 2 of the chunk, chunk
+// cc = (c & 3) | (c >> 3) << 2 of v at position cc ^ key_a(v).  Read m of a
+// k-step gives lane group kq chunk 4kq + m: per 16-lane pass, 16 rows at one
+// chunk.  Probed on the part (SQ_LDS_BANK_CONFLICT per ds_read_b128): a
+// plain 256-byte row with key r & 15 costs 4 conflict cycles per read; this
+// layout none.  a16_chunk_at(r, p) = the logical chunk at position p of row r.
+__device__ __forceinline__ int a16_chunk_at(int r, int p) {
+  const int b = p >> 3;
+  const int cc = (p & 7) ^ key_a(2 * r + b);
+  return (cc & 3) | (b << 2) | ((cc >> 2) << 3);
+}
+
 // MX fp8 rows: logical 16-byte chunk c of a k-step is stored at physical
 // chunk 2 (c mod 4) + (c >= 4) (before the row's XOR key), so the chunk pair
 // (kq, kq + 4) the MX operand layout gives lane group kq is read from
@@ -491,10 +504,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
     const int slot = i * S::THREADS + tid;
-    // bf16 rows (16 chunks) use key r & 15: a fragment read touches 16
-    // consecutive rows at one chunk index
+    // bf16 rows (16 chunks): the two-virtual-row layout of a16_chunk_at
     const int r = slot / ACH;
-    const int c = A16  ? (slot % ACH) ^ (r & 15)
+    const int c = A16  ? a16_chunk_at(r, slot % ACH)
                   : MX ? mx_chunk_of((slot & 7) ^ key_a(r))
                        : (slot & 7) ^ key_a(r);
     a_off[i] = (r < rows_here) ? (uint32_t)(a_row_of(r) * p.Kd * (A16 ? 2 : 1) + c * 16)
@@ -578,7 +590,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int a_frag1 = ml0 * kRowBytes + ((c1 ^ key_a(ml0)) << 4);
   // bf16 activations: MFMA m of a k-step covers k = 32kq + 8m + [0, 8), i.e.
   // chunk 4kq + m of the row (the weight bytes 32kq + 8m + [0, 8) match)
-  const int a16_frag = ml0 * AROW + ((4 * kq) ^ rho) * 16;
+  const int a16_v = 2 * ml0 + (kq & 1);                  // virtual row of chunk 4kq
+  const int a16_frag = a16_v * 128 + ((((kq >> 1) << 2) ^ key_a(a16_v)) << 4);
   const int sc_frag = SC_OFF + ml0 * 4;
   // MX: the panel positions of weight rows nl0 + 4i (sub-tile i)
   int wsc_frag[S::TN];
