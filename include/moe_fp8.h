@@ -190,6 +190,17 @@ typedef struct {
                               block size moe_forward uses)                    */
 } moe_sizes_t;
 
+/* Tile height.  tile_m follows the expected rows per expert, T * top_k / E:
+ * 16, 32 or 64 rows up to 12, 24 or 48 rows per expert, 128 up to 128, and
+ * 256 above (at most 128 for bf16 activations).  Two environment variables
+ * override the choice for tuning runs.  MOE_TILE_M = 16 | 32 | 64 | 128 |
+ * 192 | 256 (192 and 256 not for bf16; other values are ignored) is read by
+ * every call; all calls of one layer must see the same value, since the
+ * stage builds the tile schedule for the height the GEMM calls then read it
+ * with.  MOE_GEMM_WIDE = 0 | 1 picks 128 or 256 output columns for the
+ * 128-row tiles of the unfused GEMMs; it is read once per scale scheme, at
+ * its first GEMM call, and does not change the schedule. */
+
 /* Sizes of every buffer of `p` (host only). */
 moe_status_t moe_routing_sizes(const moe_problem_t* p, moe_sizes_t* out);
 
