@@ -52,6 +52,14 @@ SMALL = {
     "mx4_ragged": moe_synth.custom(name="mx4_ragged", T=300, E=5, top_k=3, K=384, N=384,
                                    seed=27, pad_frac=0.07, act_quant="mxfp8",
                                    weight_quant="mxfp4"),
+    # zipf-skewed routing with fp32 scales and in the batched layout: experts
+    # of a few rows next to experts of several 128-row tiles
+    "skewed_fp32": moe_synth.custom(name="skewed_fp32", T=400, E=16, top_k=4, K=256, N=256,
+                                    seed=31, routing="zipf", zipf_s=1.1, pad_frac=0.05,
+                                    act_quant="fp32"),
+    "skewed_batched": moe_synth.custom(name="skewed_batched", T=400, E=8, top_k=2, K=512,
+                                       N=256, seed=32, layout="batched", max_tokens=400,
+                                       routing="zipf", zipf_s=1.1),
     "mx4_skewed": moe_synth.custom(name="mx4_skewed", T=400, E=16, top_k=4, K=256, N=256,
                                    seed=28, routing="zipf", zipf_s=1.1, act_quant="mxfp8",
                                    weight_quant="mxfp4"),
