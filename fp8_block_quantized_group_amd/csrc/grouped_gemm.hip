@@ -362,7 +362,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       if (!schedule_item(t, nt, info)) return;
       const int t0 = (int)(info - (p.tile_list + 4)) / 8;
       tile = __builtin_amdgcn_readfirstlane(info[6] + (info[1] / S::BM) + (t - t0));
-      w_once = S::BM <= 128 && !W4 && info[3] == 1;
+      w_once = S::BM <= 128 && !W4 && info[4] <= S::BM;
     } else {
       // Block order, in groups of 8 blocks: a group of one expert's blocks
       // (consecutive m-tiles of a heavy expert) is taken n-tile-major, so
@@ -413,7 +413,6 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     const int32_t* info = nullptr;
     if (!schedule_item(t, nt, info)) return;
     const int t0 = (int)(info - (p.tile_list + 4)) / 8;
-    const int mtiles = info[3];
     tile = t;
     e = info[0];
     m0 = info[1] + (tile - t0) * S::BM;
@@ -424,7 +423,10 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     // Tiles of 192 / 256 rows are picked for experts with hundreds of rows,
     // whose weight tiles are shared: those shapes keep one load form (the
     // run-time choice alone cost 2-3 % on the Qwen3-shaped fused w13).
-    w_once = S::BM <= 128 && !W4 && mtiles == 1;
+    // An expert of one m-tile is the only reader of its weight tiles; the
+    // last chunk of a longer expert is not (its other chunks read the same
+    // tiles), whatever that chunk's own size.
+    w_once = S::BM <= 128 && !W4 && info[4] <= S::BM;
     base = info[5];
   }
   const int n0 = nt * S::BN;          // first output column (plain GEMM)

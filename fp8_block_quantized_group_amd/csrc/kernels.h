@@ -139,6 +139,9 @@ inline hipError_t launch_grouped_gemm(const GemmArgs& args, int tile_m, int max_
   }
 }
 
+// blocks of the reduce kernels' one-dimensional grid (must be < 2^31)
+int64_t reduce_blocks(int T, int K);
+
 hipError_t launch_topk_reduce(const void* down, const int32_t* slot_row, const float* w, void* out,
                               int T, int k, int K, hipStream_t stream);
 

@@ -128,6 +128,8 @@ moe_status_t validate_problem(const moe_problem_t* p) {
                                     : (int64_t)p->num_tokens * p->top_k;
     const int64_t in_rows = batched(p) ? rows : p->num_tokens;
     const int64_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
+    // (this also bounds T * hidden, so the reduce's one-dimensional grid of
+    // T * ceil(hidden / 1024) blocks stays far below 2^31)
     if (in_rows * p->hidden * elem >= ((int64_t)7 << 29) ||
         rows * p->intermediate * elem >= ((int64_t)7 << 29))
       return fail(MOE_ERR_UNSUPPORTED, "activation buffers are limited to 3.5 GiB");

@@ -10,8 +10,9 @@
 //
 // out[t, c] = bf16( sum_{j ascending, slot_row[t,j] >= 0} w[t,j] * down[slot_row[t,j], c] )
 //
-// One block of 128 threads covers 1024 columns of one token; each thread
-// owns 8 columns (one 16-byte load per routed row, one 16-byte store).  The
+// One block of 128 threads covers 1024 columns of one token (block b: token
+// b / column blocks, so the grid is one-dimensional and any token count the
+// host validation accepts fits it); each thread owns 8 columns (one 16-byte load per routed row, one 16-byte store).  The
 // token's slot rows and weights are block-uniform, so they come in through
 // scalar loads; the row loads of a thread are issued 8 at a time so that
 // they are in flight together.  Every byte is touched once, so loads and
@@ -44,9 +45,9 @@ constexpr int kReduceCols = kReduceThreads * 8;
 __global__ __launch_bounds__(kReduceThreads) void topk_reduce_kernel(
     const uint16_t* __restrict__ down, const int32_t* __restrict__ slot_row,
     const int64_t* __restrict__ idx, const float* __restrict__ w, uint16_t* __restrict__ out,
-    int k, int K, int E) {
-  const int t = blockIdx.y;
-  const int c = blockIdx.x * kReduceCols + threadIdx.x * 8;
+    int k, int K, int E, int col_blocks) {
+  const int t = (int)(blockIdx.x / (unsigned)col_blocks);
+  const int c = (int)(blockIdx.x - (unsigned)t * col_blocks) * kReduceCols + threadIdx.x * 8;
   if (c >= K) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   const float* wt = w + (int64_t)t * k;
@@ -97,21 +98,29 @@ __global__ __launch_bounds__(kReduceThreads) void topk_reduce_kernel(
 
 }  // namespace
 
+int64_t reduce_blocks(int T, int K) {
+  return (int64_t)T * ((K + kReduceCols - 1) / kReduceCols);
+}
+
 hipError_t launch_topk_reduce(const void* down, const int32_t* slot_row, const float* w, void* out,
                               int T, int k, int K, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((K + kReduceCols - 1) / kReduceCols, T);
-  topk_reduce_kernel<<<grid, kReduceThreads, 0, stream>>>(
-      (const uint16_t*)down, slot_row, nullptr, w, (uint16_t*)out, k, K, 0);
+  const int64_t blocks = reduce_blocks(T, K);
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  topk_reduce_kernel<<<dim3((unsigned)blocks), kReduceThreads, 0, stream>>>(
+      (const uint16_t*)down, slot_row, nullptr, w, (uint16_t*)out, k, K, 0,
+      (K + kReduceCols - 1) / kReduceCols);
   return hipGetLastError();
 }
 
 hipError_t launch_fused_mul_sum(const void* down, const int64_t* idx, const float* w, void* out,
                                 int T, int k, int K, int E, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((K + kReduceCols - 1) / kReduceCols, T);
-  topk_reduce_kernel<<<grid, kReduceThreads, 0, stream>>>(
-      (const uint16_t*)down, nullptr, idx, w, (uint16_t*)out, k, K, E);
+  const int64_t blocks = reduce_blocks(T, K);
+  if (blocks >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  topk_reduce_kernel<<<dim3((unsigned)blocks), kReduceThreads, 0, stream>>>(
+      (const uint16_t*)down, nullptr, idx, w, (uint16_t*)out, k, K, E,
+      (K + kReduceCols - 1) / kReduceCols);
   return hipGetLastError();
 }
 

@@ -10,10 +10,14 @@
  *      ("vllm.model_executor.layers.fused_moe.experts.fused_humming_moe",
  *      HummingGroupedExperts.apply: moe_prepare_scatter / moe_permute;
  *      BatchedHummingGroupedExperts.apply: expert_num_tokens);
- *   3. grouped GEMM with the fused gate/up weights w13;
+ *   3. grouped GEMM with the fused gate/up weights w13
+ *      ("...experts.fused_humming_moe", HummingGroupedExperts.apply and
+ *      BatchedHummingGroupedExperts.apply: the humming_forward call on the
+ *      "w13" sublayer through HummingExpertsBase.process_input);
  *   4. SiLU(gate) * up re-quantized to fp8 (HummingExpertsBase.process_input
  *      with an activation);
- *   5. grouped GEMM with the down weights w2;
+ *   5. grouped GEMM with the down weights w2 (the same apply methods: the
+ *      humming_forward call on the "w2" sublayer);
  *   6. router-weighted top-k reduce back to token order (moe_unpermute /
  *      moe_fused_mul_sum).
  *
@@ -119,8 +123,12 @@ typedef enum {
 
 /* Problem description (host struct).  T tokens, hidden size K, intermediate
  * size N, E physical experts, top_k routed experts per token.
- * Requirements: K and N multiples of 128; 1 <= E <= 1024; 1 <= top_k;
- * T * top_k < 2^31; batched layout needs max_tokens_per_expert >= 1. */
+ * Requirements: K and N multiples of 128 (at most 32768); 1 <= E <= 1024;
+ * 1 <= top_k; T * top_k < 2^31; batched layout needs
+ * max_tokens_per_expert >= 1; each activation buffer (staged rows * K and
+ * expert rows * N elements) under 3.5 GiB.  Every call checks these before
+ * it enqueues anything (MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED); no
+ * launch grid then exceeds its limits (token counts ride on grid x). */
 typedef struct {
   int32_t num_tokens;
   int32_t hidden;
@@ -229,7 +237,11 @@ moe_status_t moe_stage(const moe_problem_t* p, const void* hidden,
                        float* topk_w_out, const moe_routing_t* routing, void* ws,
                        size_t ws_bytes, void* stream);
 
-/* Step 3: gate_up[r, :] = block-scaled fp8 GEMM of activation row r with
+/* Step 3 ("...experts.fused_humming_moe", HummingGroupedExperts.apply and
+ * BatchedHummingGroupedExperts.apply: humming_forward on the "w13" sublayer,
+ * with the weight / activation pair of HummingExpertsBase.
+ * _supports_quant_scheme).
+ * gate_up[r, :] = block-scaled fp8 GEMM of activation row r with
  * w13[e] for every routed row r of expert e (rows from `routing`; the
  * contiguous layout gathers x_q rows through row_src).  gate_up: bf16
  * [expert_rows, 2N]; rows past an expert's count are not written. */
@@ -264,8 +276,12 @@ moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
                              const moe_routing_t* routing, void* a2_q, void* a2_sf,
                              void* stream);
 
-/* Step 5: down[r, :] = block-scaled GEMM of a2 row r with w2[e] (fp8 or bf16
- * a2 per the activation scheme); down: bf16 [expert_rows, K]. */
+/* Step 5 ("...experts.fused_humming_moe", HummingGroupedExperts.apply and
+ * BatchedHummingGroupedExperts.apply: humming_forward on the "w2" sublayer,
+ * fed by the activation buffer).
+ * down[r, :] = block-scaled GEMM of a2 row r with w2[e] (fp8 or bf16 a2 per
+ * the activation scheme); down: bf16 [expert_rows, K]; rows past an expert's
+ * count are not written. */
 moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const void* a2_sf,
                                  const moe_routing_t* routing, const void* w2,
                                  const void* w2_sf, void* down, void* stream);
@@ -335,7 +351,13 @@ moe_status_t moe_grouped_gemm_w2_indexed(
 moe_status_t moe_fused_mul_sum(const moe_problem_t* p, const void* down, const int64_t* topk_idx,
                                const float* topk_w, void* out, void* stream);
 
-/* Steps 1-6 on one stream (stage, fused w13 + activation, w2, reduce).
+/* Steps 1-6 on one stream: the staging of prepare_megamoe_inputs
+ * ("vllm.model_executor.layers.fused_moe.prepare_megamoe") followed by one
+ * apply() of the experts ("...experts.fused_humming_moe",
+ * HummingGroupedExperts.apply for the contiguous layout,
+ * BatchedHummingGroupedExperts.apply for the batched one,
+ * HummingIndexedExperts.apply for the indexed one): fused w13 + activation,
+ * w2, reduce.
  * Arguments as in moe_stage plus the weights and out bf16 [T, K]; ws: device
  * workspace of moe_workspace_size bytes.  Any supported scheme pair and
  * activation (_NO_MUL ones run the w13 GEMM and the activation kernel
@@ -349,7 +371,15 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
                          const void* w2, const void* w2_sf, void* out, void* ws,
                          size_t ws_bytes, void* stream);
 
-/* Message of the last failed call on this thread ("" if none). */
+/* Message of the last failed call on this thread ("" if none).  The
+ * argument errors it describes follow the ValueError conditions of
+ * prepare_megamoe_inputs and _resolve_hidden_quant
+ * ("vllm.model_executor.layers.fused_moe.prepare_megamoe": hidden size not a
+ * multiple of 128, mismatched top-k shapes, a scale buffer given or missing
+ * for the scheme) and the experts' apply() preconditions (batched format
+ * without expert_num_tokens); launch failures are reported as
+ * MOE_ERR_LAUNCH with the HIP error string.  The pointer stays valid until
+ * the next call on the same thread. */
 const char* moe_last_error(void);
 
 #ifdef __cplusplus

@@ -150,16 +150,28 @@ def ue8m0_decode(e) -> np.ndarray:
 # O2: per-128-group fp8 quantization  [STAGE, _quantize_fp8_groups]
 # ---------------------------------------------------------------------------
 
+def ceil_log2(s) -> np.ndarray:
+    """ceil(log2 s) for positive fp32 s, exactly: frexp writes s = m * 2^x
+    with m in [0.5, 1), so log2 s lies in [x - 1, x) and equals x - 1 only
+    when m = 0.5 (s is a power of two).  Infinite or NaN s gives a value
+    above every clamp (the largest scale)."""
+    s = np.asarray(s, dtype=np.float64)
+    m, x = np.frexp(np.where(np.isfinite(s), s, 1.0))
+    c = np.where(m == 0.5, x - 1, x).astype(np.int64)
+    return np.where(np.isfinite(s), c, 1 << 20)
+
+
 def quantize_groups(x32, ue8m0: bool, group: int = GROUP):
     """Quantize rows of fp32 values in groups of ``group`` consecutive columns
     (128 for the block scheme, 32 for MXFP8; any divisor of 128 for [STAGE]).
 
     Per group, in fp32: amax = max|x|, amax = max(amax, 1e-4),
-    s = amax / 448.  UE8M0: the scale is rounded up to a power of two by
-    taking the fp32 exponent field of s plus one when its mantissa field is
-    non-zero, clamped to [1, 254]; the quantizing scale is 2^(e-127) and the
-    stored value is the byte e.  fp32: the quantizing scale is s itself and
-    the stored value is s.  Values are x * (1/scale) converted to e4m3fn.
+    s = amax / 448 (one correctly rounded fp32 division).  UE8M0: the scale
+    is s rounded up to the next power of two, 2^c with c = ceil(log2 s),
+    whose biased exponent e = c + 127 is clamped to [1, 254]; the quantizing
+    scale is 2^(e-127) and the stored value is the byte e.  fp32: the
+    quantizing scale is s itself and the stored value is s.  Values are
+    x * (1/scale) converted to e4m3fn.
 
     Returns (codes uint8 [rows, C], stored scales: uint8 [rows, G] exponents
     or float32 [rows, G]).
@@ -172,10 +184,8 @@ def quantize_groups(x32, ue8m0: bool, group: int = GROUP):
     amax = np.maximum(amax, np.float32(1.0e-4))
     s = (amax / np.float32(FP8_MAX)).astype(np.float32)
     if ue8m0:
-        bits = s.view(np.uint32)
-        e = ((bits >> 23) & 0xFF) + ((bits & 0x7FFFFF) != 0).astype(np.uint32)
-        e = np.minimum(np.maximum(e, 1), 254).astype(np.uint32)
-        qscale = (e << 23).view(np.float32)
+        e = np.clip(ceil_log2(s) + 127, 1, 254)
+        qscale = np.ldexp(np.float32(1.0), e - 127).astype(np.float32)
         stored = e.astype(np.uint8)
     else:
         qscale = s

@@ -8,14 +8,26 @@ Tolerances (derived in the design notes from the arithmetic):
     term bounds the fp8 MFMA's own accumulation error: a measured
     v_mfma_f32_16x16x128_f8f6f4 misses the exact 128-term sum by up to
     2^-12.3 (mean 2^-15.8) of the sum of |products|; and the relative
-    Frobenius difference is at most 2^-8;
+    Frobenius difference is at most 2^-8.  At most GEMM_DIFF_CEIL of the
+    bf16 outputs may differ from the oracle's at all (measured 1-2 %: the
+    MFMA error moves a value across a bf16 rounding boundary only when it
+    sits close to one);
   * re-quantized fp8 activations, from the oracle's own gate_up: at most
     1 ULP (sign-magnitude ordinal, +-0 equal) in at most 0.1% of elements;
     a UE8M0 exponent may differ only where amax/448 is within 2^-20
     (relative) of a power of two; fp32 scales within 2^-21 relative;
   * re-quantized fp8 activations at the end of the GPU's own chain: each
     value within half an fp8 step on each side plus the GEMM bound above
-    carried through silu(g) * u;
+    carried through silu(g) * u; at most CHAIN_DIFF_CEIL of the codes
+    differ, and at most CHAIN_MULTI_ULP_CEIL of them by more than 1 ULP
+    (measured about 0.003 %: only where g or u is a sum with heavy
+    cancellation, whose MFMA error bound, relative to the sum of |products|,
+    spans several fp8 steps of the small result).  The pages' 1-ULP,
+    0.1 % bar holds for the activation step in isolation (check_requant);
+    at the end of the chain the gate_up inputs themselves already differ in
+    1-2 % of elements by one bf16 unit (fp8 MFMA accumulation), and a
+    2^-8 relative move flips an fp8 code (2^-3 relative steps) with
+    probability about 2^-4 per moved input, so about 0.2 % of codes differ;
   * final output: relative Frobenius <= 1e-2, max |diff| <= 2e-2 * max |ref|.
 """
 import numpy as np
@@ -72,6 +84,10 @@ def fp8_ordinal(codes):
 
 
 MFMA_REL = 2.0 ** -11
+# ceilings on the fraction of differing elements (see the module docstring)
+GEMM_DIFF_CEIL = 0.04
+CHAIN_DIFF_CEIL = 0.003
+CHAIN_MULTI_ULP_CEIL = 1e-4
 
 
 def abs_gemm(a_codes, a_scale, w_codes, w_sf):
@@ -94,7 +110,15 @@ def abs_gemm_cfg(cfg, a_codes, a_stored, w_codes, w_sf):
                          np.asarray(w_codes) & (0x77 if fp4 else 0x7F), w_sf, fp4)
 
 
-def check_gemm(got_bits, ref_bits, s_abs, what):
+def within_rate(count, size, rate):
+    """count <= what a rate ceiling allows on ``size`` elements, with a
+    3-sigma Poisson allowance so that a handful of sampled rows is judged by
+    the same rate as a whole layer."""
+    lam = rate * size
+    return count <= lam + 3.0 * np.sqrt(lam)
+
+
+def check_gemm(got_bits, ref_bits, s_abs, what, max_frac=GEMM_DIFF_CEIL):
     g = O.bf16_to_f64(got_bits)
     r = O.bf16_to_f64(ref_bits)
     assert g.shape == r.shape == s_abs.shape, what
@@ -107,7 +131,12 @@ def check_gemm(got_bits, ref_bits, s_abs, what):
     den = np.linalg.norm(r)
     rel = np.linalg.norm(d) / den if den > 0 else 0.0
     assert rel <= 2.0 ** -8, f"{what}: relative Frobenius difference {rel:.3e}"
-    return np.count_nonzero(d) / max(d.size, 1)
+    ndiff = np.count_nonzero(d)
+    frac = ndiff / max(d.size, 1)
+    if max_frac is not None:
+        assert within_rate(ndiff, d.size, max_frac), \
+            f"{what}: {frac:.3%} of bf16 outputs differ (> {max_frac:.1%})"
+    return frac
 
 
 def _fp8_step(v_over_s):
@@ -177,11 +206,13 @@ def act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation="silu"):
 
 
 def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_gate_up, ue8m0,
-                        what, group=128, activation="silu"):
+                        what, group=128, activation="silu", max_frac=CHAIN_DIFF_CEIL):
     """End of the GPU's own chain: its gate_up may differ from the oracle's
     by the GEMM bound; carry that through the activation and allow half an
-    fp8 step of rounding on each side.  Returns the fraction of codes that
-    differ."""
+    fp8 step of rounding on each side.  At most ``max_frac`` of the codes
+    differ and at most CHAIN_MULTI_ULP_CEIL of them, among groups where both
+    sides chose the same scale, by more than 1 ULP (None: not checked).
+    Returns the fraction of codes that differ."""
     rows, N = ref_q.shape
     G = N // group
     _, dh = act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation)
@@ -195,7 +226,19 @@ def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_ga
     assert not bad.any(), f"{what}: {bad.sum()} values beyond the propagated bound"
     if ue8m0:
         assert np.abs(got_sf[:, :G].astype(int) - ref_sf[:, :G].astype(int)).max() <= 1
-    return np.count_nonzero(got_q != ref_q) / got_q.size
+        same = np.repeat(got_sf[:, :G] == ref_sf[:, :G], group, axis=1)
+    else:
+        same = np.repeat(got_sf[:, :G].view(np.uint32) == ref_sf[:, :G].view(np.uint32),
+                         group, axis=1)
+    multi = np.count_nonzero(same & (np.abs(fp8_ordinal(got_q) - fp8_ordinal(ref_q)) > 1))
+    ndiff = np.count_nonzero(got_q != ref_q)
+    frac = ndiff / got_q.size
+    if max_frac is not None:
+        assert within_rate(ndiff, got_q.size, max_frac), \
+            f"{what}: {frac:.3%} of a2 codes differ (> {max_frac:.2%})"
+        assert within_rate(multi, got_q.size, CHAIN_MULTI_ULP_CEIL), \
+            f"{what}: {multi} codes ({multi / got_q.size:.4%}) more than 1 ULP apart"
+    return frac
 
 
 def check_bf16_act_chain(got_bits, ref_bits, ref_gate_up_bits, s_abs_gate_up, what,

@@ -121,6 +121,26 @@ def test_scheme_pairs(lib):
         assert ei.value.status == status, (act, wq)
 
 
+def test_large_token_counts(lib):
+    """Token counts far past 65 535 (a grid-y limit) are valid: the reduce
+    puts tokens on its one-dimensional grid.  A count whose staged
+    activations would pass the 3.5 GiB buffer limit (32-bit buffer offsets)
+    is rejected by every call before anything is enqueued -- here
+    moe_topk_reduce and moe_forward with fake pointers, which a launch would
+    fault on."""
+    assert moe.sizes(moe.Problem(1 << 20, 2048, 512, 4, 1))["slots"] == 1 << 20
+    big = moe.Problem((1 << 21) + 8, 2048, 512, 4, 1)
+    with pytest.raises(moe.MoeError) as ei:
+        moe.sizes(big)
+    assert ei.value.status == -2 and "3.5 GiB" in lib.moe_last_error().decode()
+    V = _fake()
+    st = lib.moe_topk_reduce(ctypes.byref(big.c()), V, V, V, V, None)
+    assert st == -2 and "3.5 GiB" in lib.moe_last_error().decode()
+    st = lib.moe_forward(ctypes.byref(big.c()), V, None, V, V, None, None, V, V, V, V, V, V,
+                         1 << 62, None)
+    assert st == -2 and "3.5 GiB" in lib.moe_last_error().decode()
+
+
 def test_batched_needs_max_tokens(lib):
     p = moe.Problem(16, 256, 512, 4, 2, layout=moe.LAYOUT_BATCHED, max_tokens_per_expert=0)
     with pytest.raises(moe.MoeError):

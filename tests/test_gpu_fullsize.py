@@ -97,28 +97,67 @@ def test_full_size_sampled(name):
             assert np.array_equal(xsf, O.pack_ue8m0_rows(s_ref))
         else:
             assert np.array_equal(xsf.view(np.uint32), s_ref.view(np.uint32))
-    # a few whole tokens through the oracle
-    routed = np.flatnonzero((st["slot_row"] >= 0).any(axis=1))
-    tokens = sorted(set(rng.choice(routed, min(3, routed.size), replace=False).tolist()))
+    # whole tokens through the oracle: one routed to the hottest expert (the
+    # most m-tiles, and the deepest schedule chunks), one routed to the
+    # expert with the fewest rows (a single m-tile), and random ones
+    tokens = sample_tokens(st, rng)
     print(f"[fullsize] {name}: oracle on tokens {tokens}", flush=True)
     ref = O.forward_tokens(h, tokens, st)
     gate_up, a2_q, down = (to_np(chain[k]) for k in ("gate_up", "a2_q", "down"))
     a2_sf = None if chain["a2_sf"] is None else to_np(chain["a2_sf"])
-    for r, info in ref["rows"].items():
+    GN = cfg.N // grp
+    rows = sorted(ref["rows"])
+    gu_got, gu_want, gu_abs, dn_got, dn_want, dn_abs = [], [], [], [], [], []
+    for r in rows:
+        info = ref["rows"][r]
         e = info["expert"]
-        s_abs = abs_gemm_cfg(cfg, info["x_q"][None],
-                             None if info["x_sf"] is None else info["x_sf"][None],
-                             O._np(inp["w13"][e]), O._np(inp["w13_sf"][e]))
-        check_gemm(gate_up[r:r + 1], info["gate_up"][None], s_abs, f"{name} gate_up row {r}")
-        if cfg.act_quant == "bf16":
-            check_bf16_act_chain(a2_q[r:r + 1], info["a2_q"][None], info["gate_up"][None],
-                                 s_abs, f"{name} a2 row {r}")
-        else:
-            check_requant_chain(a2_q[r:r + 1], a2_sf[r:r + 1], info["a2_q"][None],
-                                info["a2_sf"][None], info["gate_up"][None], s_abs, ue,
-                                f"{name} a2 row {r}", grp)
-        check_output(down[r:r + 1], info["down"][None], f"{name} down row {r}")
+        w13e, w13s = O._np(inp["w13"][e]), O._np(inp["w13_sf"][e])
+        w2e, w2s = O._np(inp["w2"][e]), O._np(inp["w2_sf"][e])
+        gu_abs.append(abs_gemm_cfg(cfg, info["x_q"][None],
+                                   None if info["x_sf"] is None else info["x_sf"][None],
+                                   w13e, w13s)[0])
+        gu_got.append(gate_up[r])
+        gu_want.append(info["gate_up"])
+        # w2 on the GPU's own a2 row: the GEMM alone, to its element bound
+        a_row = a2_q[r:r + 1]
+        sf_row = None if a2_sf is None else a2_sf[r:r + 1, :GN]
+        dn_want.append(O.bf16_round(O.expert_gemm(cfg, a_row, sf_row, w2e, w2s))[0])
+        dn_abs.append(abs_gemm_cfg(cfg, a_row, sf_row, w2e, w2s)[0])
+        dn_got.append(down[r])
+    gu_got, gu_want, gu_abs = np.stack(gu_got), np.stack(gu_want), np.stack(gu_abs)
+    f13 = check_gemm(gu_got, gu_want, gu_abs, f"{name} gate_up rows {rows}")
+    f2 = check_gemm(np.stack(dn_got), np.stack(dn_want), np.stack(dn_abs),
+                    f"{name} down rows {rows}")
+    a2_want = np.stack([ref["rows"][r]["a2_q"] for r in rows])
+    if cfg.act_quant == "bf16":
+        fa = check_bf16_act_chain(a2_q[rows], a2_want, gu_want, gu_abs, f"{name} a2 rows")
+    else:
+        sf_want = np.stack([ref["rows"][r]["a2_sf"] for r in rows])
+        fa = check_requant_chain(a2_q[rows], a2_sf[rows], a2_want, sf_want, gu_want, gu_abs, ue,
+                                 f"{name} a2 rows", grp)
+    check_output(down[rows], np.stack([ref["rows"][r]["down"] for r in rows]),
+                 f"{name} down rows (oracle chain)")
     got = to_np(out)[tokens]
     want = np.stack([ref["out"][t] for t in tokens])
     rel, mx = check_output(got, want, f"{name} output rows {tokens}")
-    print(f"[fullsize] {name}: sampled rel_frobenius={rel:.3e}", flush=True)
+    print(f"[fullsize] {name}: {len(rows)} rows; differing gate_up {f13:.3%}, down {f2:.3%}, "
+          f"a2 {fa:.3%}; sampled output rel_frobenius={rel:.3e}", flush=True)
+
+
+def sample_tokens(st, rng, n_random=3):
+    """A token of the hottest expert, a token of the least loaded routed
+    expert (a single m-tile wherever some expert fits in one), and n_random
+    other routed tokens."""
+    ids, counts = st["ids"], st["counts"]
+    routed_slots = st["slot_row"] >= 0
+    routed = np.flatnonzero(routed_slots.any(axis=1))
+    picks = []
+    hot = int(np.argmax(counts))
+    live = np.flatnonzero(counts > 0)
+    cold = int(live[np.argmin(counts[live])])
+    for e in (hot, cold):
+        t_of_e = np.flatnonzero(((ids == e) & routed_slots).any(axis=1))
+        picks.append(int(rng.choice(t_of_e)))
+    rest = np.setdiff1d(routed, picks)
+    picks += rng.choice(rest, min(n_random, rest.size), replace=False).tolist()
+    return sorted(set(int(t) for t in picks))

@@ -66,6 +66,36 @@ SMALL = {
 }
 
 
+# Mid-size configs: K and N between 1152 and 2048, so each GEMM runs 9-16
+# k-steps.  Every LDS ring depth (2, 3 and 4 slots) wraps several times and
+# both slots of the MX weight-scale panel (which alternate every 4 k-steps)
+# are used; N = 1152 (hidden K = 1152 for w2's output) takes the 128-column
+# w2 tiles, 2048 the 256-column ones.  Run at tile heights 16, 128 and 256
+# (128 at most for bf16 activations) with every routed row compared.
+MID = {
+    "mid_ue8m0": moe_synth.custom(name="mid_ue8m0", T=320, E=6, top_k=3, K=2048, N=1152,
+                                  seed=41, routing="zipf", zipf_s=1.1, pad_frac=0.05),
+    "mid_fp32": moe_synth.custom(name="mid_fp32", T=320, E=7, top_k=3, K=1152, N=2048,
+                                 seed=42, act_quant="fp32", num_logical=5),
+    "mid_mxfp8": moe_synth.custom(name="mid_mxfp8", T=320, E=6, top_k=3, K=2048, N=1152,
+                                  seed=43, routing="zipf", zipf_s=1.1, pad_frac=0.05,
+                                  act_quant="mxfp8", weight_quant="mxfp8"),
+    "mid_mxfp4": moe_synth.custom(name="mid_mxfp4", T=320, E=6, top_k=3, K=1152, N=2048,
+                                  seed=44, routing="zipf", zipf_s=1.1, act_quant="mxfp8",
+                                  weight_quant="mxfp4"),
+    "mid_bf16": moe_synth.custom(name="mid_bf16", T=320, E=6, top_k=3, K=2048, N=1152,
+                                 seed=45, routing="zipf", zipf_s=1.1, pad_frac=0.05,
+                                 act_quant="bf16"),
+    "mid_batched": moe_synth.custom(name="mid_batched", T=320, E=4, top_k=2, K=1152,
+                                    N=2048, seed=46, layout="batched", max_tokens=384,
+                                    routing="zipf", zipf_s=1.1),
+}
+MID_TILES = [16, 128, 256]
+MID_CASES = [(n, t) for n in MID for t in MID_TILES
+             if not (MID[n].act_quant == "bf16" and t > 128)]
+CASES = {**SMALL, **MID}
+
+
 @pytest.fixture(scope="session")
 def gpu():
     if not torch.cuda.is_available():
@@ -80,7 +110,7 @@ _CACHE = {}
 def case(name):
     """(cfg, host inputs, device inputs, oracle forward) for a small config."""
     if name not in _CACHE:
-        cfg = SMALL[name]
+        cfg = CASES[name]
         inp = moe_synth.make_inputs(cfg, "cpu")
         h = O.host_inputs(inp)
         ref = O.forward(h)
@@ -458,9 +488,13 @@ def test_gemm_w13_act_fused_equals_chain(gpu, name, tile_m, monkeypatch):
     unfused pair is itself checked against the oracle above; the fused path
     additionally against the oracle's a2 through check_requant_chain."""
     monkeypatch.setenv("MOE_TILE_M", str(tile_m))
-    cfg, h, dev, ref = case(name)
-    if cfg.act_quant == "bf16" and tile_m > 128:
+    if CASES[name].act_quant == "bf16" and tile_m > 128:
         pytest.skip("bf16 activation tiles are at most 128 rows (LDS)")
+    _fused_equals_chain(name, tile_m)
+
+
+def _fused_equals_chain(name, tile_m):
+    cfg, h, dev, ref = case(name)
     p = problem(cfg)
     s = moe.sizes(p)
     assert s["tile_m"] == tile_m
@@ -585,6 +619,10 @@ def run_forward(cfg, dev):
 
 @pytest.mark.parametrize("name", list(SMALL))
 def test_forward_end_to_end(gpu, name):
+    _forward_end_to_end(name)
+
+
+def _forward_end_to_end(name):
     cfg, h, dev, ref = case(name)
     ue = O.act_e8m0(cfg)
     chain = run_chain(cfg, dev)
@@ -625,6 +663,44 @@ def test_every_tile_height(gpu, tile_m, monkeypatch):
         check_gemm(to_np(chain["gate_up"])[vr], ref["gate_up"][vr],
                    gemm_abs(cfg, h, ref, "w13")[vr], f"{name} gate_up tile_m={tile_m}")
         check_output(to_np(chain["out"]), ref["out"], f"{name} out tile_m={tile_m}")
+
+
+# ---------------------------------------------------------------------------
+# mid-size configs (9-16 k-steps per GEMM) at three tile heights
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,tile_m", MID_CASES)
+def test_mid_stage_route_and_act(gpu, name, tile_m, monkeypatch):
+    """Staging and routing bit-exact (the schedule for this tile height), and
+    the activation step in isolation on the oracle's gate_up."""
+    monkeypatch.setenv("MOE_TILE_M", str(tile_m))
+    assert moe.sizes(problem(MID[name]))["tile_m"] == tile_m
+    test_stage_and_route_bit_exact(gpu, name)
+    if tile_m == MID_TILES[0]:
+        test_act_requant_isolated(gpu, name)
+
+
+@pytest.mark.parametrize("name,tile_m", MID_CASES)
+def test_mid_gemms_isolated(gpu, name, tile_m, monkeypatch):
+    """Both GEMMs on the oracle's inputs, every routed row against the
+    oracle, nothing written outside the experts' rows."""
+    monkeypatch.setenv("MOE_TILE_M", str(tile_m))
+    cfg, h, dev, ref = case(name)
+    assert moe.sizes(problem(cfg))["tile_m"] == tile_m
+    _gemm_isolated(cfg, h, dev, ref, "w13")
+    _gemm_isolated(cfg, h, dev, ref, "w2")
+
+
+@pytest.mark.parametrize("name,tile_m", MID_CASES)
+def test_mid_fused_equals_chain(gpu, name, tile_m, monkeypatch):
+    monkeypatch.setenv("MOE_TILE_M", str(tile_m))
+    _fused_equals_chain(name, tile_m)
+
+
+@pytest.mark.parametrize("name,tile_m", MID_CASES)
+def test_mid_forward_end_to_end(gpu, name, tile_m, monkeypatch):
+    monkeypatch.setenv("MOE_TILE_M", str(tile_m))
+    _forward_end_to_end(name)
 
 
 # ---------------------------------------------------------------------------
@@ -684,6 +760,32 @@ def test_batched_empty_slabs_and_garbage(gpu):
     inp.update(moe_synth._stage_batched(cfg, inp["tokens"], inp["topk_ids"], "cpu"))
     h = O.host_inputs(inp)
     check_output(_layer_out(cfg, inp), O.forward(h)["out"], "batched with empty slabs")
+
+
+@pytest.mark.parametrize("indexed", [False, True])
+def test_reduce_many_tokens(gpu, indexed):
+    """70 000 tokens, past a 65 535 grid-y limit: the reduce puts tokens on
+    its one-dimensional grid.  moe_topk_reduce (slot rows, 5 % unrouted) and
+    moe_fused_mul_sum ((token, slot) rows, invalid ids unrouted) against the
+    oracle's reduce, every token."""
+    T, k, K, E = 70000, 2, 384, 4
+    rng = np.random.default_rng(61)
+    M = T * k
+    down = O.bf16_round(rng.standard_normal((M, K)))
+    w = rng.random((T, k)).astype(np.float32)
+    p = moe.Problem(T, K, 256, E, k)
+    out = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+    if indexed:
+        ids = rng.integers(0, E, (T, k)).astype(np.int64)
+        ids[rng.random((T, k)) < 0.05] = -1
+        slot_row = np.where(ids >= 0, np.arange(M).reshape(T, k), -1)
+        moe.fused_mul_sum(p, to_dev(down), to_dev(ids), to_dev(w), out)
+    else:
+        slot_row = rng.permutation(M).reshape(T, k).astype(np.int32)
+        slot_row[rng.random((T, k)) < 0.05] = -1
+        moe.topk_reduce(p, to_dev(down), to_dev(slot_row), to_dev(w), out)
+    torch.cuda.synchronize()
+    check_bf16_close(to_np(out), O.topk_reduce(down, slot_row, w), f"reduce of {T} tokens")
 
 
 def test_expert_count_multiple_of_tile(gpu, monkeypatch):
