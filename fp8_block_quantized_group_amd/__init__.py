@@ -66,7 +66,8 @@ EXPORTS = ("moe_routing_sizes", "moe_stage_workspace_size", "moe_workspace_size"
            "moe_grouped_gemm_w13", "moe_grouped_gemm_w13_act", "moe_act_requant",
            "moe_grouped_gemm_w2", "moe_topk_reduce", "moe_align_capacity",
            "moe_align_block_size", "moe_grouped_gemm_w13_act_indexed",
-           "moe_grouped_gemm_w2_indexed", "moe_fused_mul_sum", "moe_forward", "moe_last_error")
+           "moe_grouped_gemm_w2_indexed", "moe_fused_mul_sum", "moe_forward",
+           "moe_forward_static", "moe_last_error")
 
 _lib = None
 
@@ -100,6 +101,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_grouped_gemm_w2_indexed.argtypes = [P(_Problem), V, V, V, V, V, I32, V, V, V, V]
     lib.moe_fused_mul_sum.argtypes = [P(_Problem), V, V, V, V, V]
     lib.moe_forward.argtypes = [P(_Problem), V, V, V, V, V, P(_Eplb), V, V, V, V, V, V, S, V]
+    lib.moe_forward_static.argtypes = [P(_Problem), V, V, V, V, V, P(_Eplb), V, V, V, V, V, V]
     lib.moe_last_error.argtypes = []
     for name in EXPORTS:
         fn = getattr(lib, name)
@@ -330,6 +332,20 @@ def forward(p: Problem, hidden, topk_ids, topk_weights, w13, w13_sf, w2, w2_sf, 
         ctypes.byref(p.c()), _ptr(hidden), _ptr(expert_num_tokens), _ptr(topk_ids),
         _ptr(topk_weights), _ptr(is_padding), e[0] if e else None, _ptr(w13), _ptr(w13_sf),
         _ptr(w2), _ptr(w2_sf), _ptr(out), _ptr(ws), ws.numel(), _stream()))
+
+
+STATIC_SCRATCH_BYTES = 64 << 20      # MOE_STATIC_SCRATCH_BYTES
+
+
+def forward_static(p: Problem, hidden, topk_ids, topk_weights, w13, w13_sf, w2, w2_sf, out,
+                   is_padding=None, expert_num_tokens=None, eplb=None):
+    """moe_forward_static: the whole layer with the library's static
+    per-GPU workspace (no allocation; calls on one GPU must not overlap)."""
+    e = _eplb(eplb)
+    _check(load_library().moe_forward_static(
+        ctypes.byref(p.c()), _ptr(hidden), _ptr(expert_num_tokens), _ptr(topk_ids),
+        _ptr(topk_weights), _ptr(is_padding), e[0] if e else None, _ptr(w13), _ptr(w13_sf),
+        _ptr(w2), _ptr(w2_sf), _ptr(out), _stream()))
 
 
 class MoeLayer:

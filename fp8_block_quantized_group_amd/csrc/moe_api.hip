@@ -16,10 +16,18 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <string>
 
 #include "../../include/moe_fp8.h"
 #include "kernels.h"
+
+// Workspace of moe_forward_static: one copy per GPU, in the library's code
+// object, held until the process ends.  Host code never passes this name to
+// a kernel (on the host it is a stand-in, not a device address): the device
+// address comes from hipGetSymbolAddress, once per device
+// (static_scratch_for_current_device below).
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
 
 namespace {
 
@@ -441,6 +449,32 @@ moe_status_t run_mul_sum(const moe_problem_t* p, const void* down, const int64_t
   return launch_status(err, "fused_mul_sum");
 }
 
+// Device address of `scratch` on the current device, looked up on the
+// first call on each device with that device current and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+moe_status_t static_scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess)
+    return fail(MOE_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    err = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (err != hipSuccess || ptr == nullptr)
+      return fail(MOE_ERR_LAUNCH, "hipGetSymbolAddress(scratch) on device %d failed: %s", dev,
+                  hipGetErrorString(err));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 moe_status_t check_indexed(const moe_problem_t* p, const int32_t* sorted_ids,
                            const int32_t* expert_ids, const int32_t* num_padded, int bs) {
   if (batched(p))
@@ -705,6 +739,25 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
   CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s));
   CHECK(run_reduce(p, w.down, w.routing.slot_row, w.w, out, s));
   return ok();
+}
+
+moe_status_t moe_forward_static(const moe_problem_t* p, const void* hidden,
+                                const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
+                                const float* topk_weights, const uint8_t* is_padding,
+                                const moe_eplb_t* eplb, const void* w13, const void* w13_sf,
+                                const void* w2, const void* w2_sf, void* out, void* stream) {
+  CHECK(validate_problem(p));
+  if (p->num_tokens == 0) return ok();
+  const size_t need = carve(make_plan(p), p, nullptr).total;
+  if (need > (size_t)MOE_STATIC_SCRATCH_BYTES)
+    return fail(MOE_ERR_WORKSPACE,
+                "moe_forward_static: this problem needs %zu workspace bytes, the static scratch "
+                "holds %zu (call moe_forward with a workspace instead)",
+                need, (size_t)MOE_STATIC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  CHECK(static_scratch_for_current_device(&ws));
+  return moe_forward(p, hidden, expert_num_tokens_in, topk_ids, topk_weights, is_padding, eplb,
+                     w13, w13_sf, w2, w2_sf, out, ws, (size_t)MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

@@ -371,6 +371,28 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
                          const void* w2, const void* w2_sf, void* out, void* ws,
                          size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments and results as moe_forward (bit-identical output), without
+ * ws / ws_bytes: the workspace is a static device array of
+ * MOE_STATIC_SCRATCH_BYTES (64 MiB) inside the library, one per GPU, held by
+ * every GPU the library runs on until the process ends; a DeepSeek-V3-shaped
+ * decode batch (64 tokens, 256 experts, top-8, K 7168, N 2048) needs about
+ * 9 MB of it.  The call allocates nothing.  A problem whose
+ * moe_workspace_size exceeds the array is rejected with MOE_ERR_WORKSPACE
+ * before anything is enqueued.  The array's device address is looked up on
+ * the first call on each device (the current device; stream and buffers
+ * must belong to it).  All calls on one GPU share its array and leave their
+ * intermediates in it: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialized by the caller; nothing in the array
+ * needs to start at zero. */
+#define MOE_STATIC_SCRATCH_BYTES (64u << 20)
+moe_status_t moe_forward_static(const moe_problem_t* p, const void* hidden,
+                                const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
+                                const float* topk_weights, const uint8_t* is_padding,
+                                const moe_eplb_t* eplb, const void* w13, const void* w13_sf,
+                                const void* w2, const void* w2_sf, void* out, void* stream);
+
 /* Message of the last failed call on this thread ("" if none).  The
  * argument errors it describes follow the ValueError conditions of
  * prepare_megamoe_inputs and _resolve_hidden_quant

@@ -141,6 +141,22 @@ def test_large_token_counts(lib):
     assert st == -2 and "3.5 GiB" in lib.moe_last_error().decode()
 
 
+def test_static_forward_rejects_oversized_problems(lib):
+    """moe_forward_static checks the problem's workspace against its static
+    array before it touches the device (so this runs without a GPU)."""
+    p = moe.Problem.from_config(moe_synth.CONFIGS["dsv3_prefill"])
+    assert moe.workspace_size(p) > moe.STATIC_SCRATCH_BYTES
+    V = _fake()
+    st = lib.moe_forward_static(ctypes.byref(p.c()), V, None, V, V, None, None, V, V, V, V, V,
+                                None)
+    assert st == -3 and "static scratch" in lib.moe_last_error().decode()
+    # a DeepSeek-V3-shaped decode batch fits
+    assert moe.workspace_size(moe.Problem.from_config(moe_synth.CONFIGS["dsv3_decode"])) < \
+        moe.STATIC_SCRATCH_BYTES // 4
+    hdr = open(HEADER).read()
+    assert f"MOE_STATIC_SCRATCH_BYTES ({moe.STATIC_SCRATCH_BYTES >> 20}u << 20)" in hdr
+
+
 def test_batched_needs_max_tokens(lib):
     p = moe.Problem(16, 256, 512, 4, 2, layout=moe.LAYOUT_BATCHED, max_tokens_per_expert=0)
     with pytest.raises(moe.MoeError):
