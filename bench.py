@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--config", default="dsv3_prefill", choices=list(moe_synth.ALL_CONFIGS))
     ap.add_argument("--kernel-iters", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mfma-workload", default="qwen3",
+                    help="workload whose GEMMs are timed for the MFMA-bound figure "
+                         "('none' to skip)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--profile-pass", action="store_true",
                     help="for counter runs: a 1 GiB device copy (counter calibration), then "
@@ -98,6 +101,64 @@ def algorithmic(cfg, counts, T_valid):
     # indexed layout: slot rows and ids in, one sorted id per routed slot out
     a["align"] = cfg.T * k * (4 + 8) + M * 4
     return a
+
+
+def per_expert_bound_ms(cfg, counts):
+    """Lower bound of each grouped GEMM in ms: every routed expert either
+    streams its weights once from HBM or runs its rows on the matrix cores at
+    the dense fp8 peak, whichever is slower, summed over experts
+    (sum_e max(flops_e / P, weight_bytes_e / B))."""
+    K, N = cfg.K, cfg.N
+    w_elem = 0.5 if cfg.weight_quant == "mxfp4" else 1
+    if cfg.weight_quant == "fp8_block128":
+        w13_sf, w2_sf = (2 * N // 128) * (K // 128) * 4, (K // 128) * (N // 128) * 4
+    else:
+        w13_sf, w2_sf = 2 * N * (K // 32), K * (N // 32)
+    P, B = FP8_PEAK_TFLOPS * 1e12, HBM_PEAK_GBS * 1e9
+    m = counts[counts > 0].astype(np.float64)
+    b13 = np.maximum(2 * m * 2 * N * K / P, (2 * N * K * w_elem + w13_sf) / B).sum()
+    b2 = np.maximum(2 * m * N * K / P, (K * N * w_elem + w2_sf) / B).sum()
+    return 1e3 * b13, 1e3 * b2
+
+
+def gemm_figures(cfg, counts, t13_ms, t2_ms):
+    """TFLOP/s of both GEMMs, their fraction of the fp8 dense peak and of
+    the per-expert bound."""
+    M = float(counts.sum())
+    flops = 2.0 * M * 2 * cfg.N * cfg.K + 2.0 * M * cfg.N * cfg.K
+    tf = flops / ((t13_ms + t2_ms) * 1e-3) / 1e12
+    b13, b2 = per_expert_bound_ms(cfg, counts)
+    return {"gemm_tflops": round(tf, 2), "gemm_frac_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4),
+            "w13_bound_ms": round(b13, 4), "w2_bound_ms": round(b2, 4),
+            "w13_frac": round(b13 / t13_ms, 4), "w2_frac": round(b2 / t2_ms, 4),
+            "frac": round((b13 + b2) / (t13_ms + t2_ms), 4)}
+
+
+def mfma_bound_workload(name, iters, flush):
+    """The GEMMs of the MFMA-bound workload (every expert has hundreds of
+    rows), timed like the headline's kernels: MALL flushed before each
+    launch, on the stream the library launches on."""
+    cfg = moe_synth.ALL_CONFIGS[name]
+    log(f"[bench] MFMA-bound workload {name}: generating inputs")
+    inp = moe_synth.make_inputs(cfg, "cuda")
+    p = moe.Problem.from_config(cfg)
+    out = torch.empty((cfg.T, cfg.K), dtype=torch.bfloat16, device="cuda")
+    bufs, calls = layer_kernels(p, cfg, inp, out)
+    for _, fn in calls:             # once in order: routing, then each GEMM's input
+        fn()
+    torch.cuda.synchronize()
+    kt = KernelTimer()
+    t = {n: kt.time(fn, iters, flush)[0] for n, fn in calls
+         if n in ("grouped_gemm_w13_act", "grouped_gemm_w2")}
+    counts = bufs["expert_num_tokens"].cpu().numpy()
+    fig = gemm_figures(cfg, counts, t["grouped_gemm_w13_act"], t["grouped_gemm_w2"])
+    res = {"workload": name, "w13_act_ms": round(t["grouped_gemm_w13_act"], 4),
+           "w2_ms": round(t["grouped_gemm_w2"], 4), "gemm_tflops": fig["gemm_tflops"],
+           "gemm_frac_fp8_peak": fig["gemm_frac_fp8_peak"],
+           "per_expert_roofline_frac": fig["frac"]}
+    del inp, bufs, calls, out
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(cfg, inp, st_dev, budget_s):
@@ -302,6 +363,11 @@ def main():
                 "kernel": "grouped_gemm_w13_act",
                 "algorithmic_bytes_per_launch": alg["w13_act_bytes"]}
 
+    per_expert = gemm_figures(cfg, counts, t_w13[0], t_w2[0])
+    mfma_wl = None
+    if args.mfma_workload != "none" and args.mfma_workload != cfg.name:
+        mfma_wl = mfma_bound_workload(args.mfma_workload, it, flush)
+
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
@@ -322,6 +388,12 @@ def main():
         "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},
         "roofline": roofline,
+        # both GEMMs against the sum over experts of max(MFMA time at the fp8
+        # dense peak, weight streaming time at the HBM peak)
+        "gemm_per_expert_roofline": {k: per_expert[k] for k in
+                                     ("w13_bound_ms", "w2_bound_ms", "w13_frac", "w2_frac",
+                                      "frac")},
+        "mfma_bound_workload": mfma_wl,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

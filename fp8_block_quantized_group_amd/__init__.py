@@ -23,7 +23,7 @@ W_FP8_BLOCK128, W_MXFP8, W_MXFP4 = 0, 1, 2
 _ACT_QUANT = {"ue8m0": Q_FP8_UE8M0, "fp32": Q_FP8_F32, "bf16": Q_BF16, "mxfp8": Q_MXFP8}
 _WEIGHT_QUANT = {"fp8_block128": W_FP8_BLOCK128, "mxfp8": W_MXFP8, "mxfp4": W_MXFP4}
 ACTIVATIONS = ("silu", "gelu", "gelu_tanh", "silu_no_mul", "gelu_no_mul", "gelu_tanh_no_mul",
-               "relu2_no_mul")                      # moe_act_t order
+               "relu2_no_mul", "swigluoai", "swiglustep")   # moe_act_t order
 LAYOUT_CONTIGUOUS, LAYOUT_BATCHED, LAYOUT_INDEXED = 0, 1, 2
 _LAYOUT = {"contiguous": LAYOUT_CONTIGUOUS, "batched": LAYOUT_BATCHED, "indexed": LAYOUT_INDEXED}
 _STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
@@ -39,7 +39,8 @@ class MoeError(RuntimeError):
 class _Problem(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "num_tokens", "hidden", "intermediate", "num_experts", "top_k", "layout",
-        "max_tokens_per_expert", "act_quant", "weight_quant", "activation")]
+        "max_tokens_per_expert", "act_quant", "weight_quant", "activation")] + [
+        ("act_limit", ctypes.c_float)]
 
 
 class _Eplb(ctypes.Structure):
@@ -143,11 +144,12 @@ class Problem:
     act_quant: int = Q_FP8_UE8M0
     weight_quant: int = W_FP8_BLOCK128
     activation: int = 0                             # index into ACTIVATIONS
+    act_limit: float = 0.0                          # clamp limit (moe_problem_t)
 
     def c(self) -> _Problem:
         return _Problem(self.num_tokens, self.hidden, self.intermediate, self.num_experts,
                         self.top_k, self.layout, self.max_tokens_per_expert, self.act_quant,
-                        self.weight_quant, self.activation)
+                        self.weight_quant, self.activation, self.act_limit)
 
     @staticmethod
     def from_config(cfg, act_quant: Optional[int] = None) -> "Problem":
@@ -155,7 +157,7 @@ class Problem:
         q = act_quant if act_quant is not None else _ACT_QUANT[cfg.act_quant]
         return Problem(cfg.T, cfg.K, cfg.N, cfg.E, cfg.top_k, _LAYOUT[cfg.layout],
                        cfg.max_tokens, q, _WEIGHT_QUANT[cfg.weight_quant],
-                       ACTIVATIONS.index(cfg.activation))
+                       ACTIVATIONS.index(cfg.activation), float(cfg.act_limit))
 
 
 def sizes(p: Problem) -> dict:

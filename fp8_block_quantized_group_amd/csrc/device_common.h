@@ -167,10 +167,14 @@ __device__ __forceinline__ void quantize_group(const uint16_t* __restrict__ x,
 
 // ---- activations ------------------------------------------------------------
 // Kinds (values match moe_act_t).  Gated kinds combine the gate column g with
-// its up column u as f(g) * u; _no_mul kinds return f(g) of the single w13
-// output column.  The experts' activation list names them; the functions are
-// the standard ones: SiLU g * sigmoid(g); GELU g * Phi(g) with the exact
-// normal CDF; the tanh form of GELU; ReLU^2 = max(g, 0)^2.
+// its up column u; _no_mul kinds return f(g) of the single w13 output
+// column.  The experts' activation list names them; the functions are the
+// standard ones: SiLU g * sigmoid(g); GELU g * Phi(g) with the exact normal
+// CDF; the tanh form of GELU; ReLU^2 = max(g, 0)^2.  The clamped SwiGLU
+// forms (named without bodies; this library's reading), with limit L > 0:
+// SiLU with a clamp limit silu(min(g, L)) * clamp(u, -L, L); SWIGLUSTEP
+// min(silu(g), L) * clamp(u, -L, L); SWIGLUOAI (clamp(u, -L, L) + 1) *
+// g' * sigmoid(1.702 g') with g' = min(g, L).
 constexpr int kActSilu = 0;
 constexpr int kActGelu = 1;
 constexpr int kActGeluTanh = 2;
@@ -178,17 +182,31 @@ constexpr int kActSiluNoMul = 3;
 constexpr int kActGeluNoMul = 4;
 constexpr int kActGeluTanhNoMul = 5;
 constexpr int kActRelu2NoMul = 6;
-constexpr bool act_is_gated(int kind) { return kind < kActSiluNoMul; }
+constexpr int kActSwigluOai = 7;
+constexpr int kActSwigluStep = 8;
+constexpr float kSwigluOaiAlpha = 1.702f;
+constexpr bool act_is_gated(int kind) { return kind < kActSiluNoMul || kind > kActRelu2NoMul; }
 
 __device__ __forceinline__ float silu_f32(float g) {
   const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
   return g * sig;
 }
 
-// kind is uniform across the launch (a kernel argument), so the switch is a
-// scalar branch.  SiLU keeps the g * sigmoid(g) * u order in fp32.
-__device__ __forceinline__ float apply_act(int kind, float g, float u) {
+// kind and limit are uniform across the launch (kernel arguments), so the
+// switch is a scalar branch.  SiLU keeps the g * sigmoid(g) * u order in
+// fp32.  limit: the clamp of the SwiGLU forms (> 0; for SiLU 0 = none).
+__device__ __forceinline__ float apply_act(int kind, float g, float u, float limit = 0.0f) {
   switch (kind) {
+    case kActSwigluOai: {
+      const float gc = fminf(g, limit);
+      const float uc = fminf(fmaxf(u, -limit), limit);
+      const float glu = gc * __builtin_amdgcn_rcpf(1.0f + __expf(-kSwigluOaiAlpha * gc));
+      return (uc + 1.0f) * glu;
+    }
+    case kActSwigluStep: {
+      const float uc = fminf(fmaxf(u, -limit), limit);
+      return fminf(silu_f32(g), limit) * uc;
+    }
     case kActGelu:
     case kActGeluNoMul: {
       // 1 + erf(g / sqrt 2) as erfc(-g / sqrt 2): no cancellation for g < 0
@@ -209,6 +227,10 @@ __device__ __forceinline__ float apply_act(int kind, float g, float u) {
     case kActSiluNoMul:
       return silu_f32(g);
     default: {
+      if (limit > 0.0f) {
+        g = fminf(g, limit);
+        u = fminf(fmaxf(u, -limit), limit);
+      }
       const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-g));
       return g * sig * u;
     }

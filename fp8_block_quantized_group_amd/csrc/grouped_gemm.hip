@@ -860,11 +860,12 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       }
     };
     // SiLU gets its own unrolled copy (no per-element branch); the other
-    // gated activations share one that switches on the kind
-    if (p.activation == kActSilu)
+    // gated activations (and SiLU with a clamp limit) share one that
+    // switches on the kind
+    if (p.activation == kActSilu && !(p.act_limit > 0.0f))
       activate([](float g, float u) { return apply_act(kActSilu, g, u); });
     else
-      activate([&](float g, float u) { return apply_act(p.activation, g, u); });
+      activate([&](float g, float u) { return apply_act(p.activation, g, u, p.act_limit); });
     if constexpr (A16) {
       // unquantized w2 input: h rounded once to bf16, 16 bytes per lane
 #pragma unroll

@@ -70,6 +70,7 @@ struct GemmArgs {
   int gather_sorted;               // A row = sorted_ids[pos] / top_k; else pos
   int scatter_sorted;              // output row = sorted_ids[pos] (padding skipped)
   int activation;             // ACT epilogue: a gated activation kind (moe_act_t)
+  float act_limit;            //   and its clamp limit (apply_act)
   int Kd;                    // reduction length, multiple of 128
   int Nout;                  // output columns, multiple of 128
 };
@@ -83,7 +84,7 @@ hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, 
 // kinds, N for the _no_mul ones
 hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t rows_cap, int N,
                               int quant, const int32_t* num_rows, const int32_t* counts,
-                              int max_tokens, int act, hipStream_t stream);
+                              int max_tokens, int act, float act_limit, hipStream_t stream);
 
 // Optional: the hidden states' group quantization run inside the routing
 // scan's launch: groups of 128 (UE8M0 or fp32 scales) or 32 (MXFP8, E8M0);

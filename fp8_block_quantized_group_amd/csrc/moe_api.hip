@@ -62,7 +62,18 @@ size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 bool batched(const moe_problem_t* p) { return p->layout == MOE_LAYOUT_BATCHED_MASKED; }
 bool indexed(const moe_problem_t* p) { return p->layout == MOE_LAYOUT_INDEXED; }
 // gated activations: w13 has 2N rows (gate, up); the _no_mul ones: N rows
-bool gated(const moe_problem_t* p) { return p->activation < MOE_ACT_SILU_NO_MUL; }
+bool gated(const moe_problem_t* p) {
+  return p->activation < MOE_ACT_SILU_NO_MUL || p->activation > MOE_ACT_RELU2_NO_MUL;
+}
+// The clamp limit the kernels apply: SWIGLUOAI / SWIGLUSTEP default to 7
+// when none is given; SiLU clamps only with an explicit limit; the others
+// take none.
+constexpr float kSwigluDefaultLimit = 7.0f;
+float effective_limit(const moe_problem_t* p) {
+  if (p->activation == MOE_ACT_SWIGLUOAI || p->activation == MOE_ACT_SWIGLUSTEP)
+    return p->act_limit > 0.0f ? p->act_limit : kSwigluDefaultLimit;
+  return p->activation == MOE_ACT_SILU ? p->act_limit : 0.0f;
+}
 int64_t w13_rows(const moe_problem_t* p) { return (gated(p) ? 2 : 1) * (int64_t)p->intermediate; }
 
 // Block sizes of the indexed layout: the GEMM tile heights.
@@ -146,8 +157,14 @@ moe_status_t validate_problem(const moe_problem_t* p) {
     return fail(MOE_ERR_INVALID_ARG, "unknown activation quantization %d", p->act_quant);
   if (p->weight_quant < MOE_W_FP8_BLOCK128 || p->weight_quant > MOE_W_MXFP4)
     return fail(MOE_ERR_INVALID_ARG, "unknown weight quantization %d", p->weight_quant);
-  if (p->activation < MOE_ACT_SILU || p->activation > MOE_ACT_RELU2_NO_MUL)
+  if (p->activation < MOE_ACT_SILU || p->activation > MOE_ACT_SWIGLUSTEP)
     return fail(MOE_ERR_INVALID_ARG, "unknown activation %d", p->activation);
+  if (!(p->act_limit >= 0.0f) || p->act_limit > 3.0e38f)
+    return fail(MOE_ERR_INVALID_ARG, "act_limit must be finite and >= 0, got %g",
+                (double)p->act_limit);
+  if (p->act_limit > 0.0f && p->activation != MOE_ACT_SILU &&
+      p->activation != MOE_ACT_SWIGLUOAI && p->activation != MOE_ACT_SWIGLUSTEP)
+    return fail(MOE_ERR_UNSUPPORTED, "activation %d takes no clamp limit", p->activation);
   // (weight, activation) pairs: block fp8 weights with per-128 or bf16
   // activations, MXFP8 or MXFP4 weights with MXFP8 activations
   const bool mx_w = p->weight_quant != MOE_W_FP8_BLOCK128;
@@ -398,6 +415,7 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
   g.Kd = w13 ? p->hidden : p->intermediate;
   g.Nout = w13 ? (int)w13_rows(p) : p->hidden;
   g.activation = p->activation;
+  g.act_limit = effective_limit(p);
   const int scheme =
       p->weight_quant == MOE_W_MXFP4 ? moe::kSchemeMxfp8W4 : p->act_quant;
   const hipError_t err = moe::launch_grouped_gemm(g, tile_m, max_tiles, scheme, act, stream);
@@ -415,7 +433,8 @@ moe_status_t run_act(const moe_problem_t* p, const Plan& pl, const void* gate_up
   const int32_t* num_rows = b || slot_order ? nullptr : r->expert_offsets + p->num_experts;
   const hipError_t err = moe::launch_act_requant(
       gate_up, a2_q, a2_sf, pl.s.expert_rows, p->intermediate, p->act_quant, num_rows,
-      b ? r->expert_num_tokens : nullptr, p->max_tokens_per_expert, p->activation, stream);
+      b ? r->expert_num_tokens : nullptr, p->max_tokens_per_expert, p->activation,
+      effective_limit(p), stream);
   return launch_status(err, "act_requant");
 }
 

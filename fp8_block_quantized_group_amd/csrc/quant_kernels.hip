@@ -66,7 +66,7 @@ template <bool UE8M0, int LANES>
 __global__ __launch_bounds__(256) void act_requant_kernel(
     const uint16_t* __restrict__ gu, uint8_t* __restrict__ aq, uint8_t* __restrict__ asf,
     int64_t num_groups, int N, int GN, int sf_row_len, const int32_t* __restrict__ num_rows,
-    const int32_t* __restrict__ counts, int max_tokens, int act) {
+    const int32_t* __restrict__ counts, int max_tokens, int act, float limit) {
   constexpr int GROUP = 8 * LANES;
   const int64_t gid = (int64_t)blockIdx.x * (256 / LANES) + threadIdx.x / LANES;
   const int lane_g = threadIdx.x % LANES;
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void act_requant_kernel(
   unpack8(*reinterpret_cast<const uint4*>(src), fg);
   if (gated) unpack8(*reinterpret_cast<const uint4*>(src + N), fu);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = apply_act(act, fg[i], gated ? fu[i] : 0.0f);
+  for (int i = 0; i < 8; ++i) h[i] = apply_act(act, fg[i], gated ? fu[i] : 0.0f, limit);
   uint8_t* sf_row = UE8M0 ? asf + row * sf_row_len : asf + row * (int64_t)GN * 4;
   quantize_store<UE8M0, LANES>(h, lane_g, aq + row * (int64_t)N + g * GROUP + lane_g * 8,
                                sf_row, g, GN, sf_row_len);
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(256) void act_requant_kernel(
 __global__ __launch_bounds__(256) void act_bf16_kernel(
     const uint16_t* __restrict__ gu, uint16_t* __restrict__ out, int64_t num_vec, int N,
     const int32_t* __restrict__ num_rows, const int32_t* __restrict__ counts, int max_tokens,
-    int act) {
+    int act, float limit) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= num_vec) return;
   const int vpr = N / 8;
@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void act_bf16_kernel(
   unpack8(*reinterpret_cast<const uint4*>(src), fg);
   if (gated) unpack8(*reinterpret_cast<const uint4*>(src + N), fu);
 #pragma unroll
-  for (int k = 0; k < 8; ++k) h[k] = apply_act(act, fg[k], gated ? fu[k] : 0.0f);
+  for (int k = 0; k < 8; ++k) h[k] = apply_act(act, fg[k], gated ? fu[k] : 0.0f, limit);
   *reinterpret_cast<uint4*>(out + row * (int64_t)N + col) =
       make_uint4(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]), pack_bf16x2(h[4], h[5]),
                  pack_bf16x2(h[6], h[7]));
@@ -135,19 +135,20 @@ hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, 
 
 hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t rows_cap, int N,
                               int quant, const int32_t* num_rows, const int32_t* counts,
-                              int max_tokens, int act, hipStream_t stream) {
+                              int max_tokens, int act, float act_limit, hipStream_t stream) {
   if (rows_cap == 0) return hipSuccess;
   if (quant == kQuantBf16) {
     const int64_t nvec = rows_cap * (N / 8);
     act_bf16_kernel<<<blocks_for(nvec, 256), 256, 0, stream>>>(
-        (const uint16_t*)gate_up, (uint16_t*)aq, nvec, N, num_rows, counts, max_tokens, act);
+        (const uint16_t*)gate_up, (uint16_t*)aq, nvec, N, num_rows, counts, max_tokens, act,
+        act_limit);
     return hipGetLastError();
   }
   if (quant == kQuantMxfp8) {
     const int GN = N / 32;
     act_requant_kernel<true, 4><<<blocks_for(rows_cap * GN, 64), 256, 0, stream>>>(
         (const uint16_t*)gate_up, (uint8_t*)aq, (uint8_t*)asf, rows_cap * GN, N, GN, GN,
-        num_rows, counts, max_tokens, act);
+        num_rows, counts, max_tokens, act, act_limit);
     return hipGetLastError();
   }
   const int GN = N / kGroup;
@@ -155,11 +156,11 @@ hipError_t launch_act_requant(const void* gate_up, void* aq, void* asf, int64_t 
   if (quant == kQuantUe8m0) {
     act_requant_kernel<true, 16><<<blocks_for(rows_cap * GN, 16), 256, 0, stream>>>(
         (const uint16_t*)gate_up, (uint8_t*)aq, (uint8_t*)asf, rows_cap * GN, N, GN,
-        sf_row_len, num_rows, counts, max_tokens, act);
+        sf_row_len, num_rows, counts, max_tokens, act, act_limit);
   } else {
     act_requant_kernel<false, 16><<<blocks_for(rows_cap * GN, 16), 256, 0, stream>>>(
         (const uint16_t*)gate_up, (uint8_t*)aq, (uint8_t*)asf, rows_cap * GN, N, GN,
-        sf_row_len, num_rows, counts, max_tokens, act);
+        sf_row_len, num_rows, counts, max_tokens, act, act_limit);
   }
   return hipGetLastError();
 }

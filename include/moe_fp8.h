@@ -93,15 +93,21 @@ typedef enum {
   MOE_W_MXFP4 = 2         /* e2m1 (two per byte), E8M0 per row and 32 cols  */
 } moe_weight_t;
 
-/* Activation between the two GEMMs (HummingExpertsBase._supports_activation
- * lists these; the pages do not show their formulas, so the standard ones are
- * used: SiLU g*sigmoid(g), GELU g*Phi(g) with the exact normal CDF, its tanh
+/* Activation between the two GEMMs ("...experts.fused_humming_moe",
+ * latest-docs page: HummingExpertsBase._supports_activation lists these and
+ * apply_activation applies swiglu_limit_func for SiLU when the quant config
+ * has a gemm1_clamp_limit; the pages show none of the formulas).  Standard
+ * ones: SiLU g*sigmoid(g), GELU g*Phi(g) with the exact normal CDF, its tanh
  * approximation 0.5 g (1 + tanh(sqrt(2/pi) (g + 0.044715 g^3))), ReLU^2
- * max(g, 0)^2).  Gated kinds: w13 has 2N rows, h = f(gate) * up.  _NO_MUL
- * kinds: w13 has N rows, h = f(w13 output) (get_buffer_metas: the w2 input
- * is the whole w13 output for non-gated activations).  SWIGLUOAI, SWIGLUSTEP
- * and the SiLU clamp limit are not provided (their parameters are not on the
- * pages). */
+ * max(g, 0)^2.  Gated kinds: w13 has 2N rows (gate rows first), h =
+ * F(gate, up).  _NO_MUL kinds: w13 has N rows, h = f(w13 output)
+ * (get_buffer_metas: the w2 input is the whole w13 output for non-gated
+ * activations).  The clamped SwiGLU forms are this library's reading (their
+ * bodies and constants are not on the pages), with L = act_limit:
+ * SiLU with act_limit > 0: silu(min(g, L)) * clamp(up, -L, L);
+ * SWIGLUSTEP: min(silu(g), L) * clamp(up, -L, L);
+ * SWIGLUOAI: (clamp(up, -L, L) + 1) * g' * sigmoid(1.702 g'), g' = min(g, L);
+ * for the last two act_limit 0 means L = 7. */
 typedef enum {
   MOE_ACT_SILU = 0,
   MOE_ACT_GELU = 1,
@@ -109,7 +115,9 @@ typedef enum {
   MOE_ACT_SILU_NO_MUL = 3,
   MOE_ACT_GELU_NO_MUL = 4,
   MOE_ACT_GELU_TANH_NO_MUL = 5,
-  MOE_ACT_RELU2_NO_MUL = 6
+  MOE_ACT_RELU2_NO_MUL = 6,
+  MOE_ACT_SWIGLUOAI = 7,
+  MOE_ACT_SWIGLUSTEP = 8
 } moe_act_t;
 
 /* Expert-row layouts ("Standard" and "BatchedExperts" activation formats of
@@ -140,6 +148,9 @@ typedef struct {
   int32_t act_quant;             /* moe_quant_t */
   int32_t weight_quant;          /* moe_weight_t */
   int32_t activation;            /* moe_act_t (0 = SiLU(gate) * up) */
+  float act_limit;               /* clamp limit of SiLU / SWIGLUOAI /
+                                    SWIGLUSTEP (>= 0; 0: none for SiLU,
+                                    7 for the other two); 0 for the rest */
 } moe_problem_t;
 
 /* Expert-parallel load balancing state (optional; all device pointers).

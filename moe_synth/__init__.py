@@ -66,10 +66,14 @@ class MoeConfig:
     pad_frac: float = 0.0
     num_logical: int = 0                # >0: EPLB with E - num_logical replicas
     weight_std: float = 0.02
-    # "silu" | "gelu" | "gelu_tanh" (gated: w13 has 2N rows, gate then up) |
-    # "silu_no_mul" | "gelu_no_mul" | "gelu_tanh_no_mul" | "relu2_no_mul"
-    # (w13 has N rows, the activation applies to all of them)
+    # "silu" | "gelu" | "gelu_tanh" | "swigluoai" | "swiglustep" (gated: w13
+    # has 2N rows, gate then up) | "silu_no_mul" | "gelu_no_mul" |
+    # "gelu_tanh_no_mul" | "relu2_no_mul" (w13 has N rows, the activation
+    # applies to all of them)
     activation: str = "silu"
+    # clamp limit of the gated SwiGLU forms (0: none for SiLU, the default
+    # for SWIGLUOAI / SWIGLUSTEP)
+    act_limit: float = 0.0
 
     @property
     def gated(self) -> bool:

@@ -54,6 +54,13 @@ reason, in the design notes):
     take their standard definitions; gated ones read w13's 2N columns as
     gate then up, the _no_mul ones act on all N columns of a w13 with N rows
     (the w2 input width is N in both cases);
+  * the clamped SwiGLU forms, named on the pages without bodies or
+    constants (parity unpinned: only the properties of this reading are
+    tested): SiLU with a clamp limit L (the experts' gemm1_clamp_limit)
+    is silu(min(g, L)) * clamp(u, -L, L); SWIGLUSTEP is
+    min(silu(g), L) * clamp(u, -L, L); SWIGLUOAI is
+    (clamp(u, -L, L) + 1) * g' * sigmoid(1.702 g') with g' = min(g, L);
+    L defaults to 7 for the last two;
   * MX: the w2 input (SiLU(gate)*up) is quantized like the staged hidden
     states, 32-column groups with E8M0 scales (Humming's own input quantizer
     is not shown); E8M0 byte e means 2^(e-127); e2m1 codes are packed two per
@@ -480,18 +487,36 @@ ACT_FUNCS = {
                                                     * (x + 0.044715 * x ** 3))),
     "relu2": lambda x: np.maximum(x, 0.0) ** 2,
 }
-GATED = ("silu", "gelu", "gelu_tanh")
+GATED = ("silu", "gelu", "gelu_tanh", "swigluoai", "swiglustep")
 NO_MUL = ("silu_no_mul", "gelu_no_mul", "gelu_tanh_no_mul", "relu2_no_mul")
+SWIGLU_DEFAULT_LIMIT = 7.0
+SWIGLUOAI_ALPHA = 1.702
 
 
-def act_f32(gate_up_bits, N: int, activation: str = "silu") -> np.ndarray:
+def gated_act(activation: str, g, u, limit: float = 0.0):
+    """h = F(g, u) for a gated activation with gate g and up u (fp64).
+    ``limit`` > 0 clamps as described in the module docstring (SiLU: only
+    when given; SWIGLUOAI / SWIGLUSTEP: 7 when 0)."""
+    if activation in ("gelu", "gelu_tanh") or (activation == "silu" and limit <= 0):
+        return ACT_FUNCS[activation](g) * u
+    L = limit if limit > 0 else SWIGLU_DEFAULT_LIMIT
+    uc = np.clip(u, -L, L)
+    if activation == "silu":
+        return ACT_FUNCS["silu"](np.minimum(g, L)) * uc
+    if activation == "swiglustep":
+        return np.minimum(ACT_FUNCS["silu"](g), L) * uc
+    assert activation == "swigluoai", activation
+    gc = np.minimum(g, L)
+    return (uc + 1.0) * gc / (1.0 + np.exp(-SWIGLUOAI_ALPHA * gc))
+
+
+def act_f32(gate_up_bits, N: int, activation: str = "silu", limit: float = 0.0) -> np.ndarray:
     """The w2 input before quantization, in fp64 rounded once to fp32.
-    Gated: bf16 [rows, 2N] -> h = f(g) * u with g = columns [0, N) and
+    Gated: bf16 [rows, 2N] -> h = F(g, u) with g = columns [0, N) and
     u = columns [N, 2N).  _no_mul: bf16 [rows, N] -> h = f(x)."""
     gu = bf16_to_f64(gate_up_bits)
     if activation in GATED:
-        g, u = gu[:, :N], gu[:, N:2 * N]
-        h = ACT_FUNCS[activation](g) * u
+        h = gated_act(activation, gu[:, :N], gu[:, N:2 * N], limit)
     else:
         assert activation in NO_MUL, activation
         h = ACT_FUNCS[activation[:-len("_no_mul")]](gu[:, :N])
@@ -503,23 +528,24 @@ def silu_mul_f32(gate_up_bits, N: int) -> np.ndarray:
 
 
 def act_requant(gate_up_bits, N: int, ue8m0: bool, group: int = GROUP,
-                activation: str = "silu"):
-    return quantize_groups(act_f32(gate_up_bits, N, activation), ue8m0, group)
+                activation: str = "silu", limit: float = 0.0):
+    return quantize_groups(act_f32(gate_up_bits, N, activation, limit), ue8m0, group)
 
 
-def act_bf16(gate_up_bits, N: int, activation: str = "silu"):
+def act_bf16(gate_up_bits, N: int, activation: str = "silu", limit: float = 0.0):
     """Unquantized w2 input: h (fp32, as above) rounded once to bf16 (the
     c_dtype of the activation buffer)."""
-    return bf16_round(act_f32(gate_up_bits, N, activation).astype(np.float64))
+    return bf16_round(act_f32(gate_up_bits, N, activation, limit).astype(np.float64))
 
 
 def act_step(cfg, gate_up_bits):
     """The w2 input in the workload's scheme: (codes or bf16 bits, scales or
     None)."""
     act = getattr(cfg, "activation", "silu")
+    limit = getattr(cfg, "act_limit", 0.0)
     if cfg.act_quant == "bf16":
-        return act_bf16(gate_up_bits, cfg.N, act), None
-    return act_requant(gate_up_bits, cfg.N, act_e8m0(cfg), act_group(cfg), act)
+        return act_bf16(gate_up_bits, cfg.N, act, limit), None
+    return act_requant(gate_up_bits, cfg.N, act_e8m0(cfg), act_group(cfg), act, limit)
 
 
 # ---------------------------------------------------------------------------

@@ -177,17 +177,29 @@ def check_requant(got_q, got_sf, ref_q, ref_sf, ref_h32, ue8m0, what, group=128)
     return frac
 
 
-def act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation="silu"):
+def act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation="silu", limit=0.0):
     """(h, dh): the oracle's h in fp64 and a bound on how far h moves when
     gate_up moves by the GEMM bound (bf16 unit + MFMA term), for the given
-    activation.  SiLU uses its derivative; the others the largest change of
-    f over [g - dg, g + dg] sampled at eight points, with a 25 % margin for
-    the curvature between samples."""
+    activation.  SiLU uses its derivative; f(g) * u forms the largest change
+    of f over [g - dg, g + dg] sampled at eight points; the clamped SwiGLU
+    forms the largest change of F(g, u) over the box [g +- dg] x [u +- du]
+    sampled on a 5 x 5 grid (clamps make F piecewise smooth; the grid holds
+    the box's corners); both with a 25 % margin for the curvature between
+    samples."""
     gu = O.bf16_to_f64(ref_gate_up_bits)
     dgu = bf16_ulp(gu) + MFMA_REL * s_abs_gate_up
     gated = activation in O.GATED
     g, dg = gu[:, :N], dgu[:, :N]
     u, du = (gu[:, N:2 * N], dgu[:, N:2 * N]) if gated else (np.ones_like(g), np.zeros_like(g))
+    if activation in ("swigluoai", "swiglustep") or (activation == "silu" and limit > 0):
+        F0 = O.gated_act(activation, g, u, limit)
+        dh = np.zeros_like(g)
+        for tg in (-1.0, -0.5, 0.0, 0.5, 1.0):
+            for tu in (-1.0, -0.5, 0.0, 0.5, 1.0):
+                dh = np.maximum(dh, np.abs(O.gated_act(activation, g + tg * dg, u + tu * du,
+                                                       limit) - F0))
+        dh = dh * 1.25 * 1.01 + np.abs(F0) * 2.0 ** -20 + 2.0 ** -40
+        return F0, dh
     if activation == "silu":
         sig = 1.0 / (1.0 + np.exp(-g))
         f = g * sig
@@ -206,7 +218,8 @@ def act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation="silu"):
 
 
 def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_gate_up, ue8m0,
-                        what, group=128, activation="silu", max_frac=CHAIN_DIFF_CEIL):
+                        what, group=128, activation="silu", max_frac=CHAIN_DIFF_CEIL,
+                        limit=0.0):
     """End of the GPU's own chain: its gate_up may differ from the oracle's
     by the GEMM bound; carry that through the activation and allow half an
     fp8 step of rounding on each side.  At most ``max_frac`` of the codes
@@ -215,7 +228,7 @@ def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_ga
     Returns the fraction of codes that differ."""
     rows, N = ref_q.shape
     G = N // group
-    _, dh = act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation)
+    _, dh = act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation, limit)
     sv_g = np.repeat(O.scale_values(got_sf[:, :G], ue8m0), group, axis=1)
     sv_r = np.repeat(O.scale_values(ref_sf[:, :G], ue8m0), group, axis=1)
     vg = O.e4m3_decode(got_q) * sv_g
@@ -242,12 +255,12 @@ def check_requant_chain(got_q, got_sf, ref_q, ref_sf, ref_gate_up_bits, s_abs_ga
 
 
 def check_bf16_act_chain(got_bits, ref_bits, ref_gate_up_bits, s_abs_gate_up, what,
-                         activation="silu"):
+                         activation="silu", limit=0.0):
     """bf16 w2 input at the end of the GPU's own chain: the GEMM bound on
     gate_up carried through the activation, plus one bf16 rounding on each
     side.  Returns the fraction of values that differ."""
     N = ref_bits.shape[1]
-    h, dh = act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation)
+    h, dh = act_error_bound(ref_gate_up_bits, s_abs_gate_up, N, activation, limit)
     vg, vr = O.bf16_to_f64(got_bits), O.bf16_to_f64(ref_bits)
     assert np.all(np.isfinite(vg)), f"{what}: non-finite values"
     bound = dh + bf16_ulp(vr)

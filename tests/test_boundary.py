@@ -296,8 +296,23 @@ def test_indexed_validation(lib):
 def test_activation_validation_and_workspace(lib):
     base = dict(num_tokens=16, hidden=256, intermediate=512, num_experts=4, top_k=2)
     with pytest.raises(moe.MoeError) as ei:
-        moe.sizes(moe.Problem(**base, activation=7))
+        moe.sizes(moe.Problem(**base, activation=9))
     assert ei.value.status == -1
+    # the clamp limit: finite and >= 0, and only for SiLU / SWIGLUOAI / SWIGLUSTEP
+    for act in (0, 7, 8):
+        moe.sizes(moe.Problem(**base, activation=act, act_limit=2.5))
+    for limit, status in [(-1.0, -1), (float("inf"), -1), (float("nan"), -1)]:
+        with pytest.raises(moe.MoeError) as ei:
+            moe.sizes(moe.Problem(**base, activation=7, act_limit=limit))
+        assert ei.value.status == status, limit
+    for act in (1, 2, 3, 6):
+        with pytest.raises(moe.MoeError) as ei:
+            moe.sizes(moe.Problem(**base, activation=act, act_limit=1.0))
+        assert ei.value.status == -2, act
+    # the clamped SwiGLU forms are gated: w13 has 2N rows, like SiLU
+    ws_silu = moe.workspace_size(moe.Problem(**base))
+    assert moe.workspace_size(moe.Problem(**base, activation=7)) == ws_silu
+    assert moe.workspace_size(moe.Problem(**base, activation=8, act_limit=1.0)) == ws_silu
     # _no_mul activations keep a gate_up region (T*k rows of N bf16) in the
     # forward workspace; gated ones do not
     ws_silu = moe.workspace_size(moe.Problem(**base))

@@ -38,6 +38,21 @@ CASES.update({
     "gelu_no_mul_batched": _cfg("gelu_no_mul_batched", "gelu_no_mul", T=250, E=4, top_k=2,
                                 N=256, seed=57, pad_frac=0.0, layout="batched",
                                 max_tokens=160),
+    # the clamped SwiGLU forms, with limits inside the gate_up range (about
+    # N(0, 0.4) here) so that every clamp is active on a good share of the
+    # values; the last two with their default limit 7 (no clamp reached)
+    "silu_clamp": _cfg("silu_clamp", "silu", act_limit=0.3, seed=58),
+    "swigluoai": _cfg("swigluoai", "swigluoai", act_limit=0.4, seed=59),
+    "swiglustep": _cfg("swiglustep", "swiglustep", act_limit=0.1, seed=60),
+    "swigluoai_mx4": _cfg("swigluoai_mx4", "swigluoai", act_limit=0.4, act_quant="mxfp8",
+                          weight_quant="mxfp4", seed=61),
+    "swiglustep_bf16": _cfg("swiglustep_bf16", "swiglustep", act_limit=0.1, act_quant="bf16",
+                            seed=62),
+    "silu_clamp_fp32_batched": _cfg("silu_clamp_fp32_batched", "silu", act_limit=0.3, T=250,
+                                    E=4, top_k=2, N=256, seed=63, pad_frac=0.0,
+                                    layout="batched", max_tokens=160, act_quant="fp32"),
+    "swigluoai_default": _cfg("swigluoai_default", "swigluoai", seed=64),
+    "swiglustep_default": _cfg("swiglustep_default", "swiglustep", seed=65),
 })
 
 _CACHE = {}
@@ -119,7 +134,7 @@ def test_activation_isolated(gpu, name):
         assert np.all(got[untouched] == SENTINEL_BF16)
         return
     got_q, got_sf = to_np(a2_q), to_np(a2_sf)
-    h32 = O.act_f32(ref["gate_up"][vr], cfg.N, cfg.activation)
+    h32 = O.act_f32(ref["gate_up"][vr], cfg.N, cfg.activation, cfg.act_limit)
     check_requant(got_q[vr], got_sf[vr], ref["a2_q"][vr], ref["a2_sf"][vr], h32,
                   O.act_e8m0(cfg), f"{name} activation", O.act_group(cfg))
     assert np.all(got_q[untouched] == SENTINEL_U8)
@@ -147,11 +162,12 @@ def test_layer_chain_and_forward(gpu, name):
     s_abs = w13_abs(cfg, h, ref)
     if cfg.act_quant == "bf16":
         check_bf16_act_chain(to_np(a2_q)[vr], ref["a2_q"][vr], ref["gate_up"][vr], s_abs,
-                             f"{name} a2 (chain)", cfg.activation)
+                             f"{name} a2 (chain)", cfg.activation, cfg.act_limit)
     else:
         check_requant_chain(to_np(a2_q)[vr], to_np(a2_sf)[vr], ref["a2_q"][vr],
                             ref["a2_sf"][vr], ref["gate_up"][vr], s_abs, O.act_e8m0(cfg),
-                            f"{name} a2 (chain)", O.act_group(cfg), cfg.activation)
+                            f"{name} a2 (chain)", O.act_group(cfg), cfg.activation,
+                            limit=cfg.act_limit)
     check_output(to_np(out), ref["out"], f"{name} chained output")
     layer = moe.MoeLayer(p, dev["w13"], dev["w13_sf"], dev["w2"], dev["w2_sf"])
     fwd = layer(dev["hidden"], dev["topk_ids"], dev["topk_weights"], None, dev["is_padding"],

@@ -602,6 +602,12 @@ _TORCH_ACT = {
     "gelu_no_mul": lambda gu, N: _F.gelu(gu[..., :N]),
     "gelu_tanh_no_mul": lambda gu, N: _F.gelu(gu[..., :N], approximate="tanh"),
     "relu2_no_mul": lambda gu, N: _F.relu(gu[..., :N]) ** 2,
+    # the clamped SwiGLU readings (limit 7), in torch's own operations
+    "swiglustep": lambda gu, N: (_F.silu(gu[..., :N]).clamp(max=7.0)
+                                 * gu[..., N:2 * N].clamp(-7.0, 7.0)),
+    "swigluoai": lambda gu, N: ((gu[..., N:2 * N].clamp(-7.0, 7.0) + 1)
+                                * gu[..., :N].clamp(max=7.0)
+                                * torch.sigmoid(1.702 * gu[..., :N].clamp(max=7.0))),
 }
 
 
@@ -641,8 +647,52 @@ def test_activation_identities():
                               O.act_f32(g, N, base + "_no_mul"))
 
 
+def test_clamped_swiglu_properties():
+    """The clamped SwiGLU readings (parity unpinned: the pages name them
+    without bodies): a limit above every value reduces them to their
+    unclamped forms; past the limits the output no longer depends on the
+    clamped input; SWIGLUOAI's gate factor g * sigmoid(1.702 g) is the
+    sigmoid approximation of GELU (within 0.03 of x * Phi(x), its published
+    accuracy), which fixes the constant."""
+    rng = np.random.default_rng(39)
+    g = rng.standard_normal((6, 64)) * 4
+    u = rng.standard_normal((6, 64)) * 4
+    silu = O.ACT_FUNCS["silu"]
+    big = 1e6
+    assert np.array_equal(O.gated_act("silu", g, u, big), silu(g) * u)
+    assert np.array_equal(O.gated_act("silu", g, u, 0.0), silu(g) * u)
+    assert np.array_equal(O.gated_act("swiglustep", g, u, big), silu(g) * u)
+    assert np.allclose(O.gated_act("swigluoai", g, u, big),
+                       (u + 1) * g / (1 + np.exp(-1.702 * g)), rtol=1e-15, atol=0)
+    x = np.linspace(-8, 8, 4001)
+    assert np.max(np.abs(x / (1 + np.exp(-1.702 * x)) - O.ACT_FUNCS["gelu"](x))) < 0.03
+    L = 1.5
+    for act in ("silu", "swiglustep", "swigluoai"):
+        h = O.gated_act(act, g, u, L)
+        # the up input matters only inside [-L, L]
+        assert np.array_equal(h, O.gated_act(act, g, np.clip(u, -L, L), L)), act
+        assert np.array_equal(O.gated_act(act, g, np.full_like(u, 3 * L), L),
+                              O.gated_act(act, g, np.full_like(u, L), L)), act
+    # the gate is capped from above only: SiLU / SWIGLUOAI at g = L, SWIGLUSTEP
+    # at silu(g) = L; far below, the output goes to zero
+    for act in ("silu", "swigluoai"):
+        assert np.array_equal(O.gated_act(act, np.full_like(u, 5 * L), u, L),
+                              O.gated_act(act, np.full_like(u, L), u, L)), act
+    gs = 2.0        # silu(2) = 1.76 > L: capped
+    assert np.array_equal(O.gated_act("swiglustep", np.full_like(u, gs), u, L),
+                          L * np.clip(u, -L, L))
+    for act in ("silu", "swiglustep", "swigluoai"):
+        assert np.max(np.abs(O.gated_act(act, np.full_like(u, -40.0), u, L))) < 1e-12
+    # defaults: 7 for SWIGLUOAI / SWIGLUSTEP
+    assert np.array_equal(O.gated_act("swiglustep", g, u, 0.0),
+                          O.gated_act("swiglustep", g, u, 7.0))
+    assert np.array_equal(O.gated_act("swigluoai", g, u, 0.0),
+                          O.gated_act("swigluoai", g, u, 7.0))
+
+
 @pytest.mark.parametrize("act", ["gelu", "gelu_tanh", "silu_no_mul", "gelu_no_mul",
-                                 "gelu_tanh_no_mul", "relu2_no_mul"])
+                                 "gelu_tanh_no_mul", "relu2_no_mul", "swiglustep",
+                                 "swigluoai"])
 def test_tiny_layer_other_activations_track_unquantized_ffn(act):
     cfg = moe_synth.custom(T=16, E=4, top_k=2, K=256, N=512, seed=1, activation=act)
     h = O.host_inputs(moe_synth.make_inputs(cfg))
