@@ -206,6 +206,7 @@ def layer_kernels(p, cfg, inp, out):
     bufs = moe.alloc_stage_outputs(p)
     a2_q, a2_sf = moe.alloc_act_outputs(p)
     down = torch.empty((s["expert_rows"], cfg.K), dtype=torch.bfloat16, device="cuda")
+    w2_ws = moe.alloc_w2_workspace(p)
 
     def do_stage():
         if inp["eplb"] is not None:
@@ -224,7 +225,7 @@ def layer_kernels(p, cfg, inp, out):
                                                       inp["w13"], inp["w13_sf"], a2_q, a2_sf)),
             ("grouped_gemm_w2",
              lambda: moe.grouped_gemm_w2_indexed(p, a2_q, a2_sf, ix, inp["w2"], inp["w2_sf"],
-                                                 down)),
+                                                 down, w2_ws)),
             ("topk_reduce",
              lambda: moe.fused_mul_sum(p, down, bufs["topk_idx"], bufs["topk_w"], out)),
         ]
@@ -234,7 +235,8 @@ def layer_kernels(p, cfg, inp, out):
              lambda: moe.grouped_gemm_w13_act(p, bufs["x_q"], bufs["x_sf"], bufs, inp["w13"],
                                               inp["w13_sf"], a2_q, a2_sf)),
             ("grouped_gemm_w2",
-             lambda: moe.grouped_gemm_w2(p, a2_q, a2_sf, bufs, inp["w2"], inp["w2_sf"], down)),
+             lambda: moe.grouped_gemm_w2(p, a2_q, a2_sf, bufs, inp["w2"], inp["w2_sf"], down,
+                                         w2_ws)),
             ("topk_reduce",
              lambda: moe.topk_reduce(p, down, bufs["slot_row"], bufs["topk_w"], out)),
         ]

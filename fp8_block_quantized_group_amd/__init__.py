@@ -63,7 +63,8 @@ class _Sizes(ctypes.Structure):
                 ("tile_m", ctypes.c_int32)]
 
 
-EXPORTS = ("moe_routing_sizes", "moe_stage_workspace_size", "moe_workspace_size", "moe_stage",
+EXPORTS = ("moe_routing_sizes", "moe_stage_workspace_size", "moe_workspace_size",
+           "moe_w2_workspace_size", "moe_stage",
            "moe_grouped_gemm_w13", "moe_grouped_gemm_w13_act", "moe_act_requant",
            "moe_grouped_gemm_w2", "moe_topk_reduce", "moe_align_capacity",
            "moe_align_block_size", "moe_grouped_gemm_w13_act_indexed",
@@ -87,19 +88,21 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_routing_sizes.argtypes = [P(_Problem), P(_Sizes)]
     lib.moe_stage_workspace_size.argtypes = [P(_Problem), P(S)]
     lib.moe_workspace_size.argtypes = [P(_Problem), P(S)]
+    lib.moe_w2_workspace_size.argtypes = [P(_Problem), P(S)]
     lib.moe_stage.argtypes = [P(_Problem), V, V, V, V, V, P(_Eplb), V, V, V, V, P(_Routing),
                               V, S, V]
     lib.moe_grouped_gemm_w13.argtypes = [P(_Problem), V, V, P(_Routing), V, V, V, V]
     lib.moe_grouped_gemm_w13_act.argtypes = [P(_Problem), V, V, P(_Routing), V, V, V, V, V]
     lib.moe_act_requant.argtypes = [P(_Problem), V, P(_Routing), V, V, V]
-    lib.moe_grouped_gemm_w2.argtypes = [P(_Problem), V, V, P(_Routing), V, V, V, V]
+    lib.moe_grouped_gemm_w2.argtypes = [P(_Problem), V, V, P(_Routing), V, V, V, V, S, V]
     lib.moe_topk_reduce.argtypes = [P(_Problem), V, V, V, V, V]
     I32, I64 = ctypes.c_int32, ctypes.c_int64
     lib.moe_align_capacity.argtypes = [P(_Problem), I32, P(I64), P(I64)]
     lib.moe_align_block_size.argtypes = [P(_Problem), V, P(_Routing), I32, V, V, V, V]
     lib.moe_grouped_gemm_w13_act_indexed.argtypes = [P(_Problem), V, V, V, V, V, I32, V, V, V,
                                                      V, V]
-    lib.moe_grouped_gemm_w2_indexed.argtypes = [P(_Problem), V, V, V, V, V, I32, V, V, V, V]
+    lib.moe_grouped_gemm_w2_indexed.argtypes = [P(_Problem), V, V, V, V, V, I32, V, V, V, V,
+                                                S, V]
     lib.moe_fused_mul_sum.argtypes = [P(_Problem), V, V, V, V, V]
     lib.moe_forward.argtypes = [P(_Problem), V, V, V, V, V, P(_Eplb), V, V, V, V, V, V, S, V]
     lib.moe_forward_static.argtypes = [P(_Problem), V, V, V, V, V, P(_Eplb), V, V, V, V, V, V]
@@ -176,6 +179,22 @@ def workspace_size(p: Problem) -> int:
     n = ctypes.c_size_t()
     _check(load_library().moe_workspace_size(ctypes.byref(p.c()), ctypes.byref(n)))
     return n.value
+
+
+def w2_workspace_size(p: Problem) -> int:
+    """Bytes of the w2 call's split-K workspace (0: w2 does not split)."""
+    n = ctypes.c_size_t()
+    _check(load_library().moe_w2_workspace_size(ctypes.byref(p.c()), ctypes.byref(n)))
+    return n.value
+
+
+def alloc_w2_workspace(p: Problem, device="cuda") -> Optional[torch.Tensor]:
+    n = w2_workspace_size(p)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n > 0 else None
+
+
+def _ws(ws: Optional[torch.Tensor]):
+    return (_ptr(ws), ws.numel()) if ws is not None else (None, 0)
 
 
 def _eplb(eplb: Optional[dict]):
@@ -267,11 +286,15 @@ def act_requant(p: Problem, gate_up, routing: dict, a2_q, a2_sf):
                                            _ptr(a2_q), _ptr(a2_sf), _stream()))
 
 
-def grouped_gemm_w2(p: Problem, a2_q, a2_sf, routing: dict, w2, w2_sf, down):
+def grouped_gemm_w2(p: Problem, a2_q, a2_sf, routing: dict, w2, w2_sf, down, ws="auto"):
+    """ws: the split-K workspace (alloc_w2_workspace); "auto" allocates it."""
     r = _routing(routing)
+    if isinstance(ws, str):
+        ws = alloc_w2_workspace(p, down.device)
+    wp, wn = _ws(ws)
     _check(load_library().moe_grouped_gemm_w2(ctypes.byref(p.c()), _ptr(a2_q), _ptr(a2_sf),
                                                ctypes.byref(r), _ptr(w2), _ptr(w2_sf),
-                                               _ptr(down), _stream()))
+                                               _ptr(down), wp, wn, _stream()))
 
 
 def topk_reduce(p: Problem, down, slot_row, topk_w, out):
@@ -313,11 +336,14 @@ def grouped_gemm_w13_act_indexed(p: Problem, a_q, a_sf, ix: dict, w13, w13_sf, a
         _ptr(w13_sf), _ptr(a2_q), _ptr(a2_sf), _stream()))
 
 
-def grouped_gemm_w2_indexed(p: Problem, a2_q, a2_sf, ix: dict, w2, w2_sf, down):
+def grouped_gemm_w2_indexed(p: Problem, a2_q, a2_sf, ix: dict, w2, w2_sf, down, ws="auto"):
+    if isinstance(ws, str):
+        ws = alloc_w2_workspace(p, down.device)
+    wp, wn = _ws(ws)
     _check(load_library().moe_grouped_gemm_w2_indexed(
         ctypes.byref(p.c()), _ptr(a2_q), _ptr(a2_sf), _ptr(ix["sorted_ids"]),
         _ptr(ix["expert_ids"]), _ptr(ix["num_tokens_padded"]), ix["block_size"], _ptr(w2),
-        _ptr(w2_sf), _ptr(down), _stream()))
+        _ptr(w2_sf), _ptr(down), wp, wn, _stream()))
 
 
 def fused_mul_sum(p: Problem, down, topk_idx, topk_w, out):

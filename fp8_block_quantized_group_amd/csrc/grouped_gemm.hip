@@ -71,6 +71,7 @@ constexpr int kMaxGroups = 256;                // reduction length <= 32768
 #define MOE_ZIP 16
 #endif
 constexpr int kZip = MOE_ZIP;                  // zipper run length (work items)
+constexpr int kMaxSplit = 4;                   // split-K ranges at most
 
 // Tile geometry.  BM activation rows x BN weight rows (output columns) per
 // block, NW waves arranged WN x WM, each owning a WAVE_N x WAVE_M sub-tile
@@ -329,6 +330,11 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // heavy experts' blocks over more XCDs.)
   const bool indexed = p.sorted_ids != nullptr;
   const int NT = p.Nout / S::BN;
+  // split-K: the S splits of one (tile, n-tile) item are consecutive work
+  // items, so they run at about the same time (the last one's partial reads
+  // then find the others' partials still in L2 / MALL)
+  const int nsplit = ACT ? 1 : max(p.ksplit, 1);
+  int split = 0;
   int tile, nt, e, m0, rows_here;
   bool w_once = false;   // this block is the weight tile's only reader
   int64_t base;
@@ -336,14 +342,17 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // taken in the zipper order described below, then the (tile, n-tile) item
   // it names.  Returns false past the work.
   auto schedule_item = [&](int& t_out, int& nt_out, const int32_t*& info_out) -> bool {
-    const int64_t work = (int64_t)p.tile_list[0] * NT;
-    const int64_t per_xcd = (work + 7) / 8;
+    // slices of whole items: an item's splits share an XCD (and its L2)
+    const int64_t work = (int64_t)p.tile_list[0] * NT * nsplit;
+    const int64_t per_xcd = ((int64_t)p.tile_list[0] * NT + 7) / 8 * nsplit;
     const int64_t xcd = blockIdx.x % 8, j = blockIdx.x / 8;
     const int64_t items = min(per_xcd, work - xcd * per_xcd);   // this XCD's slice
     if (j >= items) return false;
     const int64_t u = j / (2 * kZip), v = j % (2 * kZip);
-    const int64_t wl =
+    const int64_t wls =
         xcd * per_xcd + (v < kZip ? u * kZip + v : items - 1 - (u * kZip + v - kZip));
+    split = __builtin_amdgcn_readfirstlane((int)(wls % nsplit));
+    const int64_t wl = wls / nsplit;
     const int t0 = __builtin_amdgcn_readfirstlane((int)(wl / NT));
     const int32_t* info = p.tile_list + 4 + 8 * (int64_t)t0;
     const int first = info[2], mtiles = info[3];
@@ -369,10 +378,12 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       // that 8 consecutive items share a weight tile; other groups take each
       // block's n-tiles consecutively (they share its activation rows).
       const int64_t nblk = min(max(*p.num_padded, 0) / S::BM, p.max_blocks);
-      const int64_t work = nblk * NT;
-      const int64_t per_xcd = (work + 7) / 8;
-      const int64_t wl = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-      if (blockIdx.x / 8 >= per_xcd || wl >= work) return;
+      const int64_t work = nblk * NT * nsplit;
+      const int64_t per_xcd = (nblk * NT + 7) / 8 * nsplit;
+      const int64_t wls = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+      if (blockIdx.x / 8 >= per_xcd || wls >= work) return;
+      split = __builtin_amdgcn_readfirstlane((int)(wls % nsplit));
+      const int64_t wl = wls / nsplit;
       const int64_t g0 = wl / (8 * NT) * 8;          // the group's first block
       const int64_t r = wl - g0 * NT;
       const bool full = g0 + 8 <= nblk;
@@ -438,7 +449,17 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int wn = wave % S::WN;
   const int wm = wave / S::WN;
-  const int G = p.Kd / kGroup;
+  // k-steps of this block: all of them, or this split's range (a multiple
+  // of 4 k-steps long, so the 4-k-step cadence of the MX weight-scale panel
+  // and of the UE8M0 scale words starts at its first step).  Loop indices
+  // below are relative to k0 (ring slots, prologue), offsets absolute.
+  const int G_all = p.Kd / kGroup;
+  int k0 = 0, G = G_all;
+  if (nsplit > 1) {
+    const int chunk = ((G_all + nsplit - 1) / nsplit + 3) & ~3;
+    k0 = min(split * chunk, G_all);
+    G = min(G_all, k0 + chunk) - k0;
+  }
 
   // activation row of tile row m (an id that is padding gathers row T,
   // past the buffer's end: the buffer loads return zeros there)
@@ -487,8 +508,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     const uint32_t st = smem_base + (kb % S::STAGES) * STAGE;
 #pragma unroll
     for (int i = 0; i < BI; ++i)
-      dma16_w(rs_b, st + AB + i * S::THREADS * 16 + wave_slot, b_off[i] + (uint32_t)kb * WROW,
-              w_once);
+      dma16_w(rs_b, st + AB + i * S::THREADS * 16 + wave_slot,
+              b_off[i] + (uint32_t)(k0 + kb) * WROW, w_once);
   };
 #pragma unroll
   for (int s = 0; s < S::STAGES - 1; ++s)
@@ -556,10 +577,10 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       // ACT: block 0 = the gate rows' scale block, block 1 = the up rows'
       const int blk = ACT ? (b == 0 ? j0 : Nh + j0) / kGroup : n0 / kGroup + b;
       const v4i rs_p = buffer_rsrc((const uint8_t*)p.w_sf +
-                                       (((int64_t)e * (p.Nout / kGroup) + blk) * G) * 4,
-                                   (uint32_t)(G * 4));
+                                       (((int64_t)e * (p.Nout / kGroup) + blk) * G_all) * 4,
+                                   (uint32_t)(G_all * 4));
       const uint32_t dst = smem_base + S::STAGES * STAGE + b * kMaxGroups * 4;
-      for (int g0 = 0; g0 < G; g0 += 64)
+      for (int g0 = 0; g0 < G_all; g0 += 64)
         dma4(rs_p, dst + g0 * 4, (uint32_t)((g0 + lane) * 4));
     }
   }
@@ -607,19 +628,22 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       sw_panel + (ACT ? (kq >= 2 ? 1 : 0) : (wn * S::WAVE_N) / 128) * kMaxGroups;
 
   // the rest of a k-step: activation rows, their scales, MX weight scales
+  // (kb relative to k0; k0 is a multiple of 4, so kb & 3 is the absolute
+  // k-step's position in its group of 4)
   auto issue_as = [&](int kb) {
     const uint32_t st = smem_base + (kb % S::STAGES) * STAGE;
+    const int ka = k0 + kb;
 #pragma unroll
     for (int i = 0; i < AI; ++i)
       if (i < a_loads)
-        dma16(rs_a, st + i * S::THREADS * 16 + wave_slot, a_off[i] + (uint32_t)kb * AROW);
+        dma16(rs_a, st + i * S::THREADS * 16 + wave_slot, a_off[i] + (uint32_t)ka * AROW);
     if (loads_sc) {
-      const uint32_t soff = UE8M0 ? (uint32_t)(kb & ~3) : (uint32_t)kb * 4;
+      const uint32_t soff = UE8M0 ? (uint32_t)(ka & ~3) : (uint32_t)ka * 4;
       dma4(rs_s, st + SC_OFF + wave_sc, sc_off + soff);
     }
     if (loads_wsc && (kb & 3) == 0)
       dma16(rs_w, smem_base + S::STAGES * STAGE + ((kb >> 2) & 1) * WSC_SLOT + wave_slot,
-            wsc_off + (uint32_t)kb * 4);
+            wsc_off + (uint32_t)ka * 4);
   };
   auto issue = [&](int kb) {
     issue_as(kb);
@@ -648,7 +672,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       // 16x16x32 bf16 MFMAs per sub-tile per 128-deep block, chained in a
       // partial, then acc += partial * sw
       const uint8_t* sb = smem + (kb % S::STAGES) * STAGE;
-      const float sw = sw_mine[kb];
+      const float sw = sw_mine[k0 + kb];
       v8bf wb[S::TN][4];
 #pragma unroll
       for (int i = 0; i < S::TN; ++i) {
@@ -737,7 +761,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
         const v4i hi = *reinterpret_cast<const v4i*>(sb + w_frag1 + i * 4 * kRowBytes);
         wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      const float sw = sw_mine[kb];
+      const float sw = sw_mine[k0 + kb];
       // activation fragment j (and its scale) is read when sub-tile j-1's
       // MFMAs start, so at most two are live
       auto load_a = [&](int j, v8i& f, float& fs) {
@@ -925,6 +949,66 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   } else {
     // ---- epilogue: lane owns output row m, columns n_first .. n_first+4*TN-1
     const int n_first = n0 + wn * S::WAVE_N + kq * (4 * S::TN);
+    if (nsplit > 1) {
+      // split-K: this split's fp32 partial, then a ticket; the block with
+      // the last ticket adds the partials in split order (its own from
+      // registers: the same values it stored) and rounds once to bf16.
+      // Every thread fences its partial stores (device scope: the other
+      // splits may run on other XCDs) before the ticket is drawn, and the
+      // summing block fences before it reads.
+      const int64_t pstride = p.part_rows * (int64_t)p.Nout;
+#pragma unroll
+      for (int j = 0; j < S::TM; ++j) {
+        const int ml = ml0 + kSubStride * j;
+        if (ml >= rows_here) continue;
+        const int64_t row = out_row_of(ml);
+        if (row < 0) continue;
+        v4f* dst = reinterpret_cast<v4f*>(p.part + split * pstride + row * p.Nout + n_first);
+#pragma unroll
+        for (int i = 0; i < S::TN; ++i) dst[i] = acc[i][j];
+      }
+      // each wave's stores complete, then one device-scope release and the
+      // ticket (one L2 write-back per block rather than one per wave)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      __syncthreads();
+      int* ticket = reinterpret_cast<int*>(smem);
+      const int64_t item = (int64_t)tile * NT + nt;
+      if (tid == 0)
+        *ticket = __hip_atomic_fetch_add(p.counters + item, 1, __ATOMIC_ACQ_REL,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      if (*ticket != nsplit - 1) return;
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+#pragma unroll
+      for (int j = 0; j < S::TM; ++j) {
+        const int ml = ml0 + kSubStride * j;
+        if (ml >= rows_here) continue;
+        const int64_t row = out_row_of(ml);
+        if (row < 0) continue;
+        v4f sum[S::TN];
+#pragma unroll
+        for (int s2 = 0; s2 < kMaxSplit; ++s2) {
+          if (s2 < nsplit) {
+            v4f v[S::TN];
+            if (s2 == split) {
+#pragma unroll
+              for (int i = 0; i < S::TN; ++i) v[i] = acc[i][j];
+            } else {
+              const v4f* src =
+                  reinterpret_cast<const v4f*>(p.part + s2 * pstride + row * p.Nout + n_first);
+#pragma unroll
+              for (int i = 0; i < S::TN; ++i) v[i] = src[i];
+            }
+#pragma unroll
+            for (int i = 0; i < S::TN; ++i) sum[i] = s2 == 0 ? v[i] : sum[i] + v[i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < S::TN; ++i) acc[i][j] = sum[i];
+      }
+      if (tid == 0)
+        __hip_atomic_store(p.counters + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 #pragma unroll
     for (int j = 0; j < S::TM; ++j) {
       const int ml = ml0 + kSubStride * j;
@@ -952,7 +1036,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
 
 template <class S, int SC, bool ACT>
 hipError_t launch_shape(const GemmArgs& p, int max_tiles, hipStream_t stream) {
-  const int64_t blocks = ((int64_t)max_tiles * (p.Nout / S::BN) + 7) / 8 * 8;
+  const int64_t blocks =
+      ((int64_t)max_tiles * (p.Nout / S::BN) * (ACT ? 1 : max(p.ksplit, 1)) + 7) / 8 * 8;
   const dim3 grid((unsigned)blocks);
   if constexpr (SC == kQuantBf16) {
     // bf16 activation tiles take twice the LDS: only shapes whose ring fits

@@ -73,7 +73,21 @@ struct GemmArgs {
   float act_limit;            //   and its clamp limit (apply_act)
   int Kd;                    // reduction length, multiple of 128
   int Nout;                  // output columns, multiple of 128
+  // split-K (plain GEMM only; 1 = none): the k-steps are cut into ksplit
+  // ranges of a multiple of 4 k-steps each; split s of (tile, n-tile) item q
+  // stores its fp32 partial at part + (s * part_rows + row) * Nout, then
+  // takes a ticket from counters[q] (q = tile * (Nout / BN) + n-tile); the
+  // block that draws the last ticket adds the partials in split order,
+  // rounds once to bf16 and sets the counter back to 0.  The counters must
+  // be 0 at launch.
+  int ksplit;
+  float* part;
+  int64_t part_rows;
+  int32_t* counters;
 };
+
+// zero n int32 (a fill kernel: safe under graph capture)
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream);
 
 // Staging on its own launch: the bf16 copy.  fp8 staging runs inside
 // launch_route (StageQuant); here it returns hipErrorInvalidValue.

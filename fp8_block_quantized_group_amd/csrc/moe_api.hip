@@ -90,6 +90,24 @@ int64_t padded_capacity(const moe_problem_t* p, int64_t bs) {
   return cap / bs * bs;
 }
 
+// Split-K of the w2 GEMM: its reduction length N alone decides, so a
+// token's bits never depend on the batch.  Long reductions (N >= 8192, i.e.
+// 64+ k-steps) are cut in two: their GEMMs have few, long work items when
+// the experts have few rows (an 8-expert batch of 128 rows per expert has
+// 8 x 16 items for 256 CUs).  MOE_KSPLIT = 1 | 2 | 4 overrides it for
+// tuning runs (all calls of one layer must see the same value).
+int w2_ksplit(const moe_problem_t* p) {
+  const int G = p->intermediate / 128;
+  int s = p->intermediate >= 8192 ? 2 : 1;
+  const char* env = getenv("MOE_KSPLIT");
+  if (env != nullptr) {
+    const int v = atoi(env);
+    if (v == 1 || v == 2 || v == 4) s = v;
+  }
+  while (s > 1 && G < 4 * s) s /= 2;   // each split at least 4 k-steps
+  return s;
+}
+
 // Activation rows per GEMM tile, from the expected rows per expert.  Rows
 // per expert below 16 leave a 16-row MFMA tile mostly empty, and there the
 // GEMM streams weights at HBM speed whatever the tile height, so the
@@ -111,6 +129,13 @@ int choose_tile_m(const moe_problem_t* p) {
   const double rows = (double)p->num_tokens * p->top_k / p->num_experts;
   // bf16 activation tiles take twice the LDS: at most 128 rows
   if (p->act_quant == MOE_Q_BF16 && rows > 48.0) return 128;
+  // A split w2 wants few, whole-expert items: around 128 rows per expert a
+  // 128-row tile leaves about half the experts a nearly empty second tile
+  // (an 8-expert batch: 192 items, 384 when split = 1.5 waves of blocks for
+  // 256 CUs), a 192-row tile one tile each (256 split items).  Measured on
+  // the 8-expert N = 14336 batch: layer 0.453 ms (128 rows, unsplit) ->
+  // 0.423 ms (192 rows, split in two).
+  if (w2_ksplit(p) > 1 && rows > 96.0 && rows <= 192.0) return 192;
   if (rows <= 12.0) return 16;
   if (rows <= 24.0) return 32;
   if (rows <= 48.0) return 64;
@@ -183,6 +208,10 @@ struct Plan {
   size_t x_q_bytes, x_sf_bytes, a2_q_bytes, a2_sf_bytes, down_bytes;
   size_t gate_up_bytes;   // forward workspace: only for _no_mul activations
   size_t stage_ws_bytes;
+  int w2_split;                             // w2 split-K factor
+  size_t w2_part_bytes, w2_counters;        // its fp32 partials, its tickets
+  int64_t w2_part_rows;                     // rows of one split's partials
+  size_t w2_ws_bytes;                       // both, 256-byte aligned (0: no split)
 };
 
 Plan make_plan(const moe_problem_t* p) {
@@ -223,12 +252,30 @@ Plan make_plan(const moe_problem_t* p) {
   pl.a2_sf_bytes = p->act_quant == MOE_Q_BF16 ? 0 : (size_t)pl.s.expert_rows * pl.s.a2_sf_row * sfb;
   pl.down_bytes = (size_t)pl.s.expert_rows * K * 2;
   pl.gate_up_bytes = gated(p) ? 0 : (size_t)pl.s.expert_rows * N * 2;
+  // w2 split-K: S partial rows per output row (the indexed layout writes
+  // T*k rows, the others expert_rows), one ticket per (tile, n-tile) item of
+  // any tile height (the most tiles: 16-row blocks)
+  pl.w2_split = w2_ksplit(p);
+  pl.w2_part_bytes = 0;
+  pl.w2_counters = 0;
+  pl.w2_part_rows = 0;
+  pl.w2_ws_bytes = 0;
+  if (pl.w2_split > 1) {
+    const int64_t prow = std::max<int64_t>(pl.s.expert_rows, T * k);
+    int64_t items = pl.max_tiles;
+    if (!batched(p)) items = std::max<int64_t>(items, padded_capacity(p, 16) / 16 + E);
+    pl.w2_part_rows = prow;
+    pl.w2_part_bytes = (size_t)pl.w2_split * prow * K * 4;
+    pl.w2_counters = (size_t)items * (K / 128);
+    pl.w2_ws_bytes = round_up(pl.w2_part_bytes) + round_up(pl.w2_counters * 4);
+  }
   return pl;
 }
 
 // Device addresses of the forward workspace.
 struct Workspace {
   uint8_t* x_q; uint8_t* x_sf; uint8_t* a2_q; uint8_t* a2_sf; uint8_t* down; uint8_t* gate_up;
+  uint8_t* w2_split;
   int64_t* idx; float* w; moe_routing_t routing; int32_t* stage_ws;
   int32_t* sorted_ids; int32_t* expert_ids; int32_t* num_padded;   // indexed layout
   size_t total;
@@ -247,6 +294,7 @@ Workspace carve(const Plan& pl, const moe_problem_t* p, uint8_t* base) {
   w.a2_sf = take(pl.a2_sf_bytes);
   w.down = take(pl.down_bytes);
   w.gate_up = take(pl.gate_up_bytes);
+  w.w2_split = take(pl.w2_ws_bytes);
   const size_t slots = (size_t)pl.s.slots;
   w.idx = (int64_t*)take(slots * 8);
   w.w = (float*)take(slots * 4);
@@ -375,8 +423,20 @@ struct Indexed {
 moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const void* a_q,
                       const void* a_sf, const moe_routing_t* r, const void* w, const void* w_sf,
                       void* out, hipStream_t stream, bool act = false, void* act_q = nullptr,
-                      void* act_sf = nullptr, const Indexed* ix = nullptr) {
+                      void* act_sf = nullptr, const Indexed* ix = nullptr,
+                      void* split_ws = nullptr) {
   moe::GemmArgs g{};
+  g.ksplit = 1;
+  if (!w13 && pl.w2_split > 1) {
+    // fp32 partials, then the tickets (zeroed here: a fill kernel, so the
+    // call stays capturable)
+    g.ksplit = pl.w2_split;
+    g.part = (float*)split_ws;
+    g.part_rows = pl.w2_part_rows;
+    g.counters = (int32_t*)((uint8_t*)split_ws + round_up(pl.w2_part_bytes));
+    const hipError_t zerr = moe::launch_zero_i32(g.counters, (int64_t)pl.w2_counters, stream);
+    if (zerr != hipSuccess) return launch_status(zerr, "grouped_gemm_w2 (split tickets)");
+  }
   const size_t sfb = p->act_quant == MOE_Q_FP8_F32 ? 4 : 1;
   const size_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
   const int64_t cap = ix != nullptr ? padded_capacity(p, ix->block_size) : 0;
@@ -494,6 +554,16 @@ moe_status_t static_scratch_for_current_device(void** out) {
   return MOE_OK;
 }
 
+// The w2 call's workspace: needed (and checked) only when w2 splits.
+moe_status_t check_w2_ws(const Plan& pl, const void* ws, size_t ws_bytes) {
+  if (pl.w2_ws_bytes == 0) return MOE_OK;
+  CHECK(check_ptr(ws, "ws (w2 split-K workspace)", 16));
+  if (ws_bytes < pl.w2_ws_bytes)
+    return fail(MOE_ERR_WORKSPACE, "w2 workspace too small: %zu < %zu bytes", ws_bytes,
+                pl.w2_ws_bytes);
+  return MOE_OK;
+}
+
 moe_status_t check_indexed(const moe_problem_t* p, const int32_t* sorted_ids,
                            const int32_t* expert_ids, const int32_t* num_padded, int bs) {
   if (batched(p))
@@ -607,9 +677,17 @@ moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
   return run_act(p, pl, gate_up, routing, a2_q, a2_sf, (hipStream_t)stream);
 }
 
+moe_status_t moe_w2_workspace_size(const moe_problem_t* p, size_t* bytes) {
+  CHECK(validate_problem(p));
+  if (bytes == nullptr) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+  *bytes = make_plan(p).w2_ws_bytes;
+  return ok();
+}
+
 moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const void* a2_sf,
                                  const moe_routing_t* routing, const void* w2,
-                                 const void* w2_sf, void* down, void* stream) {
+                                 const void* w2_sf, void* down, void* ws, size_t ws_bytes,
+                                 void* stream) {
   CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
   CHECK(check_ptr(a2_q, "a2_q", 16));
@@ -619,7 +697,9 @@ moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const
   CHECK(check_ptr(w2_sf, "w2_sf", 4));
   CHECK(check_ptr(down, "down", 16));
   const Plan pl = make_plan(p);
-  return run_gemm(p, pl, false, a2_q, a2_sf, routing, w2, w2_sf, down, (hipStream_t)stream);
+  CHECK(check_w2_ws(pl, ws, ws_bytes));
+  return run_gemm(p, pl, false, a2_q, a2_sf, routing, w2, w2_sf, down, (hipStream_t)stream,
+                  false, nullptr, nullptr, nullptr, ws);
 }
 
 moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int32_t* slot_row,
@@ -681,7 +761,7 @@ moe_status_t moe_grouped_gemm_w13_act_indexed(
 moe_status_t moe_grouped_gemm_w2_indexed(
     const moe_problem_t* p, const void* a2_q, const void* a2_sf, const int32_t* sorted_ids,
     const int32_t* expert_ids, const int32_t* num_tokens_padded, int32_t block_size,
-    const void* w2, const void* w2_sf, void* down, void* stream) {
+    const void* w2, const void* w2_sf, void* down, void* ws, size_t ws_bytes, void* stream) {
   CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
   CHECK(check_indexed(p, sorted_ids, expert_ids, num_tokens_padded, block_size));
@@ -691,9 +771,10 @@ moe_status_t moe_grouped_gemm_w2_indexed(
   CHECK(check_ptr(w2_sf, "w2_sf", 4));
   CHECK(check_ptr(down, "down", 16));
   const Plan pl = make_plan(p);
+  CHECK(check_w2_ws(pl, ws, ws_bytes));
   const Indexed ix{sorted_ids, expert_ids, num_tokens_padded, block_size};
   return run_gemm(p, pl, false, a2_q, a2_sf, nullptr, w2, w2_sf, down, (hipStream_t)stream,
-                  false, nullptr, nullptr, &ix);
+                  false, nullptr, nullptr, &ix, ws);
 }
 
 moe_status_t moe_fused_mul_sum(const moe_problem_t* p, const void* down, const int64_t* topk_idx,
@@ -744,7 +825,7 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
       CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s, true));
     }
     CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s, false,
-                   nullptr, nullptr, &ix));
+                   nullptr, nullptr, &ix, w.w2_split));
     CHECK(run_mul_sum(p, w.down, w.idx, w.w, out, s));
     return ok();
   }
@@ -755,7 +836,8 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
     CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, w.gate_up, s));
     CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s));
   }
-  CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s));
+  CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s, false,
+                 nullptr, nullptr, nullptr, w.w2_split));
   CHECK(run_reduce(p, w.down, w.routing.slot_row, w.w, out, s));
   return ok();
 }

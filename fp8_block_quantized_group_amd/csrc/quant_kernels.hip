@@ -116,7 +116,18 @@ inline unsigned blocks_for(int64_t n, int per_block) {
   return (unsigned)((n + per_block - 1) / per_block);
 }
 
+__global__ __launch_bounds__(256) void zero_i32_kernel(int32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  zero_i32_kernel<<<blocks_for(n, 256), 256, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_stage_quant(const void* x, void* xq, void* xsf, int64_t rows, int K,
                               int quant, const int32_t* counts, int max_tokens,

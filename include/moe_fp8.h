@@ -211,7 +211,11 @@ typedef struct {
 
 /* Tile height.  tile_m follows the expected rows per expert, T * top_k / E:
  * 16, 32 or 64 rows up to 12, 24 or 48 rows per expert, 128 up to 128, and
- * 256 above (at most 128 for bf16 activations).  Two environment variables
+ * 256 above (at most 128 for bf16 activations); when w2 splits its reduction
+ * (N >= 8192), 192 rows between 96 and 192 rows per expert.  The tile height
+ * never changes the results' bits.  MOE_KSPLIT = 1 | 2 | 4 overrides the w2
+ * split for tuning runs (it does change them: every call of one layer must
+ * see the same value).  Two environment variables
  * override the choice for tuning runs.  MOE_TILE_M = 16 | 32 | 64 | 128 |
  * 192 | 256 (192 and 256 not for bf16; other values are ignored) is read by
  * every call; all calls of one layer must see the same value, since the
@@ -227,9 +231,10 @@ moe_status_t moe_routing_sizes(const moe_problem_t* p, moe_sizes_t* out);
 moe_status_t moe_stage_workspace_size(const moe_problem_t* p, size_t* bytes);
 
 /* Device workspace bytes moe_forward needs (host only).  It holds the staged
- * fp8 activations, the fp8 w2 input, the bf16 down projection and the
- * routing layout (the workspace of HummingExpertsBase.prepare_buffers minus
- * the gate_up buffer, which the fused w13 call never materializes). */
+ * fp8 activations, the fp8 w2 input, the bf16 down projection, the routing
+ * layout and, when w2 splits its reduction, the w2 workspace (the workspace
+ * of HummingExpertsBase.prepare_buffers minus the gate_up buffer, which the
+ * fused w13 call never materializes). */
 moe_status_t moe_workspace_size(const moe_problem_t* p, size_t* bytes);
 
 /* Steps 1-2.  hidden: bf16 [T, K] (contiguous) or [E, max_tokens, K]
@@ -292,10 +297,19 @@ moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
  * fed by the activation buffer).
  * down[r, :] = block-scaled GEMM of a2 row r with w2[e] (fp8 or bf16 a2 per
  * the activation scheme); down: bf16 [expert_rows, K]; rows past an expert's
- * count are not written. */
+ * count are not written.
+ * Split-K: when the reduction is long (N >= 8192) the k-steps are cut into
+ * ranges whose fp32 partials are added in a fixed order before the one bf16
+ * rounding (the experts pass a `locks` buffer to every Humming GEMM for the
+ * same purpose, HummingExpertsBase).  The split depends on N alone, so a
+ * token's bits do not depend on its batch.  ws: device workspace of
+ * moe_w2_workspace_size bytes (fp32 partials and per-tile tickets; may be
+ * NULL when that size is 0); calls sharing one ws must not overlap. */
+moe_status_t moe_w2_workspace_size(const moe_problem_t* p, size_t* bytes);
 moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const void* a2_sf,
                                  const moe_routing_t* routing, const void* w2,
-                                 const void* w2_sf, void* down, void* stream);
+                                 const void* w2_sf, void* down, void* ws, size_t ws_bytes,
+                                 void* stream);
 
 /* Step 6: out[t] = bf16(sum over j ascending with slot_row[t, j] >= 0 of
  * topk_w[t, j] * down[slot_row[t, j]]); tokens with no routed slot get 0.
@@ -344,7 +358,8 @@ moe_status_t moe_grouped_gemm_w13_act_indexed(
     const int32_t* expert_ids, const int32_t* num_tokens_padded, int32_t block_size,
     const void* w13, const void* w13_sf, void* a2_q, void* a2_sf, void* stream);
 
-/* Step 5 on the block map: down[s] = the w2 GEMM of a2 row s for every routed
+/* Step 5 on the block map (ws as for moe_grouped_gemm_w2): down[s] = the w2
+ * GEMM of a2 row s for every routed
  * position q with s = sorted_ids[q] (the experts run w2 with top_k 1 on the
  * (token, slot)-ordered w13 output, so its block map may be another one, of
  * another block size, from moe_align_block_size on the same routing); down
@@ -353,7 +368,7 @@ moe_status_t moe_grouped_gemm_w13_act_indexed(
 moe_status_t moe_grouped_gemm_w2_indexed(
     const moe_problem_t* p, const void* a2_q, const void* a2_sf, const int32_t* sorted_ids,
     const int32_t* expert_ids, const int32_t* num_tokens_padded, int32_t block_size,
-    const void* w2, const void* w2_sf, void* down, void* stream);
+    const void* w2, const void* w2_sf, void* down, void* ws, size_t ws_bytes, void* stream);
 
 /* Step 6 on the (token, slot) order (moe_fused_mul_sum): out[t] =
  * bf16(sum over j ascending with topk_idx[t, j] in [0, E) of topk_w[t, j] *

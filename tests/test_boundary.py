@@ -283,9 +283,11 @@ def test_indexed_validation(lib):
     st = lib.moe_grouped_gemm_w13_act_indexed(ctypes.byref(c), V, V, None, V, V, 16, V, V, V,
                                               V, None)
     assert st == -1 and "sorted_ids" in lib.moe_last_error().decode()
-    st = lib.moe_grouped_gemm_w2_indexed(ctypes.byref(c), V, V, V, V, None, 16, V, V, V, None)
+    st = lib.moe_grouped_gemm_w2_indexed(ctypes.byref(c), V, V, V, V, None, 16, V, V, V, None,
+                                         0, None)
     assert st == -1 and "num_tokens_padded" in lib.moe_last_error().decode()
-    st = lib.moe_grouped_gemm_w2_indexed(ctypes.byref(c), V, V, V, V, V, 24, V, V, V, None)
+    st = lib.moe_grouped_gemm_w2_indexed(ctypes.byref(c), V, V, V, V, V, 24, V, V, V, None,
+                                         0, None)
     assert st == -2
     st = lib.moe_fused_mul_sum(ctypes.byref(c), V, _fake((1 << 20) + 4), V, V, None)
     assert st == -1 and "topk_idx" in lib.moe_last_error().decode()

@@ -8,10 +8,12 @@ operations in the same order whatever the tile height, the column-tile width
 and the other rows of its tile -- staging and the activation quantize one
 row's groups; each GEMM output is one lane's chain of 128-deep MFMA block
 products promoted (or, for the MX schemes, accumulated by the MFMA itself)
-in ascending k order; the reduce sums a token's slots in ascending order.
+in ascending k order (a w2 whose reduction is split -- a choice made from
+N alone -- adds its ranges' fp32 partials in range order); the reduce sums
+a token's slots in ascending order.
 So a token run alone (16-row tiles), inside a small batch (16- or 32-row
-tiles) and inside a large one (128-row tiles, and 256-row tiles forced)
-must give identical bits.  The test also runs the tokens in reverse order,
+tiles) and inside a large one (its default tiles, and 128- and 256-row
+tiles forced) must give identical bits.  The test also runs the tokens in reverse order,
 which changes every expert's row order.
 """
 import numpy as np
@@ -25,6 +27,8 @@ pytestmark = pytest.mark.gpu
 
 SCHEMES = {
     "ue8m0": dict(act_quant="ue8m0"),
+    # N = 8192: w2 splits its reduction in two (the split depends on N only)
+    "ue8m0_split": dict(act_quant="ue8m0", N=8192, K=512),
     "fp32": dict(act_quant="fp32"),
     "mxfp8": dict(act_quant="mxfp8", weight_quant="mxfp8"),
     "mxfp4": dict(act_quant="mxfp8", weight_quant="mxfp4"),
@@ -57,16 +61,19 @@ def test_token_bits_independent_of_batch(scheme, monkeypatch):
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need a GPU")
     # 384 tokens x top-2 over 6 experts: 128 rows per expert on average
-    cfg = moe_synth.custom(name=f"invariance_{scheme}", T=384, E=6, top_k=2, K=1024, N=1024,
-                           seed=51, **SCHEMES[scheme])
+    sizes = dict(K=1024, N=1024)
+    sizes.update({k: v for k, v in SCHEMES[scheme].items() if k in ("K", "N")})
+    cfg = moe_synth.custom(name=f"invariance_{scheme}", T=384, E=6, top_k=2, seed=51, **sizes,
+                           **{k: v for k, v in SCHEMES[scheme].items() if k not in ("K", "N")})
     inp = moe_synth.make_inputs(cfg, "cuda")
     full, tile = _forward(cfg, inp, monkeypatch=monkeypatch)
-    assert tile == 128, tile
-    # the same batch with the other tall tile height
+    assert tile == (192 if cfg.N >= 8192 else 128), tile
+    # the same batch with other tile heights
     tall = 64 if cfg.act_quant == "bf16" else 256
-    full2, tile2 = _forward(cfg, inp, tile_m=tall, monkeypatch=monkeypatch)
-    assert tile2 == tall
-    assert np.array_equal(full, full2), f"{scheme}: 128- and {tall}-row tiles differ"
+    for other in (128, tall):
+        full2, tile2 = _forward(cfg, inp, tile_m=other, monkeypatch=monkeypatch)
+        assert tile2 == other
+        assert np.array_equal(full, full2), f"{scheme}: {tile}- and {other}-row tiles differ"
     # reversed token order: every expert's rows come in another order
     rev, _ = _forward(cfg, inp, sel=np.arange(cfg.T)[::-1].copy(), monkeypatch=monkeypatch)
     assert np.array_equal(rev[::-1], full), f"{scheme}: reversed batch differs"
@@ -84,5 +91,5 @@ def test_token_bits_independent_of_batch(scheme, monkeypatch):
     part, tile3 = _forward(cfg, inp, sel=np.arange(lo, lo + 40), monkeypatch=monkeypatch)
     assert tile3 in (16, 32), tile3
     assert np.array_equal(part, full[lo:lo + 40]), f"{scheme}: 40-token slice differs"
-    print(f"{scheme}: tokens {picks} alone, a 40-token slice, 128/{tall}-row tiles and the "
-          f"reversed batch give identical bits")
+    print(f"{scheme}: tokens {picks} alone, a 40-token slice, {tile}/128/{tall}-row tiles and "
+          f"the reversed batch give identical bits")

@@ -90,6 +90,17 @@ MID = {
                                     N=2048, seed=46, layout="batched", max_tokens=384,
                                     routing="zipf", zipf_s=1.1),
 }
+# w2 reductions of N >= 8192 split in two (split-K): N = 8192 (64 k-steps)
+MID.update({
+    "split_ue8m0": moe_synth.custom(name="split_ue8m0", T=200, E=4, top_k=2, K=512, N=8192,
+                                    seed=47, routing="zipf", zipf_s=1.1, pad_frac=0.05),
+    "split_mxfp8": moe_synth.custom(name="split_mxfp8", T=200, E=4, top_k=2, K=512, N=8192,
+                                    seed=48, act_quant="mxfp8", weight_quant="mxfp8"),
+    "split_bf16": moe_synth.custom(name="split_bf16", T=200, E=4, top_k=2, K=512, N=8192,
+                                   seed=49, act_quant="bf16"),
+    "split_batched": moe_synth.custom(name="split_batched", T=200, E=4, top_k=2, K=512,
+                                      N=8192, seed=50, layout="batched", max_tokens=160),
+})
 MID_TILES = [16, 128, 256]
 MID_CASES = [(n, t) for n in MID for t in MID_TILES
              if not (MID[n].act_quant == "bf16" and t > 128)]
@@ -701,6 +712,39 @@ def test_mid_fused_equals_chain(gpu, name, tile_m, monkeypatch):
 def test_mid_forward_end_to_end(gpu, name, tile_m, monkeypatch):
     monkeypatch.setenv("MOE_TILE_M", str(tile_m))
     _forward_end_to_end(name)
+
+
+@pytest.mark.parametrize("ksplit", [1, 2, 4])
+@pytest.mark.parametrize("name", ["mid_fp32", "mid_mxfp4", "split_ue8m0", "split_batched"])
+def test_w2_split_k(gpu, name, ksplit, monkeypatch):
+    """w2 with its reduction forced into 1, 2 or 4 ranges (MOE_KSPLIT): every
+    routed row within the GEMM bound of the oracle, nothing written outside
+    the experts' rows, the same bits on a second call (the partials are
+    added in split order, whichever split finishes last), and the whole
+    layer through moe_forward within the output bound."""
+    monkeypatch.setenv("MOE_KSPLIT", str(ksplit))
+    cfg, h, dev, ref = case(name)
+    p = problem(cfg)
+    expect = ksplit if cfg.N // 128 >= 4 * ksplit else max(1, ksplit // 2)
+    assert (moe.w2_workspace_size(p) > 0) == (expect > 1)
+    _gemm_isolated(cfg, h, dev, ref, "w2")
+    s = moe.sizes(p)
+    vr = valid_rows(cfg, ref)
+    ue = O.act_e8m0(cfg)
+    a_q = to_dev(ref["a2_q"])
+    a_sf = None if ref["a2_sf"] is None else to_dev(
+        O.pack_ue8m0_rows(ref["a2_sf"]) if ue and O.act_group(cfg) == 128 else ref["a2_sf"])
+    routing = oracle_routing(p, cfg, ref)
+    ws = moe.alloc_w2_workspace(p)
+    outs = []
+    for _ in range(2):
+        down = torch.full((s["expert_rows"], cfg.K), SENTINEL_BF16, dtype=torch.int16,
+                          device="cuda").view(torch.bfloat16)
+        moe.grouped_gemm_w2(p, a_q, a_sf, routing, dev["w2"], dev["w2_sf"], down, ws)
+        torch.cuda.synchronize()
+        outs.append(to_np(down)[vr])
+    assert np.array_equal(outs[0], outs[1]), f"{name} split {ksplit}: not deterministic"
+    check_output(to_np(run_forward(cfg, dev)), ref["out"], f"{name} split {ksplit} output")
 
 
 # ---------------------------------------------------------------------------
