@@ -117,27 +117,35 @@ __device__ __forceinline__ bool row_live(int64_t row, const int32_t* counts, int
   return (row - e * max_tokens) < (int64_t)counts[e];
 }
 
-// The group quantizer on one group gid of GROUP values (128: per-128
+// The group quantizer (load_group_chunk, then quantize_group_chunk) on one
+// group gid of GROUP values (128: per-128
 // scales, UE8M0 bytes in rows of sf_row_len or fp32 [rows, G]; 32: MXFP8,
 // E8M0 bytes in rows of G) of bf16 rows of G groups: GROUP/16 lanes per
 // group, 16 values per lane from two adjacent 16-byte loads and one 16-byte
 // store of codes.  The hidden states are read once, so the loads are
 // non-temporal; the codes are not (the w13 GEMM re-reads them).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+// This lane's 16 values of group gid (its two adjacent 16-byte chunks).
+struct GroupChunk {
+  u32x4_t a, b;
+};
+template <int GROUP>
+__device__ __forceinline__ GroupChunk load_group_chunk(const uint16_t* __restrict__ x,
+                                                       int64_t gid, int lane) {
+  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + gid * GROUP) + 2 * lane;
+  return GroupChunk{__builtin_nontemporal_load(src), __builtin_nontemporal_load(src + 1)};
+}
+// The quantizer on a loaded chunk: the group maximum across its lanes, the
+// scale, the codes and the scale byte / word.
 template <int GROUP, bool UE8M0>
-__device__ __forceinline__ void quantize_group(const uint16_t* __restrict__ x,
-                                               uint8_t* __restrict__ xq,
-                                               uint8_t* __restrict__ xsf, int64_t gid, int lane,
-                                               int G, int sf_row_len,
-                                               const int32_t* __restrict__ counts,
-                                               int max_tokens) {
+__device__ __forceinline__ void quantize_group_chunk(const GroupChunk& c,
+                                                     uint8_t* __restrict__ xq,
+                                                     uint8_t* __restrict__ xsf, int64_t gid,
+                                                     int lane, int G, int sf_row_len) {
   static_assert(GROUP == 128 || (GROUP == 32 && UE8M0), "per-128 groups, or MX groups of 32");
   const int64_t row = gid / G;
   const int g = (int)(gid - row * G);
-  if (!row_live(row, counts, max_tokens)) return;
-  const u32x4_t* src = reinterpret_cast<const u32x4_t*>(x + gid * GROUP) + 2 * lane;
-  const u32x4_t a = __builtin_nontemporal_load(src);
-  const u32x4_t b = __builtin_nontemporal_load(src + 1);
+  const u32x4_t a = c.a, b = c.b;
   float f[16];
   unpack8(make_uint4(a.x, a.y, a.z, a.w), f);
   unpack8(make_uint4(b.x, b.y, b.z, b.w), f + 8);
@@ -164,6 +172,7 @@ __device__ __forceinline__ void quantize_group(const uint16_t* __restrict__ x,
     if (lane == 0) reinterpret_cast<uint32_t*>(xsf + row * (int64_t)G * 4)[g] = gs.stored;
   }
 }
+
 
 // ---- activations ------------------------------------------------------------
 // Kinds (values match moe_act_t).  Gated kinds combine the gate column g with

@@ -16,7 +16,7 @@
 // (16 bytes), the lanes reduce |x| with DPP max steps, each lane writes 8
 // fp8 bytes.  A 64-lane wave covers 512 contiguous input values, so every
 // load and store instruction is fully coalesced.  (The hidden states' fp8
-// staging uses quantize_group from device_common.h inside the routing scan's
+// staging uses the group quantizer of device_common.h inside the routing scan's
 // launch; the kernels here copy bf16 and re-quantize the w2 input of the
 // unfused path.)
 #include "device_common.h"
