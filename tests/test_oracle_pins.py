@@ -78,6 +78,28 @@ def _frac_bf16(x: Fraction) -> Fraction:
     return sgn * fl * q
 
 
+def _frac_f32(x: Fraction) -> Fraction:
+    """Nearest binary32 value (24 significant bits), ties to even, for x in
+    the normal range (the pins below keep every intermediate there)."""
+    if x == 0:
+        return Fraction(0)
+    sgn = -1 if x < 0 else 1
+    a = abs(x)
+    e = math.floor(math.log2(a.numerator) - math.log2(a.denominator))
+    while Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    assert -126 <= e <= 127, "outside binary32's normal range"
+    q = Fraction(2) ** (e - 23)
+    n = a / q
+    fl = math.floor(n)
+    rem = n - fl
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and fl % 2 == 1):
+        fl += 1
+    return sgn * fl * q
+
+
 def _ceil_log2(r: Fraction) -> int:
     """Smallest integer j with 2^j >= r (r > 0), exactly."""
     j = math.floor(math.log2(r.numerator) - math.log2(r.denominator)) - 2
@@ -262,6 +284,56 @@ def test_fp32_scale_mode_properties():
     deq = O.e4m3_decode(codes).reshape(400, 2, 128) * s[:, :, None]
     err = np.abs(deq - g)
     assert np.all(err <= np.maximum(np.abs(g) * 2.0 ** -4, s[:, :, None] * 2.0 ** -10) * 1.0001)
+
+
+def test_fp32_scale_mode_exact_rationals():
+    """fp32 scales ([STAGE] _quantize_fp8_groups without the UE8M0 round-up,
+    readings R1-R4): s = fl32(max(amax, fl32(1e-4)) / 448), then each code is
+    the nearest e4m3fn value (saturating) of fl32(x * fl32(1 / s)).  Every
+    step is redone here in exact rationals with its own binary32 rounding;
+    groups span 2^-24 .. 2^14 in magnitude, with all-tiny groups (the 1e-4
+    floor) and groups whose largest element sits a hair under a binade."""
+    rng = np.random.default_rng(19)
+    rows, G = 80, 3
+    mag = np.exp2(rng.uniform(-24, 14, (rows, G)))
+    x = rng.standard_normal((rows, G * 128)) * np.repeat(mag, 128, axis=1)
+    x[5, :128] *= 1e-6                                # amax below the floor
+    x[6, 128:256] = 0.0                               # an all-zero group
+    x[7, 0] = np.nextafter(np.float32(448.0), np.float32(0))   # amax just under 448
+    x = x.astype(np.float32)
+    # rows 40-59, group 0: besides the group maximum, values whose scaled
+    # product lies on or next to a midpoint between two e4m3fn values, so
+    # that the binary32 rounding of x * (1/s) before the fp8 conversion
+    # decides the code (ties go to the even code)
+    floor = Fraction(float(np.float32(1e-4)))
+    mids = [(_FV[i] + _FV[i + 1]) / 2 for i in range(len(_FV) - 1)]
+    tie_rows = range(40, 60)
+    for r in tie_rows:
+        amax = np.float32(np.exp2(rng.uniform(-10, 10)))
+        x[r, :128] = 0.0
+        x[r, 0] = amax
+        inv = _frac_f32(1 / _frac_f32(max(Fraction(float(amax)), floor) / 448))
+        for c in range(1, 128):
+            m = mids[int(rng.integers(len(mids)))]
+            v = np.float32(float(m / inv))
+            v = [np.nextafter(v, np.float32(0)), v, np.nextafter(v, np.float32(np.inf))][
+                int(rng.integers(3))]
+            x[r, c] = -v if rng.random() < 0.5 else v
+    codes, s = O.quantize_groups(x, ue8m0=False)
+    for r in range(rows):
+        for g in range(G):
+            grp = x[r, 128 * g:128 * g + 128]
+            A = max(Fraction(float(np.abs(grp).max())), floor)
+            s_ref = _frac_f32(A / 448)
+            assert Fraction(float(s[r, g])) == s_ref, (r, g)
+            inv = _frac_f32(1 / s_ref)
+            cols = range(128) if (r in tie_rows and g == 0) else \
+                rng.choice(128, 24, replace=False).tolist() + [int(np.abs(grp).argmax())]
+            for c in cols:
+                xv = Fraction(float(grp[c]))
+                want = _frac_encode(_frac_f32(xv * inv) if xv != 0 else Fraction(0),
+                                    bool(np.signbit(grp[c])))
+                assert int(codes[r, 128 * g + c]) == want, (r, g, c)
 
 
 def test_pack_bytes_matches_int32_little_endian():
