@@ -84,6 +84,9 @@ struct GemmArgs {
   float* part;
   int64_t part_rows;
   int32_t* counters;
+  // item order inside a group of m-tiles: super-columns of sn n-tiles, each
+  // walked m-tile-major (sn = 1: n-tile-major); set by the launcher
+  int sn;
 };
 
 // zero n int32 (a fill kernel: safe under graph capture)

@@ -222,7 +222,10 @@ typedef struct {
  * stage builds the tile schedule for the height the GEMM calls then read it
  * with.  MOE_GEMM_WIDE = 0 | 1 picks 128 or 256 output columns for the
  * 128-row tiles of the unfused GEMMs; it is read once per scale scheme, at
- * its first GEMM call, and does not change the schedule. */
+ * its first GEMM call, and does not change the schedule.  MOE_SN = n sets how
+ * many n-tiles the GEMMs walk together inside an expert's m-tiles (default 1
+ * for tiles up to 128 rows, 2 above; read once per tile shape); it changes
+ * only the order of the blocks, never a result's bits. */
 
 /* Sizes of every buffer of `p` (host only). */
 moe_status_t moe_routing_sizes(const moe_problem_t* p, moe_sizes_t* out);
