@@ -273,12 +273,24 @@ def stage_ceiling_call(cfg, inp):
     return lambda: dst.copy_(inp["hidden"])
 
 
-def recorded_traffic(kernel_file: str, workload: str):
-    """HBM bytes per launch of the fused w13 GEMM, from the committed counter
-    summary, only if the kernel source is unchanged since it was taken."""
+# the sources that decide what the fused w13 step moves: the kernel, the tile
+# schedules the routing scan builds, and the launch configuration
+TRAFFIC_SOURCES = ("grouped_gemm.hip", "route_kernels.hip", "moe_api.hip")
+
+
+def sources_digest(files=TRAFFIC_SOURCES) -> str:
     import hashlib
-    src = os.path.join(ROOT, "fp8_block_quantized_group_amd", "csrc", kernel_file)
-    digest = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "fp8_block_quantized_group_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per call of the fused w13 step (its launches added), from the
+    committed counter summary, only if none of the sources that decide it
+    has changed since it was taken."""
+    digest = sources_digest()
     path = os.path.join(ROOT, "profiles", f"grouped_gemm_w13_act_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -287,7 +299,7 @@ def recorded_traffic(kernel_file: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != digest:
+    if fields.get("sources_sha256") != digest:
         return None
     return float(fields["hbm_bytes_per_launch"])
 
@@ -377,11 +389,15 @@ def main():
     gemm_ms = t_w13[0] + t_w2[0]
     gemm_tflops = gemm_flops / (gemm_ms * 1e-3) / 1e12
     w13_gbs = kernels["grouped_gemm_w13_act"]["GB/s"]
-    traffic = recorded_traffic("grouped_gemm.hip", cfg.name)
+    traffic = recorded_traffic(cfg.name)
+    # with a second (256-row) tile list the fused w13 step is two concurrent
+    # launches; the HIP events on the calling stream span both (the second
+    # stream joins back to it), and the traffic adds both launches' counters
     roofline = {"bound": "hbm", "achieved": round(w13_gbs, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(w13_gbs / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
                 "kernel": "grouped_gemm_w13_act",
+                "launches": 2 if s["tall_tile_m"] else 1,
                 "algorithmic_bytes_per_launch": alg["w13_act_bytes"]}
 
     per_expert = gemm_figures(cfg, counts, t_w13[0], t_w2[0])
@@ -404,7 +420,8 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "E": cfg.E, "top_k": cfg.top_k,
                    "K": cfg.K, "N": cfg.N, "layout": cfg.layout, "act_quant": cfg.act_quant,
                    "routing": cfg.routing, "pad_frac": cfg.pad_frac, "T_valid": T_valid,
-                   "routed_rows": int(counts.sum()), "tile_m": s["tile_m"]},
+                   "routed_rows": int(counts.sum()), "tile_m": s["tile_m"],
+                   "tall_tile_m": s["tall_tile_m"]},
         "gemm_tflops": round(gemm_tflops, 2),
         "gemm_frac_fp8_peak": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
         "kernels": {k: {kk: round(vv, 4) for kk, vv in v.items()} for k, v in kernels.items()},

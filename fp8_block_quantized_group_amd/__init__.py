@@ -60,7 +60,9 @@ class _Sizes(ctypes.Structure):
                 ("stage_rows", ctypes.c_int64), ("expert_rows", ctypes.c_int64),
                 ("x_sf_row", ctypes.c_int64), ("a2_sf_row", ctypes.c_int64),
                 ("padded_rows", ctypes.c_int64), ("blocks", ctypes.c_int64),
-                ("tile_m", ctypes.c_int32)]
+                ("tile_m", ctypes.c_int32), ("tall_tile_m", ctypes.c_int32),
+                ("max_tiles", ctypes.c_int64), ("tall_list_offset", ctypes.c_int64),
+                ("max_tiles_tall", ctypes.c_int64)]
 
 
 EXPORTS = ("moe_routing_sizes", "moe_stage_workspace_size", "moe_workspace_size",

@@ -116,13 +116,24 @@ struct StageQuant {
   bool ue8m0;
 };
 
+// The GEMM tile schedules the routing scan writes: the main list (tiles of
+// tile_m rows, capacity max_tiles) and, when tall is set, a second list of
+// 2 * tile_m-row tiles that takes every expert of more than tile_m rows
+// (those are then absent from the main list).
+struct TileLists {
+  int tile_m;
+  int max_tiles;
+  int32_t* list;
+  int max_tiles_tall;
+  int32_t* tall;      // nullptr: one list
+};
+
 hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint8_t* is_padding,
                         int T, int k, int E, const EplbArgs& eplb, int64_t* idx_out,
                         float* w_out, int32_t* hist, const int32_t* counts_in, int max_tokens,
-                        int tile_m, int max_tiles, int32_t* expert_num_tokens,
+                        const TileLists& tl, int32_t* expert_num_tokens,
                         int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
-                        int32_t* tile_list, hipStream_t stream,
-                        const StageQuant* sq = nullptr);
+                        hipStream_t stream, const StageQuant* sq = nullptr);
 
 // quant: the scale scheme: an activation scheme (kQuant*; kQuantMxfp8 with
 // e4m3 MX weights) or kSchemeMxfp8W4 (MXFP8 activations, e2m1 MX weights).

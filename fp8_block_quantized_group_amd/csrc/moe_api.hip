@@ -143,6 +143,24 @@ int choose_tile_m(const moe_problem_t* p) {
   return 256;
 }
 
+// Heavy experts in a second tile list.  At 128-row tiles (experts of up to
+// about 128 rows on average) the experts above 128 rows re-read their
+// weights once per 128-row tile; in tiles of 256 rows, launched alongside
+// the 128-row tiles of the other experts on a second stream, DSv3-shaped
+// prefill measured w13 1.89 -> 1.76 ms (also with MXFP4 weights: 1.52 ->
+// 1.42 ms) and w2 0.99 -> 0.96 ms; the same two launches one after the
+// other gained only 3 % on w13 and lost 3 % on w2 (each launch's last wave
+// of blocks runs half empty).  Not for bf16 activations (128-row tiles at
+// most), the indexed layout (one block size) or a split w2 (its tickets
+// are indexed by tile).  A forced tile height (MOE_TILE_M) keeps one list;
+// MOE_TALL = 0 | 1 turns the second list off / on where it can run.
+bool use_tall(const moe_problem_t* p, int tile_m, int w2_split) {
+  const bool can = tile_m == 128 && !indexed(p) && p->act_quant != MOE_Q_BF16 && w2_split == 1;
+  const char* env = getenv("MOE_TALL");
+  if (env != nullptr && (env[0] == '0' || env[0] == '1')) return can && env[0] == '1';
+  return can && getenv("MOE_TILE_M") == nullptr;
+}
+
 moe_status_t validate_problem(const moe_problem_t* p) {
   if (p == nullptr) return fail(MOE_ERR_INVALID_ARG, "problem is NULL");
   if (p->num_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "num_tokens < 0 (%d)", p->num_tokens);
@@ -205,6 +223,7 @@ struct Plan {
   moe_sizes_t s;
   int64_t route_blocks;
   int64_t max_tiles;
+  bool tall;                                // heavy experts in the second tile list
   size_t x_q_bytes, x_sf_bytes, a2_q_bytes, a2_sf_bytes, down_bytes;
   size_t gate_up_bytes;   // forward workspace: only for _no_mul activations
   size_t stage_ws_bytes;
@@ -238,6 +257,10 @@ Plan make_plan(const moe_problem_t* p) {
   // most one group per expert plus one per 8 tiles, so E + max_tiles + 1 is
   // a safe bound)
   pl.s.tile_list = 4 + 8 * pl.max_tiles + (E + pl.max_tiles + 1);
+  pl.s.max_tiles = pl.max_tiles;
+  pl.s.tall_tile_m = 0;
+  pl.s.tall_list_offset = 0;
+  pl.s.max_tiles_tall = 0;
   const bool mx = p->act_quant == MOE_Q_MXFP8;
   const bool bf = p->act_quant == MOE_Q_BF16;
   pl.s.x_sf_row = bf ? 0 : mx ? K / 32 : ue ? 4 * ((GK + 3) / 4) : GK;
@@ -268,6 +291,18 @@ Plan make_plan(const moe_problem_t* p) {
     pl.w2_part_bytes = (size_t)pl.w2_split * prow * K * 4;
     pl.w2_counters = (size_t)items * (K / 128);
     pl.w2_ws_bytes = round_up(pl.w2_part_bytes) + round_up(pl.w2_counters * 4);
+  }
+  pl.tall = use_tall(p, pl.s.tile_m, pl.w2_split);
+  if (pl.tall) {
+    // the tall list after the main one, 16-byte aligned: tiles of twice the
+    // height for experts above tile_m rows (at most one partial tile each)
+    const int64_t th = 2 * bm;
+    pl.s.tall_tile_m = (int32_t)th;
+    pl.s.max_tiles_tall = batched(p) ? E * ((p->max_tokens_per_expert + th - 1) / th)
+                                     : (T * k + th - 1) / th + E;
+    pl.s.tall_list_offset = (pl.s.tile_list + 3) / 4 * 4;
+    pl.s.tile_list = pl.s.tall_list_offset + 4 + 8 * pl.s.max_tiles_tall +
+                     (E + pl.s.max_tiles_tall + 1);
   }
   return pl;
 }
@@ -400,11 +435,14 @@ moe_status_t run_stage(const moe_problem_t* p, const Plan& pl, const void* hidde
                                 cin, p->max_tokens_per_expert, stream);
     if (err != hipSuccess) return launch_status(err, "stage_quant");
   }
+  const moe::TileLists tl{pl.s.tile_m, (int)pl.max_tiles, r->tile_list,
+                          (int)pl.s.max_tiles_tall,
+                          pl.tall ? r->tile_list + pl.s.tall_list_offset : nullptr};
   const hipError_t err = moe::launch_route(
       topk_ids, topk_weights, is_padding, p->num_tokens, p->top_k, p->num_experts,
-      eplb_args(eplb), idx_out, w_out, hist, cin, p->max_tokens_per_expert, pl.s.tile_m,
-      (int)pl.max_tiles, r->expert_num_tokens, r->expert_offsets, r->row_src, r->slot_row,
-      r->tile_list, stream, fused ? &sq : nullptr);
+      eplb_args(eplb), idx_out, w_out, hist, cin, p->max_tokens_per_expert, tl,
+      r->expert_num_tokens, r->expert_offsets, r->row_src, r->slot_row, stream,
+      fused ? &sq : nullptr);
   return launch_status(err, fused ? "route + stage_quant" : "route");
 }
 
@@ -424,7 +462,7 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
                       const void* a_sf, const moe_routing_t* r, const void* w, const void* w_sf,
                       void* out, hipStream_t stream, bool act = false, void* act_q = nullptr,
                       void* act_sf = nullptr, const Indexed* ix = nullptr,
-                      void* split_ws = nullptr) {
+                      void* split_ws = nullptr, bool tall_list = false) {
   moe::GemmArgs g{};
   g.ksplit = 1;
   if (!w13 && pl.w2_split > 1) {
@@ -471,6 +509,11 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
   } else {
     g.tile_list = r->tile_list;
     g.row_src = (w13 && !batched(p)) ? r->row_src : nullptr;
+    if (tall_list) {
+      g.tile_list = r->tile_list + pl.s.tall_list_offset;
+      tile_m = pl.s.tall_tile_m;
+      max_tiles = (int)pl.s.max_tiles_tall;
+    }
   }
   g.Kd = w13 ? p->hidden : p->intermediate;
   g.Nout = w13 ? (int)w13_rows(p) : p->hidden;
@@ -552,6 +595,77 @@ moe_status_t static_scratch_for_current_device(void** out) {
   }
   *out = g_scratch_ptr[dev];
   return MOE_OK;
+}
+
+// The second stream of the two-list GEMM steps: one per device with two
+// events, created at the first such step on that device (default priority,
+// non-blocking) and kept until the process ends.  The mutex keeps one host
+// thread's fork-launch-join sequence whole, since the events are shared.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  std::mutex mu;
+};
+std::mutex g_side_mutex;
+SideStream g_side[kMaxDevices];
+
+moe_status_t side_stream_for_current_device(SideStream** out) {
+  int dev = -1;
+  hipError_t err = hipGetDevice(&dev);
+  if (err != hipSuccess)
+    return fail(MOE_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(err));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(MOE_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_side_mutex);
+  SideStream& sd = g_side[dev];
+  if (sd.s == nullptr) {
+    hipStream_t st = nullptr;
+    hipEvent_t a = nullptr, b = nullptr;
+    err = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&a, hipEventDisableTiming);
+    if (err == hipSuccess) err = hipEventCreateWithFlags(&b, hipEventDisableTiming);
+    if (err != hipSuccess)
+      return fail(MOE_ERR_LAUNCH, "second stream on device %d: %s", dev, hipGetErrorString(err));
+    sd.fork = a;
+    sd.join = b;
+    sd.s = st;
+  }
+  *out = &sd;
+  return MOE_OK;
+}
+
+// One GEMM step over both tile lists.  launch(tall, stream) runs one list.
+// concurrent: the tall list on the second stream, forked from `stream` and
+// joined back to it with events (graph capture follows the fork), the main
+// list on `stream`; otherwise both on `stream`, tall list first.  With one
+// list only the main launch runs.
+template <class F>
+moe_status_t run_lists(const Plan& pl, hipStream_t stream, bool concurrent, F&& launch) {
+  if (!pl.tall) return launch(false, stream);
+  if (!concurrent) {
+    CHECK(launch(true, stream));
+    return launch(false, stream);
+  }
+  SideStream* sd = nullptr;
+  CHECK(side_stream_for_current_device(&sd));
+  std::lock_guard<std::mutex> lock(sd->mu);
+  hipError_t err = hipEventRecord(sd->fork, stream);
+  if (err == hipSuccess) err = hipStreamWaitEvent(sd->s, sd->fork, 0);
+  if (err != hipSuccess) return launch_status(err, "fork to the second stream");
+  const moe_status_t st_tall = launch(true, sd->s);
+  // join even after a failed launch, so a capturing stream is not left forked
+  err = hipEventRecord(sd->join, sd->s);
+  const moe_status_t st_main = launch(false, stream);
+  if (err == hipSuccess) err = hipStreamWaitEvent(stream, sd->join, 0);
+  if (err != hipSuccess) return launch_status(err, "join from the second stream");
+  return st_tall != MOE_OK ? st_tall : st_main;
+}
+
+// w2 over both lists one after the other for the MX schemes: concurrent it
+// measured slower there (MXFP4 DSv3-shaped prefill 0.79 -> 0.82 ms; in
+// order 0.80 ms), while w13 gains for every scheme
+bool w2_concurrent(const moe_problem_t* p) {
+  return p->act_quant != MOE_Q_MXFP8 && p->weight_quant == MOE_W_FP8_BLOCK128;
 }
 
 // The w2 call's workspace: needed (and checked) only when w2 splits.
@@ -642,7 +756,10 @@ moe_status_t moe_grouped_gemm_w13(const moe_problem_t* p, const void* a_q, const
   CHECK(check_ptr(w13_sf, "w13_sf", 4));
   CHECK(check_ptr(gate_up, "gate_up", 16));
   const Plan pl = make_plan(p);
-  return run_gemm(p, pl, true, a_q, a_sf, routing, w13, w13_sf, gate_up, (hipStream_t)stream);
+  return run_lists(pl, (hipStream_t)stream, true, [&](bool tall, hipStream_t st) {
+    return run_gemm(p, pl, true, a_q, a_sf, routing, w13, w13_sf, gate_up, st, false, nullptr,
+                    nullptr, nullptr, nullptr, tall);
+  });
 }
 
 moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q, const void* a_sf,
@@ -660,8 +777,10 @@ moe_status_t moe_grouped_gemm_w13_act(const moe_problem_t* p, const void* a_q, c
   CHECK(check_ptr(a2_q, "a2_q", 16));
   CHECK(check_sf(p, a2_sf, "a2_sf"));
   const Plan pl = make_plan(p);
-  return run_gemm(p, pl, true, a_q, a_sf, routing, w13, w13_sf, nullptr, (hipStream_t)stream,
-                  true, a2_q, a2_sf);
+  return run_lists(pl, (hipStream_t)stream, true, [&](bool tall, hipStream_t st) {
+    return run_gemm(p, pl, true, a_q, a_sf, routing, w13, w13_sf, nullptr, st, true, a2_q,
+                    a2_sf, nullptr, nullptr, tall);
+  });
 }
 
 moe_status_t moe_act_requant(const moe_problem_t* p, const void* gate_up,
@@ -698,8 +817,10 @@ moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const
   CHECK(check_ptr(down, "down", 16));
   const Plan pl = make_plan(p);
   CHECK(check_w2_ws(pl, ws, ws_bytes));
-  return run_gemm(p, pl, false, a2_q, a2_sf, routing, w2, w2_sf, down, (hipStream_t)stream,
-                  false, nullptr, nullptr, nullptr, ws);
+  return run_lists(pl, (hipStream_t)stream, w2_concurrent(p), [&](bool tall, hipStream_t st) {
+    return run_gemm(p, pl, false, a2_q, a2_sf, routing, w2, w2_sf, down, st, false, nullptr,
+                    nullptr, nullptr, ws, tall);
+  });
 }
 
 moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int32_t* slot_row,
@@ -788,12 +909,17 @@ moe_status_t moe_fused_mul_sum(const moe_problem_t* p, const void* down, const i
   return run_mul_sum(p, down, topk_idx, topk_w, out, (hipStream_t)stream);
 }
 
-moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
-                         const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
-                         const float* topk_weights, const uint8_t* is_padding,
-                         const moe_eplb_t* eplb, const void* w13, const void* w13_sf,
-                         const void* w2, const void* w2_sf, void* out, void* ws,
-                         size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+// side: the two-list GEMM steps may use the second stream (moe_forward);
+// otherwise their launches stay on the caller's stream (moe_forward_static)
+moe_status_t forward_impl(const moe_problem_t* p, const void* hidden,
+                          const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
+                          const float* topk_weights, const uint8_t* is_padding,
+                          const moe_eplb_t* eplb, const void* w13, const void* w13_sf,
+                          const void* w2, const void* w2_sf, void* out, void* ws,
+                          size_t ws_bytes, void* stream, bool side) {
   CHECK(validate_problem(p));
   if (p->num_tokens == 0) return ok();
   CHECK(check_stage_args(p, hidden, expert_num_tokens_in, topk_ids, topk_weights, eplb));
@@ -830,16 +956,36 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
     return ok();
   }
   if (gated(p)) {
-    CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, nullptr, s, true, w.a2_q,
-                   w.a2_sf));
+    CHECK(run_lists(pl, s, side, [&](bool tall, hipStream_t st) {
+      return run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, nullptr, st, true,
+                      w.a2_q, w.a2_sf, nullptr, nullptr, tall);
+    }));
   } else {
-    CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, w.gate_up, s));
+    CHECK(run_lists(pl, s, side, [&](bool tall, hipStream_t st) {
+      return run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, w.gate_up, st, false,
+                      nullptr, nullptr, nullptr, nullptr, tall);
+    }));
     CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s));
   }
-  CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s, false,
-                 nullptr, nullptr, nullptr, w.w2_split));
+  CHECK(run_lists(pl, s, side && w2_concurrent(p), [&](bool tall, hipStream_t st) {
+    return run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, st, false,
+                    nullptr, nullptr, nullptr, w.w2_split, tall);
+  }));
   CHECK(run_reduce(p, w.down, w.routing.slot_row, w.w, out, s));
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
+                         const int32_t* expert_num_tokens_in, const int32_t* topk_ids,
+                         const float* topk_weights, const uint8_t* is_padding,
+                         const moe_eplb_t* eplb, const void* w13, const void* w13_sf,
+                         const void* w2, const void* w2_sf, void* out, void* ws,
+                         size_t ws_bytes, void* stream) {
+  return forward_impl(p, hidden, expert_num_tokens_in, topk_ids, topk_weights, is_padding, eplb,
+                      w13, w13_sf, w2, w2_sf, out, ws, ws_bytes, stream, true);
 }
 
 moe_status_t moe_forward_static(const moe_problem_t* p, const void* hidden,
@@ -857,8 +1003,9 @@ moe_status_t moe_forward_static(const moe_problem_t* p, const void* hidden,
                 need, (size_t)MOE_STATIC_SCRATCH_BYTES);
   void* ws = nullptr;
   CHECK(static_scratch_for_current_device(&ws));
-  return moe_forward(p, hidden, expert_num_tokens_in, topk_ids, topk_weights, is_padding, eplb,
-                     w13, w13_sf, w2, w2_sf, out, ws, (size_t)MOE_STATIC_SCRATCH_BYTES, stream);
+  return forward_impl(p, hidden, expert_num_tokens_in, topk_ids, topk_weights, is_padding, eplb,
+                      w13, w13_sf, w2, w2_sf, out, ws, (size_t)MOE_STATIC_SCRATCH_BYTES, stream,
+                      false);
 }
 
 }  // extern "C"

@@ -116,8 +116,8 @@ constexpr int kChunkCap = 2048;
 
 __device__ __forceinline__ void route_scan_body(
     int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
-    int max_tokens, int tile_m, int max_tiles, int32_t* __restrict__ expert_num_tokens,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ tile_list) {
+    int max_tokens, const TileLists tl, int32_t* __restrict__ expert_num_tokens,
+    int32_t* __restrict__ expert_offsets) {
   __shared__ int buf[1024];
   __shared__ int wcnt[16][8];      // remainder chunks per wave and size class
   __shared__ int woff[16][8];      // their first index
@@ -145,7 +145,6 @@ __device__ __forceinline__ void route_scan_body(
   const int incl = block_inclusive_scan(e < E ? cnt : 0, buf);
   int rows = cnt;
   if (counts_in != nullptr && e < E) rows = min(max(counts_in[e], 0), max_tokens);
-  const int nt = e < E ? (rows + tile_m - 1) / tile_m : 0;
   if (e < E) {
     expert_offsets[e] = incl - cnt;
     expert_num_tokens[e] = counts_in != nullptr ? rows : cnt;
@@ -153,6 +152,10 @@ __device__ __forceinline__ void route_scan_body(
   }
   exp_rows[e] = rows;
   exp_base[e] = counts_in != nullptr ? e * max_tokens : incl - cnt;
+  // one list: nt m-tiles of tile_m rows for this thread's expert (0: not in
+  // this list); block-uniform arguments otherwise
+  auto schedule = [&](const int nt, const int tile_m, const int max_tiles,
+                      int32_t* __restrict__ tile_list) {
   const int incl_nt = block_inclusive_scan(nt, buf);
   exp_tile0[e] = incl_nt - nt;
   // the last thread's inclusive value is the total: broadcast it
@@ -280,14 +283,26 @@ __device__ __forceinline__ void route_scan_body(
     tile_list[3] = 0;
     group_off[nchunks] = total;
   }
+  };
+  // with a tall list, experts of more than tile_m rows go there, in tiles
+  // of 2 * tile_m rows; the rest (or every expert) to the main list
+  const bool tall = tl.tall != nullptr;                 // block-uniform
+  const bool in_tall = tall && e < E && rows > tl.tile_m;
+  schedule(e < E && !in_tall ? (rows + tl.tile_m - 1) / tl.tile_m : 0, tl.tile_m, tl.max_tiles,
+           tl.list);
+  if (tall) {
+    __syncthreads();                                    // the LDS tables are reused
+    const int th = 2 * tl.tile_m;
+    schedule(in_tall ? (rows + th - 1) / th : 0, th, tl.max_tiles_tall, tl.tall);
+  }
 }
 
 __global__ __launch_bounds__(1024) void route_scan_kernel(
     int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
-    int max_tokens, int tile_m, int max_tiles, int32_t* __restrict__ expert_num_tokens,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ tile_list) {
-  route_scan_body(hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles, expert_num_tokens,
-                  expert_offsets, tile_list);
+    int max_tokens, const TileLists tl, int32_t* __restrict__ expert_num_tokens,
+    int32_t* __restrict__ expert_offsets) {
+  route_scan_body(hist, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens,
+                  expert_offsets);
 }
 
 // The scan is one block of latency-bound work; the hidden states' group
@@ -305,13 +320,13 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
 template <int GROUP, bool UE8M0>
 __global__ __launch_bounds__(1024) void route_scan_quant_kernel(
     int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
-    int max_tokens, int tile_m, int max_tiles, int32_t* __restrict__ expert_num_tokens,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ tile_list,
+    int max_tokens, const TileLists tl, int32_t* __restrict__ expert_num_tokens,
+    int32_t* __restrict__ expert_offsets,
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
     int64_t num_groups, int G, int sf_row_len) {
   if (blockIdx.x == 0) {
-    route_scan_body(hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles,
-                    expert_num_tokens, expert_offsets, tile_list);
+    route_scan_body(hist, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens,
+                    expert_offsets);
     return;
   }
   constexpr int LANES = GROUP / 16;
@@ -442,9 +457,9 @@ hipError_t launch_align(const int64_t* idx, const int32_t* slot_row, const int32
 hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint8_t* is_padding,
                         int T, int k, int E, const EplbArgs& eplb, int64_t* idx_out,
                         float* w_out, int32_t* hist, const int32_t* counts_in, int max_tokens,
-                        int tile_m, int max_tiles, int32_t* expert_num_tokens,
+                        const TileLists& tl, int32_t* expert_num_tokens,
                         int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
-                        int32_t* tile_list, hipStream_t stream, const StageQuant* sq) {
+                        hipStream_t stream, const StageQuant* sq) {
   const int64_t total = (int64_t)T * k;
   const int nblocks = (int)((total + kRouteChunk - 1) / kRouteChunk);
   if (nblocks > 0) {
@@ -467,20 +482,19 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint
     uint8_t* xsf = (uint8_t*)sq->xsf;
     if (sq->group == 32)
       route_scan_quant_kernel<32, true><<<grid, 1024, 0, stream>>>(
-          hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles, expert_num_tokens,
-          expert_offsets, tile_list, x, xq, xsf, ng, G, G);
+          hist, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens, expert_offsets, x, xq,
+          xsf, ng, G, G);
     else if (sq->ue8m0)
       route_scan_quant_kernel<128, true><<<grid, 1024, 0, stream>>>(
-          hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles, expert_num_tokens,
-          expert_offsets, tile_list, x, xq, xsf, ng, G, 4 * ((G + 3) / 4));
+          hist, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens, expert_offsets, x, xq,
+          xsf, ng, G, 4 * ((G + 3) / 4));
     else
       route_scan_quant_kernel<128, false><<<grid, 1024, 0, stream>>>(
-          hist, nblocks, E, counts_in, max_tokens, tile_m, max_tiles, expert_num_tokens,
-          expert_offsets, tile_list, x, xq, xsf, ng, G, 4 * ((G + 3) / 4));
+          hist, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens, expert_offsets, x, xq,
+          xsf, ng, G, 4 * ((G + 3) / 4));
   } else {
-    route_scan_kernel<<<1, 1024, 0, stream>>>(hist, nblocks, E, counts_in, max_tokens, tile_m,
-                                              max_tiles, expert_num_tokens, expert_offsets,
-                                              tile_list);
+    route_scan_kernel<<<1, 1024, 0, stream>>>(hist, nblocks, E, counts_in, max_tokens, tl,
+                                              expert_num_tokens, expert_offsets);
   }
   if (nblocks > 0) {
     route_scatter_kernel<<<nblocks, kRouteThreads, E * sizeof(int32_t), stream>>>(

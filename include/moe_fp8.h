@@ -23,9 +23,15 @@
  *
  * Conventions for every call
  *  - Pointers named "device" are HIP device pointers; the caller allocates and
- *    owns every buffer; the library never allocates, frees or synchronizes.
- *    Work is enqueued on `stream` (a hipStream_t passed as void*, NULL = the
- *    null stream) and buffers must stay valid until it completes.
+ *    owns every buffer; the library never allocates device memory, frees or
+ *    synchronizes.  Work is enqueued on `stream` (a hipStream_t passed as
+ *    void*, NULL = the null stream) and buffers must stay valid until it
+ *    completes.  A GEMM step over two tile lists (see "Tile height") also
+ *    runs one launch on a second stream the library keeps per device
+ *    (created, with two events, at the first such step on the device),
+ *    forked from `stream` and joined back to it by events, so work that
+ *    follows on `stream` sees both launches done and a graph capture of
+ *    `stream` follows the fork.
  *  - Arrays are dense row-major.  Vector-accessed buffers (hidden states, fp8
  *    codes, bf16 intermediates, weights, output) must be 16-byte aligned,
  *    scale and index arrays 4-byte aligned (int64 arrays 8-byte aligned).
@@ -187,7 +193,11 @@ typedef struct {
  *                    m-tiles of one expert (more only for very large
  *                    batches), and the groups are ordered so that 8 equal
  *                    slices of the list hold similar work and weight bytes
- *                    (one slice per XCD) */
+ *                    (one slice per XCD).  When moe_sizes_t.tall_tile_m is
+ *                    not 0, a second list of the same form starts at int32
+ *                    index tall_list_offset: experts of more than tile_m
+ *                    rows are scheduled there in tiles of tall_tile_m rows
+ *                    (and are absent from the first list) */
 typedef struct {
   int32_t* expert_num_tokens;
   int32_t* expert_offsets;
@@ -207,20 +217,33 @@ typedef struct {
   int64_t blocks;          /* indexed: expert_ids capacity; else 0            */
   int32_t tile_m;          /* activation rows per GEMM tile (indexed: the
                               block size moe_forward uses)                    */
+  int32_t tall_tile_m;     /* rows per tile of the second (tall) tile list;
+                              0 when there is none                            */
+  int64_t max_tiles;       /* tile capacity of the first tile list            */
+  int64_t tall_list_offset; /* int32 index of the tall list in tile_list      */
+  int64_t max_tiles_tall;  /* its tile capacity                               */
 } moe_sizes_t;
 
 /* Tile height.  tile_m follows the expected rows per expert, T * top_k / E:
  * 16, 32 or 64 rows up to 12, 24 or 48 rows per expert, 128 up to 128, and
  * 256 above (at most 128 for bf16 activations); when w2 splits its reduction
- * (N >= 8192), 192 rows between 96 and 192 rows per expert.  The tile height
- * never changes the results' bits.  MOE_KSPLIT = 1 | 2 | 4 overrides the w2
+ * (N >= 8192), 192 rows between 96 and 192 rows per expert.  At 128-row
+ * tiles (fp8 or MXFP8 activations, an unsplit w2, not the indexed layout)
+ * the experts of more than 128 rows go to a second tile list of 256-row
+ * tiles (moe_sizes_t.tall_tile_m); every GEMM call then launches one kernel
+ * per list: the tall list's on the library's second stream beside the main
+ * list's on `stream` (w13 always; w2 for the block-scaled fp8 weights), or
+ * both on `stream`, tall list first (MX w2, moe_forward_static).  The tile
+ * height never changes the results' bits.  MOE_KSPLIT = 1 | 2 | 4 overrides the w2
  * split for tuning runs (it does change them: every call of one layer must
  * see the same value).  Two environment variables
  * override the choice for tuning runs.  MOE_TILE_M = 16 | 32 | 64 | 128 |
  * 192 | 256 (192 and 256 not for bf16; other values are ignored) is read by
  * every call; all calls of one layer must see the same value, since the
  * stage builds the tile schedule for the height the GEMM calls then read it
- * with.  MOE_GEMM_WIDE = 0 | 1 picks 128 or 256 output columns for the
+ * with; a forced height keeps one tile list.  MOE_TALL = 0 | 1 turns the
+ * second list off or on (where it can run), read by every call like
+ * MOE_TILE_M.  MOE_GEMM_WIDE = 0 | 1 picks 128 or 256 output columns for the
  * 128-row tiles of the unfused GEMMs; it is read once per scale scheme, at
  * its first GEMM call, and does not change the schedule.  MOE_SN = n sets how
  * many n-tiles the GEMMs walk together inside an expert's m-tiles (default 1
@@ -407,7 +430,9 @@ moe_status_t moe_forward(const moe_problem_t* p, const void* hidden,
  * MOE_STATIC_SCRATCH_BYTES (64 MiB) inside the library, one per GPU, held by
  * every GPU the library runs on until the process ends; a DeepSeek-V3-shaped
  * decode batch (64 tokens, 256 experts, top-8, K 7168, N 2048) needs about
- * 9 MB of it.  The call allocates nothing.  A problem whose
+ * 9 MB of it.  The call allocates nothing and creates no stream: all its
+ * launches go to `stream` (a two-list GEMM step runs its lists one after the
+ * other).  A problem whose
  * moe_workspace_size exceeds the array is rejected with MOE_ERR_WORKSPACE
  * before anything is enqueued.  The array's device address is looked up on
  * the first call on each device (the current device; stream and buffers

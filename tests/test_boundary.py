@@ -223,6 +223,44 @@ def test_empty_batch_is_a_noop(lib):
     assert lib.moe_last_error().decode() == ""
 
 
+def test_tall_list_sizes(lib, monkeypatch):
+    """The second tile list (experts above 128 rows in 256-row tiles): where
+    it applies, where it does not, and its place in the tile-list buffer."""
+    monkeypatch.delenv("MOE_TILE_M", raising=False)
+    monkeypatch.delenv("MOE_TALL", raising=False)
+    for name, cfg in {**moe_synth.CONFIGS, **moe_synth.MX_CONFIGS,
+                      **moe_synth.INDEXED_CONFIGS}.items():
+        p = moe.Problem.from_config(cfg)
+        s = moe.sizes(p)
+        E, slots = cfg.E, cfg.T * cfg.top_k
+        tall = (s["tile_m"] == 128 and cfg.layout != "indexed" and cfg.act_quant != "bf16"
+                and moe.w2_workspace_size(p) == 0)
+        assert (s["tall_tile_m"] == 256) == tall and s["tall_tile_m"] in (0, 256), name
+        main = 4 + 9 * s["max_tiles"] + E + 1
+        if not tall:
+            assert s["tile_list"] == main and s["tall_list_offset"] == 0, name
+            continue
+        off = s["tall_list_offset"]
+        assert off % 4 == 0 and main <= off < main + 4, name
+        cap = (E * -(-cfg.max_tokens // 256) if cfg.layout == "batched"
+               else -(-slots // 256) + E)
+        assert s["max_tiles_tall"] == cap, name
+        assert s["tile_list"] == off + 4 + 9 * cap + E + 1, name
+    # the DeepSeek-V3-shaped prefill batch has one; MOE_TALL=0 or a forced
+    # tile height turns it off, MOE_TALL=1 on again
+    p = moe.Problem.from_config(moe_synth.ALL_CONFIGS["dsv3_prefill"])
+    assert moe.sizes(p)["tall_tile_m"] == 256
+    monkeypatch.setenv("MOE_TALL", "0")
+    assert moe.sizes(p)["tall_tile_m"] == 0
+    monkeypatch.delenv("MOE_TALL")
+    monkeypatch.setenv("MOE_TILE_M", "128")
+    assert moe.sizes(p)["tall_tile_m"] == 0
+    monkeypatch.setenv("MOE_TALL", "1")
+    assert moe.sizes(p)["tall_tile_m"] == 256
+    monkeypatch.setenv("MOE_TILE_M", "64")
+    assert moe.sizes(p)["tall_tile_m"] == 0
+
+
 def test_indexed_sizes(lib):
     # the indexed layout: sorted_ids has the padded capacity, a2 and down T*k rows
     for name, cfg in moe_synth.INDEXED_CONFIGS.items():

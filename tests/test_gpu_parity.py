@@ -101,9 +101,24 @@ MID.update({
     "split_batched": moe_synth.custom(name="split_batched", T=200, E=4, top_k=2, K=512,
                                       N=8192, seed=50, layout="batched", max_tokens=160),
 })
+# 128-row tiles (about 96 rows per expert) with Zipf skew: the heaviest
+# experts exceed 128 rows and go to the second (256-row) tile list
+TALL = {
+    "tall_ue8m0": moe_synth.custom(name="tall_ue8m0", T=256, E=8, top_k=3, K=1024, N=1024,
+                                   seed=52, routing="zipf", zipf_s=1.1, pad_frac=0.05),
+    "tall_fp32": moe_synth.custom(name="tall_fp32", T=256, E=8, top_k=3, K=1024, N=1024,
+                                  seed=53, routing="zipf", zipf_s=1.1, act_quant="fp32"),
+    "tall_mxfp4": moe_synth.custom(name="tall_mxfp4", T=256, E=8, top_k=3, K=1024, N=1024,
+                                   seed=54, routing="zipf", zipf_s=1.1, act_quant="mxfp8",
+                                   weight_quant="mxfp4"),
+    "tall_batched": moe_synth.custom(name="tall_batched", T=256, E=8, top_k=3, K=1024,
+                                     N=1024, seed=55, layout="batched", max_tokens=256,
+                                     routing="zipf", zipf_s=1.1),
+}
+MID.update(TALL)
 MID_TILES = [16, 128, 256]
 MID_CASES = [(n, t) for n in MID for t in MID_TILES
-             if not (MID[n].act_quant == "bf16" and t > 128)]
+             if not (MID[n].act_quant == "bf16" and t > 128) and n not in TALL]
 CASES = {**SMALL, **MID}
 
 
@@ -162,17 +177,13 @@ def stage_on_gpu(cfg, dev):
     return p, bufs
 
 
-def _max_tiles(n_entries, E):
-    # n_entries = 4 + 8 * max_tiles + E + max_tiles + 1
-    return (n_entries - 5 - E) // 9
-
-
-def host_tile_list(counts, tile_m, n_entries, bases):
-    """Every (expert, m0) tile in plain expert order, one group per expert
-    (test plumbing: the GEMM must not depend on the order the routing step
-    emits).  bases: each expert's first row in the GEMM's row space."""
+def host_tile_list(counts, tile_m, n_entries, bases, max_tiles):
+    """Every (expert, m0) tile in plain expert order, one group per expert,
+    all in the main list (a tall list, if the plan has one, stays empty:
+    count 0) -- test plumbing: the GEMM must not depend on the order or the
+    split the routing step emits.  bases: each expert's first row in the
+    GEMM's row space."""
     E = len(counts)
-    max_tiles = _max_tiles(n_entries, E)
     tl = np.zeros(n_entries, np.int32)
     info = tl[4:4 + 8 * max_tiles].reshape(max_tiles, 8)
     groups = tl[4 + 8 * max_tiles:]
@@ -229,7 +240,7 @@ def oracle_routing(p, cfg, ref):
         "tile_list": to_dev(host_tile_list(
             ref["counts"], s["tile_m"], s["tile_list"],
             [e * cfg.max_tokens for e in range(cfg.E)] if cfg.layout == "batched"
-            else ref["offsets"][:-1])),
+            else ref["offsets"][:-1], s["max_tiles"])),
     }
 
 
@@ -354,17 +365,13 @@ def test_stage_and_route_bit_exact(gpu, name):
     check_schedule(bufs["tile_list"], ref["counts"], moe.sizes(p), cfg.E, bases)
 
 
-def check_schedule(tile_list, counts, s, E, bases):
-    """The tile schedule: every expert's tiles exactly once, in the
+def _check_one_list(tl, tiles, bm, max_tiles, counts, bases):
+    """One tile list: every listed expert's tiles exactly once, in the
     documented XCD-balanced order, groups of consecutive m-tiles of one
     expert, and each tile's information (group, expert rows, first row)."""
-    tl = to_np(tile_list)
     n, G = int(tl[0]), int(tl[1])
     assert tl[2] == 0 and tl[3] == 0
-    bm = s["tile_m"]
-    max_tiles = _max_tiles(s["tile_list"], E)
     info = tl[4:4 + 8 * n].reshape(n, 8)
-    tiles = [-(-int(c) // bm) for c in counts]
     seq, sizes = expected_schedule(tiles)
     tile0 = np.concatenate([[0], np.cumsum(tiles)[:-1]])
     assert [(int(e), int(m0) // bm) for e, m0 in info[:, :2]] == seq
@@ -382,6 +389,23 @@ def check_schedule(tile_list, counts, s, E, bases):
         # the expert's first m-tile in expert order (the indexed layout's
         # first block of the expert at this block size)
         assert np.all(seg[:, 6] == tile0[e]) and np.all(seg[:, 7] == 0)
+
+
+def check_schedule(tile_list, counts, s, E, bases):
+    """The tile schedule.  With a tall list (s["tall_tile_m"] != 0) the
+    experts of more than tile_m rows are scheduled there in tiles of
+    tall_tile_m rows and the others in the main list; otherwise every expert
+    is in the main list."""
+    tl = to_np(tile_list)
+    bm, tall = s["tile_m"], s["tall_tile_m"]
+    heavy = [tall != 0 and int(c) > bm for c in counts]
+    _check_one_list(tl, [0 if h else -(-int(c) // bm) for c, h in zip(counts, heavy)], bm,
+                    s["max_tiles"], counts, bases)
+    if tall:
+        off = s["tall_list_offset"]
+        assert off % 4 == 0 and off >= 4 + 9 * s["max_tiles"] + E
+        _check_one_list(tl[off:], [-(-int(c) // tall) if h else 0 for c, h in zip(counts, heavy)],
+                        tall, s["max_tiles_tall"], counts, bases)
 
 
 def test_stage_bf16_copy(gpu):
@@ -745,6 +769,43 @@ def test_w2_split_k(gpu, name, ksplit, monkeypatch):
         outs.append(to_np(down)[vr])
     assert np.array_equal(outs[0], outs[1]), f"{name} split {ksplit}: not deterministic"
     check_output(to_np(run_forward(cfg, dev)), ref["out"], f"{name} split {ksplit} output")
+
+
+# ---------------------------------------------------------------------------
+# the second (tall) tile list at the default tile height
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(TALL))
+def test_tall_list(gpu, name, monkeypatch):
+    """Experts above 128 rows in 256-row tiles of a second list, whose GEMM
+    launches run on a second stream alongside the main list's (moe_forward,
+    the GEMM entry points) or after them (moe_forward_static).  The routing
+    writes both lists bit-exact; the chain and moe_forward match the oracle;
+    the bits equal those with one list (MOE_TALL=0) and moe_forward_static's."""
+    monkeypatch.delenv("MOE_TILE_M", raising=False)
+    monkeypatch.delenv("MOE_TALL", raising=False)
+    cfg, h, dev, ref = case(name)
+    s = moe.sizes(problem(cfg))
+    assert s["tile_m"] == 128 and s["tall_tile_m"] == 256
+    counts = ref["counts"] if cfg.layout != "batched" else np.minimum(ref["counts"],
+                                                                      cfg.max_tokens)
+    assert (counts > 128).any() and ((counts > 0) & (counts <= 128)).any()
+    test_stage_and_route_bit_exact(gpu, name)
+    _fused_equals_chain(name, 128)
+    _forward_end_to_end(name)
+    out = run_forward(cfg, dev)
+    monkeypatch.setenv("MOE_TALL", "0")
+    assert moe.sizes(problem(cfg))["tall_tile_m"] == 0
+    one = run_forward(cfg, dev)
+    monkeypatch.delenv("MOE_TALL")
+    assert torch.equal(out.view(torch.int16), one.view(torch.int16)), f"{name}: one list differs"
+    p = problem(cfg)
+    st = torch.empty_like(out)
+    moe.forward_static(p, dev["hidden"], dev["topk_ids"], dev["topk_weights"], dev["w13"],
+                       dev["w13_sf"], dev["w2"], dev["w2_sf"], st, is_padding=dev["is_padding"],
+                       expert_num_tokens=dev["expert_num_tokens"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), st.view(torch.int16)), f"{name}: static differs"
 
 
 # ---------------------------------------------------------------------------
