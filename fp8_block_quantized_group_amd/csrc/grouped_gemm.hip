@@ -1135,11 +1135,14 @@ hipError_t launch_grouped_gemm_sc(const GemmArgs& p, int tile_m, int max_tiles, 
         // 256-column tiles (8 waves) halve the activation re-reads; 128-column
         // tiles run two blocks per CU, which measured faster for the MX
         // schemes (whose MFMA consumes its scales directly: less per-k-step
-        // work to hide the block prologue behind).  MOE_GEMM_WIDE=0 / 1 forces
-        // one or the other.
+        // work to hide the block prologue behind) -- unless the experts above
+        // 128 rows run in their own 256-row tile list beside this one: then
+        // 256 columns won for MX too (DSv3-shaped prefill w2, both lists
+        // concurrent: MXFP8 1.14 -> 1.00 ms, MXFP4 0.81 -> 0.76 ms).
+        // MOE_GEMM_WIDE=0 / 1 forces one or the other.
         static const char* env = getenv("MOE_GEMM_WIDE");
         constexpr bool mx = SC == kQuantMxfp8 || SC == kSchemeMxfp8W4;
-        const bool wide = env != nullptr ? env[0] != '0' : !mx;
+        const bool wide = env != nullptr ? env[0] != '0' : (!mx || p.wide == 1);
         if (wide && p.Nout % 256 == 0)
           return launch_shape<Shape<128, 256, 8, 3>, SC, false>(p, max_tiles, stream);
         return launch_shape<Shape<128, 128, 4, 2>, SC, false>(p, max_tiles, stream);

@@ -87,6 +87,9 @@ struct GemmArgs {
   // item order inside a group of m-tiles: super-columns of sn n-tiles, each
   // walked m-tile-major (sn = 1: n-tile-major); set by the launcher
   int sn;
+  // 1: 256 output columns for the unfused GEMMs' 128-row tiles whatever the
+  // scheme (set when the experts above 128 rows have their own tile list)
+  int wide;
 };
 
 // zero n int32 (a fill kernel: safe under graph capture)

@@ -491,6 +491,7 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
   g.act_sf = (uint8_t*)act_sf;
   g.act_sf_row = (int)pl.s.a2_sf_row;
   g.num_experts = p->num_experts;
+  g.wide = pl.tall ? 1 : 0;
   int tile_m = pl.s.tile_m, max_tiles = (int)pl.max_tiles;
   if (ix != nullptr) {
     g.sorted_ids = ix->sorted_ids;
@@ -661,12 +662,6 @@ moe_status_t run_lists(const Plan& pl, hipStream_t stream, bool concurrent, F&& 
   return st_tall != MOE_OK ? st_tall : st_main;
 }
 
-// w2 over both lists one after the other for the MX schemes: concurrent it
-// measured slower there (MXFP4 DSv3-shaped prefill 0.79 -> 0.82 ms; in
-// order 0.80 ms), while w13 gains for every scheme
-bool w2_concurrent(const moe_problem_t* p) {
-  return p->act_quant != MOE_Q_MXFP8 && p->weight_quant == MOE_W_FP8_BLOCK128;
-}
 
 // The w2 call's workspace: needed (and checked) only when w2 splits.
 moe_status_t check_w2_ws(const Plan& pl, const void* ws, size_t ws_bytes) {
@@ -817,7 +812,7 @@ moe_status_t moe_grouped_gemm_w2(const moe_problem_t* p, const void* a2_q, const
   CHECK(check_ptr(down, "down", 16));
   const Plan pl = make_plan(p);
   CHECK(check_w2_ws(pl, ws, ws_bytes));
-  return run_lists(pl, (hipStream_t)stream, w2_concurrent(p), [&](bool tall, hipStream_t st) {
+  return run_lists(pl, (hipStream_t)stream, true, [&](bool tall, hipStream_t st) {
     return run_gemm(p, pl, false, a2_q, a2_sf, routing, w2, w2_sf, down, st, false, nullptr,
                     nullptr, nullptr, ws, tall);
   });
@@ -967,7 +962,7 @@ moe_status_t forward_impl(const moe_problem_t* p, const void* hidden,
     }));
     CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s));
   }
-  CHECK(run_lists(pl, s, side && w2_concurrent(p), [&](bool tall, hipStream_t st) {
+  CHECK(run_lists(pl, s, side, [&](bool tall, hipStream_t st) {
     return run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, st, false,
                     nullptr, nullptr, nullptr, w.w2_split, tall);
   }));

@@ -232,9 +232,8 @@ typedef struct {
  * the experts of more than 128 rows go to a second tile list of 256-row
  * tiles (moe_sizes_t.tall_tile_m); every GEMM call then launches one kernel
  * per list: the tall list's on the library's second stream beside the main
- * list's on `stream` (w13 always; w2 for the block-scaled fp8 weights), or
- * both on `stream`, tall list first (MX w2, moe_forward_static).  The tile
- * height never changes the results' bits.  MOE_KSPLIT = 1 | 2 | 4 overrides the w2
+ * list's on `stream`, or both on `stream`, tall list first
+ * (moe_forward_static).  The tile height never changes the results' bits.  MOE_KSPLIT = 1 | 2 | 4 overrides the w2
  * split for tuning runs (it does change them: every call of one layer must
  * see the same value).  Two environment variables
  * override the choice for tuning runs.  MOE_TILE_M = 16 | 32 | 64 | 128 |
@@ -244,8 +243,9 @@ typedef struct {
  * with; a forced height keeps one tile list.  MOE_TALL = 0 | 1 turns the
  * second list off or on (where it can run), read by every call like
  * MOE_TILE_M.  MOE_GEMM_WIDE = 0 | 1 picks 128 or 256 output columns for the
- * 128-row tiles of the unfused GEMMs; it is read once per scale scheme, at
- * its first GEMM call, and does not change the schedule.  MOE_SN = n sets how
+ * 128-row tiles of the unfused GEMMs (default 256; 128 for the MX schemes
+ * when there is one tile list); it is read once per scale scheme, at its
+ * first GEMM call, and does not change the schedule.  MOE_SN = n sets how
  * many n-tiles the GEMMs walk together inside an expert's m-tiles (default 1
  * for tiles up to 128 rows, 2 above; read once per tile shape); it changes
  * only the order of the blocks, never a result's bits. */
