@@ -16,6 +16,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <functional>
 #include <mutex>
 #include <string>
 
@@ -662,6 +663,33 @@ moe_status_t run_lists(const Plan& pl, hipStream_t stream, bool concurrent, F&& 
   return st_tall != MOE_OK ? st_tall : st_main;
 }
 
+// Both GEMM steps over both tile lists.  A list's w2 reads only the a2 rows
+// of its own experts, which its own w13 launch wrote, so each stream runs
+// its list's w13 and then its w2, with one join after both: neither stream
+// waits for the other between the steps.
+template <class F>
+moe_status_t run_lists_two_steps(const Plan& pl, hipStream_t stream, bool concurrent,
+                                 F&& launch_w13, F&& launch_w2) {
+  if (!pl.tall || !concurrent) {
+    CHECK(run_lists(pl, stream, concurrent, launch_w13));
+    return run_lists(pl, stream, concurrent, launch_w2);
+  }
+  SideStream* sd = nullptr;
+  CHECK(side_stream_for_current_device(&sd));
+  std::lock_guard<std::mutex> lock(sd->mu);
+  hipError_t err = hipEventRecord(sd->fork, stream);
+  if (err == hipSuccess) err = hipStreamWaitEvent(sd->s, sd->fork, 0);
+  if (err != hipSuccess) return launch_status(err, "fork to the second stream");
+  moe_status_t st_tall = launch_w13(true, sd->s);
+  if (st_tall == MOE_OK) st_tall = launch_w2(true, sd->s);
+  err = hipEventRecord(sd->join, sd->s);
+  moe_status_t st_main = launch_w13(false, stream);
+  if (st_main == MOE_OK) st_main = launch_w2(false, stream);
+  if (err == hipSuccess) err = hipStreamWaitEvent(stream, sd->join, 0);
+  if (err != hipSuccess) return launch_status(err, "join from the second stream");
+  return st_tall != MOE_OK ? st_tall : st_main;
+}
+
 
 // The w2 call's workspace: needed (and checked) only when w2 splits.
 moe_status_t check_w2_ws(const Plan& pl, const void* ws, size_t ws_bytes) {
@@ -951,10 +979,18 @@ moe_status_t forward_impl(const moe_problem_t* p, const void* hidden,
     return ok();
   }
   if (gated(p)) {
-    CHECK(run_lists(pl, s, side, [&](bool tall, hipStream_t st) {
+    // fused w13 + activation, then w2, per tile list
+    std::function<moe_status_t(bool, hipStream_t)> w13_step = [&](bool tall, hipStream_t st) {
       return run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, nullptr, st, true,
                       w.a2_q, w.a2_sf, nullptr, nullptr, tall);
-    }));
+    };
+    std::function<moe_status_t(bool, hipStream_t)> w2_step = [&](bool tall, hipStream_t st) {
+      return run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, st, false,
+                      nullptr, nullptr, nullptr, w.w2_split, tall);
+    };
+    CHECK(run_lists_two_steps(pl, s, side, w13_step, w2_step));
+    CHECK(run_reduce(p, w.down, w.routing.slot_row, w.w, out, s));
+    return ok();
   } else {
     CHECK(run_lists(pl, s, side, [&](bool tall, hipStream_t st) {
       return run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, w.gate_up, st, false,
