@@ -122,7 +122,10 @@ struct StageQuant {
 // The GEMM tile schedules the routing scan writes: the main list (tiles of
 // tile_m rows, capacity max_tiles) and, when tall is set, a second list of
 // 2 * tile_m-row tiles that takes every expert of more than tile_m rows
-// (those are then absent from the main list).
+// (those are then absent from the main list).  hist: the per-block expert
+// histograms; hist_base: where the scan writes the per-block bases the
+// scatter reads (hist itself, or a separate array of the same size when
+// there is a tall list: a second block then builds it from hist's counts).
 struct TileLists {
   int tile_m;
   int max_tiles;
@@ -133,8 +136,8 @@ struct TileLists {
 
 hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint8_t* is_padding,
                         int T, int k, int E, const EplbArgs& eplb, int64_t* idx_out,
-                        float* w_out, int32_t* hist, const int32_t* counts_in, int max_tokens,
-                        const TileLists& tl, int32_t* expert_num_tokens,
+                        float* w_out, int32_t* hist, int32_t* hist_base,
+                        const int32_t* counts_in, int max_tokens, const TileLists& tl, int32_t* expert_num_tokens,
                         int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
                         hipStream_t stream, const StageQuant* sq = nullptr);
 

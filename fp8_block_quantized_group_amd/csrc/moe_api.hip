@@ -228,6 +228,7 @@ struct Plan {
   size_t x_q_bytes, x_sf_bytes, a2_q_bytes, a2_sf_bytes, down_bytes;
   size_t gate_up_bytes;   // forward workspace: only for _no_mul activations
   size_t stage_ws_bytes;
+  size_t hist_base_off;                     // int32 offset of the per-block bases (0: in place)
   int w2_split;                             // w2 split-K factor
   size_t w2_part_bytes, w2_counters;        // its fp32 partials, its tickets
   int64_t w2_part_rows;                     // rows of one split's partials
@@ -268,6 +269,7 @@ Plan make_plan(const moe_problem_t* p) {
   pl.s.a2_sf_row = bf ? 0 : mx ? N / 32 : ue ? 4 * ((GN + 3) / 4) : GN;
   pl.route_blocks = (T * k + moe::kRouteChunk - 1) / moe::kRouteChunk;
   pl.stage_ws_bytes = round_up((size_t)std::max<int64_t>(pl.route_blocks, 1) * E * 4);
+  pl.hist_base_off = 0;
   const size_t elem = p->act_quant == MOE_Q_BF16 ? 2 : 1;
   pl.x_q_bytes = (size_t)pl.s.stage_rows * K * elem;
   const size_t sfb = p->act_quant == MOE_Q_FP8_F32 ? 4 : 1;
@@ -295,6 +297,10 @@ Plan make_plan(const moe_problem_t* p) {
   }
   pl.tall = use_tall(p, pl.s.tile_m, pl.w2_split);
   if (pl.tall) {
+    // the per-block bases go beside the histograms, which the second scan
+    // block (the tall list's) reads meanwhile
+    pl.hist_base_off = pl.stage_ws_bytes / 4;
+    pl.stage_ws_bytes *= 2;
     // the tall list after the main one, 16-byte aligned: tiles of twice the
     // height for experts above tile_m rows (at most one partial tile each)
     const int64_t th = 2 * bm;
@@ -441,7 +447,8 @@ moe_status_t run_stage(const moe_problem_t* p, const Plan& pl, const void* hidde
                           pl.tall ? r->tile_list + pl.s.tall_list_offset : nullptr};
   const hipError_t err = moe::launch_route(
       topk_ids, topk_weights, is_padding, p->num_tokens, p->top_k, p->num_experts,
-      eplb_args(eplb), idx_out, w_out, hist, cin, p->max_tokens_per_expert, tl,
+      eplb_args(eplb), idx_out, w_out, hist, hist + pl.hist_base_off, cin,
+      p->max_tokens_per_expert, tl,
       r->expert_num_tokens, r->expert_offsets, r->row_src, r->slot_row, stream,
       fused ? &sq : nullptr);
   return launch_status(err, fused ? "route + stage_quant" : "route");

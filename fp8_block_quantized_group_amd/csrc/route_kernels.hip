@@ -114,10 +114,14 @@ __device__ int block_inclusive_scan(int v, int* buf) {
 // of the weights while others did most of the arithmetic.
 constexpr int kChunkCap = 2048;
 
+// role 0: per-block bases (into hist_base, which may be hist itself),
+// offsets, counts and the main tile list; role 1: the tall list alone (run
+// by a second block of the same launch, reading hist's counts, so hist_base
+// must then be a separate array).
 __device__ __forceinline__ void route_scan_body(
-    int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
-    int max_tokens, const TileLists tl, int32_t* __restrict__ expert_num_tokens,
-    int32_t* __restrict__ expert_offsets) {
+    int role, int32_t* __restrict__ hist, int32_t* __restrict__ hist_base, int nblocks, int E,
+    const int32_t* __restrict__ counts_in, int max_tokens, const TileLists tl,
+    int32_t* __restrict__ expert_num_tokens, int32_t* __restrict__ expert_offsets) {
   __shared__ int buf[1024];
   __shared__ int wcnt[16][8];      // remainder chunks per wave and size class
   __shared__ int woff[16][8];      // their first index
@@ -137,7 +141,7 @@ __device__ __forceinline__ void route_scan_body(
       for (int j = 0; j < 16; ++j) c[j] = b0 + j < nblocks ? hist[(int64_t)(b0 + j) * E + e] : 0;
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
-        if (b0 + j < nblocks) hist[(int64_t)(b0 + j) * E + e] = cnt;
+        if (role == 0 && b0 + j < nblocks) hist_base[(int64_t)(b0 + j) * E + e] = cnt;
         cnt += c[j];
       }
     }
@@ -145,7 +149,7 @@ __device__ __forceinline__ void route_scan_body(
   const int incl = block_inclusive_scan(e < E ? cnt : 0, buf);
   int rows = cnt;
   if (counts_in != nullptr && e < E) rows = min(max(counts_in[e], 0), max_tokens);
-  if (e < E) {
+  if (role == 0 && e < E) {
     expert_offsets[e] = incl - cnt;
     expert_num_tokens[e] = counts_in != nullptr ? rows : cnt;
     if (e == E - 1) expert_offsets[E] = incl;
@@ -284,25 +288,25 @@ __device__ __forceinline__ void route_scan_body(
     group_off[nchunks] = total;
   }
   };
-  // with a tall list, experts of more than tile_m rows go there, in tiles
-  // of 2 * tile_m rows; the rest (or every expert) to the main list
-  const bool tall = tl.tall != nullptr;                 // block-uniform
-  const bool in_tall = tall && e < E && rows > tl.tile_m;
-  schedule(e < E && !in_tall ? (rows + tl.tile_m - 1) / tl.tile_m : 0, tl.tile_m, tl.max_tiles,
-           tl.list);
-  if (tall) {
-    __syncthreads();                                    // the LDS tables are reused
+  // with a tall list, experts of more than tile_m rows go there (role 1),
+  // in tiles of 2 * tile_m rows; the rest (or every expert) to the main list
+  const bool in_tall = tl.tall != nullptr && e < E && rows > tl.tile_m;
+  if (role == 0) {
+    schedule(e < E && !in_tall ? (rows + tl.tile_m - 1) / tl.tile_m : 0, tl.tile_m,
+             tl.max_tiles, tl.list);
+  } else {
     const int th = 2 * tl.tile_m;
     schedule(in_tall ? (rows + th - 1) / th : 0, th, tl.max_tiles_tall, tl.tall);
   }
 }
 
+// one block per tile list (block 1: the tall list)
 __global__ __launch_bounds__(1024) void route_scan_kernel(
-    int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
-    int max_tokens, const TileLists tl, int32_t* __restrict__ expert_num_tokens,
-    int32_t* __restrict__ expert_offsets) {
-  route_scan_body(hist, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens,
-                  expert_offsets);
+    int32_t* __restrict__ hist, int32_t* __restrict__ hist_base, int nblocks, int E,
+    const int32_t* __restrict__ counts_in, int max_tokens, const TileLists tl,
+    int32_t* __restrict__ expert_num_tokens, int32_t* __restrict__ expert_offsets) {
+  route_scan_body((int)blockIdx.x, hist, hist_base, nblocks, E, counts_in, max_tokens, tl,
+                  expert_num_tokens, expert_offsets);
 }
 
 // The scan is one block of latency-bound work; the hidden states' group
@@ -319,21 +323,23 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
 // slower (22.2 / 23.4 us; Qwen3-shaped 45.1 / 54.0 us against 41.6 us).
 template <int GROUP, bool UE8M0>
 __global__ __launch_bounds__(1024) void route_scan_quant_kernel(
-    int32_t* __restrict__ hist, int nblocks, int E, const int32_t* __restrict__ counts_in,
-    int max_tokens, const TileLists tl, int32_t* __restrict__ expert_num_tokens,
-    int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ hist, int32_t* __restrict__ hist_base, int nblocks, int E,
+    const int32_t* __restrict__ counts_in, int max_tokens, const TileLists tl,
+    int32_t* __restrict__ expert_num_tokens, int32_t* __restrict__ expert_offsets,
     const uint16_t* __restrict__ x, uint8_t* __restrict__ xq, uint8_t* __restrict__ xsf,
     int64_t num_groups, int G, int sf_row_len) {
-  if (blockIdx.x == 0) {
-    route_scan_body(hist, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens,
-                    expert_offsets);
+  // blocks 0 (and 1 with a tall list) build the tile lists, the rest quantize
+  const int nscan = tl.tall != nullptr ? 2 : 1;
+  if ((int)blockIdx.x < nscan) {
+    route_scan_body((int)blockIdx.x, hist, hist_base, nblocks, E, counts_in, max_tokens, tl,
+                    expert_num_tokens, expert_offsets);
     return;
   }
   constexpr int LANES = GROUP / 16;
   constexpr int GPB = 1024 / LANES;                 // groups of one pass
   const int lane = threadIdx.x % LANES;
-  const int64_t stride = (int64_t)(gridDim.x - 1) * GPB;
-  for (int64_t gid = (int64_t)(blockIdx.x - 1) * GPB + threadIdx.x / LANES; gid < num_groups;
+  const int64_t stride = (int64_t)(gridDim.x - nscan) * GPB;
+  for (int64_t gid = (int64_t)(blockIdx.x - nscan) * GPB + threadIdx.x / LANES; gid < num_groups;
        gid += stride) {
     if (!row_live(gid / G, counts_in, max_tokens)) continue;
     quantize_group_chunk<GROUP, UE8M0>(load_group_chunk<GROUP>(x, gid, lane), xq, xsf, gid,
@@ -456,7 +462,8 @@ hipError_t launch_align(const int64_t* idx, const int32_t* slot_row, const int32
 
 hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint8_t* is_padding,
                         int T, int k, int E, const EplbArgs& eplb, int64_t* idx_out,
-                        float* w_out, int32_t* hist, const int32_t* counts_in, int max_tokens,
+                        float* w_out, int32_t* hist, int32_t* hist_base,
+                        const int32_t* counts_in, int max_tokens,
                         const TileLists& tl, int32_t* expert_num_tokens,
                         int32_t* expert_offsets, int32_t* row_src, int32_t* slot_row,
                         hipStream_t stream, const StageQuant* sq) {
@@ -474,31 +481,33 @@ hipError_t launch_route(const int32_t* topk_ids, const float* topk_w, const uint
     // residency limit: the scan's LDS)
     const int64_t per_pass = 1024 / (sq->group / 16);
     const int64_t passes = (ng + per_pass - 1) / per_pass;
-    const int64_t resident = 2 * (int64_t)device_cus() - 1;
+    const int nscan = tl.tall != nullptr ? 2 : 1;
+    const int64_t resident = 2 * (int64_t)device_cus() - nscan;
     const int64_t rounds = (passes + resident - 1) / resident;
-    const unsigned grid = (unsigned)(1 + (passes + rounds - 1) / rounds);
+    const unsigned grid = (unsigned)(nscan + (passes + rounds - 1) / rounds);
     const uint16_t* x = (const uint16_t*)sq->x;
     uint8_t* xq = (uint8_t*)sq->xq;
     uint8_t* xsf = (uint8_t*)sq->xsf;
     if (sq->group == 32)
       route_scan_quant_kernel<32, true><<<grid, 1024, 0, stream>>>(
-          hist, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens, expert_offsets, x, xq,
-          xsf, ng, G, G);
+          hist, hist_base, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens,
+          expert_offsets, x, xq, xsf, ng, G, G);
     else if (sq->ue8m0)
       route_scan_quant_kernel<128, true><<<grid, 1024, 0, stream>>>(
-          hist, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens, expert_offsets, x, xq,
-          xsf, ng, G, 4 * ((G + 3) / 4));
+          hist, hist_base, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens,
+          expert_offsets, x, xq, xsf, ng, G, 4 * ((G + 3) / 4));
     else
       route_scan_quant_kernel<128, false><<<grid, 1024, 0, stream>>>(
-          hist, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens, expert_offsets, x, xq,
-          xsf, ng, G, 4 * ((G + 3) / 4));
+          hist, hist_base, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens,
+          expert_offsets, x, xq, xsf, ng, G, 4 * ((G + 3) / 4));
   } else {
-    route_scan_kernel<<<1, 1024, 0, stream>>>(hist, nblocks, E, counts_in, max_tokens, tl,
-                                              expert_num_tokens, expert_offsets);
+    route_scan_kernel<<<tl.tall != nullptr ? 2 : 1, 1024, 0, stream>>>(
+        hist, hist_base, nblocks, E, counts_in, max_tokens, tl, expert_num_tokens,
+        expert_offsets);
   }
   if (nblocks > 0) {
     route_scatter_kernel<<<nblocks, kRouteThreads, E * sizeof(int32_t), stream>>>(
-        idx_out, T, k, E, hist, expert_offsets, counts_in != nullptr ? max_tokens : 0, row_src,
+        idx_out, T, k, E, hist_base, expert_offsets, counts_in != nullptr ? max_tokens : 0, row_src,
         slot_row);
   }
   return hipGetLastError();
