@@ -367,6 +367,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     info_out = info;
     return true;
   };
+  // a tile of the indexed layout's tall list (twice the block size): taken
+  // from the schedule like a contiguous tile, positions in sorted_ids
+  bool tall_ix = false;
   if (indexed) {
     if (p.tile_list != nullptr) {
       // moe_forward: the blocks in the schedule's XCD-balanced zipper order;
@@ -375,8 +378,22 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       const int32_t* info = nullptr;
       if (!schedule_item(t, nt, info)) return;
       const int t0 = (int)(info - (p.tile_list + 4)) / 8;
-      tile = __builtin_amdgcn_readfirstlane(info[6] + (info[1] / S::BM) + (t - t0));
-      w_once = S::BM <= 128 && !W4 && info[4] <= S::BM;
+      if (S::BM != p.block_size) {
+        // rows m0 .. of the expert's segment of sorted_ids, which starts at
+        // its first block; its routed entries lead the segment, so the first
+        // min(BM, count - m0) positions from m0 are all routed (and inside
+        // the segment: never the next expert's)
+        tall_ix = true;
+        tile = t;
+        e = info[0];
+        m0 = info[1] + (t - t0) * S::BM;
+        rows_here = min(S::BM, info[4] - m0);
+        base = (int64_t)info[6] * p.block_size;
+        w_once = false;
+      } else {
+        tile = __builtin_amdgcn_readfirstlane(info[6] + (info[1] / S::BM) + (t - t0));
+        w_once = S::BM <= 128 && !W4 && info[4] <= S::BM;
+      }
     } else {
       // Block order, in groups of 8 blocks: a group of one expert's blocks
       // (consecutive m-tiles of a heavy expert) is taken n-tile-major, so
@@ -400,14 +417,16 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
         nt = __builtin_amdgcn_readfirstlane((int)(r % NT));
       }
     }
-    // the block's routed entries (ids below numel) lead, padding follows
-    e = __builtin_amdgcn_readfirstlane(p.expert_ids[tile]);
-    m0 = 0;
-    base = (int64_t)tile * S::BM;
-    const bool valid =
-        threadIdx.x < S::BM && (uint32_t)p.sorted_ids[base + threadIdx.x] < (uint32_t)p.numel;
-    rows_here = __syncthreads_count(valid);
-    if ((uint32_t)e >= (uint32_t)p.num_experts) return;
+    if (!tall_ix) {
+      // the block's routed entries (ids below numel) lead, padding follows
+      e = __builtin_amdgcn_readfirstlane(p.expert_ids[tile]);
+      m0 = 0;
+      base = (int64_t)tile * S::BM;
+      const bool valid =
+          threadIdx.x < S::BM && (uint32_t)p.sorted_ids[base + threadIdx.x] < (uint32_t)p.numel;
+      rows_here = __syncthreads_count(valid);
+      if ((uint32_t)e >= (uint32_t)p.num_experts) return;
+    }
   } else {
     // Contiguous / batched layouts: XCD x walks the x-th of 8 equal slices
     // of the schedule the routing step built.  One scalar load of tile t0's

@@ -65,6 +65,7 @@ struct GemmArgs {
   const int32_t* expert_ids;
   const int32_t* num_padded;       // [1] device: the padded total
   int max_blocks;                  // blocks of sorted_ids (bounds *num_padded)
+  int block_size;                  // the block map's block size (indexed layout)
   int top_k;                       // w13: the routing's top_k; w2: 1
   int numel;                       // T * top_k
   int gather_sorted;               // A row = sorted_ids[pos] / top_k; else pos

@@ -152,11 +152,12 @@ int choose_tile_m(const moe_problem_t* p) {
 // 1.42 ms) and w2 0.99 -> 0.96 ms; the same two launches one after the
 // other gained only 3 % on w13 and lost 3 % on w2 (each launch's last wave
 // of blocks runs half empty).  Not for bf16 activations (128-row tiles at
-// most), the indexed layout (one block size) or a split w2 (its tickets
-// are indexed by tile).  A forced tile height (MOE_TILE_M) keeps one list;
-// MOE_TALL = 0 | 1 turns the second list off / on where it can run.
+// most) or a split w2 (its tickets are indexed by tile).  In the indexed
+// layout a tall tile covers 256 positions of its expert's segment of the
+// block map (block size 128).  A forced tile height (MOE_TILE_M) keeps one
+// list; MOE_TALL = 0 | 1 turns the second list off / on where it can run.
 bool use_tall(const moe_problem_t* p, int tile_m, int w2_split) {
-  const bool can = tile_m == 128 && !indexed(p) && p->act_quant != MOE_Q_BF16 && w2_split == 1;
+  const bool can = tile_m == 128 && p->act_quant != MOE_Q_BF16 && w2_split == 1;
   const char* env = getenv("MOE_TALL");
   if (env != nullptr && (env[0] == '0' || env[0] == '1')) return can && env[0] == '1';
   return can && getenv("MOE_TILE_M") == nullptr;
@@ -510,11 +511,20 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
     g.numel = p->num_tokens * p->top_k;
     g.gather_sorted = 1;
     g.scatter_sorted = 1;
+    g.block_size = ix->block_size;
     tile_m = ix->block_size;
     max_tiles = g.max_blocks;
     // moe_forward hands in its routing: with blocks of the tile height the
-    // GEMM takes them in the routing's XCD-balanced order
-    if (r != nullptr && ix->block_size == pl.s.tile_m) g.tile_list = r->tile_list;
+    // GEMM takes them in the routing's XCD-balanced order (the tall list's
+    // tiles cover two blocks of one expert)
+    if (r != nullptr && ix->block_size == pl.s.tile_m) {
+      g.tile_list = r->tile_list;
+      if (tall_list) {
+        g.tile_list = r->tile_list + pl.s.tall_list_offset;
+        tile_m = pl.s.tall_tile_m;
+        max_tiles = (int)pl.s.max_tiles_tall;
+      }
+    }
   } else {
     g.tile_list = r->tile_list;
     g.row_src = (w13 && !batched(p)) ? r->row_src : nullptr;
@@ -972,16 +982,24 @@ moe_status_t forward_impl(const moe_problem_t* p, const void* hidden,
   if (indexed(p)) {
     const Indexed ix{w.sorted_ids, w.expert_ids, w.num_padded, pl.s.tile_m};
     CHECK(run_align(p, w.idx, &w.routing, ix, s));
+    std::function<moe_status_t(bool, hipStream_t)> w2_step = [&](bool tall, hipStream_t st) {
+      return run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, st, false,
+                      nullptr, nullptr, &ix, w.w2_split, tall);
+    };
     if (gated(p)) {
-      CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, nullptr, s, true,
-                     w.a2_q, w.a2_sf, &ix));
+      std::function<moe_status_t(bool, hipStream_t)> w13_step = [&](bool tall, hipStream_t st) {
+        return run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, nullptr, st, true,
+                        w.a2_q, w.a2_sf, &ix, nullptr, tall);
+      };
+      CHECK(run_lists_two_steps(pl, s, side, w13_step, w2_step));
     } else {
-      CHECK(run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, w.gate_up, s, false,
-                     nullptr, nullptr, &ix));
+      CHECK(run_lists(pl, s, side, [&](bool tall, hipStream_t st) {
+        return run_gemm(p, pl, true, w.x_q, w.x_sf, &w.routing, w13, w13_sf, w.gate_up, st,
+                        false, nullptr, nullptr, &ix, nullptr, tall);
+      }));
       CHECK(run_act(p, pl, w.gate_up, &w.routing, w.a2_q, w.a2_sf, s, true));
+      CHECK(run_lists(pl, s, side, w2_step));
     }
-    CHECK(run_gemm(p, pl, false, w.a2_q, w.a2_sf, &w.routing, w2, w2_sf, w.down, s, false,
-                   nullptr, nullptr, &ix, w.w2_split));
     CHECK(run_mul_sum(p, w.down, w.idx, w.w, out, s));
     return ok();
   }

@@ -156,12 +156,18 @@ __device__ __forceinline__ void route_scan_body(
   }
   exp_rows[e] = rows;
   exp_base[e] = counts_in != nullptr ? e * max_tokens : incl - cnt;
+  // the expert's first m-tile in expert order counting every expert's
+  // tiles of tile_m rows (in both lists): its first block in the indexed
+  // layout's block map when the block size is tile_m
+  {
+    const int nt_all = e < E ? (rows + tl.tile_m - 1) / tl.tile_m : 0;
+    exp_tile0[e] = block_inclusive_scan(nt_all, buf) - nt_all;
+  }
   // one list: nt m-tiles of tile_m rows for this thread's expert (0: not in
   // this list); block-uniform arguments otherwise
   auto schedule = [&](const int nt, const int tile_m, const int max_tiles,
                       int32_t* __restrict__ tile_list) {
   const int incl_nt = block_inclusive_scan(nt, buf);
-  exp_tile0[e] = incl_nt - nt;
   // the last thread's inclusive value is the total: broadcast it
   if (e == 1023) buf[0] = incl_nt;
   __syncthreads();

@@ -233,7 +233,7 @@ def test_tall_list_sizes(lib, monkeypatch):
         p = moe.Problem.from_config(cfg)
         s = moe.sizes(p)
         E, slots = cfg.E, cfg.T * cfg.top_k
-        tall = (s["tile_m"] == 128 and cfg.layout != "indexed" and cfg.act_quant != "bf16"
+        tall = (s["tile_m"] == 128 and cfg.act_quant != "bf16"
                 and moe.w2_workspace_size(p) == 0)
         assert (s["tall_tile_m"] == 256) == tall and s["tall_tile_m"] in (0, 256), name
         main = 4 + 9 * s["max_tiles"] + E + 1

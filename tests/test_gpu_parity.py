@@ -365,15 +365,15 @@ def test_stage_and_route_bit_exact(gpu, name):
     check_schedule(bufs["tile_list"], ref["counts"], moe.sizes(p), cfg.E, bases)
 
 
-def _check_one_list(tl, tiles, bm, max_tiles, counts, bases):
+def _check_one_list(tl, tiles, bm, max_tiles, counts, bases, tile0):
     """One tile list: every listed expert's tiles exactly once, in the
     documented XCD-balanced order, groups of consecutive m-tiles of one
-    expert, and each tile's information (group, expert rows, first row)."""
+    expert, and each tile's information (group, expert rows, first row, the
+    expert's first block of the indexed block map: tile0)."""
     n, G = int(tl[0]), int(tl[1])
     assert tl[2] == 0 and tl[3] == 0
     info = tl[4:4 + 8 * n].reshape(n, 8)
     seq, sizes = expected_schedule(tiles)
-    tile0 = np.concatenate([[0], np.cumsum(tiles)[:-1]])
     assert [(int(e), int(m0) // bm) for e, m0 in info[:, :2]] == seq
     assert np.all(info[:, 1] % bm == 0)
     groups = tl[4 + 8 * max_tiles:4 + 8 * max_tiles + G + 1]
@@ -386,8 +386,8 @@ def _check_one_list(tl, tiles, bm, max_tiles, counts, bases):
         assert np.all(seg[:, 2] == groups[g]) and np.all(seg[:, 3] == len(seg))
         e = int(seg[0, 0])
         assert np.all(seg[:, 4] == int(counts[e])) and np.all(seg[:, 5] == int(bases[e]))
-        # the expert's first m-tile in expert order (the indexed layout's
-        # first block of the expert at this block size)
+        # the expert's first block of the indexed layout's block map (block
+        # size tile_m: every expert's blocks counted, in both lists)
         assert np.all(seg[:, 6] == tile0[e]) and np.all(seg[:, 7] == 0)
 
 
@@ -399,13 +399,15 @@ def check_schedule(tile_list, counts, s, E, bases):
     tl = to_np(tile_list)
     bm, tall = s["tile_m"], s["tall_tile_m"]
     heavy = [tall != 0 and int(c) > bm for c in counts]
-    _check_one_list(tl, [0 if h else -(-int(c) // bm) for c, h in zip(counts, heavy)], bm,
-                    s["max_tiles"], counts, bases)
+    blocks = [-(-int(c) // bm) for c in counts]
+    tile0 = np.concatenate([[0], np.cumsum(blocks)[:-1]])
+    _check_one_list(tl, [0 if h else b for b, h in zip(blocks, heavy)], bm,
+                    s["max_tiles"], counts, bases, tile0)
     if tall:
         off = s["tall_list_offset"]
         assert off % 4 == 0 and off >= 4 + 9 * s["max_tiles"] + E
         _check_one_list(tl[off:], [-(-int(c) // tall) if h else 0 for c, h in zip(counts, heavy)],
-                        tall, s["max_tiles_tall"], counts, bases)
+                        tall, s["max_tiles_tall"], counts, bases, tile0)
 
 
 def test_stage_bf16_copy(gpu):
@@ -806,6 +808,40 @@ def test_tall_list(gpu, name, monkeypatch):
                        expert_num_tokens=dev["expert_num_tokens"])
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), st.view(torch.int16)), f"{name}: static differs"
+
+
+TALL_INDEXED = moe_synth.custom(name="tall_indexed", T=256, E=8, top_k=3, K=1024, N=1024,
+                                seed=56, routing="zipf", zipf_s=1.1, pad_frac=0.05,
+                                layout="indexed")
+
+
+def test_tall_list_indexed(gpu, monkeypatch):
+    """The indexed layout with the tall list: 256-row tiles cover 256
+    positions of a heavy expert's segment of the 128-block map (never the
+    next expert's).  moe_forward matches the oracle, equals the one-list
+    run (MOE_TALL=0) and moe_forward_static bit for bit."""
+    monkeypatch.delenv("MOE_TILE_M", raising=False)
+    monkeypatch.delenv("MOE_TALL", raising=False)
+    cfg = TALL_INDEXED
+    CASES.setdefault(cfg.name, cfg)
+    _, h, dev, ref = case(cfg.name)
+    p = problem(cfg)
+    s = moe.sizes(p)
+    assert p.layout == moe.LAYOUT_INDEXED and s["tile_m"] == 128 and s["tall_tile_m"] == 256
+    counts = ref["counts"]
+    assert (counts > 128).any() and ((counts > 0) & (counts <= 128)).any()
+    out = run_forward(cfg, dev)
+    check_output(to_np(out), ref["out"], "tall_indexed moe_forward output")
+    monkeypatch.setenv("MOE_TALL", "0")
+    one = run_forward(cfg, dev)
+    monkeypatch.delenv("MOE_TALL")
+    assert torch.equal(out.view(torch.int16), one.view(torch.int16)), "one list differs"
+    st = torch.empty_like(out)
+    moe.forward_static(p, dev["hidden"], dev["topk_ids"], dev["topk_weights"], dev["w13"],
+                       dev["w13_sf"], dev["w2"], dev["w2_sf"], st, is_padding=dev["is_padding"],
+                       expert_num_tokens=dev["expert_num_tokens"])
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), st.view(torch.int16)), "static differs"
 
 
 # ---------------------------------------------------------------------------
