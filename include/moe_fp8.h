@@ -228,9 +228,10 @@ typedef struct {
  * 16, 32 or 64 rows up to 12, 24 or 48 rows per expert, 128 up to 128, and
  * 256 above (at most 128 for bf16 activations); when w2 splits its reduction
  * (N >= 8192), 192 rows between 96 and 192 rows per expert.  At 128-row
- * tiles (fp8 or MXFP8 activations, an unsplit w2, not the indexed layout)
- * the experts of more than 128 rows go to a second tile list of 256-row
- * tiles (moe_sizes_t.tall_tile_m); every GEMM call then launches one kernel
+ * tiles (fp8 or MXFP8 activations, an unsplit w2) the experts of more than
+ * 128 rows go to a second tile list of 256-row tiles
+ * (moe_sizes_t.tall_tile_m; in the indexed layout's moe_forward a tall tile
+ * covers two 128-blocks of one expert); every GEMM call then launches one kernel
  * per list: the tall list's on the library's second stream beside the main
  * list's on `stream`, or both on `stream`, tall list first
  * (moe_forward_static).  The tile height never changes the results' bits.  MOE_KSPLIT = 1 | 2 | 4 overrides the w2
