@@ -230,14 +230,16 @@ typedef struct {
  * (N >= 8192), 192 rows between 96 and 192 rows per expert.  At 128-row
  * tiles (fp8 or MXFP8 activations, an unsplit w2) the experts of more than
  * 128 rows go to a second tile list of 256-row tiles
- * (moe_sizes_t.tall_tile_m; in the indexed layout's moe_forward a tall tile
- * covers two 128-blocks of one expert); every GEMM call then launches one kernel
- * per list: the tall list's on the library's second stream beside the main
- * list's on `stream`, or both on `stream`, tall list first
- * (moe_forward_static).  The tile height never changes the results' bits.  MOE_KSPLIT = 1 | 2 | 4 overrides the w2
- * split for tuning runs (it does change them: every call of one layer must
- * see the same value).  Two environment variables
- * override the choice for tuning runs.  MOE_TILE_M = 16 | 32 | 64 | 128 |
+ * (moe_sizes_t.tall_tile_m).  The GEMM calls that take the routing
+ * (moe_grouped_gemm_w13 / _act / _w2, moe_forward, in the indexed layout's
+ * moe_forward a tall tile covering two 128-blocks of one expert) then
+ * launch one kernel per list: the tall list's on the library's second
+ * stream beside the main list's on `stream`, or both on `stream`, tall list
+ * first (moe_forward_static); the indexed entry points, which take a block
+ * map, keep one launch.  The tile height never changes the results' bits.
+ * MOE_KSPLIT = 1 | 2 | 4 overrides the w2 split for tuning runs (it does
+ * change them: every call of one layer must see the same value).  Two
+ * environment variables override the choice for tuning runs.  MOE_TILE_M = 16 | 32 | 64 | 128 |
  * 192 | 256 (192 and 256 not for bf16; other values are ignored) is read by
  * every call; all calls of one layer must see the same value, since the
  * stage builds the tile schedule for the height the GEMM calls then read it
