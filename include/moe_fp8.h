@@ -238,8 +238,8 @@ typedef struct {
  * first (moe_forward_static); the indexed entry points, which take a block
  * map, keep one launch.  The tile height never changes the results' bits.
  * MOE_KSPLIT = 1 | 2 | 4 overrides the w2 split for tuning runs (it does
- * change them: every call of one layer must see the same value).  Two
- * environment variables override the choice for tuning runs.  MOE_TILE_M = 16 | 32 | 64 | 128 |
+ * change them: every call of one layer must see the same value).  Further
+ * environment variables override the other choices for tuning runs.  MOE_TILE_M = 16 | 32 | 64 | 128 |
  * 192 | 256 (192 and 256 not for bf16; other values are ignored) is read by
  * every call; all calls of one layer must see the same value, since the
  * stage builds the tile schedule for the height the GEMM calls then read it
