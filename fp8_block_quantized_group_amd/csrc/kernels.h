@@ -51,16 +51,18 @@ struct GemmArgs {
   // row within the expert, first tile and size of its group (one expert's
   // consecutive m-tiles, groups in XCD-balanced order), the expert's rows,
   // its first row in the GEMM's row space (contiguous offset or slab), its
-  // first m-tile in expert order, 0
+  // first block in the indexed layout's block map (blocks of the main
+  // list's tile height, every expert counted), 0
   const int32_t* tile_list;
   int num_experts;
   const int32_t* row_src;    // A row gather (w13 on the contiguous layout) or nullptr
   // indexed layout (sorted_ids != nullptr): tile b is the block of BM rows
   // [b*BM, (b+1)*BM) of sorted_ids, of expert expert_ids[b]; entries not
   // below numel are padding and come after the block's routed entries.
-  // row_src unused; tile_list, when given (block size = BM = the routing's
-  // tile height), orders the blocks: the schedule's tile (e, m-tile i) is
-  // block first-m-tile(e) + i.
+  // row_src unused; tile_list, when given (block size = the routing's tile
+  // height), orders the blocks: the schedule's tile (e, m-tile i) is block
+  // first-block(e) + i; a tile of the tall list (BM = twice the block size)
+  // covers positions first-block(e) * block_size + m0 + [0, rows) instead.
   const int32_t* sorted_ids;
   const int32_t* expert_ids;
   const int32_t* num_padded;       // [1] device: the padded total

@@ -129,7 +129,7 @@ __device__ __forceinline__ void route_scan_body(
   __shared__ int chunk_bin[kChunkCap], chunk_off[kChunkCap], chunk_idx[kChunkCap];
   __shared__ int bin_load[8], bin_cnt[8];
   __shared__ int exp_rows[1024], exp_base[1024];   // per expert: GEMM rows, first row
-  __shared__ int exp_tile0[1024];                   // its first m-tile in expert order
+  __shared__ int exp_tile0[1024];                   // its first block of the block map
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E) {
@@ -278,9 +278,9 @@ __device__ __forceinline__ void route_scan_body(
     const int ex = chunk_e[i], n = chunk_n[i];
     for (int t = 0; t < n; ++t) {
       // expert, first row, its group's first tile and size, the expert's
-      // rows, its first row in the GEMM's row space and its first m-tile in
-      // expert order (the indexed layout's first block of the expert when
-      // its block size is the tile height)
+      // rows, its first row in the GEMM's row space and its first block in
+      // the indexed layout's block map of tile_m-row blocks (every expert's
+      // blocks counted, whichever list it is in)
       int4* d = reinterpret_cast<int4*>(info + 8 * (tile0 + t));
       d[0] = make_int4(ex, (chunk_m[i] + t) * tile_m, tile0, n);
       d[1] = make_int4(exp_rows[ex], exp_base[ex], exp_tile0[ex], 0);
@@ -315,10 +315,11 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(
                   expert_num_tokens, expert_offsets);
 }
 
-// The scan is one block of latency-bound work; the hidden states' group
-// quantization is independent of it and bandwidth-bound.  Block 0 runs the
-// scan while blocks 1.. quantize, so the scan hides under the
-// quantization's memory stream: one launch instead of two back to back.
+// The scan is one block of latency-bound work per tile list; the hidden
+// states' group quantization is independent of it and bandwidth-bound.
+// Block 0 (and block 1 for the tall list) runs the scan while the other
+// blocks quantize, so the scan hides under the quantization's memory
+// stream: one launch instead of two back to back.
 // The quantizing blocks are as many as the chip holds at once (or fewer)
 // and stride over the groups, 1024 / (GROUP / 16) consecutive groups per
 // pass, every block making the same number of passes: no half-empty last
