@@ -95,14 +95,20 @@ struct Shape {
   static constexpr int SC_WAVES = (BM + 63) / 64;          // waves that load row scales
   static constexpr int STAGE_BYTES = A_BYTES + B_BYTES + SC_WAVES * 256;
   static constexpr int NBLK = BN / 128;                    // weight-scale blocks per tile
-  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + NBLK * kMaxGroups * 4;
+  // the fp32 weight-scale panel after the ring: NBLK blocks of PG scales
+  // (one per k-step), kMaxGroups or, where a deep ring leaves less LDS, the
+  // multiples of 64 that still fit (the launcher checks Kd / 128 <= PG)
+  static constexpr int PG_FIT = (160 * 1024 - STAGES * STAGE_BYTES) / (NBLK * 4) / 64 * 64;
+  static constexpr int PG = PG_FIT < kMaxGroups ? PG_FIT : kMaxGroups;
+  static constexpr int LDS_BYTES = STAGES * STAGE_BYTES + NBLK * PG * 4;
   // one buffer_load ... lds instruction moves 64 lanes x 16 bytes = 1 KB
+  // (a tile of 160 rows: waves 0-3 issue one more than waves 4-7)
   static constexpr int A_CHUNKS = BM * 8;
-  static constexpr int A_INSTR = A_CHUNKS >= THREADS ? A_CHUNKS / THREADS : 1;
+  static constexpr int A_INSTR = A_CHUNKS >= THREADS ? (A_CHUNKS + THREADS - 1) / THREADS : 1;
   static constexpr int B_INSTR = BN * 8 / THREADS;
   static constexpr int BLOCKS_PER_CU = (2 * LDS_BYTES <= 160 * 1024) ? 2 : 1;
   static constexpr int MIN_WAVES_PER_EU = BLOCKS_PER_CU * NW / 4;
-  static_assert(LDS_BYTES <= 160 * 1024, "LDS ring exceeds the CU's LDS");
+  static_assert(PG >= 64 && LDS_BYTES <= 160 * 1024, "LDS ring exceeds the CU's LDS");
   static_assert(B_INSTR * THREADS == BN * 8, "weight tile split");
   // most buffer loads into LDS a wave issues per k-step
   static constexpr int LMAX = A_INSTR + B_INSTR + 1;
@@ -297,7 +303,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   constexpr int AROW = A16 ? 2 * kRowBytes : kRowBytes;
   constexpr int AB = S::BM * AROW;
   constexpr int ACH = AROW / 16;                          // 16-byte chunks per row
-  constexpr int AI = S::BM * ACH >= S::THREADS ? S::BM * ACH / S::THREADS : 1;
+  constexpr int AI = S::BM * ACH >= S::THREADS ? (S::BM * ACH + S::THREADS - 1) / S::THREADS : 1;
   constexpr int RPI = 64 / ACH;                           // rows per load instruction
   constexpr bool MX = SC == kQuantMxfp8 || W4;
   constexpr bool UE8M0 = SC == kQuantUe8m0;
@@ -312,7 +318,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // block scheme keeps its fp32 weight-scale panel there instead
   constexpr int STAGE = SC_OFF + (A16 ? 0 : S::SC_WAVES * 256);
   constexpr int WSC_SLOT = S::BN * 16;
-  constexpr int PANEL = MX ? 2 * WSC_SLOT : S::NBLK * kMaxGroups * 4;
+  constexpr int PANEL = MX ? 2 * WSC_SLOT : S::NBLK * S::PG * 4;
   constexpr int LDS = S::STAGES * STAGE + PANEL;
   constexpr int LMAX = AI + BI + 1 + (MX ? 1 : 0);
   static_assert(LDS <= 160 * 1024 && 3 * LMAX < 64, "LDS ring / vmcnt range");
@@ -392,7 +398,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
         w_once = false;
       } else {
         tile = __builtin_amdgcn_readfirstlane(info[6] + (info[1] / S::BM) + (t - t0));
-        w_once = S::BM <= 128 && !W4 && info[4] <= S::BM;
+        w_once = S::BM <= 160 && !W4 && info[4] <= S::BM;
       }
     } else {
       // Block order, in groups of 8 blocks: a group of one expert's blocks
@@ -457,11 +463,15 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     // read — measured +8 % w13, +20 % w2 at the MXFP4 DSv3 batch)
     // Tiles of 192 / 256 rows are picked for experts with hundreds of rows,
     // whose weight tiles are shared: those shapes keep one load form (the
-    // run-time choice alone cost 2-3 % on the Qwen3-shaped fused w13).
+    // run-time choice alone cost 2-3 % on the Qwen3-shaped fused w13).  The
+    // 160-row tiles hold whole experts of about 100-160 rows: there the
+    // hint halved the weight stream's time per k-step (8 experts of ~128
+    // rows, N = 14336: w2 0.213 -> 0.179 ms, fused w13 0.289 -> 0.253 ms;
+    // without it the once-read weight lines evict the shared activation rows).
     // An expert of one m-tile is the only reader of its weight tiles; the
     // last chunk of a longer expert is not (its other chunks read the same
     // tiles), whatever that chunk's own size.
-    w_once = S::BM <= 128 && !W4 && info[4] <= S::BM;
+    w_once = S::BM <= 160 && !W4 && info[4] <= S::BM;
     base = info[5];
   }
   const int n0 = nt * S::BN;          // first output column (plain GEMM)
@@ -484,6 +494,27 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     k0 = min(split * chunk, G_all);
     G = min(G_all, k0 + chunk) - k0;
   }
+  // The block walks its G k-steps from step rot on, wrapping round (p.krot):
+  // when the weight rows are a multiple of 4 KB long, blocks that stream at
+  // the same k-step read the same offset of every row, which concentrates
+  // the reads on a few HBM channels (a probe: 4.7 TB/s at a 4096-byte row
+  // stride, 6.3 TB/s with the step order staggered per block).  rot depends
+  // on the expert and on the output columns' 256-column pair only (w13:
+  // counted within the gate or the up half), so the fused and the unfused
+  // w13, every tile height and width, and every batch add a column's
+  // k-steps in the same order.
+  int rot = 0;
+  if constexpr (!MX) {
+    if (p.krot != 0 && G > 1) {
+      const int key = ((ACT ? j0 : n0) % p.rot_period) / 256;
+      rot = __builtin_amdgcn_readfirstlane((5 * key + 3 * e) % G);
+    }
+  }
+  // absolute k-step of the block's kb-th step
+  auto kabs = [&](int kb) {
+    const int r = kb + rot;
+    return k0 + (r >= G ? r - G : r);
+  };
 
   // activation row of tile row m (an id that is padding gathers row T,
   // past the buffer's end: the buffer loads return zeros there)
@@ -533,7 +564,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
 #pragma unroll
     for (int i = 0; i < BI; ++i)
       dma16_w(rs_b, st + AB + i * S::THREADS * 16 + wave_slot,
-              b_off[i] + (uint32_t)(k0 + kb) * WROW, w_once);
+              b_off[i] + (uint32_t)kabs(kb) * WROW, w_once);
   };
 #pragma unroll
   for (int s = 0; s < S::STAGES - 1; ++s)
@@ -603,7 +634,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       const v4i rs_p = buffer_rsrc((const uint8_t*)p.w_sf +
                                        (((int64_t)e * (p.Nout / kGroup) + blk) * G_all) * 4,
                                    (uint32_t)(G_all * 4));
-      const uint32_t dst = smem_base + S::STAGES * STAGE + b * kMaxGroups * 4;
+      const uint32_t dst = smem_base + S::STAGES * STAGE + b * S::PG * 4;
       for (int g0 = 0; g0 < G_all; g0 += 64)
         dma4(rs_p, dst + g0 * 4, (uint32_t)((g0 + lane) * 4));
     }
@@ -649,14 +680,14 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // the weight-scale block of this lane's output columns (ACT: lanes 0-31
   // hold gate rows, lanes 32-63 up rows)
   const float* sw_mine =
-      sw_panel + (ACT ? (kq >= 2 ? 1 : 0) : (wn * S::WAVE_N) / 128) * kMaxGroups;
+      sw_panel + (ACT ? (kq >= 2 ? 1 : 0) : (wn * S::WAVE_N) / 128) * S::PG;
 
   // the rest of a k-step: activation rows, their scales, MX weight scales
   // (kb relative to k0; k0 is a multiple of 4, so kb & 3 is the absolute
   // k-step's position in its group of 4)
   auto issue_as = [&](int kb) {
     const uint32_t st = smem_base + (kb % S::STAGES) * STAGE;
-    const int ka = k0 + kb;
+    const int ka = kabs(kb);
 #pragma unroll
     for (int i = 0; i < AI; ++i)
       if (i < a_loads)
@@ -696,7 +727,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       // 16x16x32 bf16 MFMAs per sub-tile per 128-deep block, chained in a
       // partial, then acc += partial * sw
       const uint8_t* sb = smem + (kb % S::STAGES) * STAGE;
-      const float sw = sw_mine[k0 + kb];
+      const float sw = sw_mine[kabs(kb)];
       v8bf wb[S::TN][4];
 #pragma unroll
       for (int i = 0; i < S::TN; ++i) {
@@ -785,7 +816,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
         const v4i hi = *reinterpret_cast<const v4i*>(sb + w_frag1 + i * 4 * kRowBytes);
         wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      const float sw = sw_mine[k0 + kb];
+      const float sw = sw_mine[kabs(kb)];
       // activation fragment j (and its scale) is read when sub-tile j-1's
       // MFMAs start, so at most two are live
       auto load_a = [&](int j, v8i& f, float& fs) {
@@ -793,7 +824,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
         const v4i hi = *reinterpret_cast<const v4i*>(sb + a_frag1 + j * kSubStride * kRowBytes);
         f = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         const uint32_t word = *reinterpret_cast<const uint32_t*>(sb + sc_frag + j * kSubStride * 4);
-        const float sa = UE8M0 ? __uint_as_float(((word >> ((kb & 3) * 8)) & 0xFFu) << 23)
+        const float sa = UE8M0 ? __uint_as_float(((word >> ((kabs(kb) & 3) * 8)) & 0xFFu) << 23)
                                : __uint_as_float(word);
         fs = sa * sw;
       };
@@ -1058,6 +1089,13 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   }
 }
 
+// 160-row tiles: the block scheme with fp8 activations only
+template <int SC>
+constexpr bool kTile160 = SC == kQuantUe8m0 || SC == kQuantF32;
+static_assert(Shape<160, 256, 8, 3>::PG >= kTile160MaxGroups &&
+                  Shape<160, 128, 8, 3>::PG >= kTile160MaxGroups,
+              "160-row tiles: reduction length limit");
+
 template <class S, int SC, bool ACT>
 hipError_t launch_shape(const GemmArgs& pin, int max_tiles, hipStream_t stream) {
   // Item order inside a group: consecutive blocks on an XCD start about a
@@ -1074,8 +1112,23 @@ hipError_t launch_shape(const GemmArgs& pin, int max_tiles, hipStream_t stream) 
     static const char* env = getenv("MOE_SN");
     p.sn = env != nullptr ? atoi(env) : (S::BM >= 192 ? 2 : 1);
   }
+  // k-step rotation: weight rows of a multiple of 4 KB (the MX schemes keep
+  // the plain order: their scale panel arrives in groups of 4 k-steps).
+  // MOE_KROT = 0 | 1 overrides (read at every launch).
+  {
+    constexpr bool mxs = SC == kQuantMxfp8 || SC == kSchemeMxfp8W4;
+    const char* env = getenv("MOE_KROT");
+    const bool want = env != nullptr ? env[0] == '1' : p.Kd % 4096 == 0;
+    p.krot = (!mxs && want && p.rot_period > 0 && p.rot_period % 256 == 0) ? 1 : 0;
+  }
+  // the block scheme's weight-scale panel holds S::PG k-steps
+  constexpr bool mx = SC == kQuantMxfp8 || SC == kSchemeMxfp8W4;
+  if (!mx && p.Kd / kGroup > S::PG) return hipErrorInvalidValue;
+  // every XCD's slice: whole items' splits, ceil(items / 8) * splits blocks
+  // (the schedule's slicing; rounding items * splits up to 8 instead would
+  // leave splits of the last items without a block)
   const int64_t blocks =
-      ((int64_t)max_tiles * (p.Nout / S::BN) * (ACT ? 1 : max(p.ksplit, 1)) + 7) / 8 * 8;
+      ((int64_t)max_tiles * (p.Nout / S::BN) + 7) / 8 * 8 * (ACT ? 1 : max(p.ksplit, 1));
   const dim3 grid((unsigned)blocks);
   if constexpr (SC == kQuantBf16) {
     // bf16 activation tiles take twice the LDS: only shapes whose ring fits
@@ -1141,6 +1194,10 @@ hipError_t launch_grouped_gemm_sc(const GemmArgs& p, int tile_m, int max_tiles, 
         case 32: return launch_shape<Shape<32, 256, 4, 3>, SC, true>(p, max_tiles, stream);
         case 64: return launch_shape<Shape<64, 256, 8, 3>, SC, true>(p, max_tiles, stream);
         case 128: return launch_shape<Shape<128, 256, 8, 3>, SC, true>(p, max_tiles, stream);
+        case 160:
+          if constexpr (kTile160<SC>)
+            return launch_shape<Shape<160, 256, 8, 3>, SC, true>(p, max_tiles, stream);
+          return hipErrorInvalidValue;
         case 192: return launch_shape<Shape<192, 256, 8, 2>, SC, true>(p, max_tiles, stream);
         case 256: return launch_shape<Shape<256, 256, 8, 2>, SC, true>(p, max_tiles, stream);
         default: return hipErrorInvalidValue;
@@ -1166,6 +1223,16 @@ hipError_t launch_grouped_gemm_sc(const GemmArgs& p, int tile_m, int max_tiles, 
           return launch_shape<Shape<128, 256, 8, 3>, SC, false>(p, max_tiles, stream);
         return launch_shape<Shape<128, 128, 4, 2>, SC, false>(p, max_tiles, stream);
       }
+      // Experts of about 100-160 rows (few experts, a split w2): one tile
+      // each, with the 3-slot ring that a 192-row tile cannot fit (block
+      // scheme only: the MX weight-scale panel does not fit beside it)
+      case 160:
+        if constexpr (kTile160<SC>) {
+          if (p.Nout % 256 == 0)
+            return launch_shape<Shape<160, 256, 8, 3>, SC, false>(p, max_tiles, stream);
+          return launch_shape<Shape<160, 128, 8, 3>, SC, false>(p, max_tiles, stream);
+        }
+        return hipErrorInvalidValue;
       // Experts with hundreds of rows: 1.5x / 2x fewer weight re-reads than
       // 128-row tiles, at the price of a two-slot ring (LDS) and of 128
       // accumulator VGPRs per lane at 256 rows.

@@ -19,6 +19,11 @@ constexpr int kWeightMxfp4 = 2;      // e2m1 (two per byte), E8M0 per row and 32
 // e2m1 weights
 constexpr int kSchemeMxfp8W4 = 4;
 
+// GEMM tiles of 160 rows (block scheme only) hold the fp32 weight-scale
+// panel of at most this many k-steps beside their 3-slot ring: reductions
+// of up to 192 * 128 = 24576
+constexpr int kTile160MaxGroups = 192;
+
 // routing: slots handled per block of the count / scatter kernels
 constexpr int kRouteChunk = 1024;
 constexpr int kRouteThreads = 256;
@@ -93,6 +98,12 @@ struct GemmArgs {
   // 1: 256 output columns for the unfused GEMMs' 128-row tiles whatever the
   // scheme (set when the experts above 128 rows have their own tile list)
   int wide;
+  // k-step rotation key: output column c belongs to pair (c mod rot_period)
+  // / 256 (the caller: Nout, or N for a gated w13 whose gate and up halves
+  // share pairs; 0 = never rotate); krot (set by the launcher) turns the
+  // rotation on
+  int rot_period;
+  int krot;
 };
 
 // zero n int32 (a fill kernel: safe under graph capture)

@@ -77,9 +77,18 @@ float effective_limit(const moe_problem_t* p) {
 }
 int64_t w13_rows(const moe_problem_t* p) { return (gated(p) ? 2 : 1) * (int64_t)p->intermediate; }
 
+// 160-row GEMM tiles: block-scaled weights with fp8 activations, both
+// reductions within the tiles' weight-scale panel
+bool tile160_fits(const moe_problem_t* p) {
+  return (p->act_quant == MOE_Q_FP8_UE8M0 || p->act_quant == MOE_Q_FP8_F32) &&
+         p->hidden / 128 <= moe::kTile160MaxGroups &&
+         p->intermediate / 128 <= moe::kTile160MaxGroups;
+}
+
 // Block sizes of the indexed layout: the GEMM tile heights.
 bool valid_block_size(const moe_problem_t* p, int bs) {
   if (bs == 16 || bs == 32 || bs == 64 || bs == 128) return true;
+  if (bs == 160) return tile160_fits(p);
   return (bs == 192 || bs == 256) && p->act_quant != MOE_Q_BF16;
 }
 
@@ -123,9 +132,7 @@ int choose_tile_m(const moe_problem_t* p) {
   const char* env = getenv("MOE_TILE_M");
   if (env != nullptr) {
     const int v = atoi(env);
-    if (v == 16 || v == 32 || v == 64 || v == 128 ||
-        ((v == 192 || v == 256) && p->act_quant != MOE_Q_BF16))
-      return v;
+    if (valid_block_size(p, v)) return v;
   }
   const double rows = (double)p->num_tokens * p->top_k / p->num_experts;
   // bf16 activation tiles take twice the LDS: at most 128 rows
@@ -135,8 +142,11 @@ int choose_tile_m(const moe_problem_t* p) {
   // (an 8-expert batch: 192 items, 384 when split = 1.5 waves of blocks for
   // 256 CUs), a 192-row tile one tile each (256 split items).  Measured on
   // the 8-expert N = 14336 batch: layer 0.453 ms (128 rows, unsplit) ->
-  // 0.423 ms (192 rows, split in two).
-  if (w2_ksplit(p) > 1 && rows > 96.0 && rows <= 192.0) return 192;
+  // 0.423 ms (192 rows, split in two).  A 192-row tile fits only a two-slot
+  // ring in LDS (one k-step of weights in flight per CU); a 160-row tile,
+  // where the experts' rows fit it, keeps three slots.
+  if (w2_ksplit(p) > 1 && rows > 96.0 && rows <= 192.0)
+    return rows <= 144.0 && tile160_fits(p) ? 160 : 192;
   if (rows <= 12.0) return 16;
   if (rows <= 24.0) return 32;
   if (rows <= 48.0) return 64;
@@ -536,6 +546,9 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
   }
   g.Kd = w13 ? p->hidden : p->intermediate;
   g.Nout = w13 ? (int)w13_rows(p) : p->hidden;
+  // a gated w13's gate and up halves are keyed alike (their 256-column pairs
+  // align only when N is a multiple of 256)
+  g.rot_period = !(w13 && gated(p)) ? g.Nout : p->intermediate % 256 == 0 ? p->intermediate : 0;
   g.activation = p->activation;
   g.act_limit = effective_limit(p);
   const int scheme =

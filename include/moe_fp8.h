@@ -227,7 +227,9 @@ typedef struct {
 /* Tile height.  tile_m follows the expected rows per expert, T * top_k / E:
  * 16, 32 or 64 rows up to 12, 24 or 48 rows per expert, 128 up to 128, and
  * 256 above (at most 128 for bf16 activations); when w2 splits its reduction
- * (N >= 8192), 192 rows between 96 and 192 rows per expert.  At 128-row
+ * (N >= 8192), 192 rows between 96 and 192 rows per expert (160 up to 144
+ * rows per expert when the weights are block-scaled, the activations fp8
+ * with per-128 scales and hidden and intermediate at most 24576).  At 128-row
  * tiles (fp8 or MXFP8 activations, an unsplit w2) the experts of more than
  * 128 rows go to a second tile list of 256-row tiles
  * (moe_sizes_t.tall_tile_m).  The GEMM calls that take the routing
@@ -240,7 +242,8 @@ typedef struct {
  * MOE_KSPLIT = 1 | 2 | 4 overrides the w2 split for tuning runs (it does
  * change them: every call of one layer must see the same value).  Further
  * environment variables override the other choices for tuning runs.  MOE_TILE_M = 16 | 32 | 64 | 128 |
- * 192 | 256 (192 and 256 not for bf16; other values are ignored) is read by
+ * 160 | 192 | 256 (192 and 256 not for bf16, 160 only where block_size 160
+ * is valid below; other values are ignored) is read by
  * every call; all calls of one layer must see the same value, since the
  * stage builds the tile schedule for the height the GEMM calls then read it
  * with; a forced height keeps one tile list.  MOE_TALL = 0 | 1 turns the
@@ -251,7 +254,14 @@ typedef struct {
  * first GEMM call, and does not change the schedule.  MOE_SN = n sets how
  * many n-tiles the GEMMs walk together inside an expert's m-tiles (default 1
  * for tiles up to 128 rows, 2 above; read once per tile shape); it changes
- * only the order of the blocks, never a result's bits. */
+ * only the order of the blocks, never a result's bits.  MOE_KROT = 0 | 1
+ * turns the GEMMs' k-step rotation off or on (read at every launch;
+ * default on where the weight rows are a multiple of 4096 bytes long, never
+ * for the MX schemes): each block starts its reduction at a k-step set by
+ * its expert and its output columns, so that blocks streaming at once read
+ * different offsets of their weight rows.  The start depends on neither the
+ * batch nor the tile shape, but it does set the order of the fp32 additions:
+ * every call of one layer must see the same value. */
 
 /* Sizes of every buffer of `p` (host only). */
 moe_status_t moe_routing_sizes(const moe_problem_t* p, moe_sizes_t* out);
@@ -356,8 +366,10 @@ moe_status_t moe_topk_reduce(const moe_problem_t* p, const void* down, const int
  * [b*block_size, (b+1)*block_size)); *num_tokens_padded is the padded total.
  * The pages call moe_align_block_size without showing its body; this is the
  * plain reading (the order inside a segment is the contiguous layout's row
- * order).  block_size is a GEMM tile height: 16, 32, 64, 128, and for
- * quantized activations 192 or 256.  These calls need the contiguous routing
+ * order).  block_size is a GEMM tile height: 16, 32, 64, 128, for
+ * quantized activations 192 or 256, and 160 for block-scaled weights with
+ * per-128 fp8 activations when hidden and intermediate are at most 24576
+ * (the 160-row tiles' weight-scale panel).  These calls need the contiguous routing
  * (layout CONTIGUOUS or INDEXED; BATCHED_MASKED -> MOE_ERR_UNSUPPORTED). */
 
 /* Capacity of sorted_ids (T*k + min(E, T*k) * (block_size - 1), rounded down

@@ -81,7 +81,7 @@ def test_sizes_follow_the_problem(lib):
         p = moe.Problem.from_config(cfg)
         s = moe.sizes(p)
         assert s["x_sf_row"] == cfg.K // 32 and s["a2_sf_row"] == cfg.N // 32
-        assert s["tile_m"] in (16, 32, 64, 128, 192, 256)
+        assert s["tile_m"] in (16, 32, 64, 128, 160, 192, 256)
         ws = moe.workspace_size(p)
         # staged x_q, the w2 input a2 and the bf16 down projection coexist
         # (the fused w13 call reads x_q while it writes a2)
@@ -261,6 +261,30 @@ def test_tall_list_sizes(lib, monkeypatch):
     assert moe.sizes(p)["tall_tile_m"] == 0
 
 
+def test_tile_height_160(lib, monkeypatch):
+    """The 8-expert, 128-rows-per-expert batch with a split w2 takes 160-row
+    tiles (one per expert, a 3-slot ring) in the block scheme, 192-row ones
+    where 160 cannot run (MX scales, a reduction past the weight-scale
+    panel); a forced MOE_TILE_M=160 is ignored there."""
+    monkeypatch.delenv("MOE_TILE_M", raising=False)
+    cfg = moe_synth.ALL_CONFIGS["mixtral"]
+    p = moe.Problem.from_config(cfg)
+    s = moe.sizes(p)
+    assert s["tile_m"] == 160 and s["tall_tile_m"] == 0
+    assert s["max_tiles"] == cfg.E * -(-cfg.max_tokens // 160)
+    kw = dict(layout=moe.LAYOUT_BATCHED, max_tokens_per_expert=256)
+    mx = moe.Problem(512, 4096, 14336, 8, 2, act_quant=moe.Q_MXFP8, weight_quant=moe.W_MXFP8,
+                     **kw)
+    assert moe.sizes(mx)["tile_m"] == 192
+    long_k = moe.Problem(512, 24576 + 128, 14336, 8, 2, **kw)
+    assert moe.sizes(long_k)["tile_m"] == 192
+    # more rows per expert than a 160-row tile holds comfortably
+    assert moe.sizes(moe.Problem(640, 4096, 14336, 8, 2, **kw))["tile_m"] == 192
+    monkeypatch.setenv("MOE_TILE_M", "160")
+    assert moe.sizes(moe.Problem(64, 4096, 1024, 8, 2))["tile_m"] == 160
+    assert moe.sizes(mx)["tile_m"] == 192
+
+
 def test_indexed_sizes(lib):
     # the indexed layout: sorted_ids has the padded capacity, a2 and down T*k rows
     for name, cfg in moe_synth.INDEXED_CONFIGS.items():
@@ -312,6 +336,14 @@ def test_indexed_validation(lib):
     moe.align_capacity(pb, 128)
     with pytest.raises(moe.MoeError):
         moe.align_capacity(pb, 256)
+    # 160-row blocks: per-128 fp8 activations with block-scaled weights, and
+    # reductions the 160-row tiles' weight-scale panel holds (192 k-steps)
+    moe.align_capacity(p, 160)
+    moe.align_capacity(moe.Problem(**base, act_quant=moe.Q_FP8_F32), 160)
+    for bad in (pb, moe.Problem(**base, act_quant=moe.Q_MXFP8, weight_quant=moe.W_MXFP8),
+                moe.Problem(16, 24576 + 128, 512, 4, 2)):
+        with pytest.raises(moe.MoeError):
+            moe.align_capacity(bad, 160)
     c = p.c()
     # batched routing has no block map
     pbat = moe.Problem(**base, layout=moe.LAYOUT_BATCHED, max_tokens_per_expert=8).c()

@@ -30,6 +30,9 @@ SCHEMES = {
     # N = 8192: w2 splits its reduction in two (the split depends on N only)
     "ue8m0_split": dict(act_quant="ue8m0", N=8192, K=512),
     "fp32": dict(act_quant="fp32"),
+    # K = N = 4096: weight rows of 4 KB, so both GEMMs rotate their k-step
+    # order (keyed by expert and output columns, never by the batch)
+    "ue8m0_krot": dict(act_quant="ue8m0", K=4096, N=4096),
     "mxfp8": dict(act_quant="mxfp8", weight_quant="mxfp8"),
     "mxfp4": dict(act_quant="mxfp8", weight_quant="mxfp4"),
     "bf16": dict(act_quant="bf16"),
@@ -67,7 +70,8 @@ def test_token_bits_independent_of_batch(scheme, monkeypatch):
                            **{k: v for k, v in SCHEMES[scheme].items() if k not in ("K", "N")})
     inp = moe_synth.make_inputs(cfg, "cuda")
     full, tile = _forward(cfg, inp, monkeypatch=monkeypatch)
-    assert tile == (192 if cfg.N >= 8192 else 128), tile
+    # a split w2 at 128 rows per expert: 160-row tiles (block scheme)
+    assert tile == (160 if cfg.N >= 8192 else 128), tile
     # the same batch with other tile heights
     tall = 64 if cfg.act_quant == "bf16" else 256
     for other in (128, tall):

@@ -22,7 +22,7 @@ import moe_synth
 from oracle import moe_oracle as O
 from parity_util import check_output, to_np
 from test_gpu_parity import (SENTINEL_BF16, SENTINEL_U8, SMALL, case, gpu, problem,  # noqa: F401
-                             run_chain, stage_on_gpu)
+                             run_chain, stage_on_gpu, tile160_ok)
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,8 @@ NAMES = [n for n, c in SMALL.items() if c.layout != "batched"]
 
 
 def _block_sizes(cfg):
-    return [16, 32, 64, 128] + ([] if cfg.act_quant == "bf16" else [192, 256])
+    return [16, 32, 64, 128] + ([160] if tile160_ok(cfg) else []) + \
+        ([] if cfg.act_quant == "bf16" else [192, 256])
 
 
 def run_indexed(cfg, dev, bs, bs2=None):

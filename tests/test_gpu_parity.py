@@ -117,8 +117,18 @@ TALL = {
 }
 MID.update(TALL)
 MID_TILES = [16, 128, 256]
+
+
+def tile160_ok(cfg):
+    """160-row tiles run the block scheme with per-128 fp8 activations only."""
+    return cfg.act_quant in ("ue8m0", "fp32") and cfg.weight_quant == "fp8_block128"
+
+
+# the 160-row tiles (a 3-slot ring beside a shortened weight-scale panel)
+# on every mid-size config of the block scheme
 MID_CASES = [(n, t) for n in MID for t in MID_TILES
-             if not (MID[n].act_quant == "bf16" and t > 128) and n not in TALL]
+             if not (MID[n].act_quant == "bf16" and t > 128) and n not in TALL] + \
+    [(n, 160) for n in MID if tile160_ok(MID[n]) and n not in TALL]
 CASES = {**SMALL, **MID}
 
 
@@ -516,7 +526,7 @@ def test_act_requant_isolated(gpu, name):
     assert np.all(got_q[untouched] == SENTINEL_U8)
 
 
-@pytest.mark.parametrize("tile_m", [16, 32, 64, 128, 192, 256])
+@pytest.mark.parametrize("tile_m", [16, 32, 64, 128, 160, 192, 256])
 @pytest.mark.parametrize("name", list(SMALL))
 def test_gemm_w13_act_fused_equals_chain(gpu, name, tile_m, monkeypatch):
     """The fused w13 + activation call against the two calls it replaces, on
@@ -527,6 +537,8 @@ def test_gemm_w13_act_fused_equals_chain(gpu, name, tile_m, monkeypatch):
     monkeypatch.setenv("MOE_TILE_M", str(tile_m))
     if CASES[name].act_quant == "bf16" and tile_m > 128:
         pytest.skip("bf16 activation tiles are at most 128 rows (LDS)")
+    if tile_m == 160 and not tile160_ok(CASES[name]):
+        pytest.skip("160-row tiles: block scheme with per-128 fp8 activations only")
     _fused_equals_chain(name, tile_m)
 
 
@@ -689,7 +701,7 @@ def _forward_end_to_end(name):
         assert np.all(to_np(out)[pad] == 0)
 
 
-@pytest.mark.parametrize("tile_m", [16, 32, 64, 128, 192, 256])
+@pytest.mark.parametrize("tile_m", [16, 32, 64, 128, 160, 192, 256])
 def test_every_tile_height(gpu, tile_m, monkeypatch):
     monkeypatch.setenv("MOE_TILE_M", str(tile_m))
     for name in ("ragged", "batched"):
@@ -738,6 +750,25 @@ def test_mid_fused_equals_chain(gpu, name, tile_m, monkeypatch):
 def test_mid_forward_end_to_end(gpu, name, tile_m, monkeypatch):
     monkeypatch.setenv("MOE_TILE_M", str(tile_m))
     _forward_end_to_end(name)
+
+
+@pytest.mark.parametrize("name", ["mid_ue8m0", "mid_fp32", "mid_bf16", "mid_batched",
+                                  "split_ue8m0"])
+def test_k_rotation_forced(gpu, name, monkeypatch):
+    """The GEMMs with the k-step rotation forced on (by default it runs only
+    where the weight rows are a multiple of 4 KB, which these configs' rows
+    are not): both GEMMs on the oracle's inputs, every routed row; the fused
+    w13 equal to the unfused pair bit for bit at two tile heights (they share
+    the rotation key); the forward output within its bound."""
+    monkeypatch.setenv("MOE_KROT", "1")
+    cfg, h, dev, ref = case(name)
+    _gemm_isolated(cfg, h, dev, ref, "w13")
+    _gemm_isolated(cfg, h, dev, ref, "w2")
+    for t in (16, 128):
+        monkeypatch.setenv("MOE_TILE_M", str(t))
+        _fused_equals_chain(name, t)
+    monkeypatch.delenv("MOE_TILE_M")
+    check_output(to_np(run_forward(cfg, dev)), ref["out"], f"{name} rotated output")
 
 
 @pytest.mark.parametrize("ksplit", [1, 2, 4])
