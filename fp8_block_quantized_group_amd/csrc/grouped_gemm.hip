@@ -498,7 +498,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // when the weight rows are a multiple of 4 KB long, blocks that stream at
   // the same k-step read the same offset of every row, which concentrates
   // the reads on a few HBM channels (a probe: 4.7 TB/s at a 4096-byte row
-  // stride, 6.3 TB/s with the step order staggered per block).  rot depends
+  // stride, 6.3 TB/s with the step order staggered per block; in the GEMMs,
+  // whose blocks drift apart, it measured -1.5 % on a fused w13 of 8
+  // experts at K = 4096 and -0.8 % on one of 144 experts).  rot depends
   // on the expert and on the output columns' 256-column pair only (w13:
   // counted within the gate or the up half), so the fused and the unfused
   // w13, every tile height and width, and every batch add a column's
@@ -683,8 +685,9 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       sw_panel + (ACT ? (kq >= 2 ? 1 : 0) : (wn * S::WAVE_N) / 128) * S::PG;
 
   // the rest of a k-step: activation rows, their scales, MX weight scales
-  // (kb relative to k0; k0 is a multiple of 4, so kb & 3 is the absolute
-  // k-step's position in its group of 4)
+  // (kb: the block's step index, kabs(kb) the k-step it loads; the MX
+  // schemes never rotate and k0 is a multiple of 4, so there kb & 3 is the
+  // absolute k-step's position in its group of 4)
   auto issue_as = [&](int kb) {
     const uint32_t st = smem_base + (kb % S::STAGES) * STAGE;
     const int ka = kabs(kb);
@@ -1115,14 +1118,13 @@ hipError_t launch_shape(const GemmArgs& pin, int max_tiles, hipStream_t stream) 
   // k-step rotation: weight rows of a multiple of 4 KB (the MX schemes keep
   // the plain order: their scale panel arrives in groups of 4 k-steps).
   // MOE_KROT = 0 | 1 overrides (read at every launch).
+  constexpr bool mx = SC == kQuantMxfp8 || SC == kSchemeMxfp8W4;
   {
-    constexpr bool mxs = SC == kQuantMxfp8 || SC == kSchemeMxfp8W4;
     const char* env = getenv("MOE_KROT");
     const bool want = env != nullptr ? env[0] == '1' : p.Kd % 4096 == 0;
-    p.krot = (!mxs && want && p.rot_period > 0 && p.rot_period % 256 == 0) ? 1 : 0;
+    p.krot = (!mx && want && p.rot_period > 0 && p.rot_period % 256 == 0) ? 1 : 0;
   }
   // the block scheme's weight-scale panel holds S::PG k-steps
-  constexpr bool mx = SC == kQuantMxfp8 || SC == kSchemeMxfp8W4;
   if (!mx && p.Kd / kGroup > S::PG) return hipErrorInvalidValue;
   // every XCD's slice: whole items' splits, ceil(items / 8) * splits blocks
   // (the schedule's slicing; rounding items * splits up to 8 instead would
