@@ -104,6 +104,9 @@ struct GemmArgs {
   // rotation on
   int rot_period;
   int krot;
+  // 1: each XCD walks its slice of the tile list in the zipper order (heavy
+  // groups from the front, light ones from the back); 0: in list order
+  int zip;
 };
 
 // zero n int32 (a fill kernel: safe under graph capture)

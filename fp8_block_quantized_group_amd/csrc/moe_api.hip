@@ -544,6 +544,9 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
       max_tiles = (int)pl.s.max_tiles_tall;
     }
   }
+  // the zipper mixes heavy and light experts: not for a lone list of
+  // 256-row tiles, whose experts are all heavy
+  g.zip = (tile_m == 256 && !tall_list) ? 0 : 1;
   g.Kd = w13 ? p->hidden : p->intermediate;
   g.Nout = w13 ? (int)w13_rows(p) : p->hidden;
   // a gated w13's gate and up halves are keyed alike (their 256-column pairs
