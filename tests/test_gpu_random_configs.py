@@ -61,7 +61,8 @@ def _draw(i):
     elif rng.random() < 0.5:
         kw["pad_frac"] = 0.07
     if layout == "contiguous" and E >= 4 and rng.random() < 0.5:
-        kw["num_logical"] = E - int(rng.integers(1, E // 2 + 1))   # EPLB replicas
+        # EPLB replicas of distinct logical experts; top_k of them per token
+        kw["num_logical"] = max(top_k, E - int(rng.integers(1, E // 2 + 1)))
     env = {}
     r = rng.random()
     if tall:
