@@ -430,6 +430,12 @@ moe_status_t check_stage_args(const moe_problem_t* p, const void* hidden,
   CHECK(check_ptr(topk_ids, "topk_ids", 4));
   CHECK(check_ptr(topk_weights, "topk_weights", 4));
   if (batched(p)) CHECK(check_ptr(counts_in, "expert_num_tokens (batched layout)", 4));
+  // the replica remap is part of staging token-ordered input; batched slabs
+  // come from a dispatch that already chose physical experts
+  if (batched(p) && eplb != nullptr)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "EPLB remapping needs the contiguous routing (batched slabs are per physical "
+                "expert: pass physical ids and no eplb)");
   CHECK(check_eplb(p, eplb));
   return MOE_OK;
 }

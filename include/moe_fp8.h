@@ -281,7 +281,10 @@ moe_status_t moe_workspace_size(const moe_problem_t* p, size_t* bytes);
  * topk_ids int32 [T, top_k], topk_weights fp32 [T, top_k], is_padding uint8
  * [T] or NULL (padding tokens: ids -1, weights 0, never routed; their hidden
  * rows are still quantized).  expert_num_tokens_in: batched layout only,
- * int32 [E], must equal the per-expert count of topk_ids.  eplb may be NULL.
+ * int32 [E], must equal the per-expert count of topk_ids.  eplb may be NULL;
+ * it needs the contiguous or indexed layout (batched slabs are per physical
+ * expert, from a dispatch that already chose the replicas: pass physical
+ * ids; eplb with BATCHED_MASKED -> MOE_ERR_UNSUPPORTED before any launch).
  * Outputs: x_q fp8 [rows, K] (MOE_Q_BF16: bf16 copy), x_sf (NULL for bf16),
  * topk_idx_out int64 [T, top_k], topk_w_out fp32 [T, top_k], routing.
  * ws: device scratch of moe_stage_workspace_size bytes. */

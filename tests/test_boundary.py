@@ -193,6 +193,15 @@ def test_call_validation_before_launch(lib):
     st = lib.moe_forward(ctypes.byref(pbt), V, None, V, V, None, None, V, V, V, V, V, V,
                          1 << 30, None)
     assert st == -1 and "expert_num_tokens" in lib.moe_last_error().decode()
+    # EPLB remapping needs the contiguous routing: batched slabs are already
+    # per physical expert
+    e = moe._Eplb(V, 1, V, 2, None, None, None)
+    st = lib.moe_forward(ctypes.byref(pbt), V, V, V, V, None, ctypes.byref(e), V, V, V, V, V, V,
+                         1 << 30, None)
+    assert st == -2 and "EPLB" in lib.moe_last_error().decode()
+    st = lib.moe_forward(ctypes.byref(p), V, None, V, V, None, ctypes.byref(e), V, V, V, V, V, V,
+                         16, None)
+    assert st == -3, "the contiguous layout accepts eplb (then fails on the small workspace)"
     # x_sf given for bf16 staging
     r = moe._Routing(V, V, V, V, V)
     st = lib.moe_stage(ctypes.byref(pb), V, None, V, V, None, None, V, V, V, V,

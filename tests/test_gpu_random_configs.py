@@ -5,7 +5,8 @@ these draw the corners' combinations instead: every scheme pair (UE8M0 and
 fp32 per-128 scales, MXFP8 and MXFP4 weights with MXFP8 activations, bf16
 activations), the contiguous, batched and indexed layouts, 1-320 tokens,
 1-40 experts, top-k 1-8, hidden and intermediate sizes of 1-12 scale groups,
-uniform or Zipf routing, padding tokens, EPLB replicas, and a forced tile
+uniform or Zipf routing, padding tokens, EPLB replicas (contiguous and indexed
+layouts: the batched layout takes physical ids), and a forced tile
 height (MOE_TILE_M) or w2 split (MOE_KSPLIT) on top; every fifth of the
 later draws is shaped (about 100 rows per expert, Zipf) to put its heavy
 experts in the second, 256-row tile list.  A forced tile height
@@ -60,7 +61,7 @@ def _draw(i):
         kw["max_tokens"] = T                     # an expert gets each token at most once
     elif rng.random() < 0.5:
         kw["pad_frac"] = 0.07
-    if layout == "contiguous" and E >= 4 and rng.random() < 0.5:
+    if layout != "batched" and E >= 4 and rng.random() < 0.5:
         # EPLB replicas of distinct logical experts; top_k of them per token
         kw["num_logical"] = max(top_k, E - int(rng.integers(1, E // 2 + 1)))
     env = {}
@@ -92,6 +93,8 @@ def test_random_config(gpu, i, monkeypatch):
     _, h, dev, ref = P.case(cfg.name)
     out = P.run_forward(cfg, dev)
     check_output(to_np(out), ref["out"], f"{cfg.name} moe_forward output")
+    if cfg.eplb:
+        assert np.array_equal(to_np(dev["eplb"]["expert_load"]), ref["load"])
     again = P.run_forward(cfg, dev)
     assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "not deterministic"
     if cfg.pad_frac > 0:
