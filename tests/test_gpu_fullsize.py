@@ -18,7 +18,7 @@ import fp8_block_quantized_group_amd as moe
 import moe_synth
 from oracle import moe_oracle as O
 from parity_util import (abs_gemm_cfg, check_bf16_act_chain, check_gemm, check_output,
-                         check_requant_chain, to_np)
+                         check_requant_chain, to_dev, to_np)
 from test_gpu_parity import check_schedule, run_chain, run_forward
 
 pytestmark = pytest.mark.gpu
@@ -105,10 +105,27 @@ def test_full_size_sampled(name):
     ref = O.forward_tokens(h, tokens, st)
     gate_up, a2_q, down = (to_np(chain[k]) for k in ("gate_up", "a2_q", "down"))
     a2_sf = None if chain["a2_sf"] is None else to_np(chain["a2_sf"])
-    GN = cfg.N // grp
     rows = sorted(ref["rows"])
+    # w2 alone, to its element bound: the oracle's a2 rows replace the GPU's
+    # in a copy of the chain's a2, the GPU's w2 GEMM runs on that copy, and
+    # those rows' outputs are held to the oracle's down rows (the oracle
+    # never takes a GPU intermediate as input)
+    q_rows = np.stack([ref["rows"][r]["a2_q"] for r in rows])
+    s_rows = None if a2_sf is None else np.stack([ref["rows"][r]["a2_sf"] for r in rows])
+    idx = torch.tensor(rows, dtype=torch.int64, device="cuda")
+    a2_q_in = chain["a2_q"].clone()
+    a2_q_in[idx] = to_dev(q_rows)
+    a2_sf_in = None
+    if s_rows is not None:
+        a2_sf_in = chain["a2_sf"].clone()
+        a2_sf_in[idx] = to_dev(O.pack_ue8m0_rows(s_rows) if ue and grp == 128 else s_rows)
+    down_in = torch.empty_like(chain["down"])
+    moe.grouped_gemm_w2(moe.Problem.from_config(cfg), a2_q_in, a2_sf_in, bufs, inp["w2"],
+                        inp["w2_sf"], down_in)
+    torch.cuda.synchronize()
+    down_in = to_np(down_in)
     gu_got, gu_want, gu_abs, dn_got, dn_want, dn_abs = [], [], [], [], [], []
-    for r in rows:
+    for i, r in enumerate(rows):
         info = ref["rows"][r]
         e = info["expert"]
         w13e, w13s = O._np(inp["w13"][e]), O._np(inp["w13_sf"][e])
@@ -118,16 +135,14 @@ def test_full_size_sampled(name):
                                    w13e, w13s)[0])
         gu_got.append(gate_up[r])
         gu_want.append(info["gate_up"])
-        # w2 on the GPU's own a2 row: the GEMM alone, to its element bound
-        a_row = a2_q[r:r + 1]
-        sf_row = None if a2_sf is None else a2_sf[r:r + 1, :GN]
-        dn_want.append(O.bf16_round(O.expert_gemm(cfg, a_row, sf_row, w2e, w2s))[0])
-        dn_abs.append(abs_gemm_cfg(cfg, a_row, sf_row, w2e, w2s)[0])
-        dn_got.append(down[r])
+        dn_abs.append(abs_gemm_cfg(cfg, q_rows[i:i + 1],
+                                   None if s_rows is None else s_rows[i:i + 1], w2e, w2s)[0])
+        dn_got.append(down_in[r])
+        dn_want.append(info["down"])
     gu_got, gu_want, gu_abs = np.stack(gu_got), np.stack(gu_want), np.stack(gu_abs)
     f13 = check_gemm(gu_got, gu_want, gu_abs, f"{name} gate_up rows {rows}")
     f2 = check_gemm(np.stack(dn_got), np.stack(dn_want), np.stack(dn_abs),
-                    f"{name} down rows {rows}")
+                    f"{name} down rows {rows} (w2 on the oracle's a2)")
     a2_want = np.stack([ref["rows"][r]["a2_q"] for r in rows])
     if cfg.act_quant == "bf16":
         fa = check_bf16_act_chain(a2_q[rows], a2_want, gu_want, gu_abs, f"{name} a2 rows")
