@@ -293,10 +293,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // block scales, per-128 activation scales, fp32 promotion per k-step) or
 // kQuantMxfp8 (E8M0 scale per row and 32 columns on both operands, handed
 // to the MFMA itself, which then accumulates across k-steps directly).
-template <class S, int SC, bool ACT>
+// NP: n-tiles per work item.  With NP = 2 (plain GEMM, per-128 scale
+// schemes, no split) a block computes two neighbouring n-tiles of its m-tile
+// in one k-loop of 2G steps: the second tile's first copies go out during
+// the first tile's last k-steps, and its epilogue stores overlap them.
+template <class S, int SC, bool ACT, int NP = 1>
 __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_kernel(
     const GemmArgs p) {
   static_assert(!ACT || (S::BN == 256 && S::WN == 4 && S::TN == 4), "fused activation tile");
+  static_assert(NP == 1 || (NP == 2 && !ACT && (SC == kQuantUe8m0 || SC == kQuantF32)),
+                "paired n-tiles: plain GEMM, per-128 scales");
   constexpr bool W4 = SC == kSchemeMxfp8W4;   // e2m1 weights
   constexpr bool A16 = SC == kQuantBf16;      // unquantized bf16 activations
   // activation-tile bytes per row and k-step (128 fp8 or 128 bf16 values)
@@ -318,7 +324,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // block scheme keeps its fp32 weight-scale panel there instead
   constexpr int STAGE = SC_OFF + (A16 ? 0 : S::SC_WAVES * 256);
   constexpr int WSC_SLOT = S::BN * 16;
-  constexpr int PANEL = MX ? 2 * WSC_SLOT : S::NBLK * S::PG * 4;
+  constexpr int PANEL = MX ? 2 * WSC_SLOT : NP * S::NBLK * S::PG * 4;
   constexpr int LDS = S::STAGES * STAGE + PANEL;
   constexpr int LMAX = AI + BI + 1 + (MX ? 1 : 0);
   static_assert(LDS <= 160 * 1024 && 3 * LMAX < 64, "LDS ring / vmcnt range");
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // 8 blocks dealt to the XCDs in turn measured slower: they split the
   // heavy experts' blocks over more XCDs.)
   const bool indexed = p.sorted_ids != nullptr;
-  const int NT = p.Nout / S::BN;
+  const int NT = p.Nout / S::BN / NP;   // work items per m-tile (NP n-tiles each)
   // split-K: the S splits of one (tile, n-tile) item are consecutive work
   // items, so they run at about the same time (the last one's partial reads
   // then find the others' partials still in L2 / MALL)
@@ -482,7 +488,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     w_once = S::BM <= 160 && !W4 && info[4] <= S::BM;
     base = info[5];
   }
-  const int n0 = nt * S::BN;          // first output column (plain GEMM)
+  const int n0 = nt * S::BN * NP;     // first output column (plain GEMM)
   const int Nh = p.Nout / 2;            // ACT: columns of h
   const int j0 = nt * (S::BN / 2);      // ACT: first column of h
 
@@ -513,17 +519,29 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // counted within the gate or the up half), so the fused and the unfused
   // w13, every tile height and width, and every batch add a column's
   // k-steps in the same order.
-  int rot = 0;
+  int rot = 0, rot1 = 0;   // rot1: the second n-tile's (NP = 2)
   if constexpr (!MX) {
     if (p.krot != 0 && G > 1) {
       const int key = ((ACT ? j0 : n0) % p.rot_period) / 256;
       rot = __builtin_amdgcn_readfirstlane((5 * key + 3 * e) % G);
+      if constexpr (NP == 2) {
+        const int key1 = ((n0 + S::BN) % p.rot_period) / 256;
+        rot1 = __builtin_amdgcn_readfirstlane((5 * key1 + 3 * e) % G);
+      }
     }
   }
+  // the loop's steps: G per n-tile, NP n-tiles (steps G .. 2G-1: the second)
+  const int GG = NP * G;
   // absolute k-step of the block's kb-th step
   auto kabs = [&](int kb) {
-    const int r = kb + rot;
-    return k0 + (r >= G ? r - G : r);
+    if constexpr (NP == 2) {
+      const bool h = kb >= G;
+      const int r = (h ? kb - G : kb) + (h ? rot1 : rot);
+      return k0 + (r >= G ? r - G : r);
+    } else {
+      const int r = kb + rot;
+      return k0 + (r >= G ? r - G : r);
+    }
   };
 
   // activation row of tile row m (an id that is padding gathers row T,
@@ -552,7 +570,8 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   const v4i rs_b =
       ACT ? buffer_rsrc(p.w + (int64_t)e * p.Nout * wstride,
                         (uint32_t)((int64_t)p.Nout * wstride))
-          : buffer_rsrc(p.w + ((int64_t)e * p.Nout + n0) * wstride, (uint32_t)(S::BN * wstride));
+          : buffer_rsrc(p.w + ((int64_t)e * p.Nout + n0) * wstride,
+                        (uint32_t)(NP * S::BN * wstride));
   uint32_t b_off[BI];
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
@@ -574,11 +593,13 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
 #pragma unroll
     for (int i = 0; i < BI; ++i)
       dma16_w(rs_b, st + AB + i * S::THREADS * 16 + wave_slot,
-              b_off[i] + (uint32_t)kabs(kb) * WROW, w_once);
+              b_off[i] + (NP == 2 && kb >= G ? (uint32_t)(S::BN * wstride) : 0u) +
+                  (uint32_t)kabs(kb) * WROW,
+              w_once);
   };
 #pragma unroll
   for (int s = 0; s < S::STAGES - 1; ++s)
-    if (s < G) issue_b(s);
+    if (s < GG) issue_b(s);
 
   const v4i rs_a = buffer_rsrc(p.a, p.a_bytes);
   const v4i rs_s = buffer_rsrc(p.a_sf, p.a_sf_bytes);
@@ -637,7 +658,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // first k-step's wait covers them)
   float* sw_panel = reinterpret_cast<float*>(smem + S::STAGES * STAGE);
   if constexpr (!MX) {
-    if (wave < S::NBLK) {
+    if (wave < NP * S::NBLK) {
       const int b = wave;
       // ACT: block 0 = the gate rows' scale block, block 1 = the up rows'
       const int blk = ACT ? (b == 0 ? j0 : Nh + j0) / kGroup : n0 / kGroup + b;
@@ -691,6 +712,11 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
   // hold gate rows, lanes 32-63 up rows)
   const float* sw_mine =
       sw_panel + (ACT ? (kq >= 2 ? 1 : 0) : (wn * S::WAVE_N) / 128) * S::PG;
+  // the weight scale of step kb (NP = 2: the second n-tile's blocks follow
+  // the first's in the panel)
+  auto sw_of = [&](int kb) {
+    return sw_mine[(NP == 2 && kb >= G ? S::NBLK * S::PG : 0) + kabs(kb)];
+  };
 
   // the rest of a k-step: activation rows, their scales, MX weight scales
   // (kb: the block's step index, kabs(kb) the k-step it loads; the MX
@@ -738,7 +764,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       // 16x16x32 bf16 MFMAs per sub-tile per 128-deep block, chained in a
       // partial, then acc += partial * sw
       const uint8_t* sb = smem + (kb % S::STAGES) * STAGE;
-      const float sw = sw_mine[kabs(kb)];
+      const float sw = sw_of(kb);
       v8bf wb[S::TN][4];
 #pragma unroll
       for (int i = 0; i < S::TN; ++i) {
@@ -827,7 +853,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
         const v4i hi = *reinterpret_cast<const v4i*>(sb + w_frag1 + i * 4 * kRowBytes);
         wf[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       }
-      const float sw = sw_mine[kabs(kb)];
+      const float sw = sw_of(kb);
       // activation fragment j (and its scale) is read when sub-tile j-1's
       // MFMAs start, so at most two are live
       auto load_a = [&](int j, v8i& f, float& fs) {
@@ -870,15 +896,46 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     }
   };
 
+  // plain GEMM epilogue: this lane's rows of acc as bf16, columns nf + [0, 4TN)
+  auto store_rows = [&]([[maybe_unused]] int nf) {
+    if constexpr (!ACT) {
+#pragma unroll
+      for (int j = 0; j < S::TM; ++j) {
+        const int ml = ml0 + kSubStride * j;
+        if (ml >= rows_here) continue;
+        const int64_t row = out_row_of(ml);
+        if (row < 0) continue;
+        uint16_t* dst = p.out + row * (int64_t)p.Nout + nf;
+        uint32_t packed[2 * S::TN];
+#pragma unroll
+        for (int i = 0; i < S::TN; ++i) {
+          packed[2 * i] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
+          packed[2 * i + 1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+        }
+#pragma unroll
+        for (int v = 0; v < S::TN / 2; ++v) {
+          // written once, read once by the reduce: non-temporal (measured
+          // w2 -0.6 % DSv3-shaped, -2.2 % Qwen3-shaped)
+          const v4i o = {(int)packed[4 * v], (int)packed[4 * v + 1], (int)packed[4 * v + 2],
+                         (int)packed[4 * v + 3]};
+          __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(dst) + v);
+        }
+      }
+    }
+  };
+
   auto main_loop = [&](auto live_c) {
     // prologue: STAGES-1 k-steps in flight (their weight copies went first)
 #pragma unroll
     for (int s = 0; s < S::STAGES - 1; ++s)
-      if (s < G) issue_as(s);
-    for (int kb = 0; kb < G; ++kb) {
+      if (s < GG) issue_as(s);
+    for (int kb = 0; kb < GG; ++kb) {
       // k-step kb has landed for every wave, and every wave's reads of
       // k-step kb-1 (whose slot the next issue reuses) have completed
-      const int after = min(kb + S::STAGES - 2, G - 1) - kb;
+      // (NP = 2: the first tile's epilogue stores, issued after later
+      // copies, only make these waits longer, never shorter: the copies
+      // land in issue order)
+      const int after = min(kb + S::STAGES - 2, GG - 1) - kb;
       if (kb < S::STAGES - 2) {
         // loads issued after k-step kb's last one: the activation parts of
         // the later prologue k-steps and the whole k-steps issued since
@@ -895,8 +952,18 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       } else {
         stage_landed<LMAX>(loads_per_stage, after);
       }
-      if (kb + S::STAGES - 1 < G) issue(kb + S::STAGES - 1);
+      if (kb + S::STAGES - 1 < GG) issue(kb + S::STAGES - 1);
       compute(kb, live_c);
+      if constexpr (NP == 2) {
+        if (kb == G - 1) {
+          // the first n-tile is complete: store it, start the second
+          store_rows(n0 + wn * S::WAVE_N + kq * (4 * S::TN));
+#pragma unroll
+          for (int i = 0; i < S::TN; ++i)
+#pragma unroll
+            for (int j = 0; j < S::TM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+        }
+      }
     }
   };
   // live sub-tiles of this wave (wave-uniform)
@@ -1014,7 +1081,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
     }
   } else {
     // ---- epilogue: lane owns output row m, columns n_first .. n_first+4*TN-1
-    const int n_first = n0 + wn * S::WAVE_N + kq * (4 * S::TN);
+    const int n_first = n0 + (NP - 1) * S::BN + wn * S::WAVE_N + kq * (4 * S::TN);
     if (nsplit > 1) {
       // split-K: this split's fp32 partial, then a ticket; the block with
       // the last ticket adds the partials in split order (its own from
@@ -1075,28 +1142,7 @@ __global__ __launch_bounds__(S::THREADS, S::MIN_WAVES_PER_EU) void grouped_gemm_
       if (tid == 0)
         __hip_atomic_store(p.counters + item, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-#pragma unroll
-    for (int j = 0; j < S::TM; ++j) {
-      const int ml = ml0 + kSubStride * j;
-      if (ml >= rows_here) continue;
-      const int64_t row = out_row_of(ml);
-      if (row < 0) continue;
-      uint16_t* dst = p.out + row * (int64_t)p.Nout + n_first;
-      uint32_t packed[2 * S::TN];
-#pragma unroll
-      for (int i = 0; i < S::TN; ++i) {
-        packed[2 * i] = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-        packed[2 * i + 1] = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
-      }
-#pragma unroll
-      for (int v = 0; v < S::TN / 2; ++v) {
-        // written once, read once by the reduce: non-temporal (measured
-        // w2 -0.6 % DSv3-shaped, -2.2 % Qwen3-shaped)
-        const v4i o = {(int)packed[4 * v], (int)packed[4 * v + 1], (int)packed[4 * v + 2],
-                       (int)packed[4 * v + 3]};
-        __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(dst) + v);
-      }
-    }
+    store_rows(n_first);
   }
 }
 
@@ -1107,7 +1153,7 @@ static_assert(Shape<160, 256, 8, 3>::PG >= kTile160MaxGroups &&
                   Shape<160, 128, 8, 3>::PG >= kTile160MaxGroups,
               "160-row tiles: reduction length limit");
 
-template <class S, int SC, bool ACT>
+template <class S, int SC, bool ACT, int NP = 1>
 hipError_t launch_shape(const GemmArgs& pin, int max_tiles, hipStream_t stream) {
   // Item order inside a group: consecutive blocks on an XCD start about a
   // block time / 32 apart and an operand's k-slice stays in L2 for only a few
@@ -1138,7 +1184,7 @@ hipError_t launch_shape(const GemmArgs& pin, int max_tiles, hipStream_t stream) 
   // (the schedule's slicing; rounding items * splits up to 8 instead would
   // leave splits of the last items without a block)
   const int64_t blocks =
-      ((int64_t)max_tiles * (p.Nout / S::BN) + 7) / 8 * 8 * (ACT ? 1 : max(p.ksplit, 1));
+      ((int64_t)max_tiles * (p.Nout / (S::BN * NP)) + 7) / 8 * 8 * (ACT ? 1 : max(p.ksplit, 1));
   const dim3 grid((unsigned)blocks);
   if constexpr (SC == kQuantBf16) {
     // bf16 activation tiles take twice the LDS: only shapes whose ring fits
@@ -1150,7 +1196,7 @@ hipError_t launch_shape(const GemmArgs& pin, int max_tiles, hipStream_t stream) 
     else
       return hipErrorInvalidValue;
   } else {
-    grouped_gemm_kernel<S, SC, ACT><<<grid, S::THREADS, 0, stream>>>(p);
+    grouped_gemm_kernel<S, SC, ACT, NP><<<grid, S::THREADS, 0, stream>>>(p);
   }
   return hipGetLastError();
 }
@@ -1229,6 +1275,12 @@ hipError_t launch_grouped_gemm_sc(const GemmArgs& p, int tile_m, int max_tiles, 
         static const char* env = getenv("MOE_GEMM_WIDE");
         constexpr bool mx = SC == kQuantMxfp8 || SC == kSchemeMxfp8W4;
         const bool wide = env != nullptr ? env[0] != '0' : (!mx || p.wide == 1);
+        if constexpr (SC == kQuantUe8m0 || SC == kQuantF32) {
+          // two n-tiles per block where the caller asks for it (contiguous or
+          // batched layout, no split)
+          if (p.pair == 1 && p.Nout % 512 == 0 && p.ksplit <= 1 && p.sorted_ids == nullptr)
+            return launch_shape<Shape<128, 256, 8, 3>, SC, false, 2>(p, max_tiles, stream);
+        }
         if (wide && p.Nout % 256 == 0)
           return launch_shape<Shape<128, 256, 8, 3>, SC, false>(p, max_tiles, stream);
         return launch_shape<Shape<128, 128, 4, 2>, SC, false>(p, max_tiles, stream);

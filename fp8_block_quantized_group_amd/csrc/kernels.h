@@ -107,6 +107,10 @@ struct GemmArgs {
   // 1: each XCD walks its slice of the tile list in the zipper order (heavy
   // groups from the front, light ones from the back); 0: in list order
   int zip;
+  // 1: plain GEMM at 128-row tiles computes two neighbouring 256-column
+  // n-tiles per block (per-128 scale schemes, Nout % 512 == 0, no split,
+  // not the indexed layout; otherwise ignored)
+  int pair;
 };
 
 // zero n int32 (a fill kernel: safe under graph capture)

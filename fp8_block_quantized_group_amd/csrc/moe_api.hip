@@ -553,6 +553,18 @@ moe_status_t run_gemm(const moe_problem_t* p, const Plan& pl, bool w13, const vo
   // the zipper mixes heavy and light experts: not for a lone list of
   // 256-row tiles, whose experts are all heavy
   g.zip = (tile_m == 256 && !tall_list) ? 0 : 1;
+  // w2 at 128-row tiles: two neighbouring n-tiles per block.  Its k-loop is
+  // short where N is (16 k-steps at N = 2048), and a block's prologue and
+  // epilogue, which nothing overlaps at one block per CU, are then about a
+  // fifth of its time; the pair overlaps the second tile's first copies
+  // with the first tile's last steps and stores (DSv3-shaped prefill
+  // layer 2.796 -> 2.768 ms).  Pairs of 256-row tiles measured no better
+  // (DSv3-shaped prefill +0.7 %, Qwen3-shaped within noise), so the kernel
+  // takes them at 128 rows only.  MOE_PAIR = 0 | 1 overrides.
+  {
+    const char* env = getenv("MOE_PAIR");
+    g.pair = !w13 && (env != nullptr ? env[0] == '1' : true) ? 1 : 0;
+  }
   g.Kd = w13 ? p->hidden : p->intermediate;
   g.Nout = w13 ? (int)w13_rows(p) : p->hidden;
   // a gated w13's gate and up halves are keyed alike (their 256-column pairs

@@ -804,6 +804,43 @@ def test_w2_split_k(gpu, name, ksplit, monkeypatch):
     check_output(to_np(run_forward(cfg, dev)), ref["out"], f"{name} split {ksplit} output")
 
 
+@pytest.mark.parametrize("name,tile_m", [("mid_ue8m0", "128"), ("tall_ue8m0", None),
+                                         ("tall_fp32", None), ("tall_batched", None)])
+def test_w2_paired_tiles(gpu, name, tile_m, monkeypatch):
+    """w2 at 128-row tiles takes two neighbouring 256-column n-tiles per
+    block by default (MOE_PAIR): on the oracle's a2 every routed row is
+    within the GEMM bound, and the bits equal those of one n-tile per block,
+    for the GEMM alone and through moe_forward."""
+    if tile_m is None:
+        monkeypatch.delenv("MOE_TILE_M", raising=False)
+    else:
+        monkeypatch.setenv("MOE_TILE_M", tile_m)
+    monkeypatch.delenv("MOE_TALL", raising=False)
+    cfg, h, dev, ref = case(name)
+    p = problem(cfg)
+    s = moe.sizes(p)
+    assert s["tile_m"] == 128 and cfg.K % 512 == 0 and cfg.act_quant in ("ue8m0", "fp32")
+    ue = O.act_e8m0(cfg)
+    vr = valid_rows(cfg, ref)
+    a_q = to_dev(ref["a2_q"])
+    a_sf = to_dev(O.pack_ue8m0_rows(ref["a2_sf"]) if ue else ref["a2_sf"])
+    routing = oracle_routing(p, cfg, ref)
+    got = {}
+    for v in ("1", "0"):
+        monkeypatch.setenv("MOE_PAIR", v)
+        down = torch.full((s["expert_rows"], cfg.K), SENTINEL_BF16, dtype=torch.int16,
+                          device="cuda").view(torch.bfloat16)
+        moe.grouped_gemm_w2(p, a_q, a_sf, routing, dev["w2"], dev["w2_sf"], down)
+        torch.cuda.synchronize()
+        got[v] = (to_np(down), to_np(run_forward(cfg, dev)))
+    untouched = np.setdiff1d(np.arange(s["expert_rows"]), vr)
+    assert np.all(got["1"][0][untouched] == SENTINEL_BF16), "paired w2 wrote rows outside"
+    check_gemm(got["1"][0][vr], ref["down"][vr], gemm_abs(cfg, h, ref, "w2")[vr],
+               f"{name} paired w2")
+    assert np.array_equal(got["1"][0], got["0"][0]), f"{name}: paired w2 bits differ"
+    assert np.array_equal(got["1"][1], got["0"][1]), f"{name}: paired layer bits differ"
+
+
 # ---------------------------------------------------------------------------
 # the second (tall) tile list at the default tile height
 # ---------------------------------------------------------------------------
