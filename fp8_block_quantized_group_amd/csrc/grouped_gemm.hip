@@ -1276,9 +1276,8 @@ hipError_t launch_grouped_gemm_sc(const GemmArgs& p, int tile_m, int max_tiles, 
         constexpr bool mx = SC == kQuantMxfp8 || SC == kSchemeMxfp8W4;
         const bool wide = env != nullptr ? env[0] != '0' : (!mx || p.wide == 1);
         if constexpr (SC == kQuantUe8m0 || SC == kQuantF32) {
-          // two n-tiles per block where the caller asks for it (contiguous or
-          // batched layout, no split)
-          if (p.pair == 1 && p.Nout % 512 == 0 && p.ksplit <= 1 && p.sorted_ids == nullptr)
+          // two n-tiles per block where the caller asks for it (no split)
+          if (p.pair == 1 && p.Nout % 512 == 0 && p.ksplit <= 1)
             return launch_shape<Shape<128, 256, 8, 3>, SC, false, 2>(p, max_tiles, stream);
         }
         if (wide && p.Nout % 256 == 0)

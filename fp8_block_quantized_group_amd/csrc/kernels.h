@@ -108,8 +108,8 @@ struct GemmArgs {
   // groups from the front, light ones from the back); 0: in list order
   int zip;
   // 1: plain GEMM at 128-row tiles computes two neighbouring 256-column
-  // n-tiles per block (per-128 scale schemes, Nout % 512 == 0, no split,
-  // not the indexed layout; otherwise ignored)
+  // n-tiles per block (per-128 scale schemes, Nout % 512 == 0, no split;
+  // otherwise ignored)
   int pair;
 };
 

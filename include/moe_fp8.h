@@ -263,8 +263,8 @@ typedef struct {
  * batch nor the tile shape, but it does set the order of the fp32 additions:
  * every call of one layer must see the same value.  MOE_PAIR = 0 | 1 turns
  * off or on the w2 GEMM's two 256-column n-tiles per block at 128-row tiles
- * (default on; per-128 fp8 activations, hidden a multiple of 512, no split,
- * not the indexed entry points; read at every call): the second tile's
+ * (default on; per-128 fp8 activations, hidden a multiple of 512, no split;
+ * read at every call): the second tile's
  * first copies overlap the first tile's last k-steps and stores.  It
  * changes neither the schedule nor a result's bits. */
 
