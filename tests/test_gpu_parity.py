@@ -883,6 +883,24 @@ TALL_INDEXED = moe_synth.custom(name="tall_indexed", T=256, E=8, top_k=3, K=1024
                                 layout="indexed")
 
 
+def test_w2_paired_tiles_indexed(gpu, monkeypatch):
+    """The indexed layout's moe_forward, whose w2 takes two 256-column
+    n-tiles per 128-row block by default (MOE_PAIR): the output within the
+    bound, and the same bits with the pairs off."""
+    monkeypatch.delenv("MOE_TILE_M", raising=False)
+    monkeypatch.delenv("MOE_TALL", raising=False)
+    cfg = TALL_INDEXED
+    CASES.setdefault(cfg.name, cfg)
+    _, h, dev, ref = case(cfg.name)
+    assert moe.sizes(problem(cfg))["tile_m"] == 128 and cfg.K % 512 == 0
+    outs = {}
+    for v in ("1", "0"):
+        monkeypatch.setenv("MOE_PAIR", v)
+        outs[v] = to_np(run_forward(cfg, dev))
+    check_output(outs["1"], ref["out"], "tall_indexed paired w2")
+    assert np.array_equal(outs["1"], outs["0"]), "indexed layer: paired w2 bits differ"
+
+
 def test_tall_list_indexed(gpu, monkeypatch):
     """The indexed layout with the tall list: 256-row tiles cover 256
     positions of a heavy expert's segment of the 128-block map (never the
